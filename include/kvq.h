@@ -1,0 +1,168 @@
+/*
+ * kvq.h — decode attention over a group-wise, asymmetrically quantized KV cache
+ * on AMD Instinct MI355X (gfx950).  C ABI; plain pointers and sizes only.
+ *
+ * The method (sources are cited by page title and section):
+ *   [P1] nalar.dev, "Kuantisasi KV cache mengganggu attention melalui key dan
+ *        value tersimpan": attention of one head over stored keys and values,
+ *        s = q K^T / sqrt(d), a = softmax(s), o = a V (section "Error pada key
+ *        masuk sebelum softmax"); groups of values sharing a scale and a zero
+ *        point or offset (section "Granularitas kuantisasi menentukan nilai yang
+ *        berbagi scale"); recent tokens kept at higher precision, dequantization
+ *        fused into the attention kernel (section "Pertumbuhan cache mengubah
+ *        trade pada serving").
+ *   [P3] gist.science summary of arXiv 2502.15075, "Quantize What Counts: More
+ *        for Keys, Less for Values": separate bit widths for keys and values
+ *        (section "Probleemstelling"), 4-bit keys with 2-bit values (section
+ *        "Belangrijkste Bijdragen"), key groups of 32 and value groups of 64/128,
+ *        key-only rotation (section "Resultaten").
+ *
+ * Quantizer (per token, per kv head, per group of G consecutive channels):
+ *   zero  = largest fp16 <= min(group)
+ *   scale = smallest fp16 s with zero + (2^b - 1) * s >= max(group)
+ *   code  = clamp(round_half_even((x - zero) / scale), 0, 2^b - 1) in fp64
+ *           (all codes 0 when scale == 0);  x_hat = zero + code * scale.
+ * With key rotation on, keys are first multiplied by the normalized 128-point
+ * Walsh-Hadamard matrix (fp64 butterflies in stage order 1, 2, ..., 64, then a
+ * multiply by RN64(2^-3.5)); the query is rotated the same way before scoring.
+ * Tokens t >= L - window of a length-L sequence stay unquantized in a ring
+ * buffer (slot t mod window); older tokens live in the quantized store.
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ *
+ * Storage.  Quantized tokens are kept in 16-token pages.  One page of one kv
+ * head is a record of
+ *     [K codes 256*k_bits B][K meta 64*(128/k_group) B]
+ *     [V codes 256*v_bits B][V meta 64*(128/v_group) B]
+ * whose internal order matches the register layout of the attention kernel;
+ * kvq_dequantize_debug reads it back in logical order.  Metadata entries are
+ * {fp16 scale, fp16 zero} pairs.
+ *   block_size == 0 (contiguous): page p of kv head h of sequence b is record
+ *       (b * num_kv_heads + h) * pages_per_seq + p, pages_per_seq = ceil(capacity / 16).
+ *   block_size == 16 (paged): page p of sequence b is pool page
+ *       block_table[b * max_blocks_per_seq + p]; its kv head h is record
+ *       pool_page * num_kv_heads + h.
+ * Window buffers k_win, v_win: [batch][num_kv_heads][window][128] of kv_dtype.
+ *
+ * Conventions.
+ *   - All tensor pointers are device pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes; work is enqueued on `stream`.
+ *   - Arguments are validated on the host before anything is launched.  On any
+ *     error nothing is launched and no memory is touched.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Sequence lengths are read on the device; the library never writes them.
+ *     The caller advances them between append and attention.
+ *   - Inputs must be finite with |x| < 2^15 (so fp16 metadata is finite);
+ *     non-finite inputs give unspecified (but memory-safe) results.
+ *   - Calls on different streams touching different caches may run concurrently.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,       /* null or misaligned pointer, inconsistent shapes       */
+  KVQ_EUNSUPPORTED = 2, /* a parameter outside the supported set (see below)      */
+  KVQ_ENOSPACE = 3,     /* workspace too small, or lengths beyond the capacity     */
+  KVQ_EHIP = 4          /* the HIP runtime reported an error at launch            */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+typedef enum { KVQ_ROT_NONE = 0, KVQ_ROT_WHT = 1 } kvq_rotation;
+
+/* Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
+ * k_bits, v_bits in {1, 2, 4, 8}; k_group in {32, 64, 128}; v_group in {64, 128};
+ * window >= 0; block_size in {0, 16}. */
+typedef struct {
+  int32_t head_dim;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t k_bits, k_group;
+  int32_t v_bits, v_group;
+  int32_t window;       /* R: most recent tokens kept unquantized                */
+  int32_t key_rotation; /* kvq_rotation                                           */
+  int32_t kv_dtype;     /* kvq_dtype of appended K/V and of the window buffers    */
+  int32_t block_size;   /* 0 = contiguous, 16 = paged                             */
+} kvq_params;
+
+typedef struct {
+  void *pages;                /* page records (see Storage)                        */
+  void *k_win, *v_win;        /* NULL iff window == 0                              */
+  const int32_t *block_table; /* device [batch][max_blocks_per_seq]; NULL iff block_size == 0 */
+  int32_t batch;
+  int32_t max_blocks_per_seq; /* paged: table row length (ignored when contiguous) */
+  int64_t capacity;           /* contiguous: tokens per sequence; paged: pages in the pool */
+} kvq_cache;
+
+typedef struct {
+  size_t record_bytes; /* one page of one kv head                                 */
+  size_t pages_bytes;  /* whole quantized store for (batch, capacity)             */
+  size_t window_bytes; /* each of k_win and v_win                                 */
+} kvq_sizes;
+
+/* Byte sizes of the buffers of a cache with `batch` sequences and `capacity`
+ * (tokens per sequence when contiguous, pages in the pool when paged).
+ * Memory accounting of payload plus metadata follows [P1] "Pertumbuhan cache
+ * mengubah trade pada serving".  Returns KVQ_EINVAL / KVQ_EUNSUPPORTED for bad
+ * parameters. */
+kvq_status kvq_cache_sizes(const kvq_params *params, int32_t batch, int64_t capacity, kvq_sizes *out);
+
+/* Append up to n_new tokens per sequence and quantize what leaves the window
+ * ([P1] "Granularitas ..." for the quantizer, "Pertumbuhan cache ..." for the
+ * window; [P3] "Resultaten" for key-only rotation).
+ *   seq_lens_before: device int32 [batch], current lengths L_b.
+ *   n_new_per_seq:   device int32 [batch] (each <= n_new), or NULL for n_new everywhere.
+ *   k_new, v_new:    device [batch][n_new][num_kv_heads][128] of kv_dtype; token i of
+ *                    sequence b becomes position L_b + i.
+ * Afterwards positions t < L_b + n_b - window are in the quantized store and the
+ * rest in the ring buffers.  The caller must size the cache for L_b + n_b tokens
+ * (contiguous) and fill the block table for those pages (paged). */
+kvq_status kvq_quantize_append(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens_before,
+                               const int32_t *n_new_per_seq, const void *k_new, const void *v_new, int32_t n_new,
+                               hipStream_t stream);
+
+/* Workspace bytes that kvq_decode_attention needs for this batch and maximum length. */
+size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len);
+
+/* Decode attention of one new query per sequence over its whole cache, with
+ * dequantization fused into the kernel ([P1] "Error pada key masuk sebelum
+ * softmax" for the computation, "Pertumbuhan cache ..." for the fusion).
+ *   seq_lens:    device int32 [batch], lengths after the append (each <= max_seq_len).
+ *   max_seq_len: host upper bound of seq_lens (sizes the launch; must fit the capacity).
+ *   q:           device [batch][num_q_heads][128] of q_dtype.
+ *   out:         device [batch][num_q_heads][128] of out_dtype; fp32 accumulation.
+ *   softmax_scale: 0 means 1/sqrt(128).
+ *   workspace:   device scratch of at least kvq_decode_workspace_bytes(...) bytes.
+ * A sequence of length 0 gets an all-zero output. */
+kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                                int64_t max_seq_len, const void *q, int32_t q_dtype, void *out, int32_t out_dtype,
+                                float softmax_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Read back n positions [t0, t0 + n) of sequence `seq` in logical order (debug
+ * and verification).  Any output pointer may be NULL.
+ *   k_codes, v_codes: device uint8 [n][num_kv_heads][128]; 0xFF for window tokens and t >= L.
+ *   k_meta:  device uint16 [n][num_kv_heads][128/k_group][2] fp16 bits {scale, zero};
+ *   v_meta:  device uint16 [n][num_kv_heads][128/v_group][2]; 0xFFFF for non-quantized positions.
+ *   k_hat, v_hat: device fp32 [n][num_kv_heads][128]: round-to-fp32 of zero + code*scale for
+ *            quantized positions (rotated domain for keys with rotation on), the stored
+ *            value for window positions, NaN for t >= L. */
+kvq_status kvq_dequantize_debug(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                                int32_t seq, int64_t t0, int64_t n, uint8_t *k_codes, uint8_t *v_codes,
+                                uint16_t *k_meta, uint16_t *v_meta, float *k_hat, float *v_hat,
+                                hipStream_t stream);
+
+/* Static description of a status code. */
+const char *kvq_status_str(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

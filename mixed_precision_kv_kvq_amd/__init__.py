@@ -1,0 +1,195 @@
+"""Python binding of libkvq.so: decode attention over a group-wise quantized KV cache.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libkvq.so.  Functions keep the C names of include/kvq.h and accept
+torch tensors (device pointers are taken with ``data_ptr()``) or raw integer
+addresses.  Streams default to torch's current stream.  Importing this package
+fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint8, c_uint16, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_EHIP = range(5)
+KVQ_F32, KVQ_BF16 = 0, 1
+KVQ_ROT_NONE, KVQ_ROT_WHT = 0, 1
+
+EXPORTED = [
+    "kvq_cache_sizes",
+    "kvq_quantize_append",
+    "kvq_decode_workspace_bytes",
+    "kvq_decode_attention",
+    "kvq_dequantize_debug",
+    "kvq_status_str",
+]
+
+
+class kvq_params(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", c_int32),
+        ("num_q_heads", c_int32),
+        ("num_kv_heads", c_int32),
+        ("k_bits", c_int32),
+        ("k_group", c_int32),
+        ("v_bits", c_int32),
+        ("v_group", c_int32),
+        ("window", c_int32),
+        ("key_rotation", c_int32),
+        ("kv_dtype", c_int32),
+        ("block_size", c_int32),
+    ]
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [
+        ("pages", c_void_p),
+        ("k_win", c_void_p),
+        ("v_win", c_void_p),
+        ("block_table", c_void_p),
+        ("batch", c_int32),
+        ("max_blocks_per_seq", c_int32),
+        ("capacity", c_int64),
+    ]
+
+
+class kvq_sizes(ctypes.Structure):
+    _fields_ = [("record_bytes", c_size_t), ("pages_bytes", c_size_t), ("window_bytes", c_size_t)]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kvq_status_str(status)} (status {status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m mixed_precision_kv_kvq_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path."
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    P = POINTER
+    lib.kvq_cache_sizes.argtypes = [P(kvq_params), c_int32, c_int64, P(kvq_sizes)]
+    lib.kvq_cache_sizes.restype = c_int32
+    lib.kvq_quantize_append.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                        c_void_p]
+    lib.kvq_quantize_append.restype = c_int32
+    lib.kvq_decode_workspace_bytes.argtypes = [P(kvq_params), c_int32, c_int64]
+    lib.kvq_decode_workspace_bytes.restype = c_size_t
+    lib.kvq_decode_attention.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_int32, c_void_p,
+                                         c_int32, c_float, c_void_p, c_size_t, c_void_p]
+    lib.kvq_decode_attention.restype = c_int32
+    lib.kvq_dequantize_debug.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int32, c_int64, c_int64, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.kvq_dequantize_debug.restype = c_int32
+    lib.kvq_status_str.argtypes = [c_int32]
+    lib.kvq_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st, where):
+    if st != KVQ_OK:
+        raise KvqError(st, where)
+
+
+def kvq_status_str(status: int) -> str:
+    return _lib.kvq_status_str(int(status)).decode()
+
+
+def kvq_cache_sizes(params: kvq_params, batch: int, capacity: int) -> kvq_sizes:
+    out = kvq_sizes()
+    _check(_lib.kvq_cache_sizes(ctypes.byref(params), batch, capacity, ctypes.byref(out)), "kvq_cache_sizes")
+    return out
+
+
+def kvq_quantize_append(params, cache, seq_lens_before, n_new_per_seq, k_new, v_new, n_new, stream=None, check=True):
+    st = _lib.kvq_quantize_append(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens_before),
+                                  _ptr(n_new_per_seq), _ptr(k_new), _ptr(v_new), int(n_new), _stream(stream))
+    if check:
+        _check(st, "kvq_quantize_append")
+    return st
+
+
+def kvq_decode_workspace_bytes(params, batch: int, max_seq_len: int) -> int:
+    return int(_lib.kvq_decode_workspace_bytes(ctypes.byref(params), batch, max_seq_len))
+
+
+def kvq_decode_attention(params, cache, seq_lens, max_seq_len, q, q_dtype, out, out_dtype, softmax_scale, workspace,
+                         workspace_bytes, stream=None, check=True):
+    st = _lib.kvq_decode_attention(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens), int(max_seq_len),
+                                   _ptr(q), int(q_dtype), _ptr(out), int(out_dtype), float(softmax_scale),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "kvq_decode_attention")
+    return st
+
+
+def kvq_dequantize_debug(params, cache, seq_lens, seq, t0, n, k_codes=None, v_codes=None, k_meta=None, v_meta=None,
+                         k_hat=None, v_hat=None, stream=None, check=True):
+    st = _lib.kvq_dequantize_debug(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens), int(seq), int(t0),
+                                   int(n), _ptr(k_codes), _ptr(v_codes), _ptr(k_meta), _ptr(v_meta), _ptr(k_hat),
+                                   _ptr(v_hat), _stream(stream))
+    if check:
+        _check(st, "kvq_dequantize_debug")
+    return st
+
+
+# --------------------------------------------------------------------------
+# Plumbing: device buffers for one cache, allocated with torch.
+# --------------------------------------------------------------------------
+def make_params(head_dim=128, num_q_heads=32, num_kv_heads=8, k_bits=4, k_group=32, v_bits=2, v_group=128, window=0,
+                key_rotation=0, kv_dtype=KVQ_BF16, block_size=0) -> kvq_params:
+    return kvq_params(head_dim, num_q_heads, num_kv_heads, k_bits, k_group, v_bits, v_group, window, key_rotation,
+                      kv_dtype, block_size)
+
+
+class CacheBuffers:
+    """Torch-owned device buffers of one cache and the matching kvq_cache struct."""
+
+    def __init__(self, params: kvq_params, batch: int, capacity: int, block_table=None, device="cuda"):
+        import torch
+
+        sizes = kvq_cache_sizes(params, batch, capacity)
+        self.params = params
+        self.sizes = sizes
+        self.pages = torch.empty(max(int(sizes.pages_bytes), 16), dtype=torch.uint8, device=device)
+        if params.window > 0:
+            self.k_win = torch.empty(int(sizes.window_bytes), dtype=torch.uint8, device=device)
+            self.v_win = torch.empty(int(sizes.window_bytes), dtype=torch.uint8, device=device)
+        else:
+            self.k_win = self.v_win = None
+        self.block_table = block_table
+        mbps = int(block_table.shape[1]) if block_table is not None else 0
+        self.struct = kvq_cache(_ptr(self.pages), _ptr(self.k_win), _ptr(self.v_win), _ptr(block_table), batch, mbps,
+                                capacity)

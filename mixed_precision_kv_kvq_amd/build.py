@@ -1,0 +1,100 @@
+"""Build the HIP libraries in-tree with hipcc for gfx950.
+
+* mixed_precision_kv_kvq_amd/libkvq.so — the quantized-KV attention library (C ABI in include/kvq.h)
+* workloads/libkvqgen.so                — the device-side input generator (include/kvq_gen.h)
+
+Usage:  python -m mixed_precision_kv_kvq_amd.build [--force] [--jobs N]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
+
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    # no packed-fp32 VALU instructions anywhere
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+LIB = os.path.join(PKG, "libkvq.so")
+GEN_LIB = os.path.join(ROOT, "workloads", "libkvqgen.so")
+BUILD_DIR = os.path.join(PKG, "_build")
+
+
+def _sources():
+    csrc = os.path.join(PKG, "csrc")
+    srcs = sorted(glob.glob(os.path.join(csrc, "*.hip"))) + sorted(glob.glob(os.path.join(csrc, "inst", "*.hip")))
+    srcs.append(os.path.join(csrc, "kvq_api.cpp"))
+    headers = sorted(glob.glob(os.path.join(csrc, "*.h"))) + [os.path.join(ROOT, "include", "kvq.h")]
+    return srcs, headers
+
+
+def _obj_path(src):
+    rel = os.path.relpath(src, os.path.join(PKG, "csrc")).replace(os.sep, "_")
+    return os.path.join(BUILD_DIR, rel + ".o")
+
+
+def _run(cmd):
+    t0 = time.time()
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature; drop that harmless note.
+    out = "\n".join(l for l in p.stdout.splitlines() if "packed-fp32-ops" not in l)
+    return p.returncode, out, time.time() - t0
+
+
+def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> None:
+    """Compile every HIP source for gfx950 and link the shared libraries."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs, headers = _sources()
+    newest_header = max(os.path.getmtime(h) for h in headers)
+    todo = []
+    for s in srcs:
+        o = _obj_path(s)
+        if force or not os.path.exists(o) or os.path.getmtime(o) < max(os.path.getmtime(s), newest_header):
+            todo.append((s, o))
+    jobs = jobs or min(16, os.cpu_count() or 4)
+    errors = []
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = {ex.submit(_run, [HIPCC, *COMMON, "-c", s, "-o", o]): s for s, o in todo}
+        for f in cf.as_completed(futs):
+            rc, out, dt = f.result()
+            if verbose or rc:
+                print(f"[build] {os.path.basename(futs[f])} rc={rc} {dt:.1f}s\n{out}", file=sys.stderr)
+            if rc:
+                errors.append(futs[f])
+    if errors:
+        raise RuntimeError(f"hipcc failed for: {errors}")
+    objs = [_obj_path(s) for s in srcs]
+    if force or todo or not os.path.exists(LIB):
+        rc, out, _ = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs])
+        if rc:
+            raise RuntimeError(f"link failed:\n{out}")
+        os.replace(LIB + ".tmp", LIB)
+    gen_src = os.path.join(ROOT, "workloads", "gen.hip")
+    if force or not os.path.exists(GEN_LIB) or os.path.getmtime(GEN_LIB) < os.path.getmtime(gen_src):
+        rc, out, _ = _run([HIPCC, *COMMON, "-shared", "-o", GEN_LIB + ".tmp", gen_src])
+        if rc:
+            raise RuntimeError(f"generator build failed:\n{out}")
+        os.replace(GEN_LIB + ".tmp", GEN_LIB)
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--force", action="store_true")
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args()
+    t = time.time()
+    build(force=a.force, jobs=a.jobs, verbose=a.verbose)
+    print(f"built {LIB} and {GEN_LIB} in {time.time() - t:.1f}s")

@@ -1,0 +1,216 @@
+// C-ABI front end: host-side validation, sizing and launch.
+#include <math.h>
+#include <stdlib.h>
+
+#include "kvq_internal.h"
+
+namespace {
+
+constexpr int kTargetWaves = 4096;  // 256 CUs x 16 resident waves
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool is_pow2_bits(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+
+kvq_status check_params(const kvq_params *p) {
+  if (!p) return KVQ_EINVAL;
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads) return KVQ_EINVAL;
+  if (p->window < 0 || p->key_rotation < 0 || p->key_rotation > 1) return KVQ_EINVAL;
+  if (p->kv_dtype != KVQ_F32 && p->kv_dtype != KVQ_BF16) return KVQ_EINVAL;
+  if (p->head_dim != KVQ_D) return KVQ_EUNSUPPORTED;
+  const int g = p->num_q_heads / p->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_EUNSUPPORTED;
+  if (!is_pow2_bits(p->k_bits) || !is_pow2_bits(p->v_bits)) return KVQ_EUNSUPPORTED;
+  if (p->k_group != 32 && p->k_group != 64 && p->k_group != 128) return KVQ_EUNSUPPORTED;
+  if (p->v_group != 64 && p->v_group != 128) return KVQ_EUNSUPPORTED;
+  if (p->block_size != 0 && p->block_size != KVQ_PAGE) return KVQ_EUNSUPPORTED;
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_params *p, const kvq_cache *c) {
+  if (!c || c->batch <= 0 || c->capacity <= 0) return KVQ_EINVAL;
+  if (!c->pages || !aligned16(c->pages)) return KVQ_EINVAL;
+  if (p->window > 0) {
+    if (!c->k_win || !c->v_win || !aligned16(c->k_win) || !aligned16(c->v_win)) return KVQ_EINVAL;
+  }
+  if (p->block_size) {
+    if (!c->block_table || ((uintptr_t)c->block_table & 3u) || c->max_blocks_per_seq <= 0) return KVQ_EINVAL;
+  }
+  return KVQ_OK;
+}
+
+KvqCacheDev dev_cache(const kvq_params *p, const kvq_cache *c) {
+  KvqCacheDev d;
+  d.pages = (uint8_t *)c->pages;
+  d.k_win = (uint8_t *)c->k_win;
+  d.v_win = (uint8_t *)c->v_win;
+  d.block_table = c->block_table;
+  d.batch = c->batch;
+  d.mbps = c->max_blocks_per_seq;
+  d.paged = p->block_size != 0;
+  d.pages_per_seq = d.paged ? 0 : (c->capacity + KVQ_PAGE - 1) / KVQ_PAGE;
+  d.pool_pages = d.paged ? c->capacity : 0;
+  return d;
+}
+
+KvqLayout layout_of(const kvq_params *p) { return kvq_make_layout(p->k_bits, p->k_group, p->v_bits, p->v_group); }
+
+// Virtual pages of a sequence of length L: quantized pages, then window pages.
+int64_t virtual_pages(int64_t L, int R) {
+  const int64_t nq = L > R ? L - R : 0;
+  const int64_t nw = L < R ? L : R;
+  return (nq + KVQ_PAGE - 1) / KVQ_PAGE + (nw + KVQ_PAGE - 1) / KVQ_PAGE;
+}
+
+void split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, int *splits, int *pps) {
+  const int64_t vp = virtual_pages(max_seq_len, p->window);
+  int64_t per = 0;
+  if (const char *env = getenv("KVQ_PAGES_PER_SPLIT")) per = atoll(env);
+  if (per <= 0) {
+    const int64_t total = (int64_t)batch * p->num_kv_heads * (vp > 0 ? vp : 1);
+    per = (total + kTargetWaves - 1) / kTargetWaves;
+  }
+  if (per < 2) per = 2;
+  per = (per + 1) & ~int64_t(1);
+  int64_t s = (vp + per - 1) / per;
+  if (s < 1) s = 1;
+  *splits = (int)s;
+  *pps = (int)per;
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_cache_sizes(const kvq_params *params, int32_t batch, int64_t capacity, kvq_sizes *out) {
+  if (kvq_status st = check_params(params)) return st;
+  if (!out || batch <= 0 || capacity <= 0) return KVQ_EINVAL;
+  const KvqLayout lay = layout_of(params);
+  out->record_bytes = (size_t)lay.record;
+  const size_t pages = params->block_size ? (size_t)capacity
+                                          : (size_t)batch * ((capacity + KVQ_PAGE - 1) / KVQ_PAGE);
+  out->pages_bytes = pages * params->num_kv_heads * (size_t)lay.record;
+  out->window_bytes = (size_t)batch * params->num_kv_heads * (size_t)params->window * KVQ_D *
+                      (params->kv_dtype == KVQ_F32 ? 4 : 2);
+  return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens_before,
+                               const int32_t *n_new_per_seq, const void *k_new, const void *v_new, int32_t n_new,
+                               hipStream_t stream) {
+  if (kvq_status st = check_params(params)) return st;
+  if (kvq_status st = check_cache(params, cache)) return st;
+  if (!seq_lens_before || n_new < 0) return KVQ_EINVAL;
+  if (n_new == 0) return KVQ_OK;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return KVQ_EINVAL;
+  KvqAppendArgs a;
+  a.lay = layout_of(params);
+  a.cache = dev_cache(params, cache);
+  a.seq_lens_before = seq_lens_before;
+  a.n_new_per_seq = n_new_per_seq;
+  a.k_new = (const uint8_t *)k_new;
+  a.v_new = (const uint8_t *)v_new;
+  a.n_new = n_new;
+  a.Hkv = params->num_kv_heads;
+  a.R = params->window;
+  a.rotation = params->key_rotation;
+  a.kv_f32 = params->kv_dtype == KVQ_F32;
+  return hip_status(kvq_launch_append(a, stream));
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len) {
+  if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0) return 0;
+  int splits, pps;
+  split_plan(params, batch, max_seq_len, &splits, &pps);
+  return (size_t)batch * params->num_q_heads * (size_t)splits * KVQ_PART_STRIDE * sizeof(float);
+}
+
+kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                                int64_t max_seq_len, const void *q, int32_t q_dtype, void *out, int32_t out_dtype,
+                                float softmax_scale, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (kvq_status st = check_params(params)) return st;
+  if (kvq_status st = check_cache(params, cache)) return st;
+  if (!seq_lens || !q || !out || !workspace || max_seq_len < 0) return KVQ_EINVAL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EINVAL;
+  if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
+    return KVQ_EINVAL;
+  if (!(softmax_scale >= 0.f) || isinf(softmax_scale)) return KVQ_EINVAL;
+  const int64_t nq_max = max_seq_len > params->window ? max_seq_len - params->window : 0;
+  if (params->block_size) {
+    if ((nq_max + KVQ_PAGE - 1) / KVQ_PAGE > cache->max_blocks_per_seq) return KVQ_ENOSPACE;
+  } else if (nq_max > cache->capacity) {
+    return KVQ_ENOSPACE;
+  }
+  if (workspace_bytes < kvq_decode_workspace_bytes(params, cache->batch, max_seq_len)) return KVQ_ENOSPACE;
+
+  KvqAttnArgs a;
+  a.lay = layout_of(params);
+  a.cache = dev_cache(params, cache);
+  a.seq_lens = seq_lens;
+  a.q = q;
+  a.partials = (float *)workspace;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.kv_f32 = params->kv_dtype == KVQ_F32;
+  a.Hq = params->num_q_heads;
+  a.Hkv = params->num_kv_heads;
+  a.R = params->window;
+  a.rotation = params->key_rotation;
+  split_plan(params, cache->batch, max_seq_len, &a.splits, &a.pages_per_split);
+  a.max_len = (int32_t)(max_seq_len < INT32_MAX ? max_seq_len : INT32_MAX);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
+  a.sigma_u = (float)((double)scale * 1.4426950408889634 * 8589934592.0);  // * log2(e) * 2^33
+  const int g = params->num_q_heads / params->num_kv_heads;
+  const int q_parts = (q_dtype == KVQ_BF16 && !params->key_rotation) ? 1 : 2;
+  hipError_t e = kvq_launch_attention(a, g, q_parts, stream);
+  if (e != hipSuccess) return KVQ_EHIP;
+  KvqCombineArgs c;
+  c.partials = a.partials;
+  c.out = out;
+  c.out_f32 = out_dtype == KVQ_F32;
+  c.B = cache->batch;
+  c.Hq = params->num_q_heads;
+  c.splits = a.splits;
+  return hip_status(kvq_launch_combine(c, stream));
+}
+
+kvq_status kvq_dequantize_debug(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                                int32_t seq, int64_t t0, int64_t n, uint8_t *k_codes, uint8_t *v_codes,
+                                uint16_t *k_meta, uint16_t *v_meta, float *k_hat, float *v_hat,
+                                hipStream_t stream) {
+  if (kvq_status st = check_params(params)) return st;
+  if (kvq_status st = check_cache(params, cache)) return st;
+  if (!seq_lens || seq < 0 || seq >= cache->batch || t0 < 0 || n < 0) return KVQ_EINVAL;
+  if (n == 0) return KVQ_OK;
+  KvqDebugArgs a;
+  a.lay = layout_of(params);
+  a.cache = dev_cache(params, cache);
+  a.seq_lens = seq_lens;
+  a.seq = seq;
+  a.Hkv = params->num_kv_heads;
+  a.R = params->window;
+  a.kv_f32 = params->kv_dtype == KVQ_F32;
+  a.t0 = t0;
+  a.n = n;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_meta = k_meta;
+  a.v_meta = v_meta;
+  a.k_hat = k_hat;
+  a.v_hat = v_hat;
+  return hip_status(kvq_launch_debug(a, stream));
+}
+
+const char *kvq_status_str(kvq_status status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument (null or misaligned pointer, inconsistent shapes)";
+    case KVQ_EUNSUPPORTED: return "unsupported parameter";
+    case KVQ_ENOSPACE: return "workspace too small or length beyond the cache capacity";
+    case KVQ_EHIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

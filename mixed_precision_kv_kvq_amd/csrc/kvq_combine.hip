@@ -1,0 +1,91 @@
+// Cross-split combine of flash-decoding partials and dispatch of the split kernel.
+//
+// Each split s of a (sequence, query head) holds its own max m_s (log2 units),
+// sum l_s of 2^(score - m_s) and unnormalized output acc_s.  With M = max m_s the
+// softmax of nalar.dev "Kuantisasi KV cache mengganggu attention melalui key dan
+// value tersimpan", section "Error pada key masuk sebelum softmax", is
+//   o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+#include "kvq_internal.h"
+
+namespace kvq_attn {
+hipError_t launch_k1v1(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k1v2(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k1v4(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k1v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k2v1(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k2v2(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k2v4(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k2v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k4v1(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k4v2(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k4v4(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k4v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k8v1(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k8v2(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k8v4(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+hipError_t launch_k8v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+}  // namespace kvq_attn
+
+namespace {
+
+__global__ __launch_bounds__(64) void kvq_combine_kernel(KvqCombineArgs a) {
+  const int lane = threadIdx.x;
+  const size_t bh = blockIdx.x;
+  const float *base = a.partials + bh * (size_t)a.splits * KVQ_PART_STRIDE;
+  const float ninf = -__builtin_inff();
+  float M = ninf;
+  for (int s = 0; s < a.splits; ++s) M = __builtin_fmaxf(M, base[(size_t)s * KVQ_PART_STRIDE]);
+  float o0 = 0.f, o1 = 0.f;
+  if (M != ninf) {
+    float l = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      const float *ps = base + (size_t)s * KVQ_PART_STRIDE;
+      const float ms = ps[0];
+      if (ms == ninf) continue;
+      const float w = __builtin_amdgcn_exp2f(ms - M);
+      l = __builtin_fmaf(ps[1], w, l);
+      const float2 acc = reinterpret_cast<const float2 *>(ps + 4)[lane];
+      o0 = __builtin_fmaf(acc.x, w, o0);
+      o1 = __builtin_fmaf(acc.y, w, o1);
+    }
+    o0 = o0 / l;
+    o1 = o1 / l;
+  }
+  if (a.out_f32) {
+    reinterpret_cast<float2 *>(a.out)[bh * 64 + lane] = make_float2(o0, o1);
+  } else {
+    reinterpret_cast<uint32_t *>(a.out)[bh * 64 + lane] = kvq_f32_to_bf16_rne(o0) | (kvq_f32_to_bf16_rne(o1) << 16);
+  }
+}
+
+}  // namespace
+
+hipError_t kvq_launch_combine(const KvqCombineArgs &a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kvq_combine_kernel, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t kvq_launch_attention(const KvqAttnArgs &a, int g, int q_parts, hipStream_t s) {
+  if (a.cache.batch <= 0) return hipSuccess;
+  const int nvg = a.lay.nvg;
+  switch (a.lay.kb * 16 + a.lay.vb) {
+    case 17: return kvq_attn::launch_k1v1(a, g, q_parts, nvg, s);
+    case 18: return kvq_attn::launch_k1v2(a, g, q_parts, nvg, s);
+    case 20: return kvq_attn::launch_k1v4(a, g, q_parts, nvg, s);
+    case 24: return kvq_attn::launch_k1v8(a, g, q_parts, nvg, s);
+    case 33: return kvq_attn::launch_k2v1(a, g, q_parts, nvg, s);
+    case 34: return kvq_attn::launch_k2v2(a, g, q_parts, nvg, s);
+    case 36: return kvq_attn::launch_k2v4(a, g, q_parts, nvg, s);
+    case 40: return kvq_attn::launch_k2v8(a, g, q_parts, nvg, s);
+    case 65: return kvq_attn::launch_k4v1(a, g, q_parts, nvg, s);
+    case 66: return kvq_attn::launch_k4v2(a, g, q_parts, nvg, s);
+    case 68: return kvq_attn::launch_k4v4(a, g, q_parts, nvg, s);
+    case 72: return kvq_attn::launch_k4v8(a, g, q_parts, nvg, s);
+    case 129: return kvq_attn::launch_k8v1(a, g, q_parts, nvg, s);
+    case 130: return kvq_attn::launch_k8v2(a, g, q_parts, nvg, s);
+    case 132: return kvq_attn::launch_k8v4(a, g, q_parts, nvg, s);
+    case 136: return kvq_attn::launch_k8v8(a, g, q_parts, nvg, s);
+  }
+  return hipErrorInvalidValue;
+}

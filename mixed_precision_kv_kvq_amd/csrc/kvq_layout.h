@@ -1,0 +1,156 @@
+// Page-record layout of the quantized KV store and small numeric helpers.
+//
+// One page holds 16 consecutive tokens of one kv head:
+//   [K codes 256*kb B][K meta 64*nkg B][V codes 256*vb B][V meta 64*nvg B]
+// Everything inside a record is ordered so that each lane of a 64-wide wave
+// fetches, with one 16-byte (or smaller) load, exactly the operand bits that
+// the gfx950 16x16x32 bf16 MFMA expects in that lane:
+//   A operand of v_mfma_f32_16x16x32_bf16: lane l holds row l%16, k = 8*(l/16) + e (e = 0..7)
+//   B operand:                              lane l holds col l%16, k = 8*(l/16) + e
+//   D (4 x fp32):                          lane l holds col l%16, rows 4*(l/16) + r (r = 0..3)
+//
+// K codes: lane-slot l = 16*j + n (token n of the page, channel octet j).  The
+//   slot has kb 32-bit words holding, for the four 32-channel chunks kc, the
+//   channels 32*kc + 8*j + e.  Channel e = 2*i + h of chunk kc has index
+//   u = 4*kc + i; it sits in word u / (16/kb) at bit 16*h + kb*(u % (16/kb)).
+//   So (word >> kb*s) & mask(kb, both halves) is one bf16 pair of codes.
+// K meta: entry (token 4*jj + r, group g) at dword ((jj*nkg + g)*4 + r):
+//   low half = fp16 scale, high half = fp16 zero.
+// V codes: lane-slot l = 16*jj + c16 (channels c16 + 16*m, m = 0..7; tokens
+//   4*jj + r, r = 0..3).  The slot has vb words.  Token r = 2*i + h, tile m:
+//   position p = i*8*vb + m*vb in the half-word stream h, i.e. word p / 16,
+//   bit 16*h + p % 16.  A token's bits in one slot never share a byte with
+//   another token's, so tokens of a page can be written concurrently.
+// V meta: entry (token 4*jj + r, group g) at dword ((jj*nvg + g)*4 + r).
+//
+// A code c read as a bf16 bit pattern is the value c * 2^-133 for every c in
+// 0..255 (subnormal below 128, continuing into the first normal binade), so
+// masking the packed word gives exact, offset-free MFMA operands.
+#pragma once
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#define KVQ_PAGE 16
+#define KVQ_D 128
+
+struct KvqLayout {
+  int kb, kg, vb, vg;
+  int nkg, nvg;
+  int k_codes_off, k_meta_off, v_codes_off, v_meta_off, record;
+};
+
+__host__ __device__ inline KvqLayout kvq_make_layout(int kb, int kg, int vb, int vg) {
+  KvqLayout L;
+  L.kb = kb;
+  L.kg = kg;
+  L.vb = vb;
+  L.vg = vg;
+  L.nkg = KVQ_D / kg;
+  L.nvg = KVQ_D / vg;
+  L.k_codes_off = 0;
+  L.k_meta_off = 256 * kb;
+  L.v_codes_off = L.k_meta_off + 64 * L.nkg;
+  L.v_meta_off = L.v_codes_off + 256 * vb;
+  L.record = L.v_meta_off + 64 * L.nvg;
+  return L;
+}
+
+// Byte offset (within the record) and bit of the K code of (token n, channel ch).
+__host__ __device__ inline void kvq_k_code_pos(int kb, int n, int ch, int *byte_off, int *bit) {
+  const int kc = ch >> 5, w = ch & 31, j = w >> 3, e = w & 7;
+  const int i = e >> 1, h = e & 1;
+  const int u = 4 * kc + i, per = 16 / kb;
+  const int word = u / per, s = u % per;
+  *byte_off = (16 * j + n) * 4 * kb + 4 * word;
+  *bit = 16 * h + kb * s;
+}
+
+// Byte offset (within the V-code area) and bit of the V code of (token tt, channel ch).
+__host__ __device__ inline void kvq_v_code_pos(int vb, int tt, int ch, int *byte_off, int *bit) {
+  const int jj = tt >> 2, r = tt & 3, i = r >> 1, h = r & 1;
+  const int m = ch >> 4, c16 = ch & 15;
+  const int p = i * 8 * vb + m * vb;
+  *byte_off = (16 * jj + c16) * 4 * vb + 4 * (p >> 4);
+  *bit = 16 * h + (p & 15);
+}
+
+__host__ __device__ inline int kvq_meta_dword(int ngroups, int tt, int grp) {
+  return ((tt >> 2) * ngroups + grp) * 4 + (tt & 3);
+}
+
+// Record index of (sequence b, kv head h, logical page p).  Callers keep p below
+// pages_per_seq (contiguous) or mbps (paged); a block-table entry outside
+// [0, pool_pages) is clamped so that a bad table cannot address memory outside
+// the pool.
+__host__ __device__ inline int64_t kvq_record_index(int paged, const int32_t *block_table, int mbps,
+                                                    int64_t pages_per_seq, int64_t pool_pages, int Hkv, int b, int h,
+                                                    int64_t p) {
+  if (paged) {
+    int64_t e = block_table[(int64_t)b * mbps + p];
+    e = e < 0 ? 0 : (e >= pool_pages ? pool_pages - 1 : e);
+    return e * Hkv + h;
+  }
+  return ((int64_t)b * Hkv + h) * pages_per_seq + p;
+}
+
+// ---------------------------------------------------------------------------
+// fp16 directed rounding of fp64 values, by bit manipulation (finite |x| < 65504).
+// ---------------------------------------------------------------------------
+// Largest fp16 <= a for a >= 0; *exact tells whether a is itself an fp16 value.
+__device__ inline uint32_t kvq_f16_trunc_pos(double a, bool *exact) {
+  if (a == 0.0) {
+    *exact = true;
+    return 0u;
+  }
+  if (a < 6.103515625e-05) {  // below 2^-14: subnormal fp16 m * 2^-24
+    const double y = a * 16777216.0;
+    const double fl = __builtin_floor(y);
+    *exact = (fl == y);
+    return (uint32_t)fl;
+  }
+  const uint64_t u = (uint64_t)__builtin_bit_cast(uint64_t, a);
+  const int e = (int)((u >> 52) & 0x7FF) - 1023;
+  const uint64_t man = u & 0xFFFFFFFFFFFFFull;
+  *exact = (man & ((1ull << 42) - 1)) == 0;
+  return ((uint32_t)(e + 15) << 10) | (uint32_t)(man >> 42);
+}
+
+__device__ inline uint32_t kvq_f16_round_down(double x) {
+  if (x >= 0.0) {
+    bool ex;
+    return kvq_f16_trunc_pos(x, &ex);
+  }
+  bool ex;
+  const uint32_t t = kvq_f16_trunc_pos(-x, &ex);
+  return 0x8000u | (ex ? t : t + 1u);
+}
+
+__device__ inline uint32_t kvq_f16_round_up(double x) {
+  if (x >= 0.0) {
+    bool ex;
+    const uint32_t t = kvq_f16_trunc_pos(x, &ex);
+    return ex ? t : t + 1u;
+  }
+  bool ex;
+  return 0x8000u | kvq_f16_trunc_pos(-x, &ex);
+}
+
+__host__ __device__ inline double kvq_f16_bits_to_f64(uint32_t h) {
+  const uint32_t s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = (double)m * 5.9604644775390625e-08;  // 2^-24
+  else
+    v = (double)(1024 + m) * __builtin_ldexp(1.0, (int)e - 25);
+  return s ? -v : v;
+}
+
+__host__ __device__ inline float kvq_bf16_bits_to_f32(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+
+__host__ __device__ inline uint32_t kvq_f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}

@@ -1,0 +1,155 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+headers declare, and rejects bad arguments before launching anything (these
+calls never reach the GPU, so they run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+K = pytest.importorskip("mixed_precision_kv_kvq_amd")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first or no launch happens
+
+
+def declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    return sorted(set(re.findall(r"^\s*(?:kvq_status|size_t|const char \*|int)\s*\*?\s*(kvq_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared("kvq.h")
+    assert set(names) == set(K.EXPORTED)
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_generator_exports():
+    names = declared("kvq_gen.h")
+    assert names == ["kvq_gen_kv", "kvq_gen_q"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "workloads", "libkvqgen.so"))
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def p(**kw):
+    base = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, k_bits=4, k_group=32, v_bits=2, v_group=128, window=0,
+                key_rotation=0, kv_dtype=K.KVQ_BF16, block_size=0)
+    base.update(kw)
+    return K.make_params(**base)
+
+
+@pytest.mark.parametrize("kb,vb,expect", [(4, 2, 116), (4, 4, 148), (2, 4, 116), (2, 2, 84), (1, 2, 68)])
+def test_record_size_matches_memory_model(kb, vb, expect):
+    s = K.kvq_cache_sizes(p(k_bits=kb, v_bits=vb), 2, 100)
+    assert s.record_bytes == 16 * expect == 16 * O.bytes_per_token_head(128, kb, 32, vb, 128)
+    assert s.pages_bytes == 2 * 7 * 8 * s.record_bytes  # ceil(100/16) pages per sequence
+    assert s.window_bytes == 0
+
+
+def test_window_and_paged_sizes():
+    s = K.kvq_cache_sizes(p(window=128), 16, 32832)
+    assert s.window_bytes == 16 * 8 * 128 * 128 * 2
+    s = K.kvq_cache_sizes(p(block_size=16), 8, 5000)
+    assert s.pages_bytes == 5000 * 8 * s.record_bytes
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), K.KVQ_EUNSUPPORTED),
+    (dict(k_bits=3), K.KVQ_EUNSUPPORTED),
+    (dict(v_bits=0), K.KVQ_EUNSUPPORTED),
+    (dict(k_group=16), K.KVQ_EUNSUPPORTED),
+    (dict(v_group=32), K.KVQ_EUNSUPPORTED),
+    (dict(num_q_heads=48, num_kv_heads=8), K.KVQ_EUNSUPPORTED),
+    (dict(num_q_heads=30, num_kv_heads=8), K.KVQ_EINVAL),
+    (dict(window=-1), K.KVQ_EINVAL),
+    (dict(kv_dtype=7), K.KVQ_EINVAL),
+    (dict(block_size=32), K.KVQ_EUNSUPPORTED),
+    (dict(key_rotation=2), K.KVQ_EINVAL),
+])
+def test_bad_params_rejected(kw, status):
+    out = K.kvq_sizes()
+    assert K.lib().kvq_cache_sizes(ctypes.byref(p(**kw)), 1, 16, ctypes.byref(out)) == status
+
+
+def cache(**kw):
+    base = dict(pages=FAKE, k_win=None, v_win=None, block_table=None, batch=2, max_blocks_per_seq=0, capacity=64)
+    base.update(kw)
+    return K.kvq_cache(**base)
+
+
+def test_append_validation():
+    prm = p()
+    L = K.lib()
+    assert L.kvq_quantize_append(ctypes.byref(prm), ctypes.byref(cache()), None, None, FAKE, FAKE, 1, None) == K.KVQ_EINVAL
+    assert L.kvq_quantize_append(ctypes.byref(prm), ctypes.byref(cache(pages=FAKE + 4)), FAKE, None, FAKE, FAKE, 1,
+                                 None) == K.KVQ_EINVAL
+    assert L.kvq_quantize_append(ctypes.byref(prm), ctypes.byref(cache()), FAKE, None, FAKE + 2, FAKE, 1,
+                                 None) == K.KVQ_EINVAL
+    assert L.kvq_quantize_append(ctypes.byref(prm), ctypes.byref(cache()), FAKE, None, FAKE, FAKE, -1,
+                                 None) == K.KVQ_EINVAL
+    # window without ring buffers, paged without a block table
+    assert L.kvq_quantize_append(ctypes.byref(p(window=8)), ctypes.byref(cache()), FAKE, None, FAKE, FAKE, 1,
+                                 None) == K.KVQ_EINVAL
+    assert L.kvq_quantize_append(ctypes.byref(p(block_size=16)), ctypes.byref(cache()), FAKE, None, FAKE, FAKE, 1,
+                                 None) == K.KVQ_EINVAL
+    assert L.kvq_quantize_append(ctypes.byref(p(k_bits=5)), ctypes.byref(cache()), FAKE, None, FAKE, FAKE, 1,
+                                 None) == K.KVQ_EUNSUPPORTED
+    # zero tokens: nothing to do, no launch
+    assert L.kvq_quantize_append(ctypes.byref(prm), ctypes.byref(cache()), FAKE, None, None, None, 0, None) == K.KVQ_OK
+
+
+def test_attention_validation():
+    prm = p()
+    L = K.lib()
+    need = K.kvq_decode_workspace_bytes(prm, 2, 64)
+    assert need > 0
+
+    def call(c=None, seq=FAKE, mx=64, q=FAKE, qd=K.KVQ_BF16, out=FAKE, od=K.KVQ_F32, sc=0.0, ws=FAKE, wsb=need,
+             prm_=prm):
+        return L.kvq_decode_attention(ctypes.byref(prm_), ctypes.byref(c or cache()), seq, mx, q, qd, out, od, sc,
+                                      ws, wsb, None)
+
+    assert call(wsb=need - 1) == K.KVQ_ENOSPACE
+    assert call(mx=65) == K.KVQ_ENOSPACE  # beyond the capacity of 64 tokens
+    assert call(q=None) == K.KVQ_EINVAL
+    assert call(out=FAKE + 8) == K.KVQ_EINVAL
+    assert call(qd=5) == K.KVQ_EINVAL
+    assert call(sc=-1.0) == K.KVQ_EINVAL
+    assert call(sc=float("nan")) == K.KVQ_EINVAL
+    assert call(seq=None) == K.KVQ_EINVAL
+    assert call(prm_=p(head_dim=96)) == K.KVQ_EUNSUPPORTED
+    # paged: more pages than the table row holds
+    assert call(c=cache(block_table=FAKE, max_blocks_per_seq=3), prm_=p(block_size=16), mx=49,
+                wsb=K.kvq_decode_workspace_bytes(p(block_size=16), 2, 49)) == K.KVQ_ENOSPACE
+    assert K.kvq_decode_workspace_bytes(p(k_bits=3), 2, 64) == 0
+
+
+def test_debug_validation():
+    prm = p()
+    L = K.lib()
+    args = [None] * 6
+    assert L.kvq_dequantize_debug(ctypes.byref(prm), ctypes.byref(cache()), FAKE, 2, 0, 1, *args, None) == K.KVQ_EINVAL
+    assert L.kvq_dequantize_debug(ctypes.byref(prm), ctypes.byref(cache()), FAKE, 0, -1, 1, *args, None) == K.KVQ_EINVAL
+    assert L.kvq_dequantize_debug(ctypes.byref(prm), ctypes.byref(cache()), None, 0, 0, 1, *args, None) == K.KVQ_EINVAL
+    assert L.kvq_dequantize_debug(ctypes.byref(prm), ctypes.byref(cache()), FAKE, 0, 0, 0, *args, None) == K.KVQ_OK
+
+
+def test_status_strings():
+    for s in range(5):
+        assert K.kvq_status_str(s)
+    assert "unknown" in K.kvq_status_str(99)
+
+
+def test_workspace_grows_with_length_and_split_override(monkeypatch):
+    prm = p()
+    a = K.kvq_decode_workspace_bytes(prm, 16, 32768)
+    b = K.kvq_decode_workspace_bytes(prm, 16, 131072)
+    assert 0 < a <= b
+    monkeypatch.setenv("KVQ_PAGES_PER_SPLIT", "2")
+    c = K.kvq_decode_workspace_bytes(prm, 16, 32768)
+    assert c > a

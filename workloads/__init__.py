@@ -113,9 +113,9 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    context: int  # context length before the first decode step (fixed-length workloads)
+    context: int  # tokens in the cache before decoding (fixed-length workloads)
     window: int  # most recent tokens kept unquantized
-    steps: int  # decode steps (each appends one token, then attends)
+    steps: int  # decode steps that each append one token, then attend; 0 = one attention over the context
     kv_dtype: str  # "f32" or "bf16"
     q_dtype: str
     k_bits: int
@@ -216,7 +216,7 @@ class Workload:
 
 
 def _w(**kw) -> Workload:
-    base = dict(head_dim=128, steps=1, kv_dtype="bf16", q_dtype="bf16", k_bits=4, k_group=32, v_bits=2,
+    base = dict(head_dim=128, steps=0, kv_dtype="bf16", q_dtype="bf16", k_bits=4, k_group=32, v_bits=2,
                 v_group=128, rotation=False, block_size=0, key_outliers=3, key_outlier_mult=10.0,
                 key_lognormal_sigma=0.5, window=0)
     base.update(kw)

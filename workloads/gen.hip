@@ -1,0 +1,84 @@
+// Device-side implementation of the seeded input generator (see include/kvq_gen.h).
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../include/kvq_gen.h"
+
+namespace {
+
+__device__ inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__device__ inline float draw(uint64_t key, uint64_t idx, float sigma, const float *table) {
+  const uint64_t u = mix64(key + (idx + 1ull) * 0x9E3779B97F4A7C15ull);
+  return sigma * table[u >> 48];
+}
+
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__global__ void gen_kv_kernel(void *out, int out_f32, uint64_t key, const float *sigma, const float *table, int B,
+                              int n, int Hkv, int64_t t0, int d) {
+  const int64_t total = (int64_t)B * n * Hkv * d;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(e % d);
+    int64_t r = e / d;
+    const int h = (int)(r % Hkv);
+    r /= Hkv;
+    const int64_t i = r % n;
+    const int b = (int)(r / n);
+    const uint64_t idx = (((uint64_t)b * Hkv + h) * (1ull << 24) + (uint64_t)(t0 + i)) * d + c;
+    const float v = draw(key, idx, sigma[h * d + c], table);
+    if (out_f32)
+      reinterpret_cast<float *>(out)[e] = v;
+    else
+      reinterpret_cast<uint16_t *>(out)[e] = bf16_rne(v);
+  }
+}
+
+__global__ void gen_q_kernel(void *out, int out_f32, uint64_t key, const float *table, int B, int Hq, int d,
+                             int step) {
+  const int64_t total = (int64_t)B * Hq * d;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const uint64_t idx = (uint64_t)step * B * Hq * d + (uint64_t)e;
+    const float v = draw(key, idx, 1.0f, table);
+    if (out_f32)
+      reinterpret_cast<float *>(out)[e] = v;
+    else
+      reinterpret_cast<uint16_t *>(out)[e] = bf16_rne(v);
+  }
+}
+
+unsigned grid_for(int64_t total) {
+  int64_t g = (total + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+extern "C" int kvq_gen_kv(void *out, int out_f32, uint64_t key, const float *sigma, const float *table, int B, int n,
+                          int Hkv, int64_t t0, int d, hipStream_t stream) {
+  const int64_t total = (int64_t)B * n * Hkv * d;
+  if (total <= 0) return 0;
+  hipLaunchKernelGGL(gen_kv_kernel, dim3(grid_for(total)), dim3(256), 0, stream, out, out_f32, key, sigma, table, B,
+                     n, Hkv, t0, d);
+  return (int)hipGetLastError();
+}
+
+extern "C" int kvq_gen_q(void *out, int out_f32, uint64_t key, const float *table, int B, int Hq, int d, int step,
+                         hipStream_t stream) {
+  const int64_t total = (int64_t)B * Hq * d;
+  if (total <= 0) return 0;
+  hipLaunchKernelGGL(gen_q_kernel, dim3(grid_for(total)), dim3(256), 0, stream, out, out_f32, key, table, B, Hq, d,
+                     step);
+  return (int)hipGetLastError();
+}
