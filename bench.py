@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: append one new token
+per sequence (fused quantize + pack of the token leaving the recent window),
+then decode attention of every query head over its whole cache (split-K kernel
++ cross-split combine).  Workload: batch 16, 32 query / 8 kv heads, d = 128,
+32768-token context, 4-bit keys in groups of 32 and 2-bit values in groups of
+128 with fp16 scale/zero, the most recent 128 tokens kept in bf16, bf16 queries.
+
+Prints one JSON line (metric, value = microseconds per step, roofline of the
+attention kernels, oracle CPU baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "K4V2 decode-attention µs/step + achieved HBM GB/s (% of peak), 32k ctx"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_b16_L32k.json")
+
+
+def attn_bytes(wl, L, per_token_head, win_elem_bytes):
+    """Algorithmic bytes of one attention call with all sequences at length L."""
+    nq = max(0, L - wl.window)
+    nw = min(L, wl.window)
+    units = wl.batch * wl.num_kv_heads
+    cache = units * (nq * per_token_head + nw * 2 * wl.head_dim * win_elem_bytes)
+    qo = wl.batch * wl.num_q_heads * wl.head_dim * (2 + 4)  # bf16 query in, fp32 output
+    return cache + qo
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixed_precision_kv_kvq_amd", "csrc")
+    for name in ("kvq_attn_impl.h", "kvq_layout.h", "kvq_combine.hip", "kvq_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, target_seconds=12.0, max_units=None):
+    """The CPU oracle timed on one decode step of a sample of (sequence, kv head) units.
+
+    Per unit the oracle does what a decode step needs given its stored cache:
+    quantize the token leaving the window, dequantize the stored codes, and run
+    attention for the unit's query heads.  Building the stored cache is untimed.
+    """
+    import numpy as np
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    import oracle as O
+    import workloads as W
+
+    L = wl.context + 1
+    prm = dict(k_bits=wl.k_bits, k_group=wl.k_group, v_bits=wl.v_bits, v_group=wl.v_group, window=wl.window,
+               rotation=wl.rotation)
+    units = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+    q = wl.q_f32(0).astype(np.float64)
+    g = wl.group_q
+    scale = 1.0 / np.sqrt(wl.head_dim)
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    elapsed = 0.0
+    done = 0
+    try:
+        for b, kvh in units[: max_units or len(units)]:
+            Kx = wl.kv_f32(W.TENSOR_K, b, kvh, 0, L).astype(np.float64)
+            Vx = wl.kv_f32(W.TENSOR_V, b, kvh, 0, L).astype(np.float64)
+            stored = O.build_unit_cache(Kx, Vx, L - 1, prm)  # cache before the step (untimed)
+            t0 = time.perf_counter()
+            nq = max(0, L - wl.window)
+            ev = nq - 1  # the token that leaves the window in this step
+            kc, ks, kz = O.quantize(Kx[ev:ev + 1], wl.k_bits, wl.k_group)
+            vc, vs, vz = O.quantize(Vx[ev:ev + 1], wl.v_bits, wl.v_group)
+            k_codes = np.concatenate([stored["k_codes"], kc])
+            k_scale = np.concatenate([stored["k_scale"], ks])
+            k_zero = np.concatenate([stored["k_zero"], kz])
+            v_codes = np.concatenate([stored["v_codes"], vc])
+            v_scale = np.concatenate([stored["v_scale"], vs])
+            v_zero = np.concatenate([stored["v_zero"], vz])
+            cache = dict(k_hat=O.dequantize(k_codes, k_scale, k_zero, wl.k_group),
+                         v_hat=O.dequantize(v_codes, v_scale, v_zero, wl.v_group),
+                         k_win=Kx[nq:L], v_win=Vx[nq:L])
+            for h in range(kvh * g, (kvh + 1) * g):
+                O.unit_attention(q[b, h], cache, scale, wl.rotation)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            if elapsed >= target_seconds:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    per_step_us = elapsed / done * len(units) * 1e6
+    return {
+        "value": round(per_step_us, 1),
+        "unit": "µs/step",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {len(units)} (sequence, kv head) units of one decode step at L={L}, "
+                  f"{elapsed:.1f} s of CPU time, scaled to the full step",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path shards over (sequence, kv head) "
+                                   "units across GPUs by design but no multi-GPU run is part of this build",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixed_precision_kv_kvq_amd as K
+    import workloads as W
+    from workloads.device import DeviceGenerator
+
+    wl = W.WORKLOADS[3]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    B, Hq, Hkv, d, R = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window
+    L0 = wl.context
+    total_steps = args.warmup + args.steps
+    params = K.make_params(d, Hq, Hkv, wl.k_bits, wl.k_group, wl.v_bits, wl.v_group, R, 0, K.KVQ_BF16, 0)
+    cap = L0 + total_steps
+    cache = K.CacheBuffers(params, B, cap)
+    gen = DeviceGenerator(wl)
+    stream = torch.cuda.current_stream()
+
+    # ---- untimed set-up: prefill the cache with the context ------------------
+    t_setup = time.time()
+    chunk = 2048
+    for t0 in range(0, L0, chunk):
+        n = min(chunk, L0 - t0)
+        k = gen.kv(W.TENSOR_K, t0, n)
+        v = gen.kv(W.TENSOR_V, t0, n)
+        before = torch.full((B,), t0, dtype=torch.int32, device=dev)
+        K.kvq_quantize_append(params, cache.struct, before, None, k, v, n)
+    # per-step inputs, resident in HBM before timing
+    k_steps = [gen.kv(W.TENSOR_K, L0 + s, 1) for s in range(total_steps)]
+    v_steps = [gen.kv(W.TENSOR_V, L0 + s, 1) for s in range(total_steps)]
+    q_steps = [gen.q(s) for s in range(total_steps)]
+    lens = [torch.full((B,), L0 + s, dtype=torch.int32, device=dev) for s in range(total_steps + 1)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws_bytes = K.kvq_decode_workspace_bytes(params, B, cap)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    def step(s):
+        K.kvq_quantize_append(params, cache.struct, lens[s], None, k_steps[s], v_steps[s], 1, stream)
+        K.kvq_decode_attention(params, cache.struct, lens[s + 1], L0 + s + 1, q_steps[s], K.KVQ_BF16, out,
+                               K.KVQ_F32, 0.0, ws, ws_bytes, stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    # ---- timed region ----------------------------------------------------------
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = args.warmup + i
+        ev[i][0].record(stream)
+        K.kvq_quantize_append(params, cache.struct, lens[s], None, k_steps[s], v_steps[s], 1, stream)
+        ev[i][1].record(stream)
+        K.kvq_decode_attention(params, cache.struct, lens[s + 1], L0 + s + 1, q_steps[s], K.KVQ_BF16, out,
+                               K.KVQ_F32, 0.0, ws, ws_bytes, stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    append_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    per_th = (d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4)
+    step_bytes = np.array([attn_bytes(wl, L0 + args.warmup + i + 1, per_th, 2) for i in range(args.steps)])
+    achieved = float(step_bytes.mean() / (attn_ms.mean() * 1e-3) / 1e9)
+    us_per_step = wall / args.steps * 1e6
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_digest") == source_digest():
+            traffic = tr.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    res = {
+        "metric": METRIC,
+        "value": round(us_per_step, 2),
+        "unit": "µs/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_step / 1000.0, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 normal-quantile generator; key channel std log-normal(0,0.5), "
+                "3 outlier channels x10 per kv head)",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "context": L0, "window": R, "k_bits": wl.k_bits, "k_group": wl.k_group, "v_bits": wl.v_bits,
+                   "v_group": wl.v_group, "step": "append 1 token/sequence + decode attention"},
+        "attention_us": round(float(attn_ms.mean()) * 1e3, 2),
+        "append_us": round(float(append_ms.mean()) * 1e3, 2),
+        "attention_GBps": round(achieved, 1),
+        "attention_pct_peak_hbm": round(100.0 * achieved / PEAK_HBM_GBS, 1),
+        "tokens_per_s": round(B / (us_per_step * 1e-6), 1),
+        "kv_positions_per_s": round(B * (L0 + args.warmup + args.steps / 2) / (attn_ms.mean() * 1e-3), 1),
+        "roofline": {"kernel": "kvq_decode_attention (split-K kernel + combine, event-timed together)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(step_bytes.mean())},
+        "setup_s": round(setup_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

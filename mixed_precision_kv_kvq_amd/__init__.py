@@ -12,8 +12,13 @@ import ctypes
 import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint8, c_uint16, c_void_p
 
+# torch first: libkvq.so resolves its HIP runtime by soname (libamdhip64.so.7), which then binds
+# to the copy torch has already loaded.  Loaded before torch, the library would pull in a second
+# HIP runtime next to torch's own, and that second runtime finds no device.
+import torch  # noqa: F401,E402
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_EHIP = range(5)
 KVQ_F32, KVQ_BF16 = 0, 1

@@ -20,16 +20,19 @@ ROOT = os.path.dirname(PKG)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
+EXTRA = os.environ.get("KVQ_EXTRA_FLAGS", "").split()
+
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     # no packed-fp32 VALU instructions anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
+    *EXTRA,
 ]
 
-LIB = os.path.join(PKG, "libkvq.so")
+LIB = os.environ.get("KVQ_LIB_OUT") or os.path.join(PKG, "libkvq.so")
 GEN_LIB = os.path.join(ROOT, "workloads", "libkvqgen.so")
-BUILD_DIR = os.path.join(PKG, "_build")
+BUILD_DIR = os.environ.get("KVQ_BUILD_DIR") or os.path.join(PKG, "_build")
 
 
 def _sources():

@@ -6,6 +6,7 @@ namespace kvq_attn {
 template <int G, int P, int NVG>
 static hipError_t launch(const KvqAttnArgs &a, hipStream_t s) {
   const unsigned waves = (unsigned)((int64_t)a.cache.batch * a.Hkv * a.splits);
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
   hipLaunchKernelGGL((kvq_attn_split_kernel<1, 8, G, P, NVG>), dim3(waves), dim3(64), 0, s, a);
   return hipGetLastError();
 }

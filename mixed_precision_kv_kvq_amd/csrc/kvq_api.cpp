@@ -6,7 +6,7 @@
 
 namespace {
 
-constexpr int kTargetWaves = 4096;  // 256 CUs x 16 resident waves
+constexpr int kNumCUs = 256;  // MI355X
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -55,27 +55,54 @@ KvqCacheDev dev_cache(const kvq_params *p, const kvq_cache *c) {
 
 KvqLayout layout_of(const kvq_params *p) { return kvq_make_layout(p->k_bits, p->k_group, p->v_bits, p->v_group); }
 
-// Virtual pages of a sequence of length L: quantized pages, then window pages.
-int64_t virtual_pages(int64_t L, int R) {
-  const int64_t nq = L > R ? L - R : 0;
-  const int64_t nw = L < R ? L : R;
-  return (nq + KVQ_PAGE - 1) / KVQ_PAGE + (nw + KVQ_PAGE - 1) / KVQ_PAGE;
-}
+// Split plan.  Splits [0, wsplits) cover the recent window (KVQ_WIN_PAGES
+// pages each) and come first in dispatch order, so that their short,
+// latency-bound work overlaps the streaming of the quantized pages; the
+// remaining splits cover the quantized pages, pps pages each, sized so that
+// all waves of the launch are resident at once.
+struct SplitPlan {
+  int splits, wsplits, pps;
+  int bound;  // most splits any length <= max_seq_len can get (workspace size)
+};
 
-void split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, int *splits, int *pps) {
-  const int64_t vp = virtual_pages(max_seq_len, p->window);
-  int64_t per = 0;
+SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len) {
+  const int R = p->window;
+  const int64_t nq = max_seq_len > R ? max_seq_len - R : 0;
+  const int64_t nw = max_seq_len < R ? max_seq_len : R;
+  const int64_t qpages = (nq + KVQ_PAGE - 1) / KVQ_PAGE;
+  const int64_t wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;
+  SplitPlan sp;
+  sp.wsplits = (int)((wpages + KVQ_WIN_PAGES - 1) / KVQ_WIN_PAGES);
+  const int64_t units = (int64_t)batch * p->num_kv_heads;
+  int64_t per = 0, cap = 0;
   if (const char *env = getenv("KVQ_PAGES_PER_SPLIT")) per = atoll(env);
-  if (per <= 0) {
-    const int64_t total = (int64_t)batch * p->num_kv_heads * (vp > 0 ? vp : 1);
-    per = (total + kTargetWaves - 1) / kTargetWaves;
+  const bool fixed = per > 0;
+  if (!fixed) {
+    int64_t target = (int64_t)kNumCUs * kvq_attn_waves_per_cu(p->k_bits, p->v_bits, KVQ_D / p->v_group);
+    if (const char *env = getenv("KVQ_TARGET_WAVES")) target = atoll(env) > 0 ? atoll(env) : target;
+    // quantized splits per unit: at most ceil(target / units) - wsplits, at least 1
+    cap = (target + units - 1) / units - sp.wsplits;
+    if (cap < 1) cap = 1;
+    per = (qpages + cap - 1) / cap;
   }
   if (per < 2) per = 2;
   per = (per + 1) & ~int64_t(1);
-  int64_t s = (vp + per - 1) / per;
-  if (s < 1) s = 1;
-  *splits = (int)s;
-  *pps = (int)per;
+  const int64_t qsplits = (qpages + per - 1) / per;
+  sp.pps = (int)per;
+  sp.splits = (int)(sp.wsplits + qsplits);
+  if (sp.splits < 1) sp.splits = 1;
+  // Bound over all lengths up to max_seq_len.  wsplits(L) + ceil(qpages(L) / per) is
+  // non-decreasing in L for a fixed per; otherwise qsplits <= min(ceil(qpages / 2), cap) and
+  // both wsplits + ceil(qpages / 2) and wsplits + cap = max(ceil(target / units), wsplits + 1)
+  // are non-decreasing in L, so their minimum at max_seq_len bounds every shorter length.
+  int64_t bound = sp.wsplits + qsplits;
+  if (!fixed) {
+    const int64_t a = sp.wsplits + (qpages + 1) / 2, b = sp.wsplits + cap;
+    bound = a < b ? a : b;
+  }
+  if (bound < sp.splits) bound = sp.splits;
+  sp.bound = (int)bound;
+  return sp;
 }
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
@@ -122,9 +149,8 @@ kvq_status kvq_quantize_append(const kvq_params *params, const kvq_cache *cache,
 
 size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len) {
   if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0) return 0;
-  int splits, pps;
-  split_plan(params, batch, max_seq_len, &splits, &pps);
-  return (size_t)batch * params->num_q_heads * (size_t)splits * KVQ_PART_STRIDE * sizeof(float);
+  const SplitPlan sp = split_plan(params, batch, max_seq_len);
+  return (size_t)batch * params->num_q_heads * (size_t)sp.bound * KVQ_PART_STRIDE * sizeof(float);
 }
 
 kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
@@ -157,7 +183,10 @@ kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache
   a.Hkv = params->num_kv_heads;
   a.R = params->window;
   a.rotation = params->key_rotation;
-  split_plan(params, cache->batch, max_seq_len, &a.splits, &a.pages_per_split);
+  const SplitPlan sp = split_plan(params, cache->batch, max_seq_len);
+  a.splits = sp.splits;
+  a.wsplits = sp.wsplits;
+  a.pages_per_split = sp.pps;
   a.max_len = (int32_t)(max_seq_len < INT32_MAX ? max_seq_len : INT32_MAX);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
   a.sigma_u = (float)((double)scale * 1.4426950408889634 * 8589934592.0);  // * log2(e) * 2^33

@@ -215,6 +215,7 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
 hipError_t kvq_launch_append(const KvqAppendArgs &a, hipStream_t s) {
   if (a.n_new <= 0 || a.cache.batch <= 0) return hipSuccess;
   dim3 grid((unsigned)a.n_new, (unsigned)a.Hkv, (unsigned)a.cache.batch);
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
   hipLaunchKernelGGL(kvq_append_kernel, grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -31,11 +31,9 @@
 //      part x head, k = 32 tokens), B = value codes (k = tokens, col = channel).
 // Every operand comes from one coalesced load per lane (see kvq_layout.h).
 #pragma once
-#include "kvq_internal.h"
+#include <type_traits>
 
-#ifndef KVQ_WPE
-#define KVQ_WPE 4
-#endif
+#include "kvq_internal.h"
 
 namespace kvq_attn {
 
@@ -45,34 +43,65 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float EXP2_M66 = 0x1p-66f;
 constexpr float EXP2_M67 = 0x1p-67f;  // 2^-66 * 2^-67 = 2^-133
-constexpr float EXP2_EQ = 0x1p100f;   // query operand scale
-constexpr float EXP2_EW = 0x1p100f;   // weight operand scale
-constexpr float EXP2_OUT = 0x1p33f;   // 2^(133 - 100): value accumulators back to real units
-constexpr float EXP2_WIN_W = 0x1p-33f;
+constexpr float EXP2_EQ = 0x1p100f;  // query operand scale
+// Softmax weights are carried as p * 2^64 (l, the zero-point sums, the value
+// accumulators and the window sums all share that factor, which cancels in the
+// final normalization).  Value MFMA products are (p 2^64 scale)(c 2^s 2^-133)
+// for tile scale s, so an accumulator D is brought to the common scale by
+// 2^(133 - s) = 2^69 * 2^(64 - s), applied as two exact multiplies.
+constexpr float P_BIAS_LOG2 = 64.0f;
+constexpr float EXP2_OUT = 0x1p69f;
+
+// Position of a b-bit field within a 16-bit half when extracted without a full
+// shift: fields whose bits end inside the low byte are read in place (a bf16
+// bit pattern x in the low byte is the value x * 2^-133, so a field at bit s
+// reads as code * 2^s); higher fields are first shifted down by 8.
+template <int B>
+__device__ __forceinline__ constexpr int field_scale_log2(int bit) {
+  return (bit + B <= 8) ? bit : bit - 8;
+}
+// Extract the field of both 16-bit halves at `bit` as a bf16 pair, scaled by 2^field_scale_log2.
+template <int B>
+__device__ __forceinline__ uint32_t field_pair(uint32_t word, uint32_t word_sh8, int bit) {
+  constexpr uint32_t m = ((1u << B) - 1u) * 0x00010001u;
+  return (bit + B <= 8) ? (word & (m << bit)) : (word_sh8 & (m << (bit - 8)));
+}
 
 template <int N>
 struct Words {
   uint32_t w[N];
 };
 
+#define KVQ_GLOBAL __attribute__((address_space(1)))
+
+// Loads through global-address-space pointers (global_load_*, not flat_load_*).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2e __attribute__((ext_vector_type(2)));
+typedef float f32x4e __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ T gload(const void *p) {
+  return *(const KVQ_GLOBAL T *)(p);
+}
+
 template <int N>
 __device__ __forceinline__ Words<N> load_words(const uint8_t *p) {
   Words<N> r;
   if constexpr (N == 1) {
-    r.w[0] = *reinterpret_cast<const uint32_t *>(p);
+    r.w[0] = gload<uint32_t>(p);
   } else if constexpr (N == 2) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    const u32x2 v = gload<u32x2>(p);
     r.w[0] = v.x;
     r.w[1] = v.y;
   } else if constexpr (N == 4) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    const u32x4 v = gload<u32x4>(p);
     r.w[0] = v.x;
     r.w[1] = v.y;
     r.w[2] = v.z;
     r.w[3] = v.w;
   } else {
-    const uint4 v0 = reinterpret_cast<const uint4 *>(p)[0];
-    const uint4 v1 = reinterpret_cast<const uint4 *>(p)[1];
+    const u32x4 v0 = gload<u32x4>(p);
+    const u32x4 v1 = gload<u32x4>(p + 16);
     r.w[0] = v0.x;
     r.w[1] = v0.y;
     r.w[2] = v0.z;
@@ -93,7 +122,10 @@ __device__ __forceinline__ Words<N> zero_words() {
   return r;
 }
 
-__device__ __forceinline__ uint4 load_u4(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ uint4 load_u4(const uint8_t *p) {
+  const u32x4 v = gload<u32x4>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ uint32_t u4_get(const uint4 &v, int r) {
   return r == 0 ? v.x : (r == 1 ? v.y : (r == 2 ? v.z : v.w));
@@ -108,11 +140,20 @@ __device__ __forceinline__ bf16x8 pack8(uint32_t a, uint32_t b, uint32_t c, uint
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) { return kvq_f32_to_bf16_rne(f); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
+
+__device__ __forceinline__ float bf16lo_f32(uint32_t pair) { return __builtin_bit_cast(float, pair << 16); }
+__device__ __forceinline__ float bf16hi_f32(uint32_t pair) { return __builtin_bit_cast(float, pair & 0xFFFF0000u); }
 
 __device__ __forceinline__ float ror_add(float v, int sh) {
   int r;
@@ -125,6 +166,26 @@ __device__ __forceinline__ float ror_add(float v, int sh) {
   return v + __builtin_bit_cast(float, r);
 }
 
+// Reductions over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48)
+// with v_permlane16_swap / v_permlane32_swap: swapping a value with itself
+// leaves the xor-16 (xor-32) partner pair in the two results.
+__device__ __forceinline__ float rows_max(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  auto p16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = __builtin_fmaxf(__builtin_bit_cast(float, (int)p16[0]), __builtin_bit_cast(float, (int)p16[1]));
+  const int c = __builtin_bit_cast(int, v);
+  auto p32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (int)p32[0]), __builtin_bit_cast(float, (int)p32[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  auto p16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = __builtin_bit_cast(float, (int)p16[0]) + __builtin_bit_cast(float, (int)p16[1]);
+  const int c = __builtin_bit_cast(int, v);
+  auto p32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __builtin_bit_cast(float, (int)p32[0]) + __builtin_bit_cast(float, (int)p32[1]);
+}
+
 template <int G>
 __device__ __forceinline__ float replica_allreduce(float v) {
 #pragma unroll
@@ -132,22 +193,63 @@ __device__ __forceinline__ float replica_allreduce(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Page prefetch ring in LDS.  In the steady-state loop every page record is
+// copied verbatim into a per-wave LDS slot with direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l writes 16 bytes at slot + 16*l), a few page
+// pairs ahead of use, and read back with ds_read when processed.  In-flight
+// data therefore never occupies a VGPR.  The waits are explicit: vmcnt counts
+// vector-memory operations in issue order, so after N newer loads,
+// s_waitcnt vmcnt(N) means every older load has landed in LDS.  Every DMA
+// instruction keeps all 64 lanes active (lanes past the end of a record re-read
+// an in-range chunk into the slot's padding) so that the counts are exact, and
+// no other vector-memory load is issued inside that loop.
+// ---------------------------------------------------------------------------
+template <int CNT>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
+}
+
+typedef __attribute__((address_space(3))) void *lds_vptr;
+
+template <int N>
+struct RawWords;
+template <>
+struct RawWords<1> {
+  uint32_t v;
+  __device__ __forceinline__ uint32_t w(int) const { return v; }
+};
+template <>
+struct RawWords<2> {
+  u32x2 v;
+  __device__ __forceinline__ uint32_t w(int i) const { return v[i]; }
+};
+template <>
+struct RawWords<4> {
+  u32x4 v;
+  __device__ __forceinline__ uint32_t w(int i) const { return v[i]; }
+};
+template <>
+struct RawWords<8> {
+  u32x4 a, b;
+  __device__ __forceinline__ uint32_t w(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+
 // Per-wave running state of the online softmax.
-template <int G, int NVG>
+template <int NVG>
 struct State {
   f32x4 acc[8];     // value MFMA accumulators (rows = part x head, col = channel)
   float m;          // running max of this lane's head, in score units
   float l;          // this lane's partial sum of p
   float zacc[NVG];  // this lane's partial sum of p * zero_v per value group
-  float ow[G][2];   // window contribution for channels 2*lane, 2*lane+1 (real units)
 };
 
 template <int KB, int VB, int G, int P, int NVG>
 struct Kern {
-  static constexpr int REP = 16 / G;                 // replicas of each head in the 16 columns
-  static constexpr int X = REP / P;                  // chunk slots per query part
-  static constexpr int XE = X < 4 ? X : 4;           // chunk slots in use
-  static constexpr int NACC = 4 / XE;                // score accumulators
+  static constexpr int REP = 16 / G;        // replicas of each head in the 16 columns
+  static constexpr int X = REP / P;         // chunk slots per query part
+  static constexpr int XE = X < 4 ? X : 4;  // chunk slots in use
+  static constexpr int NACC = 4 / XE;       // score accumulators
   static constexpr int PERK = 16 / KB;
   static constexpr uint32_t MASKK = ((1u << KB) - 1u) * 0x00010001u;
   static constexpr uint32_t MASKV = ((1u << VB) - 1u) * 0x00010001u;
@@ -157,12 +259,21 @@ struct Kern {
     float Qs[NACC];  // sum of this column's query operand per accumulator, x 2^-133
     int kmeta_off[NACC];
     int vmeta_off[NVG];
-    int lane, col, quad, rowpart;
-    float sig;  // softmax scale in score units (log2 domain)
+    int lane, col, quad;
+    float sig;     // softmax scale in score units (log2 domain)
+    float tau;     // lazy-max margin in score units (16 in log2 units)
+    float sel_lo;  // 1 for rows that carry the low bf16 part of the weights
   };
 
-  // Build the query operand from q (fp32, [G][128] in LDS).
-  static __device__ __forceinline__ void build_q(Ctx &cx, const float *qs) {
+  // Scale (log2) at which the key codes of chunk kc, pair slot i are read (see field_pair).
+  static __device__ __forceinline__ constexpr int kslot_scale(int kc, int i) {
+    return field_scale_log2<KB>(KB * ((4 * kc + i) % PERK));
+  }
+
+  // Build the query operand from q (fp32, [G][128] in LDS).  For code operands
+  // (code_scaled), entries of slots whose codes are read scaled by 2^k are
+  // divided by 2^k (exact); raw window keys need the unscaled operand.
+  static __device__ __forceinline__ void build_q(Ctx &cx, const float *qs, bool code_scaled = true) {
     const int y = cx.col / G, h = cx.col % G;
     const int part = y / X, x = y % X;
     const bool valid = x < XE;
@@ -175,38 +286,36 @@ struct Kern {
       const bool use = valid && (kc % XE) == x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint32_t pr = 0;
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          const int ch = 32 * kc + 8 * cx.quad + 2 * i + e2;
-          uint32_t bits = 0;
-          if (use) {
-            const float v = qs[h * KVQ_D + ch] * EXP2_EQ;
-            const uint32_t hb = bf16_rne(v);
-            if (P == 1 || part == 0) {
-              bits = hb;
-            } else {
-              bits = bf16_rne(v - kvq_bf16_bits_to_f32(hb));
-            }
-            qsum[kc / XE] += kvq_bf16_bits_to_f32(bits);
-          }
-          pr |= bits << (16 * e2);
+        const int ch = 32 * kc + 8 * cx.quad + 2 * i;
+        const float v0 = use ? qs[h * KVQ_D + ch] * EXP2_EQ : 0.f;
+        const float v1 = use ? qs[h * KVQ_D + ch + 1] * EXP2_EQ : 0.f;
+        uint32_t pr = pack_bf16x2(v0, v1);
+        if (P == 2) {
+          const uint32_t lo = pack_bf16x2(v0 - bf16lo_f32(pr), v1 - bf16hi_f32(pr));
+          pr = part ? lo : pr;
         }
-        w[i] = pr;
+        const float e0 = bf16lo_f32(pr), e1 = bf16hi_f32(pr);
+        qsum[kc / XE] += e0 + e1;
+        const float f = code_scaled ? __builtin_amdgcn_ldexpf(1.0f, -kslot_scale(kc, i)) : 1.0f;
+        w[i] = pack_bf16x2(e0 * f, e1 * f);  // exact: power-of-two scaling of bf16 values
       }
       cx.qB[kc] = pack8(w[0], w[1], w[2], w[3]);
     }
 #pragma unroll
     for (int a = 0; a < NACC; ++a) {
-      float s = qsum[a];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      cx.Qs[a] = s * EXP2_M66 * EXP2_M67;
+      cx.Qs[a] = rows_sum(qsum[a]) * EXP2_M66 * EXP2_M67;
     }
   }
 
-  static __device__ __forceinline__ void init_meta(Ctx &cx, const KvqLayout &lay) {
-    const int y = cx.col / G, x = y % X;
+  static __device__ __forceinline__ void init_ctx(Ctx &cx, const KvqLayout &lay, float sig) {
+    cx.lane = threadIdx.x;
+    cx.col = cx.lane & 15;
+    cx.quad = cx.lane >> 4;
+    cx.sig = sig;
+    cx.tau = 16.0f / sig;
+    const int rowpart = cx.col / G;  // A-operand row of the value MFMA: 0 = hi, 1 = lo, else unused
+    cx.sel_lo = rowpart == 1 ? 1.f : 0.f;
+    const int x = (cx.col / G) % X;
     const bool valid = x < XE;
 #pragma unroll
     for (int a = 0; a < NACC; ++a) {
@@ -243,48 +352,66 @@ struct Kern {
     for (int v = 0; v < NVG; ++v) pd.vm[v] = make_uint4(0, 0, 0, 0);
   }
 
-  // Scores of the 16 tokens of one page for this lane's head: s[r] for token 4*quad + r.
-  static __device__ __forceinline__ void page_scores(const Ctx &cx, const PageData &pd, float s[4]) {
-    f32x4 D[NACC];
+  // Key codes of chunk kc of one page as the A operand (slot scales per kslot_scale).
+  static __device__ __forceinline__ bf16x8 key_operand(const PageData &pd, int kc) {
+    uint32_t w[4];
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) D[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      const int u = 4 * kc + i;
+      const uint32_t word = pd.kc.w[u / PERK];
+      w[i] = field_pair<KB>(word, word >> 8, KB * (u % PERK));
+    }
+    return pack8(w[0], w[1], w[2], w[3]);
+  }
+
+  static __device__ __forceinline__ float score_epilogue(const Ctx &cx, const PageData &pd, const f32x4 *D, int r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) {
+      const uint32_t md = u4_get(pd.km[a], r);
+      acc = __builtin_fmaf(h2f(md >> 16), cx.Qs[a], acc);
+      acc = __builtin_fmaf(D[a][r], h2f(md & 0xFFFF), acc);
+    }
+    return replica_allreduce<G>(acc);
+  }
+
+  // Scores of the 32 tokens of a page pair for this lane's head: s0[r] / s1[r] for token 4*quad + r.
+  static __device__ __forceinline__ void pair_scores(const Ctx &cx, const PageData &A, const PageData &B,
+                                                     float s0[4], float s1[4]) {
+    f32x4 DA[NACC], DB[NACC];
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) {
+      DA[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      DB[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int u = 4 * kc + i;
-        w[i] = (pd.kc.w[u / PERK] >> (KB * (u % PERK))) & MASKK;
-      }
-      D[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(w[0], w[1], w[2], w[3]), cx.qB[kc], D[kc / XE], 0, 0, 0);
+      DA[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(key_operand(A, kc), cx.qB[kc], DA[kc / XE], 0, 0, 0);
+      DB[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(key_operand(B, kc), cx.qB[kc], DB[kc / XE], 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int a = 0; a < NACC; ++a) {
-        const uint32_t md = u4_get(pd.km[a], r);
-        acc = __builtin_fmaf(h2f(md >> 16), cx.Qs[a], acc);
-        acc = __builtin_fmaf(D[a][r], h2f(md & 0xFFFF), acc);
-      }
-      s[r] = replica_allreduce<G>(acc);
+      s0[r] = score_epilogue(cx, A, DA, r);
+      s1[r] = score_epilogue(cx, B, DB, r);
     }
   }
 
-  // Online-softmax update with the 8 scores of a page pair; returns p in place.
-  template <bool MASKED>
-  static __device__ __forceinline__ void softmax_update(const Ctx &cx, State<G, NVG> &st, float s0[4], float s1[4]) {
-    float t = s0[0];
-#pragma unroll
-    for (int r = 1; r < 4; ++r) t = __builtin_fmaxf(t, s0[r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) t = __builtin_fmaxf(t, s1[r]);
-    t = __builtin_fmaxf(t, __shfl_xor(t, 16));
-    t = __builtin_fmaxf(t, __shfl_xor(t, 32));
-    const float mnew = __builtin_fmaxf(st.m, t);
-    if (__builtin_amdgcn_ballot_w64(mnew > st.m)) {
-      const float alpha = (mnew > st.m) ? __builtin_amdgcn_exp2f(cx.sig * (st.m - mnew)) : 1.0f;
+  // Online-softmax update with the 8 scores of a page pair; returns p * 2^64 in place.
+  // Lazy running max: weights are formed against the running max m, which is
+  // only raised (with the cross-lane tile max and a rescale of everything
+  // accumulated so far) when some lane sees a score more than 16 (log2 units)
+  // above it, so weights stay below 2^(64+16).  m is always the same in every
+  // lane that holds a given head.
+  template <bool MASKED, bool WIN>
+  static __device__ __forceinline__ void softmax_update(const Ctx &cx, State<NVG> &st, float s0[4], float s1[4],
+                                                        float (*ow)[2]) {
+    float t = __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), __builtin_fmaxf(s0[2], s0[3]));
+    t = __builtin_fmaxf(t, __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), __builtin_fmaxf(s1[2], s1[3])));
+    if (__builtin_amdgcn_ballot_w64(t > st.m + cx.tau)) {
+      t = rows_max(t);  // tile max of this lane's head
+      const float mnew = __builtin_fmaxf(st.m, t);
       // st.m == -inf gives alpha = 0 (nothing accumulated yet).
+      const float alpha = (mnew > st.m) ? __builtin_amdgcn_exp2f(cx.sig * (st.m - mnew)) : 1.0f;
       st.l *= alpha;
 #pragma unroll
       for (int v = 0; v < NVG; ++v) st.zacc[v] *= alpha;
@@ -295,15 +422,18 @@ struct Kern {
 #pragma unroll
         for (int m = 0; m < 8; ++m) st.acc[m][r] *= ar;
       }
+      if constexpr (WIN) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ah = __shfl(alpha, h);
-        st.ow[h][0] *= ah;
-        st.ow[h][1] *= ah;
+        for (int h = 0; h < G; ++h) {
+          const float ah = __shfl(alpha, h);
+          ow[h][0] *= ah;
+          ow[h][1] *= ah;
+        }
       }
       st.m = mnew;
     }
-    const float nb = -cx.sig * st.m;
+    const float nb = __builtin_fmaf(-cx.sig, st.m, P_BIAS_LOG2);
+    float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.sig, nb));
@@ -314,55 +444,56 @@ struct Kern {
       }
       s0[r] = p0;
       s1[r] = p1;
-      st.l += p0 + p1;
+      lsum += p0 + p1;
     }
+    st.l += lsum;
   }
 
-  // Weights operand (A of the value MFMA) for value group v from per-token weights.
+  // Weights operand (A of the value MFMA): rows 0..G-1 carry bf16(w), rows G..2G-1 bf16(w - bf16(w));
+  // rows 2G.. (unused) carry bf16(w) too, which only reaches accumulator rows that are never read.
   static __device__ __forceinline__ bf16x8 weights_operand(const Ctx &cx, const float w0[4], const float w1[4]) {
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float a0 = (i < 2) ? w0[2 * i] : w1[2 * i - 4];
-      float a1 = (i < 2) ? w0[2 * i + 1] : w1[2 * i - 3];
-      if (cx.rowpart == 1) {
-        a0 = a0 - kvq_bf16_bits_to_f32(bf16_rne(a0));
-        a1 = a1 - kvq_bf16_bits_to_f32(bf16_rne(a1));
-      } else if (cx.rowpart > 1) {
-        a0 = 0.f;
-        a1 = 0.f;
-      }
-      o[i] = pack_bf16x2(a0, a1);
+      const float a0 = (i < 2) ? w0[2 * i] : w1[2 * i - 4];
+      const float a1 = (i < 2) ? w0[2 * i + 1] : w1[2 * i - 3];
+      const uint32_t hp = pack_bf16x2(a0, a1);
+      o[i] = pack_bf16x2(__builtin_fmaf(-cx.sel_lo, bf16lo_f32(hp), a0),
+                         __builtin_fmaf(-cx.sel_lo, bf16hi_f32(hp), a1));
     }
     return pack8(o[0], o[1], o[2], o[3]);
   }
 
-  // Value contraction of a page pair with probabilities p0 (page A) and p1 (page B).
+  // Scale (log2) at which the value codes of tile m are read (independent of the pair slot).
+  static __device__ __forceinline__ constexpr int vtile_scale(int m) { return field_scale_log2<VB>((m * VB) & 15); }
+
+  // Value contraction of a page pair with weights p0 (page A) and p1 (page B), both carried as p * 2^64.
   template <bool MASKED>
-  static __device__ __forceinline__ void pair_values(const Ctx &cx, State<G, NVG> &st, const PageData &A,
+  static __device__ __forceinline__ void pair_values(const Ctx &cx, State<NVG> &st, const PageData &A,
                                                      const PageData &B, const float p0[4], const float p1[4],
                                                      int validA, int validB) {
     bf16x8 Aop[NVG];
 #pragma unroll
     for (int v = 0; v < NVG; ++v) {
       float w0[4], w1[4];
-      float z = 0.f;
+      float z = st.zacc[v];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t ma = u4_get(A.vm[v], r), mb = u4_get(B.vm[v], r);
-        float za = p0[r] * h2f(ma >> 16), zb = p1[r] * h2f(mb >> 16);
-        w0[r] = p0[r] * h2f(ma & 0xFFFF) * EXP2_EW;
-        w1[r] = p1[r] * h2f(mb & 0xFFFF) * EXP2_EW;
-        if (MASKED) {
+        float sa = h2f(ma & 0xFFFF), za = h2f(ma >> 16), sb = h2f(mb & 0xFFFF), zb = h2f(mb >> 16);
+        if (MASKED) {  // metadata of invalid tokens may be anything, keep it out
           const bool va = 4 * cx.quad + r < validA, vb = 4 * cx.quad + r < validB;
+          sa = va ? sa : 0.f;
           za = va ? za : 0.f;
+          sb = vb ? sb : 0.f;
           zb = vb ? zb : 0.f;
-          w0[r] = va ? w0[r] : 0.f;
-          w1[r] = vb ? w1[r] : 0.f;
         }
-        z += za + zb;
+        w0[r] = __builtin_fmaf(p0[r], sa, 0.f);
+        w1[r] = __builtin_fmaf(p1[r], sb, 0.f);
+        z = __builtin_fmaf(p0[r], za, z);
+        z = __builtin_fmaf(p1[r], zb, z);
       }
-      st.zacc[v] += z;
+      st.zacc[v] = z;
       Aop[v] = weights_operand(cx, w0, w1);
     }
 #pragma unroll
@@ -370,21 +501,133 @@ struct Kern {
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int il = i & 1;
-        const int pos = il * 8 * VB + m * VB;
+        const int pos = (i & 1) * 8 * VB + m * VB;
         const uint32_t word = (i < 2) ? A.vc.w[pos >> 4] : B.vc.w[pos >> 4];
-        w[i] = (word >> (pos & 15)) & MASKV;
+        w[i] = field_pair<VB>(word, word >> 8, pos & 15);
       }
       st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop[m / (8 / NVG)], pack8(w[0], w[1], w[2], w[3]), st.acc[m], 0, 0, 0);
     }
   }
 
+  // ---- LDS ring -------------------------------------------------------------
+  static constexpr int MAX_REC16 = 16 * KB + 16 + 16 * VB + 4 * NVG;  // record in 16-byte units (k_group 32)
+  static constexpr int DMAS_PER_PAGE = (MAX_REC16 + 63) / 64;
+  static constexpr int SLOT_PAGE_BYTES = DMAS_PER_PAGE * 1024;
+  static constexpr int PAIR_BYTES = 2 * SLOT_PAGE_BYTES;
+  static constexpr int NSLOT = kvq_ring_slots(PAIR_BYTES);
+  static constexpr int STAGE_BYTES = (2 * 8 * KVQ_D + 8 * 4) * 4;  // query / accumulator staging
+  static constexpr int LDS_BYTES = NSLOT * PAIR_BYTES > STAGE_BYTES ? NSLOT * PAIR_BYTES : STAGE_BYTES;
+  static_assert(LDS_BYTES == kvq_attn_lds_bytes(KB, VB, NVG), "host and device LDS sizing disagree");
+
+  // Copy one page record into an LDS slot page (DMAS_PER_PAGE wave-wide DMAs).
+  static __device__ __forceinline__ void dma_page(uint8_t *slot_page, const uint8_t *rec, int rec16, int lane) {
+#pragma unroll
+    for (int k = 0; k < DMAS_PER_PAGE; ++k) {
+      int c = 64 * k + lane;
+      c = c < rec16 ? c : rec16 - 1;
+      __builtin_amdgcn_global_load_lds((const void *)(rec + 16 * c), (lds_vptr)(slot_page + 1024 * k), 16, 0, 0);
+    }
+  }
+
+  // Read one page of a ring slot.  The reads are inline asm: the compiler cannot
+  // tell that they do not alias the ring's in-flight DMAs and would otherwise
+  // drain every outstanding load before them.  A single lgkmcnt(0) wait ties
+  // every read result, and nothing touches a result before that wait.
+  template <int N>
+  static __device__ __forceinline__ void ds_read_words(RawWords<N> &d, uint32_t addr) {
+    if constexpr (N == 1) {
+      asm volatile("ds_read_b32 %0, %1" : "=v"(d.v) : "v"(addr));
+    } else if constexpr (N == 2) {
+      asm volatile("ds_read_b64 %0, %1" : "=v"(d.v) : "v"(addr));
+    } else if constexpr (N == 4) {
+      asm volatile("ds_read_b128 %0, %1" : "=v"(d.v) : "v"(addr));
+    } else {
+      asm volatile("ds_read_b128 %0, %1" : "=v"(d.a) : "v"(addr));
+      asm volatile("ds_read_b128 %0, %1 offset:16" : "=v"(d.b) : "v"(addr));
+    }
+  }
+
+  static __device__ __forceinline__ void read_page(PageData &pd, const Ctx &cx, const uint8_t *sp,
+                                                   const KvqLayout &lay) {
+    const uint32_t base = (uint32_t)(uintptr_t)sp;  // LDS offset (low 32 bits of the shared-aperture address)
+    RawWords<KB> rk;
+    RawWords<VB> rv;
+    u32x4 km[NACC], vm[NVG];
+    ds_read_words(rk, base + lay.k_codes_off + cx.lane * 4 * KB);
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) {
+      const uint32_t addr = base + cx.kmeta_off[a];
+      asm volatile("ds_read_b128 %0, %1" : "=v"(km[a]) : "v"(addr));
+    }
+    ds_read_words(rv, base + lay.v_codes_off + cx.lane * 4 * VB);
+#pragma unroll
+    for (int v = 0; v < NVG; ++v) {
+      const uint32_t addr = base + cx.vmeta_off[v];
+      asm volatile("ds_read_b128 %0, %1" : "=v"(vm[v]) : "v"(addr));
+    }
+    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 1 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(rv.v), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 1 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 2 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(rv.v), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 2 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 4 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.v), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 4 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 1 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 1 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 2 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 2 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 4 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 4 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 1 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(rv.v), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 1 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 2 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(rv.v), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 2 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 4 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.v), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 4 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 1 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 1 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 2 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 2 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 4 && NVG == 1)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
+    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 4 && NVG == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
+#pragma unroll
+    for (int i = 0; i < KB; ++i) pd.kc.w[i] = rk.w(i);
+#pragma unroll
+    for (int i = 0; i < VB; ++i) pd.vc.w[i] = rv.w(i);
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) pd.km[a] = make_uint4(km[a].x, km[a].y, km[a].z, km[a].w);
+#pragma unroll
+    for (int v = 0; v < NVG; ++v) pd.vm[v] = make_uint4(vm[v].x, vm[v].y, vm[v].z, vm[v].w);
+  }
+
   template <bool MASKED>
-  static __device__ __forceinline__ void process_pair(const Ctx &cx, State<G, NVG> &st, const PageData &A,
+  static __device__ __forceinline__ void process_pair(const Ctx &cx, State<NVG> &st, const PageData &A,
                                                       const PageData &B, int validA, int validB) {
     float s0[4], s1[4];
-    page_scores(cx, A, s0);
-    page_scores(cx, B, s1);
+    pair_scores(cx, A, B, s0, s1);
     if (MASKED) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -392,48 +635,58 @@ struct Kern {
         s1[r] = (4 * cx.quad + r < validB) ? s1[r] : -__builtin_inff();
       }
     }
-    softmax_update<MASKED>(cx, st, s0, s1);
+    softmax_update<MASKED, false>(cx, st, s0, s1, nullptr);
     pair_values<MASKED>(cx, st, A, B, s0, s1, validA, validB);
   }
 
   // Window tokens [w0, w0 + 32) of the ring (valid below wend): scores on MFMA, values on the VALU.
-  static __device__ __forceinline__ void window_chunk(const Ctx &cx, State<G, NVG> &st, const uint8_t *kwin,
-                                                      const uint8_t *vwin, int kv_f32, int w0, int wend) {
+  // Value rows are requested before the scores are computed (all 32 rows for bf16, the first
+  // 16 for fp32), so their latency overlaps the key loads and the MFMAs.
+  template <bool F32>
+  static __device__ __forceinline__ void window_chunk(const Ctx &cx, State<NVG> &st, float (*ow)[2],
+                                                      const uint8_t *kwin, const uint8_t *vwin, int w0, int wend) {
+    constexpr int VT = F32 ? 16 : 32;  // value rows held in registers at once
+    using VRow = typename std::conditional<F32, f32x2e, uint32_t>::type;
+    const int nval = (wend - w0) < 32 ? (wend - w0) : 32;
+    // this lane's two channels of value row w0 + t (rows past the end re-read row w0)
+    auto vload = [&](int t) -> VRow {
+      return gload<VRow>(vwin + ((size_t)(w0 + (t < nval ? t : 0)) * KVQ_D + 2 * cx.lane) * (F32 ? 4 : 2));
+    };
+    VRow vr[VT];
+#pragma unroll
+    for (int t = 0; t < VT; ++t) vr[t] = vload(t);
     float s[2][4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int slot = w0 + 16 * sub + cx.col;  // A-operand row = token
+      int slot = w0 + 16 * sub + cx.col;  // A-operand row = token
       const bool ok = slot < wend;
+      slot = ok ? slot : w0;
       f32x4 D[NACC];
 #pragma unroll
       for (int a = 0; a < NACC; ++a) D[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (F32) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int ch = 32 * kc + 8 * cx.quad;
-        uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
-        if (ok) {
-          if (kv_f32) {
-            const float *rp = reinterpret_cast<const float *>(kwin) + (size_t)slot * KVQ_D + ch;
-            const float4 f0 = reinterpret_cast<const float4 *>(rp)[0];
-            const float4 f1 = reinterpret_cast<const float4 *>(rp)[1];
-            const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        for (int kc = 0; kc < 4; ++kc) {
+          const uint8_t *rp = kwin + ((size_t)slot * KVQ_D + 32 * kc + 8 * cx.quad) * 4;
+          const f32x4e f0 = gload<f32x4e>(rp);
+          const f32x4e f1 = gload<f32x4e>(rp + 16);
+          const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+          uint32_t hi[4], lo[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t h0 = bf16_rne(f[2 * i]), h1 = bf16_rne(f[2 * i + 1]);
-              hi[i] = h0 | (h1 << 16);
-              lo[i] = pack_bf16x2(f[2 * i] - kvq_bf16_bits_to_f32(h0), f[2 * i + 1] - kvq_bf16_bits_to_f32(h1));
-            }
-          } else {
-            const uint4 v = *reinterpret_cast<const uint4 *>(kwin + ((size_t)slot * KVQ_D + ch) * 2);
-            hi[0] = v.x;
-            hi[1] = v.y;
-            hi[2] = v.z;
-            hi[3] = v.w;
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+            lo[i] = pack_bf16x2(f[2 * i] - bf16lo_f32(hi[i]), f[2 * i + 1] - bf16hi_f32(hi[i]));
           }
-        }
-        D[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(hi[0], hi[1], hi[2], hi[3]), cx.qB[kc], D[kc / XE], 0, 0, 0);
-        if (kv_f32)
+          D[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(hi[0], hi[1], hi[2], hi[3]), cx.qB[kc], D[kc / XE], 0, 0, 0);
           D[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(lo[0], lo[1], lo[2], lo[3]), cx.qB[kc], D[kc / XE], 0, 0, 0);
+        }
+      } else {
+        u32x4 kr[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kr[kc] = gload<u32x4>(kwin + ((size_t)slot * KVQ_D + 32 * kc + 8 * cx.quad) * 2);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          D[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(kr[kc].x, kr[kc].y, kr[kc].z, kr[kc].w), cx.qB[kc], D[kc / XE], 0, 0, 0);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -444,38 +697,67 @@ struct Kern {
         s[sub][r] = (w0 + 16 * sub + 4 * cx.quad + r < wend) ? acc : -__builtin_inff();
       }
     }
-    softmax_update<true>(cx, st, s[0], s[1]);
+    softmax_update<true, true>(cx, st, s[0], s[1], ow);
     // Values: this lane owns channels 2*lane, 2*lane+1; p of (head h, token) lives in lane 16*quad + h.
-    const int nval = (wend - w0) < 32 ? (wend - w0) : 32;
-    for (int tk = 0; tk < nval; ++tk) {
-      const int sub = tk >> 4, tq = (tk & 15) >> 2, r = tk & 3;
-      float v0, v1;
-      if (kv_f32) {
-        const float2 f = reinterpret_cast<const float2 *>(vwin + (size_t)(w0 + tk) * KVQ_D * 4)[cx.lane];
-        v0 = f.x;
-        v1 = f.y;
-      } else {
-        const uint32_t u = reinterpret_cast<const uint32_t *>(vwin + (size_t)(w0 + tk) * KVQ_D * 2)[cx.lane];
-        v0 = kvq_bf16_bits_to_f32(u & 0xFFFF);
-        v1 = kvq_bf16_bits_to_f32(u >> 16);
-      }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float pv;
-        switch (r) {
-          case 0: pv = sub ? s[1][0] : s[0][0]; break;
-          case 1: pv = sub ? s[1][1] : s[0][1]; break;
-          case 2: pv = sub ? s[1][2] : s[0][2]; break;
-          default: pv = sub ? s[1][3] : s[0][3]; break;
+    for (int half = 0; half < 32 / VT; ++half) {
+      if (half > 0) {
+#pragma unroll
+        for (int t = 0; t < VT; ++t) vr[t] = vload(VT * half + t);
+      }
+      // Tokens past the end carry p = 0 (their scores were -inf), so the loop runs in full.
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        const int tk = VT * half + t;
+        const int sub = tk >> 4, tq = (tk & 15) >> 2, r = tk & 3;
+        const float pv = s[sub][r];
+        float v0, v1;
+        if constexpr (F32) {
+          v0 = vr[t].x;
+          v1 = vr[t].y;
+        } else {
+          v0 = kvq_bf16_bits_to_f32(vr[t] & 0xFFFF);
+          v1 = kvq_bf16_bits_to_f32(vr[t] >> 16);
         }
-        const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), 16 * tq + h));
-        st.ow[h][0] = __builtin_fmaf(p, v0, st.ow[h][0]);
-        st.ow[h][1] = __builtin_fmaf(p, v1, st.ow[h][1]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), 16 * tq + h));
+          ow[h][0] = __builtin_fmaf(p, v0, ow[h][0]);
+          ow[h][1] = __builtin_fmaf(p, v1, ow[h][1]);
+        }
       }
     }
   }
 
-  static __device__ void run(const KvqAttnArgs &args, float *lds) {
+  // Queries of the G heads of kv head kvh -> LDS (fp32 [G][128]); rotated when `rotate`.
+  static __device__ __forceinline__ void stage_q(const KvqAttnArgs &args, float *qs, int b, int hq0, bool rotate) {
+    const int lane = threadIdx.x;
+    __syncthreads();
+    for (int i = lane; i < G * KVQ_D; i += 64) {
+      const size_t gi = ((size_t)b * args.Hq + hq0) * KVQ_D + i;
+      qs[i] = args.q_f32 ? gload<float>((const float *)args.q + gi)
+                         : kvq_bf16_bits_to_f32(gload<uint16_t>((const uint16_t *)args.q + gi));
+    }
+    __syncthreads();
+    if (rotate) {
+      for (int hs = 1; hs < KVQ_D; hs <<= 1) {
+        for (int pidx = lane; pidx < G * KVQ_D / 2; pidx += 64) {
+          const int hh = pidx / (KVQ_D / 2), pp = pidx % (KVQ_D / 2);
+          const int i0 = (pp / hs) * 2 * hs + (pp % hs);
+          float *row = qs + hh * KVQ_D;
+          const float x0 = row[i0], x1 = row[i0 + hs];
+          row[i0] = x0 + x1;
+          row[i0 + hs] = x0 - x1;
+        }
+        __syncthreads();
+      }
+      for (int i = lane; i < G * KVQ_D; i += 64) qs[i] *= (float)KVQ_WHT_C;
+      __syncthreads();
+    }
+  }
+
+  static __device__ void run(const KvqAttnArgs &args, uint8_t *smem) {
+    float *lds = reinterpret_cast<float *>(smem);
     const int lane = threadIdx.x;
     const int64_t wave = blockIdx.x;
     const int S = args.splits;
@@ -492,90 +774,114 @@ struct Kern {
     const int nw = L < R ? L : R;
     const int qpages = (nq + KVQ_PAGE - 1) / KVQ_PAGE;
     const int wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;
-    const int vp_total = qpages + wpages;
-    const int v0 = split * args.pages_per_split;
-    int v1 = v0 + args.pages_per_split;
-    if (v1 > vp_total) v1 = vp_total;
+    // Window splits first, then quantized splits (see the host split plan).
+    const bool win_split = split < args.wsplits;
+    int v0 = 0, v1 = 0, wv0 = 0, wv1 = 0;
+    if (win_split) {
+      wv0 = split * KVQ_WIN_PAGES;
+      wv1 = wv0 + KVQ_WIN_PAGES < wpages ? wv0 + KVQ_WIN_PAGES : wpages;
+    } else {
+      v0 = (split - args.wsplits) * args.pages_per_split;
+      v1 = v0 + args.pages_per_split < qpages ? v0 + args.pages_per_split : qpages;
+    }
 
     Ctx cx;
-    cx.lane = lane;
-    cx.col = lane & 15;
-    cx.quad = lane >> 4;
-    cx.rowpart = cx.col / G;
-    cx.sig = args.sigma_u;
-
-    // Query of the G heads of this kv head -> LDS (fp32), rotated when keys are.
-    float *qraw = lds;               // [G][128]
-    float *qrot = lds + G * KVQ_D;   // [G][128]
+    init_ctx(cx, lay, args.sigma_u);
     const int hq0 = kvh * G;
-    for (int i = lane; i < G * KVQ_D; i += 64) {
-      const size_t gi = ((size_t)b * args.Hq + hq0) * KVQ_D + i;
-      qraw[i] = args.q_f32 ? reinterpret_cast<const float *>(args.q)[gi]
-                           : kvq_bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(args.q)[gi]);
-    }
-    __syncthreads();
-    if (args.rotation) {
-      for (int i = lane; i < G * KVQ_D; i += 64) qrot[i] = qraw[i];
-      __syncthreads();
-      for (int hs = 1; hs < KVQ_D; hs <<= 1) {
-        for (int pidx = lane; pidx < G * KVQ_D / 2; pidx += 64) {
-          const int hh = pidx / (KVQ_D / 2), pp = pidx % (KVQ_D / 2);
-          const int i0 = (pp / hs) * 2 * hs + (pp % hs);
-          float *row = qrot + hh * KVQ_D;
-          const float x0 = row[i0], x1 = row[i0 + hs];
-          row[i0] = x0 + x1;
-          row[i0 + hs] = x0 - x1;
-        }
-        __syncthreads();
-      }
-      for (int i = lane; i < G * KVQ_D; i += 64) qrot[i] *= (float)KVQ_WHT_C;
-      __syncthreads();
-      build_q(cx, qrot);
-    } else {
-      build_q(cx, qraw);
-    }
-    init_meta(cx, lay);
-
-    State<G, NVG> st;
+    State<NVG> st;
 #pragma unroll
     for (int m = 0; m < 8; ++m) st.acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m = -__builtin_inff();
     st.l = 0.f;
 #pragma unroll
     for (int v = 0; v < NVG; ++v) st.zacc[v] = 0.f;
+
+    if (win_split) {
+      // Window pages: raw (and unrotated) keys, scored with the raw, unscaled query operand.
+      float ow[G][2];
 #pragma unroll
-    for (int h = 0; h < G; ++h) st.ow[h][0] = st.ow[h][1] = 0.f;
+      for (int h = 0; h < G; ++h) ow[h][0] = ow[h][1] = 0.f;
+      if (wv1 > wv0) {
+        stage_q(args, lds, b, hq0, false);
+        build_q(cx, lds, false);
+        const size_t win_off = ((size_t)b * Hkv + kvh) * R * KVQ_D * (args.kv_f32 ? 4 : 2);
+        const int wend = (wv1 * KVQ_PAGE) < nw ? wv1 * KVQ_PAGE : nw;
+        for (int w = wv0 * KVQ_PAGE; w < wend; w += 32) {
+          if (args.kv_f32)
+            window_chunk<true>(cx, st, ow, args.cache.k_win + win_off, args.cache.v_win + win_off, w, wend);
+          else
+            window_chunk<false>(cx, st, ow, args.cache.k_win + win_off, args.cache.v_win + win_off, w, wend);
+        }
+      }
+      write_partial<true>(args, cx, st, ow, lds, b, hq0, split);
+      return;
+    }
+
+    stage_q(args, lds, b, hq0, args.rotation != 0);
+    build_q(cx, lds);
+    __syncthreads();  // the staging area is reused by the prefetch ring
 
     const int full_pages = nq / KVQ_PAGE;  // pages with all 16 tokens quantized
     const int qend = v1 < qpages ? v1 : qpages;
+    const uint8_t *pages = args.cache.pages;
+    // Block-table entries are wave-uniform: read them with scalar loads (constant address space) so
+    // that waiting for one never drains the vector-memory queue of prefetched pages.
+    typedef const __attribute__((address_space(4))) int32_t *const_i32p;
+    const_i32p btab = (const_i32p)args.cache.block_table;
+    const int64_t bt_row = (int64_t)b * args.cache.mbps;
+    const int64_t contig_base = ((int64_t)b * Hkv + kvh) * args.cache.pages_per_seq;
+    const int64_t pool_last = args.cache.pool_pages - 1;
+    const int paged = args.cache.paged;
     auto rec_ptr = [&](int p) -> const uint8_t * {
-      const int64_t ri = kvq_record_index(args.cache.paged, args.cache.block_table, args.cache.mbps,
-                                          args.cache.pages_per_seq, args.cache.pool_pages, Hkv, b, kvh, p);
-      return args.cache.pages + (size_t)ri * lay.record;
+      int64_t ri;
+      if (paged) {
+        int64_t e = btab[bt_row + p];
+        e = e < 0 ? 0 : (e > pool_last ? pool_last : e);
+        ri = e * Hkv + kvh;
+      } else {
+        ri = contig_base + p;
+      }
+      return pages + (size_t)ri * lay.record;
     };
     int p = v0;
-    // Fast path: pairs of full pages.
-    if (p + 1 < qend && p + 1 < full_pages) {
-      PageData A, B;
-      load_page(A, cx, rec_ptr(p), lay);
-      load_page(B, cx, rec_ptr(p + 1), lay);
-      while (true) {
-        const int pn = p + 2;
-        const bool more = (pn + 1 < qend) && (pn + 1 < full_pages);
-        PageData An, Bn;
-        if (more) {
-          load_page(An, cx, rec_ptr(pn), lay);
-          load_page(Bn, cx, rec_ptr(pn + 1), lay);
+    // Fast path: pairs of full pages, next pair prefetched while the current one is processed.
+    const int fast_end = qend < full_pages ? qend : full_pages;
+    const int npairs = fast_end > v0 ? (fast_end - v0) / 2 : 0;
+    if (npairs > 0) {
+      // Prefetch ring: pair j lives in slot j % NSLOT; NSLOT - 1 pairs are in flight while one is processed.
+      constexpr int DPP2 = 2 * DMAS_PER_PAGE;  // DMA instructions per pair
+      const int rec16 = lay.record / 16;
+      auto issue_pair = [&](int j) {
+        uint8_t *slot = smem + (j % NSLOT) * PAIR_BYTES;
+        dma_page(slot, rec_ptr(p + 2 * j), rec16, lane);
+        dma_page(slot + SLOT_PAGE_BYTES, rec_ptr(p + 2 * j + 1), rec16, lane);
+      };
+#pragma unroll
+      for (int j = 0; j < NSLOT - 1; ++j)
+        if (j < npairs) issue_pair(j);
+      for (int i = 0; i < npairs; ++i) {
+        // Slot (i + NSLOT - 1) % NSLOT held pair i - 1, whose reads completed before it was processed.
+        const int ahead = npairs - 1 - i;  // pairs still to be issued or in flight after pair i
+        if (i + NSLOT - 1 < npairs) {
+          issue_pair(i + NSLOT - 1);
+          wait_vmcnt<(NSLOT - 1) * DPP2>();
+        } else if (ahead >= 2 && NSLOT >= 3) {
+          wait_vmcnt<2 * DPP2>();
+        } else if (ahead >= 1) {
+          wait_vmcnt<DPP2>();
+        } else {
+          wait_vmcnt<0>();
         }
+        const uint8_t *slot = smem + (i % NSLOT) * PAIR_BYTES;
+        PageData A, B;
+        read_page(A, cx, slot, lay);
+        read_page(B, cx, slot + SLOT_PAGE_BYTES, lay);
         process_pair<false>(cx, st, A, B, 16, 16);
-        p = pn;
-        if (!more) break;
-        A = An;
-        B = Bn;
       }
+      p += 2 * npairs;
     }
     // Remaining quantized pages (partial page or an odd page): masked pairs.
-    while (p < qend) {
+    for (; p < qend; p += 2) {
       PageData A, B;
       const int va = (nq - p * KVQ_PAGE) < KVQ_PAGE ? (nq - p * KVQ_PAGE) : KVQ_PAGE;
       load_page(A, cx, rec_ptr(p), lay);
@@ -587,39 +893,31 @@ struct Kern {
         zero_page(B);
       }
       process_pair<true>(cx, st, A, B, va, vb);
-      p += 2;
     }
-    // Window pages of this split.
-    const int wv0 = (v0 > qpages ? v0 : qpages) - qpages;
-    const int wv1 = v1 - qpages;
-    if (wv1 > wv0) {
-      if (args.rotation) build_q(cx, qraw);  // window keys are stored unrotated
-      const size_t win_off = ((size_t)b * Hkv + kvh) * R * KVQ_D * (args.kv_f32 ? 4 : 2);
-      const int wend = (wv1 * KVQ_PAGE) < nw ? wv1 * KVQ_PAGE : nw;
-      for (int w = wv0 * KVQ_PAGE; w < wend; w += 32)
-        window_chunk(cx, st, args.cache.k_win + win_off, args.cache.v_win + win_off, args.kv_f32, w, wend);
-    }
+    write_partial<false>(args, cx, st, nullptr, lds, b, hq0, split);
+  }
 
-    // ---- reduce and write this split's partial result -------------------------
-    float l = st.l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+  // Reduce the state across rows/replicas and write this split's partial result:
+  // [m (log2 units), l, 0, 0, o[128]] per query head, o unnormalised.
+  template <bool WIN>
+  static __device__ __forceinline__ void write_partial(const KvqAttnArgs &args, const Ctx &cx, const State<NVG> &st,
+                                                       float (*ow)[2], float *lds, int b, int hq0, int split) {
+    const int lane = threadIdx.x;
+    const float l = rows_sum(st.l);
     float z[NVG];
 #pragma unroll
-    for (int v = 0; v < NVG; ++v) {
-      z[v] = st.zacc[v];
-      z[v] += __shfl_xor(z[v], 16);
-      z[v] += __shfl_xor(z[v], 32);
-    }
+    for (int v = 0; v < NVG; ++v) z[v] = WIN ? 0.f : rows_sum(st.zacc[v]);
     __syncthreads();
-    float *accs = lds;                   // [2G][128]
-    float *hdr = lds + 2 * G * KVQ_D;    // [G][4]: m, l, z0, z1
+    float *accs = lds;                 // [2G][128]
+    float *hdr = lds + 2 * G * KVQ_D;  // [G][4]: m, l, z0, z1
+    if constexpr (!WIN) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+      for (int m = 0; m < 8; ++m) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * cx.quad + r;
-        if (row < 2 * G) accs[row * KVQ_D + 16 * m + cx.col] = st.acc[m][r];
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * cx.quad + r;
+          if (row < 2 * G) accs[row * KVQ_D + 16 * m + cx.col] = st.acc[m][r];
+        }
       }
     }
     if (lane < G) {
@@ -630,6 +928,7 @@ struct Kern {
     }
     __syncthreads();
     const int vshift = (NVG == 1) ? 7 : 6;  // channel -> value group
+    const int S = args.splits;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float *dst = args.partials + (((size_t)b * args.Hq + hq0 + h) * S + split) * KVQ_PART_STRIDE;
@@ -637,8 +936,13 @@ struct Kern {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int c = 2 * lane + e;
-        const float a = accs[h * KVQ_D + c] + accs[(G + h) * KVQ_D + c];
-        o[e] = __builtin_fmaf(a, EXP2_OUT, hdr[h * 4 + 2 + (c >> vshift)]) + st.ow[h][e];
+        if constexpr (WIN) {
+          o[e] = ow[h][e];
+        } else {
+          const float a = accs[h * KVQ_D + c] + accs[(G + h) * KVQ_D + c];
+          const float outscale = __builtin_amdgcn_ldexpf(1.0f, (int)P_BIAS_LOG2 - vtile_scale(c >> 4));
+          o[e] = __builtin_fmaf(a * EXP2_OUT, outscale, hdr[h * 4 + 2 + (c >> vshift)]);
+        }
       }
       reinterpret_cast<float2 *>(dst + 4)[lane] = make_float2(o[0], o[1]);
       if (lane == 0) {
@@ -653,8 +957,8 @@ struct Kern {
 
 template <int KB, int VB, int G, int P, int NVG>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_WPE))) void kvq_attn_split_kernel(KvqAttnArgs args) {
-  __shared__ float lds[2 * 8 * KVQ_D + 8 * 4];
-  Kern<KB, VB, G, P, NVG>::run(args, lds);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Kern<KB, VB, G, P, NVG>::LDS_BYTES];
+  Kern<KB, VB, G, P, NVG>::run(args, smem);
 }
 
 }  // namespace kvq_attn

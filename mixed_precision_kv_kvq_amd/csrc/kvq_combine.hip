@@ -28,26 +28,53 @@ hipError_t launch_k8v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t 
 
 namespace {
 
+// One wave per (sequence, query head).  Split headers are read lane-parallel
+// (lane s holds split s), the weights 2^(m_s - M) are broadcast with readlane,
+// and the accumulator rows are loaded several splits at a time.
 __global__ __launch_bounds__(64) void kvq_combine_kernel(KvqCombineArgs a) {
   const int lane = threadIdx.x;
   const size_t bh = blockIdx.x;
   const float *base = a.partials + bh * (size_t)a.splits * KVQ_PART_STRIDE;
   const float ninf = -__builtin_inff();
   float M = ninf;
-  for (int s = 0; s < a.splits; ++s) M = __builtin_fmaxf(M, base[(size_t)s * KVQ_PART_STRIDE]);
-  float o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < a.splits; s0 += 64) {
+    const int s = s0 + lane;
+    const float ms = s < a.splits ? base[(size_t)s * KVQ_PART_STRIDE] : ninf;
+    M = __builtin_fmaxf(M, ms);
+  }
+  for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
+  float o0 = 0.f, o1 = 0.f, l = 0.f;
   if (M != ninf) {
-    float l = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float *ps = base + (size_t)s * KVQ_PART_STRIDE;
-      const float ms = ps[0];
-      if (ms == ninf) continue;
-      const float w = __builtin_amdgcn_exp2f(ms - M);
-      l = __builtin_fmaf(ps[1], w, l);
-      const float2 acc = reinterpret_cast<const float2 *>(ps + 4)[lane];
-      o0 = __builtin_fmaf(acc.x, w, o0);
-      o1 = __builtin_fmaf(acc.y, w, o1);
+    for (int s0 = 0; s0 < a.splits; s0 += 64) {
+      const int s = s0 + lane;
+      float w = 0.f;
+      if (s < a.splits) {
+        const float ms = base[(size_t)s * KVQ_PART_STRIDE];
+        w = (ms == ninf) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        l = __builtin_fmaf(base[(size_t)s * KVQ_PART_STRIDE + 1], w, l);
+      }
+      const int n = (a.splits - s0) < 64 ? (a.splits - s0) : 64;
+      int j = 0;
+      for (; j + 8 <= n; j += 8) {
+        float2 acc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          acc[u] = reinterpret_cast<const float2 *>(base + (size_t)(s0 + j + u) * KVQ_PART_STRIDE + 4)[lane];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+          o0 = __builtin_fmaf(acc[u].x, wj, o0);
+          o1 = __builtin_fmaf(acc[u].y, wj, o1);
+        }
+      }
+      for (; j < n; ++j) {
+        const float2 acc = reinterpret_cast<const float2 *>(base + (size_t)(s0 + j) * KVQ_PART_STRIDE + 4)[lane];
+        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+        o0 = __builtin_fmaf(acc.x, wj, o0);
+        o1 = __builtin_fmaf(acc.y, wj, o1);
+      }
     }
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
     o0 = o0 / l;
     o1 = o1 / l;
   }
@@ -62,6 +89,7 @@ __global__ __launch_bounds__(64) void kvq_combine_kernel(KvqCombineArgs a) {
 
 hipError_t kvq_launch_combine(const KvqCombineArgs &a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
   hipLaunchKernelGGL(kvq_combine_kernel, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(64) void kvq_debug_kernel(KvqDebugArgs a) {
 hipError_t kvq_launch_debug(const KvqDebugArgs &a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   dim3 grid((unsigned)a.n, (unsigned)a.Hkv);
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
   hipLaunchKernelGGL(kvq_debug_kernel, grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }

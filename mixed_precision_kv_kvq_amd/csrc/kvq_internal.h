@@ -37,7 +37,8 @@ struct KvqAttnArgs {
   const void *q;
   float *partials;  // [B][Hq][S][KVQ_PART_STRIDE]
   int32_t q_f32, kv_f32, Hq, Hkv, R, rotation;
-  int32_t splits, pages_per_split;
+  int32_t splits, pages_per_split;  // all splits; quantized pages per quantized split
+  int32_t wsplits;                   // leading splits that cover the recent window, KVQ_WIN_PAGES pages each
   int32_t max_len;  // host-validated upper bound of seq_lens (device lengths are clamped to it)
   float sigma_u;  // softmax_scale * log2(e) * 2^33
 };
@@ -59,7 +60,38 @@ struct KvqDebugArgs {
   float *k_hat, *v_hat;
 };
 
-#define KVQ_PART_STRIDE 132  // floats per partial: m, l, pad, pad, acc[128]
+#define KVQ_PART_STRIDE 132
+#define KVQ_WIN_PAGES 8  // window pages (128 tokens) per window split
+
+// Waves per SIMD the split kernel is compiled for (register budget 512 / KVQ_WPE).
+#ifndef KVQ_WPE
+#define KVQ_WPE 3
+#endif
+
+#define KVQ_LDS_PER_CU (160 * 1024)
+
+// Page-pair slots of the split kernel's LDS prefetch ring for a given pair size:
+// as many as fit in the LDS share of one wave at the compiled occupancy, 2..4.
+__host__ __device__ constexpr int kvq_ring_slots(int pair_bytes) {
+  return (KVQ_LDS_PER_CU / (4 * KVQ_WPE)) / pair_bytes < 2
+             ? 2
+             : ((KVQ_LDS_PER_CU / (4 * KVQ_WPE)) / pair_bytes > 4 ? 4 : (KVQ_LDS_PER_CU / (4 * KVQ_WPE)) / pair_bytes);
+}
+
+// LDS bytes of one split-kernel workgroup (one wave) for key/value bit widths and value groups.
+__host__ __device__ constexpr int kvq_attn_lds_bytes(int kb, int vb, int nvg) {
+  return (2 * (((16 * kb + 16 + 16 * vb + 4 * nvg) + 63) / 64) * 1024) * kvq_ring_slots(2 * (((16 * kb + 16 + 16 * vb + 4 * nvg) + 63) / 64) * 1024) >
+                 (2 * 8 * 128 + 8 * 4) * 4
+             ? (2 * (((16 * kb + 16 + 16 * vb + 4 * nvg) + 63) / 64) * 1024) *
+                   kvq_ring_slots(2 * (((16 * kb + 16 + 16 * vb + 4 * nvg) + 63) / 64) * 1024)
+             : (2 * 8 * 128 + 8 * 4) * 4;
+}
+
+// Resident split-kernel waves per CU: the register limit or the LDS limit.
+__host__ __device__ constexpr int kvq_attn_waves_per_cu(int kb, int vb, int nvg) {
+  return (4 * KVQ_WPE) < (KVQ_LDS_PER_CU / kvq_attn_lds_bytes(kb, vb, nvg)) ? 4 * KVQ_WPE
+                                                                           : KVQ_LDS_PER_CU / kvq_attn_lds_bytes(kb, vb, nvg);
+}  // floats per partial: m, l, pad, pad, acc[128]
 
 hipError_t kvq_launch_append(const KvqAppendArgs &a, hipStream_t s);
 hipError_t kvq_launch_attention(const KvqAttnArgs &a, int g, int q_parts, hipStream_t s);

@@ -153,3 +153,32 @@ def test_workspace_grows_with_length_and_split_override(monkeypatch):
     monkeypatch.setenv("KVQ_PAGES_PER_SPLIT", "2")
     c = K.kvq_decode_workspace_bytes(prm, 16, 32768)
     assert c > a
+
+
+@pytest.mark.parametrize("window,batch,heads", [(0, 1, 8), (128, 16, 8), (40, 3, 2), (16, 64, 8)])
+def test_workspace_is_monotone_in_length(window, batch, heads, monkeypatch):
+    """A workspace sized for a maximum length serves every shorter length: the size never drops as the
+    length grows (the split count of a shorter length can exceed that of a longer one, the size covers both)."""
+    prm = p(window=window, num_kv_heads=heads, num_q_heads=4 * heads)
+    for env in (None, "6"):
+        if env:
+            monkeypatch.setenv("KVQ_PAGES_PER_SPLIT", env)
+        prev = 0
+        for L in list(range(0, 3000)) + list(range(3000, 300000, 997)):
+            w = K.kvq_decode_workspace_bytes(prm, batch, L)
+            assert w >= prev, (L, w, prev)
+            prev = w
+
+
+def test_package_shares_torchs_hip_runtime():
+    """Importing the package first must not map a second HIP runtime beside torch's (a second
+    runtime finds no device).  Checked in a fresh interpreter, where the import order is ours."""
+    import subprocess
+    import sys
+
+    code = ("import mixed_precision_kv_kvq_amd, workloads.device, torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

@@ -69,6 +69,7 @@ extern "C" int kvq_gen_kv(void *out, int out_f32, uint64_t key, const float *sig
                           int Hkv, int64_t t0, int d, hipStream_t stream) {
   const int64_t total = (int64_t)B * n * Hkv * d;
   if (total <= 0) return 0;
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
   hipLaunchKernelGGL(gen_kv_kernel, dim3(grid_for(total)), dim3(256), 0, stream, out, out_f32, key, sigma, table, B,
                      n, Hkv, t0, d);
   return (int)hipGetLastError();
@@ -78,6 +79,7 @@ extern "C" int kvq_gen_q(void *out, int out_f32, uint64_t key, const float *tabl
                          hipStream_t stream) {
   const int64_t total = (int64_t)B * Hq * d;
   if (total <= 0) return 0;
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
   hipLaunchKernelGGL(gen_q_kernel, dim3(grid_for(total)), dim3(256), 0, stream, out, out_f32, key, table, B, Hq, d,
                      step);
   return (int)hipGetLastError();
