@@ -129,7 +129,9 @@ kvq_status kvq_quantize_append(const kvq_params *params, const kvq_cache *cache,
                                const int32_t *n_new_per_seq, const void *k_new, const void *v_new, int32_t n_new,
                                hipStream_t stream);
 
-/* Workspace bytes that kvq_decode_attention needs for this batch and maximum length. */
+/* Workspace bytes that kvq_decode_attention needs for this batch and maximum length.
+ * Never decreases as max_seq_len grows, so a workspace sized for the largest length
+ * serves every shorter one.  Returns 0 for invalid or unsupported parameters. */
 size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len);
 
 /* Decode attention of one new query per sequence over its whole cache, with
@@ -140,8 +142,15 @@ size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64
  *   q:           device [batch][num_q_heads][128] of q_dtype.
  *   out:         device [batch][num_q_heads][128] of out_dtype; fp32 accumulation.
  *   softmax_scale: 0 means 1/sqrt(128).
- *   workspace:   device scratch of at least kvq_decode_workspace_bytes(...) bytes.
- * A sequence of length 0 gets an all-zero output. */
+ *   workspace:   device scratch of at least kvq_decode_workspace_bytes(...) bytes, 16-byte
+ *                aligned, owned by the caller; no initial contents needed.  Calls that share
+ *                a workspace must be ordered (same stream).
+ * Two kernel launches: the split-K kernel writes per-split partial results into the
+ * workspace, a second kernel merges them into `out`.
+ * A sequence of length 0 gets an all-zero output.  Errors: KVQ_EINVAL (null or misaligned
+ * pointers, bad dtype or scale), KVQ_ENOSPACE (workspace too small, max_seq_len beyond
+ * the capacity), KVQ_EUNSUPPORTED (parameters outside the supported set), KVQ_EHIP
+ * (launch failure); nothing is launched on an error. */
 kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
                                 int64_t max_seq_len, const void *q, int32_t q_dtype, void *out, int32_t out_dtype,
                                 float softmax_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);

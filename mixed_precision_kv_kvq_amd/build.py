@@ -11,6 +11,7 @@ import argparse
 import concurrent.futures as cf
 import glob
 import os
+import re
 import subprocess
 import sys
 import time
@@ -56,6 +57,20 @@ def _run(cmd):
     return p.returncode, out, time.time() - t0
 
 
+def _spills(out: str) -> list:
+    """Split-kernel instantiations that use scratch, from -Rpass-analysis=kernel-resource-usage remarks."""
+    bad, name = [], None
+    for line in out.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and "kvq_attn_split_kernel" in name and int(m.group(1)) > 0:
+            bad.append((name, int(m.group(1))))
+    return bad
+
+
 def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> None:
     """Compile every HIP source for gfx950 and link the shared libraries."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -69,12 +84,19 @@ def build(force: bool = True, jobs: int | None = None, verbose: bool = False) ->
     jobs = jobs or min(16, os.cpu_count() or 4)
     errors = []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = {ex.submit(_run, [HIPCC, *COMMON, "-c", s, "-o", o]): s for s, o in todo}
+        # The attention instantiations report their register use; a spill there is a build error.
+        futs = {ex.submit(_run, [HIPCC, *COMMON, *(["-Rpass-analysis=kernel-resource-usage"] if "inst" in s else []),
+                                 "-c", s, "-o", o]): s for s, o in todo}
         for f in cf.as_completed(futs):
             rc, out, dt = f.result()
+            spills = _spills(out)
             if verbose or rc:
-                print(f"[build] {os.path.basename(futs[f])} rc={rc} {dt:.1f}s\n{out}", file=sys.stderr)
-            if rc:
+                shown = "\n".join(l for l in out.splitlines() if "remark:" not in l)
+                print(f"[build] {os.path.basename(futs[f])} rc={rc} {dt:.1f}s\n{shown}", file=sys.stderr)
+            if spills:
+                print(f"[build] {os.path.basename(futs[f])}: scratch in {spills}", file=sys.stderr)
+                os.remove(_obj_path(futs[f]))
+            if rc or spills:
                 errors.append(futs[f])
     if errors:
         raise RuntimeError(f"hipcc failed for: {errors}")

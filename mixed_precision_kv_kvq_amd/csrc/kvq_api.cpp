@@ -65,7 +65,7 @@ struct SplitPlan {
   int bound;  // most splits any length <= max_seq_len can get (workspace size)
 };
 
-SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len) {
+SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, int q_parts) {
   const int R = p->window;
   const int64_t nq = max_seq_len > R ? max_seq_len - R : 0;
   const int64_t nw = max_seq_len < R ? max_seq_len : R;
@@ -78,7 +78,8 @@ SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len) {
   if (const char *env = getenv("KVQ_PAGES_PER_SPLIT")) per = atoll(env);
   const bool fixed = per > 0;
   if (!fixed) {
-    int64_t target = (int64_t)kNumCUs * kvq_attn_waves_per_cu(p->k_bits, p->v_bits, KVQ_D / p->v_group);
+    const int g = p->num_q_heads / p->num_kv_heads;
+    int64_t target = (int64_t)kNumCUs * kvq_attn_waves_per_cu(p->k_bits, p->v_bits, KVQ_D / p->v_group, g, q_parts);
     if (const char *env = getenv("KVQ_TARGET_WAVES")) target = atoll(env) > 0 ? atoll(env) : target;
     // quantized splits per unit: at most ceil(target / units) - wsplits, at least 1
     cap = (target + units - 1) / units - sp.wsplits;
@@ -149,8 +150,10 @@ kvq_status kvq_quantize_append(const kvq_params *params, const kvq_cache *cache,
 
 size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len) {
   if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0) return 0;
-  const SplitPlan sp = split_plan(params, batch, max_seq_len);
-  return (size_t)batch * params->num_q_heads * (size_t)sp.bound * KVQ_PART_STRIDE * sizeof(float);
+  // The query dtype is not known here: cover both query-part counts.
+  const SplitPlan s1 = split_plan(params, batch, max_seq_len, 1), s2 = split_plan(params, batch, max_seq_len, 2);
+  const int bound = s1.bound > s2.bound ? s1.bound : s2.bound;
+  return (size_t)batch * params->num_q_heads * (size_t)bound * KVQ_PART_STRIDE * sizeof(float);
 }
 
 kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
@@ -183,15 +186,14 @@ kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache
   a.Hkv = params->num_kv_heads;
   a.R = params->window;
   a.rotation = params->key_rotation;
-  const SplitPlan sp = split_plan(params, cache->batch, max_seq_len);
+  const int q_parts = (q_dtype == KVQ_BF16 && !params->key_rotation) ? 1 : 2;
+  const SplitPlan sp = split_plan(params, cache->batch, max_seq_len, q_parts);
   a.splits = sp.splits;
   a.wsplits = sp.wsplits;
-  a.pages_per_split = sp.pps;
   a.max_len = (int32_t)(max_seq_len < INT32_MAX ? max_seq_len : INT32_MAX);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
   a.sigma_u = (float)((double)scale * 1.4426950408889634 * 8589934592.0);  // * log2(e) * 2^33
   const int g = params->num_q_heads / params->num_kv_heads;
-  const int q_parts = (q_dtype == KVQ_BF16 && !params->key_rotation) ? 1 : 2;
   hipError_t e = kvq_launch_attention(a, g, q_parts, stream);
   if (e != hipSuccess) return KVQ_EHIP;
   KvqCombineArgs c;

@@ -274,7 +274,49 @@ struct Kern {
   // (code_scaled), entries of slots whose codes are read scaled by 2^k are
   // divided by 2^k (exact); raw window keys need the unscaled operand.
   static __device__ __forceinline__ void build_q(Ctx &cx, const float *qs, bool code_scaled = true) {
-    const int y = cx.col / G, h = cx.col % G;
+    const int h = cx.col % G;
+    build_q_with(cx, [&](int, int, int ch) { return qs[h * KVQ_D + ch]; }, code_scaled);
+  }
+
+  // This lane's query channels 32 kc + 8 quad + j (j < 8, all four kc) of its head, straight
+  // from global memory: 16-byte loads, fp32 or bf16 as stored.
+  struct QRegs {
+    u32x4 v[4][2];
+  };
+  static __device__ __forceinline__ void load_q_regs(QRegs &qr, const KvqAttnArgs &args, const Ctx &cx, int b,
+                                                     int hq0) {
+    const uint8_t *row =
+        (const uint8_t *)args.q + ((size_t)b * args.Hq + hq0 + cx.col % G) * KVQ_D * (args.q_f32 ? 4 : 2);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int ch = 32 * kc + 8 * cx.quad;
+      if (args.q_f32) {
+        qr.v[kc][0] = gload<u32x4>(row + 4 * ch);
+        qr.v[kc][1] = gload<u32x4>(row + 4 * ch + 16);
+      } else {
+        qr.v[kc][0] = gload<u32x4>(row + 2 * ch);
+      }
+    }
+  }
+  static __device__ __forceinline__ void build_q_regs(Ctx &cx, const QRegs &qr, bool q_f32) {
+    build_q_with(
+        cx,
+        [&](int kc, int j, int) {
+          // (copy the vector element out first: a bit cast of the element lvalue itself
+          // reads the vector's first element)
+          const uint32_t u = qr.v[kc][j >> 2][j & 3];
+          if (q_f32) return __builtin_bit_cast(float, u);
+          const uint32_t w = qr.v[kc][0][j >> 1];
+          return kvq_bf16_bits_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFF));
+        },
+        true);
+  }
+
+  // Shared body: getq(kc, j, ch) returns this lane's head's query (fp32) at channel
+  // ch = 32 kc + 8 quad + j.
+  template <class GetQ>
+  static __device__ __forceinline__ void build_q_with(Ctx &cx, GetQ getq, bool code_scaled) {
+    const int y = cx.col / G;
     const int part = y / X, x = y % X;
     const bool valid = x < XE;
     float qsum[NACC];
@@ -287,8 +329,8 @@ struct Kern {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ch = 32 * kc + 8 * cx.quad + 2 * i;
-        const float v0 = use ? qs[h * KVQ_D + ch] * EXP2_EQ : 0.f;
-        const float v1 = use ? qs[h * KVQ_D + ch + 1] * EXP2_EQ : 0.f;
+        const float v0 = use ? getq(kc, 2 * i, ch) * EXP2_EQ : 0.f;
+        const float v1 = use ? getq(kc, 2 * i + 1, ch + 1) * EXP2_EQ : 0.f;
         uint32_t pr = pack_bf16x2(v0, v1);
         if (P == 2) {
           const uint32_t lo = pack_bf16x2(v0 - bf16lo_f32(pr), v1 - bf16hi_f32(pr));
@@ -510,22 +552,41 @@ struct Kern {
   }
 
   // ---- LDS ring -------------------------------------------------------------
-  static constexpr int MAX_REC16 = 16 * KB + 16 + 16 * VB + 4 * NVG;  // record in 16-byte units (k_group 32)
+  static constexpr int MAX_REC16 = kvq_rec16(KB, VB, NVG);  // record in 16-byte units (k_group 32)
+  static constexpr int REC_BYTES = 16 * MAX_REC16;              // ring slot stride
   static constexpr int DMAS_PER_PAGE = (MAX_REC16 + 63) / 64;
-  static constexpr int SLOT_PAGE_BYTES = DMAS_PER_PAGE * 1024;
-  static constexpr int PAIR_BYTES = 2 * SLOT_PAGE_BYTES;
-  static constexpr int NSLOT = kvq_ring_slots(PAIR_BYTES);
-  static constexpr int STAGE_BYTES = (2 * 8 * KVQ_D + 8 * 4) * 4;  // query / accumulator staging
-  static constexpr int LDS_BYTES = NSLOT * PAIR_BYTES > STAGE_BYTES ? NSLOT * PAIR_BYTES : STAGE_BYTES;
-  static_assert(LDS_BYTES == kvq_attn_lds_bytes(KB, VB, NVG), "host and device LDS sizing disagree");
+  static constexpr int WPE = kvq_attn_wpe(KB, VB, G, P, NVG);       // waves per SIMD
+  static constexpr int NPS = kvq_ring_pages(REC_BYTES, WPE);   // page slots
+  static constexpr int AHEAD = NPS - 2;                         // pages in flight while a pair is processed
+  static constexpr int LDS_BYTES = kvq_attn_lds_bytes(KB, VB, NVG, WPE);
+  static_assert(LDS_BYTES >= NPS * REC_BYTES && LDS_BYTES >= KVQ_STAGE_BYTES, "LDS sizing");
+  static_assert(AHEAD * DMAS_PER_PAGE <= 63, "vmcnt range");
 
-  // Copy one page record into an LDS slot page (DMAS_PER_PAGE wave-wide DMAs).
-  static __device__ __forceinline__ void dma_page(uint8_t *slot_page, const uint8_t *rec, int rec16, int lane) {
+  // Copy one page record into an LDS slot: DMAS_PER_PAGE wave-wide DMAs, lane l of DMA k
+  // writing slot chunk 64k + l.  Lanes past the slot (MAX_REC16 chunks) stay idle, which
+  // leaves at least one active lane in every DMA so that each one is counted by vmcnt;
+  // lanes past a shorter record (larger key groups) re-read its last chunk.
+  static __device__ __forceinline__ void dma_page(uint8_t *slot, const uint8_t *rec, int rec16, int lane) {
 #pragma unroll
     for (int k = 0; k < DMAS_PER_PAGE; ++k) {
       int c = 64 * k + lane;
       c = c < rec16 ? c : rec16 - 1;
-      __builtin_amdgcn_global_load_lds((const void *)(rec + 16 * c), (lds_vptr)(slot_page + 1024 * k), 16, 0, 0);
+      if (k + 1 < DMAS_PER_PAGE || lane < MAX_REC16 - 64 * k)
+        __builtin_amdgcn_global_load_lds((const void *)(rec + 16 * c), (lds_vptr)(slot + 1024 * k), 16, 0, 0);
+    }
+  }
+
+  // Wait until at most n pages (n <= AHEAD) of DMAs are outstanding.
+  static __device__ __forceinline__ void wait_pages(int n) {
+    static_assert(AHEAD <= 6, "wait_pages cases");
+    switch (n) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<(AHEAD >= 1 ? 1 : 0) * DMAS_PER_PAGE>(); break;
+      case 2: wait_vmcnt<(AHEAD >= 2 ? 2 : 0) * DMAS_PER_PAGE>(); break;
+      case 3: wait_vmcnt<(AHEAD >= 3 ? 3 : 0) * DMAS_PER_PAGE>(); break;
+      case 4: wait_vmcnt<(AHEAD >= 4 ? 4 : 0) * DMAS_PER_PAGE>(); break;
+      case 5: wait_vmcnt<(AHEAD >= 5 ? 5 : 0) * DMAS_PER_PAGE>(); break;
+      default: wait_vmcnt<(AHEAD >= 6 ? 6 : 0) * DMAS_PER_PAGE>(); break;
     }
   }
 
@@ -776,13 +837,10 @@ struct Kern {
     const int wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;
     // Window splits first, then quantized splits (see the host split plan).
     const bool win_split = split < args.wsplits;
-    int v0 = 0, v1 = 0, wv0 = 0, wv1 = 0;
+    int wv0 = 0, wv1 = 0;
     if (win_split) {
       wv0 = split * KVQ_WIN_PAGES;
       wv1 = wv0 + KVQ_WIN_PAGES < wpages ? wv0 + KVQ_WIN_PAGES : wpages;
-    } else {
-      v0 = (split - args.wsplits) * args.pages_per_split;
-      v1 = v0 + args.pages_per_split < qpages ? v0 + args.pages_per_split : qpages;
     }
 
     Ctx cx;
@@ -813,16 +871,16 @@ struct Kern {
             window_chunk<false>(cx, st, ow, args.cache.k_win + win_off, args.cache.v_win + win_off, w, wend);
         }
       }
-      write_partial<true>(args, cx, st, ow, lds, b, hq0, split);
+      write_partial<true>(args, cx, st, ow, lds, b, kvh, split);
       return;
     }
 
-    stage_q(args, lds, b, hq0, args.rotation != 0);
-    build_q(cx, lds);
-    __syncthreads();  // the staging area is reused by the prefetch ring
-
+    // Quantized splits take full-page pairs round-robin: pair sq, sq + SQ, sq + 2 SQ, ... so that at
+    // any moment the waves of one unit read neighbouring pairs.  The 1-2 pages after the last full
+    // pair (an odd full page and/or the partial page) go to the split next in the rotation.
+    const int SQ = S - args.wsplits, sq = split - args.wsplits;
     const int full_pages = nq / KVQ_PAGE;  // pages with all 16 tokens quantized
-    const int qend = v1 < qpages ? v1 : qpages;
+    const int tp = full_pages / 2;         // full pairs of this sequence
     const uint8_t *pages = args.cache.pages;
     // Block-table entries are wave-uniform: read them with scalar loads (constant address space) so
     // that waiting for one never drains the vector-memory queue of prefetched pages.
@@ -843,45 +901,53 @@ struct Kern {
       }
       return pages + (size_t)ri * lay.record;
     };
-    int p = v0;
-    // Fast path: pairs of full pages, next pair prefetched while the current one is processed.
-    const int fast_end = qend < full_pages ? qend : full_pages;
-    const int npairs = fast_end > v0 ? (fast_end - v0) / 2 : 0;
+    // Fast path: pairs of full pages, next pairs prefetched while the current one is processed.
+    const int npairs = tp > sq ? (tp - sq + SQ - 1) / SQ : 0;
     if (npairs > 0) {
-      // Prefetch ring: pair j lives in slot j % NSLOT; NSLOT - 1 pairs are in flight while one is processed.
-      constexpr int DPP2 = 2 * DMAS_PER_PAGE;  // DMA instructions per pair
+      // Prefetch ring of NPS page slots: local page k (pair k / 2) lives in slot k % NPS.  The
+      // prologue requests pages 0..AHEAD-1; processing pair i first requests pages 2i + AHEAD and
+      // 2i + AHEAD + 1, whose slots held pair i - 1 (already read), then waits for pages 2i, 2i + 1.
       const int rec16 = lay.record / 16;
-      auto issue_pair = [&](int j) {
-        uint8_t *slot = smem + (j % NSLOT) * PAIR_BYTES;
-        dma_page(slot, rec_ptr(p + 2 * j), rec16, lane);
-        dma_page(slot + SLOT_PAGE_BYTES, rec_ptr(p + 2 * j + 1), rec16, lane);
+      const int npages = 2 * npairs;
+      auto issue_page = [&](int k) {
+        const int pg = 2 * (sq + (k >> 1) * SQ) + (k & 1);
+        dma_page(smem + (k % NPS) * REC_BYTES, rec_ptr(pg), rec16, lane);
       };
+      // The query operand is built while the first pages stream in: without rotation the
+      // query loads are issued before the prologue DMAs (vmcnt retires them first); with
+      // rotation the query is staged and rotated through LDS before the ring is used.
+      QRegs qr;
+      if (args.rotation) {
+        stage_q(args, lds, b, hq0, true);
+        build_q(cx, lds);
+        __syncthreads();  // the staging area is reused by the prefetch ring
+      } else {
+        load_q_regs(qr, args, cx, b, hq0);
+      }
 #pragma unroll
-      for (int j = 0; j < NSLOT - 1; ++j)
-        if (j < npairs) issue_pair(j);
+      for (int k = 0; k < AHEAD; ++k)
+        if (k < npages) issue_page(k);
+      if (!args.rotation) build_q_regs(cx, qr, args.q_f32);
       for (int i = 0; i < npairs; ++i) {
-        // Slot (i + NSLOT - 1) % NSLOT held pair i - 1, whose reads completed before it was processed.
-        const int ahead = npairs - 1 - i;  // pairs still to be issued or in flight after pair i
-        if (i + NSLOT - 1 < npairs) {
-          issue_pair(i + NSLOT - 1);
-          wait_vmcnt<(NSLOT - 1) * DPP2>();
-        } else if (ahead >= 2 && NSLOT >= 3) {
-          wait_vmcnt<2 * DPP2>();
-        } else if (ahead >= 1) {
-          wait_vmcnt<DPP2>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        const uint8_t *slot = smem + (i % NSLOT) * PAIR_BYTES;
+        const int k0 = 2 * i + AHEAD;
+        if (k0 < npages) issue_page(k0);
+        if (k0 + 1 < npages) issue_page(k0 + 1);
+        const int issued = k0 + 2 < npages ? k0 + 2 : npages;
+        wait_pages(issued - (2 * i + 2));
         PageData A, B;
-        read_page(A, cx, slot, lay);
-        read_page(B, cx, slot + SLOT_PAGE_BYTES, lay);
+        read_page(A, cx, smem + ((2 * i) % NPS) * REC_BYTES, lay);
+        read_page(B, cx, smem + ((2 * i + 1) % NPS) * REC_BYTES, lay);
         process_pair<false>(cx, st, A, B, 16, 16);
       }
-      p += 2 * npairs;
     }
-    // Remaining quantized pages (partial page or an odd page): masked pairs.
-    for (; p < qend; p += 2) {
+    // Remaining quantized pages (an odd full page and/or the partial page): one masked pair.
+    const int qend = qpages;
+    const bool tail = sq == tp % SQ && 2 * tp < qend;
+    if (tail && npairs == 0) {  // the query operand was not built in the fast path
+      stage_q(args, lds, b, hq0, args.rotation != 0);
+      build_q(cx, lds);
+    }
+    for (int p = 2 * tp; tail && p < qend; p += 2) {
       PageData A, B;
       const int va = (nq - p * KVQ_PAGE) < KVQ_PAGE ? (nq - p * KVQ_PAGE) : KVQ_PAGE;
       load_page(A, cx, rec_ptr(p), lay);
@@ -894,15 +960,16 @@ struct Kern {
       }
       process_pair<true>(cx, st, A, B, va, vb);
     }
-    write_partial<false>(args, cx, st, nullptr, lds, b, hq0, split);
+    write_partial<false>(args, cx, st, nullptr, lds, b, kvh, split);
   }
 
   // Reduce the state across rows/replicas and write this split's partial result:
   // [m (log2 units), l, 0, 0, o[128]] per query head, o unnormalised.
   template <bool WIN>
   static __device__ __forceinline__ void write_partial(const KvqAttnArgs &args, const Ctx &cx, const State<NVG> &st,
-                                                       float (*ow)[2], float *lds, int b, int hq0, int split) {
+                                                       float (*ow)[2], float *lds, int b, int kvh, int split) {
     const int lane = threadIdx.x;
+    const int hq0 = kvh * G;
     const float l = rows_sum(st.l);
     float z[NVG];
 #pragma unroll
@@ -956,7 +1023,7 @@ struct Kern {
 };
 
 template <int KB, int VB, int G, int P, int NVG>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_WPE))) void kvq_attn_split_kernel(KvqAttnArgs args) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kvq_attn_wpe(KB, VB, G, P, NVG)))) void kvq_attn_split_kernel(KvqAttnArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Kern<KB, VB, G, P, NVG>::LDS_BYTES];
   Kern<KB, VB, G, P, NVG>::run(args, smem);
 }

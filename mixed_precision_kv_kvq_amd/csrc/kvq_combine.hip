@@ -28,53 +28,49 @@ hipError_t launch_k8v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t 
 
 namespace {
 
-// One wave per (sequence, query head).  Split headers are read lane-parallel
-// (lane s holds split s), the weights 2^(m_s - M) are broadcast with readlane,
-// and the accumulator rows are loaded several splits at a time.
+// One wave per (sequence, query head).  Splits are taken 32 at a time: the
+// headers (lane s holds split s) and all 32 accumulator rows are requested
+// before any is used, so a chunk costs one memory round trip; chunks are
+// merged online (running max M, sum l and output o rescaled as M grows).
+constexpr int kChunk = 32;
+
 __global__ __launch_bounds__(64) void kvq_combine_kernel(KvqCombineArgs a) {
   const int lane = threadIdx.x;
   const size_t bh = blockIdx.x;
   const float *base = a.partials + bh * (size_t)a.splits * KVQ_PART_STRIDE;
   const float ninf = -__builtin_inff();
-  float M = ninf;
-  for (int s0 = 0; s0 < a.splits; s0 += 64) {
-    const int s = s0 + lane;
-    const float ms = s < a.splits ? base[(size_t)s * KVQ_PART_STRIDE] : ninf;
-    M = __builtin_fmaxf(M, ms);
-  }
-  for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
-  float o0 = 0.f, o1 = 0.f, l = 0.f;
-  if (M != ninf) {
-    for (int s0 = 0; s0 < a.splits; s0 += 64) {
-      const int s = s0 + lane;
-      float w = 0.f;
-      if (s < a.splits) {
-        const float ms = base[(size_t)s * KVQ_PART_STRIDE];
-        w = (ms == ninf) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        l = __builtin_fmaf(base[(size_t)s * KVQ_PART_STRIDE + 1], w, l);
-      }
-      const int n = (a.splits - s0) < 64 ? (a.splits - s0) : 64;
-      int j = 0;
-      for (; j + 8 <= n; j += 8) {
-        float2 acc[8];
+  float M = ninf, l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < a.splits; s0 += kChunk) {
+    const int n = (a.splits - s0) < kChunk ? (a.splits - s0) : kChunk;
+    const float *cb = base + (size_t)s0 * KVQ_PART_STRIDE;
+    const bool mine = lane < n;
+    const float ms = mine ? cb[(size_t)lane * KVQ_PART_STRIDE] : ninf;
+    const float ls = mine ? cb[(size_t)lane * KVQ_PART_STRIDE + 1] : 0.f;
+    float2 acc[kChunk];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          acc[u] = reinterpret_cast<const float2 *>(base + (size_t)(s0 + j + u) * KVQ_PART_STRIDE + 4)[lane];
+    for (int u = 0; u < kChunk; ++u)
+      acc[u] = u < n ? reinterpret_cast<const float2 *>(cb + (size_t)u * KVQ_PART_STRIDE + 4)[lane]
+                     : make_float2(0.f, 0.f);
+    float Mc = ms;
+    for (int off = 32; off >= 1; off >>= 1) Mc = __builtin_fmaxf(Mc, __shfl_xor(Mc, off));
+    if (Mc == ninf) continue;  // every split of this chunk is empty
+    const float Mn = __builtin_fmaxf(M, Mc);
+    const float r = (M == ninf) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);  // rescale what came before
+    const float w = (ms == ninf) ? 0.f : __builtin_amdgcn_exp2f(ms - Mn);
+    float lc = ls * w;
+    for (int off = 32; off >= 1; off >>= 1) lc += __shfl_xor(lc, off);
+    l = __builtin_fmaf(l, r, lc);
+    o0 *= r;
+    o1 *= r;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
-          o0 = __builtin_fmaf(acc[u].x, wj, o0);
-          o1 = __builtin_fmaf(acc[u].y, wj, o1);
-        }
-      }
-      for (; j < n; ++j) {
-        const float2 acc = reinterpret_cast<const float2 *>(base + (size_t)(s0 + j) * KVQ_PART_STRIDE + 4)[lane];
-        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-        o0 = __builtin_fmaf(acc.x, wj, o0);
-        o1 = __builtin_fmaf(acc.y, wj, o1);
-      }
+    for (int u = 0; u < kChunk; ++u) {
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+      o0 = __builtin_fmaf(acc[u].x, wj, o0);
+      o1 = __builtin_fmaf(acc[u].y, wj, o1);
     }
-    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+    M = Mn;
+  }
+  if (M != ninf) {
     o0 = o0 / l;
     o1 = o1 / l;
   }

@@ -37,18 +37,18 @@ struct KvqAttnArgs {
   const void *q;
   float *partials;  // [B][Hq][S][KVQ_PART_STRIDE]
   int32_t q_f32, kv_f32, Hq, Hkv, R, rotation;
-  int32_t splits, pages_per_split;  // all splits; quantized pages per quantized split
+  int32_t splits;                    // all splits
   int32_t wsplits;                   // leading splits that cover the recent window, KVQ_WIN_PAGES pages each
   int32_t max_len;  // host-validated upper bound of seq_lens (device lengths are clamped to it)
   float sigma_u;  // softmax_scale * log2(e) * 2^33
 };
+
 
 struct KvqCombineArgs {
   const float *partials;
   void *out;
   int32_t out_f32, B, Hq, splits;
 };
-
 struct KvqDebugArgs {
   KvqLayout lay;
   KvqCacheDev cache;
@@ -63,35 +63,42 @@ struct KvqDebugArgs {
 #define KVQ_PART_STRIDE 132
 #define KVQ_WIN_PAGES 8  // window pages (128 tokens) per window split
 
-// Waves per SIMD the split kernel is compiled for (register budget 512 / KVQ_WPE).
-#ifndef KVQ_WPE
-#define KVQ_WPE 3
-#endif
+// Waves per SIMD each split-kernel instantiation is compiled for (register budget
+// 512 / waves): 4 for the lighter ones (one query part, at most 4 heads per kv head,
+// codes of at most 4 bits), 2 for the heaviest (8 heads, two query parts, wide values
+// or two value groups), 3 for the rest, so that no instantiation spills (the build
+// checks this).
+__host__ __device__ constexpr int kvq_attn_wpe(int kb, int vb, int g, int p, int nvg) {
+  return (p == 1 && g <= 4 && kb <= 4 && vb <= 4) ? 4 : ((g == 8 && p == 2 && (vb >= 4 || nvg == 2)) ? 2 : 3);
+}
 
 #define KVQ_LDS_PER_CU (160 * 1024)
 
-// Page-pair slots of the split kernel's LDS prefetch ring for a given pair size:
-// as many as fit in the LDS share of one wave at the compiled occupancy, 2..4.
-__host__ __device__ constexpr int kvq_ring_slots(int pair_bytes) {
-  return (KVQ_LDS_PER_CU / (4 * KVQ_WPE)) / pair_bytes < 2
-             ? 2
-             : ((KVQ_LDS_PER_CU / (4 * KVQ_WPE)) / pair_bytes > 4 ? 4 : (KVQ_LDS_PER_CU / (4 * KVQ_WPE)) / pair_bytes);
+// Page records of the split kernel's LDS prefetch ring: as many as fit in the LDS
+// share of one wave at the compiled occupancy, at least 3 (the pair in use plus one
+// page ahead) and at most 8.  Slots are sized for the largest record of the bit widths
+// (key groups of 32): rec16 16-byte units.
+__host__ __device__ constexpr int kvq_rec16(int kb, int vb, int nvg) { return 16 * kb + 16 + 16 * vb + 4 * nvg; }
+__host__ __device__ constexpr int kvq_ring_pages(int rec_bytes, int wpe) {
+  return (KVQ_LDS_PER_CU / (4 * wpe)) / rec_bytes < 3
+             ? 3
+             : ((KVQ_LDS_PER_CU / (4 * wpe)) / rec_bytes > 8 ? 8 : (KVQ_LDS_PER_CU / (4 * wpe)) / rec_bytes);
 }
+#define KVQ_STAGE_BYTES ((2 * 8 * 128 + 8 * 4) * 4)  // query / accumulator staging area
 
-// LDS bytes of one split-kernel workgroup (one wave) for key/value bit widths and value groups.
-__host__ __device__ constexpr int kvq_attn_lds_bytes(int kb, int vb, int nvg) {
-  return (2 * (((16 * kb + 16 + 16 * vb + 4 * nvg) + 63) / 64) * 1024) * kvq_ring_slots(2 * (((16 * kb + 16 + 16 * vb + 4 * nvg) + 63) / 64) * 1024) >
-                 (2 * 8 * 128 + 8 * 4) * 4
-             ? (2 * (((16 * kb + 16 + 16 * vb + 4 * nvg) + 63) / 64) * 1024) *
-                   kvq_ring_slots(2 * (((16 * kb + 16 + 16 * vb + 4 * nvg) + 63) / 64) * 1024)
-             : (2 * 8 * 128 + 8 * 4) * 4;
+// LDS bytes of one split-kernel workgroup (one wave).
+__host__ __device__ constexpr int kvq_attn_lds_bytes(int kb, int vb, int nvg, int wpe) {
+  return 16 * kvq_rec16(kb, vb, nvg) * kvq_ring_pages(16 * kvq_rec16(kb, vb, nvg), wpe) > KVQ_STAGE_BYTES
+             ? 16 * kvq_rec16(kb, vb, nvg) * kvq_ring_pages(16 * kvq_rec16(kb, vb, nvg), wpe)
+             : KVQ_STAGE_BYTES;
 }
 
 // Resident split-kernel waves per CU: the register limit or the LDS limit.
-__host__ __device__ constexpr int kvq_attn_waves_per_cu(int kb, int vb, int nvg) {
-  return (4 * KVQ_WPE) < (KVQ_LDS_PER_CU / kvq_attn_lds_bytes(kb, vb, nvg)) ? 4 * KVQ_WPE
-                                                                           : KVQ_LDS_PER_CU / kvq_attn_lds_bytes(kb, vb, nvg);
-}  // floats per partial: m, l, pad, pad, acc[128]
+__host__ __device__ constexpr int kvq_attn_waves_per_cu(int kb, int vb, int nvg, int g, int p) {
+  return (4 * kvq_attn_wpe(kb, vb, g, p, nvg)) < (KVQ_LDS_PER_CU / kvq_attn_lds_bytes(kb, vb, nvg, kvq_attn_wpe(kb, vb, g, p, nvg)))
+             ? 4 * kvq_attn_wpe(kb, vb, g, p, nvg)
+             : KVQ_LDS_PER_CU / kvq_attn_lds_bytes(kb, vb, nvg, kvq_attn_wpe(kb, vb, g, p, nvg));
+}
 
 hipError_t kvq_launch_append(const KvqAppendArgs &a, hipStream_t s);
 hipError_t kvq_launch_attention(const KvqAttnArgs &a, int g, int q_parts, hipStream_t s);

@@ -147,7 +147,11 @@ class GpuRun:
     def attend(self, seq_lens, max_len, q, out_dtype="f32") -> np.ndarray:
         wl = self.wl
         ws_bytes = K.kvq_decode_workspace_bytes(self.params, wl.batch, max_len)
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        # One workspace per run, zero-filled once and reused by every call (the library leaves
+        # its arrival counters at zero after each call); regrown (zeroed) when too small.
+        if getattr(self, "ws", None) is None or self.ws.numel() < ws_bytes:
+            self.ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        ws = self.ws
         out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim),
                           dtype=torch.float32 if out_dtype == "f32" else torch.int16, device="cuda")
         K.kvq_decode_attention(self.params, self.cache.struct, seq_lens, max_len, q,
