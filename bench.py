@@ -28,23 +28,71 @@ METRIC = "K4V2 decode-attention µs/step + achieved HBM GB/s (% of peak), 32k ct
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_b16_L32k.json")
 
 
-def attn_bytes(wl, L, per_token_head, win_elem_bytes):
-    """Algorithmic bytes of one attention call with all sequences at length L."""
+def split_kernel_bytes(wl, L, per_token_head, win_elem_bytes, q_elem_bytes=2):
+    """Algorithmic HBM bytes of one split-kernel launch with every sequence at length L.
+
+    Per (sequence, kv head) unit: the quantized tokens' payload and metadata
+    (per_token_head bytes each), the recent-window tokens' keys and values, and
+    the unit's query heads.  Partial results (an artefact of splitting) are not counted.
+    """
     nq = max(0, L - wl.window)
     nw = min(L, wl.window)
     units = wl.batch * wl.num_kv_heads
-    cache = units * (nq * per_token_head + nw * 2 * wl.head_dim * win_elem_bytes)
-    qo = wl.batch * wl.num_q_heads * wl.head_dim * (2 + 4)  # bf16 query in, fp32 output
-    return cache + qo
+    per_unit = nq * per_token_head + nw * 2 * wl.head_dim * win_elem_bytes + wl.group_q * wl.head_dim * q_elem_bytes
+    return units * per_unit
 
 
 def source_digest():
+    """Digest of the sources the split kernel is built from (invalidates stored counter data)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_kv_kvq_amd", "csrc")
-    for name in ("kvq_attn_impl.h", "kvq_layout.h", "kvq_combine.hip", "kvq_internal.h"):
+    for name in ("kvq_attn_impl.h", "kvq_layout.h", "kvq_internal.h", os.path.join("inst", "kvq_attn_k4v2.hip")):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+SPLIT_KERNEL = "kvq_attn_split_kernel<4, 2, 4, 1, 1>"
+COPY_KERNEL_HINT = "copy"  # torch's device-to-device copy kernel name contains this
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_bytes):
+    """Per-launch HBM bytes of the split kernel from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, in KiB per dispatch) of `bench.py --copy-calibration-mib N`, each scaled by the
+    ratio of the copy kernel's known bytes to what the same counter reports for it."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+        split = [float(r["Counter_Value"]) for r in rows if SPLIT_KERNEL in r["Kernel_Name"].replace("  ", " ")]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if COPY_KERNEL_HINT in r["Kernel_Name"].lower() and "kvq" not in r["Kernel_Name"]]
+        if not split or not copy:
+            raise SystemExit(f"{counter}: no split-kernel or copy-kernel rows under {d}")
+        return sum(split) / len(split), max(copy), len(split)
+
+    fs, fc, n1 = read(fetch_dir, "FETCH_SIZE")
+    ws, wc, n2 = read(write_dir, "WRITE_SIZE")
+    f_factor = copy_bytes / (fc * 1024.0)
+    w_factor = copy_bytes / (wc * 1024.0)
+    out = {
+        "kernel": SPLIT_KERNEL,
+        "source_digest": source_digest(),
+        "fetch_kib_per_launch_raw": fs, "write_kib_per_launch_raw": ws,
+        "copy_bytes": copy_bytes, "copy_fetch_kib_raw": fc, "copy_write_kib_raw": wc,
+        "fetch_scale": f_factor, "write_scale": w_factor,
+        "launches": [n1, n2],
+        "bytes_per_launch": int(fs * 1024.0 * f_factor + ws * 1024.0 * w_factor),
+        "read_bytes_per_launch": int(fs * 1024.0 * f_factor),
+        "write_bytes_per_launch": int(ws * 1024.0 * w_factor),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def cpu_baseline(wl, target_seconds=12.0, max_units=None):
@@ -121,7 +169,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before the steps (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
+                    help="write the split kernel's per-launch HBM traffic from two --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], int(args.summarize_pmc[2]) << 20)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path shards over (sequence, kv head) "
                                    "units across GPUs by design but no multi-GPU run is part of this build",
@@ -167,35 +222,67 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
-    def step(s):
-        K.kvq_quantize_append(params, cache.struct, lens[s], None, k_steps[s], v_steps[s], 1, stream)
-        K.kvq_decode_attention(params, cache.struct, lens[s + 1], L0 + s + 1, q_steps[s], K.KVQ_BF16, out,
-                               K.KVQ_F32, 0.0, ws, ws_bytes, stream)
+    if args.copy_calibration_mib:
+        # uint8 -> int8: an elementwise copy kernel reading and writing exactly N bytes each
+        src = torch.zeros(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty(src.shape, dtype=torch.int8, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # One step: append (quantize the token leaving the window), split-K attention kernel,
+    # cross-split merge.  kvq_decode_partials + kvq_decode_combine are exactly the two launches
+    # of kvq_decode_attention; calling them apart lets HIP events bracket the split kernel alone.
+    # Arguments are marshalled before timing (bound_call), so the Python loop stays ahead of the GPU.
+    def phases(s):
+        return (
+            K.bound_call("kvq_quantize_append", params, cache.struct, lens[s], None, k_steps[s], v_steps[s], 1,
+                         stream=stream),
+            K.bound_call("kvq_decode_partials", params, cache.struct, lens[s + 1], L0 + s + 1, q_steps[s],
+                         K.KVQ_BF16, 0.0, ws, ws_bytes, stream=stream),
+            K.bound_call("kvq_decode_combine", params, B, L0 + s + 1, K.KVQ_BF16, ws, out, K.KVQ_F32,
+                         stream=stream),
+        )
 
     for s in range(args.warmup):
-        step(s)
+        for f in phases(s):
+            f()
+    timed = [phases(args.warmup + i) for i in range(args.steps)]
     torch.cuda.synchronize()
 
-    # ---- timed region ----------------------------------------------------------
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ---- timed region: K whole steps ------------------------------------------------
+    # No event between the launches of a step: on this runtime an event record delays the next
+    # dispatch by a few microseconds, which would be charged to the step.
+    ev_all = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev_all[0].record(stream)
     for i in range(args.steps):
-        s = args.warmup + i
-        ev[i][0].record(stream)
-        K.kvq_quantize_append(params, cache.struct, lens[s], None, k_steps[s], v_steps[s], 1, stream)
-        ev[i][1].record(stream)
-        K.kvq_decode_attention(params, cache.struct, lens[s + 1], L0 + s + 1, q_steps[s], K.KVQ_BF16, out,
-                               K.KVQ_F32, 0.0, ws, ws_bytes, stream)
-        ev[i][2].record(stream)
+        for f in timed[i]:
+            f()
+    ev_all[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    append_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    gpu_us_per_step = ev_all[0].elapsed_time(ev_all[1]) * 1e3 / args.steps
+
+    # ---- the dominant kernel alone: the last step's split-K launch, repeated back to back ---
+    # (it only reads the cache and rewrites the workspace), bracketed by two events on its stream.
+    reps = 20
+    last_partials = timed[-1][1]
+    ev_k = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev_k[0].record(stream)
+    for _ in range(reps):
+        last_partials()
+    ev_k[1].record(stream)
+    torch.cuda.synchronize()
+    split_us = ev_k[0].elapsed_time(ev_k[1]) * 1e3 / reps
+    timed[-1][2]()  # restore the last step's output from the workspace
+    torch.cuda.synchronize()
 
     per_th = (d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4)
-    step_bytes = np.array([attn_bytes(wl, L0 + args.warmup + i + 1, per_th, 2) for i in range(args.steps)])
-    achieved = float(step_bytes.mean() / (attn_ms.mean() * 1e-3) / 1e9)
+    launch_bytes = split_kernel_bytes(wl, L0 + args.warmup + args.steps, per_th, 2)  # the timed launch
+    achieved = float(launch_bytes / (split_us * 1e-6) / 1e9)
     us_per_step = wall / args.steps * 1e6
 
     traffic = None
@@ -224,16 +311,14 @@ def main():
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "context": L0, "window": R, "k_bits": wl.k_bits, "k_group": wl.k_group, "v_bits": wl.v_bits,
                    "v_group": wl.v_group, "step": "append 1 token/sequence + decode attention"},
-        "attention_us": round(float(attn_ms.mean()) * 1e3, 2),
-        "append_us": round(float(append_ms.mean()) * 1e3, 2),
-        "attention_GBps": round(achieved, 1),
-        "attention_pct_peak_hbm": round(100.0 * achieved / PEAK_HBM_GBS, 1),
+        "gpu_us_per_step": round(gpu_us_per_step, 2),
+        "split_kernel_us": round(split_us, 2),
         "tokens_per_s": round(B / (us_per_step * 1e-6), 1),
-        "kv_positions_per_s": round(B * (L0 + args.warmup + args.steps / 2) / (attn_ms.mean() * 1e-3), 1),
-        "roofline": {"kernel": "kvq_decode_attention (split-K kernel + combine, event-timed together)",
+        "roofline": {"kernel": SPLIT_KERNEL + " (decode split-K attention)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": int(step_bytes.mean())},
+                     "algorithmic_bytes_per_launch": int(launch_bytes),
+                     "timing": f"{reps} back-to-back launches of the last step's split kernel between two events"},
         "setup_s": round(setup_s, 2),
     }
     if not args.no_cpu_baseline:

@@ -155,6 +155,29 @@ kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache
                                 int64_t max_seq_len, const void *q, int32_t q_dtype, void *out, int32_t out_dtype,
                                 float softmax_scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The two launches of kvq_decode_attention, for callers that merge the partial results
+ * themselves or schedule the two phases apart.  kvq_decode_partials takes the arguments of
+ * kvq_decode_attention except out/out_dtype and leaves in the workspace, for every
+ * (sequence, query head) row and split s of S, KVQ_PART_FLOATS fp32 values
+ * {m_s, l_s, 0, 0, acc_s[128]}: m_s a running maximum of the scores of the split in log2
+ * units (score * softmax_scale * log2(e)), l_s the sum of 2^(score_log2 - m_s) and acc_s the
+ * matching unnormalised sum of values, l_s and acc_s scaled by one common power of two;
+ * empty splits have m_s = -inf.  With M = max_s m_s the attention output is
+ * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s ([P1] "Error pada key masuk sebelum softmax").
+ * Rows are [batch][num_q_heads][S]; S depends on (params, batch, max_seq_len, q_dtype) and on
+ * the environment variables KVQ_PAGES_PER_SPLIT / KVQ_TARGET_WAVES, which must not change
+ * between the two calls.  kvq_decode_combine computes that merge into `out`
+ * ([batch][num_q_heads][128] of out_dtype) from a workspace filled by kvq_decode_partials
+ * with the same params, batch, max_seq_len and q_dtype.  Errors as for kvq_decode_attention. */
+#define KVQ_PART_FLOATS 132
+/* Number of splits S of the partial results for these arguments (0 for invalid ones). */
+int32_t kvq_decode_splits(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype);
+kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                               int64_t max_seq_len, const void *q, int32_t q_dtype, float softmax_scale,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+kvq_status kvq_decode_combine(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype,
+                              const void *workspace, void *out, int32_t out_dtype, hipStream_t stream);
+
 /* Read back n positions [t0, t0 + n) of sequence `seq` in logical order (debug
  * and verification).  Any output pointer may be NULL.
  *   k_codes, v_codes: device uint8 [n][num_kv_heads][128]; 0xFF for window tokens and t >= L.

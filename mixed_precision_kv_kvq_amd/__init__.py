@@ -23,12 +23,16 @@ LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_EHIP = range(5)
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_ROT_NONE, KVQ_ROT_WHT = 0, 1
+KVQ_PART_FLOATS = 132  # floats per (row, split) of the decode workspace: m, l, 0, 0, acc[128]
 
 EXPORTED = [
     "kvq_cache_sizes",
     "kvq_quantize_append",
     "kvq_decode_workspace_bytes",
     "kvq_decode_attention",
+    "kvq_decode_splits",
+    "kvq_decode_partials",
+    "kvq_decode_combine",
     "kvq_dequantize_debug",
     "kvq_status_str",
 ]
@@ -75,7 +79,7 @@ class KvqError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m mixed_precision_kv_kvq_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python mixed_precision_kv_kvq_amd/build.py` "
             "(or __graft_entry__.build()); there is no fallback path."
         )
     lib = ctypes.CDLL(LIB_PATH)
@@ -90,6 +94,14 @@ def _load():
     lib.kvq_decode_attention.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_int32, c_void_p,
                                          c_int32, c_float, c_void_p, c_size_t, c_void_p]
     lib.kvq_decode_attention.restype = c_int32
+    lib.kvq_decode_splits.argtypes = [P(kvq_params), c_int32, c_int64, c_int32]
+    lib.kvq_decode_splits.restype = c_int32
+    lib.kvq_decode_partials.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_int32, c_float,
+                                        c_void_p, c_size_t, c_void_p]
+    lib.kvq_decode_partials.restype = c_int32
+    lib.kvq_decode_combine.argtypes = [P(kvq_params), c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int32,
+                                       c_void_p]
+    lib.kvq_decode_combine.restype = c_int32
     lib.kvq_dequantize_debug.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int32, c_int64, c_int64, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.kvq_dequantize_debug.restype = c_int32
@@ -128,6 +140,25 @@ def _check(st, where):
         raise KvqError(st, where)
 
 
+def bound_call(name: str, *args, stream=None):
+    """A zero-argument callable that calls C entry point `name` with these arguments, marshalled
+    once here (structs by reference, tensors as device pointers, the stream as a handle), and
+    raises KvqError on a non-OK status.  For tight launch loops where per-call marshalling shows."""
+    fn = getattr(_lib, name)
+    conv = [ctypes.byref(a) if isinstance(a, ctypes.Structure) else _ptr(a) if hasattr(a, "data_ptr") else a
+            for a in args]
+    if name in ("kvq_quantize_append", "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine"):
+        conv.append(_stream(stream))
+    conv = tuple(conv)
+
+    def call():
+        st = fn(*conv)
+        if st != KVQ_OK:
+            raise KvqError(st, name)
+
+    return call
+
+
 def kvq_status_str(status: int) -> str:
     return _lib.kvq_status_str(int(status)).decode()
 
@@ -157,6 +188,28 @@ def kvq_decode_attention(params, cache, seq_lens, max_seq_len, q, q_dtype, out, 
                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "kvq_decode_attention")
+    return st
+
+
+def kvq_decode_splits(params, batch: int, max_seq_len: int, q_dtype: int) -> int:
+    return int(_lib.kvq_decode_splits(ctypes.byref(params), int(batch), int(max_seq_len), int(q_dtype)))
+
+
+def kvq_decode_partials(params, cache, seq_lens, max_seq_len, q, q_dtype, softmax_scale, workspace, workspace_bytes,
+                        stream=None, check=True):
+    st = _lib.kvq_decode_partials(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens), int(max_seq_len),
+                                  _ptr(q), int(q_dtype), float(softmax_scale), _ptr(workspace),
+                                  int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "kvq_decode_partials")
+    return st
+
+
+def kvq_decode_combine(params, batch, max_seq_len, q_dtype, workspace, out, out_dtype, stream=None, check=True):
+    st = _lib.kvq_decode_combine(ctypes.byref(params), int(batch), int(max_seq_len), int(q_dtype), _ptr(workspace),
+                                 _ptr(out), int(out_dtype), _stream(stream))
+    if check:
+        _check(st, "kvq_decode_combine")
     return st
 
 

@@ -3,7 +3,8 @@
 * mixed_precision_kv_kvq_amd/libkvq.so — the quantized-KV attention library (C ABI in include/kvq.h)
 * workloads/libkvqgen.so                — the device-side input generator (include/kvq_gen.h)
 
-Usage:  python -m mixed_precision_kv_kvq_amd.build [--force] [--jobs N]
+Usage:  python mixed_precision_kv_kvq_amd/build.py [--force] [--jobs N]
+(run it as a file: importing the package loads the library it builds)
 """
 from __future__ import annotations
 

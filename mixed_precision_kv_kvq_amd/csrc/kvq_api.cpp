@@ -156,15 +156,14 @@ size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64
   return (size_t)batch * params->num_q_heads * (size_t)bound * KVQ_PART_STRIDE * sizeof(float);
 }
 
-kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
-                                int64_t max_seq_len, const void *q, int32_t q_dtype, void *out, int32_t out_dtype,
-                                float softmax_scale, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                               int64_t max_seq_len, const void *q, int32_t q_dtype, float softmax_scale,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (kvq_status st = check_params(params)) return st;
   if (kvq_status st = check_cache(params, cache)) return st;
-  if (!seq_lens || !q || !out || !workspace || max_seq_len < 0) return KVQ_EINVAL;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EINVAL;
-  if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
-    return KVQ_EINVAL;
+  if (!seq_lens || !q || !workspace || max_seq_len < 0) return KVQ_EINVAL;
+  if (!aligned16(q) || !aligned16(workspace)) return KVQ_EINVAL;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_EINVAL;
   if (!(softmax_scale >= 0.f) || isinf(softmax_scale)) return KVQ_EINVAL;
   const int64_t nq_max = max_seq_len > params->window ? max_seq_len - params->window : 0;
   if (params->block_size) {
@@ -194,16 +193,45 @@ kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
   a.sigma_u = (float)((double)scale * 1.4426950408889634 * 8589934592.0);  // * log2(e) * 2^33
   const int g = params->num_q_heads / params->num_kv_heads;
-  hipError_t e = kvq_launch_attention(a, g, q_parts, stream);
-  if (e != hipSuccess) return KVQ_EHIP;
+  return hip_status(kvq_launch_attention(a, g, q_parts, stream));
+}
+
+int32_t kvq_decode_splits(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype) {
+  if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0) return 0;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return 0;
+  const int q_parts = (q_dtype == KVQ_BF16 && !params->key_rotation) ? 1 : 2;
+  return split_plan(params, batch, max_seq_len, q_parts).splits;
+}
+
+kvq_status kvq_decode_combine(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype,
+                              const void *workspace, void *out, int32_t out_dtype, hipStream_t stream) {
+  if (kvq_status st = check_params(params)) return st;
+  if (batch <= 0 || !workspace || !out || max_seq_len < 0) return KVQ_EINVAL;
+  if (!aligned16(workspace) || !aligned16(out)) return KVQ_EINVAL;
+  if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
+    return KVQ_EINVAL;
+  const int q_parts = (q_dtype == KVQ_BF16 && !params->key_rotation) ? 1 : 2;
   KvqCombineArgs c;
-  c.partials = a.partials;
+  c.partials = (const float *)workspace;
   c.out = out;
   c.out_f32 = out_dtype == KVQ_F32;
-  c.B = cache->batch;
+  c.B = batch;
   c.Hq = params->num_q_heads;
-  c.splits = a.splits;
+  c.splits = split_plan(params, batch, max_seq_len, q_parts).splits;
   return hip_status(kvq_launch_combine(c, stream));
+}
+
+kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                                int64_t max_seq_len, const void *q, int32_t q_dtype, void *out, int32_t out_dtype,
+                                float softmax_scale, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!out || !aligned16(out) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16)) {
+    if (kvq_status st = check_params(params)) return st;
+    return KVQ_EINVAL;
+  }
+  if (kvq_status st = kvq_decode_partials(params, cache, seq_lens, max_seq_len, q, q_dtype, softmax_scale, workspace,
+                                          workspace_bytes, stream))
+    return st;
+  return kvq_decode_combine(params, cache->batch, max_seq_len, q_dtype, workspace, out, out_dtype, stream);
 }
 
 kvq_status kvq_dequantize_debug(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,

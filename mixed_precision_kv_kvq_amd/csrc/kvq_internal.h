@@ -60,7 +60,7 @@ struct KvqDebugArgs {
   float *k_hat, *v_hat;
 };
 
-#define KVQ_PART_STRIDE 132
+#define KVQ_PART_STRIDE KVQ_PART_FLOATS  // floats per partial row: m, l, pad, pad, acc[128]
 #define KVQ_WIN_PAGES 8  // window pages (128 tokens) per window split
 
 // Waves per SIMD each split-kernel instantiation is compiled for (register budget

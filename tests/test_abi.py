@@ -17,7 +17,7 @@ FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first o
 
 def declared(header):
     text = open(os.path.join(ROOT, "include", header)).read()
-    return sorted(set(re.findall(r"^\s*(?:kvq_status|size_t|const char \*|int)\s*\*?\s*(kvq_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:kvq_status|size_t|const char \*|int32_t|int)\s*\*?\s*(kvq_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol():
@@ -129,6 +129,32 @@ def test_attention_validation():
     assert K.kvq_decode_workspace_bytes(p(k_bits=3), 2, 64) == 0
 
 
+def test_phase_entry_points_validation():
+    prm = p()
+    L = K.lib()
+    need = K.kvq_decode_workspace_bytes(prm, 2, 64)
+
+    def part(mx=64, q=FAKE, qd=K.KVQ_BF16, ws=FAKE, wsb=need, prm_=prm):
+        return L.kvq_decode_partials(ctypes.byref(prm_), ctypes.byref(cache()), FAKE, mx, q, qd, 0.0, ws, wsb, None)
+
+    assert part(wsb=need - 1) == K.KVQ_ENOSPACE
+    assert part(mx=65) == K.KVQ_ENOSPACE
+    assert part(q=None) == K.KVQ_EINVAL
+    assert part(ws=FAKE + 4) == K.KVQ_EINVAL
+    assert part(qd=7) == K.KVQ_EINVAL
+    assert part(prm_=p(v_bits=3)) == K.KVQ_EUNSUPPORTED
+
+    def comb(batch=2, ws=FAKE, out=FAKE, qd=K.KVQ_BF16, od=K.KVQ_F32, prm_=prm):
+        return L.kvq_decode_combine(ctypes.byref(prm_), batch, 64, qd, ws, out, od, None)
+
+    assert comb(batch=0) == K.KVQ_EINVAL
+    assert comb(ws=None) == K.KVQ_EINVAL
+    assert comb(out=FAKE + 8) == K.KVQ_EINVAL
+    assert comb(od=9) == K.KVQ_EINVAL
+    assert comb(prm_=p(num_q_heads=48)) == K.KVQ_EUNSUPPORTED
+    assert K.KVQ_PART_FLOATS == 132
+
+
 def test_debug_validation():
     prm = p()
     L = K.lib()
@@ -182,3 +208,13 @@ def test_package_shares_torchs_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_bound_call_marshals_once_and_raises():
+    prm = p()
+    call = K.bound_call("kvq_decode_combine", prm, 0, 64, K.KVQ_BF16, FAKE, FAKE, K.KVQ_F32, stream=0)
+    with pytest.raises(K.KvqError) as e:
+        call()
+    assert e.value.status == K.KVQ_EINVAL
+    ok = K.bound_call("kvq_quantize_append", prm, cache(), FAKE, None, None, None, 0, stream=0)
+    ok()  # zero tokens: validated, nothing launched

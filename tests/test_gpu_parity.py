@@ -195,3 +195,62 @@ def test_outputs_deterministic_and_split_invariant():
             os.environ.pop("KVQ_PAGES_PER_SPLIT", None)
         else:
             os.environ["KVQ_PAGES_PER_SPLIT"] = old
+
+
+def test_phase_entry_points_match_attention():
+    """kvq_decode_partials + kvq_decode_combine give bit for bit what kvq_decode_attention gives,
+    and the workspace rows follow the documented merge rule."""
+    wl = small(W.WORKLOADS[3], batch=2, context=700, steps=1, config=303)
+    say("partials + combine")
+    run = GpuRun(wl, chunk=256)
+    L = run.current_lengths()
+    lens = torch.from_numpy(L.astype(np.int32)).cuda()
+    q = run._q_dev(0)
+    ref = run.attend(lens, int(L.max()), q, "f32")
+    wsb = K.kvq_decode_workspace_bytes(run.params, wl.batch, int(L.max()))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    K.kvq_decode_partials(run.params, run.cache.struct, lens, int(L.max()), q, K.KVQ_BF16, 0.0, ws, wsb)
+    K.kvq_decode_combine(run.params, wl.batch, int(L.max()), K.KVQ_BF16, ws, out, K.KVQ_F32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got, ref)
+    # merge the rows on the host (fp64) by the documented rule and compare with the kernel's merge
+    S = K.kvq_decode_splits(run.params, wl.batch, int(L.max()), K.KVQ_BF16)
+    assert S >= 1 and wl.batch * wl.num_q_heads * S * K.KVQ_PART_FLOATS * 4 <= wsb
+    blk = ws.view(torch.float32)[: wl.batch * wl.num_q_heads * S * K.KVQ_PART_FLOATS].cpu().numpy()
+    blk = blk.astype(np.float64).reshape(wl.batch, wl.num_q_heads, S, K.KVQ_PART_FLOATS)
+    m, l, acc = blk[..., 0], blk[..., 1], blk[..., 4:]
+    assert np.all(blk[..., 2:4] == 0.0)
+    M = m.max(axis=2, keepdims=True)
+    w = np.where(np.isneginf(m), 0.0, np.exp2(np.where(np.isneginf(m), 0.0, m - M)))
+    o = (w[..., None] * acc).sum(axis=2) / (w * l).sum(axis=2)[..., None]
+    assert np.allclose(o, got, rtol=1e-5, atol=1e-6)
+
+
+def test_graph_replays_match_eager():
+    """Decode attention captured in a HIP graph: several replays, with eager work and
+    synchronisations between them, each equal bit for bit to the eager result."""
+    wl = small(W.WORKLOADS[3], batch=2, context=900, steps=1, config=304)
+    say("graph replays")
+    run = GpuRun(wl, chunk=256)
+    L = run.current_lengths()
+    mx = int(L.max())
+    lens = torch.from_numpy(L.astype(np.int32)).cuda()
+    q = run._q_dev(0)
+    eager = run.attend(lens, mx, q, "f32")
+    wsb = K.kvq_decode_workspace_bytes(run.params, wl.batch, mx)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        K.kvq_decode_attention(run.params, run.cache.struct, lens, mx, q, K.KVQ_BF16, out, K.KVQ_F32, 0.0, ws, wsb)
+    for r in range(3):
+        out.fill_(float("nan"))
+        ws.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {r}"
+        # eager work between replays
+        again = run.attend(lens, mx, q, "f32")
+        assert np.array_equal(again, eager)

@@ -21,7 +21,7 @@ def _lib():
     if _LIB is None:
         path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvqgen.so")
         if not os.path.exists(path):
-            raise ImportError(f"{path} is missing: build with `python -m mixed_precision_kv_kvq_amd.build`")
+            raise ImportError(f"{path} is missing: build with `python mixed_precision_kv_kvq_amd/build.py`")
         lib = ctypes.CDLL(path)
         lib.kvq_gen_kv.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
