@@ -36,8 +36,10 @@
  * whose internal order matches the register layout of the attention kernel;
  * kvq_dequantize_debug reads it back in logical order.  Metadata entries are
  * {fp16 scale, fp16 zero} pairs.
- *   block_size == 0 (contiguous): page p of kv head h of sequence b is record
- *       (b * num_kv_heads + h) * pages_per_seq + p, pages_per_seq = ceil(capacity / 16).
+ *   block_size == 0 (contiguous, page-major): page p of kv head h of sequence b is
+ *       record p * (batch * num_kv_heads) + b * num_kv_heads + h, for
+ *       p < ceil(capacity / 16); the records of one (sequence, kv head) are spread
+ *       evenly over the whole allocation.
  *   block_size == 16 (paged): page p of sequence b is pool page
  *       block_table[b * max_blocks_per_seq + p]; its kv head h is record
  *       pool_page * num_kv_heads + h.

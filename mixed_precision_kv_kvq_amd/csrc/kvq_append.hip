@@ -163,8 +163,8 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
   const int64_t page = t_q / KVQ_PAGE;
   const int n = (int)(t_q % KVQ_PAGE);
   if (page >= (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq)) return;  // beyond the cache
-  const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps, a.cache.pages_per_seq,
-                                           a.cache.pool_pages, Hkv, b, h, page);
+  const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
+                                           (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, b, h, page);
   uint8_t *rec = a.cache.pages + (size_t)rec_idx * lay.record;
 
   // K codes: 4 slots (octets j) x kb words.

@@ -887,7 +887,8 @@ struct Kern {
     typedef const __attribute__((address_space(4))) int32_t *const_i32p;
     const_i32p btab = (const_i32p)args.cache.block_table;
     const int64_t bt_row = (int64_t)b * args.cache.mbps;
-    const int64_t contig_base = ((int64_t)b * Hkv + kvh) * args.cache.pages_per_seq;
+    // contiguous records are page-major: page p of this unit is record p * units + unit
+    const int64_t unit_idx = (int64_t)b * Hkv + kvh, units_all = (int64_t)args.cache.batch * Hkv;
     const int64_t pool_last = args.cache.pool_pages - 1;
     const int paged = args.cache.paged;
     auto rec_ptr = [&](int p) -> const uint8_t * {
@@ -897,7 +898,7 @@ struct Kern {
         e = e < 0 ? 0 : (e > pool_last ? pool_last : e);
         ri = e * Hkv + kvh;
       } else {
-        ri = contig_base + p;
+        ri = (int64_t)p * units_all + unit_idx;
       }
       return pages + (size_t)ri * lay.record;
     };

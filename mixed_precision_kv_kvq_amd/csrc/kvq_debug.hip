@@ -26,7 +26,7 @@ __global__ __launch_bounds__(64) void kvq_debug_kernel(KvqDebugArgs a) {
     float kh = qnan, vh = qnan;
     if (t < nq) {
       const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
-                                               a.cache.pages_per_seq, a.cache.pool_pages, Hkv, a.seq, h,
+                                               (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, a.seq, h,
                                                t / KVQ_PAGE);
       const uint8_t *rec = a.cache.pages + (size_t)rec_idx * lay.record;
       const int n = (int)(t % KVQ_PAGE);

@@ -79,19 +79,20 @@ __host__ __device__ inline int kvq_meta_dword(int ngroups, int tt, int grp) {
   return ((tt >> 2) * ngroups + grp) * 4 + (tt & 3);
 }
 
-// Record index of (sequence b, kv head h, logical page p).  Callers keep p below
-// pages_per_seq (contiguous) or mbps (paged); a block-table entry outside
-// [0, pool_pages) is clamped so that a bad table cannot address memory outside
-// the pool.
+// Record index of (sequence b, kv head h, logical page p).  Contiguous mode is page-major:
+// page p of every (sequence, kv head) unit, then page p + 1, ..., so each unit's pages are
+// spread evenly over the whole allocation (units = batch * Hkv).  Callers keep p below
+// pages_per_seq (contiguous) or mbps (paged); a block-table entry outside [0, pool_pages)
+// is clamped so that a bad table cannot address memory outside the pool.
 __host__ __device__ inline int64_t kvq_record_index(int paged, const int32_t *block_table, int mbps,
-                                                    int64_t pages_per_seq, int64_t pool_pages, int Hkv, int b, int h,
+                                                    int64_t units, int64_t pool_pages, int Hkv, int b, int h,
                                                     int64_t p) {
   if (paged) {
     int64_t e = block_table[(int64_t)b * mbps + p];
     e = e < 0 ? 0 : (e >= pool_pages ? pool_pages - 1 : e);
     return e * Hkv + h;
   }
-  return ((int64_t)b * Hkv + h) * pages_per_seq + p;
+  return p * units + ((int64_t)b * Hkv + h);
 }
 
 // ---------------------------------------------------------------------------
