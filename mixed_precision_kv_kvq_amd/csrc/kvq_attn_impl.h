@@ -196,14 +196,15 @@ __device__ __forceinline__ float replica_allreduce(float v) {
 // ---------------------------------------------------------------------------
 // Page prefetch ring in LDS.  In the steady-state loop every page record is
 // copied verbatim into a per-wave LDS slot with direct-to-LDS loads
-// (global_load_lds_dwordx4: lane l writes 16 bytes at slot + 16*l), a few page
+// (buffer_load_dwordx4 ... lds: lane l writes 16 bytes at slot + 16*l), a few page
 // pairs ahead of use, and read back with ds_read when processed.  In-flight
 // data therefore never occupies a VGPR.  The waits are explicit: vmcnt counts
 // vector-memory operations in issue order, so after N newer loads,
 // s_waitcnt vmcnt(N) means every older load has landed in LDS.  Every DMA
-// instruction keeps all 64 lanes active (lanes past the end of a record re-read
-// an in-range chunk into the slot's padding) so that the counts are exact, and
-// no other vector-memory load is issued inside that loop.
+// instruction has active lanes (lanes past the end of a shorter record re-read an
+// in-range chunk into the slot's padding; only lanes past the slot itself are
+// idle), so each one is counted, and no other vector-memory load is issued inside
+// that loop.
 // ---------------------------------------------------------------------------
 template <int CNT>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -562,31 +563,18 @@ struct Kern {
   static_assert(LDS_BYTES >= NPS * REC_BYTES && LDS_BYTES >= KVQ_STAGE_BYTES, "LDS sizing");
   static_assert(AHEAD * DMAS_PER_PAGE <= 63, "vmcnt range");
 
-  // Copy one page record into an LDS slot: DMAS_PER_PAGE wave-wide DMAs, lane l of DMA k
-  // writing slot chunk 64k + l.  Lanes past the slot (MAX_REC16 chunks) stay idle, which
-  // leaves at least one active lane in every DMA so that each one is counted by vmcnt;
-  // lanes past a shorter record (larger key groups) re-read its last chunk.
-  static __device__ __forceinline__ void dma_page(uint8_t *slot, const uint8_t *rec, int rec16, int lane) {
+  // Copy one page record into an LDS slot: DMAS_PER_PAGE wave-wide DMAs, lane l of DMA k writing
+  // slot chunk 64k + l, through a buffer resource spanning just the record (scalar base and size),
+  // with 32-bit lane offsets (16-byte chunks, clamped into the record) and the slot given as an
+  // LDS byte address (base: the low 32 bits of the slot's shared-aperture address); lanes past
+  // the slot stay idle.  The resource's range check also keeps every lane inside the record.
+  static __device__ __forceinline__ void dma_page_buf(uint32_t slot_lds, const uint8_t *rec, int rec_bytes,
+                                                      const uint32_t (&loff)[DMAS_PER_PAGE], int lane) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, 0, rec_bytes, 0x00020000);
 #pragma unroll
     for (int k = 0; k < DMAS_PER_PAGE; ++k) {
-      int c = 64 * k + lane;
-      c = c < rec16 ? c : rec16 - 1;
       if (k + 1 < DMAS_PER_PAGE || lane < MAX_REC16 - 64 * k)
-        __builtin_amdgcn_global_load_lds((const void *)(rec + 16 * c), (lds_vptr)(slot + 1024 * k), 16, 0, 0);
-    }
-  }
-
-  // Wait until at most n pages (n <= AHEAD) of DMAs are outstanding.
-  static __device__ __forceinline__ void wait_pages(int n) {
-    static_assert(AHEAD <= 6, "wait_pages cases");
-    switch (n) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<(AHEAD >= 1 ? 1 : 0) * DMAS_PER_PAGE>(); break;
-      case 2: wait_vmcnt<(AHEAD >= 2 ? 2 : 0) * DMAS_PER_PAGE>(); break;
-      case 3: wait_vmcnt<(AHEAD >= 3 ? 3 : 0) * DMAS_PER_PAGE>(); break;
-      case 4: wait_vmcnt<(AHEAD >= 4 ? 4 : 0) * DMAS_PER_PAGE>(); break;
-      case 5: wait_vmcnt<(AHEAD >= 5 ? 5 : 0) * DMAS_PER_PAGE>(); break;
-      default: wait_vmcnt<(AHEAD >= 6 ? 6 : 0) * DMAS_PER_PAGE>(); break;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(size_t)(slot_lds + 1024u * k), 16, loff[k], 0, 0, 0);
     }
   }
 
@@ -608,9 +596,8 @@ struct Kern {
     }
   }
 
-  static __device__ __forceinline__ void read_page(PageData &pd, const Ctx &cx, const uint8_t *sp,
-                                                   const KvqLayout &lay) {
-    const uint32_t base = (uint32_t)(uintptr_t)sp;  // LDS offset (low 32 bits of the shared-aperture address)
+  static __device__ __forceinline__ void read_page_at(PageData &pd, const Ctx &cx, uint32_t base,
+                                                      const KvqLayout &lay) {
     RawWords<KB> rk;
     RawWords<VB> rv;
     u32x4 km[NACC], vm[NVG];
@@ -890,7 +877,7 @@ struct Kern {
     // contiguous records are page-major: page p of this unit is record p * units + unit
     const int64_t unit_idx = (int64_t)b * Hkv + kvh, units_all = (int64_t)args.cache.batch * Hkv;
     const int64_t pool_last = args.cache.pool_pages - 1;
-    const int paged = args.cache.paged;
+    const bool paged = args.cache.paged != 0;
     auto rec_ptr = [&](int p) -> const uint8_t * {
       int64_t ri;
       if (paged) {
@@ -905,15 +892,6 @@ struct Kern {
     // Fast path: pairs of full pages, next pairs prefetched while the current one is processed.
     const int npairs = tp > sq ? (tp - sq + SQ - 1) / SQ : 0;
     if (npairs > 0) {
-      // Prefetch ring of NPS page slots: local page k (pair k / 2) lives in slot k % NPS.  The
-      // prologue requests pages 0..AHEAD-1; processing pair i first requests pages 2i + AHEAD and
-      // 2i + AHEAD + 1, whose slots held pair i - 1 (already read), then waits for pages 2i, 2i + 1.
-      const int rec16 = lay.record / 16;
-      const int npages = 2 * npairs;
-      auto issue_page = [&](int k) {
-        const int pg = 2 * (sq + (k >> 1) * SQ) + (k & 1);
-        dma_page(smem + (k % NPS) * REC_BYTES, rec_ptr(pg), rec16, lane);
-      };
       // The query operand is built while the first pages stream in: without rotation the
       // query loads are issued before the prologue DMAs (vmcnt retires them first); with
       // rotation the query is staged and rotated through LDS before the ring is used.
@@ -925,21 +903,7 @@ struct Kern {
       } else {
         load_q_regs(qr, args, cx, b, hq0);
       }
-#pragma unroll
-      for (int k = 0; k < AHEAD; ++k)
-        if (k < npages) issue_page(k);
-      if (!args.rotation) build_q_regs(cx, qr, args.q_f32);
-      for (int i = 0; i < npairs; ++i) {
-        const int k0 = 2 * i + AHEAD;
-        if (k0 < npages) issue_page(k0);
-        if (k0 + 1 < npages) issue_page(k0 + 1);
-        const int issued = k0 + 2 < npages ? k0 + 2 : npages;
-        wait_pages(issued - (2 * i + 2));
-        PageData A, B;
-        read_page(A, cx, smem + ((2 * i) % NPS) * REC_BYTES, lay);
-        read_page(B, cx, smem + ((2 * i + 1) % NPS) * REC_BYTES, lay);
-        process_pair<false>(cx, st, A, B, 16, 16);
-      }
+      stream_pairs(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs);
     }
     // Remaining quantized pages (an odd full page and/or the partial page): one masked pair.
     const int qend = qpages;
@@ -962,6 +926,75 @@ struct Kern {
       process_pair<true>(cx, st, A, B, va, vb);
     }
     write_partial<false>(args, cx, st, nullptr, lds, b, kvh, split);
+  }
+
+  // Pairs sq, sq + SQ, ... (npairs of them) of one unit through the wave's LDS ring of NPS page
+  // slots: local page k (pair k / 2) lives in slot k mod NPS.  The first AHEAD pages are requested
+  // up front; processing pair i first requests pages 2i + AHEAD and 2i + AHEAD + 1 (the slots of
+  // pair i - 1, already read), then waits until those two are the only pages still in flight
+  // behind pair i.  Requests follow a cursor that steps through the pairs in order (the parity of
+  // every request site is fixed, so the cursor moves by constant strides), and the slot addresses
+  // rotate through the ring, so the loop does no index arithmetic beyond those steps.
+  static __device__ __forceinline__ void stream_pairs(const KvqAttnArgs &args, Ctx &cx, State<NVG> &st, uint8_t *smem,
+                                                      const QRegs &qr, int b, int kvh, int sq, int SQ, int npairs) {
+    const KvqLayout &lay = args.lay;
+    const int lane = cx.lane, Hkv = args.Hkv;
+    const int rec = lay.record, rec16 = rec / 16;
+    uint32_t loff[DMAS_PER_PAGE];  // this lane's 16-byte chunk of each DMA, clamped into the record
+#pragma unroll
+    for (int k = 0; k < DMAS_PER_PAGE; ++k) {
+      const int c = 64 * k + lane;
+      loff[k] = (uint32_t)(c < rec16 ? c : rec16 - 1) << 4;
+    }
+    // Cursor: the pair holding the next page to request.
+    const uint8_t *pages = args.cache.pages;
+    const size_t page_stride = (size_t)args.cache.batch * Hkv * rec;  // contiguous: page p -> p + 1
+    const size_t pair_step = 2 * (size_t)SQ * page_stride;            // contiguous: pair j -> j + SQ
+    const uint8_t *cur = pages + ((size_t)b * Hkv + kvh) * rec + 2 * (size_t)sq * page_stride;
+    typedef const __attribute__((address_space(4))) int32_t *const_i32p;
+    const_i32p tcur = (const_i32p)args.cache.block_table + (int64_t)b * args.cache.mbps + 2 * sq;
+    const int pool_last = (int)(args.cache.pool_pages - 1);
+    const bool paged = args.cache.paged != 0;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)smem, ring_end = ring0 + NPS * REC_BYTES;
+    uint32_t wslot = ring0, rslot = ring0;
+    auto next_slot = [&](uint32_t sl) { return sl + REC_BYTES == ring_end ? ring0 : sl + REC_BYTES; };
+    auto issue = [&](bool odd) {
+      const uint8_t *src;
+      if (paged) {
+        int e = tcur[odd ? 1 : 0];
+        e = e < 0 ? 0 : (e > pool_last ? pool_last : e);
+        src = pages + ((size_t)e * Hkv + kvh) * rec;
+        if (odd) tcur += 2 * SQ;
+      } else {
+        src = odd ? cur + page_stride : cur;
+        if (odd) cur += pair_step;
+      }
+      dma_page_buf(wslot, src, rec, loff, lane);
+      wslot = next_slot(wslot);
+    };
+    const int npages = 2 * npairs;
+#pragma unroll
+    for (int k = 0; k < AHEAD; ++k)
+      if (k < npages) issue((k & 1) != 0);
+    if (!args.rotation) build_q_regs(cx, qr, args.q_f32);
+    constexpr bool FIRST_ODD = (AHEAD & 1) != 0;  // parity of page 2i + AHEAD
+    for (int i = 0; i < npairs; ++i) {
+      const int k0 = 2 * i + AHEAD;
+      if (k0 + 1 < npages) {  // steady state: two requests, AHEAD pages stay in flight
+        issue(FIRST_ODD);
+        issue(!FIRST_ODD);
+        wait_vmcnt<AHEAD * DMAS_PER_PAGE>();
+      } else {  // the last pairs: at most one more request, then drain
+        if (k0 < npages) issue(FIRST_ODD);
+        wait_vmcnt<0>();
+      }
+      PageData A, B;
+      read_page_at(A, cx, rslot, lay);
+      rslot = next_slot(rslot);
+      read_page_at(B, cx, rslot, lay);
+      rslot = next_slot(rslot);
+      process_pair<false>(cx, st, A, B, 16, 16);
+    }
   }
 
   // Reduce the state across rows/replicas and write this split's partial result:
@@ -1024,7 +1057,7 @@ struct Kern {
 };
 
 template <int KB, int VB, int G, int P, int NVG>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kvq_attn_wpe(KB, VB, G, P, NVG)))) void kvq_attn_split_kernel(KvqAttnArgs args) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kvq_attn_wpe(KB, VB, G, P, NVG), kvq_attn_wpe(KB, VB, G, P, NVG)))) void kvq_attn_split_kernel(KvqAttnArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Kern<KB, VB, G, P, NVG>::LDS_BYTES];
   Kern<KB, VB, G, P, NVG>::run(args, smem);
 }
