@@ -84,49 +84,6 @@ __device__ __forceinline__ T gload(const void *p) {
   return *(const KVQ_GLOBAL T *)(p);
 }
 
-template <int N>
-__device__ __forceinline__ Words<N> load_words(const uint8_t *p) {
-  Words<N> r;
-  if constexpr (N == 1) {
-    r.w[0] = gload<uint32_t>(p);
-  } else if constexpr (N == 2) {
-    const u32x2 v = gload<u32x2>(p);
-    r.w[0] = v.x;
-    r.w[1] = v.y;
-  } else if constexpr (N == 4) {
-    const u32x4 v = gload<u32x4>(p);
-    r.w[0] = v.x;
-    r.w[1] = v.y;
-    r.w[2] = v.z;
-    r.w[3] = v.w;
-  } else {
-    const u32x4 v0 = gload<u32x4>(p);
-    const u32x4 v1 = gload<u32x4>(p + 16);
-    r.w[0] = v0.x;
-    r.w[1] = v0.y;
-    r.w[2] = v0.z;
-    r.w[3] = v0.w;
-    r.w[4] = v1.x;
-    r.w[5] = v1.y;
-    r.w[6] = v1.z;
-    r.w[7] = v1.w;
-  }
-  return r;
-}
-
-template <int N>
-__device__ __forceinline__ Words<N> zero_words() {
-  Words<N> r;
-#pragma unroll
-  for (int i = 0; i < N; ++i) r.w[i] = 0;
-  return r;
-}
-
-__device__ __forceinline__ uint4 load_u4(const uint8_t *p) {
-  const u32x4 v = gload<u32x4>(p);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 __device__ __forceinline__ uint32_t u4_get(const uint4 &v, int r) {
   return r == 0 ? v.x : (r == 1 ? v.y : (r == 2 ? v.z : v.w));
 }
@@ -375,25 +332,6 @@ struct Kern {
     Words<VB> vc;
     uint4 vm[NVG];
   };
-
-  static __device__ __forceinline__ void load_page(PageData &pd, const Ctx &cx, const uint8_t *rec,
-                                                   const KvqLayout &lay) {
-    pd.kc = load_words<KB>(rec + lay.k_codes_off + cx.lane * 4 * KB);
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) pd.km[a] = load_u4(rec + cx.kmeta_off[a]);
-    pd.vc = load_words<VB>(rec + lay.v_codes_off + cx.lane * 4 * VB);
-#pragma unroll
-    for (int v = 0; v < NVG; ++v) pd.vm[v] = load_u4(rec + cx.vmeta_off[v]);
-  }
-
-  static __device__ __forceinline__ void zero_page(PageData &pd) {
-    pd.kc = zero_words<KB>();
-    pd.vc = zero_words<VB>();
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) pd.km[a] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < NVG; ++v) pd.vm[v] = make_uint4(0, 0, 0, 0);
-  }
 
   // Key codes of chunk kc of one page as the A operand (slot scales per kslot_scale).
   static __device__ __forceinline__ bf16x8 key_operand(const PageData &pd, int kc) {
@@ -863,35 +801,23 @@ struct Kern {
     }
 
     // Quantized splits take full-page pairs round-robin: pair sq, sq + SQ, sq + 2 SQ, ... so that at
-    // any moment the waves of one unit read neighbouring pairs.  The 1-2 pages after the last full
-    // pair (an odd full page and/or the partial page) go to the split next in the rotation.
+    // any moment the waves of one unit read neighbouring pairs.
     const int SQ = S - args.wsplits, sq = split - args.wsplits;
     const int full_pages = nq / KVQ_PAGE;  // pages with all 16 tokens quantized
     const int tp = full_pages / 2;         // full pairs of this sequence
-    const uint8_t *pages = args.cache.pages;
-    // Block-table entries are wave-uniform: read them with scalar loads (constant address space) so
-    // that waiting for one never drains the vector-memory queue of prefetched pages.
-    typedef const __attribute__((address_space(4))) int32_t *const_i32p;
-    const_i32p btab = (const_i32p)args.cache.block_table;
-    const int64_t bt_row = (int64_t)b * args.cache.mbps;
-    // contiguous records are page-major: page p of this unit is record p * units + unit
-    const int64_t unit_idx = (int64_t)b * Hkv + kvh, units_all = (int64_t)args.cache.batch * Hkv;
-    const int64_t pool_last = args.cache.pool_pages - 1;
-    const bool paged = args.cache.paged != 0;
-    auto rec_ptr = [&](int p) -> const uint8_t * {
-      int64_t ri;
-      if (paged) {
-        int64_t e = btab[bt_row + p];
-        e = e < 0 ? 0 : (e > pool_last ? pool_last : e);
-        ri = e * Hkv + kvh;
-      } else {
-        ri = (int64_t)p * units_all + unit_idx;
-      }
-      return pages + (size_t)ri * lay.record;
-    };
-    // Fast path: pairs of full pages, next pairs prefetched while the current one is processed.
+    // Pairs of full pages, next pairs prefetched while the current one is processed.  The 1-2
+    // pages after the last full pair (an odd full page and/or the partial page) form one masked
+    // pair; it goes to the split next in the rotation, whose cursor reaches it right after its
+    // full pairs, so it streams through the same ring.
     const int npairs = tp > sq ? (tp - sq + SQ - 1) / SQ : 0;
-    if (npairs > 0) {
+    const bool tail = sq == tp % SQ && 2 * tp < qpages;
+    if (npairs > 0 || tail) {
+      int tail_va = 0, tail_vb = 0;
+      if (tail) {
+        const int p = 2 * tp;
+        tail_va = (nq - p * KVQ_PAGE) < KVQ_PAGE ? (nq - p * KVQ_PAGE) : KVQ_PAGE;
+        tail_vb = p + 1 < qpages ? ((nq - (p + 1) * KVQ_PAGE) < KVQ_PAGE ? (nq - (p + 1) * KVQ_PAGE) : KVQ_PAGE) : 0;
+      }
       // The query operand is built while the first pages stream in: without rotation the
       // query loads are issued before the prologue DMAs (vmcnt retires them first); with
       // rotation the query is staged and rotated through LDS before the ring is used.
@@ -903,27 +829,7 @@ struct Kern {
       } else {
         load_q_regs(qr, args, cx, b, hq0);
       }
-      stream_pairs(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs);
-    }
-    // Remaining quantized pages (an odd full page and/or the partial page): one masked pair.
-    const int qend = qpages;
-    const bool tail = sq == tp % SQ && 2 * tp < qend;
-    if (tail && npairs == 0) {  // the query operand was not built in the fast path
-      stage_q(args, lds, b, hq0, args.rotation != 0);
-      build_q(cx, lds);
-    }
-    for (int p = 2 * tp; tail && p < qend; p += 2) {
-      PageData A, B;
-      const int va = (nq - p * KVQ_PAGE) < KVQ_PAGE ? (nq - p * KVQ_PAGE) : KVQ_PAGE;
-      load_page(A, cx, rec_ptr(p), lay);
-      int vb = 0;
-      if (p + 1 < qend) {
-        vb = (nq - (p + 1) * KVQ_PAGE) < KVQ_PAGE ? (nq - (p + 1) * KVQ_PAGE) : KVQ_PAGE;
-        load_page(B, cx, rec_ptr(p + 1), lay);
-      } else {
-        zero_page(B);
-      }
-      process_pair<true>(cx, st, A, B, va, vb);
+      stream_pairs(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
     }
     write_partial<false>(args, cx, st, nullptr, lds, b, kvh, split);
   }
@@ -936,7 +842,8 @@ struct Kern {
   // every request site is fixed, so the cursor moves by constant strides), and the slot addresses
   // rotate through the ring, so the loop does no index arithmetic beyond those steps.
   static __device__ __forceinline__ void stream_pairs(const KvqAttnArgs &args, Ctx &cx, State<NVG> &st, uint8_t *smem,
-                                                      const QRegs &qr, int b, int kvh, int sq, int SQ, int npairs) {
+                                                      const QRegs &qr, int b, int kvh, int sq, int SQ, int npairs,
+                                                      bool tail, int tail_va, int tail_vb) {
     const KvqLayout &lay = args.lay;
     const int lane = cx.lane, Hkv = args.Hkv;
     const int rec = lay.record, rec16 = rec / 16;
@@ -951,6 +858,8 @@ struct Kern {
     const size_t page_stride = (size_t)args.cache.batch * Hkv * rec;  // contiguous: page p -> p + 1
     const size_t pair_step = 2 * (size_t)SQ * page_stride;            // contiguous: pair j -> j + SQ
     const uint8_t *cur = pages + ((size_t)b * Hkv + kvh) * rec + 2 * (size_t)sq * page_stride;
+    // Block-table entries are wave-uniform: read them with scalar loads (constant address space) so
+    // that waiting for one never drains the vector-memory queue of requested pages.
     typedef const __attribute__((address_space(4))) int32_t *const_i32p;
     const_i32p tcur = (const_i32p)args.cache.block_table + (int64_t)b * args.cache.mbps + 2 * sq;
     const int pool_last = (int)(args.cache.pool_pages - 1);
@@ -958,34 +867,37 @@ struct Kern {
     const uint32_t ring0 = (uint32_t)(uintptr_t)smem, ring_end = ring0 + NPS * REC_BYTES;
     uint32_t wslot = ring0, rslot = ring0;
     auto next_slot = [&](uint32_t sl) { return sl + REC_BYTES == ring_end ? ring0 : sl + REC_BYTES; };
-    auto issue = [&](bool odd) {
+    const int npages = 2 * (npairs + (tail ? 1 : 0));
+    // A masked pair with no second page requests its first page twice (never past the cache).
+    const bool dup_last = tail && tail_vb == 0;
+    auto issue = [&](bool odd, int k) {
+      const bool dup = odd && dup_last && k == npages - 1;
       const uint8_t *src;
       if (paged) {
-        int e = tcur[odd ? 1 : 0];
+        int e = tcur[(odd && !dup) ? 1 : 0];
         e = e < 0 ? 0 : (e > pool_last ? pool_last : e);
         src = pages + ((size_t)e * Hkv + kvh) * rec;
         if (odd) tcur += 2 * SQ;
       } else {
-        src = odd ? cur + page_stride : cur;
+        src = (odd && !dup) ? cur + page_stride : cur;
         if (odd) cur += pair_step;
       }
       dma_page_buf(wslot, src, rec, loff, lane);
       wslot = next_slot(wslot);
     };
-    const int npages = 2 * npairs;
 #pragma unroll
     for (int k = 0; k < AHEAD; ++k)
-      if (k < npages) issue((k & 1) != 0);
+      if (k < npages) issue((k & 1) != 0, k);
     if (!args.rotation) build_q_regs(cx, qr, args.q_f32);
     constexpr bool FIRST_ODD = (AHEAD & 1) != 0;  // parity of page 2i + AHEAD
     for (int i = 0; i < npairs; ++i) {
       const int k0 = 2 * i + AHEAD;
       if (k0 + 1 < npages) {  // steady state: two requests, AHEAD pages stay in flight
-        issue(FIRST_ODD);
-        issue(!FIRST_ODD);
+        issue(FIRST_ODD, k0);
+        issue(!FIRST_ODD, k0 + 1);
         wait_vmcnt<AHEAD * DMAS_PER_PAGE>();
       } else {  // the last pairs: at most one more request, then drain
-        if (k0 < npages) issue(FIRST_ODD);
+        if (k0 < npages) issue(FIRST_ODD, k0);
         wait_vmcnt<0>();
       }
       PageData A, B;
@@ -994,6 +906,14 @@ struct Kern {
       read_page_at(B, cx, rslot, lay);
       rslot = next_slot(rslot);
       process_pair<false>(cx, st, A, B, 16, 16);
+    }
+    if (tail) {  // its pages were requested with the others
+      wait_vmcnt<0>();
+      PageData A, B;
+      read_page_at(A, cx, rslot, lay);
+      rslot = next_slot(rslot);
+      read_page_at(B, cx, rslot, lay);
+      process_pair<true>(cx, st, A, B, tail_va, tail_vb);
     }
   }
 
