@@ -625,22 +625,46 @@ struct Kern {
     pair_values<MASKED>(cx, st, A, B, s0, s1, validA, validB);
   }
 
-  // Window tokens [w0, w0 + 32) of the ring (valid below wend): scores on MFMA, values on the VALU.
-  // Value rows are requested before the scores are computed (all 32 rows for bf16, the first
-  // 16 for fp32), so their latency overlaps the key loads and the MFMAs.
+  // Window tokens [w0, w0 + 32) of the ring (valid below wend), scores on MFMA.  The values of
+  // a bf16 ring go through MFMA as well (exact bf16 B operand, weights as the hi/lo A operand
+  // of the quantized path, accumulated in st.acc); those of an fp32 ring are accumulated on the
+  // VALU in ow.  Value data is requested before the scores are computed, so its latency overlaps
+  // the key loads and the MFMAs.
   template <bool F32>
   static __device__ __forceinline__ void window_chunk(const Ctx &cx, State<NVG> &st, float (*ow)[2],
                                                       const uint8_t *kwin, const uint8_t *vwin, int w0, int wend) {
-    constexpr int VT = F32 ? 16 : 32;  // value rows held in registers at once
-    using VRow = typename std::conditional<F32, f32x2e, uint32_t>::type;
     const int nval = (wend - w0) < 32 ? (wend - w0) : 32;
-    // this lane's two channels of value row w0 + t (rows past the end re-read row w0)
-    auto vload = [&](int t) -> VRow {
-      return gload<VRow>(vwin + ((size_t)(w0 + (t < nval ? t : 0)) * KVQ_D + 2 * cx.lane) * (F32 ? 4 : 2));
+    // fp32: this lane's two channels of value row w0 + t (rows past the end re-read row w0)
+    constexpr int VT = 16;
+    auto vload = [&](int t) -> f32x2e {
+      return gload<f32x2e>(vwin + ((size_t)(w0 + (t < nval ? t : 0)) * KVQ_D + 2 * cx.lane) * 4);
     };
-    VRow vr[VT];
+    f32x2e vr[F32 ? VT : 1];
+    // bf16: B operand of value tile m for this lane = channel 16 m + col of the 8 tokens of its k
+    // slots (slot j: token 4 quad + j for j < 4, 16 + 4 quad + j - 4 after; the order in which
+    // weights_operand places the weights), packed in pairs.
+    uint32_t vb[F32 ? 1 : 8][4];
+    if constexpr (F32) {
 #pragma unroll
-    for (int t = 0; t < VT; ++t) vr[t] = vload(t);
+      for (int t = 0; t < VT; ++t) vr[t] = vload(t);
+    } else {
+      const uint16_t *vrow[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int t = j < 4 ? 4 * cx.quad + j : 16 + 4 * cx.quad + (j - 4);
+        t = t < nval ? t : 0;  // rows past the end re-read row w0 (their weight is 0)
+        vrow[j] = reinterpret_cast<const uint16_t *>(vwin) + (size_t)(w0 + t) * KVQ_D + cx.col;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = gload<uint16_t>(vrow[2 * i] + 16 * m);
+          const uint32_t hi = gload<uint16_t>(vrow[2 * i + 1] + 16 * m);
+          vb[m][i] = lo | (hi << 16);
+        }
+      }
+    }
     float s[2][4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -683,35 +707,35 @@ struct Kern {
         s[sub][r] = (w0 + 16 * sub + 4 * cx.quad + r < wend) ? acc : -__builtin_inff();
       }
     }
-    softmax_update<true, true>(cx, st, s[0], s[1], ow);
-    // Values: this lane owns channels 2*lane, 2*lane+1; p of (head h, token) lives in lane 16*quad + h.
+    if constexpr (F32) {
+      softmax_update<true, true>(cx, st, s[0], s[1], ow);
+      // Values: this lane owns channels 2*lane, 2*lane+1; p of (head h, token) lives in lane 16*quad + h.
 #pragma unroll
-    for (int half = 0; half < 32 / VT; ++half) {
-      if (half > 0) {
+      for (int half = 0; half < 32 / VT; ++half) {
+        if (half > 0) {
 #pragma unroll
-        for (int t = 0; t < VT; ++t) vr[t] = vload(VT * half + t);
-      }
-      // Tokens past the end carry p = 0 (their scores were -inf), so the loop runs in full.
-#pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        const int tk = VT * half + t;
-        const int sub = tk >> 4, tq = (tk & 15) >> 2, r = tk & 3;
-        const float pv = s[sub][r];
-        float v0, v1;
-        if constexpr (F32) {
-          v0 = vr[t].x;
-          v1 = vr[t].y;
-        } else {
-          v0 = kvq_bf16_bits_to_f32(vr[t] & 0xFFFF);
-          v1 = kvq_bf16_bits_to_f32(vr[t] >> 16);
+          for (int t = 0; t < VT; ++t) vr[t] = vload(VT * half + t);
         }
+        // Tokens past the end carry p = 0 (their scores were -inf), so the loop runs in full.
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), 16 * tq + h));
-          ow[h][0] = __builtin_fmaf(p, v0, ow[h][0]);
-          ow[h][1] = __builtin_fmaf(p, v1, ow[h][1]);
+        for (int t = 0; t < VT; ++t) {
+          const int tk = VT * half + t;
+          const int sub = tk >> 4, tq = (tk & 15) >> 2, r = tk & 3;
+          const float pv = s[sub][r];
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), 16 * tq + h));
+            ow[h][0] = __builtin_fmaf(p, vr[t].x, ow[h][0]);
+            ow[h][1] = __builtin_fmaf(p, vr[t].y, ow[h][1]);
+          }
         }
       }
+    } else {
+      softmax_update<true, false>(cx, st, s[0], s[1], nullptr);
+      const bf16x8 Aop = weights_operand(cx, s[0], s[1]);
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, pack8(vb[m][0], vb[m][1], vb[m][2], vb[m][3]), st.acc[m], 0, 0, 0);
     }
   }
 
@@ -796,7 +820,10 @@ struct Kern {
             window_chunk<false>(cx, st, ow, args.cache.k_win + win_off, args.cache.v_win + win_off, w, wend);
         }
       }
-      write_partial<true>(args, cx, st, ow, lds, b, kvh, split);
+      if (args.kv_f32)
+        write_partial<PART_WIN_VALU>(args, cx, st, ow, lds, b, kvh, split);
+      else
+        write_partial<PART_WIN_ACC>(args, cx, st, ow, lds, b, kvh, split);
       return;
     }
 
@@ -831,7 +858,7 @@ struct Kern {
       }
       stream_pairs(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
     }
-    write_partial<false>(args, cx, st, nullptr, lds, b, kvh, split);
+    write_partial<PART_CODES>(args, cx, st, nullptr, lds, b, kvh, split);
   }
 
   // Pairs sq, sq + SQ, ... (npairs of them) of one unit through the wave's LDS ring of NPS page
@@ -919,9 +946,14 @@ struct Kern {
 
   // Reduce the state across rows/replicas and write this split's partial result:
   // [m (log2 units), l, 0, 0, o[128]] per query head, o unnormalised.
-  template <bool WIN>
+  // MODE: PART_CODES (quantized pages: value-code scales and zero-point sums apply),
+  // PART_WIN_ACC (bf16 window: MFMA accumulators hold the output as is), PART_WIN_VALU (fp32
+  // window: the output is in ow).
+  static constexpr int PART_CODES = 0, PART_WIN_ACC = 1, PART_WIN_VALU = 2;
+  template <int MODE>
   static __device__ __forceinline__ void write_partial(const KvqAttnArgs &args, const Ctx &cx, const State<NVG> &st,
                                                        float (*ow)[2], float *lds, int b, int kvh, int split) {
+    constexpr bool WIN = MODE != PART_CODES;
     const int lane = threadIdx.x;
     const int hq0 = kvh * G;
     const float l = rows_sum(st.l);
@@ -931,7 +963,7 @@ struct Kern {
     __syncthreads();
     float *accs = lds;                 // [2G][128]
     float *hdr = lds + 2 * G * KVQ_D;  // [G][4]: m, l, z0, z1
-    if constexpr (!WIN) {
+    if constexpr (MODE != PART_WIN_VALU) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
@@ -957,8 +989,10 @@ struct Kern {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int c = 2 * lane + e;
-        if constexpr (WIN) {
+        if constexpr (MODE == PART_WIN_VALU) {
           o[e] = ow[h][e];
+        } else if constexpr (MODE == PART_WIN_ACC) {
+          o[e] = accs[h * KVQ_D + c] + accs[(G + h) * KVQ_D + c];
         } else {
           const float a = accs[h * KVQ_D + c] + accs[(G + h) * KVQ_D + c];
           const float outscale = __builtin_amdgcn_ldexpf(1.0f, (int)P_BIAS_LOG2 - vtile_scale(c >> 4));
