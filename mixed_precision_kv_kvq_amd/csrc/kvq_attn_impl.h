@@ -20,8 +20,10 @@
 // always the softmax weights p * scale).  Scale, zero, exponent and max
 // bookkeeping stays in fp32 on the VALU.
 //
-// One 64-lane wave per (sequence, kv head, split); a split is a run of
-// 16-token pages.  Per pair of pages (32 tokens):
+// One 64-lane wave per (sequence, kv head, split).  A quantized split takes every
+// S_q-th pair of 16-token pages of its sequence and kv head (the page records are
+// streamed into an LDS ring, see stream_pairs); a window split takes 128 tokens of
+// the recent window.  Per pair of pages (32 tokens):
 //   K: 4 MFMAs per page, A = codes (rows = 16 tokens, k = 32 channels of one
 //      chunk), B = query matrix whose 16 columns hold the g heads replicated
 //      16/g times; replica slots carry different 32-channel chunks (and the hi
@@ -29,10 +31,9 @@
 //      per-chunk partial dots that a row-rotation DPP all-reduce sums.
 //   V: 8 MFMAs (one per 16-channel tile), A = softmax weights (rows = hi/lo
 //      part x head, k = 32 tokens), B = value codes (k = tokens, col = channel).
-// Every operand comes from one coalesced load per lane (see kvq_layout.h).
+// Every operand comes from one 4- to 16-byte read per lane of the page record (see
+// kvq_layout.h for the order of the record's words).
 #pragma once
-#include <type_traits>
-
 #include "kvq_internal.h"
 
 namespace kvq_attn {
