@@ -24,15 +24,19 @@
 // S_q-th pair of 16-token pages of its sequence and kv head (the page records are
 // streamed into an LDS ring, see stream_pairs); a window split takes 128 tokens of
 // the recent window.  Per pair of pages (32 tokens):
-//   K: 4 MFMAs per page, A = codes (rows = 16 tokens, k = 32 channels of one
-//      chunk), B = query matrix whose 16 columns hold the g heads replicated
-//      16/g times; replica slots carry different 32-channel chunks (and the hi
-//      and lo parts of the query), zero elsewhere, so one accumulator collects
-//      per-chunk partial dots that a row-rotation DPP all-reduce sums.
+//   K: per page and 32-channel chunk, one MFMA per score accumulator with
+//      A = query rows (head slot q, chunk j; only rows of the chunk being
+//      contracted are non-zero) and B = codes (k = 32 channels, col = 16 tokens).
+//      Lane 16 q + t then holds, in accumulator row r, head q's partial dot with
+//      chunk r of token t, so the group scales and zero points are applied and the
+//      chunks summed inside the lane: one score per (token, head) per lane, no
+//      cross-lane reduction and no replicated softmax work.
 //   V: 8 MFMAs (one per 16-channel tile), A = softmax weights (rows = hi/lo
 //      part x head, k = 32 tokens), B = value codes (k = tokens, col = channel).
-// Every operand comes from one 4- to 16-byte read per lane of the page record (see
-// kvq_layout.h for the order of the record's words).
+//      The weights reach the A-operand layout through a small per-wave LDS
+//      exchange buffer (four 2-byte writes and one 16-byte read per lane).
+// Every code and metadata operand comes from one 4- to 16-byte read per lane of the
+// page record (see kvq_layout.h for the order of the record's words).
 #pragma once
 #include "kvq_internal.h"
 
@@ -113,28 +117,9 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) { return pack_bf16x2(f, 0.
 __device__ __forceinline__ float bf16lo_f32(uint32_t pair) { return __builtin_bit_cast(float, pair << 16); }
 __device__ __forceinline__ float bf16hi_f32(uint32_t pair) { return __builtin_bit_cast(float, pair & 0xFFFF0000u); }
 
-__device__ __forceinline__ float ror_add(float v, int sh) {
-  int r;
-  switch (sh) {
-    case 8: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false); break;
-    default: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false); break;
-  }
-  return v + __builtin_bit_cast(float, r);
-}
-
-// Reductions over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48)
-// with v_permlane16_swap / v_permlane32_swap: swapping a value with itself
-// leaves the xor-16 (xor-32) partner pair in the two results.
-__device__ __forceinline__ float rows_max(float v) {
-  const int b = __builtin_bit_cast(int, v);
-  auto p16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  v = __builtin_fmaxf(__builtin_bit_cast(float, (int)p16[0]), __builtin_bit_cast(float, (int)p16[1]));
-  const int c = __builtin_bit_cast(int, v);
-  auto p32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
-  return __builtin_fmaxf(__builtin_bit_cast(float, (int)p32[0]), __builtin_bit_cast(float, (int)p32[1]));
-}
+// Sum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48) with
+// v_permlane16_swap / v_permlane32_swap: swapping a value with itself leaves the
+// xor-16 (xor-32) partner pair in the two results.
 __device__ __forceinline__ float rows_sum(float v) {
   const int b = __builtin_bit_cast(int, v);
   auto p16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
@@ -142,13 +127,6 @@ __device__ __forceinline__ float rows_sum(float v) {
   const int c = __builtin_bit_cast(int, v);
   auto p32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
   return __builtin_bit_cast(float, (int)p32[0]) + __builtin_bit_cast(float, (int)p32[1]);
-}
-
-template <int G>
-__device__ __forceinline__ float replica_allreduce(float v) {
-#pragma unroll
-  for (int sh = 8; sh >= G; sh >>= 1) v = ror_add(v, sh);
-  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -194,34 +172,55 @@ struct RawWords<8> {
   __device__ __forceinline__ uint32_t w(int i) const { return i < 4 ? a[i] : b[i - 4]; }
 };
 
-// Per-wave running state of the online softmax.
-template <int NVG>
+// Reductions over the 16 lanes of one row of the wave (lanes 16q .. 16q + 15): row
+// rotations by 8, 4, 2, 1 leave the full result in every lane of the row.
+__device__ __forceinline__ float row_ror(float v, int sh) {
+  int r;
+  switch (sh) {
+    case 8: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int sh = 8; sh >= 1; sh >>= 1) v += row_ror(v, sh);
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+  for (int sh = 8; sh >= 1; sh >>= 1) v = __builtin_fmaxf(v, row_ror(v, sh));
+  return v;
+}
+
+// Per-wave running state of the online softmax.  Score-side values (m, l, z) live in the
+// score layout: lane 16 q + t holds token column t of heads q + 4 hb.
+template <int HB, int NVG>
 struct State {
-  f32x4 acc[8];     // value MFMA accumulators (rows = part x head, col = channel)
-  float m;          // running max of this lane's head, in score units
-  float l;          // this lane's partial sum of p
-  float zacc[NVG];  // this lane's partial sum of p * zero_v per value group
+  f32x4 acc[8];        // value MFMA accumulators (rows = part x head, col = channel)
+  float m[HB];         // running max of head q + 4 hb, in score units (uniform in the row)
+  float l[HB];         // this lane's partial sum of p
+  float z[HB][NVG];    // this lane's partial sum of p * zero_v per value group
 };
 
 template <int KB, int VB, int G, int P, int NVG>
 struct Kern {
-  static constexpr int REP = 16 / G;        // replicas of each head in the 16 columns
-  static constexpr int X = REP / P;         // chunk slots per query part
-  static constexpr int XE = X < 4 ? X : 4;  // chunk slots in use
-  static constexpr int NACC = 4 / XE;       // score accumulators
+  static constexpr int HB = (G + 3) / 4;   // head blocks: row q of the score layout holds heads q + 4 hb
+  static constexpr int HSN = G < 4 ? G : 4;  // rows of the score layout in use
+  static constexpr int NACC = HB;           // score accumulators (both query parts add into one)
   static constexpr int PERK = 16 / KB;
-  static constexpr uint32_t MASKK = ((1u << KB) - 1u) * 0x00010001u;
-  static constexpr uint32_t MASKV = ((1u << VB) - 1u) * 0x00010001u;
+  typedef State<HB, NVG> St;
 
   struct Ctx {
-    bf16x8 qB[4];    // query operand per 32-channel chunk
-    float Qs[NACC];  // sum of this column's query operand per accumulator, x 2^-133
-    int kmeta_off[NACC];
-    int vmeta_off[NVG];
+    bf16x8 qA[P][HB][4];  // query operand per part, head block and 32-channel chunk
+    float Qc[HB][4];     // sum of the query operand over chunk r of head quad + 4 hb, x 2^-133
+    uint32_t xw;         // exchange-buffer address of this lane's (head row, page-A slot)
+    uint32_t xr;         // exchange-buffer address of this lane's A-operand row segment
     int lane, col, quad;
-    float sig;     // softmax scale in score units (log2 domain)
-    float tau;     // lazy-max margin in score units (16 in log2 units)
-    float sel_lo;  // 1 for rows that carry the low bf16 part of the weights
+    float sig;  // softmax scale in score units (log2 domain)
+    float tau;  // lazy-max margin in score units (16 in log2 units)
   };
 
   // Scale (log2) at which the key codes of chunk kc, pair slot i are read (see field_pair).
@@ -229,113 +228,132 @@ struct Kern {
     return field_scale_log2<KB>(KB * ((4 * kc + i) % PERK));
   }
 
-  // Build the query operand from q (fp32, [G][128] in LDS).  For code operands
-  // (code_scaled), entries of slots whose codes are read scaled by 2^k are
-  // divided by 2^k (exact); raw window keys need the unscaled operand.
-  static __device__ __forceinline__ void build_q(Ctx &cx, const float *qs, bool code_scaled = true) {
-    const int h = cx.col % G;
-    build_q_with(cx, [&](int, int, int ch) { return qs[h * KVQ_D + ch]; }, code_scaled);
+  // The query operand (A of the score contraction).  Row rho = 4 hs + j of head block hb
+  // holds head hs + 4 hb (part: hi or lo bf16 part of q * 2^100, both contracted into the
+  // same accumulator) restricted to chunk j: in the contraction of chunk kc only rows with j == kc are
+  // non-zero, so D row 4 q + r (lane 16 q + t) collects head q's partial dot with
+  // chunk r of token t.  getq(hb, e) returns the fp32 query of head (lane & 15) / 4 + 4 hb
+  // at channel 32 ((lane & 15) % 4) + 8 (lane / 16) + e.  For code operands
+  // (code_scaled) the entries of slots whose codes are read scaled by 2^k are divided
+  // by 2^k (exact); raw window keys need the unscaled operand.
+  template <class GetQ>
+  static __device__ __forceinline__ void build_q_with(Ctx &cx, GetQ getq, bool code_scaled) {
+    const int rho = cx.lane & 15, hs = rho >> 2, j = rho & 3;
+    const bool live = hs < HSN;
+    float qsum[P][HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = live ? getq(hb, e) * EXP2_EQ : 0.f;
+#pragma unroll
+      for (int part = 0; part < P; ++part) {
+        float e0[4], e1[4];
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t pr = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+          if (part == 1) pr = pack_bf16x2(v[2 * i] - bf16lo_f32(pr), v[2 * i + 1] - bf16hi_f32(pr));
+          e0[i] = bf16lo_f32(pr);
+          e1[i] = bf16hi_f32(pr);
+          s += e0[i] + e1[i];
+        }
+        qsum[part][hb] = s;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float f = code_scaled ? __builtin_amdgcn_ldexpf(1.0f, -kslot_scale(kc, i)) : 1.0f;
+            w[i] = kc == j ? pack_bf16x2(e0[i] * f, e1[i] * f) : 0u;  // exact: power-of-two scaling
+          }
+          cx.qA[part][hb][kc] = pack8(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
+    // Chunk sums: the four lanes of a row rho (one per channel octet) hold its 32 channels.
+#pragma unroll
+    for (int part = 0; part < P; ++part) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) qsum[part][hb] = rows_sum(qsum[part][hb]) * EXP2_M66 * EXP2_M67;
+    }
+    // Lane 16 q + t needs the sums of rows 4 q + r (its head, chunk r), both parts.
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float q = 0.f;
+#pragma unroll
+        for (int part = 0; part < P; ++part) q += __shfl(qsum[part][hb], 4 * cx.quad + r);
+        cx.Qc[hb][r] = q;
+      }
+    }
   }
 
-  // This lane's query channels 32 kc + 8 quad + j (j < 8, all four kc) of its head, straight
-  // from global memory: 16-byte loads, fp32 or bf16 as stored.
+  // Query from LDS (fp32 [G][128]).
+  static __device__ __forceinline__ void build_q(Ctx &cx, const float *qs, bool code_scaled = true) {
+    const int rho = cx.lane & 15, hs = (rho >> 2) < HSN ? (rho >> 2) : 0, ch0 = 32 * (rho & 3) + 8 * cx.quad;
+    build_q_with(cx, [&](int hb, int e) { return qs[(hs + 4 * hb) * KVQ_D + ch0 + e]; }, code_scaled);
+  }
+
+  // This lane's query channels (one octet of one chunk per head block), straight from global
+  // memory: 16-byte loads, fp32 or bf16 as stored.
   struct QRegs {
-    u32x4 v[4][2];
+    u32x4 v[HB][2];
   };
   static __device__ __forceinline__ void load_q_regs(QRegs &qr, const KvqAttnArgs &args, const Ctx &cx, int b,
                                                      int hq0) {
-    const uint8_t *row =
-        (const uint8_t *)args.q + ((size_t)b * args.Hq + hq0 + cx.col % G) * KVQ_D * (args.q_f32 ? 4 : 2);
+    const int rho = cx.lane & 15, hs = (rho >> 2) < HSN ? (rho >> 2) : 0, ch0 = 32 * (rho & 3) + 8 * cx.quad;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int ch = 32 * kc + 8 * cx.quad;
+    for (int hb = 0; hb < HB; ++hb) {
+      const uint8_t *row =
+          (const uint8_t *)args.q + ((size_t)b * args.Hq + hq0 + hs + 4 * hb) * KVQ_D * (args.q_f32 ? 4 : 2);
       if (args.q_f32) {
-        qr.v[kc][0] = gload<u32x4>(row + 4 * ch);
-        qr.v[kc][1] = gload<u32x4>(row + 4 * ch + 16);
+        qr.v[hb][0] = gload<u32x4>(row + 4 * ch0);
+        qr.v[hb][1] = gload<u32x4>(row + 4 * ch0 + 16);
       } else {
-        qr.v[kc][0] = gload<u32x4>(row + 2 * ch);
+        qr.v[hb][0] = gload<u32x4>(row + 2 * ch0);
       }
     }
   }
   static __device__ __forceinline__ void build_q_regs(Ctx &cx, const QRegs &qr, bool q_f32) {
     build_q_with(
         cx,
-        [&](int kc, int j, int) {
+        [&](int hb, int e) {
           // (copy the vector element out first: a bit cast of the element lvalue itself
           // reads the vector's first element)
-          const uint32_t u = qr.v[kc][j >> 2][j & 3];
+          const uint32_t u = qr.v[hb][e >> 2][e & 3];
           if (q_f32) return __builtin_bit_cast(float, u);
-          const uint32_t w = qr.v[kc][0][j >> 1];
-          return kvq_bf16_bits_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFF));
+          const uint32_t w = qr.v[hb][0][e >> 1];
+          return kvq_bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFF));
         },
         true);
   }
 
-  // Shared body: getq(kc, j, ch) returns this lane's head's query (fp32) at channel
-  // ch = 32 kc + 8 quad + j.
-  template <class GetQ>
-  static __device__ __forceinline__ void build_q_with(Ctx &cx, GetQ getq, bool code_scaled) {
-    const int y = cx.col / G;
-    const int part = y / X, x = y % X;
-    const bool valid = x < XE;
-    float qsum[NACC];
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) qsum[a] = 0.f;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      uint32_t w[4];
-      const bool use = valid && (kc % XE) == x;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ch = 32 * kc + 8 * cx.quad + 2 * i;
-        const float v0 = use ? getq(kc, 2 * i, ch) * EXP2_EQ : 0.f;
-        const float v1 = use ? getq(kc, 2 * i + 1, ch + 1) * EXP2_EQ : 0.f;
-        uint32_t pr = pack_bf16x2(v0, v1);
-        if (P == 2) {
-          const uint32_t lo = pack_bf16x2(v0 - bf16lo_f32(pr), v1 - bf16hi_f32(pr));
-          pr = part ? lo : pr;
-        }
-        const float e0 = bf16lo_f32(pr), e1 = bf16hi_f32(pr);
-        qsum[kc / XE] += e0 + e1;
-        const float f = code_scaled ? __builtin_amdgcn_ldexpf(1.0f, -kslot_scale(kc, i)) : 1.0f;
-        w[i] = pack_bf16x2(e0 * f, e1 * f);  // exact: power-of-two scaling of bf16 values
-      }
-      cx.qB[kc] = pack8(w[0], w[1], w[2], w[3]);
-    }
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) {
-      cx.Qs[a] = rows_sum(qsum[a]) * EXP2_M66 * EXP2_M67;
-    }
-  }
-
-  static __device__ __forceinline__ void init_ctx(Ctx &cx, const KvqLayout &lay, float sig) {
+  static __device__ __forceinline__ void init_ctx(Ctx &cx, float sig, uint32_t xbase) {
     cx.lane = threadIdx.x;
     cx.col = cx.lane & 15;
     cx.quad = cx.lane >> 4;
     cx.sig = sig;
     cx.tau = 16.0f / sig;
-    const int rowpart = cx.col / G;  // A-operand row of the value MFMA: 0 = hi, 1 = lo, else unused
-    cx.sel_lo = rowpart == 1 ? 1.f : 0.f;
-    const int x = (cx.col / G) % X;
-    const bool valid = x < XE;
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) {
-      const int grp = valid ? ((a * XE + x) * 32) / lay.kg : 0;
-      cx.kmeta_off[a] = lay.k_meta_off + 16 * (cx.quad * lay.nkg + grp);
-    }
-#pragma unroll
-    for (int v = 0; v < NVG; ++v) cx.vmeta_off[v] = lay.v_meta_off + 16 * (cx.quad * NVG + v);
+    // Weights exchange buffer per value group: [16 rows][32 k slots] bf16, row = part * G + head,
+    // slot 8 q' + e: page-A token 4 q' + e (e < 4), page-B token 4 q' + e - 4 (e >= 4).
+    cx.xw = xbase + 64 * cx.quad + 2 * (8 * (cx.col >> 2) + (cx.col & 3));
+    cx.xr = xbase + 64 * cx.col + 16 * cx.quad;
   }
 
+  template <int KS>
   struct PageData {
+    static constexpr int NKM = 4 >> KS;  // key groups per token
     Words<KB> kc;
-    uint4 km[NACC];
+    uint32_t km[NKM];  // this lane's token: {scale, zero} per key group
     Words<VB> vc;
-    uint4 vm[NVG];
+    uint32_t vm[NVG];  // this lane's token: {scale, zero} per value group
   };
 
-  // Key codes of chunk kc of one page as the A operand (slot scales per kslot_scale).
-  static __device__ __forceinline__ bf16x8 key_operand(const PageData &pd, int kc) {
+  // Key codes of chunk kc of one page as the B operand (slot scales per kslot_scale).
+  template <int KS>
+  static __device__ __forceinline__ bf16x8 key_operand(const PageData<KS> &pd, int kc) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -346,138 +364,140 @@ struct Kern {
     return pack8(w[0], w[1], w[2], w[3]);
   }
 
-  static __device__ __forceinline__ float score_epilogue(const Ctx &cx, const PageData &pd, const f32x4 *D, int r) {
+  // Score of this lane's token for head quad + 4 hb: sum over chunks r of
+  // scale_g(r) * (q . c) + sum over groups g of zero_g * sum(q over g).
+  template <int KS>
+  static __device__ __forceinline__ float score_one(const PageData<KS> &pd, const f32x4 *D, const float (*Qg)[4],
+                                                    int hb) {
     float acc = 0.f;
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) {
-      const uint32_t md = u4_get(pd.km[a], r);
-      acc = __builtin_fmaf(h2f(md >> 16), cx.Qs[a], acc);
-      acc = __builtin_fmaf(D[a][r], h2f(md & 0xFFFF), acc);
-    }
-    return replica_allreduce<G>(acc);
+    for (int r = 0; r < 4; ++r) acc = __builtin_fmaf(D[hb][r], h2f(pd.km[r >> KS] & 0xFFFF), acc);
+#pragma unroll
+    for (int g = 0; g < (4 >> KS); ++g) acc = __builtin_fmaf(h2f(pd.km[g] >> 16), Qg[hb][g], acc);
+    return acc;
   }
 
-  // Scores of the 32 tokens of a page pair for this lane's head: s0[r] / s1[r] for token 4*quad + r.
-  static __device__ __forceinline__ void pair_scores(const Ctx &cx, const PageData &A, const PageData &B,
-                                                     float s0[4], float s1[4]) {
-    f32x4 DA[NACC], DB[NACC];
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) {
-      DA[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-      DB[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      DA[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(key_operand(A, kc), cx.qB[kc], DA[kc / XE], 0, 0, 0);
-      DB[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(key_operand(B, kc), cx.qB[kc], DB[kc / XE], 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s0[r] = score_epilogue(cx, A, DA, r);
-      s1[r] = score_epilogue(cx, B, DB, r);
-    }
-  }
-
-  // Online-softmax update with the 8 scores of a page pair; returns p * 2^64 in place.
-  // Lazy running max: weights are formed against the running max m, which is
-  // only raised (with the cross-lane tile max and a rescale of everything
-  // accumulated so far) when some lane sees a score more than 16 (log2 units)
-  // above it, so weights stay below 2^(64+16).  m is always the same in every
-  // lane that holds a given head.
-  template <bool MASKED, bool WIN>
-  static __device__ __forceinline__ void softmax_update(const Ctx &cx, State<NVG> &st, float s0[4], float s1[4],
+  // Online-softmax update with the scores of two 16-token column sets (a page pair, or
+  // two window halves); returns p * 2^64 in place.  Lazy running max: weights are formed
+  // against the running max m, which is only raised (with the row's tile max and a rescale
+  // of everything accumulated so far) when some lane sees a score more than 16 (log2
+  // units) above it, so weights stay below 2^(64+16).
+  template <bool MASKED, bool WINF32>
+  static __device__ __forceinline__ void softmax_update(const Ctx &cx, St &st, float sA[HB], float sB[HB],
                                                         float (*ow)[2]) {
-    float t = __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), __builtin_fmaxf(s0[2], s0[3]));
-    t = __builtin_fmaxf(t, __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), __builtin_fmaxf(s1[2], s1[3])));
-    if (__builtin_amdgcn_ballot_w64(t > st.m + cx.tau)) {
-      t = rows_max(t);  // tile max of this lane's head
-      const float mnew = __builtin_fmaxf(st.m, t);
-      // st.m == -inf gives alpha = 0 (nothing accumulated yet).
-      const float alpha = (mnew > st.m) ? __builtin_amdgcn_exp2f(cx.sig * (st.m - mnew)) : 1.0f;
-      st.l *= alpha;
+    float t[HB];
+    bool up = false;
 #pragma unroll
-      for (int v = 0; v < NVG; ++v) st.zacc[v] *= alpha;
+    for (int hb = 0; hb < HB; ++hb) {
+      t[hb] = __builtin_fmaxf(sA[hb], sB[hb]);
+      up = up || (t[hb] > st.m[hb] + cx.tau);
+    }
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      float alpha[HB];  // per lane, uniform in the row
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const float tm = row16_max(t[hb]);
+        const float mnew = __builtin_fmaxf(st.m[hb], tm);
+        // st.m == -inf gives alpha = 0 (nothing accumulated yet).
+        alpha[hb] = (mnew > st.m[hb]) ? __builtin_amdgcn_exp2f(cx.sig * (st.m[hb] - mnew)) : 1.0f;
+        st.l[hb] *= alpha[hb];
+#pragma unroll
+        for (int v = 0; v < NVG; ++v) st.z[hb][v] *= alpha[hb];
+        st.m[hb] = mnew;
+      }
+      // alpha of head h, wave-uniform: row h mod 4 of the score layout, register h / 4.
+      auto head_alpha = [&](int h) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[h >> 2]), 16 * (h & 3)));
+      };
+      // Value accumulator row 4 quad + r is (part, head (4 quad + r) mod G).
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 4 * cx.quad + r;
-        const float ar = __shfl(alpha, (cx.quad << 4) + (row % G));
+        float ar;
+        if constexpr (G == 8) {
+          const float a0 = head_alpha(r), a1 = head_alpha(4 + r);
+          ar = (cx.quad & 1) ? a1 : a0;
+        } else {
+          ar = head_alpha(r % G);
+        }
 #pragma unroll
         for (int m = 0; m < 8; ++m) st.acc[m][r] *= ar;
       }
-      if constexpr (WIN) {
+      if constexpr (WINF32) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float ah = __shfl(alpha, h);
+          const float ah = head_alpha(h);
           ow[h][0] *= ah;
           ow[h][1] *= ah;
         }
       }
-      st.m = mnew;
     }
-    const float nb = __builtin_fmaf(-cx.sig, st.m, P_BIAS_LOG2);
-    float lsum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.sig, nb));
-      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.sig, nb));
+    for (int hb = 0; hb < HB; ++hb) {
+      const float nb = __builtin_fmaf(-cx.sig, st.m[hb], P_BIAS_LOG2);
+      float pA = __builtin_amdgcn_exp2f(__builtin_fmaf(sA[hb], cx.sig, nb));
+      float pB = __builtin_amdgcn_exp2f(__builtin_fmaf(sB[hb], cx.sig, nb));
       if (MASKED) {
-        p0 = (s0[r] == -__builtin_inff()) ? 0.f : p0;
-        p1 = (s1[r] == -__builtin_inff()) ? 0.f : p1;
+        pA = (sA[hb] == -__builtin_inff()) ? 0.f : pA;
+        pB = (sB[hb] == -__builtin_inff()) ? 0.f : pB;
       }
-      s0[r] = p0;
-      s1[r] = p1;
-      lsum += p0 + p1;
+      st.l[hb] += pA + pB;
+      sA[hb] = pA;
+      sB[hb] = pB;
     }
-    st.l += lsum;
   }
 
-  // Weights operand (A of the value MFMA): rows 0..G-1 carry bf16(w), rows G..2G-1 bf16(w - bf16(w));
-  // rows 2G.. (unused) carry bf16(w) too, which only reaches accumulator rows that are never read.
-  static __device__ __forceinline__ bf16x8 weights_operand(const Ctx &cx, const float w0[4], const float w1[4]) {
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a0 = (i < 2) ? w0[2 * i] : w1[2 * i - 4];
-      const float a1 = (i < 2) ? w0[2 * i + 1] : w1[2 * i - 3];
-      const uint32_t hp = pack_bf16x2(a0, a1);
-      o[i] = pack_bf16x2(__builtin_fmaf(-cx.sel_lo, bf16lo_f32(hp), a0),
-                         __builtin_fmaf(-cx.sel_lo, bf16hi_f32(hp), a1));
+  // Weights of this lane's tokens (page A, page B) for head quad + 4 hb -> exchange buffer v as
+  // bf16 hi part (row head) and lo part (row G + head).  Rows of heads beyond G are not written.
+  static __device__ __forceinline__ void xchg_put(const Ctx &cx, int v, int hb, float wA, float wB) {
+    const uint32_t hi = pack_bf16x2(wA, wB);
+    const uint32_t lo = pack_bf16x2(wA - bf16lo_f32(hi), wB - bf16hi_f32(hi));
+    if (HSN == 4 || cx.quad < HSN) {
+      const uint32_t addr = cx.xw + KVQ_XCHG_BYTES * v + 256 * hb;
+      asm volatile("ds_write_b16 %0, %1" ::"v"(addr), "v"(hi));
+      asm volatile("ds_write_b16_d16_hi %0, %1 offset:8" ::"v"(addr), "v"(hi));
+      asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(addr), "v"(lo), "n"(64 * G));
+      asm volatile("ds_write_b16_d16_hi %0, %1 offset:%2" ::"v"(addr), "v"(lo), "n"(64 * G + 8));
     }
-    return pack8(o[0], o[1], o[2], o[3]);
+  }
+  // A operand of the value contraction for value group v (LDS operations of a wave complete in
+  // order, so this read sees the writes above).
+  static __device__ __forceinline__ u32x4 xchg_get(const Ctx &cx, int v) {
+    u32x4 x;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(x) : "v"(cx.xr + KVQ_XCHG_BYTES * v));
+    return x;
   }
 
   // Scale (log2) at which the value codes of tile m are read (independent of the pair slot).
   static __device__ __forceinline__ constexpr int vtile_scale(int m) { return field_scale_log2<VB>((m * VB) & 15); }
 
-  // Value contraction of a page pair with weights p0 (page A) and p1 (page B), both carried as p * 2^64.
-  template <bool MASKED>
-  static __device__ __forceinline__ void pair_values(const Ctx &cx, State<NVG> &st, const PageData &A,
-                                                     const PageData &B, const float p0[4], const float p1[4],
+  // Value contraction of a page pair: weights p (carried as p * 2^64) times the value scale of
+  // each token go through the exchange buffer into the A operand, the masked codes are B.
+  template <int KS, bool MASKED>
+  static __device__ __forceinline__ void pair_values(const Ctx &cx, St &st, const PageData<KS> &A,
+                                                     const PageData<KS> &B, const float pA[HB], const float pB[HB],
                                                      int validA, int validB) {
-    bf16x8 Aop[NVG];
 #pragma unroll
     for (int v = 0; v < NVG; ++v) {
-      float w0[4], w1[4];
-      float z = st.zacc[v];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t ma = u4_get(A.vm[v], r), mb = u4_get(B.vm[v], r);
-        float sa = h2f(ma & 0xFFFF), za = h2f(ma >> 16), sb = h2f(mb & 0xFFFF), zb = h2f(mb >> 16);
-        if (MASKED) {  // metadata of invalid tokens may be anything, keep it out
-          const bool va = 4 * cx.quad + r < validA, vb = 4 * cx.quad + r < validB;
-          sa = va ? sa : 0.f;
-          za = va ? za : 0.f;
-          sb = vb ? sb : 0.f;
-          zb = vb ? zb : 0.f;
-        }
-        w0[r] = __builtin_fmaf(p0[r], sa, 0.f);
-        w1[r] = __builtin_fmaf(p1[r], sb, 0.f);
-        z = __builtin_fmaf(p0[r], za, z);
-        z = __builtin_fmaf(p1[r], zb, z);
+      float sa = h2f(A.vm[v] & 0xFFFF), za = h2f(A.vm[v] >> 16), sb = h2f(B.vm[v] & 0xFFFF),
+            zb = h2f(B.vm[v] >> 16);
+      if (MASKED) {  // metadata of invalid tokens may be anything, keep it out
+        const bool va = cx.col < validA, vb = cx.col < validB;
+        sa = va ? sa : 0.f;
+        za = va ? za : 0.f;
+        sb = vb ? sb : 0.f;
+        zb = vb ? zb : 0.f;
       }
-      st.zacc[v] = z;
-      Aop[v] = weights_operand(cx, w0, w1);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        st.z[hb][v] = __builtin_fmaf(pB[hb], zb, __builtin_fmaf(pA[hb], za, st.z[hb][v]));
+        xchg_put(cx, v, hb, pA[hb] * sa, pB[hb] * sb);
+      }
     }
+    u32x4 xa[NVG];
+#pragma unroll
+    for (int v = 0; v < NVG; ++v) xa[v] = xchg_get(cx, v);
+    if constexpr (NVG == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xa[0])::"memory");
+    if constexpr (NVG == 2) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xa[0]), "+v"(xa[1])::"memory");
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       uint32_t w[4];
@@ -487,7 +507,9 @@ struct Kern {
         const uint32_t word = (i < 2) ? A.vc.w[pos >> 4] : B.vc.w[pos >> 4];
         w[i] = field_pair<VB>(word, word >> 8, pos & 15);
       }
-      st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop[m / (8 / NVG)], pack8(w[0], w[1], w[2], w[3]), st.acc[m], 0, 0, 0);
+      const u32x4 x = xa[m / (8 / NVG)];
+      st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), pack8(w[0], w[1], w[2], w[3]),
+                                                          st.acc[m], 0, 0, 0);
     }
   }
 
@@ -496,10 +518,11 @@ struct Kern {
   static constexpr int REC_BYTES = 16 * MAX_REC16;              // ring slot stride
   static constexpr int DMAS_PER_PAGE = (MAX_REC16 + 63) / 64;
   static constexpr int WPE = kvq_attn_wpe(KB, VB, G, P, NVG);       // waves per SIMD
-  static constexpr int NPS = kvq_ring_pages(REC_BYTES, WPE);   // page slots
-  static constexpr int AHEAD = NPS - 2;                         // pages in flight while a pair is processed
+  static constexpr int NPS = kvq_ring_pages(REC_BYTES, WPE, NVG);  // page slots
+  static constexpr int AHEAD = NPS - 2;                             // pages in flight while a pair is processed
+  static constexpr int XCHG_OFF = NPS * REC_BYTES;                  // exchange buffers after the ring
   static constexpr int LDS_BYTES = kvq_attn_lds_bytes(KB, VB, NVG, WPE);
-  static_assert(LDS_BYTES >= NPS * REC_BYTES && LDS_BYTES >= KVQ_STAGE_BYTES, "LDS sizing");
+  static_assert(LDS_BYTES >= XCHG_OFF + KVQ_XCHG_BYTES * NVG && LDS_BYTES >= KVQ_STAGE_BYTES, "LDS sizing");
   static_assert(AHEAD * DMAS_PER_PAGE <= 63, "vmcnt range");
 
   // Copy one page record into an LDS slot: DMAS_PER_PAGE wave-wide DMAs, lane l of DMA k writing
@@ -519,8 +542,9 @@ struct Kern {
 
   // Read one page of a ring slot.  The reads are inline asm: the compiler cannot
   // tell that they do not alias the ring's in-flight DMAs and would otherwise
-  // drain every outstanding load before them.  A single lgkmcnt(0) wait ties
-  // every read result, and nothing touches a result before that wait.
+  // drain every outstanding load before them.  One lgkmcnt(0) wait follows them, and
+  // every result passes through an empty asm statement placed after that wait before
+  // anything uses it.
   template <int N>
   static __device__ __forceinline__ void ds_read_words(RawWords<N> &d, uint32_t addr) {
     if constexpr (N == 1) {
@@ -534,121 +558,112 @@ struct Kern {
       asm volatile("ds_read_b128 %0, %1 offset:16" : "=v"(d.b) : "v"(addr));
     }
   }
+  template <int N>
+  static __device__ __forceinline__ void tie(RawWords<N> &d) {
+    if constexpr (N == 8)
+      asm volatile("" : "+v"(d.a), "+v"(d.b));
+    else
+      asm volatile("" : "+v"(d.v));
+  }
 
-  static __device__ __forceinline__ void read_page_at(PageData &pd, const Ctx &cx, uint32_t base,
-                                                      const KvqLayout &lay) {
+  // Offsets of this lane's operands inside a record.
+  struct RecOff {
+    uint32_t kc, km, vc, vm;
+  };
+  template <int KS>
+  static __device__ __forceinline__ RecOff rec_offsets(const Ctx &cx, const KvqLayout &lay) {
+    RecOff o;
+    o.kc = lay.k_codes_off + cx.lane * 4 * KB;
+    o.km = lay.k_meta_off + cx.col * 4 * (4 >> KS);
+    o.vc = lay.v_codes_off + cx.lane * 4 * VB;
+    o.vm = lay.v_meta_off + cx.col * 4 * NVG;
+    return o;
+  }
+
+  template <int KS>
+  static __device__ __forceinline__ void read_page_at(PageData<KS> &pd, uint32_t base, const RecOff &o) {
+    constexpr int NKM = 4 >> KS;
     RawWords<KB> rk;
+    RawWords<NKM> rkm;
     RawWords<VB> rv;
-    u32x4 km[NACC], vm[NVG];
-    ds_read_words(rk, base + lay.k_codes_off + cx.lane * 4 * KB);
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) {
-      const uint32_t addr = base + cx.kmeta_off[a];
-      asm volatile("ds_read_b128 %0, %1" : "=v"(km[a]) : "v"(addr));
-    }
-    ds_read_words(rv, base + lay.v_codes_off + cx.lane * 4 * VB);
-#pragma unroll
-    for (int v = 0; v < NVG; ++v) {
-      const uint32_t addr = base + cx.vmeta_off[v];
-      asm volatile("ds_read_b128 %0, %1" : "=v"(vm[v]) : "v"(addr));
-    }
-    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 1 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(rv.v), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 1 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 2 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(rv.v), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 2 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 4 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.v), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == false && NACC == 4 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 1 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 1 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 2 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 2 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 4 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == false && (VB == 8) == true && NACC == 4 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.v), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 1 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(rv.v), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 1 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 2 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(rv.v), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 2 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 4 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.v), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == false && NACC == 4 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.v), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 1 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 1 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 2 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 2 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 4 && NVG == 1)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0])::"memory");
-    if constexpr ((KB == 8) == true && (VB == 8) == true && NACC == 4 && NVG == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rk.a), "+v"(rk.b), "+v"(km[0]), "+v"(km[1]), "+v"(km[2]), "+v"(km[3]), "+v"(rv.a), "+v"(rv.b), "+v"(vm[0]), "+v"(vm[1])::"memory");
+    RawWords<NVG> rvm;
+    ds_read_words(rk, base + o.kc);
+    ds_read_words(rkm, base + o.km);
+    ds_read_words(rv, base + o.vc);
+    ds_read_words(rvm, base + o.vm);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    tie(rk);
+    tie(rkm);
+    tie(rv);
+    tie(rvm);
 #pragma unroll
     for (int i = 0; i < KB; ++i) pd.kc.w[i] = rk.w(i);
 #pragma unroll
+    for (int i = 0; i < NKM; ++i) pd.km[i] = rkm.w(i);
+#pragma unroll
     for (int i = 0; i < VB; ++i) pd.vc.w[i] = rv.w(i);
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) pd.km[a] = make_uint4(km[a].x, km[a].y, km[a].z, km[a].w);
-#pragma unroll
-    for (int v = 0; v < NVG; ++v) pd.vm[v] = make_uint4(vm[v].x, vm[v].y, vm[v].z, vm[v].w);
+    for (int v = 0; v < NVG; ++v) pd.vm[v] = rvm.w(v);
   }
 
-  template <bool MASKED>
-  static __device__ __forceinline__ void process_pair(const Ctx &cx, State<NVG> &st, const PageData &A,
-                                                      const PageData &B, int validA, int validB) {
-    float s0[4], s1[4];
-    pair_scores(cx, A, B, s0, s1);
-    if (MASKED) {
+  // Scores of this lane's token of one page for its heads quad + 4 hb.
+  template <int KS>
+  static __device__ __forceinline__ void page_scores(const Ctx &cx, const float (*Qg)[4], const PageData<KS> &pd,
+                                                     float s[HB]) {
+    f32x4 D[NACC];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s0[r] = (4 * cx.quad + r < validA) ? s0[r] : -__builtin_inff();
-        s1[r] = (4 * cx.quad + r < validB) ? s1[r] : -__builtin_inff();
+    for (int a = 0; a < NACC; ++a) D[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 k = key_operand(pd, kc);
+#pragma unroll
+      for (int part = 0; part < P; ++part) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+          D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], k, D[hb], 0, 0, 0);
       }
     }
-    softmax_update<MASKED, false>(cx, st, s0, s1, nullptr);
-    pair_values<MASKED>(cx, st, A, B, s0, s1, validA, validB);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) s[hb] = score_one(pd, D, Qg, hb);
   }
 
-  // Window tokens [w0, w0 + 32) of the ring (valid below wend), scores on MFMA.  The values of
-  // a bf16 ring go through MFMA as well (exact bf16 B operand, weights as the hi/lo A operand
-  // of the quantized path, accumulated in st.acc); those of an fp32 ring are accumulated on the
-  // VALU in ow.  Value data is requested before the scores are computed, so its latency overlaps
-  // the key loads and the MFMAs.
+  template <int KS, bool MASKED>
+  static __device__ __forceinline__ void process_pair(const Ctx &cx, St &st, const float (*Qg)[4],
+                                                      const PageData<KS> &A, const PageData<KS> &B, int validA,
+                                                      int validB) {
+    float sA[HB], sB[HB];
+    page_scores(cx, Qg, A, sA);
+    page_scores(cx, Qg, B, sB);
+    if (MASKED) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        sA[hb] = cx.col < validA ? sA[hb] : -__builtin_inff();
+        sB[hb] = cx.col < validB ? sB[hb] : -__builtin_inff();
+      }
+    }
+    softmax_update<MASKED, false>(cx, st, sA, sB, nullptr);
+    pair_values<KS, MASKED>(cx, st, A, B, sA, sB, validA, validB);
+  }
+
+  // Window tokens [w0, w0 + 32) of the ring (valid below wend), scores on MFMA with the raw
+  // keys as the B operand.  The values of a bf16 ring go through MFMA as well (exact bf16 B
+  // operand, weights through the exchange buffer as for the quantized pages, accumulated in
+  // st.acc); those of an fp32 ring are accumulated on the VALU in ow.  Value data is requested
+  // before the scores are computed, so its latency overlaps the key loads and the MFMAs.
   template <bool F32>
-  static __device__ __forceinline__ void window_chunk(const Ctx &cx, State<NVG> &st, float (*ow)[2],
-                                                      const uint8_t *kwin, const uint8_t *vwin, int w0, int wend) {
+  static __device__ __forceinline__ void window_chunk(const Ctx &cx, St &st, float (*ow)[2], const uint8_t *kwin,
+                                                      const uint8_t *vwin, int w0, int wend) {
     const int nval = (wend - w0) < 32 ? (wend - w0) : 32;
     // fp32: this lane's two channels of value row w0 + t (rows past the end re-read row w0)
-    constexpr int VT = 16;
+    constexpr int VT = G * P >= 16 ? 8 : 16;  // value rows in registers at a time
     auto vload = [&](int t) -> f32x2e {
       return gload<f32x2e>(vwin + ((size_t)(w0 + (t < nval ? t : 0)) * KVQ_D + 2 * cx.lane) * 4);
     };
     f32x2e vr[F32 ? VT : 1];
     // bf16: B operand of value tile m for this lane = channel 16 m + col of the 8 tokens of its k
-    // slots (slot j: token 4 quad + j for j < 4, 16 + 4 quad + j - 4 after; the order in which
-    // weights_operand places the weights), packed in pairs.
+    // slots (slot j: token 4 quad + j for j < 4, 16 + 4 quad + j - 4 after), packed in pairs.
     uint32_t vb[F32 ? 1 : 8][4];
-    if constexpr (F32) {
-#pragma unroll
-      for (int t = 0; t < VT; ++t) vr[t] = vload(t);
-    } else {
+    auto load_vb = [&]() {
       const uint16_t *vrow[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -665,11 +680,20 @@ struct Kern {
           vb[m][i] = lo | (hi << 16);
         }
       }
+    };
+    // With 16 query rows (8 heads, hi/lo parts) the value rows are fetched after the scores, which
+    // keeps the register footprint inside the occupancy budget.
+    constexpr bool EARLY_V = G * P < 16;
+    if constexpr (F32) {
+#pragma unroll
+      for (int t = 0; t < VT; ++t) vr[t] = vload(t);
+    } else if constexpr (EARLY_V) {
+      load_vb();
     }
-    float s[2][4];
+    float s[2][HB];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      int slot = w0 + 16 * sub + cx.col;  // A-operand row = token
+      int slot = w0 + 16 * sub + cx.col;  // B-operand column = token
       const bool ok = slot < wend;
       slot = ok ? slot : w0;
       f32x4 D[NACC];
@@ -688,29 +712,41 @@ struct Kern {
             hi[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
             lo[i] = pack_bf16x2(f[2 * i] - bf16lo_f32(hi[i]), f[2 * i + 1] - bf16hi_f32(hi[i]));
           }
-          D[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(hi[0], hi[1], hi[2], hi[3]), cx.qB[kc], D[kc / XE], 0, 0, 0);
-          D[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(lo[0], lo[1], lo[2], lo[3]), cx.qB[kc], D[kc / XE], 0, 0, 0);
+          const bf16x8 kh = pack8(hi[0], hi[1], hi[2], hi[3]), kl = pack8(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+          for (int part = 0; part < P; ++part) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+              D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], kh, D[hb], 0, 0, 0);
+              D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], kl, D[hb], 0, 0, 0);
+            }
+          }
         }
       } else {
         u32x4 kr[4];
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) kr[kc] = gload<u32x4>(kwin + ((size_t)slot * KVQ_D + 32 * kc + 8 * cx.quad) * 2);
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          D[kc / XE] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(kr[kc].x, kr[kc].y, kr[kc].z, kr[kc].w), cx.qB[kc], D[kc / XE], 0, 0, 0);
+        for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+          for (int part = 0; part < P; ++part) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+              D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], __builtin_bit_cast(bf16x8, kr[kc]),
+                                                              D[hb], 0, 0, 0);
+          }
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float acc = 0.f;
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) acc += D[a][r];
-        acc = replica_allreduce<G>(acc * EXP2_M66 * EXP2_M67);
-        s[sub][r] = (w0 + 16 * sub + 4 * cx.quad + r < wend) ? acc : -__builtin_inff();
+      for (int hb = 0; hb < HB; ++hb) {
+        const float acc = (D[hb][0] + D[hb][1]) + (D[hb][2] + D[hb][3]);
+        s[sub][hb] = ok ? acc * EXP2_M66 * EXP2_M67 : -__builtin_inff();
       }
     }
+    softmax_update<true, F32>(cx, st, s[0], s[1], ow);
     if constexpr (F32) {
-      softmax_update<true, true>(cx, st, s[0], s[1], ow);
-      // Values: this lane owns channels 2*lane, 2*lane+1; p of (head h, token) lives in lane 16*quad + h.
+      // Values: this lane owns channels 2*lane, 2*lane+1; p of (head h, token tk) lives in lane
+      // 16 (h mod 4) + tk mod 16, register s[tk / 16][h / 4].
 #pragma unroll
       for (int half = 0; half < 32 / VT; ++half) {
         if (half > 0) {
@@ -721,19 +757,23 @@ struct Kern {
 #pragma unroll
         for (int t = 0; t < VT; ++t) {
           const int tk = VT * half + t;
-          const int sub = tk >> 4, tq = (tk & 15) >> 2, r = tk & 3;
-          const float pv = s[sub][r];
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), 16 * tq + h));
+            const float pv = s[tk >> 4][h >> 2];
+            const float p = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), 16 * (h & 3) + (tk & 15)));
             ow[h][0] = __builtin_fmaf(p, vr[t].x, ow[h][0]);
             ow[h][1] = __builtin_fmaf(p, vr[t].y, ow[h][1]);
           }
         }
       }
     } else {
-      softmax_update<true, false>(cx, st, s[0], s[1], nullptr);
-      const bf16x8 Aop = weights_operand(cx, s[0], s[1]);
+      if constexpr (!EARLY_V) load_vb();
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) xchg_put(cx, 0, hb, s[0][hb], s[1][hb]);
+      u32x4 xa = xchg_get(cx, 0);
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xa)::"memory");
+      const bf16x8 Aop = __builtin_bit_cast(bf16x8, xa);
 #pragma unroll
       for (int m = 0; m < 8; ++m)
         st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, pack8(vb[m][0], vb[m][1], vb[m][2], vb[m][3]), st.acc[m], 0, 0, 0);
@@ -793,16 +833,27 @@ struct Kern {
       wv1 = wv0 + KVQ_WIN_PAGES < wpages ? wv0 + KVQ_WIN_PAGES : wpages;
     }
 
+    // Exchange buffers start zeroed: rows no lane writes (heads beyond G) then stay finite.
+    const uint32_t xbase = (uint32_t)(uintptr_t)smem + XCHG_OFF;
+#pragma unroll
+    for (int v = 0; v < NVG; ++v) {
+      const uint32_t addr = xbase + KVQ_XCHG_BYTES * v + 16 * lane;
+      asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(u32x4{0u, 0u, 0u, 0u}));
+    }
+
     Ctx cx;
-    init_ctx(cx, lay, args.sigma_u);
+    init_ctx(cx, args.sigma_u, xbase);
     const int hq0 = kvh * G;
-    State<NVG> st;
+    St st;
 #pragma unroll
     for (int m = 0; m < 8; ++m) st.acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m = -__builtin_inff();
-    st.l = 0.f;
 #pragma unroll
-    for (int v = 0; v < NVG; ++v) st.zacc[v] = 0.f;
+    for (int hb = 0; hb < HB; ++hb) {
+      st.m[hb] = -__builtin_inff();
+      st.l[hb] = 0.f;
+#pragma unroll
+      for (int v = 0; v < NVG; ++v) st.z[hb][v] = 0.f;
+    }
 
     if (win_split) {
       // Window pages: raw (and unrotated) keys, scored with the raw, unscaled query operand.
@@ -857,7 +908,12 @@ struct Kern {
       } else {
         load_q_regs(qr, args, cx, b, hq0);
       }
-      stream_pairs(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+      if (lay.kg == 32)
+        stream_pairs<0>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+      else if (lay.kg == 64)
+        stream_pairs<1>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+      else
+        stream_pairs<2>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
     }
     write_partial<PART_CODES>(args, cx, st, nullptr, lds, b, kvh, split);
   }
@@ -869,7 +925,9 @@ struct Kern {
   // behind pair i.  Requests follow a cursor that steps through the pairs in order (the parity of
   // every request site is fixed, so the cursor moves by constant strides), and the slot addresses
   // rotate through the ring, so the loop does no index arithmetic beyond those steps.
-  static __device__ __forceinline__ void stream_pairs(const KvqAttnArgs &args, Ctx &cx, State<NVG> &st, uint8_t *smem,
+  // KS = log2(key group / 32).
+  template <int KS>
+  static __device__ __forceinline__ void stream_pairs(const KvqAttnArgs &args, Ctx &cx, St &st, uint8_t *smem,
                                                       const QRegs &qr, int b, int kvh, int sq, int SQ, int npairs,
                                                       bool tail, int tail_va, int tail_vb) {
     const KvqLayout &lay = args.lay;
@@ -917,6 +975,16 @@ struct Kern {
     for (int k = 0; k < AHEAD; ++k)
       if (k < npages) issue((k & 1) != 0, k);
     if (!args.rotation) build_q_regs(cx, qr, args.q_f32);
+    // Zero-point query sums per key group.
+    float Qg[HB][4];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) Qg[hb][g] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Qg[hb][r >> KS] += cx.Qc[hb][r];
+    }
+    const RecOff ro = rec_offsets<KS>(cx, lay);
     constexpr bool FIRST_ODD = (AHEAD & 1) != 0;  // parity of page 2i + AHEAD
     for (int i = 0; i < npairs; ++i) {
       const int k0 = 2 * i + AHEAD;
@@ -928,39 +996,42 @@ struct Kern {
         if (k0 < npages) issue(FIRST_ODD, k0);
         wait_vmcnt<0>();
       }
-      PageData A, B;
-      read_page_at(A, cx, rslot, lay);
+      PageData<KS> A, B;
+      read_page_at(A, rslot, ro);
       rslot = next_slot(rslot);
-      read_page_at(B, cx, rslot, lay);
+      read_page_at(B, rslot, ro);
       rslot = next_slot(rslot);
-      process_pair<false>(cx, st, A, B, 16, 16);
+      process_pair<KS, false>(cx, st, Qg, A, B, 16, 16);
     }
     if (tail) {  // its pages were requested with the others
       wait_vmcnt<0>();
-      PageData A, B;
-      read_page_at(A, cx, rslot, lay);
+      PageData<KS> A, B;
+      read_page_at(A, rslot, ro);
       rslot = next_slot(rslot);
-      read_page_at(B, cx, rslot, lay);
-      process_pair<true>(cx, st, A, B, tail_va, tail_vb);
+      read_page_at(B, rslot, ro);
+      process_pair<KS, true>(cx, st, Qg, A, B, tail_va, tail_vb);
     }
   }
 
-  // Reduce the state across rows/replicas and write this split's partial result:
+  // Reduce the state across lanes and write this split's partial result:
   // [m (log2 units), l, 0, 0, o[128]] per query head, o unnormalised.
   // MODE: PART_CODES (quantized pages: value-code scales and zero-point sums apply),
   // PART_WIN_ACC (bf16 window: MFMA accumulators hold the output as is), PART_WIN_VALU (fp32
   // window: the output is in ow).
   static constexpr int PART_CODES = 0, PART_WIN_ACC = 1, PART_WIN_VALU = 2;
   template <int MODE>
-  static __device__ __forceinline__ void write_partial(const KvqAttnArgs &args, const Ctx &cx, const State<NVG> &st,
+  static __device__ __forceinline__ void write_partial(const KvqAttnArgs &args, const Ctx &cx, const St &st,
                                                        float (*ow)[2], float *lds, int b, int kvh, int split) {
     constexpr bool WIN = MODE != PART_CODES;
     const int lane = threadIdx.x;
     const int hq0 = kvh * G;
-    const float l = rows_sum(st.l);
-    float z[NVG];
+    float lt[HB], zt[HB][NVG];
 #pragma unroll
-    for (int v = 0; v < NVG; ++v) z[v] = WIN ? 0.f : rows_sum(st.zacc[v]);
+    for (int hb = 0; hb < HB; ++hb) {
+      lt[hb] = row16_sum(st.l[hb]);
+#pragma unroll
+      for (int v = 0; v < NVG; ++v) zt[hb][v] = WIN ? 0.f : row16_sum(st.z[hb][v]);
+    }
     __syncthreads();
     float *accs = lds;                 // [2G][128]
     float *hdr = lds + 2 * G * KVQ_D;  // [G][4]: m, l, z0, z1
@@ -974,11 +1045,15 @@ struct Kern {
         }
       }
     }
-    if (lane < G) {
-      hdr[lane * 4 + 0] = st.m * cx.sig;  // log2 units
-      hdr[lane * 4 + 1] = l;
+    if (cx.col == 0 && cx.quad < HSN) {
 #pragma unroll
-      for (int v = 0; v < NVG; ++v) hdr[lane * 4 + 2 + v] = z[v];
+      for (int hb = 0; hb < HB; ++hb) {
+        const int h = 4 * hb + cx.quad;
+        hdr[h * 4 + 0] = st.m[hb] * cx.sig;  // log2 units
+        hdr[h * 4 + 1] = lt[hb];
+#pragma unroll
+        for (int v = 0; v < NVG; ++v) hdr[h * 4 + 2 + v] = zt[hb][v];
+      }
     }
     __syncthreads();
     const int vshift = (NVG == 1) ? 7 : 6;  // channel -> value group

@@ -64,33 +64,42 @@ struct KvqDebugArgs {
 #define KVQ_WIN_PAGES 8  // window pages (128 tokens) per window split
 
 // Waves per SIMD each split-kernel instantiation is compiled for (register budget
-// 512 / waves), the same for all: 2.  With 8 waves per CU each wave gets an LDS ring of up
-// to 8 pages (6 in flight while a pair is processed, the same bytes in flight per CU as 16
-// waves with 3 each), and the 32k batch-16 K4V2 launch measured 91 µs against 94 µs at 4
-// waves per SIMD (3 waves per SIMD measured 114 µs, 1 wave 143 µs).  No instantiation
-// spills at this budget (the build checks this).
+// 512 / waves): 2 for all but the widest ones.  With 8 waves per CU each wave gets an LDS ring
+// of up to 8 pages (6 in flight while a pair is processed, the same bytes in flight per CU as
+// 16 waves with 3 each), and the 32k batch-16 K4V2 launch measured 91 µs against 94 µs at 4
+// waves per SIMD (3 waves per SIMD measured 114 µs, 1 wave 143 µs).  Sixteen query rows
+// (8 heads per kv head, query split into hi and lo parts) with records wider than K4V2's
+// (more bits, or two value groups) do not fit 256 registers and run at 1 wave per SIMD.
+// No instantiation spills at its budget (the build checks this).
 __host__ __device__ constexpr int kvq_attn_wpe(int kb, int vb, int g, int p, int nvg) {
-  return (void)kb, (void)vb, (void)g, (void)p, (void)nvg, 2;
+  return (g * p == 16 && (kb + vb > 6 || nvg == 2)) ? 1 : 2;
 }
 
 #define KVQ_LDS_PER_CU (160 * 1024)
 
 // Page records of the split kernel's LDS prefetch ring: as many as fit in the LDS
-// share of one wave at the compiled occupancy, at least 3 (the pair in use plus one
-// page ahead) and at most 8.  Slots are sized for the largest record of the bit widths
-// (key groups of 32): rec16 16-byte units.
+// share of one wave at the compiled occupancy after its weight-exchange buffers
+// (KVQ_XCHG_BYTES per value group), at least 3 (the pair in use plus one page ahead)
+// and at most 8.  Slots are sized for the largest record of the bit widths (key
+// groups of 32): rec16 16-byte units.
+#define KVQ_XCHG_BYTES 1024  // 16 rows x 32 bf16 weights: the A operand of one value contraction
 __host__ __device__ constexpr int kvq_rec16(int kb, int vb, int nvg) { return 16 * kb + 16 + 16 * vb + 4 * nvg; }
-__host__ __device__ constexpr int kvq_ring_pages(int rec_bytes, int wpe) {
-  return (KVQ_LDS_PER_CU / (4 * wpe)) / rec_bytes < 3
+__host__ __device__ constexpr int kvq_ring_pages(int rec_bytes, int wpe, int nvg) {
+  return (KVQ_LDS_PER_CU / (4 * wpe) - KVQ_XCHG_BYTES * nvg) / rec_bytes < 3
              ? 3
-             : ((KVQ_LDS_PER_CU / (4 * wpe)) / rec_bytes > 8 ? 8 : (KVQ_LDS_PER_CU / (4 * wpe)) / rec_bytes);
+             : ((KVQ_LDS_PER_CU / (4 * wpe) - KVQ_XCHG_BYTES * nvg) / rec_bytes > 8
+                    ? 8
+                    : (KVQ_LDS_PER_CU / (4 * wpe) - KVQ_XCHG_BYTES * nvg) / rec_bytes);
 }
 #define KVQ_STAGE_BYTES ((2 * 8 * 128 + 8 * 4) * 4)  // query / accumulator staging area
 
-// LDS bytes of one split-kernel workgroup (one wave).
+// LDS bytes of one split-kernel workgroup (one wave): the ring, then the exchange buffers.
+__host__ __device__ constexpr int kvq_attn_ring_bytes(int kb, int vb, int nvg, int wpe) {
+  return 16 * kvq_rec16(kb, vb, nvg) * kvq_ring_pages(16 * kvq_rec16(kb, vb, nvg), wpe, nvg);
+}
 __host__ __device__ constexpr int kvq_attn_lds_bytes(int kb, int vb, int nvg, int wpe) {
-  return 16 * kvq_rec16(kb, vb, nvg) * kvq_ring_pages(16 * kvq_rec16(kb, vb, nvg), wpe) > KVQ_STAGE_BYTES
-             ? 16 * kvq_rec16(kb, vb, nvg) * kvq_ring_pages(16 * kvq_rec16(kb, vb, nvg), wpe)
+  return kvq_attn_ring_bytes(kb, vb, nvg, wpe) + KVQ_XCHG_BYTES * nvg > KVQ_STAGE_BYTES
+             ? kvq_attn_ring_bytes(kb, vb, nvg, wpe) + KVQ_XCHG_BYTES * nvg
              : KVQ_STAGE_BYTES;
 }
 

@@ -14,14 +14,15 @@
 //   channels 32*kc + 8*j + e.  Channel e = 2*i + h of chunk kc has index
 //   u = 4*kc + i; it sits in word u / (16/kb) at bit 16*h + kb*(u % (16/kb)).
 //   So (word >> kb*s) & mask(kb, both halves) is one bf16 pair of codes.
-// K meta: entry (token 4*jj + r, group g) at dword ((jj*nkg + g)*4 + r):
+// K meta: entry (token n, group g) at dword n*nkg + g (a token's groups are
+//   contiguous, so one lane reads all of them with one load):
 //   low half = fp16 scale, high half = fp16 zero.
 // V codes: lane-slot l = 16*jj + c16 (channels c16 + 16*m, m = 0..7; tokens
 //   4*jj + r, r = 0..3).  The slot has vb words.  Token r = 2*i + h, tile m:
 //   position p = i*8*vb + m*vb in the half-word stream h, i.e. word p / 16,
 //   bit 16*h + p % 16.  A token's bits in one slot never share a byte with
 //   another token's, so tokens of a page can be written concurrently.
-// V meta: entry (token 4*jj + r, group g) at dword ((jj*nvg + g)*4 + r).
+// V meta: entry (token n, group g) at dword n*nvg + g.
 //
 // A code c read as a bf16 bit pattern is the value c * 2^-133 for every c in
 // 0..255 (subnormal below 128, continuing into the first normal binade), so
@@ -75,9 +76,7 @@ __host__ __device__ inline void kvq_v_code_pos(int vb, int tt, int ch, int *byte
   *bit = 16 * h + (p & 15);
 }
 
-__host__ __device__ inline int kvq_meta_dword(int ngroups, int tt, int grp) {
-  return ((tt >> 2) * ngroups + grp) * 4 + (tt & 3);
-}
+__host__ __device__ inline int kvq_meta_dword(int ngroups, int tt, int grp) { return tt * ngroups + grp; }
 
 // Record index of (sequence b, kv head h, logical page p).  Contiguous mode is page-major:
 // page p of every (sequence, kv head) unit, then page p + 1, ..., so each unit's pages are
