@@ -167,8 +167,9 @@ kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache
  * empty splits have m_s = -inf.  With M = max_s m_s the attention output is
  * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s ([P1] "Error pada key masuk sebelum softmax").
  * Rows are [batch][num_q_heads][S]; S depends on (params, batch, max_seq_len, q_dtype) and on
- * the environment variables KVQ_PAGES_PER_SPLIT / KVQ_TARGET_WAVES, which must not change
- * between the two calls.  kvq_decode_combine computes that merge into `out`
+ * the environment variables KVQ_PAGES_PER_SPLIT / KVQ_TARGET_WAVES / KVQ_WINDOW_FOLD (1: the
+ * bf16 recent window is processed by the quantized splits instead of splits of its own), which
+ * must not change between the two calls.  kvq_decode_combine computes that merge into `out`
  * ([batch][num_q_heads][128] of out_dtype) from a workspace filled by kvq_decode_partials
  * with the same params, batch, max_seq_len and q_dtype.  Errors as for kvq_decode_attention. */
 #define KVQ_PART_FLOATS 132

@@ -55,24 +55,27 @@ KvqCacheDev dev_cache(const kvq_params *p, const kvq_cache *c) {
 
 KvqLayout layout_of(const kvq_params *p) { return kvq_make_layout(p->k_bits, p->k_group, p->v_bits, p->v_group); }
 
-// Split plan.  Splits [0, wsplits) cover the recent window (KVQ_WIN_PAGES
-// pages each) and come first in dispatch order, so that their short,
-// latency-bound work overlaps the streaming of the quantized pages; the
-// remaining splits cover the quantized pages, pps pages each, sized so that
-// all waves of the launch are resident at once.
+// Split plan.  Quantized splits cover the quantized pages, pps pages each, sized so that all
+// waves of the launch are resident at once.  A bf16 recent window (no key rotation) is folded
+// into them: 16-token block i of the ring goes to the i-th split from the end, processed while
+// that split's first pages stream in, so no wave is left with only the window's short,
+// latency-bound work.  Otherwise (fp32 window, rotated keys, or more window blocks than splits)
+// splits [0, wsplits) cover the window, KVQ_WIN_PAGES pages each, and come first in dispatch
+// order so that their work overlaps the streaming of the quantized pages.
 struct SplitPlan {
-  int splits, wsplits, pps;
+  int splits, wsplits, pps, wfold;
   int bound;  // most splits any length <= max_seq_len can get (workspace size)
 };
 
-SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, int q_parts) {
+SplitPlan split_plan_mode(const kvq_params *p, int32_t batch, int64_t max_seq_len, int q_parts, bool fold) {
   const int R = p->window;
   const int64_t nq = max_seq_len > R ? max_seq_len - R : 0;
   const int64_t nw = max_seq_len < R ? max_seq_len : R;
   const int64_t qpages = (nq + KVQ_PAGE - 1) / KVQ_PAGE;
-  const int64_t wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;
+  const int64_t wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;  // also the folded window blocks
   SplitPlan sp;
-  sp.wsplits = (int)((wpages + KVQ_WIN_PAGES - 1) / KVQ_WIN_PAGES);
+  sp.wfold = fold ? 1 : 0;
+  sp.wsplits = fold ? 0 : (int)((wpages + KVQ_WIN_PAGES - 1) / KVQ_WIN_PAGES);
   const int64_t units = (int64_t)batch * p->num_kv_heads;
   int64_t per = 0, cap = 0;
   if (const char *env = getenv("KVQ_PAGES_PER_SPLIT")) per = atoll(env);
@@ -88,22 +91,42 @@ SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, in
   }
   if (per < 2) per = 2;
   per = (per + 1) & ~int64_t(1);
-  const int64_t qsplits = (qpages + per - 1) / per;
+  int64_t qsplits = (qpages + per - 1) / per;
+  if (fold && qsplits < wpages) qsplits = wpages;  // every window block needs a split
   sp.pps = (int)per;
   sp.splits = (int)(sp.wsplits + qsplits);
   if (sp.splits < 1) sp.splits = 1;
   // Bound over all lengths up to max_seq_len.  wsplits(L) + ceil(qpages(L) / per) is
   // non-decreasing in L for a fixed per; otherwise qsplits <= min(ceil(qpages / 2), cap) and
   // both wsplits + ceil(qpages / 2) and wsplits + cap = max(ceil(target / units), wsplits + 1)
-  // are non-decreasing in L, so their minimum at max_seq_len bounds every shorter length.
+  // are non-decreasing in L, so their minimum at max_seq_len bounds every shorter length.  A
+  // folded plan has at least wpages(L) splits, also non-decreasing in L.
   int64_t bound = sp.wsplits + qsplits;
   if (!fixed) {
     const int64_t a = sp.wsplits + (qpages + 1) / 2, b = sp.wsplits + cap;
     bound = a < b ? a : b;
+    if (fold && bound < wpages) bound = wpages;
   }
   if (bound < sp.splits) bound = sp.splits;
   sp.bound = (int)bound;
   return sp;
+}
+
+bool fold_allowed(const kvq_params *p) {
+  if (p->window <= 0 || p->kv_dtype != KVQ_BF16 || p->key_rotation != KVQ_ROT_NONE) return false;
+  const char *env = getenv("KVQ_WINDOW_FOLD");  // opt-in: measured slower at the 32k config
+  return env && env[0] == '1';
+}
+
+SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, int q_parts) {
+  if (fold_allowed(p)) {
+    // Fold when every window block finds a split of its own.
+    const SplitPlan f = split_plan_mode(p, batch, max_seq_len, q_parts, true);
+    const SplitPlan u = split_plan_mode(p, batch, max_seq_len, q_parts, false);
+    if (f.splits <= u.splits) return f;
+    return u;
+  }
+  return split_plan_mode(p, batch, max_seq_len, q_parts, false);
 }
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
@@ -151,8 +174,15 @@ kvq_status kvq_quantize_append(const kvq_params *params, const kvq_cache *cache,
 size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len) {
   if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0) return 0;
   // The query dtype is not known here: cover both query-part counts.
-  const SplitPlan s1 = split_plan(params, batch, max_seq_len, 1), s2 = split_plan(params, batch, max_seq_len, 2);
-  const int bound = s1.bound > s2.bound ? s1.bound : s2.bound;
+  // Cover both query-part counts and both window plans (the choice between them can change
+  // with the length).
+  int bound = 0;
+  for (int parts = 1; parts <= 2; ++parts) {
+    for (int fold = 0; fold <= 1; ++fold) {
+      const SplitPlan sp = split_plan_mode(params, batch, max_seq_len, parts, fold != 0);
+      bound = sp.bound > bound ? sp.bound : bound;
+    }
+  }
   return (size_t)batch * params->num_q_heads * (size_t)bound * KVQ_PART_STRIDE * sizeof(float);
 }
 
@@ -189,6 +219,7 @@ kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache,
   const SplitPlan sp = split_plan(params, cache->batch, max_seq_len, q_parts);
   a.splits = sp.splits;
   a.wsplits = sp.wsplits;
+  a.wfold = sp.wfold;
   a.max_len = (int32_t)(max_seq_len < INT32_MAX ? max_seq_len : INT32_MAX);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
   a.sigma_u = (float)((double)scale * 1.4426950408889634 * 8589934592.0);  // * log2(e) * 2^33

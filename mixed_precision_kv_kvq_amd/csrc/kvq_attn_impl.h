@@ -316,7 +316,7 @@ struct Kern {
       }
     }
   }
-  static __device__ __forceinline__ void build_q_regs(Ctx &cx, const QRegs &qr, bool q_f32) {
+  static __device__ __forceinline__ void build_q_regs(Ctx &cx, const QRegs &qr, bool q_f32, bool code_scaled = true) {
     build_q_with(
         cx,
         [&](int hb, int e) {
@@ -327,7 +327,7 @@ struct Kern {
           const uint32_t w = qr.v[hb][0][e >> 1];
           return kvq_bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFF));
         },
-        true);
+        code_scaled);
   }
 
   static __device__ __forceinline__ void init_ctx(Ctx &cx, float sig, uint32_t xbase) {
@@ -515,9 +515,10 @@ struct Kern {
 
   // ---- LDS ring -------------------------------------------------------------
   static constexpr int MAX_REC16 = kvq_rec16(KB, VB, NVG);  // record in 16-byte units (k_group 32)
-  static constexpr int REC_BYTES = 16 * MAX_REC16;              // ring slot stride
   static constexpr int DMAS_PER_PAGE = (MAX_REC16 + 63) / 64;
   static constexpr int WPE = kvq_attn_wpe(KB, VB, G, P, NVG);       // waves per SIMD
+  static constexpr bool PAD = kvq_slot_pad(KB, VB, NVG, WPE);       // slots of whole DMAs: all lanes land
+  static constexpr int REC_BYTES = kvq_slot_bytes(KB, VB, NVG, WPE);  // ring slot stride
   static constexpr int NPS = kvq_ring_pages(REC_BYTES, WPE, NVG);  // page slots
   static constexpr int AHEAD = NPS - 2;                             // pages in flight while a pair is processed
   static constexpr int XCHG_OFF = NPS * REC_BYTES;                  // exchange buffers after the ring
@@ -529,13 +530,15 @@ struct Kern {
   // slot chunk 64k + l, through a buffer resource spanning just the record (scalar base and size),
   // with 32-bit lane offsets (16-byte chunks, clamped into the record) and the slot given as an
   // LDS byte address (base: the low 32 bits of the slot's shared-aperture address); lanes past
-  // the slot stay idle.  The resource's range check also keeps every lane inside the record.
+  // the slot stay idle (none when slots are padded to whole DMAs: lanes past the record re-read
+  // its last chunk into the padding).  The resource's range check also keeps every lane inside
+  // the record.
   static __device__ __forceinline__ void dma_page_buf(uint32_t slot_lds, const uint8_t *rec, int rec_bytes,
                                                       const uint32_t (&loff)[DMAS_PER_PAGE], int lane) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, 0, rec_bytes, 0x00020000);
 #pragma unroll
     for (int k = 0; k < DMAS_PER_PAGE; ++k) {
-      if (k + 1 < DMAS_PER_PAGE || lane < MAX_REC16 - 64 * k)
+      if (PAD || k + 1 < DMAS_PER_PAGE || lane < MAX_REC16 - 64 * k)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(size_t)(slot_lds + 1024u * k), 16, loff[k], 0, 0, 0);
     }
   }
@@ -780,6 +783,79 @@ struct Kern {
     }
   }
 
+  // A folded block of up to 16 bf16 window tokens (ring slots [w0, w0 + n)), processed by a
+  // quantized split before its pairs: one 16-token column set of the score contraction (raw
+  // keys, unscaled query), weights through the exchange buffer (page-A slots; page-B slots get
+  // zero weights), exact bf16 values as the B operand of the value contraction.  The value
+  // accumulators hold only this block's output afterwards; they are brought to the scale of the
+  // quantized code contractions (tile m: 2^(s_m - 133), see write_partial) with exact
+  // power-of-two multiplies, so the pages that follow accumulate on top.
+  struct WinBlock {
+    int w0, n;
+    const uint8_t *kwin, *vwin;
+  };
+  struct WinRegs {
+    u32x4 kr[4];        // B operand of the score contraction, per 32-channel chunk
+    uint32_t vb[8][2];  // value tile m, k slots 0..3 (tokens 4 quad + 0..3) packed in pairs
+  };
+  static __device__ __forceinline__ void load_win_block(WinRegs &wr, const Ctx &cx, const WinBlock &wb) {
+    const int slot = wb.w0 + (cx.col < wb.n ? cx.col : 0);  // columns past the block re-read its first row
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+      wr.kr[kc] = gload<u32x4>(wb.kwin + ((size_t)slot * KVQ_D + 32 * kc + 8 * cx.quad) * 2);
+    const uint16_t *vrow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * cx.quad + j;
+      vrow[j] = reinterpret_cast<const uint16_t *>(wb.vwin) + (size_t)(wb.w0 + (t < wb.n ? t : 0)) * KVQ_D + cx.col;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t lo = gload<uint16_t>(vrow[2 * i] + 16 * m);
+        const uint32_t hi = gload<uint16_t>(vrow[2 * i + 1] + 16 * m);
+        wr.vb[m][i] = lo | (hi << 16);
+      }
+    }
+  }
+  // Needs the unscaled query operand in cx.qA; leaves the code-scale accumulators in st.
+  static __device__ __forceinline__ void win_block(const Ctx &cx, St &st, const WinRegs &wr, const WinBlock &wb) {
+    f32x4 D[NACC];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) D[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int part = 0; part < P; ++part) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+          D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], __builtin_bit_cast(bf16x8, wr.kr[kc]),
+                                                          D[hb], 0, 0, 0);
+      }
+    }
+    float sA[HB], sB[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const float acc = (D[hb][0] + D[hb][1]) + (D[hb][2] + D[hb][3]);
+      sA[hb] = cx.col < wb.n ? acc * EXP2_M66 * EXP2_M67 : -__builtin_inff();
+      sB[hb] = -__builtin_inff();
+    }
+    softmax_update<true, false>(cx, st, sA, sB, nullptr);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) xchg_put(cx, 0, hb, sA[hb], 0.f);
+    u32x4 xa = xchg_get(cx, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xa)::"memory");
+    const bf16x8 Aop = __builtin_bit_cast(bf16x8, xa);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, pack8(wr.vb[m][0], wr.vb[m][1], 0u, 0u), st.acc[m], 0, 0, 0);
+      const float f = __builtin_amdgcn_ldexpf(1.0f, vtile_scale(m) - 66);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.acc[m][r] = st.acc[m][r] * f * EXP2_M67;
+    }
+  }
+
   // Queries of the G heads of kv head kvh -> LDS (fp32 [G][128]); rotated when `rotate`.
   static __device__ __forceinline__ void stage_q(const KvqAttnArgs &args, float *qs, int b, int hq0, bool rotate) {
     const int lane = threadIdx.x;
@@ -813,7 +889,11 @@ struct Kern {
     const int64_t wave = blockIdx.x;
     const int S = args.splits;
     const int64_t unit = wave / S;
-    const int split = (int)(wave % S);
+    // Consecutive blocks go to the 8 XCDs in turn (block mod 8), so with S a multiple of 8 the
+    // split at position k of every unit would land on the same XCD: rotating the split index by
+    // the unit spreads each split (the window splits in particular, which carry less work) evenly
+    // over the XCDs.
+    const int split = (int)((wave % S + unit) % S);
     const int Hkv = args.Hkv;
     const int kvh = (int)(unit % Hkv), b = (int)(unit / Hkv);
     if (b >= args.cache.batch) return;
@@ -825,7 +905,8 @@ struct Kern {
     const int nw = L < R ? L : R;
     const int qpages = (nq + KVQ_PAGE - 1) / KVQ_PAGE;
     const int wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;
-    // Window splits first, then quantized splits (see the host split plan).
+    // Window splits first, then quantized splits (see the host split plan).  With the window
+    // folded into the quantized splits there are no window splits.
     const bool win_split = split < args.wsplits;
     int wv0 = 0, wv1 = 0;
     if (win_split) {
@@ -890,7 +971,21 @@ struct Kern {
     // full pairs, so it streams through the same ring.
     const int npairs = tp > sq ? (tp - sq + SQ - 1) / SQ : 0;
     const bool tail = sq == tp % SQ && 2 * tp < qpages;
-    if (npairs > 0 || tail) {
+    // Folded window (bf16 rings): 16-token block i of the ring goes to split SQ - 1 - i, the
+    // splits that end the pair rotation and so have at most as many pairs as the others.
+    WinBlock wb;
+    wb.w0 = -1;
+    if (args.wfold) {
+      const int i = SQ - 1 - sq;
+      if (i * KVQ_PAGE < nw) {
+        wb.w0 = i * KVQ_PAGE;
+        wb.n = (nw - wb.w0) < KVQ_PAGE ? (nw - wb.w0) : KVQ_PAGE;
+        const size_t win_off = ((size_t)b * Hkv + kvh) * R * KVQ_D * 2;
+        wb.kwin = args.cache.k_win + win_off;
+        wb.vwin = args.cache.v_win + win_off;
+      }
+    }
+    if (npairs > 0 || tail || wb.w0 >= 0) {
       int tail_va = 0, tail_vb = 0;
       if (tail) {
         const int p = 2 * tp;
@@ -909,11 +1004,11 @@ struct Kern {
         load_q_regs(qr, args, cx, b, hq0);
       }
       if (lay.kg == 32)
-        stream_pairs<0>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+        stream_pairs<0>(args, cx, st, smem, qr, wb, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
       else if (lay.kg == 64)
-        stream_pairs<1>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+        stream_pairs<1>(args, cx, st, smem, qr, wb, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
       else
-        stream_pairs<2>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+        stream_pairs<2>(args, cx, st, smem, qr, wb, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
     }
     write_partial<PART_CODES>(args, cx, st, nullptr, lds, b, kvh, split);
   }
@@ -928,8 +1023,8 @@ struct Kern {
   // KS = log2(key group / 32).
   template <int KS>
   static __device__ __forceinline__ void stream_pairs(const KvqAttnArgs &args, Ctx &cx, St &st, uint8_t *smem,
-                                                      const QRegs &qr, int b, int kvh, int sq, int SQ, int npairs,
-                                                      bool tail, int tail_va, int tail_vb) {
+                                                      const QRegs &qr, const WinBlock &wb, int b, int kvh, int sq,
+                                                      int SQ, int npairs, bool tail, int tail_va, int tail_vb) {
     const KvqLayout &lay = args.lay;
     const int lane = cx.lane, Hkv = args.Hkv;
     const int rec = lay.record, rec16 = rec / 16;
@@ -959,7 +1054,9 @@ struct Kern {
     auto issue = [&](bool odd, int k) {
       const bool dup = odd && dup_last && k == npages - 1;
       const uint8_t *src;
-      if (paged) {
+      if (k >= npages) {  // prologue filler: the unit's first page (always allocated), never read
+        src = pages + (paged ? (size_t)kvh : ((size_t)b * Hkv + kvh)) * rec;
+      } else if (paged) {
         int e = tcur[(odd && !dup) ? 1 : 0];
         e = e < 0 ? 0 : (e > pool_last ? pool_last : e);
         src = pages + ((size_t)e * Hkv + kvh) * rec;
@@ -971,9 +1068,19 @@ struct Kern {
       dma_page_buf(wslot, src, rec, loff, lane);
       wslot = next_slot(wslot);
     };
+    // A folded window block's loads are issued before the prologue DMAs, so that they retire
+    // first (vmcnt counts in issue order) and the block is processed while the ring fills.
+    WinRegs wr;
+    const bool has_win = wb.w0 >= 0;
+    if (has_win) load_win_block(wr, cx, wb);
+    // The prologue always issues AHEAD pages (fillers past the split's own pages), so the number
+    // of DMAs behind the window loads is fixed.
 #pragma unroll
-    for (int k = 0; k < AHEAD; ++k)
-      if (k < npages) issue((k & 1) != 0, k);
+    for (int k = 0; k < AHEAD; ++k) issue((k & 1) != 0, k);
+    if (has_win) {
+      build_q_regs(cx, qr, args.q_f32, false);
+      win_block(cx, st, wr, wb);
+    }
     if (!args.rotation) build_q_regs(cx, qr, args.q_f32);
     // Zero-point query sums per key group.
     float Qg[HB][4];
@@ -1011,6 +1118,7 @@ struct Kern {
       read_page_at(B, rslot, ro);
       process_pair<KS, true>(cx, st, Qg, A, B, tail_va, tail_vb);
     }
+    wait_vmcnt<0>();  // no DMA (fillers included) may still be writing the ring when the wave ends
   }
 
   // Reduce the state across lanes and write this split's partial result:

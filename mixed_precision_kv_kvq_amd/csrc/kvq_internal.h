@@ -39,6 +39,7 @@ struct KvqAttnArgs {
   int32_t q_f32, kv_f32, Hq, Hkv, R, rotation;
   int32_t splits;                    // all splits
   int32_t wsplits;                   // leading splits that cover the recent window, KVQ_WIN_PAGES pages each
+  int32_t wfold;                     // 1: no window splits; 16-token window blocks go to the quantized splits
   int32_t max_len;  // host-validated upper bound of seq_lens (device lengths are clamped to it)
   float sigma_u;  // softmax_scale * log2(e) * 2^33
 };
@@ -68,11 +69,12 @@ struct KvqDebugArgs {
 // of up to 8 pages (6 in flight while a pair is processed, the same bytes in flight per CU as
 // 16 waves with 3 each), and the 32k batch-16 K4V2 launch measured 91 µs against 94 µs at 4
 // waves per SIMD (3 waves per SIMD measured 114 µs, 1 wave 143 µs).  Sixteen query rows
-// (8 heads per kv head, query split into hi and lo parts) with records wider than K4V2's
-// (more bits, or two value groups) do not fit 256 registers and run at 1 wave per SIMD.
-// No instantiation spills at its budget (the build checks this).
+// (8 heads per kv head, query split into hi and lo parts) fit 256 registers only for 4-bit
+// keys, 2-bit values and one value group (the rotated-key configuration); the other
+// sixteen-row instantiations run at 1 wave per SIMD.  No instantiation spills at its budget
+// (the build checks this).
 __host__ __device__ constexpr int kvq_attn_wpe(int kb, int vb, int g, int p, int nvg) {
-  return (g * p == 16 && (kb + vb > 6 || nvg == 2)) ? 1 : 2;
+  return (g * p == 16 && !(kb == 4 && vb == 2 && nvg == 1)) ? 1 : 2;
 }
 
 #define KVQ_LDS_PER_CU (160 * 1024)
@@ -80,22 +82,38 @@ __host__ __device__ constexpr int kvq_attn_wpe(int kb, int vb, int g, int p, int
 // Page records of the split kernel's LDS prefetch ring: as many as fit in the LDS
 // share of one wave at the compiled occupancy after its weight-exchange buffers
 // (KVQ_XCHG_BYTES per value group), at least 3 (the pair in use plus one page ahead)
-// and at most 8.  Slots are sized for the largest record of the bit widths (key
-// groups of 32): rec16 16-byte units.
+// and at most KVQ_RING_MAX.  Slots are sized for the largest record of the bit widths (key
+// groups of 32): rec16 16-byte units, rounded up to whole 1 KiB DMAs (64 lanes x 16 B)
+// when KVQ_RING_MAX such slots still fit, so that every lane of every DMA lands inside its slot.
 #define KVQ_XCHG_BYTES 1024  // 16 rows x 32 bf16 weights: the A operand of one value contraction
+#ifndef KVQ_RING_MAX
+#define KVQ_RING_MAX 8  // most ring slots per wave
+#endif
+#ifndef KVQ_SLOT_PAD
+#define KVQ_SLOT_PAD 1  // pad slots to whole DMAs when KVQ_RING_MAX of them still fit
+#endif
 __host__ __device__ constexpr int kvq_rec16(int kb, int vb, int nvg) { return 16 * kb + 16 + 16 * vb + 4 * nvg; }
-__host__ __device__ constexpr int kvq_ring_pages(int rec_bytes, int wpe, int nvg) {
-  return (KVQ_LDS_PER_CU / (4 * wpe) - KVQ_XCHG_BYTES * nvg) / rec_bytes < 3
+__host__ __device__ constexpr int kvq_lds_share(int wpe, int nvg) {
+  return KVQ_LDS_PER_CU / (4 * wpe) - KVQ_XCHG_BYTES * nvg;
+}
+__host__ __device__ constexpr int kvq_slot_padded(int kb, int vb, int nvg) { return 1024 * ((kvq_rec16(kb, vb, nvg) + 63) / 64); }
+__host__ __device__ constexpr bool kvq_slot_pad(int kb, int vb, int nvg, int wpe) {
+  return KVQ_SLOT_PAD && kvq_lds_share(wpe, nvg) / kvq_slot_padded(kb, vb, nvg) >= KVQ_RING_MAX;
+}
+__host__ __device__ constexpr int kvq_slot_bytes(int kb, int vb, int nvg, int wpe) {
+  return kvq_slot_pad(kb, vb, nvg, wpe) ? kvq_slot_padded(kb, vb, nvg) : 16 * kvq_rec16(kb, vb, nvg);
+}
+__host__ __device__ constexpr int kvq_ring_pages(int slot_bytes, int wpe, int nvg) {
+  return kvq_lds_share(wpe, nvg) / slot_bytes < 3
              ? 3
-             : ((KVQ_LDS_PER_CU / (4 * wpe) - KVQ_XCHG_BYTES * nvg) / rec_bytes > 8
-                    ? 8
-                    : (KVQ_LDS_PER_CU / (4 * wpe) - KVQ_XCHG_BYTES * nvg) / rec_bytes);
+             : (kvq_lds_share(wpe, nvg) / slot_bytes > KVQ_RING_MAX ? KVQ_RING_MAX
+                                                                   : kvq_lds_share(wpe, nvg) / slot_bytes);
 }
 #define KVQ_STAGE_BYTES ((2 * 8 * 128 + 8 * 4) * 4)  // query / accumulator staging area
 
 // LDS bytes of one split-kernel workgroup (one wave): the ring, then the exchange buffers.
 __host__ __device__ constexpr int kvq_attn_ring_bytes(int kb, int vb, int nvg, int wpe) {
-  return 16 * kvq_rec16(kb, vb, nvg) * kvq_ring_pages(16 * kvq_rec16(kb, vb, nvg), wpe, nvg);
+  return kvq_slot_bytes(kb, vb, nvg, wpe) * kvq_ring_pages(kvq_slot_bytes(kb, vb, nvg, wpe), wpe, nvg);
 }
 __host__ __device__ constexpr int kvq_attn_lds_bytes(int kb, int vb, int nvg, int wpe) {
   return kvq_attn_ring_bytes(kb, vb, nvg, wpe) + KVQ_XCHG_BYTES * nvg > KVQ_STAGE_BYTES

@@ -156,6 +156,30 @@ def test_edge_case(name):
     full_check(run, 0)
 
 
+# The recent window folded into the quantized splits (opt-in split plan, KVQ_WINDOW_FOLD=1): the
+# same comparisons on configurations with a bf16 window.
+FOLD = {
+    "config3-structure": dict(batch=2, context=1000, window=128, steps=3),
+    "window-ragged": dict(context=300, window=40),
+    "window-longer-than-seq": dict(context=50, window=128),
+    "window-plus-one": dict(context=129, window=128),
+    "paged-window": dict(context=0, var_len=(1, 300), block_size=16, window=16, batch=4),
+    "g8-window": dict(context=150, num_q_heads=16, num_kv_heads=2, window=32),
+    "f32-q-window": dict(context=160, window=48, q_dtype="f32"),
+    "kgroup64-vgroup64-window": dict(context=150, k_group=64, v_group=64, window=40),
+}
+
+
+@pytest.mark.parametrize("name", list(FOLD))
+def test_folded_window(name, monkeypatch):
+    monkeypatch.setenv("KVQ_WINDOW_FOLD", "1")
+    wl = small(BASE, config=400 + list(FOLD).index(name), **FOLD[name])
+    say(f"folded window {name}: {FOLD[name]}")
+    run = GpuRun(wl, chunk=64)
+    for s in range(wl.steps):
+        full_check(run, s, out_check_bf16=(s == 0))
+
+
 def test_empty_sequences_give_zero():
     wl = small(BASE, context=0, config=300, batch=2)
     say("empty sequences")
