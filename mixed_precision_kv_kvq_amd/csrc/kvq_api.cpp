@@ -48,7 +48,7 @@ KvqCacheDev dev_cache(const kvq_params *p, const kvq_cache *c) {
   d.batch = c->batch;
   d.mbps = c->max_blocks_per_seq;
   d.paged = p->block_size != 0;
-  d.pages_per_seq = d.paged ? 0 : (c->capacity + KVQ_PAGE - 1) / KVQ_PAGE;
+  d.pages_per_seq = d.paged ? 0 : kvq_pages_per_seq(c->capacity);
   d.pool_pages = d.paged ? c->capacity : 0;
   return d;
 }
@@ -141,7 +141,7 @@ kvq_status kvq_cache_sizes(const kvq_params *params, int32_t batch, int64_t capa
   const KvqLayout lay = layout_of(params);
   out->record_bytes = (size_t)lay.record;
   const size_t pages = params->block_size ? (size_t)capacity
-                                          : (size_t)batch * ((capacity + KVQ_PAGE - 1) / KVQ_PAGE);
+                                          : (size_t)batch * kvq_pages_per_seq(capacity);
   out->pages_bytes = pages * params->num_kv_heads * (size_t)lay.record;
   out->window_bytes = (size_t)batch * params->num_kv_heads * (size_t)params->window * KVQ_D *
                       (params->kv_dtype == KVQ_F32 ? 4 : 2);

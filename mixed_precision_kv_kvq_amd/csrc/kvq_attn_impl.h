@@ -891,9 +891,11 @@ struct Kern {
     const int64_t unit = wave / S;
     // Consecutive blocks go to the 8 XCDs in turn (block mod 8), so with S a multiple of 8 the
     // split at position k of every unit would land on the same XCD: rotating the split index by
-    // the unit spreads each split (the window splits in particular, which carry less work) evenly
-    // over the XCDs.
-    const int split = (int)((wave % S + unit) % S);
+    // the unit pair spreads each split (the window splits in particular, which carry less work)
+    // evenly over the XCDs.  Units 2i and 2i+1 keep the same rotation: their page records are
+    // adjacent and share a cache line (a 1856-byte K4V2 record is 14.5 lines), which is then
+    // fetched into one XCD's L2 only.
+    const int split = (int)((wave % S + unit / 2) % S);
     const int Hkv = args.Hkv;
     const int kvh = (int)(unit % Hkv), b = (int)(unit / Hkv);
     if (b >= args.cache.batch) return;
@@ -1036,9 +1038,12 @@ struct Kern {
     }
     // Cursor: the pair holding the next page to request.
     const uint8_t *pages = args.cache.pages;
-    const size_t page_stride = (size_t)args.cache.batch * Hkv * rec;  // contiguous: page p -> p + 1
-    const size_t pair_step = 2 * (size_t)SQ * page_stride;            // contiguous: pair j -> j + SQ
-    const uint8_t *cur = pages + ((size_t)b * Hkv + kvh) * rec + 2 * (size_t)sq * page_stride;
+    const size_t units = (size_t)args.cache.batch * Hkv;
+    const size_t unit_idx = (size_t)b * Hkv + kvh;
+    const size_t page_stride = units * rec;                  // contiguous: page p -> p + 1
+    const size_t pair_step = 2 * (size_t)SQ * page_stride;   // contiguous: pair j -> j + SQ
+    const uint8_t *unit_first = pages + unit_idx * rec;      // the unit's page 0
+    const uint8_t *cur = unit_first + 2 * (size_t)sq * page_stride;
     // Block-table entries are wave-uniform: read them with scalar loads (constant address space) so
     // that waiting for one never drains the vector-memory queue of requested pages.
     typedef const __attribute__((address_space(4))) int32_t *const_i32p;
@@ -1055,7 +1060,7 @@ struct Kern {
       const bool dup = odd && dup_last && k == npages - 1;
       const uint8_t *src;
       if (k >= npages) {  // prologue filler: the unit's first page (always allocated), never read
-        src = pages + (paged ? (size_t)kvh : ((size_t)b * Hkv + kvh)) * rec;
+        src = paged ? pages + (size_t)kvh * rec : unit_first;
       } else if (paged) {
         int e = tcur[(odd && !dup) ? 1 : 0];
         e = e < 0 ? 0 : (e > pool_last ? pool_last : e);

@@ -34,6 +34,8 @@
 
 #define KVQ_PAGE 16
 #define KVQ_D 128
+// Pages per sequence of a contiguous store of `capacity` tokens.
+__host__ __device__ inline int64_t kvq_pages_per_seq(int64_t capacity) { return (capacity + KVQ_PAGE - 1) / KVQ_PAGE; }
 
 struct KvqLayout {
   int kb, kg, vb, vg;
