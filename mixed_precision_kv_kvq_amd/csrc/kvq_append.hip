@@ -30,6 +30,57 @@ __device__ inline double load_elem(const uint8_t *row, int c, int kv_f32) {
   return (double)kvq_bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(row)[c]);
 }
 
+// Metadata of one group from its exact minimum and maximum: zero = RD16(min),
+// scale = RU16((max - zero) / (2^b - 1)), raised one fp16 step if zero + (2^b - 1) * scale
+// still falls below max (fp64, no contraction, in this order).
+struct GroupMeta {
+  uint32_t zb, sb;  // fp16 bits
+  double zf, sf, qmax;
+};
+__device__ inline GroupMeta group_meta(double mn, double mx, int bits) {
+  GroupMeta g;
+  mn = mn + 0.0;  // -0 -> +0
+  mx = mx + 0.0;
+  g.qmax = (double)((1 << bits) - 1);
+  g.zb = kvq_f16_round_down(mn);
+  g.zf = kvq_f16_bits_to_f64(g.zb);
+  g.sb = kvq_f16_round_up((mx - g.zf) / g.qmax);
+  g.sf = kvq_f16_bits_to_f64(g.sb);
+  if (g.zf + g.qmax * g.sf < mx) {
+    g.sb += 1u;
+    g.sf = kvq_f16_bits_to_f64(g.sb);
+  }
+  return g;
+}
+// Code of x: round half to even of (x - zero) / scale, clamped to [0, 2^b - 1]; 0 when scale == 0.
+__device__ inline uint32_t group_code(double x, const GroupMeta &g) {
+  // Computed unconditionally and selected (no branch per code): with scale 0 the quotient is
+  // +-inf or NaN, which the clamp keeps finite, and the select then yields 0.
+  double y = __builtin_rint((x - g.zf) / g.sf);
+  y = __builtin_fmin(__builtin_fmax(y, 0.0), g.qmax);
+  return g.sf == 0.0 ? 0u : (uint32_t)y;
+}
+
+// Codes of the 32 values x[0..31] of one group, equal to group_code of each.  With
+// d = x - zero in fp64 (as in group_code) and q = d / scale, the fp32 value
+// q32 = fp32(d) * fp32(1 / scale) is within 3.01 * 2^-24 * q < 2^-14 of q for q < 256, and
+// the fp64 quotient group_code rounds is within 2^-44 of q; so unless q32 lies within 2^-13
+// of a half-integer, both round to the same integer.  Codes in that band (exact ties
+// included) take group_code's fp64 division.
+__device__ inline void group_codes32(const double (&x)[32], const GroupMeta &g, uint32_t (&c)[32]) {
+  const float r32 = 1.0f / (float)g.sf;  // fp16 scale, exact in fp32; correctly rounded reciprocal
+  const float qmax32 = (float)g.qmax;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const double d = x[e] - g.zf;
+    const float qv = (float)d * r32;
+    const float fr = qv - __builtin_floorf(qv);
+    const float y = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(qv), 0.f), qmax32);
+    c[e] = g.sf == 0.0 ? 0u : (uint32_t)y;
+    if (__builtin_fabsf(fr - 0.5f) <= 0x1p-13f) c[e] = group_code(x[e], g);
+  }
+}
+
 // Quantize the 128 values held two per lane in groups of G; returns the codes of
 // this lane's two channels and the {scale, zero} metadata word of its group.
 __device__ inline void quantize_pair(double x0, double x1, int bits, int G, uint32_t *c0, uint32_t *c1,
@@ -39,29 +90,10 @@ __device__ inline void quantize_pair(double x0, double x1, int bits, int G, uint
     mn = __builtin_fmin(mn, __shfl_xor(mn, off));
     mx = __builtin_fmax(mx, __shfl_xor(mx, off));
   }
-  mn = mn + 0.0;
-  mx = mx + 0.0;
-  const double qmax = (double)((1 << bits) - 1);
-  const uint32_t zb = kvq_f16_round_down(mn);
-  const double zf = kvq_f16_bits_to_f64(zb);
-  uint32_t sb = kvq_f16_round_up((mx - zf) / qmax);
-  double sf = kvq_f16_bits_to_f64(sb);
-  if (zf + qmax * sf < mx) {
-    sb += 1u;
-    sf = kvq_f16_bits_to_f64(sb);
-  }
-  uint32_t r0 = 0, r1 = 0;
-  if (sf != 0.0) {
-    double y0 = __builtin_rint((x0 - zf) / sf);
-    double y1 = __builtin_rint((x1 - zf) / sf);
-    y0 = __builtin_fmin(__builtin_fmax(y0, 0.0), qmax);
-    y1 = __builtin_fmin(__builtin_fmax(y1, 0.0), qmax);
-    r0 = (uint32_t)y0;
-    r1 = (uint32_t)y1;
-  }
-  *c0 = r0;
-  *c1 = r1;
-  *meta = sb | (zb << 16);
+  const GroupMeta g = group_meta(mn, mx, bits);
+  *c0 = group_code(x0, g);
+  *c1 = group_code(x1, g);
+  *meta = g.sb | (g.zb << 16);
 }
 
 // Normalized 128-point Walsh-Hadamard transform of the values held two per lane.
@@ -84,6 +116,29 @@ __device__ inline void wht128_fp64(double &x0, double &x1, int lane) {
   }
   x0 = x0 * KVQ_WHT_C;
   x1 = x1 * KVQ_WHT_C;
+}
+
+// Tokens quantized on arrival (an append of n > R tokens to a length-L sequence: input tokens
+// j < m = n - R go to positions L + j) are split between the two kernels: whole 16-token pages
+// inside [L, L + m) go to the page kernel, the partial pages at either end to the per-token
+// kernel (at most 15 tokens each).
+struct DirectSplit {
+  int64_t p_start, p_end;  // whole pages [p_start, p_end)
+  int head, tail;          // tokens before p_start and after p_end handled one by one
+};
+__device__ inline DirectSplit direct_split(int64_t L, int m) {
+  DirectSplit d;
+  d.p_start = (L + KVQ_PAGE - 1) / KVQ_PAGE;
+  d.p_end = (L + m) / KVQ_PAGE;
+  if (d.p_end > d.p_start) {
+    d.head = (int)(d.p_start * KVQ_PAGE - L);
+    d.tail = (int)(L + m - d.p_end * KVQ_PAGE);
+  } else {
+    d.p_end = d.p_start;
+    d.head = m;
+    d.tail = 0;
+  }
+  return d;
 }
 
 __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
@@ -123,7 +178,16 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
     newK = a.k_new + in_off;
     newV = a.v_new + in_off;
   } else {
-    const int j = item - R;
+    // item nring + k: the k-th token quantized on arrival that is not in a whole page
+    const DirectSplit d = direct_split(L, nb - R);
+    const int k = item - nring;
+    int j;
+    if (k < d.head)
+      j = k;
+    else if (k - d.head < d.tail)
+      j = (int)(d.p_end * KVQ_PAGE - L) + (k - d.head);
+    else
+      return;
     t_q = (int64_t)L + j;
     const size_t in_off = (((size_t)b * a.n_new + j) * Hkv + h) * row_bytes;
     srcK = a.k_new + in_off;
@@ -210,12 +274,171 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
     reinterpret_cast<uint32_t *>(rec + lay.v_meta_off)[kvq_meta_dword(lay.nvg, n, lane)] = mv[lane];
 }
 
+// Whole pages of tokens quantized on arrival: one wave per (page, kv head, sequence).  Lane
+// 16 q + t holds channels [32 q, 32 q + 32) of the page's token t, so a 32-channel group's
+// minimum and maximum are taken inside the lane (wider groups combine 2 or 4 lanes); the
+// record is assembled in LDS (codes OR-ed into their words) and written with 16-byte stores.
+// Same quantizer arithmetic as the per-token kernel (group_meta / group_code), so the codes
+// and metadata are identical.
+__global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
+  constexpr int kMaxRecordWords = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 4;
+  __shared__ __attribute__((aligned(16))) uint32_t rw[kMaxRecordWords];
+  const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int L = a.seq_lens_before[b];
+  const int nb = a.n_new_per_seq ? a.n_new_per_seq[b] : a.n_new;
+  const int m = nb - a.R;
+  if (m <= 0) return;
+  const DirectSplit d = direct_split(L, m);
+  const int64_t page = d.p_start + blockIdx.x;
+  if (page >= d.p_end) return;
+  if (page >= (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq)) return;  // beyond the cache
+  const KvqLayout &lay = a.lay;
+  const int Hkv = a.Hkv;
+  const int t = lane & 15, q = lane >> 4;
+  const int esz = a.kv_f32 ? 4 : 2;
+  const size_t row_bytes = (size_t)KVQ_D * esz;
+  const int j = (int)(page * KVQ_PAGE + t - L);  // input token of this lane's page token
+  const size_t in_off = (((size_t)b * a.n_new + j) * Hkv + h) * row_bytes;
+  for (int w = lane; w < lay.record / 4; w += 64) rw[w] = 0u;
+  __syncthreads();
+
+  double x[32];
+  // This lane's 32 channels of a key or value row: 16-byte loads of bf16 or fp32 values.
+  auto load32 = [&](const uint8_t *row) {
+    if (a.kv_f32) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(row + 128 * q);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint4 w = p[k];
+        x[4 * k + 0] = (double)__builtin_bit_cast(float, w.x);
+        x[4 * k + 1] = (double)__builtin_bit_cast(float, w.y);
+        x[4 * k + 2] = (double)__builtin_bit_cast(float, w.z);
+        x[4 * k + 3] = (double)__builtin_bit_cast(float, w.w);
+      }
+    } else {
+      const uint4 *p = reinterpret_cast<const uint4 *>(row + 64 * q);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 w = p[k];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[8 * k + 2 * i] = (double)kvq_bf16_bits_to_f32(ws[i] & 0xFFFFu);
+          x[8 * k + 2 * i + 1] = (double)kvq_bf16_bits_to_f32(ws[i] >> 16);
+        }
+      }
+    }
+  };
+  // ---- keys ----
+  load32(a.k_new + in_off);
+  if (a.rotation) {
+    // 128-point butterflies in stage order 1, 2, ..., 64: stages up to 16 inside the lane,
+    // 32 and 64 across lanes q ^ 1 and q ^ 2 (same operands and order as the definition).
+#pragma unroll
+    for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        if ((e & hs) == 0) {
+          const double u = x[e], v = x[e + hs];
+          x[e] = u + v;
+          x[e + hs] = u - v;
+        }
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int lx = st == 0 ? 16 : 32;  // lane distance of channel distance 32 / 64
+      const bool upper = (lane & lx) != 0;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const double p = __shfl_xor(x[e], lx);
+        x[e] = upper ? p - x[e] : x[e] + p;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = x[e] * KVQ_WHT_C;
+  }
+  {
+    double mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) {
+      mn = __builtin_fmin(mn, x[e]);
+      mx = __builtin_fmax(mx, x[e]);
+    }
+    for (int off = 16; off < 16 * (lay.kg / 32); off <<= 1) {  // groups wider than 32 channels
+      mn = __builtin_fmin(mn, __shfl_xor(mn, off));
+      mx = __builtin_fmax(mx, __shfl_xor(mx, off));
+    }
+    const GroupMeta g = group_meta(mn, mx, lay.kb);
+    uint32_t cd[32];
+    group_codes32(x, g, cd);
+    const int kb = lay.kb, per = 16 / kb;
+    uint32_t *kw = rw + lay.k_codes_off / 4;
+#pragma unroll
+    for (int jo = 0; jo < 4; ++jo) {      // channel octet within the chunk
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {       // channel pair within the octet
+        const uint32_t c0 = cd[8 * jo + 2 * i], c1 = cd[8 * jo + 2 * i + 1];
+        const int u = 4 * q + i;
+        const uint32_t bits = (c0 << (kb * (u % per))) | (c1 << (16 + kb * (u % per)));
+        atomicOr(kw + (16 * jo + t) * kb + u / per, bits);
+      }
+    }
+    const int grp = (32 * q) / lay.kg;
+    if ((32 * q) % lay.kg == 0) rw[lay.k_meta_off / 4 + kvq_meta_dword(lay.nkg, t, grp)] = g.sb | (g.zb << 16);
+  }
+  // ---- values ----
+  load32(a.v_new + in_off);
+  {
+    double mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) {
+      mn = __builtin_fmin(mn, x[e]);
+      mx = __builtin_fmax(mx, x[e]);
+    }
+    for (int off = 16; off < 16 * (lay.vg / 32); off <<= 1) {
+      mn = __builtin_fmin(mn, __shfl_xor(mn, off));
+      mx = __builtin_fmax(mx, __shfl_xor(mx, off));
+    }
+    const GroupMeta g = group_meta(mn, mx, lay.vb);
+    uint32_t cd[32];
+    group_codes32(x, g, cd);
+    const int vb = lay.vb;
+    const int jj = t >> 2, r = t & 3, iv = r >> 1, hv = r & 1;
+    uint32_t *vw = rw + lay.v_codes_off / 4;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int c = 32 * q + e, mt = c >> 4, c16 = c & 15;
+      const int pos = iv * 8 * vb + mt * vb;
+      atomicOr(vw + (16 * jj + c16) * vb + (pos >> 4), cd[e] << (16 * hv + (pos & 15)));
+    }
+    const int grp = (32 * q) / lay.vg;
+    if ((32 * q) % lay.vg == 0) rw[lay.v_meta_off / 4 + kvq_meta_dword(lay.nvg, t, grp)] = g.sb | (g.zb << 16);
+  }
+  __syncthreads();
+  const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
+                                           (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, b, h, page);
+  uint4 *rec = reinterpret_cast<uint4 *>(a.cache.pages + (size_t)rec_idx * lay.record);
+  const uint4 *src = reinterpret_cast<const uint4 *>(rw);
+  for (int c = lane; c < lay.record / 16; c += 64) rec[c] = src[c];
+}
+
 }  // namespace
 
 hipError_t kvq_launch_append(const KvqAppendArgs &a, hipStream_t s) {
   if (a.n_new <= 0 || a.cache.batch <= 0) return hipSuccess;
-  dim3 grid((unsigned)a.n_new, (unsigned)a.Hkv, (unsigned)a.cache.batch);
   (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
-  hipLaunchKernelGGL(kvq_append_kernel, grid, dim3(64), 0, s, a);
+  // per-token kernel: the ring items, then at most 2 * 15 tokens quantized on arrival outside
+  // whole pages; page kernel: the whole pages (at most (n - R) / 16 per sequence)
+  const int ring = a.n_new < a.R ? a.n_new : a.R;
+  const int direct = a.n_new - ring;
+  const int items = ring + (direct < 2 * (KVQ_PAGE - 1) ? direct : 2 * (KVQ_PAGE - 1));
+  hipLaunchKernelGGL(kvq_append_kernel, dim3((unsigned)items, (unsigned)a.Hkv, (unsigned)a.cache.batch), dim3(64), 0,
+                     s, a);
+  if (direct >= KVQ_PAGE) {
+    const unsigned pages = (unsigned)(direct / KVQ_PAGE);
+    hipLaunchKernelGGL(kvq_append_pages_kernel, dim3(pages, (unsigned)a.Hkv, (unsigned)a.cache.batch), dim3(64), 0,
+                       s, a);
+  }
   return hipGetLastError();
 }

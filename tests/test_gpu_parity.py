@@ -180,6 +180,42 @@ def test_folded_window(name, monkeypatch):
         full_check(run, s, out_check_bf16=(s == 0))
 
 
+def test_exact_ties_in_both_append_kernels():
+    """Inputs built so that many (x - zero) / scale are exact half-integers (values k/16 with a
+    group minimum 0 and maximum 30/16 for 4-bit keys, 3 for 2-bit values): codes must follow
+    round-half-to-even bit for bit, both for tokens appended one by one and for whole pages."""
+    import oracle as O
+
+    rng = np.random.default_rng(11)
+    n = 80
+    Kx = rng.integers(0, 31, size=(n, 128)).astype(np.float32) / 16
+    Kx[:, 0::32], Kx[:, 1::32] = 0.0, 30.0 / 16
+    Vx = rng.integers(0, 49, size=(n, 128)).astype(np.float32) / 16
+    Vx[:, 0], Vx[:, 1] = 0.0, 3.0
+    prm = K.make_params(128, 1, 1, 4, 32, 2, 128, 0, 0, K.KVQ_BF16, 0)
+    cache = K.CacheBuffers(prm, 1, 128)
+
+    def rows(x, t0, t1):
+        return torch.from_numpy(W.f32_to_bf16_bits(x[t0:t1]).view(np.int16).reshape(1, t1 - t0, 1, 128)).cuda()
+
+    # 5 tokens one by one (per-token kernel), then 75: 11 single tokens up to the page boundary and
+    # 4 whole pages (page kernel)
+    for t0, t1 in ((0, 5), (5, 80)):
+        before = torch.tensor([t0], dtype=torch.int32, device="cuda")
+        K.kvq_quantize_append(prm, cache.struct, before, None, rows(Kx, t0, t1), rows(Vx, t0, t1), t1 - t0)
+    lens = torch.tensor([n], dtype=torch.int32, device="cuda")
+    kc = torch.empty((n, 1, 128), dtype=torch.uint8, device="cuda")
+    vc = torch.empty((n, 1, 128), dtype=torch.uint8, device="cuda")
+    K.kvq_dequantize_debug(prm, cache.struct, lens, 0, 0, n, k_codes=kc, v_codes=vc)
+    torch.cuda.synchronize()
+    ek, _, _ = O.quantize(Kx.astype(np.float64), 4, 32)
+    ev, _, _ = O.quantize(Vx.astype(np.float64), 2, 128)
+    ties_k = np.sum(((Kx.astype(np.float64) / 0.125) % 1.0) == 0.5)
+    assert ties_k > 1000, ties_k  # the construction does produce exact ties
+    assert np.array_equal(kc.cpu().numpy()[:, 0], ek), "key codes differ from the oracle"
+    assert np.array_equal(vc.cpu().numpy()[:, 0], ev), "value codes differ from the oracle"
+
+
 def test_empty_sequences_give_zero():
     wl = small(BASE, context=0, config=300, batch=2)
     say("empty sequences")
