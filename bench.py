@@ -223,19 +223,23 @@ def main():
     # ---- set-up: prefill the cache with the context (bulk append + quantize, timed apart) ----
     t_setup = time.time()
     chunk = 2048
-    prefill_us, prefill_bytes = 0.0, 0
-    ev_p = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    # all prefill inputs generated into HBM first (2.1 GB of bf16 rows), then the appends
+    # back to back between two events
+    pre = []
     for t0 in range(0, L0, chunk):
         n = min(chunk, L0 - t0)
-        k = gen.kv(W.TENSOR_K, t0, n)
-        v = gen.kv(W.TENSOR_V, t0, n)
-        before = torch.full((B,), t0, dtype=torch.int32, device=dev)
-        ev_p[0].record(stream)
+        pre.append((t0, n, gen.kv(W.TENSOR_K, t0, n), gen.kv(W.TENSOR_V, t0, n),
+                    torch.full((B,), t0, dtype=torch.int32, device=dev)))
+    prefill_bytes = sum(append_bytes(wl, t0, n) for t0, n, _, _, _ in pre)
+    ev_p = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev_p[0].record(stream)
+    for t0, n, k, v, before in pre:
         K.kvq_quantize_append(params, cache.struct, before, None, k, v, n)
-        ev_p[1].record(stream)
-        torch.cuda.synchronize()
-        prefill_us += ev_p[0].elapsed_time(ev_p[1]) * 1e3
-        prefill_bytes += append_bytes(wl, t0, n)
+    ev_p[1].record(stream)
+    torch.cuda.synchronize()
+    prefill_us = ev_p[0].elapsed_time(ev_p[1]) * 1e3
+    del pre
     # per-step inputs, resident in HBM before timing
     k_steps = [gen.kv(W.TENSOR_K, L0 + s, 1) for s in range(total_steps)]
     v_steps = [gen.kv(W.TENSOR_V, L0 + s, 1) for s in range(total_steps)]
@@ -347,7 +351,8 @@ def main():
         "setup_s": round(setup_s, 2),
         "prefill_quantize": {
             "what": f"bulk append + quantize of the {L0}-token context, {(L0 + chunk - 1) // chunk} appends of "
-                    f"{chunk} tokens per sequence (kvq_quantize_append), each between two events",
+                    f"{chunk} tokens per sequence (kvq_quantize_append) back to back between two events, "
+                    f"inputs already in HBM",
             "us": round(prefill_us, 1), "algorithmic_bytes": int(prefill_bytes),
             "achieved_GBs": round(prefill_bytes / (prefill_us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(prefill_bytes / (prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),

@@ -19,6 +19,8 @@
 // Each ring slot is owned by exactly one wave, so the read of the old token and
 // the write of the new one never race.  All quantizer arithmetic is IEEE fp64
 // with no contraction, in the same operation order as its definition.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 #pragma clang fp contract(off)
@@ -61,24 +63,20 @@ __device__ inline uint32_t group_code(double x, const GroupMeta &g) {
   return g.sf == 0.0 ? 0u : (uint32_t)y;
 }
 
-// Codes of the 32 values x[0..31] of one group, equal to group_code of each.  With
+// group_code of x, computed in fp32 where that is provably the same integer.  With
 // d = x - zero in fp64 (as in group_code) and q = d / scale, the fp32 value
-// q32 = fp32(d) * fp32(1 / scale) is within 3.01 * 2^-24 * q < 2^-14 of q for q < 256, and
-// the fp64 quotient group_code rounds is within 2^-44 of q; so unless q32 lies within 2^-13
-// of a half-integer, both round to the same integer.  Codes in that band (exact ties
-// included) take group_code's fp64 division.
-__device__ inline void group_codes32(const double (&x)[32], const GroupMeta &g, uint32_t (&c)[32]) {
-  const float r32 = 1.0f / (float)g.sf;  // fp16 scale, exact in fp32; correctly rounded reciprocal
-  const float qmax32 = (float)g.qmax;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    const double d = x[e] - g.zf;
-    const float qv = (float)d * r32;
-    const float fr = qv - __builtin_floorf(qv);
-    const float y = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(qv), 0.f), qmax32);
-    c[e] = g.sf == 0.0 ? 0u : (uint32_t)y;
-    if (__builtin_fabsf(fr - 0.5f) <= 0x1p-13f) c[e] = group_code(x[e], g);
-  }
+// q32 = fp32(d) * r32, r32 = fp32(1 / scale), is within 3.01 * 2^-24 * q < 2^-14 of q for
+// q < 256, and the fp64 quotient group_code rounds is within 2^-44 of q; so unless q32 lies
+// within 2^-13 of a half-integer, both round to the same integer.  Codes in that band (exact
+// ties included) take group_code's fp64 division.
+__device__ inline uint32_t group_code_fast(double x, const GroupMeta &g, float r32, float qmax32) {
+  const double d = x - g.zf;
+  const float qv = (float)d * r32;
+  const float fr = qv - __builtin_floorf(qv);
+  const float y = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(qv), 0.f), qmax32);
+  uint32_t c = g.sf == 0.0 ? 0u : (uint32_t)y;
+  if (__builtin_fabsf(fr - 0.5f) <= 0x1p-13f) c = group_code(x, g);
+  return c;
 }
 
 // Quantize the 128 values held two per lane in groups of G; returns the codes of
@@ -280,6 +278,9 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
 // record is assembled in LDS (codes OR-ed into their words) and written with 16-byte stores.
 // Same quantizer arithmetic as the per-token kernel (group_meta / group_code), so the codes
 // and metadata are identical.
+// ROT: keys are rotated first; the lane's values are then fp64 (the transform's results).
+// Without rotation they are the inputs themselves, exact in fp32, which halves the registers.
+template <bool ROT>
 __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   constexpr int kMaxRecordWords = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 4;
   __shared__ __attribute__((aligned(16))) uint32_t rw[kMaxRecordWords];
@@ -302,7 +303,8 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   for (int w = lane; w < lay.record / 4; w += 64) rw[w] = 0u;
   __syncthreads();
 
-  double x[32];
+  typedef typename std::conditional<ROT, double, float>::type Val;
+  Val x[32];
   // This lane's 32 channels of a key or value row: 16-byte loads of bf16 or fp32 values.
   auto load32 = [&](const uint8_t *row) {
     if (a.kv_f32) {
@@ -310,10 +312,10 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const uint4 w = p[k];
-        x[4 * k + 0] = (double)__builtin_bit_cast(float, w.x);
-        x[4 * k + 1] = (double)__builtin_bit_cast(float, w.y);
-        x[4 * k + 2] = (double)__builtin_bit_cast(float, w.z);
-        x[4 * k + 3] = (double)__builtin_bit_cast(float, w.w);
+        x[4 * k + 0] = (Val)__builtin_bit_cast(float, w.x);
+        x[4 * k + 1] = (Val)__builtin_bit_cast(float, w.y);
+        x[4 * k + 2] = (Val)__builtin_bit_cast(float, w.z);
+        x[4 * k + 3] = (Val)__builtin_bit_cast(float, w.w);
       }
     } else {
       const uint4 *p = reinterpret_cast<const uint4 *>(row + 64 * q);
@@ -323,15 +325,15 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[8 * k + 2 * i] = (double)kvq_bf16_bits_to_f32(ws[i] & 0xFFFFu);
-          x[8 * k + 2 * i + 1] = (double)kvq_bf16_bits_to_f32(ws[i] >> 16);
+          x[8 * k + 2 * i] = (Val)kvq_bf16_bits_to_f32(ws[i] & 0xFFFFu);
+          x[8 * k + 2 * i + 1] = (Val)kvq_bf16_bits_to_f32(ws[i] >> 16);
         }
       }
     }
   };
   // ---- keys ----
   load32(a.k_new + in_off);
-  if (a.rotation) {
+  if constexpr (ROT) {
     // 128-point butterflies in stage order 1, 2, ..., 64: stages up to 16 inside the lane,
     // 32 and 64 across lanes q ^ 1 and q ^ 2 (same operands and order as the definition).
 #pragma unroll
@@ -359,26 +361,27 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     for (int e = 0; e < 32; ++e) x[e] = x[e] * KVQ_WHT_C;
   }
   {
-    double mn = x[0], mx = x[0];
+    Val mnv = x[0], mxv = x[0];
 #pragma unroll
     for (int e = 1; e < 32; ++e) {
-      mn = __builtin_fmin(mn, x[e]);
-      mx = __builtin_fmax(mx, x[e]);
+      mnv = mnv < x[e] ? mnv : x[e];  // exact in either precision
+      mxv = mxv > x[e] ? mxv : x[e];
     }
+    double mn = (double)mnv, mx = (double)mxv;
     for (int off = 16; off < 16 * (lay.kg / 32); off <<= 1) {  // groups wider than 32 channels
       mn = __builtin_fmin(mn, __shfl_xor(mn, off));
       mx = __builtin_fmax(mx, __shfl_xor(mx, off));
     }
     const GroupMeta g = group_meta(mn, mx, lay.kb);
-    uint32_t cd[32];
-    group_codes32(x, g, cd);
+    const float r32 = 1.0f / (float)g.sf, qmax32 = (float)g.qmax;  // fp16 scale: exact in fp32
     const int kb = lay.kb, per = 16 / kb;
     uint32_t *kw = rw + lay.k_codes_off / 4;
 #pragma unroll
     for (int jo = 0; jo < 4; ++jo) {      // channel octet within the chunk
 #pragma unroll
       for (int i = 0; i < 4; ++i) {       // channel pair within the octet
-        const uint32_t c0 = cd[8 * jo + 2 * i], c1 = cd[8 * jo + 2 * i + 1];
+        const uint32_t c0 = group_code_fast((double)x[8 * jo + 2 * i], g, r32, qmax32);
+        const uint32_t c1 = group_code_fast((double)x[8 * jo + 2 * i + 1], g, r32, qmax32);
         const int u = 4 * q + i;
         const uint32_t bits = (c0 << (kb * (u % per))) | (c1 << (16 + kb * (u % per)));
         atomicOr(kw + (16 * jo + t) * kb + u / per, bits);
@@ -390,19 +393,19 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   // ---- values ----
   load32(a.v_new + in_off);
   {
-    double mn = x[0], mx = x[0];
+    Val mnv = x[0], mxv = x[0];
 #pragma unroll
     for (int e = 1; e < 32; ++e) {
-      mn = __builtin_fmin(mn, x[e]);
-      mx = __builtin_fmax(mx, x[e]);
+      mnv = mnv < x[e] ? mnv : x[e];
+      mxv = mxv > x[e] ? mxv : x[e];
     }
+    double mn = (double)mnv, mx = (double)mxv;
     for (int off = 16; off < 16 * (lay.vg / 32); off <<= 1) {
       mn = __builtin_fmin(mn, __shfl_xor(mn, off));
       mx = __builtin_fmax(mx, __shfl_xor(mx, off));
     }
     const GroupMeta g = group_meta(mn, mx, lay.vb);
-    uint32_t cd[32];
-    group_codes32(x, g, cd);
+    const float r32 = 1.0f / (float)g.sf, qmax32 = (float)g.qmax;
     const int vb = lay.vb;
     const int jj = t >> 2, r = t & 3, iv = r >> 1, hv = r & 1;
     uint32_t *vw = rw + lay.v_codes_off / 4;
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     for (int e = 0; e < 32; ++e) {
       const int c = 32 * q + e, mt = c >> 4, c16 = c & 15;
       const int pos = iv * 8 * vb + mt * vb;
-      atomicOr(vw + (16 * jj + c16) * vb + (pos >> 4), cd[e] << (16 * hv + (pos & 15)));
+      atomicOr(vw + (16 * jj + c16) * vb + (pos >> 4), group_code_fast((double)x[e], g, r32, qmax32) << (16 * hv + (pos & 15)));
     }
     const int grp = (32 * q) / lay.vg;
     if ((32 * q) % lay.vg == 0) rw[lay.v_meta_off / 4 + kvq_meta_dword(lay.nvg, t, grp)] = g.sb | (g.zb << 16);
@@ -437,8 +440,11 @@ hipError_t kvq_launch_append(const KvqAppendArgs &a, hipStream_t s) {
                      s, a);
   if (direct >= KVQ_PAGE) {
     const unsigned pages = (unsigned)(direct / KVQ_PAGE);
-    hipLaunchKernelGGL(kvq_append_pages_kernel, dim3(pages, (unsigned)a.Hkv, (unsigned)a.cache.batch), dim3(64), 0,
-                       s, a);
+    const dim3 grid(pages, (unsigned)a.Hkv, (unsigned)a.cache.batch);
+    if (a.rotation)
+      hipLaunchKernelGGL(kvq_append_pages_kernel<true>, grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL(kvq_append_pages_kernel<false>, grid, dim3(64), 0, s, a);
   }
   return hipGetLastError();
 }
