@@ -1,0 +1,108 @@
+"""GPU parity at the full workload sizes, on sampled (sequence, kv head) units.
+
+The caches are filled on the device (the device generator, checked bit-identical to the host one
+in test_gpu_parity.py) through kvq_quantize_append — whole pages by the page kernel, window
+tokens and page remainders one by one — and attended with the launch configuration bench.py
+times (split plan for the full batch and length).  For sampled units the oracle rebuilds the
+cache from the host generator: codes, fp16 metadata and dequantized values are compared bit for
+bit over sampled windows of positions, and the outputs of every query head of the unit within
+max-abs 2e-3 and relative L2 1e-3 (fp32 output); the bf16 output equals round-to-nearest-even
+of the fp32 output everywhere.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle as O  # noqa: E402
+import workloads as W  # noqa: E402
+from kvq_harness import GpuRun, assert_close, oracle_heads, oracle_params  # noqa: E402
+
+
+def say(msg):
+    print(f"[gpu-full] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def windows_of(L, n=512):
+    """Position windows checked bit for bit: start, middle and end of the sequence."""
+    starts = sorted({0, max(0, L // 2 - n // 2), max(0, L - n)})
+    return [(t0, min(n, L - t0)) for t0 in starts if L - t0 > 0]
+
+
+def check_units(run: GpuRun, units, step, o32, obf):
+    wl = run.wl
+    g = wl.group_q
+    assert np.array_equal(obf, W.bf16_bits_to_f32(W.f32_to_bf16_bits(o32))), "bf16 output is not RNE of fp32"
+    for b, kvh in units:
+        L = int(run.current_lengths()[b])
+        Kx = wl.kv_f32(W.TENSOR_K, b, kvh, 0, L).astype(np.float64)
+        Vx = wl.kv_f32(W.TENSOR_V, b, kvh, 0, L).astype(np.float64)
+        cache = O.build_unit_cache(Kx, Vx, L, oracle_params(wl))
+        nq = cache["nq"]
+        for t0, n in windows_of(L):
+            rb = run.readback(b, t0, n)
+            q1 = min(max(nq - t0, 0), n)  # quantized positions in the window
+            if q1:
+                sl = slice(t0, t0 + q1)
+                assert np.array_equal(rb["k_codes"][:q1, kvh], cache["k_codes"][sl]), f"key codes ({b},{kvh}) @{t0}"
+                assert np.array_equal(rb["v_codes"][:q1, kvh], cache["v_codes"][sl]), f"value codes ({b},{kvh}) @{t0}"
+                assert np.array_equal(rb["k_meta"][:q1, kvh, :, 0], O.f16_bits(cache["k_scale"][sl]))
+                assert np.array_equal(rb["k_meta"][:q1, kvh, :, 1], O.f16_bits(cache["k_zero"][sl]))
+                assert np.array_equal(rb["v_meta"][:q1, kvh, :, 0], O.f16_bits(cache["v_scale"][sl]))
+                assert np.array_equal(rb["v_meta"][:q1, kvh, :, 1], O.f16_bits(cache["v_zero"][sl]))
+                assert np.array_equal(rb["k_hat"][:q1, kvh], cache["k_hat"][sl].astype(np.float32))
+                assert np.array_equal(rb["v_hat"][:q1, kvh], cache["v_hat"][sl].astype(np.float32))
+            if q1 < n:  # window positions hold the exact values
+                assert np.array_equal(rb["k_hat"][q1:n, kvh], Kx[t0 + q1:t0 + n].astype(np.float32))
+                assert np.array_equal(rb["v_hat"][q1:n, kvh], Vx[t0 + q1:t0 + n].astype(np.float32))
+        ref = oracle_heads(run, cache, b, kvh, step)
+        maxabs, rel = assert_close(o32[b, kvh * g:(kvh + 1) * g], ref, f"unit ({b},{kvh}) L={L}")
+        say(f"unit ({b},{kvh}) L={L}: codes exact on {len(windows_of(L))} windows, max-abs {maxabs:.2e}, "
+            f"rel-L2 {rel:.2e}")
+
+
+def attend_both(run: GpuRun, step: int):
+    L = run.current_lengths()
+    lens = torch.from_numpy(L.astype(np.int32)).cuda()
+    q = run._q_dev(step)
+    return run.attend(lens, int(L.max()), q, "f32"), run.attend(lens, int(L.max()), q, "bf16")
+
+
+def test_full_config3_all_steps():
+    """Batch 16, 32 q / 8 kv heads, 32768 tokens, window 128: prefill, all 64 decode steps
+    (append + attention), outputs and codes of sampled units checked after the last step."""
+    wl = W.WORKLOADS[3]
+    say(f"config 3 full: {wl.name}")
+    run = GpuRun(wl, device_gen=True, chunk=2048)
+    for s in range(wl.steps - 1):
+        run.decode(s)
+    run.decode(wl.steps - 1)
+    o32, obf = attend_both(run, wl.steps - 1)
+    check_units(run, [(0, 0), (3, 2), (6, 6), (9, 5), (12, 1), (15, 7)], wl.steps - 1, o32, obf)
+
+
+@pytest.mark.parametrize("kb,vb", W.SWEEP_BITS)
+def test_full_config4_paged_sweep(kb, vb):
+    """Batch 8, lengths uniform in [1024, 16384], paged 16-token blocks through a seeded block table."""
+    wl = W.WORKLOADS[4].with_bits(kb, vb)
+    say(f"config 4 full K{kb}V{vb}: lengths {wl.context_lengths().tolist()}")
+    run = GpuRun(wl, device_gen=True, chunk=4096)
+    o32, obf = attend_both(run, 0)
+    check_units(run, [(0, 0), (3, 4), (4, 2), (7, 7)], 0, o32, obf)
+
+
+def test_full_config5_rotated():
+    """Batch 64, 64 q / 8 kv heads, 131072 tokens, key-only Walsh-Hadamard rotation."""
+    wl = W.WORKLOADS[5]
+    say(f"config 5 full: {wl.name}")
+    run = GpuRun(wl, device_gen=True, chunk=4096)
+    o32, obf = attend_both(run, 0)
+    check_units(run, [(0, 0), (21, 3), (42, 5), (63, 7)], 0, o32, obf)
