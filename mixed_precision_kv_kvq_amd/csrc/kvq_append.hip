@@ -68,7 +68,17 @@ __device__ inline uint32_t group_code(double x, const GroupMeta &g) {
 // q32 = fp32(d) * r32, r32 = fp32(1 / scale), is within 3.01 * 2^-24 * q < 2^-14 of q for
 // q < 256, and the fp64 quotient group_code rounds is within 2^-44 of q; so unless q32 lies
 // within 2^-13 of a half-integer, both round to the same integer.  Codes in that band (exact
-// ties included) take group_code's fp64 division.
+// ties included) take group_code's fp64 division.  For an fp32 input x (a bf16 or fp32 value)
+// the fp64 difference with the fp16 zero is exact, so fp32(d) is just x - zero rounded once in
+// fp32; an fp64 input (a rotated key) is subtracted in fp64 first.
+__device__ inline uint32_t group_code_fast(float x, const GroupMeta &g, float r32, float qmax32) {
+  const float qv = (x - (float)g.zf) * r32;
+  const float fr = qv - __builtin_floorf(qv);
+  const float y = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(qv), 0.f), qmax32);
+  uint32_t c = g.sf == 0.0 ? 0u : (uint32_t)y;
+  if (__builtin_fabsf(fr - 0.5f) <= 0x1p-13f) c = group_code((double)x, g);
+  return c;
+}
 __device__ inline uint32_t group_code_fast(double x, const GroupMeta &g, float r32, float qmax32) {
   const double d = x - g.zf;
   const float qv = (float)d * r32;
@@ -380,8 +390,8 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     for (int jo = 0; jo < 4; ++jo) {      // channel octet within the chunk
 #pragma unroll
       for (int i = 0; i < 4; ++i) {       // channel pair within the octet
-        const uint32_t c0 = group_code_fast((double)x[8 * jo + 2 * i], g, r32, qmax32);
-        const uint32_t c1 = group_code_fast((double)x[8 * jo + 2 * i + 1], g, r32, qmax32);
+        const uint32_t c0 = group_code_fast(x[8 * jo + 2 * i], g, r32, qmax32);
+        const uint32_t c1 = group_code_fast(x[8 * jo + 2 * i + 1], g, r32, qmax32);
         const int u = 4 * q + i;
         const uint32_t bits = (c0 << (kb * (u % per))) | (c1 << (16 + kb * (u % per)));
         atomicOr(kw + (16 * jo + t) * kb + u / per, bits);
@@ -413,7 +423,7 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     for (int e = 0; e < 32; ++e) {
       const int c = 32 * q + e, mt = c >> 4, c16 = c & 15;
       const int pos = iv * 8 * vb + mt * vb;
-      atomicOr(vw + (16 * jj + c16) * vb + (pos >> 4), group_code_fast((double)x[e], g, r32, qmax32) << (16 * hv + (pos & 15)));
+      atomicOr(vw + (16 * jj + c16) * vb + (pos >> 4), group_code_fast(x[e], g, r32, qmax32) << (16 * hv + (pos & 15)));
     }
     const int grp = (32 * q) / lay.vg;
     if ((32 * q) % lay.vg == 0) rw[lay.v_meta_off / 4 + kvq_meta_dword(lay.nvg, t, grp)] = g.sb | (g.zb << 16);
