@@ -419,11 +419,14 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     const int vb = lay.vb;
     const int jj = t >> 2, r = t & 3, iv = r >> 1, hv = r & 1;
     uint32_t *vw = rw + lay.v_codes_off / 4;
+    // channels 32 q + e and 32 q + 16 + e (tiles 2q and 2q + 1, same column) share a record word
+    // for every value bit width: one OR for both codes
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int c = 32 * q + e, mt = c >> 4, c16 = c & 15;
-      const int pos = iv * 8 * vb + mt * vb;
-      atomicOr(vw + (16 * jj + c16) * vb + (pos >> 4), group_code_fast(x[e], g, r32, qmax32) << (16 * hv + (pos & 15)));
+    for (int e = 0; e < 16; ++e) {
+      const int m0 = 2 * q, pos0 = iv * 8 * vb + m0 * vb, pos1 = pos0 + vb;
+      const uint32_t bits = (group_code_fast(x[e], g, r32, qmax32) << (16 * hv + (pos0 & 15))) |
+                            (group_code_fast(x[e + 16], g, r32, qmax32) << (16 * hv + (pos1 & 15)));
+      atomicOr(vw + (16 * jj + e) * vb + (pos0 >> 4), bits);
     }
     const int grp = (32 * q) / lay.vg;
     if ((32 * q) % lay.vg == 0) rw[lay.v_meta_off / 4 + kvq_meta_dword(lay.nvg, t, grp)] = g.sb | (g.zb << 16);
