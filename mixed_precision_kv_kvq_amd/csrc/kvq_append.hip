@@ -388,14 +388,23 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     uint32_t *kw = rw + lay.k_codes_off / 4;
 #pragma unroll
     for (int jo = 0; jo < 4; ++jo) {      // channel octet within the chunk
+      // the octet's channel pairs u = 4q + i fill word u / per of slot 16 jo + t: one word for
+      // bit widths up to 4, two at 8; the codes are gathered per word before one OR
+      uint32_t acc = 0;
+      int wcur = (4 * q) / per;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {       // channel pair within the octet
         const uint32_t c0 = group_code_fast(x[8 * jo + 2 * i], g, r32, qmax32);
         const uint32_t c1 = group_code_fast(x[8 * jo + 2 * i + 1], g, r32, qmax32);
         const int u = 4 * q + i;
-        const uint32_t bits = (c0 << (kb * (u % per))) | (c1 << (16 + kb * (u % per)));
-        atomicOr(kw + (16 * jo + t) * kb + u / per, bits);
+        if (u / per != wcur) {
+          atomicOr(kw + (16 * jo + t) * kb + wcur, acc);
+          acc = 0;
+          wcur = u / per;
+        }
+        acc |= (c0 << (kb * (u % per))) | (c1 << (16 + kb * (u % per)));
       }
+      atomicOr(kw + (16 * jo + t) * kb + wcur, acc);
     }
     const int grp = (32 * q) / lay.kg;
     if ((32 * q) % lay.kg == 0) rw[lay.k_meta_off / 4 + kvq_meta_dword(lay.nkg, t, grp)] = g.sb | (g.zb << 16);
