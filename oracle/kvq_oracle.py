@@ -39,6 +39,9 @@ Readings taken where the pages leave a step open (all listed in the design doc):
 * Key rotation: 128-point normalized Sylvester Walsh-Hadamard transform,
   butterflies in stage order h = 1, 2, ..., d/2 on fp64, then a multiply by
   c = RN64(2^-3.5).  Window keys stay raw and are scored with the raw query.
+* Value rotation (a variant): the same transform on the values before they are
+  quantized; the attention output over the quantized tokens is transformed back
+  (the normalized Sylvester matrix is symmetric and orthogonal, its own inverse).
 * GQA: query head h reads kv head floor(h / g), g = Hq / Hkv.
 """
 from __future__ import annotations
@@ -180,20 +183,26 @@ def build_unit_cache(K: np.ndarray, V: np.ndarray, L: int, wl_params: dict):
     """Quantized cache state of one (sequence, kv head) after L tokens.
 
     K, V: [L][d] raw values (exactly representable in fp64).
-    wl_params: k_bits, k_group, v_bits, v_group, window, rotation.
+    wl_params: k_bits, k_group, v_bits, v_group, window, rotation and optionally
+    value_rotation.
     Returns a dict with the codes and fp16 metadata of the quantized tokens,
-    the dequantized keys (rotated domain when rotation is on) and values, and
-    the raw window tokens.
+    the dequantized keys and values (rotated domain when the respective
+    rotation is on), and the raw window tokens.
     """
     R = wl_params["window"]
     nq = max(0, L - R)
     Kq = np.asarray(K[:nq], dtype=F64)
     if wl_params["rotation"]:
         Kq = wht_rotate(Kq)
+    Vq = np.asarray(V[:nq], dtype=F64)
+    v_rot = bool(wl_params.get("value_rotation", False))
+    if v_rot:
+        Vq = wht_rotate(Vq)
     kc, ks, kz = quantize(Kq, wl_params["k_bits"], wl_params["k_group"])
-    vc, vs, vz = quantize(np.asarray(V[:nq], dtype=F64), wl_params["v_bits"], wl_params["v_group"])
+    vc, vs, vz = quantize(Vq, wl_params["v_bits"], wl_params["v_group"])
     return dict(
         nq=nq,
+        v_rotated=v_rot,
         k_codes=kc, k_scale=ks, k_zero=kz,
         v_codes=vc, v_scale=vs, v_zero=vz,
         k_hat=dequantize(kc, ks, kz, wl_params["k_group"]),
@@ -229,9 +238,16 @@ def unit_scores(q: np.ndarray, cache: dict, scale: float, rotation: bool) -> np.
 
 
 def unit_attention(q: np.ndarray, cache: dict, scale: float, rotation: bool) -> np.ndarray:
-    """Decode attention of one query head over one (sequence, kv head) cache."""
+    """Decode attention of one query head over one (sequence, kv head) cache.
+
+    With value rotation the quantized tokens' values are in the rotated domain:
+    their weighted sum is transformed back before the window tokens are added.
+    """
     s = unit_scores(q, cache, scale, rotation)
     a = softmax(s)
+    nq = cache["nq"]
+    if cache.get("v_rotated", False):
+        return wht_rotate(a[:nq] @ cache["v_hat"]) + a[nq:] @ cache["v_win"]
     Vall = np.concatenate([cache["v_hat"], cache["v_win"]], axis=0)
     return a @ Vall
 

@@ -118,8 +118,20 @@ def mut_softmax_no_max_shift_wrong_axis(M):
     M.softmax = softmax
 
 
+def mut_value_rotation_not_undone(M):
+    orig = M.unit_attention
+
+    def unit_attention(q, cache, scale, rotation):
+        if not cache.get("v_rotated", False):
+            return orig(q, cache, scale, rotation)
+        a = M.softmax(M.unit_scores(q, cache, scale, rotation))
+        nq = cache["nq"]
+        return a[:nq] @ cache["v_hat"] + a[nq:] @ cache["v_win"]  # mistake: output left in the rotated domain
+    M.unit_attention = unit_attention
+
+
 MUTATIONS = [
-    mut_zero_round_nearest, mut_scale_round_nearest, mut_round_half_up, mut_dequant_sign,
+    mut_value_rotation_not_undone, mut_zero_round_nearest, mut_scale_round_nearest, mut_round_half_up, mut_dequant_sign,
     mut_dequant_group_index, mut_attention_no_scale, mut_attention_reversed_values, mut_gqa_modulo,
     mut_window_off_by_one, mut_wht_no_normalization, mut_wht_constant_low, mut_softmax_no_max_shift_wrong_axis,
 ]

@@ -343,6 +343,36 @@ def check_rotation_special_case(O_):
     assert np.max(np.abs(s - (cache["k_hat"] @ (H @ q)) * sc)) < 1e-12
 
 
+def check_value_rotation(O_):
+    """Value rotation (a variant): the output over the quantized tokens is the Hadamard matrix
+    (scipy's, normalized — a route independent of the oracle's butterflies) applied to the
+    weighted dequantized rotated values; and, with the same quantized keys, it stays within the
+    value quantization error of attention over the raw values: the rotation back is orthogonal,
+    so |o - o_raw|_2 <= max_t |v_hat_t - v_t|_2 <= sqrt(128) * max scale / 2."""
+    from scipy.linalg import hadamard
+
+    H = hadamard(128) / np.sqrt(128.0)
+    rng = np.random.default_rng(91)
+    L, d = 40, 128
+    K = random_bf16_like(rng, (L, d), 1.0)
+    V = random_bf16_like(rng, (L, d), 1.0)
+    V[:, 3] *= 12.0  # an outlier channel, which the rotation spreads
+    q = random_bf16_like(rng, (d,), 1.0)
+    sc = 1.0 / np.sqrt(d)
+    for vb in (2, 4, 8):
+        prm = dict(_params(R=0, kb=4, vb=vb), value_rotation=True)
+        cache = O_.build_unit_cache(K, V, L, prm)
+        o = O_.unit_attention(q, cache, sc, False)
+        a = O_.softmax(cache["k_hat"] @ q * sc)
+        assert np.max(np.abs(o - H @ (a @ cache["v_hat"]))) < 1e-12
+        o_raw = a @ V.astype(np.float64)
+        bound = np.sqrt(128.0) * np.max(cache["v_scale"].astype(np.float64)) / 2
+        assert np.linalg.norm(o - o_raw) <= bound * (1 + 1e-12)
+        # the rotated values really are what was quantized: codes of H v, not of v
+        c, _, _ = O_.quantize(V.astype(np.float64) @ H, vb, 128)
+        assert np.array_equal(cache["v_codes"], c)
+
+
 def check_memory_model(O_):
     expect = {(4, 2): 116, (4, 4): 148, (2, 4): 116, (2, 2): 84, (1, 2): 68}
     for (kb, vb), b in expect.items():
@@ -376,7 +406,7 @@ def check_outlier(O_):
 ALL_CHECKS = [
     check_fp16_directed, check_golden, check_wht, check_attention_library, check_attention_decimal,
     check_end_to_end_exact, check_error_identities, check_window, check_gqa, check_rotation_special_case,
-    check_memory_model, check_group_size_monotone, check_outlier,
+    check_memory_model, check_group_size_monotone, check_outlier, check_value_rotation,
 ]
 
 
@@ -444,3 +474,7 @@ def test_group_size_monotone():
 
 def test_outlier_widens_scale():
     check_outlier(O)
+
+
+def test_value_rotation_variant():
+    check_value_rotation(O)
