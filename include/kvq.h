@@ -82,7 +82,7 @@ typedef enum { KVQ_ROT_NONE = 0, KVQ_ROT_WHT = 1 } kvq_rotation;
 
 /* Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
  * k_bits, v_bits in {1, 2, 4, 8}; k_group in {32, 64, 128}; v_group in {64, 128};
- * window >= 0; block_size in {0, 16}. */
+ * window >= 0; block_size in {0, 16}; value_rotation only with window == 0. */
 typedef struct {
   int32_t head_dim;
   int32_t num_q_heads;
@@ -93,6 +93,9 @@ typedef struct {
   int32_t key_rotation; /* kvq_rotation                                           */
   int32_t kv_dtype;     /* kvq_dtype of appended K/V and of the window buffers    */
   int32_t block_size;   /* 0 = contiguous, 16 = paged                             */
+  int32_t value_rotation; /* kvq_rotation of the values (a variant of [P3] "Resultaten"):
+                           * values are rotated before they are quantized and the
+                           * attention output is rotated back by the merge            */
 } kvq_params;
 
 typedef struct {

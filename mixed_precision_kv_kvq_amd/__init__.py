@@ -51,6 +51,7 @@ class kvq_params(ctypes.Structure):
         ("key_rotation", c_int32),
         ("kv_dtype", c_int32),
         ("block_size", c_int32),
+        ("value_rotation", c_int32),
     ]
 
 
@@ -227,9 +228,9 @@ def kvq_dequantize_debug(params, cache, seq_lens, seq, t0, n, k_codes=None, v_co
 # Plumbing: device buffers for one cache, allocated with torch.
 # --------------------------------------------------------------------------
 def make_params(head_dim=128, num_q_heads=32, num_kv_heads=8, k_bits=4, k_group=32, v_bits=2, v_group=128, window=0,
-                key_rotation=0, kv_dtype=KVQ_BF16, block_size=0) -> kvq_params:
+                key_rotation=0, kv_dtype=KVQ_BF16, block_size=0, value_rotation=0) -> kvq_params:
     return kvq_params(head_dim, num_q_heads, num_kv_heads, k_bits, k_group, v_bits, v_group, window, key_rotation,
-                      kv_dtype, block_size)
+                      kv_dtype, block_size, value_rotation)
 
 
 class CacheBuffers:

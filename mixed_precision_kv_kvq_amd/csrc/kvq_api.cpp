@@ -16,6 +16,7 @@ kvq_status check_params(const kvq_params *p) {
   if (!p) return KVQ_EINVAL;
   if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads) return KVQ_EINVAL;
   if (p->window < 0 || p->key_rotation < 0 || p->key_rotation > 1) return KVQ_EINVAL;
+  if (p->value_rotation < 0 || p->value_rotation > 1) return KVQ_EINVAL;
   if (p->kv_dtype != KVQ_F32 && p->kv_dtype != KVQ_BF16) return KVQ_EINVAL;
   if (p->head_dim != KVQ_D) return KVQ_EUNSUPPORTED;
   const int g = p->num_q_heads / p->num_kv_heads;
@@ -24,6 +25,8 @@ kvq_status check_params(const kvq_params *p) {
   if (p->k_group != 32 && p->k_group != 64 && p->k_group != 128) return KVQ_EUNSUPPORTED;
   if (p->v_group != 64 && p->v_group != 128) return KVQ_EUNSUPPORTED;
   if (p->block_size != 0 && p->block_size != KVQ_PAGE) return KVQ_EUNSUPPORTED;
+  // rotated values cannot share one accumulator with the window's unrotated ones
+  if (p->value_rotation && p->window > 0) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -167,6 +170,7 @@ kvq_status kvq_quantize_append(const kvq_params *params, const kvq_cache *cache,
   a.Hkv = params->num_kv_heads;
   a.R = params->window;
   a.rotation = params->key_rotation;
+  a.value_rotation = params->value_rotation;
   a.kv_f32 = params->kv_dtype == KVQ_F32;
   return hip_status(kvq_launch_append(a, stream));
 }
@@ -249,6 +253,7 @@ kvq_status kvq_decode_combine(const kvq_params *params, int32_t batch, int64_t m
   c.B = batch;
   c.Hq = params->num_q_heads;
   c.splits = split_plan(params, batch, max_seq_len, q_parts).splits;
+  c.value_rotation = params->value_rotation;
   return hip_status(kvq_launch_combine(c, stream));
 }
 

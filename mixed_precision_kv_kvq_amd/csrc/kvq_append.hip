@@ -221,6 +221,7 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
   if (t_q < 0) return;
 
   if (a.rotation) wht128_fp64(k0, k1, lane);
+  if (a.value_rotation) wht128_fp64(v0, v1, lane);
   uint32_t a0, a1, am, b0, b1, bm;
   quantize_pair(k0, k1, lay.kb, lay.kg, &a0, &a1, &am);
   quantize_pair(v0, v1, lay.vb, lay.vg, &b0, &b1, &bm);
@@ -288,8 +289,9 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
 // record is assembled in LDS (codes OR-ed into their words) and written with 16-byte stores.
 // Same quantizer arithmetic as the per-token kernel (group_meta / group_code), so the codes
 // and metadata are identical.
-// ROT: keys are rotated first; the lane's values are then fp64 (the transform's results).
-// Without rotation they are the inputs themselves, exact in fp32, which halves the registers.
+// ROT: keys and/or values (a.rotation, a.value_rotation) are rotated first; the lane's values
+// are then fp64 (the transform's results).  Without rotation they are the inputs themselves,
+// exact in fp32, which halves the registers.
 template <bool ROT>
 __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   constexpr int kMaxRecordWords = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 4;
@@ -341,11 +343,10 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
       }
     }
   };
-  // ---- keys ----
-  load32(a.k_new + in_off);
-  if constexpr (ROT) {
-    // 128-point butterflies in stage order 1, 2, ..., 64: stages up to 16 inside the lane,
-    // 32 and 64 across lanes q ^ 1 and q ^ 2 (same operands and order as the definition).
+  // Normalized 128-point Walsh-Hadamard transform of the row: butterflies in stage order
+  // 1, 2, ..., 64, stages up to 16 inside the lane, 32 and 64 across lanes q ^ 1 and q ^ 2
+  // (same operands and order as the definition).
+  auto rotate = [&]() {
 #pragma unroll
     for (int hs = 1; hs < 32; hs <<= 1) {
 #pragma unroll
@@ -369,6 +370,11 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = x[e] * KVQ_WHT_C;
+  };
+  // ---- keys ----
+  load32(a.k_new + in_off);
+  if constexpr (ROT) {
+    if (a.rotation) rotate();
   }
   {
     Val mnv = x[0], mxv = x[0];
@@ -411,6 +417,9 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   }
   // ---- values ----
   load32(a.v_new + in_off);
+  if constexpr (ROT) {
+    if (a.value_rotation) rotate();
+  }
   {
     Val mnv = x[0], mxv = x[0];
 #pragma unroll
@@ -463,7 +472,7 @@ hipError_t kvq_launch_append(const KvqAppendArgs &a, hipStream_t s) {
   if (direct >= KVQ_PAGE) {
     const unsigned pages = (unsigned)(direct / KVQ_PAGE);
     const dim3 grid(pages, (unsigned)a.Hkv, (unsigned)a.cache.batch);
-    if (a.rotation)
+    if (a.rotation || a.value_rotation)
       hipLaunchKernelGGL(kvq_append_pages_kernel<true>, grid, dim3(64), 0, s, a);
     else
       hipLaunchKernelGGL(kvq_append_pages_kernel<false>, grid, dim3(64), 0, s, a);

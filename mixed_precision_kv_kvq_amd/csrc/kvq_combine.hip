@@ -74,6 +74,22 @@ __global__ __launch_bounds__(64) void kvq_combine_kernel(KvqCombineArgs a) {
     o0 = o0 / l;
     o1 = o1 / l;
   }
+  if (a.value_rotation) {
+    // Normalized 128-point Walsh-Hadamard transform of the row (it is its own inverse);
+    // lane holds channels 2*lane and 2*lane+1, so channel distance h >= 2 is lane distance h/2.
+    const float x = o0, y = o1;
+    o0 = x + y;
+    o1 = x - y;
+    for (int h = 2; h < KVQ_D; h <<= 1) {
+      const int pl = h >> 1;
+      const float p0 = __shfl_xor(o0, pl), p1 = __shfl_xor(o1, pl);
+      const bool upper = (lane & pl) != 0;
+      o0 = upper ? p0 - o0 : o0 + p0;
+      o1 = upper ? p1 - o1 : o1 + p1;
+    }
+    o0 *= (float)KVQ_WHT_C;
+    o1 *= (float)KVQ_WHT_C;
+  }
   if (a.out_f32) {
     reinterpret_cast<float2 *>(a.out)[bh * 64 + lane] = make_float2(o0, o1);
   } else {

@@ -28,6 +28,7 @@ struct KvqAppendArgs {
   const int32_t *n_new_per_seq;
   const uint8_t *k_new, *v_new;
   int32_t n_new, Hkv, R, rotation, kv_f32;
+  int32_t value_rotation;
 };
 
 struct KvqAttnArgs {
@@ -49,6 +50,7 @@ struct KvqCombineArgs {
   const float *partials;
   void *out;
   int32_t out_f32, B, Hq, splits;
+  int32_t value_rotation;  // the partials are over rotated values: rotate the merged row back
 };
 struct KvqDebugArgs {
   KvqLayout lay;

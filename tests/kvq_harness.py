@@ -18,12 +18,12 @@ REL_L2_TOL = 1e-3
 def params_of(wl: W.Workload) -> K.kvq_params:
     return K.make_params(wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.k_bits, wl.k_group, wl.v_bits, wl.v_group,
                          wl.window, int(wl.rotation), K.KVQ_F32 if wl.kv_dtype == "f32" else K.KVQ_BF16,
-                         wl.block_size)
+                         wl.block_size, int(wl.value_rotation))
 
 
 def oracle_params(wl: W.Workload) -> dict:
     return dict(k_bits=wl.k_bits, k_group=wl.k_group, v_bits=wl.v_bits, v_group=wl.v_group, window=wl.window,
-                rotation=wl.rotation)
+                rotation=wl.rotation, value_rotation=wl.value_rotation)
 
 
 def to_device_kv(x: np.ndarray, kv_dtype: str) -> torch.Tensor:

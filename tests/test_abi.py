@@ -127,6 +127,12 @@ def test_attention_validation():
     assert call(c=cache(block_table=FAKE, max_blocks_per_seq=3), prm_=p(block_size=16), mx=49,
                 wsb=K.kvq_decode_workspace_bytes(p(block_size=16), 2, 49)) == K.KVQ_ENOSPACE
     assert K.kvq_decode_workspace_bytes(p(k_bits=3), 2, 64) == 0
+    # value rotation: a flag, and not with a recent window (the window's values are not rotated)
+    assert call(prm_=p(value_rotation=2)) == K.KVQ_EINVAL
+    assert K.kvq_decode_workspace_bytes(p(value_rotation=1), 2, 64) > 0
+    assert K.kvq_decode_workspace_bytes(p(value_rotation=1, window=8), 2, 64) == 0
+    assert L.kvq_quantize_append(ctypes.byref(p(value_rotation=1, window=8)), ctypes.byref(cache()), FAKE, None,
+                                 FAKE, FAKE, 1, None) == K.KVQ_EUNSUPPORTED
 
 
 def test_phase_entry_points_validation():

@@ -176,7 +176,29 @@ def test_folded_window(name, monkeypatch):
     wl = small(BASE, config=400 + list(FOLD).index(name), **FOLD[name])
     say(f"folded window {name}: {FOLD[name]}")
     run = GpuRun(wl, chunk=64)
-    for s in range(wl.steps):
+    for s in range(max(wl.steps, 1)):  # steps == 0: one attention over the context
+        full_check(run, s, out_check_bf16=(s == 0))
+
+
+# Values rotated before quantization and the output rotated back in the merge: whole pages go
+# through the page kernel, the rest through the per-token kernel.
+VROT = {
+    "values-only": dict(context=300, value_rotation=True),
+    "keys-and-values": dict(context=250, rotation=True, value_rotation=True),
+    "keys-and-values-g8": dict(context=200, num_q_heads=16, num_kv_heads=2, rotation=True, value_rotation=True),
+    "values-g8-vgroup64": dict(context=170, num_q_heads=16, num_kv_heads=2, v_group=64, value_rotation=True),
+    "values-f32": dict(context=160, kv_dtype="f32", q_dtype="f32", value_rotation=True),
+    "values-paged": dict(context=0, var_len=(1, 300), block_size=16, batch=4, value_rotation=True),
+    "values-steps": dict(batch=2, context=700, steps=3, rotation=True, value_rotation=True),
+}
+
+
+@pytest.mark.parametrize("name", list(VROT))
+def test_value_rotation(name):
+    wl = small(BASE, config=500 + list(VROT).index(name), **VROT[name])
+    say(f"value rotation {name}: {VROT[name]}")
+    run = GpuRun(wl, chunk=64)
+    for s in range(max(wl.steps, 1)):
         full_check(run, s, out_check_bf16=(s == 0))
 
 

@@ -129,6 +129,7 @@ class Workload:
     key_lognormal_sigma: float  # 0 = unit channel std
     var_len: Optional[tuple] = None  # (lo, hi) inclusive uniform context lengths
     seed: int = 0
+    value_rotation: bool = False  # the same rotation applied to the values (no recent window)
 
     @property
     def group_q(self) -> int:
