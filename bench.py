@@ -187,6 +187,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the timed steps")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the unfused baseline (dequantize to a dense bf16 cache, then dense attention)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
@@ -332,6 +334,66 @@ def main():
     timed[-1][2]()  # restore the last step's output from the workspace
     torch.cuda.synchronize()
 
+    # ---- unfused baseline at the last step's state: the fused attention (split kernel + merge)
+    # against dequantize-to-dense-bf16 + dense attention over the same cache and query.
+    unfused = None
+    if not args.no_unfused:
+        L_last = L0 + args.warmup + args.steps
+        lens_last = lens[args.warmup + args.steps]
+        q_last = q_steps[args.warmup + args.steps - 1]
+        kd = torch.empty((B, Hkv, L_last, d), dtype=torch.int16, device=dev)
+        vd = torch.empty_like(kd)
+        dws = K.kvq_dense_workspace_bytes(params, B, L_last)
+        dw = torch.empty(dws, dtype=torch.uint8, device=dev)
+        out_u = torch.empty_like(out)
+        deq = K.bound_call("kvq_dequantize_dense", params, cache.struct, lens_last, L_last, kd, vd, stream=stream)
+        dense = K.bound_call("kvq_dense_decode_attention", params, B, kd, vd, lens_last, L_last, q_last, K.KVQ_BF16,
+                             out_u, K.KVQ_F32, 0.0, dw, dws, stream=stream)
+        fused = (timed[-1][1], timed[-1][2])
+
+        def time_calls(calls, n=5):
+            for f in calls:  # warm
+                f()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            e[0].record(stream)
+            for _ in range(n):
+                for f in calls:
+                    f()
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            return e[0].elapsed_time(e[1]) * 1e3 / n
+
+        fused_us = time_calls(fused)
+        deq_us = time_calls([deq])
+        dense_us = time_calls([dense])
+        both_us = time_calls([deq, dense])
+        timed[-1][2]()
+        torch.cuda.synchronize()
+        diff = float((out_u - out).abs().max())
+        units = B * Hkv
+        nq_last = max(L_last - R, 0)
+        per_th_q = (d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4)
+        deq_bytes = units * (nq_last * per_th_q + (L_last - nq_last) * 2 * d * 2 + L_last * 2 * d * 2)
+        dense_bytes = units * L_last * 2 * d * 2
+        unfused = {
+            "what": "dequantize the whole cache to dense bf16 K/V (kvq_dequantize_dense), then dense decode "
+                    "attention over it (kvq_dense_decode_attention, splits of 256 positions + the same merge); "
+                    "fused = kvq_decode_partials + kvq_decode_combine; last step's state, 5 back-to-back "
+                    "repetitions between two events each",
+            "length": L_last,
+            "fused_attention_us": round(fused_us, 2),
+            "unfused_us": round(both_us, 2),
+            "dequantize_us": round(deq_us, 2), "dequantize_bytes": int(deq_bytes),
+            "dequantize_GBs": round(deq_bytes / (deq_us * 1e-6) / 1e9, 1),
+            "dense_attention_us": round(dense_us, 2), "dense_attention_bytes": int(dense_bytes),
+            "dense_attention_GBs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+            "fusion_speedup": round(both_us / fused_us, 2),
+            "max_abs_output_difference": diff,
+        }
+        del kd, vd, dw
+        torch.cuda.synchronize()
+
     per_th = (d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4)
     launch_bytes = split_kernel_bytes(wl, L0 + args.warmup + args.steps, per_th, 2)  # the timed launch
     achieved = float(launch_bytes / (split_us * 1e-6) / 1e9)
@@ -382,6 +444,8 @@ def main():
             "frac_of_peak": round(prefill_bytes / (prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "tokens_per_s": round(B * L0 / (prefill_us * 1e-6), 1)},
     }
+    if unfused is not None:
+        res["unfused_baseline"] = unfused
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -197,6 +197,35 @@ kvq_status kvq_dequantize_debug(const kvq_params *params, const kvq_cache *cache
                                 uint16_t *k_meta, uint16_t *v_meta, float *k_hat, float *v_hat,
                                 hipStream_t stream);
 
+/* Unfused baseline ([P1] "Pertumbuhan cache mengubah trade pada serving": dequantizing into
+ * temporary storage instead of inside the attention kernel).  It exists to measure what the
+ * fused path gains; the fused entry points above do not use it.
+ *
+ * kvq_dequantize_dense writes positions t < min(seq_lens[b], max_seq_len) of every sequence b
+ * and kv head h into dense bf16 arrays k_out, v_out, each [batch][num_kv_heads][max_seq_len][128]
+ * (device, caller-owned, 16-byte aligned, max_seq_len <= 2^31 - 1): a quantized position as
+ * round-to-nearest-even of zero + code * scale evaluated exactly in fp64, rotated back to the
+ * original domain first when its tensor is rotated (the transform is its own inverse); a window
+ * position as its stored value (fp32 rounded to nearest even).  Positions t >= seq_lens[b] are not
+ * written; positions beyond the cache capacity are written as zeros.  Errors as for
+ * kvq_dequantize_debug.
+ *
+ * kvq_dense_decode_attention computes, for every sequence b and query head h, the softmax
+ * attention of q[b][h] over positions t < min(seq_lens[b], max_seq_len) of dense bf16 k, v laid
+ * out as above (query head h reads kv head h / (num_q_heads / num_kv_heads); all-zero output for
+ * an empty sequence), in fp32 with splits of 256 positions merged as in kvq_decode_combine.
+ * Only num_q_heads / num_kv_heads of params are used (params must still be valid).  q, out,
+ * softmax_scale as for kvq_decode_attention; workspace (device, 16-byte aligned) of at least
+ * kvq_dense_workspace_bytes(params, batch, max_seq_len) bytes.  Errors: KVQ_EINVAL for null or
+ * misaligned pointers or bad dtypes or scale, KVQ_ENOSPACE for a short workspace. */
+kvq_status kvq_dequantize_dense(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                                int64_t max_seq_len, uint16_t *k_out, uint16_t *v_out, hipStream_t stream);
+size_t kvq_dense_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len);
+kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, const uint16_t *k, const uint16_t *v,
+                                      const int32_t *seq_lens, int64_t max_seq_len, const void *q, int32_t q_dtype,
+                                      void *out, int32_t out_dtype, float softmax_scale, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *kvq_status_str(kvq_status status);
 

@@ -34,6 +34,9 @@ EXPORTED = [
     "kvq_decode_partials",
     "kvq_decode_combine",
     "kvq_dequantize_debug",
+    "kvq_dequantize_dense",
+    "kvq_dense_workspace_bytes",
+    "kvq_dense_decode_attention",
     "kvq_status_str",
 ]
 
@@ -106,6 +109,15 @@ def _load():
     lib.kvq_dequantize_debug.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int32, c_int64, c_int64, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.kvq_dequantize_debug.restype = c_int32
+    lib.kvq_dequantize_dense.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_void_p,
+                                         c_void_p]
+    lib.kvq_dequantize_dense.restype = c_int32
+    lib.kvq_dense_workspace_bytes.argtypes = [P(kvq_params), c_int32, c_int64]
+    lib.kvq_dense_workspace_bytes.restype = c_size_t
+    lib.kvq_dense_decode_attention.argtypes = [P(kvq_params), c_int32, c_void_p, c_void_p, c_void_p, c_int64,
+                                               c_void_p, c_int32, c_void_p, c_int32, c_float, c_void_p, c_size_t,
+                                               c_void_p]
+    lib.kvq_dense_decode_attention.restype = c_int32
     lib.kvq_status_str.argtypes = [c_int32]
     lib.kvq_status_str.restype = ctypes.c_char_p
     return lib
@@ -148,7 +160,8 @@ def bound_call(name: str, *args, stream=None):
     fn = getattr(_lib, name)
     conv = [ctypes.byref(a) if isinstance(a, ctypes.Structure) else _ptr(a) if hasattr(a, "data_ptr") else a
             for a in args]
-    if name in ("kvq_quantize_append", "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine"):
+    if name in ("kvq_quantize_append", "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine",
+                "kvq_dequantize_dense", "kvq_dense_decode_attention"):
         conv.append(_stream(stream))
     conv = tuple(conv)
 
@@ -221,6 +234,28 @@ def kvq_dequantize_debug(params, cache, seq_lens, seq, t0, n, k_codes=None, v_co
                                    _ptr(v_hat), _stream(stream))
     if check:
         _check(st, "kvq_dequantize_debug")
+    return st
+
+
+def kvq_dequantize_dense(params, cache, seq_lens, max_seq_len, k_out, v_out, stream=None, check=True):
+    st = _lib.kvq_dequantize_dense(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens), int(max_seq_len),
+                                   _ptr(k_out), _ptr(v_out), _stream(stream))
+    if check:
+        _check(st, "kvq_dequantize_dense")
+    return st
+
+
+def kvq_dense_workspace_bytes(params, batch: int, max_seq_len: int) -> int:
+    return int(_lib.kvq_dense_workspace_bytes(ctypes.byref(params), int(batch), int(max_seq_len)))
+
+
+def kvq_dense_decode_attention(params, batch, k, v, seq_lens, max_seq_len, q, q_dtype, out, out_dtype, softmax_scale,
+                               workspace, workspace_bytes, stream=None, check=True):
+    st = _lib.kvq_dense_decode_attention(ctypes.byref(params), int(batch), _ptr(k), _ptr(v), _ptr(seq_lens),
+                                         int(max_seq_len), _ptr(q), int(q_dtype), _ptr(out), int(out_dtype),
+                                         float(softmax_scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "kvq_dense_decode_attention")
     return st
 
 

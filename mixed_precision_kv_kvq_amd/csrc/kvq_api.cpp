@@ -297,6 +297,77 @@ kvq_status kvq_dequantize_debug(const kvq_params *params, const kvq_cache *cache
   return hip_status(kvq_launch_debug(a, stream));
 }
 
+static int dense_splits(int64_t max_seq_len) {
+  const int64_t s = (max_seq_len + KVQ_DENSE_SPLIT - 1) / KVQ_DENSE_SPLIT;
+  return s < 1 ? 1 : (int)s;
+}
+
+kvq_status kvq_dequantize_dense(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                                int64_t max_seq_len, uint16_t *k_out, uint16_t *v_out, hipStream_t stream) {
+  if (kvq_status st = check_params(params)) return st;
+  if (kvq_status st = check_cache(params, cache)) return st;
+  if (!seq_lens || max_seq_len < 0 || max_seq_len > INT32_MAX) return KVQ_EINVAL;
+  if (!k_out || !v_out || !aligned16(k_out) || !aligned16(v_out)) return KVQ_EINVAL;
+  KvqDenseArgs a = {};
+  a.lay = layout_of(params);
+  a.cache = dev_cache(params, cache);
+  a.seq_lens = seq_lens;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.max_len = max_seq_len;
+  a.B = cache->batch;
+  a.Hkv = params->num_kv_heads;
+  a.R = params->window;
+  a.kv_f32 = params->kv_dtype == KVQ_F32;
+  a.rotation = params->key_rotation;
+  a.value_rotation = params->value_rotation;
+  return hip_status(kvq_launch_dequantize_dense(a, stream));
+}
+
+size_t kvq_dense_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len) {
+  if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0 || max_seq_len > INT32_MAX) return 0;
+  return (size_t)batch * params->num_q_heads * (size_t)dense_splits(max_seq_len) * KVQ_PART_STRIDE * sizeof(float);
+}
+
+kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, const uint16_t *k, const uint16_t *v,
+                                      const int32_t *seq_lens, int64_t max_seq_len, const void *q, int32_t q_dtype,
+                                      void *out, int32_t out_dtype, float softmax_scale, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  if (kvq_status st = check_params(params)) return st;
+  if (batch <= 0 || !seq_lens || max_seq_len < 0 || max_seq_len > INT32_MAX) return KVQ_EINVAL;
+  if (!k || !v || !q || !out || !workspace) return KVQ_EINVAL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EINVAL;
+  if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
+    return KVQ_EINVAL;
+  if (!(softmax_scale >= 0.f) || isinf(softmax_scale)) return KVQ_EINVAL;
+  if (workspace_bytes < kvq_dense_workspace_bytes(params, batch, max_seq_len)) return KVQ_ENOSPACE;
+  KvqDenseArgs a = {};
+  a.seq_lens = seq_lens;
+  a.k_in = k;
+  a.v_in = v;
+  a.q = q;
+  a.partials = (float *)workspace;
+  a.max_len = max_seq_len;
+  a.B = batch;
+  a.Hq = params->num_q_heads;
+  a.Hkv = params->num_kv_heads;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.splits = dense_splits(max_seq_len);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
+  a.sigma = (float)((double)scale * 1.4426950408889634);  // * log2(e)
+  if (hipError_t e = kvq_launch_dense_partials(a, params->num_q_heads / params->num_kv_heads, stream))
+    return hip_status(e);
+  KvqCombineArgs c = {};
+  c.partials = a.partials;
+  c.out = out;
+  c.out_f32 = out_dtype == KVQ_F32;
+  c.B = batch;
+  c.Hq = a.Hq;
+  c.splits = a.splits;
+  c.value_rotation = 0;  // the dense cache is in the original domain
+  return hip_status(kvq_launch_combine(c, stream));
+}
+
 const char *kvq_status_str(kvq_status status) {
   switch (status) {
     case KVQ_OK: return "ok";

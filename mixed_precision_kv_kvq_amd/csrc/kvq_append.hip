@@ -104,27 +104,6 @@ __device__ inline void quantize_pair(double x0, double x1, int bits, int G, uint
   *meta = g.sb | (g.zb << 16);
 }
 
-// Normalized 128-point Walsh-Hadamard transform of the values held two per lane.
-__device__ inline void wht128_fp64(double &x0, double &x1, int lane) {
-  {
-    const double a = x0, b = x1;
-    x0 = a + b;
-    x1 = a - b;
-  }
-  for (int h = 2; h < 128; h <<= 1) {
-    const int pl = h >> 1;
-    const double p0 = __shfl_xor(x0, pl), p1 = __shfl_xor(x1, pl);
-    if ((lane & pl) == 0) {
-      x0 = x0 + p0;
-      x1 = x1 + p1;
-    } else {
-      x0 = p0 - x0;
-      x1 = p1 - x1;
-    }
-  }
-  x0 = x0 * KVQ_WHT_C;
-  x1 = x1 * KVQ_WHT_C;
-}
 
 // Tokens quantized on arrival (an append of n > R tokens to a length-L sequence: input tokens
 // j < m = n - R go to positions L + j) are split between the two kernels: whole 16-token pages
@@ -220,8 +199,8 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
   }
   if (t_q < 0) return;
 
-  if (a.rotation) wht128_fp64(k0, k1, lane);
-  if (a.value_rotation) wht128_fp64(v0, v1, lane);
+  if (a.rotation) kvq_wht128_fp64(k0, k1, lane);
+  if (a.value_rotation) kvq_wht128_fp64(v0, v1, lane);
   uint32_t a0, a1, am, b0, b1, bm;
   quantize_pair(k0, k1, lay.kb, lay.kg, &a0, &a1, &am);
   quantize_pair(v0, v1, lay.vb, lay.vg, &b0, &b1, &bm);

@@ -11,6 +11,31 @@
 // 2^-3.5 rounded to fp64 (the normalization of the 128-point Hadamard transform).
 #define KVQ_WHT_C 0x1.6a09e667f3bcdp-4
 
+// Normalized 128-point Walsh-Hadamard transform of a row held two channels per lane (lane l:
+// channels 2l, 2l + 1) in fp64: butterflies in stage order 1, 2, ..., 64, then the multiply
+// by KVQ_WHT_C.  The matrix is symmetric and orthogonal, so the transform is its own inverse.
+__device__ inline void kvq_wht128_fp64(double &x0, double &x1, int lane) {
+#pragma clang fp contract(off)
+  {
+    const double a = x0, b = x1;
+    x0 = a + b;
+    x1 = a - b;
+  }
+  for (int h = 2; h < 128; h <<= 1) {
+    const int pl = h >> 1;
+    const double p0 = __shfl_xor(x0, pl), p1 = __shfl_xor(x1, pl);
+    if ((lane & pl) == 0) {
+      x0 = x0 + p0;
+      x1 = x1 + p1;
+    } else {
+      x0 = p0 - x0;
+      x1 = p1 - x1;
+    }
+  }
+  x0 = x0 * KVQ_WHT_C;
+  x1 = x1 * KVQ_WHT_C;
+}
+
 struct KvqCacheDev {
   uint8_t *pages;
   uint8_t *k_win, *v_win;
@@ -134,4 +159,21 @@ hipError_t kvq_launch_append(const KvqAppendArgs &a, hipStream_t s);
 hipError_t kvq_launch_attention(const KvqAttnArgs &a, int g, int q_parts, hipStream_t s);
 hipError_t kvq_launch_combine(const KvqCombineArgs &a, hipStream_t s);
 hipError_t kvq_launch_debug(const KvqDebugArgs &a, hipStream_t s);
+
+// Unfused baseline: dense bf16 cache [B][Hkv][max_len][128] and dense decode attention over it.
+struct KvqDenseArgs {
+  KvqLayout lay;
+  KvqCacheDev cache;
+  const int32_t *seq_lens;
+  uint16_t *k_out, *v_out;           // dequantize: written
+  const uint16_t *k_in, *v_in;       // attention: read
+  const void *q;
+  float *partials;                   // [B][Hq][S][KVQ_PART_STRIDE]
+  int64_t max_len;
+  int32_t B, Hq, Hkv, R, kv_f32, q_f32, rotation, value_rotation, splits;
+  float sigma;                       // softmax scale * log2(e)
+};
+#define KVQ_DENSE_SPLIT 256  // tokens per split of the dense attention
+hipError_t kvq_launch_dequantize_dense(const KvqDenseArgs &a, hipStream_t s);
+hipError_t kvq_launch_dense_partials(const KvqDenseArgs &a, int g, hipStream_t s);
 bool kvq_attention_supported(int kb, int vb, int g, int q_parts, int nvg);

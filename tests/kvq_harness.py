@@ -243,5 +243,17 @@ def assert_close(o_gpu, o_ref, what=""):
     return maxabs, rel
 
 
+def bf16_bits_rne_f64(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of round-to-nearest-even of fp64 values (normal bf16 range, or zero).
+
+    x = m 2^e with 1/2 <= |m| < 1; m 2^8 is exact in fp64 and numpy rounds it half to even,
+    so the 8 significant bits are the correctly rounded ones; the result is bf16-exact, so the
+    fp32 cast and the bit extraction below are exact.
+    """
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    y = np.ldexp(np.round(m * 256.0), e - 8)
+    return W.f32_to_bf16_bits(y.astype(np.float32))
+
+
 def small(wl: W.Workload, **kw) -> W.Workload:
     return dataclasses.replace(wl, **kw)

@@ -70,6 +70,8 @@ def test_window_and_paged_sizes():
     (dict(kv_dtype=7), K.KVQ_EINVAL),
     (dict(block_size=32), K.KVQ_EUNSUPPORTED),
     (dict(key_rotation=2), K.KVQ_EINVAL),
+    (dict(value_rotation=-1), K.KVQ_EINVAL),
+    (dict(value_rotation=1, window=4), K.KVQ_EUNSUPPORTED),
 ])
 def test_bad_params_rejected(kw, status):
     out = K.kvq_sizes()
@@ -169,6 +171,40 @@ def test_debug_validation():
     assert L.kvq_dequantize_debug(ctypes.byref(prm), ctypes.byref(cache()), FAKE, 0, -1, 1, *args, None) == K.KVQ_EINVAL
     assert L.kvq_dequantize_debug(ctypes.byref(prm), ctypes.byref(cache()), None, 0, 0, 1, *args, None) == K.KVQ_EINVAL
     assert L.kvq_dequantize_debug(ctypes.byref(prm), ctypes.byref(cache()), FAKE, 0, 0, 0, *args, None) == K.KVQ_OK
+
+
+def test_unfused_baseline_validation():
+    prm = p()
+    L = K.lib()
+
+    def deq(c=None, seq=FAKE, mx=64, ko=FAKE, vo=FAKE, prm_=prm):
+        return L.kvq_dequantize_dense(ctypes.byref(prm_), ctypes.byref(c or cache()), seq, mx, ko, vo, None)
+
+    assert deq(seq=None) == K.KVQ_EINVAL
+    assert deq(ko=None) == K.KVQ_EINVAL
+    assert deq(vo=FAKE + 2) == K.KVQ_EINVAL
+    assert deq(mx=-1) == K.KVQ_EINVAL
+    assert deq(mx=1 << 31) == K.KVQ_EINVAL
+    assert deq(c=cache(pages=FAKE + 8)) == K.KVQ_EINVAL
+    assert deq(prm_=p(k_bits=3)) == K.KVQ_EUNSUPPORTED
+
+    need = K.kvq_dense_workspace_bytes(prm, 2, 600)
+    assert need == 2 * 32 * 3 * K.KVQ_PART_FLOATS * 4  # three splits of 256 positions
+    assert K.kvq_dense_workspace_bytes(prm, 2, 0) == 2 * 32 * 1 * K.KVQ_PART_FLOATS * 4
+    assert K.kvq_dense_workspace_bytes(p(k_bits=3), 2, 600) == 0
+
+    def att(b=2, k=FAKE, v=FAKE, seq=FAKE, mx=600, q=FAKE, qd=K.KVQ_BF16, out=FAKE, od=K.KVQ_F32, sc=0.0, ws=FAKE,
+            wsb=need):
+        return L.kvq_dense_decode_attention(ctypes.byref(prm), b, k, v, seq, mx, q, qd, out, od, sc, ws, wsb, None)
+
+    assert att(wsb=need - 1) == K.KVQ_ENOSPACE
+    assert att(b=0) == K.KVQ_EINVAL
+    assert att(k=None) == K.KVQ_EINVAL
+    assert att(v=FAKE + 4) == K.KVQ_EINVAL
+    assert att(qd=3) == K.KVQ_EINVAL
+    assert att(od=9) == K.KVQ_EINVAL
+    assert att(sc=float("inf")) == K.KVQ_EINVAL
+    assert att(seq=None) == K.KVQ_EINVAL
 
 
 def test_status_strings():

@@ -1,0 +1,101 @@
+"""GPU parity of the unfused baseline (dequantize to a dense bf16 cache, then dense decode
+attention), through the C ABI, against the CPU oracle.
+
+The dense cache is compared bit for bit with round-to-nearest-even (to bf16) of the oracle's
+dequantized values (rotated back to the original domain for rotated tensors) and of the stored
+window values; positions past each sequence's length must stay untouched.  The dense attention
+is compared, to the path's tolerance, with the oracle's exact attention over the same bf16
+values; bf16 outputs must equal round-to-nearest-even of the fp32 outputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import mixed_precision_kv_kvq_amd as K  # noqa: E402
+import oracle as O  # noqa: E402
+import workloads as W  # noqa: E402
+from kvq_harness import GpuRun, assert_close, bf16_bits_rne_f64, oracle_unit, small  # noqa: E402
+
+SENTINEL = -2  # int16 bit pattern 0xFFFE (a NaN in bf16): positions that must stay unwritten
+
+BASE = W.WORKLOADS[2]
+CASES = {
+    "three-splits": dict(context=700),
+    "window-ragged": dict(context=300, window=40),
+    "keys-and-values-rotated": dict(context=250, rotation=True, value_rotation=True),
+    "rotated-keys-window": dict(context=200, window=24, rotation=True),
+    "g8-vgroup64": dict(context=170, num_q_heads=16, num_kv_heads=2, v_group=64),
+    "g1-k8v8": dict(context=150, num_q_heads=8, num_kv_heads=8, k_bits=8, v_bits=8),
+    "g2-k1v1": dict(context=90, num_q_heads=16, num_kv_heads=8, k_bits=1, v_bits=1),
+    "f32-kv-window": dict(context=160, window=20, kv_dtype="f32", q_dtype="f32"),
+    "paged-window": dict(context=0, var_len=(1, 300), block_size=16, window=16, batch=4),
+    "ragged-lengths-with-empty": dict(context=0, var_len=(0, 1100), batch=5),
+}
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_unfused_matches_oracle(name):
+    wl = small(BASE, config=600 + list(CASES).index(name), **CASES[name])
+    say(f"unfused {name}: {CASES[name]}")
+    run = GpuRun(wl, chunk=64)
+    L = run.current_lengths()
+    B, Hkv, Hq, d, g = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.group_q
+    max_len = int(L.max()) + 5  # a few positions past every sequence
+    seq_lens = torch.from_numpy(L.astype(np.int32)).cuda()
+    kd = torch.full((B, Hkv, max_len, d), SENTINEL, dtype=torch.int16, device="cuda")
+    vd = torch.full_like(kd, SENTINEL)
+    K.kvq_dequantize_dense(run.params, run.cache.struct, seq_lens, max_len, kd, vd)
+    torch.cuda.synchronize()
+    kh = kd.cpu().numpy().view(np.uint16)
+    vh = vd.cpu().numpy().view(np.uint16)
+
+    q = run.q_host(0).astype(np.float64)
+    if wl.q_dtype != "f32":
+        q = W.bf16_bits_to_f32(W.f32_to_bf16_bits(q.astype(np.float32))).astype(np.float64)
+    scale = 1.0 / np.sqrt(d)
+    ref = np.zeros((B, Hq, d))
+    for b in range(B):
+        Lb = int(L[b])
+        assert np.all(kh[b, :, Lb:] == np.uint16(SENTINEL & 0xFFFF)), "keys written past the length"
+        assert np.all(vh[b, :, Lb:] == np.uint16(SENTINEL & 0xFFFF)), "values written past the length"
+        for kvh in range(Hkv):
+            if Lb == 0:
+                continue
+            cache, _, _ = oracle_unit(run, b, kvh)
+            k_hat = O.wht_rotate(cache["k_hat"]) if wl.rotation else cache["k_hat"]
+            v_hat = O.wht_rotate(cache["v_hat"]) if wl.value_rotation else cache["v_hat"]
+            k_exp = bf16_bits_rne_f64(np.concatenate([k_hat, cache["k_win"]]))
+            v_exp = bf16_bits_rne_f64(np.concatenate([v_hat, cache["v_win"]]))
+            assert np.array_equal(kh[b, kvh, :Lb], k_exp), f"dense keys differ (b {b}, kv head {kvh})"
+            assert np.array_equal(vh[b, kvh, :Lb], v_exp), f"dense values differ (b {b}, kv head {kvh})"
+            Kd = W.bf16_bits_to_f32(kh[b, kvh, :Lb]).astype(np.float64)
+            Vd = W.bf16_bits_to_f32(vh[b, kvh, :Lb]).astype(np.float64)
+            for h in range(kvh * g, (kvh + 1) * g):
+                ref[b, h] = O.attention(q[b, h], Kd, Vd, scale)
+
+    wsb = K.kvq_dense_workspace_bytes(run.params, B, max_len)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    q_dev = run._q_dev(0)
+    qd = K.KVQ_F32 if wl.q_dtype == "f32" else K.KVQ_BF16
+    o32 = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    ob = torch.empty((B, Hq, d), dtype=torch.int16, device="cuda")
+    K.kvq_dense_decode_attention(run.params, B, kd, vd, seq_lens, max_len, q_dev, qd, o32, K.KVQ_F32, 0.0, ws, wsb)
+    K.kvq_dense_decode_attention(run.params, B, kd, vd, seq_lens, max_len, q_dev, qd, ob, K.KVQ_BF16, 0.0, ws, wsb)
+    torch.cuda.synchronize()
+    got = o32.cpu().numpy()
+    assert_close(got, ref, f"unfused {name}")
+    rne = W.bf16_bits_to_f32(W.f32_to_bf16_bits(got))
+    assert np.array_equal(W.bf16_bits_to_f32(ob.cpu().numpy().view(np.uint16)), rne)

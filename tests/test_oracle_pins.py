@@ -478,3 +478,43 @@ def test_outlier_widens_scale():
 
 def test_value_rotation_variant():
     check_value_rotation(O)
+
+
+def test_bf16_rounding_helper_of_the_parity_tests():
+    """The fp64 -> bf16 round-to-nearest-even used to state expected dense values, against exact
+    rational rounding: random values, and exact ties between neighbours (which go to even)."""
+    from fractions import Fraction
+
+    import workloads as W
+    from kvq_harness import bf16_bits_rne_f64
+
+    def exact(x):
+        if x == 0:
+            return 0 if np.copysign(1.0, x) > 0 else 0x8000
+        fx = Fraction(x)
+        a = abs(fx)
+        e = 0
+        while a >= 2:
+            a /= 2
+            e += 1
+        while a < 1:
+            a *= 2
+            e -= 1
+        m = a * 128  # 8 significant bits: 128 <= m < 256
+        r = int(m)
+        frac = m - r
+        if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and r % 2 == 1):
+            r += 1
+        val = Fraction(r, 128) * Fraction(2) ** e * (1 if fx > 0 else -1)
+        return int(W.f32_to_bf16_bits(np.array([float(val)], dtype=np.float32))[0])
+
+    rng = np.random.default_rng(7)
+    xs = list(rng.standard_normal(300) * np.exp2(rng.integers(-30, 30, 300)))
+    # exact ties: a bf16 value plus half its unit in the last place, both parities
+    for m in (128, 129, 200, 255):
+        for e in (-20, 0, 13):
+            xs += [(m + 0.5) * 2.0 ** (e - 7), -(m + 0.5) * 2.0 ** (e - 7)]
+    xs += [0.0, 1.0, -3.0]
+    got = bf16_bits_rne_f64(np.array(xs))
+    want = np.array([exact(x) for x in xs], dtype=np.uint16)
+    assert np.array_equal(got, want)
