@@ -157,7 +157,7 @@ def cpu_baseline(wl, target_seconds=12.0, max_units=None):
             v_codes = np.concatenate([stored["v_codes"], vc])
             v_scale = np.concatenate([stored["v_scale"], vs])
             v_zero = np.concatenate([stored["v_zero"], vz])
-            cache = dict(k_hat=O.dequantize(k_codes, k_scale, k_zero, wl.k_group),
+            cache = dict(nq=nq, k_hat=O.dequantize(k_codes, k_scale, k_zero, wl.k_group),
                          v_hat=O.dequantize(v_codes, v_scale, v_zero, wl.v_group),
                          k_win=Kx[nq:L], v_win=Vx[nq:L])
             for h in range(kvh * g, (kvh + 1) * g):

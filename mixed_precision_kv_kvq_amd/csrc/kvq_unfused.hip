@@ -77,6 +77,67 @@ __global__ __launch_bounds__(64) void kvq_dequantize_dense_kernel(KvqDenseArgs a
   const size_t row0 = ((size_t)b * Hkv + h) * (size_t)a.max_len;
   const int esz = a.kv_f32 ? 4 : 2;
   const uint32_t kmask = (1u << lay.kb) - 1u, vmask = (1u << lay.vb) - 1u;
+  if (!a.rotation && !a.value_rotation) {
+    // Lane 16 r + c8 writes channels [8 c8, 8 c8 + 8) of position 4 it + r: one 16-byte store
+    // per tensor, four whole 256-byte rows per store instruction.
+    const int r = lane >> 4, c8 = lane & 15;
+#pragma unroll
+    for (int it = 0; it < KVQ_PAGE / 4; ++it) {
+      const int n = 4 * it + r;
+      const int64_t t = t_first + n;
+      if (t >= L) break;
+      uint32_t ko[4], vo[4];
+      if (t < nq) {
+        const uint32_t km = reinterpret_cast<const uint32_t *>(rs + lay.k_meta_off)[kvq_meta_dword(lay.nkg, n, (8 * c8) / lay.kg)];
+        const uint32_t vm = reinterpret_cast<const uint32_t *>(rs + lay.v_meta_off)[kvq_meta_dword(lay.nvg, n, (8 * c8) / lay.vg)];
+        const float kz = f16_bits_to_f32(km >> 16), ks = f16_bits_to_f32(km & 0xFFFF);
+        const float vz = f16_bits_to_f32(vm >> 16), vs = f16_bits_to_f32(vm & 0xFFFF);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t kc[2], vc[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int ch = 8 * c8 + 2 * i + e;
+            int off, bit;
+            kvq_k_code_pos(lay.kb, n, ch, &off, &bit);
+            kc[e] = (*reinterpret_cast<const uint32_t *>(rs + lay.k_codes_off + off) >> bit) & kmask;
+            kvq_v_code_pos(lay.vb, n, ch, &off, &bit);
+            vc[e] = (*reinterpret_cast<const uint32_t *>(rs + lay.v_codes_off + off) >> bit) & vmask;
+          }
+          ko[i] = affine_bf16(kz, ks, kc[0]) | (affine_bf16(kz, ks, kc[1]) << 16);
+          vo[i] = affine_bf16(vz, vs, vc[0]) | (affine_bf16(vz, vs, vc[1]) << 16);
+        }
+      } else if (t < wstart) {  // beyond the cache: not stored
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ko[i] = vo[i] = 0u;
+      } else {  // recent window: ring slot t mod R
+        const size_t off = (((size_t)b * Hkv + h) * R + (size_t)(t % R)) * KVQ_D * esz;
+        if (a.kv_f32) {
+          const float4 *kf = reinterpret_cast<const float4 *>(a.cache.k_win + off) + 2 * c8;
+          const float4 *vf = reinterpret_cast<const float4 *>(a.cache.v_win + off) + 2 * c8;
+          const float4 k0 = kf[0], k1 = kf[1], v0 = vf[0], v1 = vf[1];
+          ko[0] = kvq_f32_to_bf16_rne(k0.x) | (kvq_f32_to_bf16_rne(k0.y) << 16);
+          ko[1] = kvq_f32_to_bf16_rne(k0.z) | (kvq_f32_to_bf16_rne(k0.w) << 16);
+          ko[2] = kvq_f32_to_bf16_rne(k1.x) | (kvq_f32_to_bf16_rne(k1.y) << 16);
+          ko[3] = kvq_f32_to_bf16_rne(k1.z) | (kvq_f32_to_bf16_rne(k1.w) << 16);
+          vo[0] = kvq_f32_to_bf16_rne(v0.x) | (kvq_f32_to_bf16_rne(v0.y) << 16);
+          vo[1] = kvq_f32_to_bf16_rne(v0.z) | (kvq_f32_to_bf16_rne(v0.w) << 16);
+          vo[2] = kvq_f32_to_bf16_rne(v1.x) | (kvq_f32_to_bf16_rne(v1.y) << 16);
+          vo[3] = kvq_f32_to_bf16_rne(v1.z) | (kvq_f32_to_bf16_rne(v1.w) << 16);
+        } else {
+          const uint4 kw = reinterpret_cast<const uint4 *>(a.cache.k_win + off)[c8];
+          const uint4 vw = reinterpret_cast<const uint4 *>(a.cache.v_win + off)[c8];
+          ko[0] = kw.x; ko[1] = kw.y; ko[2] = kw.z; ko[3] = kw.w;
+          vo[0] = vw.x; vo[1] = vw.y; vo[2] = vw.z; vo[3] = vw.w;
+        }
+      }
+      reinterpret_cast<uint4 *>(a.k_out + (row0 + (size_t)t) * KVQ_D)[c8] = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+      reinterpret_cast<uint4 *>(a.v_out + (row0 + (size_t)t) * KVQ_D)[c8] = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+    }
+    return;
+  }
+  // Rotated keys or values: lane l holds channels 2l, 2l + 1 of one position at a time, the
+  // layout of the cross-lane transform.
 #pragma unroll 4
   for (int n = 0; n < KVQ_PAGE; ++n) {
     const int64_t t = t_first + n;

@@ -1,8 +1,12 @@
 """Host checks of the seeded input generator (no method arithmetic involved)."""
+import os
+
 import numpy as np
 import torch
 
 import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_splitmix64_reference_outputs():
@@ -41,3 +45,18 @@ def test_generator_determinism_and_shapes():
     table, pool = W.WORKLOADS[4].block_table()
     used = table[table >= 0]
     assert np.array_equal(np.sort(used), np.arange(pool))
+
+
+def test_bench_cpu_baseline_runs_on_a_small_sample():
+    """bench.py's cpu_baseline leg (the oracle timed on a sample of one decode step) runs and
+    reports its sample, on a shortened version of the 32k workload."""
+    import dataclasses
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    wl = dataclasses.replace(W.WORKLOADS[3], context=400)
+    r = bench.cpu_baseline(wl, target_seconds=0.01, max_units=2)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+    assert r["sample"].startswith("1 of ") or r["sample"].startswith("2 of ")
