@@ -266,6 +266,64 @@ def decode_attention(q: np.ndarray, caches: list, num_kv_heads: int, scale: floa
 
 
 # --------------------------------------------------------------------------
+# Error budgets  ([P1] "Error pada key masuk sebelum softmax": a key error E_K
+# moves the scores by q E_K^T / sqrt(d) before the softmax; "Error pada value
+# masuk setelah bobot attention terbentuk": with the weights fixed, a value
+# error moves the output by a E_V; "Evaluasi harus sesuai ...": judge the
+# attention quantities, not only reconstruction error; [P2] entries on
+# separate key and value error budgets)
+# --------------------------------------------------------------------------
+def error_budget(q: np.ndarray, K: np.ndarray, V: np.ndarray, cache: dict, scale: float):
+    """Error statistics of one query head against one unit cache (no rotation).
+
+    K, V: the original [L][d] rows; cache: build_unit_cache of the same rows.
+    Window positions are stored exactly, so their reconstruction is the row.
+    Returns (head, unit):
+      head = [max |s' - s|, rms (s' - s), TV(a', a), |a V_hat - a V|,
+              |a' V - a V|, |a' V_hat - a V|, |a V|, 0]
+        with s = scale K q, s' = scale K_hat q, a = softmax(s), a' = softmax(s');
+        the fourth entry is the value error alone (a E_V), the fifth the key
+        error alone, the sixth both; TV is half the L1 distance.
+      unit = [sum E_K^2, sum E_V^2, max |E_K|, max |E_V|, sum K^2, sum V^2,
+              number of quantized positions, 0] over the quantized positions.
+    An empty sequence gives zeros.
+    """
+    if cache.get("v_rotated", False):
+        raise ValueError("error budgets are defined here for unrotated caches")
+    nq = cache["nq"]
+    K = np.asarray(K, dtype=F64)
+    V = np.asarray(V, dtype=F64)
+    L = K.shape[0]
+    EK = cache["k_hat"] - K[:nq]
+    EV = cache["v_hat"] - V[:nq]
+    unit = np.array([np.sum(EK * EK), np.sum(EV * EV),
+                     np.max(np.abs(EK)) if nq else 0.0, np.max(np.abs(EV)) if nq else 0.0,
+                     np.sum(K[:nq] ** 2), np.sum(V[:nq] ** 2), float(nq), 0.0])
+    if L == 0:
+        return np.zeros(8), unit
+    K_hat = np.concatenate([cache["k_hat"], K[nq:]])
+    V_hat = np.concatenate([cache["v_hat"], V[nq:]])
+    q = np.asarray(q, dtype=F64)
+    s = (K @ q) * scale
+    s_q = (K_hat @ q) * scale
+    a = softmax(s)
+    a_q = softmax(s_q)
+    o = a @ V
+    ds = s_q - s
+    head = np.array([
+        np.max(np.abs(ds)),
+        np.sqrt(np.mean(ds * ds)),
+        0.5 * np.sum(np.abs(a_q - a)),
+        np.linalg.norm(a @ V_hat - o),
+        np.linalg.norm(a_q @ V - o),
+        np.linalg.norm(a_q @ V_hat - o),
+        np.linalg.norm(o),
+        0.0,
+    ])
+    return head, unit
+
+
+# --------------------------------------------------------------------------
 # Memory accounting  ([P1] "Pertumbuhan cache ...": payload plus metadata;
 # [P3] "Belangrijkste Bijdragen": K4V2 vs K4V4)
 # --------------------------------------------------------------------------

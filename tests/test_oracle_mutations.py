@@ -130,8 +130,23 @@ def mut_value_rotation_not_undone(M):
     M.unit_attention = unit_attention
 
 
+def mut_error_budget_weights_from_quantized_keys(M):
+    orig = M.error_budget
+
+    def error_budget(q, K, V, cache, scale):
+        head, unit = orig(q, K, V, cache, scale)
+        nq = cache["nq"]
+        K_hat = np.concatenate([cache["k_hat"], np.asarray(K, dtype=np.float64)[nq:]])
+        V_hat = np.concatenate([cache["v_hat"], np.asarray(V, dtype=np.float64)[nq:]])
+        if len(K_hat):
+            a_q = M.softmax(K_hat @ q * scale)
+            head[3] = np.linalg.norm(a_q @ V_hat - a_q @ V)  # mistake: value error under the quantized weights
+        return head, unit
+    M.error_budget = error_budget
+
+
 MUTATIONS = [
-    mut_value_rotation_not_undone, mut_zero_round_nearest, mut_scale_round_nearest, mut_round_half_up, mut_dequant_sign,
+    mut_error_budget_weights_from_quantized_keys, mut_value_rotation_not_undone, mut_zero_round_nearest, mut_scale_round_nearest, mut_round_half_up, mut_dequant_sign,
     mut_dequant_group_index, mut_attention_no_scale, mut_attention_reversed_values, mut_gqa_modulo,
     mut_window_off_by_one, mut_wht_no_normalization, mut_wht_constant_low, mut_softmax_no_max_shift_wrong_axis,
 ]

@@ -403,10 +403,64 @@ def check_outlier(O_):
             assert np.all(s.astype(np.float64)[:, 0] >= delta / ((1 << bits) - 1))
 
 
+def check_error_budget(O_):
+    """Error budgets, pinned by what the definitions force rather than by retyping them:
+    * an exact cache gives zero errors and |a V| equal to scipy-softmax attention's norm;
+    * keys shifted by one common vector u move every score by scale q.u: the max and rms score
+      errors equal |scale q.u|, while the weights, and so TV and the key-only output error, do
+      not move (softmax is shift invariant);
+    * on a real quantization, the value-only output error equals |a E_V| with a from scipy's
+      softmax ([P1]'s o' = o + a E_V), TV equals half the L1 distance of scipy softmaxes, and
+      the key-only and joint errors equal the distances between attention outputs; window
+      positions carry no error and the unit statistics cover exactly the L - R quantized ones."""
+    from scipy.special import softmax as sp_softmax
+
+    rng = np.random.default_rng(101)
+    L, d = 50, 128
+    K = random_bf16_like(rng, (L, d), 1.0)
+    K[:, 9] *= 10.0
+    V = random_bf16_like(rng, (L, d), 1.0)
+    q = random_bf16_like(rng, (d,), 1.0)
+    sc = 1.0 / np.sqrt(d)
+    exact = dict(nq=L, k_hat=K.copy(), v_hat=V.copy(), k_win=K[L:], v_win=V[L:])
+    head, unit = O_.error_budget(q, K, V, exact, sc)
+    o_ref = sp_softmax(K @ q * sc) @ V
+    assert np.all(head[:6] == 0) and np.all(unit[:4] == 0)
+    assert abs(head[6] - np.linalg.norm(o_ref)) < 1e-12 and unit[6] == L
+    u = random_bf16_like(rng, (d,), 0.3)
+    shifted = dict(exact, k_hat=K + u)
+    head, unit = O_.error_budget(q, K, V, shifted, sc)
+    shift = abs(sc * float(q @ u))
+    assert shift > 1e-3
+    assert abs(head[0] - shift) < 1e-9 and abs(head[1] - shift) < 1e-9
+    assert head[2] < 1e-12 and head[4] < 1e-9 and head[3] == 0
+    assert abs(unit[0] - L * float(u @ u)) < 1e-8 * L * float(u @ u)
+    for kb, vb, R in ((4, 2, 0), (2, 4, 7), (1, 1, 12)):
+        prm = _params(R=R, kb=kb, vb=vb)
+        cache = O_.build_unit_cache(K, V, L, prm)
+        head, unit = O_.error_budget(q, K, V, cache, sc)
+        nq = L - R
+        Kh = np.concatenate([cache["k_hat"], K[nq:]])
+        Vh = np.concatenate([cache["v_hat"], V[nq:]])
+        a = sp_softmax(K @ q * sc)
+        a_q = sp_softmax(Kh @ q * sc)
+        assert abs(head[3] - np.linalg.norm(a @ (Vh - V))) < 1e-12
+        assert abs(head[2] - 0.5 * np.abs(a_q - a).sum()) < 1e-12
+        assert abs(head[4] - np.linalg.norm(a_q @ V - a @ V)) < 1e-12
+        assert abs(head[5] - np.linalg.norm(a_q @ Vh - a @ V)) < 1e-12
+        assert unit[6] == nq
+        assert abs(unit[1] - np.sum((Vh - V) ** 2)) < 1e-12 * max(1.0, unit[1])
+        assert unit[2] == np.max(np.abs(Kh - K)) and head[0] == np.max(np.abs((Kh - K) @ q * sc))
+        assert head[3] > 0 and head[4] > 0
+    empty = O_.build_unit_cache(K[:0], V[:0], 0, _params())
+    head, unit = O_.error_budget(q, K[:0], V[:0], empty, sc)
+    assert np.all(head == 0) and np.all(unit == 0)
+
+
 ALL_CHECKS = [
     check_fp16_directed, check_golden, check_wht, check_attention_library, check_attention_decimal,
     check_end_to_end_exact, check_error_identities, check_window, check_gqa, check_rotation_special_case,
-    check_memory_model, check_group_size_monotone, check_outlier, check_value_rotation,
+    check_memory_model, check_group_size_monotone, check_outlier, check_value_rotation, check_error_budget,
 ]
 
 
@@ -518,3 +572,7 @@ def test_bf16_rounding_helper_of_the_parity_tests():
     got = bf16_bits_rne_f64(np.array(xs))
     want = np.array([exact(x) for x in xs], dtype=np.uint16)
     assert np.array_equal(got, want)
+
+
+def test_error_budget_definitions():
+    check_error_budget(O)
