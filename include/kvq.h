@@ -226,6 +226,30 @@ kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, c
                                       void *out, int32_t out_dtype, float softmax_scale, void *workspace,
                                       size_t workspace_bytes, hipStream_t stream);
 
+/* Error-budget diagnostics ([P1] "Error pada key masuk sebelum softmax", "Error pada value masuk
+ * setelah bobot attention terbentuk", "Evaluasi harus sesuai dengan besaran yang ingin
+ * dipertahankan"; [P2]'s entries on separate key and value error budgets).  Compares the cache
+ * with the original keys and values k_ref, v_ref (device bf16 [batch][max_seq_len][num_kv_heads]
+ * [128], the rows that were appended; 16-byte aligned) for the query q (as for
+ * kvq_decode_attention).  For sequence b, query head h, over positions t < min(seq_lens[b],
+ * max_seq_len), with exact scores s_t = scale * q.k_t, quantized scores s'_t = scale * q.k_hat_t,
+ * a = softmax(s), a' = softmax(s') and window positions exact (k_hat = k, v_hat = v there),
+ * head_stats[b][h][0..7] (device fp32, 16-byte aligned) receives
+ *   {max_t |s'_t - s_t|, sqrt(mean_t (s'_t - s_t)^2), sum_t |a'_t - a_t| / 2,
+ *    |a V_hat - a V| (value error alone), |a' V - a V| (key error alone),
+ *    |a' V_hat - a V| (both), |a V|, 0}     (Euclidean norms over the 128 channels),
+ * and unit_stats[b][kv][0..7] (device fp32, 16-byte aligned) the reconstruction errors over the
+ * quantized positions {sum (k_hat - k)^2, sum (v_hat - v)^2, max |k_hat - k|, max |v_hat - v|,
+ *    sum k^2, sum v^2, number of quantized positions, 0}.
+ * fp32 arithmetic, reconstructions zero + code * scale rounded to fp32.  Caches with key or
+ * value rotation: KVQ_EUNSUPPORTED.  Errors otherwise as for kvq_decode_attention. */
+#define KVQ_EB_HEAD 8
+#define KVQ_EB_UNIT 8
+kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                            int64_t max_seq_len, const uint16_t *k_ref, const uint16_t *v_ref, const void *q,
+                            int32_t q_dtype, float softmax_scale, float *head_stats, float *unit_stats,
+                            hipStream_t stream);
+
 /* Static description of a status code. */
 const char *kvq_status_str(kvq_status status);
 

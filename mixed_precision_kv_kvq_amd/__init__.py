@@ -37,6 +37,7 @@ EXPORTED = [
     "kvq_dequantize_dense",
     "kvq_dense_workspace_bytes",
     "kvq_dense_decode_attention",
+    "kvq_error_budget",
     "kvq_status_str",
 ]
 
@@ -118,6 +119,9 @@ def _load():
                                                c_void_p, c_int32, c_void_p, c_int32, c_float, c_void_p, c_size_t,
                                                c_void_p]
     lib.kvq_dense_decode_attention.restype = c_int32
+    lib.kvq_error_budget.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+                                     c_int32, c_float, c_void_p, c_void_p, c_void_p]
+    lib.kvq_error_budget.restype = c_int32
     lib.kvq_status_str.argtypes = [c_int32]
     lib.kvq_status_str.restype = ctypes.c_char_p
     return lib
@@ -161,7 +165,7 @@ def bound_call(name: str, *args, stream=None):
     conv = [ctypes.byref(a) if isinstance(a, ctypes.Structure) else _ptr(a) if hasattr(a, "data_ptr") else a
             for a in args]
     if name in ("kvq_quantize_append", "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine",
-                "kvq_dequantize_dense", "kvq_dense_decode_attention"):
+                "kvq_dequantize_dense", "kvq_dense_decode_attention", "kvq_error_budget"):
         conv.append(_stream(stream))
     conv = tuple(conv)
 
@@ -256,6 +260,20 @@ def kvq_dense_decode_attention(params, batch, k, v, seq_lens, max_seq_len, q, q_
                                          float(softmax_scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "kvq_dense_decode_attention")
+    return st
+
+
+KVQ_EB_HEAD = 8  # per (sequence, query head) error statistics
+KVQ_EB_UNIT = 8  # per (sequence, kv head) reconstruction statistics
+
+
+def kvq_error_budget(params, cache, seq_lens, max_seq_len, k_ref, v_ref, q, q_dtype, softmax_scale, head_stats,
+                     unit_stats, stream=None, check=True):
+    st = _lib.kvq_error_budget(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens), int(max_seq_len),
+                               _ptr(k_ref), _ptr(v_ref), _ptr(q), int(q_dtype), float(softmax_scale),
+                               _ptr(head_stats), _ptr(unit_stats), _stream(stream))
+    if check:
+        _check(st, "kvq_error_budget")
     return st
 
 

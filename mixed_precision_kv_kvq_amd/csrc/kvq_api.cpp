@@ -368,6 +368,38 @@ kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, c
   return hip_status(kvq_launch_combine(c, stream));
 }
 
+kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                            int64_t max_seq_len, const uint16_t *k_ref, const uint16_t *v_ref, const void *q,
+                            int32_t q_dtype, float softmax_scale, float *head_stats, float *unit_stats,
+                            hipStream_t stream) {
+  if (kvq_status st = check_params(params)) return st;
+  if (kvq_status st = check_cache(params, cache)) return st;
+  if (params->key_rotation || params->value_rotation) return KVQ_EUNSUPPORTED;
+  if (!seq_lens || max_seq_len < 0 || max_seq_len > INT32_MAX) return KVQ_EINVAL;
+  if (!k_ref || !v_ref || !q || !head_stats || !unit_stats) return KVQ_EINVAL;
+  if (!aligned16(k_ref) || !aligned16(v_ref) || !aligned16(q) || !aligned16(head_stats) || !aligned16(unit_stats))
+    return KVQ_EINVAL;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_EINVAL;
+  if (!(softmax_scale >= 0.f) || isinf(softmax_scale)) return KVQ_EINVAL;
+  KvqErrArgs a = {};
+  a.lay = layout_of(params);
+  a.cache = dev_cache(params, cache);
+  a.seq_lens = seq_lens;
+  a.k_ref = k_ref;
+  a.v_ref = v_ref;
+  a.q = q;
+  a.head_stats = head_stats;
+  a.unit_stats = unit_stats;
+  a.max_len = max_seq_len;
+  a.B = cache->batch;
+  a.Hq = params->num_q_heads;
+  a.Hkv = params->num_kv_heads;
+  a.R = params->window;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
+  return hip_status(kvq_launch_errbudget(a, stream));
+}
+
 const char *kvq_status_str(kvq_status status) {
   switch (status) {
     case KVQ_OK: return "ok";

@@ -1,0 +1,278 @@
+// Error-budget diagnostics of a quantized cache against the original keys and values.
+// nalar.dev "Kuantisasi KV cache mengganggu attention melalui key dan value tersimpan":
+// section "Error pada key masuk sebelum softmax" (a key error E_K shifts the scores by
+// q E_K^T / sqrt(d) before the softmax), section "Error pada value masuk setelah bobot attention
+// terbentuk" (a value error E_V moves the output by a E_V after the weights are formed), and
+// section "Evaluasi harus sesuai dengan besaran yang ingin dipertahankan" (judge the attention
+// quantities, not only reconstruction error); the nalar.dev tag page's entries on separate key
+// and value error budgets.
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+__device__ __attribute__((always_inline)) inline void bf16x8(const uint4 w, float *x) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = kvq_bf16_bits_to_f32(ws[i] & 0xFFFFu);
+    x[2 * i + 1] = kvq_bf16_bits_to_f32(ws[i] >> 16);
+  }
+}
+
+__device__ inline float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+
+__device__ inline float row16_sum(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+struct Pos {
+  bool valid, quant;
+  const uint8_t *rec;  // page record of a quantized position
+  int n;               // position within the page
+};
+
+// Keys (or values) of 8 channels [8c, 8c + 8) of one position: original and reconstructed.
+// Window positions are stored exactly, so their reconstruction is the original row.
+template <bool KEYS>
+__device__ __attribute__((always_inline)) inline void load8(const KvqErrArgs &a, const Pos &p, const uint16_t *ref_row, int c, float *x,
+                             float *xh) {
+  if (!p.valid) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = xh[e] = 0.f;
+    return;
+  }
+  bf16x8(reinterpret_cast<const uint4 *>(ref_row)[c], x);
+  if (!p.quant) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xh[e] = x[e];
+    return;
+  }
+  const KvqLayout &lay = a.lay;
+  const int bits = KEYS ? lay.kb : lay.vb;
+  const int grp = (8 * c) / (KEYS ? lay.kg : lay.vg);
+  const uint32_t m = *reinterpret_cast<const uint32_t *>(
+      p.rec + (KEYS ? lay.k_meta_off : lay.v_meta_off) + 4 * kvq_meta_dword(KEYS ? lay.nkg : lay.nvg, p.n, grp));
+  const float zero = f16f(m >> 16), scale = f16f(m & 0xFFFF);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    int off, bit;
+    if (KEYS)
+      kvq_k_code_pos(bits, p.n, 8 * c + e, &off, &bit);
+    else
+      kvq_v_code_pos(bits, p.n, 8 * c + e, &off, &bit);
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(p.rec + (KEYS ? lay.k_codes_off : lay.v_codes_off) + off);
+    xh[e] = zero + (float)((w >> bit) & ((1u << bits) - 1u)) * scale;
+  }
+}
+
+// One wave per (query head, sequence), lane 16 r + c holding channels [8c, 8c + 8) of position
+// 4 i + r.  Pass 1: exact and quantized scores with online maxima and sums (log2 units) and the
+// score-error statistics; the first query head of each kv head also accumulates the key
+// reconstruction error.  Pass 2: the weights a (exact keys) and a' (quantized keys), their total
+// variation, and the four weighted sums a V, a V_hat, a' V, a' V_hat.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void kvq_errbudget_kernel(KvqErrArgs a) {
+  const int lane = threadIdx.x, hq = blockIdx.x, b = blockIdx.y;
+  const int r = lane >> 4, c = lane & 15;
+  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, h = hq / g;
+  const bool unit_lead = (hq % g) == 0;
+  int64_t L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+  int64_t nq = L > a.R ? L - a.R : 0;
+  const int64_t cap_tokens = (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq) * KVQ_PAGE;
+  if (nq > cap_tokens) nq = cap_tokens;
+  const float ninf = -__builtin_inff();
+
+  float q[8];
+  {
+    const size_t qrow = ((size_t)b * a.Hq + hq) * KVQ_D + 8 * c;
+    if (a.q_f32) {
+      const float4 *qp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow);
+      const float4 x = qp[0], y = qp[1];
+      q[0] = x.x; q[1] = x.y; q[2] = x.z; q[3] = x.w; q[4] = y.x; q[5] = y.y; q[6] = y.z; q[7] = y.w;
+    } else {
+      bf16x8(*reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qrow), q);
+    }
+  }
+  auto pos_of = [&](int64_t t) {
+    Pos p;
+    p.valid = t < L;
+    p.quant = t < nq;
+    p.n = (int)(t % KVQ_PAGE);
+    p.rec = nullptr;
+    if (p.valid && p.quant) {
+      const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
+                                               (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, b, h,
+                                               t / KVQ_PAGE);
+      p.rec = a.cache.pages + (size_t)rec_idx * a.lay.record;
+    }
+    return p;
+  };
+  auto ref_row = [&](const uint16_t *base, int64_t t) {
+    return base + (((size_t)b * a.max_len + (size_t)t) * Hkv + h) * KVQ_D;
+  };
+  const float sl2 = a.scale * 1.4426950408889634f;  // softmax scale in log2 units
+
+  // ---- pass 1 ----
+  float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f;  // exact / quantized scores (log2 units)
+  float ds_max = 0.f, ds_sq = 0.f;                // score error (natural units)
+  float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;    // key reconstruction error (lead wave)
+  for (int64_t i0 = 0; i0 < L; i0 += 4) {
+    const int64_t t = i0 + r;
+    const Pos p = pos_of(t);
+    float k[8], kh[8];
+    load8<true>(a, p, ref_row(a.k_ref, t < L ? t : 0), c, k, kh);
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      d0 = __builtin_fmaf(q[e], k[e], d0);
+      d1 = __builtin_fmaf(q[e], kh[e], d1);
+    }
+    d0 = row16_sum(d0);
+    d1 = row16_sum(d1);
+    if (p.valid) {
+      const float s0 = d0 * sl2, s1 = d1 * sl2;
+      const float n0 = __builtin_fmaxf(m0, s0), n1 = __builtin_fmaxf(m1, s1);
+      z0 = z0 * __builtin_amdgcn_exp2f(m0 - n0) + __builtin_amdgcn_exp2f(s0 - n0);
+      z1 = z1 * __builtin_amdgcn_exp2f(m1 - n1) + __builtin_amdgcn_exp2f(s1 - n1);
+      m0 = n0;
+      m1 = n1;
+      const float ds = (d1 - d0) * a.scale;
+      ds_max = __builtin_fmaxf(ds_max, __builtin_fabsf(ds));
+      ds_sq = __builtin_fmaf(ds, ds, ds_sq);
+      if (unit_lead && p.quant) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float err = kh[e] - k[e];
+          ek_sq = __builtin_fmaf(err, err, ek_sq);
+          ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
+          k_sq = __builtin_fmaf(k[e], k[e], k_sq);
+        }
+      }
+    }
+  }
+  // combine the four position classes (lanes of one row hold equal values)
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float om0 = __shfl_xor(m0, off), oz0 = __shfl_xor(z0, off);
+    const float om1 = __shfl_xor(m1, off), oz1 = __shfl_xor(z1, off);
+    const float n0 = __builtin_fmaxf(m0, om0), n1 = __builtin_fmaxf(m1, om1);
+    z0 = (n0 == ninf) ? 0.f : z0 * __builtin_amdgcn_exp2f(m0 - n0) + oz0 * __builtin_amdgcn_exp2f(om0 - n0);
+    z1 = (n1 == ninf) ? 0.f : z1 * __builtin_amdgcn_exp2f(m1 - n1) + oz1 * __builtin_amdgcn_exp2f(om1 - n1);
+    m0 = n0;
+    m1 = n1;
+    ds_max = __builtin_fmaxf(ds_max, __shfl_xor(ds_max, off));
+    ds_sq += __shfl_xor(ds_sq, off);
+  }
+
+  // ---- pass 2 ----
+  const float iz0 = z0 > 0.f ? 1.f / z0 : 0.f, iz1 = z1 > 0.f ? 1.f / z1 : 0.f;
+  float tv = 0.f;
+  float ev_sq = 0.f, ev_max = 0.f, v_sq = 0.f;
+  float o[8], ov[8], ok[8], oj[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = ov[e] = ok[e] = oj[e] = 0.f;
+  for (int64_t i0 = 0; i0 < L; i0 += 4) {
+    const int64_t t = i0 + r;
+    const Pos p = pos_of(t);
+    float k[8], kh[8], v[8], vh[8];
+    load8<true>(a, p, ref_row(a.k_ref, t < L ? t : 0), c, k, kh);
+    load8<false>(a, p, ref_row(a.v_ref, t < L ? t : 0), c, v, vh);
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      d0 = __builtin_fmaf(q[e], k[e], d0);
+      d1 = __builtin_fmaf(q[e], kh[e], d1);
+    }
+    d0 = row16_sum(d0);
+    d1 = row16_sum(d1);
+    const float w0 = p.valid ? __builtin_amdgcn_exp2f(d0 * sl2 - m0) * iz0 : 0.f;
+    const float w1 = p.valid ? __builtin_amdgcn_exp2f(d1 * sl2 - m1) * iz1 : 0.f;
+    if (c == 0) tv += __builtin_fabsf(w1 - w0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] = __builtin_fmaf(w0, v[e], o[e]);
+      ov[e] = __builtin_fmaf(w0, vh[e], ov[e]);
+      ok[e] = __builtin_fmaf(w1, v[e], ok[e]);
+      oj[e] = __builtin_fmaf(w1, vh[e], oj[e]);
+    }
+    if (unit_lead && p.valid && p.quant) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float err = vh[e] - v[e];
+        ev_sq = __builtin_fmaf(err, err, ev_sq);
+        ev_max = __builtin_fmaxf(ev_max, __builtin_fabsf(err));
+        v_sq = __builtin_fmaf(v[e], v[e], v_sq);
+      }
+    }
+  }
+  // sums over the position classes, then norms over the channels
+  float nv = 0.f, nk = 0.f, nj = 0.f, no = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    o[e] += __shfl_xor(o[e], 16);
+    o[e] += __shfl_xor(o[e], 32);
+    ov[e] += __shfl_xor(ov[e], 16);
+    ov[e] += __shfl_xor(ov[e], 32);
+    ok[e] += __shfl_xor(ok[e], 16);
+    ok[e] += __shfl_xor(ok[e], 32);
+    oj[e] += __shfl_xor(oj[e], 16);
+    oj[e] += __shfl_xor(oj[e], 32);
+    const float dv = ov[e] - o[e], dk = ok[e] - o[e], dj = oj[e] - o[e];
+    nv = __builtin_fmaf(dv, dv, nv);
+    nk = __builtin_fmaf(dk, dk, nk);
+    nj = __builtin_fmaf(dj, dj, nj);
+    no = __builtin_fmaf(o[e], o[e], no);
+  }
+  nv = row16_sum(nv);
+  nk = row16_sum(nk);
+  nj = row16_sum(nj);
+  no = row16_sum(no);
+  for (int off = 1; off <= 32; off <<= 1) tv += __shfl_xor(tv, off);
+  float *hs = a.head_stats + ((size_t)b * a.Hq + hq) * KVQ_EB_HEAD;
+  if (lane == 0) {
+    const float n = (float)L;
+    hs[0] = ds_max;
+    hs[1] = L > 0 ? sqrtf(ds_sq / n) : 0.f;
+    hs[2] = 0.5f * tv;
+    hs[3] = sqrtf(nv);
+    hs[4] = sqrtf(nk);
+    hs[5] = sqrtf(nj);
+    hs[6] = sqrtf(no);
+    hs[7] = 0.f;
+  }
+  if (unit_lead) {
+    for (int off = 1; off <= 32; off <<= 1) {
+      ek_sq += __shfl_xor(ek_sq, off);
+      k_sq += __shfl_xor(k_sq, off);
+      ev_sq += __shfl_xor(ev_sq, off);
+      v_sq += __shfl_xor(v_sq, off);
+      ek_max = __builtin_fmaxf(ek_max, __shfl_xor(ek_max, off));
+      ev_max = __builtin_fmaxf(ev_max, __shfl_xor(ev_max, off));
+    }
+    float *us = a.unit_stats + ((size_t)b * Hkv + h) * KVQ_EB_UNIT;
+    if (lane == 0) {
+      us[0] = ek_sq;
+      us[1] = ev_sq;
+      us[2] = ek_max;
+      us[3] = ev_max;
+      us[4] = k_sq;
+      us[5] = v_sq;
+      us[6] = (float)nq;
+      us[7] = 0.f;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
+  hipLaunchKernelGGL(kvq_errbudget_kernel, dim3((unsigned)a.Hq, (unsigned)a.B), dim3(64), 0, s, a);
+  return hipGetLastError();
+}

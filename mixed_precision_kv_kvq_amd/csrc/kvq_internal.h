@@ -176,4 +176,18 @@ struct KvqDenseArgs {
 #define KVQ_DENSE_SPLIT 256  // tokens per split of the dense attention
 hipError_t kvq_launch_dequantize_dense(const KvqDenseArgs &a, hipStream_t s);
 hipError_t kvq_launch_dense_partials(const KvqDenseArgs &a, int g, hipStream_t s);
+
+// Error-budget diagnostics against the original keys and values.
+struct KvqErrArgs {
+  KvqLayout lay;
+  KvqCacheDev cache;
+  const int32_t *seq_lens;
+  const uint16_t *k_ref, *v_ref;  // bf16 [B][max_len][Hkv][128]
+  const void *q;
+  float *head_stats, *unit_stats;
+  int64_t max_len;
+  int32_t B, Hq, Hkv, R, q_f32;
+  float scale;
+};
+hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s);
 bool kvq_attention_supported(int kb, int vb, int g, int q_parts, int nvg);

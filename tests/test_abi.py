@@ -207,6 +207,26 @@ def test_unfused_baseline_validation():
     assert att(seq=None) == K.KVQ_EINVAL
 
 
+def test_error_budget_validation():
+    L = K.lib()
+
+    def call(prm_=None, c=None, seq=FAKE, mx=64, kr=FAKE, vr=FAKE, q=FAKE, qd=K.KVQ_BF16, sc=0.0, hs=FAKE, us=FAKE):
+        return L.kvq_error_budget(ctypes.byref(prm_ or p()), ctypes.byref(c or cache()), seq, mx, kr, vr, q, qd, sc,
+                                  hs, us, None)
+
+    assert call(prm_=p(key_rotation=1)) == K.KVQ_EUNSUPPORTED
+    assert call(prm_=p(value_rotation=1)) == K.KVQ_EUNSUPPORTED
+    assert call(seq=None) == K.KVQ_EINVAL
+    assert call(kr=None) == K.KVQ_EINVAL
+    assert call(vr=FAKE + 2) == K.KVQ_EINVAL
+    assert call(hs=FAKE + 4) == K.KVQ_EINVAL
+    assert call(us=None) == K.KVQ_EINVAL
+    assert call(qd=4) == K.KVQ_EINVAL
+    assert call(sc=-2.0) == K.KVQ_EINVAL
+    assert call(mx=-1) == K.KVQ_EINVAL
+    assert call(prm_=p(v_group=32)) == K.KVQ_EUNSUPPORTED
+
+
 def test_status_strings():
     for s in range(5):
         assert K.kvq_status_str(s)
