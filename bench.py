@@ -394,6 +394,50 @@ def main():
         del kd, vd, dw
         torch.cuda.synchronize()
 
+    # ---- error-budget diagnostics at the last step's state, against the original rows ----
+    errb = None
+    if not args.no_unfused:
+        L_last = L0 + args.warmup + args.steps
+        lens_last = lens[args.warmup + args.steps]
+        q_last = q_steps[args.warmup + args.steps - 1]
+        k_ref = gen.kv(W.TENSOR_K, 0, L_last)
+        v_ref = gen.kv(W.TENSOR_V, 0, L_last)
+        hs = torch.empty((B, Hq, K.KVQ_EB_HEAD), dtype=torch.float32, device=dev)
+        us = torch.empty((B, Hkv, K.KVQ_EB_UNIT), dtype=torch.float32, device=dev)
+        eb = K.bound_call("kvq_error_budget", params, cache.struct, lens_last, L_last, k_ref, v_ref, q_last,
+                          K.KVQ_BF16, 0.0, hs, us, stream=stream)
+        eb()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        for _ in range(3):
+            eb()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        eb_us = e[0].elapsed_time(e[1]) * 1e3 / 3
+        h_ = hs.cpu().numpy().astype(np.float64)
+        u_ = us.cpu().numpy().astype(np.float64)
+        per_th_q = (d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4)
+        nq_last = max(L_last - R, 0)
+        eb_bytes = B * Hkv * (L_last * 2 * d * 2 + nq_last * per_th_q)  # originals and the store, read once
+        errb = {
+            "what": "kvq_error_budget at the last step's state against the original bf16 rows (8 waves per "
+                    "query head, two passes), 3 launches between two events",
+            "us": round(eb_us, 1), "unit_bytes_read_once": int(eb_bytes),
+            "GBs_vs_read_once": round(eb_bytes / (eb_us * 1e-6) / 1e9, 1),
+            "median_over_heads": {
+                "max_score_error": float(np.median(h_[..., 0])), "rms_score_error": float(np.median(h_[..., 1])),
+                "weight_total_variation": float(np.median(h_[..., 2])),
+                "output_error_values_only": float(np.median(h_[..., 3])),
+                "output_error_keys_only": float(np.median(h_[..., 4])),
+                "output_error_both": float(np.median(h_[..., 5])), "output_norm": float(np.median(h_[..., 6]))},
+            "relative_reconstruction_error": {
+                "keys": float(np.sqrt(u_[..., 0].sum() / u_[..., 4].sum())),
+                "values": float(np.sqrt(u_[..., 1].sum() / u_[..., 5].sum()))},
+        }
+        del k_ref, v_ref
+        torch.cuda.synchronize()
+
     per_th = (d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4)
     launch_bytes = split_kernel_bytes(wl, L0 + args.warmup + args.steps, per_th, 2)  # the timed launch
     achieved = float(launch_bytes / (split_us * 1e-6) / 1e9)
@@ -446,6 +490,8 @@ def main():
     }
     if unfused is not None:
         res["unfused_baseline"] = unfused
+    if errb is not None:
+        res["error_budget"] = errb
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -71,13 +71,18 @@ __device__ __attribute__((always_inline)) inline void load8(const KvqErrArgs &a,
   }
 }
 
-// One wave per (query head, sequence), lane 16 r + c holding channels [8c, 8c + 8) of position
-// 4 i + r.  Pass 1: exact and quantized scores with online maxima and sums (log2 units) and the
-// score-error statistics; the first query head of each kv head also accumulates the key
-// reconstruction error.  Pass 2: the weights a (exact keys) and a' (quantized keys), their total
-// variation, and the four weighted sums a V, a V_hat, a' V, a' V_hat.
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void kvq_errbudget_kernel(KvqErrArgs a) {
-  const int lane = threadIdx.x, hq = blockIdx.x, b = blockIdx.y;
+// One workgroup of EB_WAVES waves per (query head, sequence); wave w takes positions 4 (w + k
+// EB_WAVES) + r, lane 16 r + c holding channels [8c, 8c + 8).  Pass 1: exact and quantized
+// scores with online maxima and sums (log2 units) and the score-error statistics; the first
+// query head of each kv head also accumulates the key reconstruction error.  The waves' maxima
+// and sums are merged through LDS (every wave merges them in the same order).  Pass 2: the
+// weights a (exact keys) and a' (quantized keys), their total variation, and the four weighted
+// sums a V, a V_hat, a' V, a' V_hat, merged over the waves through LDS at the end.
+constexpr int EB_WAVES = 8;
+__global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs a) {
+  __shared__ float red[EB_WAVES][8];
+  __shared__ float accs[4][KVQ_D];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = blockIdx.x, b = blockIdx.y;
   const int r = lane >> 4, c = lane & 15;
   const int Hkv = a.Hkv, g = a.Hq / a.Hkv, h = hq / g;
   const bool unit_lead = (hq % g) == 0;
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f;  // exact / quantized scores (log2 units)
   float ds_max = 0.f, ds_sq = 0.f;                // score error (natural units)
   float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;    // key reconstruction error (lead wave)
-  for (int64_t i0 = 0; i0 < L; i0 += 4) {
+  for (int64_t i0 = 4 * w; i0 < L; i0 += 4 * EB_WAVES) {
     const int64_t t = i0 + r;
     const Pos p = pos_of(t);
     float k[8], kh[8];
@@ -168,6 +173,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     ds_max = __builtin_fmaxf(ds_max, __shfl_xor(ds_max, off));
     ds_sq += __shfl_xor(ds_sq, off);
   }
+  // merge the waves (same order in every wave)
+  if (lane == 0) {
+    red[w][0] = m0;
+    red[w][1] = z0;
+    red[w][2] = m1;
+    red[w][3] = z1;
+    red[w][4] = ds_max;
+    red[w][5] = ds_sq;
+  }
+  __syncthreads();
+  {
+    float M0 = ninf, M1 = ninf;
+    for (int i = 0; i < EB_WAVES; ++i) {
+      M0 = __builtin_fmaxf(M0, red[i][0]);
+      M1 = __builtin_fmaxf(M1, red[i][2]);
+    }
+    float Z0 = 0.f, Z1 = 0.f, dmx = 0.f, dsq = 0.f;
+    for (int i = 0; i < EB_WAVES; ++i) {
+      if (red[i][0] != ninf) Z0 += red[i][1] * __builtin_amdgcn_exp2f(red[i][0] - M0);
+      if (red[i][2] != ninf) Z1 += red[i][3] * __builtin_amdgcn_exp2f(red[i][2] - M1);
+      dmx = __builtin_fmaxf(dmx, red[i][4]);
+      dsq += red[i][5];
+    }
+    m0 = M0;
+    z0 = Z0;
+    m1 = M1;
+    z1 = Z1;
+    ds_max = dmx;
+    ds_sq = dsq;
+  }
+  __syncthreads();
 
   // ---- pass 2 ----
   const float iz0 = z0 > 0.f ? 1.f / z0 : 0.f, iz1 = z1 > 0.f ? 1.f / z1 : 0.f;
@@ -176,7 +212,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   float o[8], ov[8], ok[8], oj[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = ov[e] = ok[e] = oj[e] = 0.f;
-  for (int64_t i0 = 0; i0 < L; i0 += 4) {
+  for (int64_t i0 = 4 * w; i0 < L; i0 += 4 * EB_WAVES) {
     const int64_t t = i0 + r;
     const Pos p = pos_of(t);
     float k[8], kh[8], v[8], vh[8];
@@ -210,8 +246,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
       }
     }
   }
-  // sums over the position classes, then norms over the channels
-  float nv = 0.f, nk = 0.f, nj = 0.f, no = 0.f;
+  // sums over the position classes, then over the waves (one wave at a time into LDS)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     o[e] += __shfl_xor(o[e], 16);
@@ -222,17 +257,68 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     ok[e] += __shfl_xor(ok[e], 32);
     oj[e] += __shfl_xor(oj[e], 16);
     oj[e] += __shfl_xor(oj[e], 32);
-    const float dv = ov[e] - o[e], dk = ok[e] - o[e], dj = oj[e] - o[e];
+  }
+  for (int off = 1; off <= 32; off <<= 1) tv += __shfl_xor(tv, off);
+  if (unit_lead) {
+    for (int off = 1; off <= 32; off <<= 1) {
+      ek_sq += __shfl_xor(ek_sq, off);
+      k_sq += __shfl_xor(k_sq, off);
+      ev_sq += __shfl_xor(ev_sq, off);
+      v_sq += __shfl_xor(v_sq, off);
+      ek_max = __builtin_fmaxf(ek_max, __shfl_xor(ek_max, off));
+      ev_max = __builtin_fmaxf(ev_max, __shfl_xor(ev_max, off));
+    }
+  }
+  if (lane == 0) {
+    red[w][0] = tv;
+    red[w][1] = ek_sq;
+    red[w][2] = ev_sq;
+    red[w][3] = ek_max;
+    red[w][4] = ev_max;
+    red[w][5] = k_sq;
+    red[w][6] = v_sq;
+  }
+  for (int i = 0; i < EB_WAVES; ++i) {
+    if (w == i && r == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ch = 8 * c + e;
+        accs[0][ch] = (i == 0 ? 0.f : accs[0][ch]) + o[e];
+        accs[1][ch] = (i == 0 ? 0.f : accs[1][ch]) + ov[e];
+        accs[2][ch] = (i == 0 ? 0.f : accs[2][ch]) + ok[e];
+        accs[3][ch] = (i == 0 ? 0.f : accs[3][ch]) + oj[e];
+      }
+    }
+    __syncthreads();
+  }
+  if (w != 0) return;
+  tv = 0.f;
+  ek_sq = ev_sq = ek_max = ev_max = k_sq = v_sq = 0.f;
+  for (int i = 0; i < EB_WAVES; ++i) {
+    tv += red[i][0];
+    ek_sq += red[i][1];
+    ev_sq += red[i][2];
+    ek_max = __builtin_fmaxf(ek_max, red[i][3]);
+    ev_max = __builtin_fmaxf(ev_max, red[i][4]);
+    k_sq += red[i][5];
+    v_sq += red[i][6];
+  }
+  // norms over the channels: lane l takes channels l and l + 64
+  float nv = 0.f, nk = 0.f, nj = 0.f, no = 0.f;
+  for (int ch = lane; ch < KVQ_D; ch += 64) {
+    const float oo = accs[0][ch];
+    const float dv = accs[1][ch] - oo, dk = accs[2][ch] - oo, dj = accs[3][ch] - oo;
     nv = __builtin_fmaf(dv, dv, nv);
     nk = __builtin_fmaf(dk, dk, nk);
     nj = __builtin_fmaf(dj, dj, nj);
-    no = __builtin_fmaf(o[e], o[e], no);
+    no = __builtin_fmaf(oo, oo, no);
   }
-  nv = row16_sum(nv);
-  nk = row16_sum(nk);
-  nj = row16_sum(nj);
-  no = row16_sum(no);
-  for (int off = 1; off <= 32; off <<= 1) tv += __shfl_xor(tv, off);
+  for (int off = 1; off <= 32; off <<= 1) {
+    nv += __shfl_xor(nv, off);
+    nk += __shfl_xor(nk, off);
+    nj += __shfl_xor(nj, off);
+    no += __shfl_xor(no, off);
+  }
   float *hs = a.head_stats + ((size_t)b * a.Hq + hq) * KVQ_EB_HEAD;
   if (lane == 0) {
     const float n = (float)L;
@@ -246,14 +332,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     hs[7] = 0.f;
   }
   if (unit_lead) {
-    for (int off = 1; off <= 32; off <<= 1) {
-      ek_sq += __shfl_xor(ek_sq, off);
-      k_sq += __shfl_xor(k_sq, off);
-      ev_sq += __shfl_xor(ev_sq, off);
-      v_sq += __shfl_xor(v_sq, off);
-      ek_max = __builtin_fmaxf(ek_max, __shfl_xor(ek_max, off));
-      ev_max = __builtin_fmaxf(ev_max, __shfl_xor(ev_max, off));
-    }
     float *us = a.unit_stats + ((size_t)b * Hkv + h) * KVQ_EB_UNIT;
     if (lane == 0) {
       us[0] = ek_sq;
@@ -273,6 +351,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
-  hipLaunchKernelGGL(kvq_errbudget_kernel, dim3((unsigned)a.Hq, (unsigned)a.B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(kvq_errbudget_kernel, dim3((unsigned)a.Hq, (unsigned)a.B), dim3(64 * EB_WAVES), 0, s, a);
   return hipGetLastError();
 }
