@@ -180,6 +180,54 @@ def cpu_baseline(wl, target_seconds=12.0, max_units=None):
     }
 
 
+def error_budget_sweep(dev):
+    """kvq_error_budget over the bit pairs of the paged batch-8 workload (lengths 1k-16k, 3 key
+    outlier channels x10 per kv head): each pair's cache is filled by one append of every
+    sequence's rows, then diagnosed against those rows for decode step 0's query."""
+    import numpy as np
+    import torch
+
+    import mixed_precision_kv_kvq_amd as K
+    import workloads as W
+    from workloads.device import DeviceGenerator
+
+    rows = []
+    for kb, vb in W.SWEEP_BITS:
+        wl = W.WORKLOADS[4].with_bits(kb, vb)
+        Lb = wl.context_lengths()
+        Lmax = int(Lb.max())
+        table_np, pool = wl.block_table()
+        table = torch.from_numpy(table_np).to(dev)
+        prm = K.make_params(wl.head_dim, wl.num_q_heads, wl.num_kv_heads, kb, wl.k_group, vb, wl.v_group, wl.window,
+                            0, K.KVQ_BF16, wl.block_size)
+        cb = K.CacheBuffers(prm, wl.batch, pool, table)
+        gen = DeviceGenerator(wl)
+        k_ref = gen.kv(W.TENSOR_K, 0, Lmax)
+        v_ref = gen.kv(W.TENSOR_V, 0, Lmax)
+        before = torch.zeros(wl.batch, dtype=torch.int32, device=dev)
+        n_new = torch.from_numpy(Lb.astype(np.int32)).to(dev)
+        K.kvq_quantize_append(prm, cb.struct, before, n_new, k_ref, v_ref, Lmax)
+        hs = torch.empty((wl.batch, wl.num_q_heads, K.KVQ_EB_HEAD), dtype=torch.float32, device=dev)
+        us = torch.empty((wl.batch, wl.num_kv_heads, K.KVQ_EB_UNIT), dtype=torch.float32, device=dev)
+        K.kvq_error_budget(prm, cb.struct, n_new, Lmax, k_ref, v_ref, gen.q(0), K.KVQ_BF16, 0.0, hs, us)
+        torch.cuda.synchronize()
+        h_ = hs.cpu().numpy().astype(np.float64)
+        u_ = us.cpu().numpy().astype(np.float64)
+        rows.append({
+            "k_bits": kb, "v_bits": vb, "payload_bits_per_key_value_pair": kb + vb,
+            "rel_reconstruction_error_keys": round(float(np.sqrt(u_[..., 0].sum() / u_[..., 4].sum())), 4),
+            "rel_reconstruction_error_values": round(float(np.sqrt(u_[..., 1].sum() / u_[..., 5].sum())), 4),
+            "median_rms_score_error": round(float(np.median(h_[..., 1])), 4),
+            "median_weight_total_variation": round(float(np.median(h_[..., 2])), 4),
+            "median_rel_output_error_values_only": round(float(np.median(h_[..., 3] / h_[..., 6])), 4),
+            "median_rel_output_error_keys_only": round(float(np.median(h_[..., 4] / h_[..., 6])), 4),
+            "median_rel_output_error_both": round(float(np.median(h_[..., 5] / h_[..., 6])), 4),
+        })
+        del cb, k_ref, v_ref, table
+        torch.cuda.synchronize()
+    return {"workload": W.WORKLOADS[4].name, "query": "decode step 0", "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -492,6 +540,7 @@ def main():
         res["unfused_baseline"] = unfused
     if errb is not None:
         res["error_budget"] = errb
+        res["error_budget_bit_pairs"] = error_budget_sweep(dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)
