@@ -106,3 +106,60 @@ def test_full_config5_rotated():
     run = GpuRun(wl, device_gen=True, chunk=4096)
     o32, obf = attend_both(run, 0)
     check_units(run, [(0, 0), (21, 3), (42, 5), (63, 7)], 0, o32, obf)
+
+
+def test_full_config3_unfused_and_error_budget():
+    """Batch 16, 32 q / 8 kv heads, 32768 tokens, window 128 (the bench's shape): the unfused
+    baseline and the error-budget diagnostics over the whole batch, checked on sampled units —
+    the dense bf16 cache bit for bit over every position of the unit, the dense attention of the
+    unit's query heads to the tolerance, and the diagnostics' statistics to relative 2e-3."""
+    import dataclasses
+
+    import mixed_precision_kv_kvq_amd as K
+    from kvq_harness import bf16_bits_rne_f64
+
+    wl = dataclasses.replace(W.WORKLOADS[3], steps=0)
+    run = GpuRun(wl, device_gen=True, chunk=4096)
+    L = run.current_lengths()
+    B, Hkv, Hq, d, g = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.group_q
+    Lmax = int(L.max())
+    say(f"unfused + error budget at B {B}, L {Lmax}")
+    seq_lens = torch.from_numpy(L.astype(np.int32)).cuda()
+    kd = torch.empty((B, Hkv, Lmax, d), dtype=torch.int16, device="cuda")
+    vd = torch.empty_like(kd)
+    K.kvq_dequantize_dense(run.params, run.cache.struct, seq_lens, Lmax, kd, vd)
+    wsb = K.kvq_dense_workspace_bytes(run.params, B, Lmax)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    o32 = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    q_dev = run._q_dev(0)
+    K.kvq_dense_decode_attention(run.params, B, kd, vd, seq_lens, Lmax, q_dev, K.KVQ_BF16, o32, K.KVQ_F32, 0.0, ws, wsb)
+    k_ref = run.dgen.kv(W.TENSOR_K, 0, Lmax)
+    v_ref = run.dgen.kv(W.TENSOR_V, 0, Lmax)
+    hs = torch.empty((B, Hq, K.KVQ_EB_HEAD), dtype=torch.float32, device="cuda")
+    us = torch.empty((B, Hkv, K.KVQ_EB_UNIT), dtype=torch.float32, device="cuda")
+    K.kvq_error_budget(run.params, run.cache.struct, seq_lens, Lmax, k_ref, v_ref, q_dev, K.KVQ_BF16, 0.0, hs, us)
+    torch.cuda.synchronize()
+    o32 = o32.cpu().numpy()
+    hs = hs.cpu().numpy().astype(np.float64)
+    us = us.cpu().numpy().astype(np.float64)
+    q = run.q_host(0).astype(np.float64)
+    scale = 1.0 / np.sqrt(d)
+    for b, kvh in [(0, 0), (9, 5), (15, 7)]:
+        Lb = int(L[b])
+        Kx = wl.kv_f32(W.TENSOR_K, b, kvh, 0, Lb).astype(np.float64)
+        Vx = wl.kv_f32(W.TENSOR_V, b, kvh, 0, Lb).astype(np.float64)
+        cache = O.build_unit_cache(Kx, Vx, Lb, oracle_params(wl))
+        kh = kd[b, kvh, :Lb].cpu().numpy().view(np.uint16)
+        vh = vd[b, kvh, :Lb].cpu().numpy().view(np.uint16)
+        assert np.array_equal(kh, bf16_bits_rne_f64(np.concatenate([cache["k_hat"], cache["k_win"]]))), (b, kvh)
+        assert np.array_equal(vh, bf16_bits_rne_f64(np.concatenate([cache["v_hat"], cache["v_win"]]))), (b, kvh)
+        Kd = W.bf16_bits_to_f32(kh).astype(np.float64)
+        Vd = W.bf16_bits_to_f32(vh).astype(np.float64)
+        ref = np.stack([O.attention(q[b, h], Kd, Vd, scale) for h in range(kvh * g, (kvh + 1) * g)])
+        maxabs, rel = assert_close(o32[b, kvh * g:(kvh + 1) * g], ref, f"dense attention ({b},{kvh})")
+        for h in range(kvh * g, (kvh + 1) * g):
+            head, unit = O.error_budget(q[b, h], Kx, Vx, cache, scale)
+            np.testing.assert_allclose(hs[b, h], head, rtol=2e-3, atol=2e-5, err_msg=f"head stats ({b},{h})")
+        np.testing.assert_allclose(us[b, kvh], unit, rtol=2e-3, atol=2e-5, err_msg=f"unit stats ({b},{kvh})")
+        say(f"unit ({b},{kvh}) L={Lb}: dense cache exact, dense attention max-abs {maxabs:.2e} rel-L2 {rel:.2e}, "
+            f"error budget within 2e-3")
