@@ -6,7 +6,7 @@
 
 namespace {
 
-constexpr int kNumCUs = 256;  // MI355X
+constexpr int kNumCUs = KVQ_NUM_CUS;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 

@@ -1098,7 +1098,21 @@ struct Kern {
     }
     const RecOff ro = rec_offsets<KS>(cx, lay);
     constexpr bool FIRST_ODD = (AHEAD & 1) != 0;  // parity of page 2i + AHEAD
+#if KVQ_SLOT_PRIO
+    // With two waves per SIMD the dispatcher gives every SIMD one wave before any gets a second
+    // (blocks 0 .. SIMDs - 1 first), and the older wave wins instruction arbitration: measured per
+    // wave at the 32k batch-16 launch, the second waves ended ≈9 µs after the first and set the
+    // kernel's end.  The second waves therefore issue at priority 1 for the first 5/8 of their
+    // pairs (measured best of 0, 2/8, 4/8, 5/8, 6/8 and all: 86.6 µs against 93.0 µs).  Timing
+    // only: which pages a wave reads, and so the result, does not change.
+    const bool late = WPE == 2 && blockIdx.x >= 4 * KVQ_NUM_CUS;
+    const int prio_until = (KVQ_SLOT_PRIO * npairs) / 8;
+    if (late) __builtin_amdgcn_s_setprio(1);
+#endif
     for (int i = 0; i < npairs; ++i) {
+#if KVQ_SLOT_PRIO
+      if (late && i == prio_until) __builtin_amdgcn_s_setprio(0);
+#endif
       const int k0 = 2 * i + AHEAD;
       if (k0 + 1 < npages) {  // steady state: two requests, AHEAD pages stay in flight
         issue(FIRST_ODD, k0);

@@ -116,6 +116,12 @@ __host__ __device__ constexpr int kvq_attn_wpe(int kb, int vb, int g, int p, int
 #ifndef KVQ_RING_MAX
 #define KVQ_RING_MAX 8  // most ring slots per wave
 #endif
+#define KVQ_NUM_CUS 256  // MI355X: 256 compute units, 4 SIMDs each
+// Split-kernel waves dispatched after every SIMD already holds one (block index >= the SIMD
+// count) run their first KVQ_SLOT_PRIO eighths of page pairs at raised issue priority (0 = off).
+#ifndef KVQ_SLOT_PRIO
+#define KVQ_SLOT_PRIO 5
+#endif
 #ifndef KVQ_SLOT_PAD
 #define KVQ_SLOT_PAD 1  // pad slots to whole DMAs when KVQ_RING_MAX of them still fit
 #endif
