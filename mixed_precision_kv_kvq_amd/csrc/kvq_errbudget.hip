@@ -71,21 +71,25 @@ __device__ __attribute__((always_inline)) inline void load8(const KvqErrArgs &a,
   }
 }
 
-// One workgroup of EB_WAVES waves per (query head, sequence); wave w takes positions 4 (w + k
-// EB_WAVES) + r, lane 16 r + c holding channels [8c, 8c + 8).  Pass 1: exact and quantized
-// scores with online maxima and sums (log2 units) and the score-error statistics; the first
-// query head of each kv head also accumulates the key reconstruction error.  The waves' maxima
-// and sums are merged through LDS (every wave merges them in the same order).  Pass 2: the
-// weights a (exact keys) and a' (quantized keys), their total variation, and the four weighted
-// sums a V, a V_hat, a' V, a' V_hat, merged over the waves through LDS at the end.
+// One workgroup of EB_WAVES waves per (group of HG query heads of one kv head, sequence); wave w
+// takes positions 4 (w + k EB_WAVES) + r, lane 16 r + c holding channels [8c, 8c + 8), so each
+// position's keys and values are decoded once for the HG heads.  Pass 1: exact and quantized
+// scores with online maxima and sums (log2 units) and the score-error statistics; the first head
+// group of each kv head also accumulates the key reconstruction error.  The waves' maxima and
+// sums are merged through LDS (every wave merges them in the same order).  Pass 2: the weights a
+// (exact keys) and a' (quantized keys), their total variation, and the four weighted sums a V,
+// a V_hat, a' V, a' V_hat, merged over the waves through LDS at the end.
 constexpr int EB_WAVES = 8;
+template <int HG>
 __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs a) {
-  __shared__ float red[EB_WAVES][8];
-  __shared__ float accs[4][KVQ_D];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = blockIdx.x, b = blockIdx.y;
+  __shared__ float red[EB_WAVES][6 * HG];
+  __shared__ float ured[EB_WAVES][6];
+  __shared__ float accs[4][HG][KVQ_D];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, b = blockIdx.y;
+  const int hq0 = blockIdx.x * HG;  // first query head of the group
   const int r = lane >> 4, c = lane & 15;
-  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, h = hq / g;
-  const bool unit_lead = (hq % g) == 0;
+  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, h = hq0 / g;
+  const bool unit_lead = (hq0 % g) == 0;
   int64_t L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   int64_t nq = L > a.R ? L - a.R : 0;
@@ -93,15 +97,17 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   if (nq > cap_tokens) nq = cap_tokens;
   const float ninf = -__builtin_inff();
 
-  float q[8];
-  {
-    const size_t qrow = ((size_t)b * a.Hq + hq) * KVQ_D + 8 * c;
+  float q[HG][8];
+#pragma unroll
+  for (int j = 0; j < HG; ++j) {
+    const size_t qrow = ((size_t)b * a.Hq + hq0 + j) * KVQ_D + 8 * c;
     if (a.q_f32) {
       const float4 *qp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow);
       const float4 x = qp[0], y = qp[1];
-      q[0] = x.x; q[1] = x.y; q[2] = x.z; q[3] = x.w; q[4] = y.x; q[5] = y.y; q[6] = y.z; q[7] = y.w;
+      q[j][0] = x.x; q[j][1] = x.y; q[j][2] = x.z; q[j][3] = x.w;
+      q[j][4] = y.x; q[j][5] = y.y; q[j][6] = y.z; q[j][7] = y.w;
     } else {
-      bf16x8(*reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qrow), q);
+      bf16x8(*reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qrow), q[j]);
     }
   }
   auto pos_of = [&](int64_t t) {
@@ -124,117 +130,133 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   const float sl2 = a.scale * 1.4426950408889634f;  // softmax scale in log2 units
 
   // ---- pass 1 ----
-  float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f;  // exact / quantized scores (log2 units)
-  float ds_max = 0.f, ds_sq = 0.f;                // score error (natural units)
-  float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;    // key reconstruction error (lead wave)
+  float m0[HG], z0[HG], m1[HG], z1[HG], ds_max[HG], ds_sq[HG];
+#pragma unroll
+  for (int j = 0; j < HG; ++j) {
+    m0[j] = m1[j] = ninf;
+    z0[j] = z1[j] = ds_max[j] = ds_sq[j] = 0.f;
+  }
+  float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;  // key reconstruction error (lead group)
   for (int64_t i0 = 4 * w; i0 < L; i0 += 4 * EB_WAVES) {
     const int64_t t = i0 + r;
     const Pos p = pos_of(t);
     float k[8], kh[8];
     load8<true>(a, p, ref_row(a.k_ref, t < L ? t : 0), c, k, kh);
-    float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      d0 = __builtin_fmaf(q[e], k[e], d0);
-      d1 = __builtin_fmaf(q[e], kh[e], d1);
+    for (int j = 0; j < HG; ++j) {
+      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        d0 = __builtin_fmaf(q[j][e], k[e], d0);
+        d1 = __builtin_fmaf(q[j][e], kh[e], d1);
+      }
+      d0 = row16_sum(d0);
+      d1 = row16_sum(d1);
+      if (p.valid) {
+        const float s0 = d0 * sl2, s1 = d1 * sl2;
+        const float n0 = __builtin_fmaxf(m0[j], s0), n1 = __builtin_fmaxf(m1[j], s1);
+        z0[j] = z0[j] * __builtin_amdgcn_exp2f(m0[j] - n0) + __builtin_amdgcn_exp2f(s0 - n0);
+        z1[j] = z1[j] * __builtin_amdgcn_exp2f(m1[j] - n1) + __builtin_amdgcn_exp2f(s1 - n1);
+        m0[j] = n0;
+        m1[j] = n1;
+        const float ds = (d1 - d0) * a.scale;
+        ds_max[j] = __builtin_fmaxf(ds_max[j], __builtin_fabsf(ds));
+        ds_sq[j] = __builtin_fmaf(ds, ds, ds_sq[j]);
+      }
     }
-    d0 = row16_sum(d0);
-    d1 = row16_sum(d1);
-    if (p.valid) {
-      const float s0 = d0 * sl2, s1 = d1 * sl2;
-      const float n0 = __builtin_fmaxf(m0, s0), n1 = __builtin_fmaxf(m1, s1);
-      z0 = z0 * __builtin_amdgcn_exp2f(m0 - n0) + __builtin_amdgcn_exp2f(s0 - n0);
-      z1 = z1 * __builtin_amdgcn_exp2f(m1 - n1) + __builtin_amdgcn_exp2f(s1 - n1);
-      m0 = n0;
-      m1 = n1;
-      const float ds = (d1 - d0) * a.scale;
-      ds_max = __builtin_fmaxf(ds_max, __builtin_fabsf(ds));
-      ds_sq = __builtin_fmaf(ds, ds, ds_sq);
-      if (unit_lead && p.quant) {
+    if (unit_lead && p.valid && p.quant) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float err = kh[e] - k[e];
-          ek_sq = __builtin_fmaf(err, err, ek_sq);
-          ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
-          k_sq = __builtin_fmaf(k[e], k[e], k_sq);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float err = kh[e] - k[e];
+        ek_sq = __builtin_fmaf(err, err, ek_sq);
+        ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
+        k_sq = __builtin_fmaf(k[e], k[e], k_sq);
       }
     }
   }
-  // combine the four position classes (lanes of one row hold equal values)
-  for (int off = 16; off <= 32; off <<= 1) {
-    const float om0 = __shfl_xor(m0, off), oz0 = __shfl_xor(z0, off);
-    const float om1 = __shfl_xor(m1, off), oz1 = __shfl_xor(z1, off);
-    const float n0 = __builtin_fmaxf(m0, om0), n1 = __builtin_fmaxf(m1, om1);
-    z0 = (n0 == ninf) ? 0.f : z0 * __builtin_amdgcn_exp2f(m0 - n0) + oz0 * __builtin_amdgcn_exp2f(om0 - n0);
-    z1 = (n1 == ninf) ? 0.f : z1 * __builtin_amdgcn_exp2f(m1 - n1) + oz1 * __builtin_amdgcn_exp2f(om1 - n1);
-    m0 = n0;
-    m1 = n1;
-    ds_max = __builtin_fmaxf(ds_max, __shfl_xor(ds_max, off));
-    ds_sq += __shfl_xor(ds_sq, off);
-  }
-  // merge the waves (same order in every wave)
-  if (lane == 0) {
-    red[w][0] = m0;
-    red[w][1] = z0;
-    red[w][2] = m1;
-    red[w][3] = z1;
-    red[w][4] = ds_max;
-    red[w][5] = ds_sq;
+  // combine the four position classes (lanes of one row hold equal values), then the waves
+#pragma unroll
+  for (int j = 0; j < HG; ++j) {
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float om0 = __shfl_xor(m0[j], off), oz0 = __shfl_xor(z0[j], off);
+      const float om1 = __shfl_xor(m1[j], off), oz1 = __shfl_xor(z1[j], off);
+      const float n0 = __builtin_fmaxf(m0[j], om0), n1 = __builtin_fmaxf(m1[j], om1);
+      z0[j] = (n0 == ninf) ? 0.f : z0[j] * __builtin_amdgcn_exp2f(m0[j] - n0) + oz0 * __builtin_amdgcn_exp2f(om0 - n0);
+      z1[j] = (n1 == ninf) ? 0.f : z1[j] * __builtin_amdgcn_exp2f(m1[j] - n1) + oz1 * __builtin_amdgcn_exp2f(om1 - n1);
+      m0[j] = n0;
+      m1[j] = n1;
+      ds_max[j] = __builtin_fmaxf(ds_max[j], __shfl_xor(ds_max[j], off));
+      ds_sq[j] += __shfl_xor(ds_sq[j], off);
+    }
+    if (lane == 0) {
+      red[w][6 * j + 0] = m0[j];
+      red[w][6 * j + 1] = z0[j];
+      red[w][6 * j + 2] = m1[j];
+      red[w][6 * j + 3] = z1[j];
+      red[w][6 * j + 4] = ds_max[j];
+      red[w][6 * j + 5] = ds_sq[j];
+    }
   }
   __syncthreads();
-  {
+#pragma unroll
+  for (int j = 0; j < HG; ++j) {
     float M0 = ninf, M1 = ninf;
     for (int i = 0; i < EB_WAVES; ++i) {
-      M0 = __builtin_fmaxf(M0, red[i][0]);
-      M1 = __builtin_fmaxf(M1, red[i][2]);
+      M0 = __builtin_fmaxf(M0, red[i][6 * j + 0]);
+      M1 = __builtin_fmaxf(M1, red[i][6 * j + 2]);
     }
     float Z0 = 0.f, Z1 = 0.f, dmx = 0.f, dsq = 0.f;
     for (int i = 0; i < EB_WAVES; ++i) {
-      if (red[i][0] != ninf) Z0 += red[i][1] * __builtin_amdgcn_exp2f(red[i][0] - M0);
-      if (red[i][2] != ninf) Z1 += red[i][3] * __builtin_amdgcn_exp2f(red[i][2] - M1);
-      dmx = __builtin_fmaxf(dmx, red[i][4]);
-      dsq += red[i][5];
+      if (red[i][6 * j + 0] != ninf) Z0 += red[i][6 * j + 1] * __builtin_amdgcn_exp2f(red[i][6 * j + 0] - M0);
+      if (red[i][6 * j + 2] != ninf) Z1 += red[i][6 * j + 3] * __builtin_amdgcn_exp2f(red[i][6 * j + 2] - M1);
+      dmx = __builtin_fmaxf(dmx, red[i][6 * j + 4]);
+      dsq += red[i][6 * j + 5];
     }
-    m0 = M0;
-    z0 = Z0;
-    m1 = M1;
-    z1 = Z1;
-    ds_max = dmx;
-    ds_sq = dsq;
+    m0[j] = M0;
+    m1[j] = M1;
+    z0[j] = Z0 > 0.f ? 1.f / Z0 : 0.f;  // from here on: reciprocal sums
+    z1[j] = Z1 > 0.f ? 1.f / Z1 : 0.f;
+    ds_max[j] = dmx;
+    ds_sq[j] = dsq;
   }
   __syncthreads();
 
   // ---- pass 2 ----
-  const float iz0 = z0 > 0.f ? 1.f / z0 : 0.f, iz1 = z1 > 0.f ? 1.f / z1 : 0.f;
-  float tv = 0.f;
-  float ev_sq = 0.f, ev_max = 0.f, v_sq = 0.f;
-  float o[8], ov[8], ok[8], oj[8];
+  float tv[HG];
+  float o[HG][8], ov[HG][8], ok[HG][8], oj[HG][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = ov[e] = ok[e] = oj[e] = 0.f;
+  for (int j = 0; j < HG; ++j) {
+    tv[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = ov[j][e] = ok[j][e] = oj[j][e] = 0.f;
+  }
+  float ev_sq = 0.f, ev_max = 0.f, v_sq = 0.f;
   for (int64_t i0 = 4 * w; i0 < L; i0 += 4 * EB_WAVES) {
     const int64_t t = i0 + r;
     const Pos p = pos_of(t);
     float k[8], kh[8], v[8], vh[8];
     load8<true>(a, p, ref_row(a.k_ref, t < L ? t : 0), c, k, kh);
     load8<false>(a, p, ref_row(a.v_ref, t < L ? t : 0), c, v, vh);
-    float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      d0 = __builtin_fmaf(q[e], k[e], d0);
-      d1 = __builtin_fmaf(q[e], kh[e], d1);
-    }
-    d0 = row16_sum(d0);
-    d1 = row16_sum(d1);
-    const float w0 = p.valid ? __builtin_amdgcn_exp2f(d0 * sl2 - m0) * iz0 : 0.f;
-    const float w1 = p.valid ? __builtin_amdgcn_exp2f(d1 * sl2 - m1) * iz1 : 0.f;
-    if (c == 0) tv += __builtin_fabsf(w1 - w0);
+    for (int j = 0; j < HG; ++j) {
+      float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[e] = __builtin_fmaf(w0, v[e], o[e]);
-      ov[e] = __builtin_fmaf(w0, vh[e], ov[e]);
-      ok[e] = __builtin_fmaf(w1, v[e], ok[e]);
-      oj[e] = __builtin_fmaf(w1, vh[e], oj[e]);
+      for (int e = 0; e < 8; ++e) {
+        d0 = __builtin_fmaf(q[j][e], k[e], d0);
+        d1 = __builtin_fmaf(q[j][e], kh[e], d1);
+      }
+      d0 = row16_sum(d0);
+      d1 = row16_sum(d1);
+      const float w0 = p.valid ? __builtin_amdgcn_exp2f(d0 * sl2 - m0[j]) * z0[j] : 0.f;
+      const float w1 = p.valid ? __builtin_amdgcn_exp2f(d1 * sl2 - m1[j]) * z1[j] : 0.f;
+      if (c == 0) tv[j] += __builtin_fabsf(w1 - w0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[j][e] = __builtin_fmaf(w0, v[e], o[j][e]);
+        ov[j][e] = __builtin_fmaf(w0, vh[e], ov[j][e]);
+        ok[j][e] = __builtin_fmaf(w1, v[e], ok[j][e]);
+        oj[j][e] = __builtin_fmaf(w1, vh[e], oj[j][e]);
+      }
     }
     if (unit_lead && p.valid && p.quant) {
 #pragma unroll
@@ -248,17 +270,20 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   }
   // sums over the position classes, then over the waves (one wave at a time into LDS)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    o[e] += __shfl_xor(o[e], 16);
-    o[e] += __shfl_xor(o[e], 32);
-    ov[e] += __shfl_xor(ov[e], 16);
-    ov[e] += __shfl_xor(ov[e], 32);
-    ok[e] += __shfl_xor(ok[e], 16);
-    ok[e] += __shfl_xor(ok[e], 32);
-    oj[e] += __shfl_xor(oj[e], 16);
-    oj[e] += __shfl_xor(oj[e], 32);
+  for (int j = 0; j < HG; ++j) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[j][e] += __shfl_xor(o[j][e], 16);
+      o[j][e] += __shfl_xor(o[j][e], 32);
+      ov[j][e] += __shfl_xor(ov[j][e], 16);
+      ov[j][e] += __shfl_xor(ov[j][e], 32);
+      ok[j][e] += __shfl_xor(ok[j][e], 16);
+      ok[j][e] += __shfl_xor(ok[j][e], 32);
+      oj[j][e] += __shfl_xor(oj[j][e], 16);
+      oj[j][e] += __shfl_xor(oj[j][e], 32);
+    }
+    for (int off = 1; off <= 32; off <<= 1) tv[j] += __shfl_xor(tv[j], off);
   }
-  for (int off = 1; off <= 32; off <<= 1) tv += __shfl_xor(tv, off);
   if (unit_lead) {
     for (int off = 1; off <= 32; off <<= 1) {
       ek_sq += __shfl_xor(ek_sq, off);
@@ -270,79 +295,92 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     }
   }
   if (lane == 0) {
-    red[w][0] = tv;
-    red[w][1] = ek_sq;
-    red[w][2] = ev_sq;
-    red[w][3] = ek_max;
-    red[w][4] = ev_max;
-    red[w][5] = k_sq;
-    red[w][6] = v_sq;
+#pragma unroll
+    for (int j = 0; j < HG; ++j) red[w][j] = tv[j];
+    ured[w][0] = ek_sq;
+    ured[w][1] = ev_sq;
+    ured[w][2] = ek_max;
+    ured[w][3] = ev_max;
+    ured[w][4] = k_sq;
+    ured[w][5] = v_sq;
   }
   for (int i = 0; i < EB_WAVES; ++i) {
     if (w == i && r == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ch = 8 * c + e;
-        accs[0][ch] = (i == 0 ? 0.f : accs[0][ch]) + o[e];
-        accs[1][ch] = (i == 0 ? 0.f : accs[1][ch]) + ov[e];
-        accs[2][ch] = (i == 0 ? 0.f : accs[2][ch]) + ok[e];
-        accs[3][ch] = (i == 0 ? 0.f : accs[3][ch]) + oj[e];
+      for (int j = 0; j < HG; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ch = 8 * c + e;
+          accs[0][j][ch] = (i == 0 ? 0.f : accs[0][j][ch]) + o[j][e];
+          accs[1][j][ch] = (i == 0 ? 0.f : accs[1][j][ch]) + ov[j][e];
+          accs[2][j][ch] = (i == 0 ? 0.f : accs[2][j][ch]) + ok[j][e];
+          accs[3][j][ch] = (i == 0 ? 0.f : accs[3][j][ch]) + oj[j][e];
+        }
       }
     }
     __syncthreads();
   }
-  if (w != 0) return;
-  tv = 0.f;
-  ek_sq = ev_sq = ek_max = ev_max = k_sq = v_sq = 0.f;
-  for (int i = 0; i < EB_WAVES; ++i) {
-    tv += red[i][0];
-    ek_sq += red[i][1];
-    ev_sq += red[i][2];
-    ek_max = __builtin_fmaxf(ek_max, red[i][3]);
-    ev_max = __builtin_fmaxf(ev_max, red[i][4]);
-    k_sq += red[i][5];
-    v_sq += red[i][6];
-  }
-  // norms over the channels: lane l takes channels l and l + 64
-  float nv = 0.f, nk = 0.f, nj = 0.f, no = 0.f;
-  for (int ch = lane; ch < KVQ_D; ch += 64) {
-    const float oo = accs[0][ch];
-    const float dv = accs[1][ch] - oo, dk = accs[2][ch] - oo, dj = accs[3][ch] - oo;
-    nv = __builtin_fmaf(dv, dv, nv);
-    nk = __builtin_fmaf(dk, dk, nk);
-    nj = __builtin_fmaf(dj, dj, nj);
-    no = __builtin_fmaf(oo, oo, no);
-  }
-  for (int off = 1; off <= 32; off <<= 1) {
-    nv += __shfl_xor(nv, off);
-    nk += __shfl_xor(nk, off);
-    nj += __shfl_xor(nj, off);
-    no += __shfl_xor(no, off);
-  }
-  float *hs = a.head_stats + ((size_t)b * a.Hq + hq) * KVQ_EB_HEAD;
-  if (lane == 0) {
-    const float n = (float)L;
-    hs[0] = ds_max;
-    hs[1] = L > 0 ? sqrtf(ds_sq / n) : 0.f;
-    hs[2] = 0.5f * tv;
-    hs[3] = sqrtf(nv);
-    hs[4] = sqrtf(nk);
-    hs[5] = sqrtf(nj);
-    hs[6] = sqrtf(no);
-    hs[7] = 0.f;
-  }
-  if (unit_lead) {
-    float *us = a.unit_stats + ((size_t)b * Hkv + h) * KVQ_EB_UNIT;
-    if (lane == 0) {
-      us[0] = ek_sq;
-      us[1] = ev_sq;
-      us[2] = ek_max;
-      us[3] = ev_max;
-      us[4] = k_sq;
-      us[5] = v_sq;
-      us[6] = (float)nq;
-      us[7] = 0.f;
+  // wave j < HG finishes head j: norms over the channels (lane l takes channels l and l + 64)
+  if (w < HG) {
+    const int j = w;
+    float tvj = 0.f;
+    for (int i = 0; i < EB_WAVES; ++i) tvj += red[i][j];
+    float nv = 0.f, nk = 0.f, nj = 0.f, no = 0.f;
+    for (int ch = lane; ch < KVQ_D; ch += 64) {
+      const float oo = accs[0][j][ch];
+      const float dv = accs[1][j][ch] - oo, dk = accs[2][j][ch] - oo, dj = accs[3][j][ch] - oo;
+      nv = __builtin_fmaf(dv, dv, nv);
+      nk = __builtin_fmaf(dk, dk, nk);
+      nj = __builtin_fmaf(dj, dj, nj);
+      no = __builtin_fmaf(oo, oo, no);
     }
+    for (int off = 1; off <= 32; off <<= 1) {
+      nv += __shfl_xor(nv, off);
+      nk += __shfl_xor(nk, off);
+      nj += __shfl_xor(nj, off);
+      no += __shfl_xor(no, off);
+    }
+    // the head's pass-1 statistics: every wave merged them identically
+    float dmx = 0.f, dsq = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < HG; ++jj) {
+      if (jj == j) {
+        dmx = ds_max[jj];
+        dsq = ds_sq[jj];
+      }
+    }
+    float *hs = a.head_stats + ((size_t)b * a.Hq + hq0 + j) * KVQ_EB_HEAD;
+    if (lane == 0) {
+      const float n = (float)L;
+      hs[0] = dmx;
+      hs[1] = L > 0 ? sqrtf(dsq / n) : 0.f;
+      hs[2] = 0.5f * tvj;
+      hs[3] = sqrtf(nv);
+      hs[4] = sqrtf(nk);
+      hs[5] = sqrtf(nj);
+      hs[6] = sqrtf(no);
+      hs[7] = 0.f;
+    }
+  }
+  if (unit_lead && w == 0 && lane == 0) {
+    float s[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < EB_WAVES; ++i) {
+      s[0] += ured[i][0];
+      s[1] += ured[i][1];
+      s[2] = __builtin_fmaxf(s[2], ured[i][2]);
+      s[3] = __builtin_fmaxf(s[3], ured[i][3]);
+      s[4] += ured[i][4];
+      s[5] += ured[i][5];
+    }
+    float *us = a.unit_stats + ((size_t)b * Hkv + h) * KVQ_EB_UNIT;
+    us[0] = s[0];
+    us[1] = s[1];
+    us[2] = s[2];
+    us[3] = s[3];
+    us[4] = s[4];
+    us[5] = s[5];
+    us[6] = (float)nq;
+    us[7] = 0.f;
   }
 }
 
@@ -351,6 +389,12 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
 hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
-  hipLaunchKernelGGL(kvq_errbudget_kernel, dim3((unsigned)a.Hq, (unsigned)a.B), dim3(64 * EB_WAVES), 0, s, a);
+  // two heads per group: four would need more than the 256 registers of two waves per SIMD
+  const int g = a.Hq / a.Hkv, hg = g < 2 ? g : 2;
+  const dim3 grid((unsigned)(a.Hq / hg), (unsigned)a.B), block(64 * EB_WAVES);
+  if (hg == 1)
+    hipLaunchKernelGGL(kvq_errbudget_kernel<1>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(kvq_errbudget_kernel<2>, grid, block, 0, s, a);
   return hipGetLastError();
 }
