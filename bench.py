@@ -470,7 +470,7 @@ def main():
         eb_bytes = B * Hkv * (L_last * 2 * d * 2 + nq_last * per_th_q)  # originals and the store, read once
         errb = {
             "what": "kvq_error_budget at the last step's state against the original bf16 rows (8 waves per pair of "
-                    "query head, two passes), 3 launches between two events",
+                    "query heads, two passes), 3 launches between two events",
             "us": round(eb_us, 1), "unit_bytes_read_once": int(eb_bytes),
             "GBs_vs_read_once": round(eb_bytes / (eb_us * 1e-6) / 1e9, 1),
             "median_over_heads": {
