@@ -202,6 +202,7 @@ def build_unit_cache(K: np.ndarray, V: np.ndarray, L: int, wl_params: dict):
     vc, vs, vz = quantize(Vq, wl_params["v_bits"], wl_params["v_group"])
     return dict(
         nq=nq,
+        k_rotated=bool(wl_params["rotation"]),
         v_rotated=v_rot,
         k_codes=kc, k_scale=ks, k_zero=kz,
         v_codes=vc, v_scale=vs, v_zero=vz,
@@ -274,10 +275,12 @@ def decode_attention(q: np.ndarray, caches: list, num_kv_heads: int, scale: floa
 # separate key and value error budgets)
 # --------------------------------------------------------------------------
 def error_budget(q: np.ndarray, K: np.ndarray, V: np.ndarray, cache: dict, scale: float):
-    """Error statistics of one query head against one unit cache (no rotation).
+    """Error statistics of one query head against one unit cache.
 
     K, V: the original [L][d] rows; cache: build_unit_cache of the same rows.
     Window positions are stored exactly, so their reconstruction is the row.
+    Reconstructions of rotated tensors are rotated back first (the transform is
+    its own inverse): every error is taken in the original domain.
     Returns (head, unit):
       head = [max |s' - s|, rms (s' - s), TV(a', a), |a V_hat - a V|,
               |a' V - a V|, |a' V_hat - a V|, |a V|, 0]
@@ -288,21 +291,21 @@ def error_budget(q: np.ndarray, K: np.ndarray, V: np.ndarray, cache: dict, scale
               number of quantized positions, 0] over the quantized positions.
     An empty sequence gives zeros.
     """
-    if cache.get("v_rotated", False):
-        raise ValueError("error budgets are defined here for unrotated caches")
     nq = cache["nq"]
     K = np.asarray(K, dtype=F64)
     V = np.asarray(V, dtype=F64)
     L = K.shape[0]
-    EK = cache["k_hat"] - K[:nq]
-    EV = cache["v_hat"] - V[:nq]
+    k_hat = wht_rotate(cache["k_hat"]) if cache.get("k_rotated", False) else cache["k_hat"]
+    v_hat = wht_rotate(cache["v_hat"]) if cache.get("v_rotated", False) else cache["v_hat"]
+    EK = k_hat - K[:nq]
+    EV = v_hat - V[:nq]
     unit = np.array([np.sum(EK * EK), np.sum(EV * EV),
                      np.max(np.abs(EK)) if nq else 0.0, np.max(np.abs(EV)) if nq else 0.0,
                      np.sum(K[:nq] ** 2), np.sum(V[:nq] ** 2), float(nq), 0.0])
     if L == 0:
         return np.zeros(8), unit
-    K_hat = np.concatenate([cache["k_hat"], K[nq:]])
-    V_hat = np.concatenate([cache["v_hat"], V[nq:]])
+    K_hat = np.concatenate([k_hat, K[nq:]])
+    V_hat = np.concatenate([v_hat, V[nq:]])
     q = np.asarray(q, dtype=F64)
     s = (K @ q) * scale
     s_q = (K_hat @ q) * scale

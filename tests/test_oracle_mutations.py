@@ -145,8 +145,17 @@ def mut_error_budget_weights_from_quantized_keys(M):
     M.error_budget = error_budget
 
 
+def mut_error_budget_rotated_domain(M):
+    orig = M.error_budget
+
+    def error_budget(q, K, V, cache, scale):
+        c = dict(cache, k_rotated=False)  # mistake: rotated keys compared in the rotated domain
+        return orig(q, K, V, c, scale)
+    M.error_budget = error_budget
+
+
 MUTATIONS = [
-    mut_error_budget_weights_from_quantized_keys, mut_value_rotation_not_undone, mut_zero_round_nearest, mut_scale_round_nearest, mut_round_half_up, mut_dequant_sign,
+    mut_error_budget_rotated_domain, mut_error_budget_weights_from_quantized_keys, mut_value_rotation_not_undone, mut_zero_round_nearest, mut_scale_round_nearest, mut_round_half_up, mut_dequant_sign,
     mut_dequant_group_index, mut_attention_no_scale, mut_attention_reversed_values, mut_gqa_modulo,
     mut_window_off_by_one, mut_wht_no_normalization, mut_wht_constant_low, mut_softmax_no_max_shift_wrong_axis,
 ]

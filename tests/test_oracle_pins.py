@@ -452,6 +452,19 @@ def check_error_budget(O_):
         assert abs(unit[1] - np.sum((Vh - V) ** 2)) < 1e-12 * max(1.0, unit[1])
         assert unit[2] == np.max(np.abs(Kh - K)) and head[0] == np.max(np.abs((Kh - K) @ q * sc))
         assert head[3] > 0 and head[4] > 0
+    # rotated caches: the same statistics as an unrotated cache holding the hats rotated back
+    # with scipy's (normalized) Hadamard matrix, a route independent of the oracle's butterflies
+    from scipy.linalg import hadamard
+    H = hadamard(128) / np.sqrt(128.0)
+    for rot, vrot in ((True, False), (False, True), (True, True)):
+        prm = dict(_params(R=0, rot=rot, kb=4, vb=2), value_rotation=vrot)
+        cache = O_.build_unit_cache(K, V, L, prm)
+        plain = dict(nq=L, k_hat=cache["k_hat"] @ H if rot else cache["k_hat"],
+                     v_hat=cache["v_hat"] @ H if vrot else cache["v_hat"], k_win=K[L:], v_win=V[L:])
+        head, unit = O_.error_budget(q, K, V, cache, sc)
+        head_p, unit_p = O_.error_budget(q, K, V, plain, sc)
+        assert np.allclose(head, head_p, rtol=1e-10, atol=1e-12) and np.allclose(unit, unit_p, rtol=1e-10, atol=1e-12)
+        assert head[3] > 0 and head[4] > 0
     empty = O_.build_unit_cache(K[:0], V[:0], 0, _params())
     head, unit = O_.error_budget(q, K[:0], V[:0], empty, sc)
     assert np.all(head == 0) and np.all(unit == 0)
