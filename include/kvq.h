@@ -241,8 +241,9 @@ kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, c
  * and unit_stats[b][kv][0..7] (device fp32, 16-byte aligned) the reconstruction errors over the
  * quantized positions {sum (k_hat - k)^2, sum (v_hat - v)^2, max |k_hat - k|, max |v_hat - v|,
  *    sum k^2, sum v^2, number of quantized positions, 0}.
- * fp32 arithmetic, reconstructions zero + code * scale rounded to fp32.  Caches with key or
- * value rotation: KVQ_EUNSUPPORTED.  Errors otherwise as for kvq_decode_attention. */
+ * fp32 arithmetic, reconstructions zero + code * scale rounded to fp32.  Reconstructions of
+ * rotated keys or values are rotated back first: every error is taken in the original domain.
+ * Errors as for kvq_decode_attention. */
 #define KVQ_EB_HEAD 8
 #define KVQ_EB_UNIT 8
 kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,

@@ -374,7 +374,6 @@ kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, co
                             hipStream_t stream) {
   if (kvq_status st = check_params(params)) return st;
   if (kvq_status st = check_cache(params, cache)) return st;
-  if (params->key_rotation || params->value_rotation) return KVQ_EUNSUPPORTED;
   if (!seq_lens || max_seq_len < 0 || max_seq_len > INT32_MAX) return KVQ_EINVAL;
   if (!k_ref || !v_ref || !q || !head_stats || !unit_stats) return KVQ_EINVAL;
   if (!aligned16(k_ref) || !aligned16(v_ref) || !aligned16(q) || !aligned16(head_stats) || !aligned16(unit_stats))
@@ -396,6 +395,8 @@ kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, co
   a.Hkv = params->num_kv_heads;
   a.R = params->window;
   a.q_f32 = q_dtype == KVQ_F32;
+  a.rotation = params->key_rotation;
+  a.value_rotation = params->value_rotation;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
   return hip_status(kvq_launch_errbudget(a, stream));
 }

@@ -31,6 +31,55 @@ __device__ inline float row16_sum(float v) {
   return v;
 }
 
+// Normalized 128-point Walsh-Hadamard transform of a row held as 8 channels [8c, 8c + 8) in
+// each of the 16 lanes of a lane row (c = lane mod 16), fp32: butterflies in stage order 1, 2,
+// 4 inside the lane, then 8, 16, 32, 64 across lanes c ^ 1, c ^ 2, c ^ 4, c ^ 8.  Every lane of
+// the wave must take part (cross-lane reads).
+__device__ __attribute__((always_inline)) inline void row_wht(float *x, int c) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if ((e & h) == 0) {
+        const float u = x[e], v = x[e + h];
+        x[e] = u + v;
+        x[e + h] = u - v;
+      }
+    }
+  }
+#pragma unroll
+  for (int lx = 1; lx < 16; lx <<= 1) {
+    const bool upper = (c & lx) != 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __shfl_xor(x[e], lx);
+      x[e] = upper ? p - x[e] : x[e] + p;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= (float)KVQ_WHT_C;
+}
+
+// The same transform for a row held as channels 2l, 2l + 1 in lane l of the wave: stage 1 inside
+// the lane, stages 2 .. 64 across lanes l ^ (h / 2).
+__device__ __attribute__((always_inline)) inline void pair_wht(float &x0, float &x1, int lane) {
+  {
+    const float u = x0, v = x1;
+    x0 = u + v;
+    x1 = u - v;
+  }
+#pragma unroll
+  for (int h = 2; h < KVQ_D; h <<= 1) {
+    const int lx = h >> 1;
+    const float p0 = __shfl_xor(x0, lx), p1 = __shfl_xor(x1, lx);
+    const bool upper = (lane & lx) != 0;
+    x0 = upper ? p0 - x0 : x0 + p0;
+    x1 = upper ? p1 - x1 : x1 + p1;
+  }
+  x0 *= (float)KVQ_WHT_C;
+  x1 *= (float)KVQ_WHT_C;
+}
+
 struct Pos {
   bool valid, quant;
   const uint8_t *rec;  // page record of a quantized position
@@ -110,6 +159,14 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       bf16x8(*reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qrow), q[j]);
     }
   }
+  // Rotated keys are scored with the rotated query: (H q).(H k) = q.k.  Window keys stay raw.
+  float qr[HG][8];
+#pragma unroll
+  for (int j = 0; j < HG; ++j) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qr[j][e] = q[j][e];
+    if (a.rotation) row_wht(qr[j], c);
+  }
   auto pos_of = [&](int64_t t) {
     Pos p;
     p.valid = t < L;
@@ -142,13 +199,14 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     const Pos p = pos_of(t);
     float k[8], kh[8];
     load8<true>(a, p, ref_row(a.k_ref, t < L ? t : 0), c, k, kh);
+    const bool krot = a.rotation && p.quant;  // uniform over the lane row of one position
 #pragma unroll
     for (int j = 0; j < HG; ++j) {
       float d0 = 0.f, d1 = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         d0 = __builtin_fmaf(q[j][e], k[e], d0);
-        d1 = __builtin_fmaf(q[j][e], kh[e], d1);
+        d1 = __builtin_fmaf(krot ? qr[j][e] : q[j][e], kh[e], d1);
       }
       d0 = row16_sum(d0);
       d1 = row16_sum(d1);
@@ -164,6 +222,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
         ds_sq[j] = __builtin_fmaf(ds, ds, ds_sq[j]);
       }
     }
+    if (unit_lead && a.rotation) row_wht(kh, c);  // reconstruction in the original domain
     if (unit_lead && p.valid && p.quant) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -237,13 +296,14 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     float k[8], kh[8], v[8], vh[8];
     load8<true>(a, p, ref_row(a.k_ref, t < L ? t : 0), c, k, kh);
     load8<false>(a, p, ref_row(a.v_ref, t < L ? t : 0), c, v, vh);
+    const bool krot = a.rotation && p.quant;
 #pragma unroll
     for (int j = 0; j < HG; ++j) {
       float d0 = 0.f, d1 = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         d0 = __builtin_fmaf(q[j][e], k[e], d0);
-        d1 = __builtin_fmaf(q[j][e], kh[e], d1);
+        d1 = __builtin_fmaf(krot ? qr[j][e] : q[j][e], kh[e], d1);
       }
       d0 = row16_sum(d0);
       d1 = row16_sum(d1);
@@ -258,6 +318,9 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
         oj[j][e] = __builtin_fmaf(w1, vh[e], oj[j][e]);
       }
     }
+    // With rotated values the sums over vh are in the rotated domain (rotated back per head at
+    // the end; no recent window then); the reconstruction statistics rotate each position back.
+    if (unit_lead && a.value_rotation) row_wht(vh, c);
     if (unit_lead && p.valid && p.quant) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -325,10 +388,24 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     const int j = w;
     float tvj = 0.f;
     for (int i = 0; i < EB_WAVES; ++i) tvj += red[i][j];
+    // lane l takes channels 2l, 2l + 1; sums over rotated values are rotated back first
+    float o2[2], v2[2], k2[2], j2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      o2[e] = accs[0][j][2 * lane + e];
+      v2[e] = accs[1][j][2 * lane + e];
+      k2[e] = accs[2][j][2 * lane + e];
+      j2[e] = accs[3][j][2 * lane + e];
+    }
+    if (a.value_rotation) {
+      pair_wht(v2[0], v2[1], lane);
+      pair_wht(j2[0], j2[1], lane);
+    }
     float nv = 0.f, nk = 0.f, nj = 0.f, no = 0.f;
-    for (int ch = lane; ch < KVQ_D; ch += 64) {
-      const float oo = accs[0][j][ch];
-      const float dv = accs[1][j][ch] - oo, dk = accs[2][j][ch] - oo, dj = accs[3][j][ch] - oo;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float oo = o2[e];
+      const float dv = v2[e] - oo, dk = k2[e] - oo, dj = j2[e] - oo;
       nv = __builtin_fmaf(dv, dv, nv);
       nk = __builtin_fmaf(dk, dk, nk);
       nj = __builtin_fmaf(dj, dj, nj);

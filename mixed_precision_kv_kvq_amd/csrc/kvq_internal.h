@@ -193,6 +193,7 @@ struct KvqErrArgs {
   float *head_stats, *unit_stats;
   int64_t max_len;
   int32_t B, Hq, Hkv, R, q_f32;
+  int32_t rotation, value_rotation;  // stored keys / values are rotated
   float scale;
 };
 hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s);

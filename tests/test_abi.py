@@ -214,8 +214,6 @@ def test_error_budget_validation():
         return L.kvq_error_budget(ctypes.byref(prm_ or p()), ctypes.byref(c or cache()), seq, mx, kr, vr, q, qd, sc,
                                   hs, us, None)
 
-    assert call(prm_=p(key_rotation=1)) == K.KVQ_EUNSUPPORTED
-    assert call(prm_=p(value_rotation=1)) == K.KVQ_EUNSUPPORTED
     assert call(seq=None) == K.KVQ_EINVAL
     assert call(kr=None) == K.KVQ_EINVAL
     assert call(vr=FAKE + 2) == K.KVQ_EINVAL

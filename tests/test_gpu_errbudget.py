@@ -32,6 +32,9 @@ CASES = {
     "g8-vgroup64": dict(context=170, num_q_heads=16, num_kv_heads=2, v_group=64),
     "f32-query": dict(context=160, q_dtype="f32"),
     "g1": dict(context=150, num_q_heads=8, num_kv_heads=8),
+    "rotated-keys-window": dict(context=260, window=24, rotation=True),
+    "rotated-values": dict(context=230, value_rotation=True),
+    "rotated-both-g8": dict(context=200, num_q_heads=16, num_kv_heads=2, rotation=True, value_rotation=True),
     "g2-window": dict(context=220, num_q_heads=16, num_kv_heads=8, window=24),
     "paged-window": dict(context=0, var_len=(1, 300), block_size=16, window=16, batch=4),
     "ragged-lengths-with-empty": dict(context=0, var_len=(0, 600), batch=4),
