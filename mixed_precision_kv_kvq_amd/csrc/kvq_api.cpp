@@ -2,7 +2,7 @@
 #include <math.h>
 #include <stdlib.h>
 
-#include "kvq_internal.h"
+#include "kvq_extras.h"
 
 namespace {
 

@@ -6,7 +6,7 @@
 // section "Evaluasi harus sesuai dengan besaran yang ingin dipertahankan" (judge the attention
 // quantities, not only reconstruction error); the nalar.dev tag page's entries on separate key
 // and value error budgets.
-#include "kvq_internal.h"
+#include "kvq_extras.h"
 
 #pragma clang fp contract(off)
 

@@ -6,7 +6,7 @@
 // measures what the fused kernel gains.  Dequantization follows section "Granularitas kuantisasi
 // menentukan nilai yang berbagi scale" (x_hat = zero + code * scale); attention follows section
 // "Error pada key masuk sebelum softmax" (s = q K^T / sqrt(d), a = softmax(s), o = a V).
-#include "kvq_internal.h"
+#include "kvq_extras.h"
 
 #pragma clang fp contract(off)
 
