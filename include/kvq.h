@@ -184,6 +184,25 @@ kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache,
 kvq_status kvq_decode_combine(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype,
                               const void *workspace, void *out, int32_t out_dtype, hipStream_t stream);
 
+/* Decode attention that allocates nothing, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and launches as kvq_decode_attention, with the partial rows kept in a
+ * device array inside the library instead of a caller workspace.  Arguments as for
+ * kvq_decode_attention without workspace/workspace_bytes.
+ *   Limit: kvq_decode_workspace_bytes(params, batch, max_seq_len) must not exceed
+ *   KVQ_NOALLOC_SCRATCH_BYTES (16 MiB: every workload up to batch 64 x 64 query heads x 131072
+ *   tokens fits); larger calls return KVQ_ENOSPACE and launch nothing.
+ *   Each GPU holds one copy of the array from the first call on it until the process ends; the
+ *   first call on a GPU looks up that copy's address (no allocation).  All calls on one GPU
+ *   share the array and keep nothing from one call to the next, so calls that may overlap in
+ *   time on one GPU (different streams without ordering) race and must not be issued.
+ *   The stream's device is the device used (the current device for the null stream).  Errors as
+ *   for kvq_decode_attention, KVQ_EHIP also when the array's address cannot be obtained. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                                        int64_t max_seq_len, const void *q, int32_t q_dtype, void *out,
+                                        int32_t out_dtype, float softmax_scale, hipStream_t stream);
+
 /* Read back n positions [t0, t0 + n) of sequence `seq` in logical order (debug
  * and verification).  Any output pointer may be NULL.
  *   k_codes, v_codes: device uint8 [n][num_kv_heads][128]; 0xFF for window tokens and t >= L.

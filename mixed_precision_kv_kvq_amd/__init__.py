@@ -33,6 +33,7 @@ EXPORTED = [
     "kvq_decode_splits",
     "kvq_decode_partials",
     "kvq_decode_combine",
+    "kvq_decode_attention_noalloc",
     "kvq_dequantize_debug",
     "kvq_dequantize_dense",
     "kvq_dense_workspace_bytes",
@@ -107,6 +108,9 @@ def _load():
     lib.kvq_decode_combine.argtypes = [P(kvq_params), c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int32,
                                        c_void_p]
     lib.kvq_decode_combine.restype = c_int32
+    lib.kvq_decode_attention_noalloc.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_int32,
+                                                 c_void_p, c_int32, c_float, c_void_p]
+    lib.kvq_decode_attention_noalloc.restype = c_int32
     lib.kvq_dequantize_debug.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int32, c_int64, c_int64, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.kvq_dequantize_debug.restype = c_int32
@@ -165,6 +169,7 @@ def bound_call(name: str, *args, stream=None):
     conv = [ctypes.byref(a) if isinstance(a, ctypes.Structure) else _ptr(a) if hasattr(a, "data_ptr") else a
             for a in args]
     if name in ("kvq_quantize_append", "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine",
+                "kvq_decode_attention_noalloc",
                 "kvq_dequantize_dense", "kvq_dense_decode_attention", "kvq_error_budget"):
         conv.append(_stream(stream))
     conv = tuple(conv)
@@ -228,6 +233,19 @@ def kvq_decode_combine(params, batch, max_seq_len, q_dtype, workspace, out, out_
                                  _ptr(out), int(out_dtype), _stream(stream))
     if check:
         _check(st, "kvq_decode_combine")
+    return st
+
+
+KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20  # device array behind kvq_decode_attention_noalloc
+
+
+def kvq_decode_attention_noalloc(params, cache, seq_lens, max_seq_len, q, q_dtype, out, out_dtype, softmax_scale,
+                                 stream=None, check=True):
+    st = _lib.kvq_decode_attention_noalloc(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens),
+                                           int(max_seq_len), _ptr(q), int(q_dtype), _ptr(out), int(out_dtype),
+                                           float(softmax_scale), _stream(stream))
+    if check:
+        _check(st, "kvq_decode_attention_noalloc")
     return st
 
 

@@ -278,3 +278,19 @@ def test_bound_call_marshals_once_and_raises():
     assert e.value.status == K.KVQ_EINVAL
     ok = K.bound_call("kvq_quantize_append", prm, cache(), FAKE, None, None, None, 0, stream=0)
     ok()  # zero tokens: validated, nothing launched
+
+
+def test_noalloc_validation():
+    """The allocation-free entry point rejects calls whose partial rows exceed its device array
+    (before touching the device), and bad arguments as kvq_decode_attention does."""
+    L = K.lib()
+    prm = p(num_q_heads=64, key_rotation=1)
+    assert K.kvq_decode_workspace_bytes(prm, 512, 131072) > K.KVQ_NOALLOC_SCRATCH_BYTES
+    cs = K.kvq_cache(FAKE, None, None, None, 512, 0, 131072)
+    st = L.kvq_decode_attention_noalloc(ctypes.byref(prm), ctypes.byref(cs), FAKE, 131072, FAKE, K.KVQ_BF16, FAKE,
+                                        K.KVQ_F32, 0.0, None)
+    assert st == K.KVQ_ENOSPACE
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(p(k_bits=3)), ctypes.byref(cs), FAKE, 16, FAKE, K.KVQ_BF16,
+                                          FAKE, K.KVQ_F32, 0.0, None) == K.KVQ_EUNSUPPORTED
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(prm), None, FAKE, 16, FAKE, K.KVQ_BF16, FAKE, K.KVQ_F32, 0.0,
+                                          None) == K.KVQ_EINVAL
