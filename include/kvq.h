@@ -53,8 +53,12 @@
  *   - Device pointers must be 16-byte aligned.
  *   - Sequence lengths are read on the device; the library never writes them.
  *     The caller advances them between append and attention.
- *   - Inputs must be finite with |x| < 2^15 (so fp16 metadata is finite);
- *     non-finite inputs give unspecified (but memory-safe) results.
+ *   - Inputs must be finite with |x| < 2^15; non-finite inputs give unspecified (but
+ *     memory-safe) results.  The fp16 metadata is then finite for 2..8-bit codes.  With
+ *     1-bit codes a group whose range (max - zero) exceeds 65504 has no finite fp16 scale:
+ *     it gets scale +inf and all codes 0, as the quantizer's definition gives, and its
+ *     dequantized values (and any attention over them) are NaN; |x| < 2^14 (or bf16 inputs,
+ *     whose largest value below 2^15 is 32640) keeps 1-bit metadata finite.
  *   - Calls on different streams touching different caches may run concurrently.
  */
 #ifndef KVQ_H
@@ -74,7 +78,9 @@ typedef enum {
   KVQ_EINVAL = 1,       /* null or misaligned pointer, inconsistent shapes       */
   KVQ_EUNSUPPORTED = 2, /* a parameter outside the supported set (see below)      */
   KVQ_ENOSPACE = 3,     /* workspace too small, or lengths beyond the capacity     */
-  KVQ_EHIP = 4          /* the HIP runtime reported an error at launch            */
+  KVQ_EHIP = 4,         /* the HIP runtime reported an error at launch            */
+  KVQ_EDEVICE = 5       /* kernels met device-side inputs they could not honour
+                         * (reported by kvq_device_status, see kvq_cache)          */
 } kvq_status;
 
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
@@ -105,7 +111,33 @@ typedef struct {
   int32_t batch;
   int32_t max_blocks_per_seq; /* paged: table row length (ignored when contiguous) */
   int64_t capacity;           /* contiguous: tokens per sequence; paged: pages in the pool */
+  uint32_t *error_flags;      /* optional device word (NULL: none), caller-owned and cleared by
+                               * the caller; kernels OR in KVQ_DEV_* flags below             */
 } kvq_cache;
+
+/* Device-side input errors.  Inputs that only the device sees (lengths, per-sequence counts,
+ * block-table entries) cannot be validated before launch.  The kernels keep every access inside
+ * the buffers regardless (clamping or dropping as described below), so such inputs give wrong
+ * results for the affected sequences but never touch memory outside the cache; when
+ * cache->error_flags is set they also OR the matching flag into that word:
+ *   KVQ_DEV_TABLE_ENTRY  a block-table entry read for a page holding data lies outside
+ *                        [0, pool pages): the page read or written is the nearest pool page;
+ *   KVQ_DEV_CAPACITY     an append reached a page beyond the cache (contiguous: capacity;
+ *                        paged: max_blocks_per_seq): those quantized tokens were dropped;
+ *   KVQ_DEV_LENGTH       a sequence length outside [0, max_seq_len] (attention, read-back,
+ *                        diagnostics) or negative (append), or a length whose quantized part
+ *                        exceeds the cache: it was clamped;
+ *   KVQ_DEV_COUNT        an n_new_per_seq entry outside [0, n_new]: it was clamped. */
+#define KVQ_DEV_TABLE_ENTRY 1u
+#define KVQ_DEV_CAPACITY 2u
+#define KVQ_DEV_LENGTH 4u
+#define KVQ_DEV_COUNT 8u
+
+/* Waits for the work queued on `stream` (a synchronizing call: not for use under graph
+ * capture), then copies cache->error_flags into *flags.  Returns KVQ_EDEVICE if any flag is
+ * set, KVQ_OK otherwise; KVQ_EINVAL without an error word or output pointer; KVQ_EHIP if the
+ * copy fails.  The word is not cleared. */
+kvq_status kvq_device_status(const kvq_cache *cache, uint32_t *flags, hipStream_t stream);
 
 typedef struct {
   size_t record_bytes; /* one page of one kv head                                 */

@@ -20,7 +20,8 @@ import torch  # noqa: F401,E402
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
 
-KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_EHIP = range(5)
+KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_EHIP, KVQ_EDEVICE = range(6)
+KVQ_DEV_TABLE_ENTRY, KVQ_DEV_CAPACITY, KVQ_DEV_LENGTH, KVQ_DEV_COUNT = 1, 2, 4, 8
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_ROT_NONE, KVQ_ROT_WHT = 0, 1
 KVQ_PART_FLOATS = 132  # floats per (row, split) of the decode workspace: m, l, 0, 0, acc[128]
@@ -39,6 +40,7 @@ EXPORTED = [
     "kvq_dense_workspace_bytes",
     "kvq_dense_decode_attention",
     "kvq_error_budget",
+    "kvq_device_status",
     "kvq_status_str",
 ]
 
@@ -69,6 +71,7 @@ class kvq_cache(ctypes.Structure):
         ("batch", c_int32),
         ("max_blocks_per_seq", c_int32),
         ("capacity", c_int64),
+        ("error_flags", c_void_p),
     ]
 
 
@@ -126,6 +129,8 @@ def _load():
     lib.kvq_error_budget.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                                      c_int32, c_float, c_void_p, c_void_p, c_void_p]
     lib.kvq_error_budget.restype = c_int32
+    lib.kvq_device_status.argtypes = [P(kvq_cache), P(ctypes.c_uint32), c_void_p]
+    lib.kvq_device_status.restype = c_int32
     lib.kvq_status_str.argtypes = [c_int32]
     lib.kvq_status_str.restype = ctypes.c_char_p
     return lib
@@ -180,6 +185,13 @@ def bound_call(name: str, *args, stream=None):
             raise KvqError(st, name)
 
     return call
+
+
+def kvq_device_status(cache, stream=None):
+    """(status, flags): waits for the stream, reads the cache's device error word."""
+    flags = ctypes.c_uint32(0)
+    st = _lib.kvq_device_status(ctypes.byref(cache), ctypes.byref(flags), _stream(stream))
+    return st, int(flags.value)
 
 
 def kvq_status_str(status: int) -> str:
@@ -321,5 +333,14 @@ class CacheBuffers:
             self.k_win = self.v_win = None
         self.block_table = block_table
         mbps = int(block_table.shape[1]) if block_table is not None else 0
+        # device error word (KVQ_DEV_* flags), zero until a kernel meets a bad device-side input
+        self.error_word = torch.zeros(4, dtype=torch.int32, device=device)
         self.struct = kvq_cache(_ptr(self.pages), _ptr(self.k_win), _ptr(self.v_win), _ptr(block_table), batch, mbps,
-                                capacity)
+                                capacity, _ptr(self.error_word))
+
+    def device_errors(self) -> int:
+        """KVQ_DEV_* flags the kernels have raised on this cache so far (synchronizes)."""
+        return kvq_device_status(self.struct)[1]
+
+    def clear_device_errors(self) -> None:
+        self.error_word.zero_()

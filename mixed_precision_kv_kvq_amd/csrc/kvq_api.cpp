@@ -33,6 +33,7 @@ kvq_status check_params(const kvq_params *p) {
 kvq_status check_cache(const kvq_params *p, const kvq_cache *c) {
   if (!c || c->batch <= 0 || c->capacity <= 0) return KVQ_EINVAL;
   if (!c->pages || !aligned16(c->pages)) return KVQ_EINVAL;
+  if (((uintptr_t)c->error_flags & 3u)) return KVQ_EINVAL;
   if (p->window > 0) {
     if (!c->k_win || !c->v_win || !aligned16(c->k_win) || !aligned16(c->v_win)) return KVQ_EINVAL;
   }
@@ -53,6 +54,7 @@ KvqCacheDev dev_cache(const kvq_params *p, const kvq_cache *c) {
   d.paged = p->block_size != 0;
   d.pages_per_seq = d.paged ? 0 : kvq_pages_per_seq(c->capacity);
   d.pool_pages = d.paged ? c->capacity : 0;
+  d.err = c->error_flags;
   return d;
 }
 
@@ -401,6 +403,16 @@ kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, co
   return hip_status(kvq_launch_errbudget(a, stream));
 }
 
+kvq_status kvq_device_status(const kvq_cache *cache, uint32_t *flags, hipStream_t stream) {
+  if (!cache || !cache->error_flags || !flags) return KVQ_EINVAL;
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, cache->error_flags, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return KVQ_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return KVQ_EHIP;
+  *flags = v;
+  return v ? KVQ_EDEVICE : KVQ_OK;
+}
+
 const char *kvq_status_str(kvq_status status) {
   switch (status) {
     case KVQ_OK: return "ok";
@@ -408,6 +420,7 @@ const char *kvq_status_str(kvq_status status) {
     case KVQ_EUNSUPPORTED: return "unsupported parameter";
     case KVQ_ENOSPACE: return "workspace too small or length beyond the cache capacity";
     case KVQ_EHIP: return "HIP runtime error at launch";
+    case KVQ_EDEVICE: return "device-side input error (block-table entry, capacity, length or count out of range)";
   }
   return "unknown status";
 }

@@ -128,6 +128,23 @@ __device__ inline DirectSplit direct_split(int64_t L, int m) {
   return d;
 }
 
+// Tokens appended to sequence b: n_new_per_seq[b] clamped into [0, n_new] (the rows of k_new and
+// v_new end there), or n_new for every sequence.
+// A clamped entry is reported as KVQ_DEV_COUNT.
+__device__ inline int append_count(const KvqAppendArgs &a, int b) {
+  if (!a.n_new_per_seq) return a.n_new;
+  const int n = a.n_new_per_seq[b];
+  kvq_raise(a.cache, n < 0 || n > a.n_new, KVQ_DEV_COUNT);
+  return n < 0 ? 0 : (n > a.n_new ? a.n_new : n);
+}
+// Length of sequence b before the append; a negative length is taken as 0 and reported as
+// KVQ_DEV_LENGTH.
+__device__ inline int append_base(const KvqAppendArgs &a, int b) {
+  const int L = a.seq_lens_before[b];
+  kvq_raise(a.cache, L < 0, KVQ_DEV_LENGTH);
+  return L < 0 ? 0 : L;
+}
+
 __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
   __shared__ uint8_t ck[KVQ_D];
   __shared__ uint8_t cv[KVQ_D];
@@ -135,8 +152,8 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
   __shared__ uint32_t mv[KVQ_D / 64];
 
   const int item = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  const int L = a.seq_lens_before[b];
-  const int nb = a.n_new_per_seq ? a.n_new_per_seq[b] : a.n_new;
+  const int L = append_base(a, b);
+  const int nb = append_count(a, b);
   if (item >= nb) return;
   const int R = a.R, Hkv = a.Hkv;
   const int esz = a.kv_f32 ? 4 : 2;
@@ -214,9 +231,11 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
 
   const int64_t page = t_q / KVQ_PAGE;
   const int n = (int)(t_q % KVQ_PAGE);
-  if (page >= (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq)) return;  // beyond the cache
-  const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
-                                           (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, b, h, page);
+  if (page >= (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq)) {  // beyond the cache: dropped
+    kvq_raise(a.cache, true, KVQ_DEV_CAPACITY);
+    return;
+  }
+  const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, b, h, page);
   uint8_t *rec = a.cache.pages + (size_t)rec_idx * lay.record;
 
   // K codes: 4 slots (octets j) x kb words.
@@ -276,14 +295,17 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   constexpr int kMaxRecordWords = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 4;
   __shared__ __attribute__((aligned(16))) uint32_t rw[kMaxRecordWords];
   const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  const int L = a.seq_lens_before[b];
-  const int nb = a.n_new_per_seq ? a.n_new_per_seq[b] : a.n_new;
+  const int L = append_base(a, b);
+  const int nb = append_count(a, b);
   const int m = nb - a.R;
   if (m <= 0) return;
   const DirectSplit d = direct_split(L, m);
   const int64_t page = d.p_start + blockIdx.x;
   if (page >= d.p_end) return;
-  if (page >= (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq)) return;  // beyond the cache
+  if (page >= (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq)) {  // beyond the cache: dropped
+    kvq_raise(a.cache, true, KVQ_DEV_CAPACITY);
+    return;
+  }
   const KvqLayout &lay = a.lay;
   const int Hkv = a.Hkv;
   const int t = lane & 15, q = lane >> 4;
@@ -429,8 +451,7 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     if ((32 * q) % lay.vg == 0) rw[lay.v_meta_off / 4 + kvq_meta_dword(lay.nvg, t, grp)] = g.sb | (g.zb << 16);
   }
   __syncthreads();
-  const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
-                                           (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, b, h, page);
+  const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, b, h, page);
   uint4 *rec = reinterpret_cast<uint4 *>(a.cache.pages + (size_t)rec_idx * lay.record);
   const uint4 *src = reinterpret_cast<const uint4 *>(rw);
   for (int c = lane; c < lay.record / 16; c += 64) rec[c] = src[c];

@@ -902,6 +902,8 @@ struct Kern {
     const KvqLayout &lay = args.lay;
     const int R = args.R;
     int L = args.seq_lens[b];
+    // a length outside [0, max_len] is clamped (reported once per unit, by its split 0)
+    kvq_raise(args.cache, split == 0 && (L < 0 || L > args.max_len), KVQ_DEV_LENGTH);
     L = L < 0 ? 0 : (L > args.max_len ? args.max_len : L);
     const int nq = L > R ? L - R : 0;
     const int nw = L < R ? L : R;
@@ -1063,7 +1065,10 @@ struct Kern {
         src = paged ? pages + (size_t)kvh * rec : unit_first;
       } else if (paged) {
         int e = tcur[(odd && !dup) ? 1 : 0];
-        e = e < 0 ? 0 : (e > pool_last ? pool_last : e);
+        if ((uint32_t)e > (uint32_t)pool_last) {  // outside the pool: clamped and reported
+          kvq_raise(args.cache, true, KVQ_DEV_TABLE_ENTRY);
+          e = e < 0 ? 0 : pool_last;
+        }
         src = pages + ((size_t)e * Hkv + kvh) * rec;
         if (odd) tcur += 2 * SQ;
       } else {

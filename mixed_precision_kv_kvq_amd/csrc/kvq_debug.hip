@@ -16,6 +16,7 @@ __global__ __launch_bounds__(64) void kvq_debug_kernel(KvqDebugArgs a) {
   const int R = a.R;
   int64_t nq = L > R ? (int64_t)L - R : 0;
   const int64_t cap_tokens = (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq) * KVQ_PAGE;
+  kvq_raise(a.cache, idx == 0 && h == 0 && (L < 0 || nq > cap_tokens), KVQ_DEV_LENGTH);
   if (nq > cap_tokens) nq = cap_tokens;  // lengths beyond the cache read nothing
   const KvqLayout &lay = a.lay;
   const int64_t ob = idx * Hkv + h;  // output row
@@ -25,9 +26,7 @@ __global__ __launch_bounds__(64) void kvq_debug_kernel(KvqDebugArgs a) {
     uint32_t kc = 0xFF, vc = 0xFF;
     float kh = qnan, vh = qnan;
     if (t < nq) {
-      const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
-                                               (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, a.seq, h,
-                                               t / KVQ_PAGE);
+      const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, a.seq, h, t / KVQ_PAGE);
       const uint8_t *rec = a.cache.pages + (size_t)rec_idx * lay.record;
       const int n = (int)(t % KVQ_PAGE);
       int off, bit;

@@ -140,6 +140,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   const int Hkv = a.Hkv, g = a.Hq / a.Hkv, h = hq0 / g;
   const bool unit_lead = (hq0 % g) == 0;
   int64_t L = a.seq_lens[b];
+  kvq_raise(a.cache, hq0 == 0 && (L < 0 || L > a.max_len), KVQ_DEV_LENGTH);
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   int64_t nq = L > a.R ? L - a.R : 0;
   const int64_t cap_tokens = (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq) * KVQ_PAGE;
@@ -174,9 +175,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     p.n = (int)(t % KVQ_PAGE);
     p.rec = nullptr;
     if (p.valid && p.quant) {
-      const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
-                                               (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, b, h,
-                                               t / KVQ_PAGE);
+      const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, b, h, t / KVQ_PAGE);
       p.rec = a.cache.pages + (size_t)rec_idx * a.lay.record;
     }
     return p;

@@ -44,7 +44,26 @@ struct KvqCacheDev {
   int64_t pages_per_seq;  // contiguous mode
   int64_t pool_pages;     // paged mode: pages in the pool
   int paged;
+  uint32_t *err;          // optional device error word (kvq_cache::error_flags), or null
 };
+
+// OR `flag` into the cache's device error word (when there is one) from the active lanes that
+// saw the condition: one atomic per wave, issued by the lowest such lane.
+__device__ inline void kvq_raise(const KvqCacheDev &c, bool cond, uint32_t flag) {
+  if (!c.err) return;
+  const uint64_t m = __ballot(cond);
+  if (m && (int)__lane_id() == __ffsll((unsigned long long)m) - 1) atomicOr(c.err, flag);
+}
+
+// Record of (sequence b, kv head h, logical page p), with an out-of-range block-table entry
+// clamped into the pool and reported as KVQ_DEV_TABLE_ENTRY.
+__device__ inline int64_t kvq_record_index_dev(const KvqCacheDev &c, int Hkv, int b, int h, int64_t p) {
+  if (c.paged) {
+    const int64_t e = c.block_table[(int64_t)b * c.mbps + p];
+    kvq_raise(c, e < 0 || e >= c.pool_pages, KVQ_DEV_TABLE_ENTRY);
+  }
+  return kvq_record_index(c.paged, c.block_table, c.mbps, (int64_t)c.batch * Hkv, c.pool_pages, Hkv, b, h, p);
+}
 
 struct KvqAppendArgs {
   KvqLayout lay;

@@ -138,11 +138,16 @@ __device__ inline uint32_t kvq_f16_round_up(double x) {
   return 0x8000u | kvq_f16_trunc_pos(-x, &ex);
 }
 
+// fp16 bit pattern -> fp64 value (exact), infinities and NaN included: a 1-bit group whose range
+// exceeds the largest fp16 gets the scale +inf from the directed rounding, and its codes then
+// follow from x / inf = 0.
 __host__ __device__ inline double kvq_f16_bits_to_f64(uint32_t h) {
   const uint32_t s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
   double v;
   if (e == 0)
     v = (double)m * 5.9604644775390625e-08;  // 2^-24
+  else if (e == 31)
+    v = m ? __builtin_nan("") : __builtin_inf();
   else
     v = (double)(1024 + m) * __builtin_ldexp(1.0, (int)e - 25);
   return s ? -v : v;

@@ -58,6 +58,7 @@ __global__ __launch_bounds__(64) void kvq_dequantize_dense_kernel(KvqDenseArgs a
   const int64_t page = blockIdx.x;
   const int Hkv = a.Hkv, R = a.R;
   int64_t L = a.seq_lens[b];
+  kvq_raise(a.cache, page == 0 && h == 0 && (L < 0 || L > a.max_len), KVQ_DEV_LENGTH);
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int64_t t_first = page * KVQ_PAGE;
   if (t_first >= L) return;
@@ -67,8 +68,7 @@ __global__ __launch_bounds__(64) void kvq_dequantize_dense_kernel(KvqDenseArgs a
   const int64_t wstart = L > R ? L - R : 0;  // first window position
   const KvqLayout &lay = a.lay;
   if (t_first < nq) {
-    const int64_t rec_idx = kvq_record_index(a.cache.paged, a.cache.block_table, a.cache.mbps,
-                                             (int64_t)a.cache.batch * Hkv, a.cache.pool_pages, Hkv, b, h, page);
+    const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, b, h, page);
     const uint4 *rec = reinterpret_cast<const uint4 *>(a.cache.pages + (size_t)rec_idx * lay.record);
     for (int c = lane; c < lay.record / 16; c += 64) rec_s[c] = rec[c];
     __syncthreads();

@@ -226,8 +226,9 @@ def test_error_budget_validation():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert K.kvq_status_str(s)
+    assert "device" in K.kvq_status_str(K.KVQ_EDEVICE)
     assert "unknown" in K.kvq_status_str(99)
 
 
@@ -294,3 +295,19 @@ def test_noalloc_validation():
                                           FAKE, K.KVQ_F32, 0.0, None) == K.KVQ_EUNSUPPORTED
     assert L.kvq_decode_attention_noalloc(ctypes.byref(prm), None, FAKE, 16, FAKE, K.KVQ_BF16, FAKE, K.KVQ_F32, 0.0,
                                           None) == K.KVQ_EINVAL
+
+
+def test_device_status_validation():
+    """kvq_device_status needs an error word and an output; a misaligned error word is rejected by
+    every entry point that takes the cache (host checks only: nothing is launched)."""
+    L = K.lib()
+    flags = ctypes.c_uint32(0)
+    cs = K.kvq_cache(FAKE, None, None, None, 1, 0, 16)
+    assert L.kvq_device_status(ctypes.byref(cs), ctypes.byref(flags), None) == K.KVQ_EINVAL
+    assert L.kvq_device_status(None, ctypes.byref(flags), None) == K.KVQ_EINVAL
+    cs.error_flags = FAKE
+    assert L.kvq_device_status(ctypes.byref(cs), None, None) == K.KVQ_EINVAL
+    cs.error_flags = FAKE + 2  # not 4-byte aligned
+    assert L.kvq_quantize_append(ctypes.byref(p()), ctypes.byref(cs), FAKE, None, FAKE, FAKE, 1, None) == K.KVQ_EINVAL
+    assert L.kvq_decode_attention(ctypes.byref(p()), ctypes.byref(cs), FAKE, 16, FAKE, K.KVQ_BF16, FAKE, K.KVQ_F32,
+                                  0.0, FAKE, 1 << 30, None) == K.KVQ_EINVAL

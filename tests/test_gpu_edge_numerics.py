@@ -1,0 +1,197 @@
+"""GPU parity of the quantizer's edge numerics (codes and fp16 metadata bit for bit, outputs to
+the tolerance), through both append kernels and the attention kernel.
+
+Inputs are built group by group from the kinds below, so that one cache holds every edge case
+next to ordinary groups:
+  * groups whose range / (2^b - 1) and whose minimum fall below 2^-14, so that the scale and the
+    zero point are fp16 subnormals (the subnormal branch of the device's directed rounding, and
+    the page kernel's fp32 code path with 1/scale up to 2^24);
+  * tiny groups of either sign around zero (subnormal negative zero points);
+  * all-negative groups;
+  * groups holding -0.0 (the quantizer takes min and max after adding +0.0), and groups of
+    signed zeros only (scale 0, all codes 0);
+  * constant groups whose value is not an fp16 (a subnormal-sized scale above zero);
+  * 1-bit groups spanning almost the whole range below 2^15 (scale 65280; p * scale near 2^96 in
+    the value contraction), and fp32 1-bit groups wider than 65504 (no finite fp16 scale: scale
+    +inf, codes 0, reconstruction NaN on both sides).
+A prefill of T tokens in one append sends whole pages to the page kernel and the partial pages
+and the recent window to the per-token kernel; the decode steps then quantize the tokens leaving
+the window with the per-token kernel."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import mixed_precision_kv_kvq_amd as K  # noqa: E402
+import oracle as O  # noqa: E402
+import workloads as W  # noqa: E402
+from kvq_harness import (GpuRun, close_stats, compare_codes, oracle_heads, oracle_unit,  # noqa: E402
+                         REL_L2_TOL, MAX_ABS_TOL)
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _bf16(x):
+    return W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+def _kind(rng, kind, n):
+    if kind == "normal":
+        return rng.standard_normal(n) * 3.0
+    if kind == "tiny_pos":  # scale and zero fp16 subnormals for every bit width
+        return rng.uniform(0.0, 4e-5, n)
+    if kind == "tiny_mixed":
+        return rng.uniform(-3e-5, 3e-5, n)
+    if kind == "negative":
+        return -rng.uniform(0.5, 6.0, n)
+    if kind == "neg_zero":
+        x = rng.standard_normal(n)
+        x[rng.random(n) < 0.3] = -0.0
+        return x
+    if kind == "signed_zeros":
+        return np.where(rng.random(n) < 0.5, -0.0, 0.0)
+    if kind == "const_inexact":  # bf16 1.23e-6 is not an fp16 value
+        return np.full(n, 1.23e-6)
+    if kind == "wide":  # bf16 values up to 32640 (the largest bf16 below 2^15)
+        x = rng.uniform(-32640.0, 32640.0, n)
+        x[0], x[1] = -32640.0, 32640.0
+        return x
+    if kind == "overflow":  # fp32 values whose 1-bit range exceeds 65504
+        x = rng.uniform(-32767.5, 32767.5, n)
+        x[0], x[1] = -32767.5, 32767.5
+        return x
+    raise ValueError(kind)
+
+
+EDGE_KINDS = ["normal", "tiny_pos", "tiny_mixed", "negative", "neg_zero", "signed_zeros", "const_inexact"]
+
+
+def edge_rows(wl, T, kinds, seed, whole_token=False):
+    """K, V host arrays [B][T][Hkv][128] (bf16-exact for bf16 workloads): every key group of k_group
+    channels and every value group of v_group channels drawn from one kind (one kind per token and
+    tensor when whole_token, so that a rotation keeps tiny tokens tiny)."""
+    rng = np.random.default_rng(seed)
+    B, H, d = wl.batch, wl.num_kv_heads, wl.head_dim
+    out = []
+    for G in (wl.k_group, wl.v_group):
+        x = np.empty((B, T, H, d), dtype=np.float64)
+        for b in range(B):
+            for t in range(T):
+                for h in range(H):
+                    if whole_token:
+                        k = kinds[rng.integers(len(kinds))]
+                        x[b, t, h] = _kind(rng, k, d)
+                    else:
+                        for g in range(d // G):
+                            k = kinds[rng.integers(len(kinds))]
+                            x[b, t, h, g * G:(g + 1) * G] = _kind(rng, k, G)
+        x = x.astype(np.float32)
+        if wl.kv_dtype == "bf16":
+            x = _bf16(x)
+        out.append(x)
+    return out
+
+
+def base(**kw):
+    wl = dataclasses.replace(W.WORKLOADS[3], name="edge", batch=2, num_q_heads=8, num_kv_heads=2, context=300,
+                             window=16, steps=3)
+    return dataclasses.replace(wl, **kw)
+
+
+CASES = {
+    "k4v2-window": (base(), False),
+    "k1v1-g32-g64": (base(k_bits=1, v_bits=1, v_group=64), False),
+    "k8v8-g64-no-window": (base(k_bits=8, v_bits=8, k_group=64, window=0), False),
+    "k2v4-key-rotation": (base(k_bits=2, v_bits=4, rotation=True, window=8), True),
+    "k4v2-value-rotation": (base(value_rotation=True, window=0, steps=2), True),
+    "f32-k4v2-window": (base(kv_dtype="f32", q_dtype="f32"), False),
+    "paged-k4v4": (base(k_bits=4, v_bits=4, block_size=16, window=4), False),
+}
+
+
+def _run_case(wl, whole_token, kinds=EDGE_KINDS, seed=11, scaled_tol=False):
+    T = int(wl.context) + wl.steps
+    Kx, Vx = edge_rows(wl, T, kinds, seed, whole_token)
+    run = GpuRun(wl, kv_override=(Kx, Vx))
+    g = wl.group_q
+    for step in range(max(wl.steps, 1)):
+        o = run.decode(step)
+        got, ref = [], []
+        L = int(run.current_lengths()[0])
+        for b in range(wl.batch):
+            rb = run.readback(b, 0, L)
+            for h in range(wl.num_kv_heads):
+                cache, K_, V_ = oracle_unit(run, b, h)
+                compare_codes(run, b, h, cache, K_, V_, rb)
+                ref.append(oracle_heads(run, cache, b, h, step))
+                got.append(o[b, h * g:(h + 1) * g])
+        got, ref = np.concatenate(got), np.concatenate(ref)
+        maxabs, rel = close_stats(got, ref)
+        # fp32 accumulation has relative precision: for outputs of magnitude M >> 1 the absolute
+        # bound is scaled by M (relative L2 unchanged)
+        mag = max(1.0, float(np.abs(ref).max())) if scaled_tol else 1.0
+        assert maxabs <= MAX_ABS_TOL * mag and rel <= REL_L2_TOL, f"step {step}: max-abs {maxabs:.3e} rel {rel:.3e}"
+    return run
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_edge_groups_bit_exact(name):
+    wl, whole = CASES[name]
+    say(f"edge numerics {name}")
+    _run_case(wl, whole)
+
+
+def test_one_bit_wide_groups_large_scale():
+    """bf16 1-bit groups spanning [-32640, 32640]: scale 65280 (finite), p * scale in the value
+    contraction near 2^96; outputs of magnitude ~3e4 compared with the absolute bound scaled by
+    the output magnitude."""
+    wl = base(k_bits=1, v_bits=1, k_group=32, v_group=128)
+    say("edge numerics 1-bit wide groups")
+    _run_case(wl, False, kinds=["wide", "normal"], seed=5, scaled_tol=True)
+
+
+def test_one_bit_overflow_scale_is_inf():
+    """fp32 1-bit groups wider than 65504: both kernels and the oracle give scale +inf (0x7C00),
+    zero RD16(min) and all codes 0; reconstructions are NaN on both sides (attention over such a
+    cache is NaN by the definition, so only the stored codes and metadata are compared)."""
+    wl = base(k_bits=1, v_bits=1, kv_dtype="f32", q_dtype="f32", steps=2)
+    say("edge numerics 1-bit overflow")
+    T = int(wl.context) + wl.steps
+    Kx, Vx = edge_rows(wl, T, ["overflow", "normal"], 3)
+    run = GpuRun(wl, kv_override=(Kx, Vx))
+    for step in range(wl.steps):  # appends through the per-token kernel (eviction from the window)
+        pos = run.current_lengths()
+        k = run._rows_at(W.TENSOR_K, pos)
+        v = run._rows_at(W.TENSOR_V, pos)
+        K.kvq_quantize_append(run.params, run.cache.struct, torch.from_numpy(pos.astype(np.int32)).cuda(), None, k,
+                              v, 1)
+        run.steps_done += 1
+    torch.cuda.synchronize()
+    L = int(run.current_lengths()[0])
+    n_inf = 0
+    for b in range(wl.batch):
+        rb = run.readback(b, 0, L)
+        for h in range(wl.num_kv_heads):
+            cache, K_, V_ = oracle_unit(run, b, h)
+            nq = cache["nq"]
+            assert np.array_equal(rb["k_codes"][:nq, h], cache["k_codes"])
+            assert np.array_equal(rb["v_codes"][:nq, h], cache["v_codes"])
+            assert np.array_equal(rb["k_meta"][:nq, h, :, 0], O.f16_bits(cache["k_scale"]))
+            assert np.array_equal(rb["k_meta"][:nq, h, :, 1], O.f16_bits(cache["k_zero"]))
+            assert np.array_equal(rb["v_meta"][:nq, h, :, 0], O.f16_bits(cache["v_scale"]))
+            assert np.array_equal(rb["v_meta"][:nq, h, :, 1], O.f16_bits(cache["v_zero"]))
+            assert np.array_equal(rb["k_hat"][:nq, h], cache["k_hat"].astype(np.float32), equal_nan=True)
+            assert np.array_equal(rb["v_hat"][:nq, h], cache["v_hat"].astype(np.float32), equal_nan=True)
+            n_inf += int(np.sum(rb["k_meta"][:nq, h, :, 0] == 0x7C00))
+    assert n_inf > 0, "no group reached the +inf scale"

@@ -470,10 +470,34 @@ def check_error_budget(O_):
     assert np.all(head == 0) and np.all(unit == 0)
 
 
+def check_one_bit_range_limit(O_):
+    """1-bit groups at the edge of the fp16 range.  A group spanning [-32767.5, 32767.5] has
+    zero = -32768 and needs a scale >= 65535.5: no finite fp16 reaches it (brute force over all of
+    them), so the smallest fp16 >= the need is +inf, every code is 0 (x / inf rounds to 0) and the
+    reconstruction is NaN.  The widest bf16 group below 2^15, [-32640, 32640], stays finite and
+    agrees with the exact-rational quantizer."""
+    xs = [-32767.5, -10.0, 0.0, 32767.5]
+    zero = Fraction(float(rd16_brute(min(xs))))
+    assert zero == -32768
+    need = Fraction(max(xs)) - zero
+    assert all(Fraction(float(v)) < need for v in all_finite_fp16_sorted()), "a finite fp16 covers the group"
+    codes, scale, z = O_.quantize(np.array(xs), 1, len(xs))
+    assert int(O_.f16_bits(scale)[0]) == 0x7C00, "scale is not +inf"
+    assert Fraction(float(z[0])) == zero
+    assert codes.tolist() == [0, 0, 0, 0]
+    assert np.all(np.isnan(O_.dequantize(codes, scale, z, len(xs))))
+    xs = [-32640.0, -3.0, 5.0, 32640.0]
+    zero, sc, ref_codes, _ = exact_group_quant(xs, 1)
+    codes, scale, z = O_.quantize(np.array(xs), 1, len(xs))
+    assert np.isfinite(float(scale[0])) and Fraction(float(scale[0])) == sc and Fraction(float(z[0])) == zero
+    assert codes.tolist() == ref_codes
+
+
 ALL_CHECKS = [
     check_fp16_directed, check_golden, check_wht, check_attention_library, check_attention_decimal,
     check_end_to_end_exact, check_error_identities, check_window, check_gqa, check_rotation_special_case,
     check_memory_model, check_group_size_monotone, check_outlier, check_value_rotation, check_error_budget,
+    check_one_bit_range_limit,
 ]
 
 
@@ -589,3 +613,7 @@ def test_bf16_rounding_helper_of_the_parity_tests():
 
 def test_error_budget_definitions():
     check_error_budget(O)
+
+
+def test_one_bit_range_limit():
+    check_one_bit_range_limit(O)
