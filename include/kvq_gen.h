@@ -28,6 +28,13 @@ int kvq_gen_kv(void *out, int out_f32, uint64_t key, const float *sigma, const f
 int kvq_gen_q(void *out, int out_f32, uint64_t key, const float *table, int B, int Hq, int d, int step,
               hipStream_t stream);
 
+/* Benchmark ceiling: read floor(bytes / 16) 16-byte words of device buffer `buf` (16-byte
+ * aligned) once, with `blocks` workgroups of 256 lanes, plain or non-temporal loads; `sink`
+ * (device, >= 256 uint32) is written only in the unlikely case that the xor of all words a lane
+ * read equals 0x9E3779B9.  Returns a hipError_t. */
+int kvq_gen_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int nontemporal,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

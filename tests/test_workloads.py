@@ -57,6 +57,8 @@ def test_bench_cpu_baseline_runs_on_a_small_sample():
     bench = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(bench)
     wl = dataclasses.replace(W.WORKLOADS[3], context=400)
-    r = bench.cpu_baseline(wl, target_seconds=0.01, max_units=2)
-    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+    r = bench.cpu_baseline(wl, target_seconds=0.01, max_units=2, workers=1)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0 and r["value_1core"] > 0
     assert r["sample"].startswith("1 of ") or r["sample"].startswith("2 of ")
+    r = bench.cpu_baseline(wl, target_seconds=0.01, max_units=4, workers=2)  # two forked workers
+    assert r["cores"] == 2 and r["value"] > 0 and r["value"] <= r["value_1core"] * 1.5

@@ -30,6 +30,9 @@ def _lib():
         lib.kvq_gen_q.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         lib.kvq_gen_q.restype = ctypes.c_int
+        lib.kvq_gen_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_void_p]
+        lib.kvq_gen_stream_read.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -71,3 +74,16 @@ class DeviceGenerator:
         if rc:
             raise RuntimeError(f"kvq_gen_q failed: hip error {rc}")
         return out
+
+
+def stream_read_call(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, blocks: int, nontemporal: bool, stream):
+    """A zero-argument callable launching the read-only streaming kernel over nbytes of buf."""
+    fn = _lib().kvq_gen_stream_read
+    args = (buf.data_ptr(), int(nbytes), sink.data_ptr(), int(blocks), int(nontemporal), stream.cuda_stream)
+
+    def call():
+        rc = fn(*args)
+        if rc:
+            raise RuntimeError(f"kvq_gen_stream_read failed: hip error {rc}")
+
+    return call

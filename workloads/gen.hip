@@ -56,6 +56,29 @@ __global__ void gen_q_kernel(void *out, int out_f32, uint64_t key, const float *
   }
 }
 
+// Read-only streaming of n16 16-byte words (benchmark ceiling of a read-once kernel): consecutive
+// lanes read consecutive words, four loads in flight per lane per iteration, grid-stride over the
+// buffer.  The words are folded with xor and stored only if the fold equals a value it never takes
+// in practice, so no load can be dropped and almost nothing is written.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4v *p, int64_t n16, uint32_t *sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  auto ld = [&](int64_t k) -> u32x4v {
+    if constexpr (NT) return __builtin_nontemporal_load(p + k);
+    return p[k];
+  };
+  auto fold = [](u32x4v v) { return v.x ^ v.y ^ v.z ^ v.w; };
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4v a = ld(i), b = ld(i + stride), c = ld(i + 2 * stride), d = ld(i + 3 * stride);
+    acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
+  }
+  for (; i < n16; i += stride) acc ^= fold(ld(i));
+  if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
+}
+
 unsigned grid_for(int64_t total) {
   int64_t g = (total + 255) / 256;
   if (g > 65536) g = 65536;
@@ -82,5 +105,19 @@ extern "C" int kvq_gen_q(void *out, int out_f32, uint64_t key, const float *tabl
   (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
   hipLaunchKernelGGL(gen_q_kernel, dim3(grid_for(total)), dim3(256), 0, stream, out, out_f32, key, table, B, Hq, d,
                      step);
+  return (int)hipGetLastError();
+}
+
+extern "C" int kvq_gen_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int nontemporal,
+                                   hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 <= 0 || blocks <= 0) return 0;
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const u32x4v *)buf, n16, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const u32x4v *)buf, n16, sink);
   return (int)hipGetLastError();
 }
