@@ -113,6 +113,67 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes):
     print(json.dumps(out))
 
 
+def summarize_trace(trace_dir, bench_json, out_md, command):
+    """Per-phase average durations of the split kernel (and the other kernels' averages) from a
+    `rocprofv3 --kernel-trace` run of this script, sliced by the dispatch plan the run printed."""
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    for f in glob.glob(os.path.join(trace_dir, "**", "*results.db"), recursive=True):  # rocpd database output
+        import sqlite3
+
+        con = sqlite3.connect(f)
+        rows += [{"Kernel_Name": n, "Start_Timestamp": a, "End_Timestamp": b}
+                 for n, a, b in con.execute("select name, start, end from kernels")]
+        con.close()
+    if not rows:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    with open(bench_json) as fh:
+        res = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def dur(r):
+        return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # ns -> µs
+
+    split = [r for r in rows if SPLIT_KERNEL in r["Kernel_Name"].replace("  ", " ")]
+    lines = [f"# Kernel trace of `{res['config']['workload']}`", "", "Command (repository root on the GPU box):", "",
+             "```", command, "```", "",
+             f"Split kernel `{SPLIT_KERNEL}`: {len(split)} dispatches; the plan printed by the run expects "
+             f"{sum(p['launches'] for p in res['split_kernel_dispatch_plan'])}.", "",
+             "| phase | launches | timed | trace avg µs | trace min µs | trace max µs |", "|---|---:|---:|---:|---:|---:|"]
+    i = 0
+    for ph in res["split_kernel_dispatch_plan"]:
+        seg = split[i:i + ph["launches"]][ph["untimed_first"]:]
+        i += ph["launches"]
+        if seg:
+            d = [dur(r) for r in seg]
+            lines.append(f"| {ph['phase']} | {ph['launches']} | {len(seg)} | {sum(d) / len(d):.2f} | {min(d):.2f} | "
+                         f"{max(d):.2f} |")
+        else:
+            lines.append(f"| {ph['phase']} | {ph['launches']} | 0 | | | |")
+    lines += ["", "Bench figures of the same run (HIP events):", "",
+              f"- value (µs per fused step, wall clock): {res['value']}; events: {res['gpu_us_per_step']}",
+              f"- split kernel cold / warm (µs): {res['split_kernel_us_cold']} / {res['split_kernel_us_warm']}",
+              f"- attention-only split kernel cold / warm (µs): {res['attention_split_kernel']['us_cold']} / "
+              f"{res['attention_split_kernel']['us_warm']}",
+              f"- merge (µs): {res['combine_us']}", "", "Other kernels (all dispatches):", "",
+              "| kernel | dispatches | avg µs |", "|---|---:|---:|"]
+    by = {}
+    for r in rows:
+        if SPLIT_KERNEL in r["Kernel_Name"].replace("  ", " "):
+            continue
+        by.setdefault(r["Kernel_Name"][:90], []).append(dur(r))
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1]))[:12]:
+        lines.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _oracle_units_worker(job):
     """Worker of cpu_baseline: the oracle's decode-step work for some (sequence, kv head) units,
     one thread, returning the timed seconds per unit."""
@@ -382,7 +443,12 @@ def main():
                     help="run one device copy of this many MiB before the steps (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
                     help="write the split kernel's per-launch HBM traffic from two --pmc runs and exit")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD", "COMMAND"),
+                    help="per-phase split-kernel durations of a --kernel-trace run of this script, and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], int(args.summarize_pmc[2]) << 20)
         return
@@ -409,7 +475,7 @@ def main():
     torch.cuda.set_device(dev)
     B, Hq, Hkv, d, R = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window
     L0 = wl.context
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + 2 * args.steps  # fused steps, then as many through separate launches
     params = K.make_params(d, Hq, Hkv, wl.k_bits, wl.k_group, wl.v_bits, wl.v_group, R, 0, K.KVQ_BF16, 0)
     cap = L0 + total_steps
     cache = K.CacheBuffers(params, B, cap)
@@ -456,11 +522,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # One step: append (quantize the token leaving the window), split-K attention kernel,
-    # cross-split merge.  kvq_decode_partials + kvq_decode_combine are exactly the two launches
-    # of kvq_decode_attention; calling them apart lets HIP events bracket the split kernel alone.
-    # Arguments are marshalled before timing (bound_call), so the Python loop stays ahead of the GPU.
-    def phases(s, c=cache):
+    # One decode step = kvq_decode_step: the split-K launch with the 1-token append fused in (the
+    # split holding the new token's ring slot quantizes the token leaving the window), then the
+    # cross-split merge.  kvq_decode_step_partials + kvq_decode_combine are exactly its two
+    # launches; calling them apart lets HIP events bracket the split kernel alone.  The same steps
+    # through separate launches (append kernel, kvq_decode_partials, kvq_decode_combine) are timed
+    # next for comparison.  Arguments are marshalled before timing (bound_call), so the Python loop
+    # stays ahead of the GPU.
+    def step_fused(s, c=cache):
+        return (
+            K.bound_call("kvq_decode_step_partials", params, c.struct, lens[s], k_steps[s], v_steps[s], L0 + s + 1,
+                         q_steps[s], K.KVQ_BF16, 0.0, ws, ws_bytes, stream=stream),
+            K.bound_call("kvq_decode_combine", params, B, L0 + s + 1, K.KVQ_BF16, ws, out, K.KVQ_F32,
+                         stream=stream),
+        )
+
+    def step_separate(s, c=cache):
         return (
             K.bound_call("kvq_quantize_append", params, c.struct, lens[s], None, k_steps[s], v_steps[s], 1,
                          stream=stream),
@@ -470,40 +547,50 @@ def main():
                          stream=stream),
         )
 
-    for s in range(args.warmup):
-        for f in phases(s):
-            f()
-    timed = [phases(args.warmup + i) for i in range(args.steps)]
-    torch.cuda.synchronize()
+    def run_steps(steps):
+        """Wall-clock and event µs per step of back-to-back steps (no event between launches: on
+        this runtime an event record delays the next dispatch by a few microseconds)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for st_ in steps:
+            for f in st_:
+                f()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / len(steps) * 1e6, ev[0].elapsed_time(ev[1]) * 1e3 / len(steps)
 
-    # ---- timed region: K whole steps ------------------------------------------------
-    # No event between the launches of a step: on this runtime an event record delays the next
-    # dispatch by a few microseconds, which would be charged to the step.
-    ev_all = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev_all[0].record(stream)
-    for i in range(args.steps):
-        for f in timed[i]:
+    dispatch_plan = []  # split-kernel launches of each phase, in launch order (for kernel traces)
+
+    def plan(phase, launches, untimed_first=0):
+        dispatch_plan.append({"phase": phase, "launches": int(launches), "untimed_first": int(untimed_first)})
+
+    for s in range(args.warmup):
+        for f in step_fused(s):
             f()
-    ev_all[1].record(stream)
+    plan("warm-up fused steps", args.warmup, args.warmup)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_us_per_step = ev_all[0].elapsed_time(ev_all[1]) * 1e3 / args.steps
-    us_per_step = wall / args.steps * 1e6
+    gclone = None if args.no_graph else clone_cache(K, torch, cache, params, B, cap)  # state before the timed steps
+
+    # ---- timed region: K whole fused steps ----------------------------------------------
+    us_per_step, gpu_us_per_step = run_steps([step_fused(args.warmup + i) for i in range(args.steps)])
+    plan("timed fused steps", args.steps)
+    s0 = args.warmup + args.steps
+    sep_us_per_step, sep_gpu_us = run_steps([step_separate(s0 + i) for i in range(args.steps)])
+    plan("timed separate-launch steps", args.steps)
     L_last = L0 + total_steps  # every sequence's length after the last step
 
-    # ---- the same K steps captured once in a HIP graph and replayed (no per-launch dispatch
-    # from the host; the cache state then repeats the last steps' appends, which is the same work).
+    # ---- the timed fused steps captured once in a HIP graph and replayed on a copy of the cache
+    # taken before them (the second replay repeats the same appends: the same work).
     graph_us_per_step = None
-    if not args.no_graph:
+    if gclone is not None:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(args.steps):
                 s_ = args.warmup + i
-                K.kvq_quantize_append(params, cache.struct, lens[s_], None, k_steps[s_], v_steps[s_], 1)
-                K.kvq_decode_partials(params, cache.struct, lens[s_ + 1], L0 + s_ + 1, q_steps[s_], K.KVQ_BF16,
-                                      0.0, ws, ws_bytes)
+                K.kvq_decode_step_partials(params, gclone.struct, lens[s_], k_steps[s_], v_steps[s_], L0 + s_ + 1,
+                                           q_steps[s_], K.KVQ_BF16, 0.0, ws, ws_bytes)
                 K.kvq_decode_combine(params, B, L0 + s_ + 1, K.KVQ_BF16, ws, out, K.KVQ_F32)
         g.replay()  # warm
         torch.cuda.synchronize()
@@ -513,35 +600,55 @@ def main():
         ev_g[1].record(stream)
         torch.cuda.synchronize()
         graph_us_per_step = ev_g[0].elapsed_time(ev_g[1]) * 1e3 / args.steps
-        del g
+        plan("graph replays of the fused steps", 2 * args.steps, args.steps)
+        del g, gclone
+        torch.cuda.synchronize()
 
     # ---- the dominant kernel alone, at the last step's state -----------------------------
-    # warm: the last step's split-K launch repeated back to back (it only reads the cache and
-    # rewrites the workspace); cold: the same launch cycling over copies of the cache whose total
-    # is far above the Infinity Cache, so every launch streams its cache from HBM.
+    # The fused split kernel of a step at length L_last (append of the token at L_last - 1 + attention
+    # over L_last tokens), run on copies of the cache (it rewrites a ring slot and one token of a
+    # record each time: the same work on every repetition).  warm: repeated on one copy; cold:
+    # cycling over copies whose total is far above the Infinity Cache, so every launch streams its
+    # cache from HBM.  The attention-only split kernel (kvq_decode_partials, read-only) is timed the
+    # same way.
     per_th = (d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4)
-    launch_bytes = split_kernel_bytes(wl, L_last, per_th, 2)  # the timed launch
-    last_partials = timed[-1][1]
-    split_warm_us = time_calls(torch, [last_partials], reps, stream)
+    attn_bytes = split_kernel_bytes(wl, L_last, per_th, 2)
+    # + per unit: the evicted row read from the ring and the new row written to it (the evicted
+    # token's 116 B record write replaces its read in attn_bytes)
+    launch_bytes = attn_bytes + B * Hkv * 2 * (2 * d * 2)
     n_cp = copies_for(launch_bytes)
-    copies = [cache] + [clone_cache(K, torch, cache, params, B, cap) for _ in range(n_cp - 1)]
+    copies = [clone_cache(K, torch, cache, params, B, cap) for _ in range(n_cp)]
     torch.cuda.synchronize()
-    cold_calls = [K.bound_call("kvq_decode_partials", params, c.struct, lens[-1], L_last, q_steps[-1], K.KVQ_BF16,
+    sl = total_steps - 1
+    fused_calls = [K.bound_call("kvq_decode_step_partials", params, c.struct, lens[sl], k_steps[sl], v_steps[sl],
+                                L_last, q_steps[sl], K.KVQ_BF16, 0.0, ws, ws_bytes, stream=stream) for c in copies]
+    attn_calls = [K.bound_call("kvq_decode_partials", params, c.struct, lens[-1], L_last, q_steps[-1], K.KVQ_BF16,
                                0.0, ws, ws_bytes, stream=stream) for c in copies]
-    split_cold_us = time_rotating(torch, cold_calls, reps, stream)
-    combine_us = time_calls(torch, [timed[-1][2]], reps, stream)
-    # the separate 1-token append (on a copy of the cache: it rewrites a ring slot and a record)
-    app_copy = copies[1]
-    app_call = K.bound_call("kvq_quantize_append", params, app_copy.struct, lens[-2], None, k_steps[-1],
-                            v_steps[-1], 1, stream=stream)
+    split_warm_us = time_calls(torch, fused_calls[:1], reps, stream)
+    plan("fused split kernel, warm", 1 + reps, 1)
+    split_cold_us = time_rotating(torch, fused_calls, reps, stream)
+    plan("fused split kernel, cold", n_cp + reps, n_cp)
+    attn_warm_us = time_calls(torch, attn_calls[:1], reps, stream)
+    plan("attention-only split kernel, warm", 1 + reps, 1)
+    attn_cold_us = time_rotating(torch, attn_calls, reps, stream)
+    plan("attention-only split kernel, cold", n_cp + reps, n_cp)
+    combine_call = K.bound_call("kvq_decode_combine", params, B, L_last, K.KVQ_BF16, ws, out, K.KVQ_F32,
+                                stream=stream)
+    combine_us = time_calls(torch, [combine_call], reps, stream)
+    # the separate 1-token append (on a copy of the cache)
+    app_call = K.bound_call("kvq_quantize_append", params, copies[0].struct, lens[sl], None, k_steps[sl],
+                            v_steps[sl], 1, stream=stream)
     append_us = time_calls(torch, [app_call], reps, stream)
-    timed[-1][2]()  # restore the last step's output from the workspace
-    torch.cuda.synchronize()
-    del copies, cold_calls, app_copy
+    del copies, fused_calls, attn_calls
+    # restore the last step's output (merge of the last separate step's partials)
+    for f in step_separate(total_steps - 1)[1:]:
+        f()
+    plan("restore the last step's output", 1)
     torch.cuda.synchronize()
     ceiling = stream_ceiling(torch, launch_bytes, stream, reps)
     ceil_GBs = ceiling["best"]["cold_GBs"]
     split_rf = kernel_roofline(split_cold_us, split_warm_us, launch_bytes, ceil_GBs)
+    attn_rf = kernel_roofline(attn_cold_us, attn_warm_us, attn_bytes, ceil_GBs)
 
     # ---- unfused baseline at the last step's state: the fused attention (split kernel + merge)
     # against dequantize-to-dense-bf16 + dense attention over the same cache and query.
@@ -557,12 +664,13 @@ def main():
         deq = K.bound_call("kvq_dequantize_dense", params, cache.struct, lens_last, L_last, kd, vd, stream=stream)
         dense = K.bound_call("kvq_dense_decode_attention", params, B, kd, vd, lens_last, L_last, q_last, K.KVQ_BF16,
                              out_u, K.KVQ_F32, 0.0, dw, dws, stream=stream)
-        fused = (timed[-1][1], timed[-1][2])
+        fused = step_separate(total_steps - 1)[1:]  # kvq_decode_partials + kvq_decode_combine
         fused_us = time_calls(torch, fused, 5, stream)
+        plan("unfused comparison: fused attention", 6, 1)
         deq_us = time_calls(torch, [deq], 5, stream)
         dense_us = time_calls(torch, [dense], 5, stream)
         both_us = time_calls(torch, [deq, dense], 5, stream)
-        timed[-1][2]()
+        fused[1]()
         torch.cuda.synchronize()
         diff = float((out_u - out).abs().max())
         units = B * Hkv
@@ -631,7 +739,7 @@ def main():
     except (OSError, ValueError):
         pass
 
-    attn_cold_us = split_cold_us + combine_us
+    step_cold_us = split_cold_us + combine_us  # the two launches of a cold decode step
     res = {
         "metric": METRIC,
         "value": round(us_per_step, 2),
@@ -649,23 +757,29 @@ def main():
         "config": {"workload": f"b16-gqa32x8-L{L0}-win{R}-{args.warmup}+{args.steps}steps", "batch": B,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "context": L0, "window": R, "k_bits": wl.k_bits,
                    "k_group": wl.k_group, "v_bits": wl.v_bits, "v_group": wl.v_group,
-                   "step": "append 1 token/sequence + decode attention"},
+                   "step": "kvq_decode_step: append 1 token/sequence fused into the split-K attention launch, "
+                           "then the merge launch"},
         "gpu_us_per_step": round(gpu_us_per_step, 2),
         "graph_us_per_step": None if graph_us_per_step is None else round(graph_us_per_step, 2),
+        "separate_launch_step": {"what": "the same steps as append kernel + kvq_decode_partials + "
+                                         "kvq_decode_combine (three launches), the next K steps",
+                                 "us_per_step": round(sep_us_per_step, 2), "gpu_us_per_step": round(sep_gpu_us, 2)},
         "split_kernel_us_cold": round(split_cold_us, 2),
         "split_kernel_us_warm": round(split_warm_us, 2),
+        "attention_split_kernel": dict(attn_rf, what="kvq_decode_partials at the same length (attention only, "
+                                                     "read-only)"),
         "combine_us": round(combine_us, 2),
-        "decode_append_us": round(append_us, 2),
+        "decode_append_us_separate_kernel": round(append_us, 2),
         "tokens_per_s": round(B / (us_per_step * 1e-6), 1),
-        "effective_tokens_per_s": round(B * L_last / (attn_cold_us * 1e-6), 1),
+        "effective_tokens_per_s": round(B * L_last / (step_cold_us * 1e-6), 1),
         "effective_tokens_per_s_step": round(B * L_last / (us_per_step * 1e-6), 1),
-        "roofline": {"kernel": SPLIT_KERNEL + " (decode split-K attention)",
+        "roofline": {"kernel": SPLIT_KERNEL + " (decode step: split-K attention with the 1-token append fused in)",
                      "bound": "hbm", "achieved": split_rf["GBs_cold"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": split_rf["frac_cold"], "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(launch_bytes),
-                     "timing": f"cold: {reps} back-to-back launches of the last step's split kernel cycling over "
-                               f"{n_cp} copies of the cache ({n_cp * launch_bytes / 1e9:.2f} GB, far above the "
-                               f"256 MB Infinity Cache), between two events",
+                     "timing": f"cold: {reps} back-to-back launches of a step's split kernel at L={L_last} cycling "
+                               f"over {n_cp} copies of the cache ({n_cp * launch_bytes / 1e9:.2f} GB, far above "
+                               f"the 256 MB Infinity Cache), between two events",
                      "achieved_warm": split_rf["GBs_warm"], "frac_warm": split_rf["frac_warm"],
                      "stream_ceiling_GBs": ceil_GBs, "stream_ceiling_frac": round(ceil_GBs / PEAK_HBM_GBS, 4),
                      "frac_of_stream_ceiling": split_rf["frac_of_stream_ceiling_cold"]},
@@ -687,6 +801,7 @@ def main():
         res["error_budget_bit_pairs"] = error_budget_sweep(dev)
     if cpu_res is not None:
         res["cpu_baseline"] = cpu_res
+    res["split_kernel_dispatch_plan"] = dispatch_plan
     print(json.dumps(res), flush=True)
 
 

@@ -216,6 +216,32 @@ kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache,
 kvq_status kvq_decode_combine(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype,
                               const void *workspace, void *out, int32_t out_dtype, hipStream_t stream);
 
+/* One decode step: append one token per sequence, then decode attention over the cache including
+ * it -- the same results as kvq_quantize_append(n_new = 1) followed by kvq_decode_attention at
+ * the lengths plus one, in fewer launches ([P1] "Pertumbuhan cache mengubah trade pada serving":
+ * the recent window, and dequantization fused into the attention kernel).
+ *   seq_lens_before: device int32 [batch], lengths L_b before the step (not modified; the caller
+ *                    advances them afterwards).
+ *   k_new, v_new:    device [batch][1][num_kv_heads][128] of kv_dtype, the token at position L_b.
+ *   max_seq_len:     host upper bound of L_b + 1 (sizes the launch, as for kvq_decode_attention).
+ *   q, out, softmax_scale, workspace: as for kvq_decode_attention (the same workspace size).
+ * With a bf16 window (window > 0) the append runs inside the split-K launch: the split holding
+ * the new token's ring slot quantizes the token leaving the window, stores it, attends it and
+ * writes the new token into the ring, while the other splits read the stored tokens before the
+ * step; then the merge launch.  Otherwise (no window, fp32 rings, or KVQ_WINDOW_FOLD=1) the
+ * append kernel runs first, then the split-K and merge launches.
+ * kvq_decode_step_partials stops before the merge: kvq_decode_combine(params, batch, max_seq_len,
+ * q_dtype, ...) completes it.  Errors as for kvq_decode_attention, plus KVQ_EINVAL for null or
+ * misaligned k_new / v_new; nothing is launched on an error. */
+kvq_status kvq_decode_step(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens_before,
+                           const void *k_new, const void *v_new, int64_t max_seq_len, const void *q, int32_t q_dtype,
+                           void *out, int32_t out_dtype, float softmax_scale, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+kvq_status kvq_decode_step_partials(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens_before,
+                                    const void *k_new, const void *v_new, int64_t max_seq_len, const void *q,
+                                    int32_t q_dtype, float softmax_scale, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
 /* Decode attention that allocates nothing, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same computation and launches as kvq_decode_attention, with the partial rows kept in a

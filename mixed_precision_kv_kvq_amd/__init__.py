@@ -35,6 +35,8 @@ EXPORTED = [
     "kvq_decode_partials",
     "kvq_decode_combine",
     "kvq_decode_attention_noalloc",
+    "kvq_decode_step",
+    "kvq_decode_step_partials",
     "kvq_dequantize_debug",
     "kvq_dequantize_dense",
     "kvq_dense_workspace_bytes",
@@ -114,6 +116,12 @@ def _load():
     lib.kvq_decode_attention_noalloc.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_int32,
                                                  c_void_p, c_int32, c_float, c_void_p]
     lib.kvq_decode_attention_noalloc.restype = c_int32
+    lib.kvq_decode_step.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_void_p, c_void_p, c_int64, c_void_p,
+                                    c_int32, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]
+    lib.kvq_decode_step.restype = c_int32
+    lib.kvq_decode_step_partials.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_void_p, c_void_p, c_int64,
+                                             c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]
+    lib.kvq_decode_step_partials.restype = c_int32
     lib.kvq_dequantize_debug.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int32, c_int64, c_int64, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.kvq_dequantize_debug.restype = c_int32
@@ -174,7 +182,7 @@ def bound_call(name: str, *args, stream=None):
     conv = [ctypes.byref(a) if isinstance(a, ctypes.Structure) else _ptr(a) if hasattr(a, "data_ptr") else a
             for a in args]
     if name in ("kvq_quantize_append", "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine",
-                "kvq_decode_attention_noalloc",
+                "kvq_decode_attention_noalloc", "kvq_decode_step", "kvq_decode_step_partials",
                 "kvq_dequantize_dense", "kvq_dense_decode_attention", "kvq_error_budget"):
         conv.append(_stream(stream))
     conv = tuple(conv)
@@ -245,6 +253,26 @@ def kvq_decode_combine(params, batch, max_seq_len, q_dtype, workspace, out, out_
                                  _ptr(out), int(out_dtype), _stream(stream))
     if check:
         _check(st, "kvq_decode_combine")
+    return st
+
+
+def kvq_decode_step(params, cache, seq_lens_before, k_new, v_new, max_seq_len, q, q_dtype, out, out_dtype,
+                    softmax_scale, workspace, workspace_bytes, stream=None, check=True):
+    st = _lib.kvq_decode_step(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens_before), _ptr(k_new),
+                              _ptr(v_new), int(max_seq_len), _ptr(q), int(q_dtype), _ptr(out), int(out_dtype),
+                              float(softmax_scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "kvq_decode_step")
+    return st
+
+
+def kvq_decode_step_partials(params, cache, seq_lens_before, k_new, v_new, max_seq_len, q, q_dtype, softmax_scale,
+                             workspace, workspace_bytes, stream=None, check=True):
+    st = _lib.kvq_decode_step_partials(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens_before), _ptr(k_new),
+                                       _ptr(v_new), int(max_seq_len), _ptr(q), int(q_dtype), float(softmax_scale),
+                                       _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "kvq_decode_step_partials")
     return st
 
 

@@ -192,9 +192,20 @@ size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64
   return (size_t)batch * params->num_q_heads * (size_t)bound * KVQ_PART_STRIDE * sizeof(float);
 }
 
-kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
-                               int64_t max_seq_len, const void *q, int32_t q_dtype, float softmax_scale,
-                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode steps fuse their append into the attention launch for bf16 rings (window > 0) with the
+// window in splits of its own; otherwise the append kernel runs first.
+bool step_fusable(const kvq_params *p) { return p->window > 0 && p->kv_dtype == KVQ_BF16 && !fold_allowed(p); }
+
+// The split-kernel launch of kvq_decode_partials (step = 0) or of a decode step (step = 1: lengths
+// before the step, attended at length + 1; k_new / v_new appended in the same launch when fuse).
+kvq_status partials_impl(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                         int64_t max_seq_len, const void *q, int32_t q_dtype, float softmax_scale, void *workspace,
+                         size_t workspace_bytes, int step, const void *k_new, const void *v_new, bool fuse,
+                         hipStream_t stream, bool validate_only = false) {
   if (kvq_status st = check_params(params)) return st;
   if (kvq_status st = check_cache(params, cache)) return st;
   if (!seq_lens || !q || !workspace || max_seq_len < 0) return KVQ_EINVAL;
@@ -229,8 +240,67 @@ kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache,
   a.max_len = (int32_t)(max_seq_len < INT32_MAX ? max_seq_len : INT32_MAX);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
   a.sigma_u = (float)((double)scale * 1.4426950408889634 * 8589934592.0);  // * log2(e) * 2^33
+  a.k_new = (const uint8_t *)k_new;
+  a.v_new = (const uint8_t *)v_new;
+  a.fuse = fuse ? 1 : 0;
+  a.len_plus1 = step;
+  if (step && max_seq_len < 1) return KVQ_EINVAL;
+  if (validate_only) return KVQ_OK;
   const int g = params->num_q_heads / params->num_kv_heads;
   return hip_status(kvq_launch_attention(a, g, q_parts, stream));
+}
+
+// Validation and launches of a decode step up to (not including) the merge.
+kvq_status step_impl(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens_before,
+                     const void *k_new, const void *v_new, int64_t max_seq_len, const void *q, int32_t q_dtype,
+                     float softmax_scale, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (kvq_status st = check_params(params)) return st;
+  if (kvq_status st = check_cache(params, cache)) return st;
+  if (!seq_lens_before || !k_new || !v_new || !aligned16(k_new) || !aligned16(v_new) || max_seq_len < 1)
+    return KVQ_EINVAL;
+  if (step_fusable(params))
+    return partials_impl(params, cache, seq_lens_before, max_seq_len, q, q_dtype, softmax_scale, workspace,
+                         workspace_bytes, 1, k_new, v_new, true, stream);
+  // Validate the attention half before the append launches anything.
+  if (kvq_status st = partials_impl(params, cache, seq_lens_before, max_seq_len, q, q_dtype, softmax_scale,
+                                    workspace, workspace_bytes, 1, nullptr, nullptr, false, stream, true))
+    return st;
+  if (kvq_status st = kvq_quantize_append(params, cache, seq_lens_before, nullptr, k_new, v_new, 1, stream)) return st;
+  return partials_impl(params, cache, seq_lens_before, max_seq_len, q, q_dtype, softmax_scale, workspace,
+                       workspace_bytes, 1, nullptr, nullptr, false, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
+                               int64_t max_seq_len, const void *q, int32_t q_dtype, float softmax_scale,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return partials_impl(params, cache, seq_lens, max_seq_len, q, q_dtype, softmax_scale, workspace, workspace_bytes,
+                       0, nullptr, nullptr, false, stream);
+}
+
+kvq_status kvq_decode_step_partials(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens_before,
+                                    const void *k_new, const void *v_new, int64_t max_seq_len, const void *q,
+                                    int32_t q_dtype, float softmax_scale, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  return step_impl(params, cache, seq_lens_before, k_new, v_new, max_seq_len, q, q_dtype, softmax_scale, workspace,
+                   workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_step(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens_before,
+                           const void *k_new, const void *v_new, int64_t max_seq_len, const void *q, int32_t q_dtype,
+                           void *out, int32_t out_dtype, float softmax_scale, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (!out || !aligned16(out) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16)) {
+    if (kvq_status st = check_params(params)) return st;
+    return KVQ_EINVAL;
+  }
+  if (kvq_status st = step_impl(params, cache, seq_lens_before, k_new, v_new, max_seq_len, q, q_dtype, softmax_scale,
+                                workspace, workspace_bytes, stream))
+    return st;
+  return kvq_decode_combine(params, cache->batch, max_seq_len, q_dtype, workspace, out, out_dtype, stream);
 }
 
 int32_t kvq_decode_splits(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype) {

@@ -38,7 +38,7 @@
 // Every code and metadata operand comes from one 4- to 16-byte read per lane of the
 // page record (see kvq_layout.h for the order of the record's words).
 #pragma once
-#include "kvq_internal.h"
+#include "kvq_quant.h"
 
 namespace kvq_attn {
 
@@ -653,9 +653,13 @@ struct Kern {
   // operand, weights through the exchange buffer as for the quantized pages, accumulated in
   // st.acc); those of an fp32 ring are accumulated on the VALU in ow.  Value data is requested
   // before the scores are computed, so its latency overlaps the key loads and the MFMAs.
+  // s_new >= 0 (bf16 rings only): ring slot whose token is read from knew / vnew instead (the
+  // token appended by a fused decode step, written to that slot by this launch).
   template <bool F32>
   static __device__ __forceinline__ void window_chunk(const Ctx &cx, St &st, float (*ow)[2], const uint8_t *kwin,
-                                                      const uint8_t *vwin, int w0, int wend) {
+                                                      const uint8_t *vwin, int w0, int wend, int s_new = -1,
+                                                      const uint8_t *knew = nullptr,
+                                                      const uint8_t *vnew = nullptr) {
     const int nval = (wend - w0) < 32 ? (wend - w0) : 32;
     // fp32: this lane's two channels of value row w0 + t (rows past the end re-read row w0)
     constexpr int VT = G * P >= 16 ? 8 : 16;  // value rows in registers at a time
@@ -672,7 +676,8 @@ struct Kern {
       for (int j = 0; j < 8; ++j) {
         int t = j < 4 ? 4 * cx.quad + j : 16 + 4 * cx.quad + (j - 4);
         t = t < nval ? t : 0;  // rows past the end re-read row w0 (their weight is 0)
-        vrow[j] = reinterpret_cast<const uint16_t *>(vwin) + (size_t)(w0 + t) * KVQ_D + cx.col;
+        vrow[j] = (w0 + t == s_new) ? reinterpret_cast<const uint16_t *>(vnew) + cx.col
+                                    : reinterpret_cast<const uint16_t *>(vwin) + (size_t)(w0 + t) * KVQ_D + cx.col;
       }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -727,8 +732,9 @@ struct Kern {
         }
       } else {
         u32x4 kr[4];
+        const uint8_t *krow = slot == s_new ? knew : kwin + (size_t)slot * KVQ_D * 2;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) kr[kc] = gload<u32x4>(kwin + ((size_t)slot * KVQ_D + 32 * kc + 8 * cx.quad) * 2);
+        for (int kc = 0; kc < 4; ++kc) kr[kc] = gload<u32x4>(krow + (32 * kc + 8 * cx.quad) * 2);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
@@ -856,6 +862,100 @@ struct Kern {
     }
   }
 
+  // ---- fused decode step ---------------------------------------------------------------
+  // LDS of a window split beyond the staged query ([G][128] fp32): a page record holding only the
+  // token that leaves the window (at token slot 0), then that token's codes and metadata words.
+  static constexpr int VREC_OFF = G * KVQ_D * 4;
+  static constexpr int QSCR_OFF = VREC_OFF + 16 * MAX_REC16;
+  static_assert(QSCR_OFF + 2 * KVQ_D + 4 * 4 + 2 * 4 <= XCHG_OFF, "fused-step scratch overlaps the exchange buffer");
+
+  // The append of a fused decode step, by the window split whose range holds the new token's ring
+  // slot s_new = Lb mod R (Lb = length before the step).  When the ring is full (Lb >= R) the
+  // token in that slot, position Lb - R, leaves the window: it is read from the ring (before the
+  // slot is overwritten: same lanes, same addresses, its loads waited for), rotated if keys are,
+  // quantized with the append kernels' fp64 sequence, written into its page record (token slot
+  // (Lb - R) mod 16; other splits of this launch read that page only with the token masked out)
+  // and into a one-token record at VREC_OFF for evicted_pair.  The new token is written to slot
+  // s_new.  Returns whether a token left the window.
+  static __device__ bool fused_append(const KvqAttnArgs &args, uint8_t *smem, int b, int kvh, int Lb, int s_new) {
+    const int lane = threadIdx.x, R = args.R, Hkv = args.Hkv;
+    const KvqLayout &lay = args.lay;
+    const size_t row = (size_t)KVQ_D * 2, unit = (size_t)b * Hkv + kvh;
+    uint8_t *kslot = args.cache.k_win + (unit * R + s_new) * row;
+    uint8_t *vslot = args.cache.v_win + (unit * R + s_new) * row;
+    const bool evict = Lb >= R;
+    uint32_t ko = 0, vo = 0;
+    if (evict) {
+      ko = gload<uint32_t>(kslot + 4 * lane);
+      vo = gload<uint32_t>(vslot + 4 * lane);
+    }
+    const uint32_t kn = gload<uint32_t>(args.k_new + unit * row + 4 * lane);
+    const uint32_t vn = gload<uint32_t>(args.v_new + unit * row + 4 * lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the old token is in registers before the slot is written
+    *reinterpret_cast<uint32_t *>(kslot + 4 * lane) = kn;
+    *reinterpret_cast<uint32_t *>(vslot + 4 * lane) = vn;
+    if (!evict) return false;
+    double k0 = (double)kvq_bf16_bits_to_f32(ko & 0xFFFFu), k1 = (double)kvq_bf16_bits_to_f32(ko >> 16);
+    const double v0 = (double)kvq_bf16_bits_to_f32(vo & 0xFFFFu), v1 = (double)kvq_bf16_bits_to_f32(vo >> 16);
+    if (args.rotation) kvq_wht128_fp64(k0, k1, lane);
+    uint32_t a0, a1, am, b0, b1, bm;
+    kvq_quant::quantize_pair(k0, k1, lay.kb, lay.kg, &a0, &a1, &am);
+    kvq_quant::quantize_pair(v0, v1, lay.vb, lay.vg, &b0, &b1, &bm);
+    uint8_t *ck = smem + QSCR_OFF, *cv = ck + KVQ_D;
+    uint32_t *mk = reinterpret_cast<uint32_t *>(cv + KVQ_D), *mv = mk + 4;
+    ck[2 * lane] = (uint8_t)a0;
+    ck[2 * lane + 1] = (uint8_t)a1;
+    cv[2 * lane] = (uint8_t)b0;
+    cv[2 * lane + 1] = (uint8_t)b1;
+    if (((2 * lane) % lay.kg) == 0) mk[(2 * lane) / lay.kg] = am;
+    if (((2 * lane) % lay.vg) == 0) mv[(2 * lane) / lay.vg] = bm;
+    uint32_t *vrec = reinterpret_cast<uint32_t *>(smem + VREC_OFF);
+    for (int w = lane; w < lay.record / 4; w += 64) vrec[w] = 0u;
+    __syncthreads();
+    const int64_t t_ev = (int64_t)Lb - R, page = t_ev / KVQ_PAGE;
+    if (page < (args.cache.paged ? (int64_t)args.cache.mbps : args.cache.pages_per_seq)) {
+      const int64_t ri = kvq_record_index_dev(args.cache, Hkv, b, kvh, page);
+      kvq_quant::kvq_write_token(args.cache.pages + (size_t)ri * lay.record, lay, (int)(t_ev % KVQ_PAGE), ck, cv, mk,
+                                 mv, lane);
+    } else {
+      kvq_raise(args.cache, true, KVQ_DEV_CAPACITY);  // not stored (still attended below)
+    }
+    kvq_quant::kvq_write_token(smem + VREC_OFF, lay, 0, ck, cv, mk, mv, lane);
+    __syncthreads();
+    return true;
+  }
+
+  // Attention over the token that left the window (the one-token record at VREC_OFF), on top of
+  // the window tokens already in st: the value accumulators are brought from the window's scale
+  // to the scale of the code contractions (exact power-of-two multiplies, as for a folded window
+  // block), the code-scaled query operand (rotated when keys are) is built, and the record goes
+  // through the masked pair path with one valid token.
+  template <int KS>
+  static __device__ __forceinline__ void evicted_pair(const KvqAttnArgs &args, Ctx &cx, St &st, uint8_t *smem,
+                                                      int b, int hq0) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float f = __builtin_amdgcn_ldexpf(1.0f, vtile_scale(m) - 66);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.acc[m][r] = st.acc[m][r] * f * EXP2_M67;
+    }
+    float *lds = reinterpret_cast<float *>(smem);
+    stage_q(args, lds, b, hq0, args.rotation != 0);
+    build_q(cx, lds);
+    float Qg[HB][4];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) Qg[hb][g] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Qg[hb][r >> KS] += cx.Qc[hb][r];
+    }
+    const RecOff ro = rec_offsets<KS>(cx, args.lay);
+    PageData<KS> A;
+    read_page_at(A, (uint32_t)(uintptr_t)smem + VREC_OFF, ro);
+    process_pair<KS, true>(cx, st, Qg, A, A, 1, 0);
+  }
+
   // Queries of the G heads of kv head kvh -> LDS (fp32 [G][128]); rotated when `rotate`.
   static __device__ __forceinline__ void stage_q(const KvqAttnArgs &args, float *qs, int b, int hq0, bool rotate) {
     const int lane = threadIdx.x;
@@ -902,12 +1002,15 @@ struct Kern {
     const KvqLayout &lay = args.lay;
     const int R = args.R;
     int L = args.seq_lens[b];
-    // a length outside [0, max_len] is clamped (reported once per unit, by its split 0)
-    kvq_raise(args.cache, split == 0 && (L < 0 || L > args.max_len), KVQ_DEV_LENGTH);
-    L = L < 0 ? 0 : (L > args.max_len ? args.max_len : L);
+    // a length outside [0, max_len] is clamped (reported once per unit, by its split 0); in a fused
+    // step the lengths are those before the appended token: [0, max_len - 1]
+    const int lmax = args.max_len - args.len_plus1;
+    kvq_raise(args.cache, split == 0 && (L < 0 || L > lmax), KVQ_DEV_LENGTH);
+    L = L < 0 ? 0 : (L > lmax ? lmax : L);
+    const int Lb = L;  // decode step: length before the step
+    L += args.len_plus1;
     const int nq = L > R ? L - R : 0;
     const int nw = L < R ? L : R;
-    const int qpages = (nq + KVQ_PAGE - 1) / KVQ_PAGE;
     const int wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;
     // Window splits first, then quantized splits (see the host split plan).  With the window
     // folded into the quantized splits there are no window splits.
@@ -945,6 +1048,17 @@ struct Kern {
       float ow[G][2];
 #pragma unroll
       for (int h = 0; h < G; ++h) ow[h][0] = ow[h][1] = 0.f;
+      // Fused step: the new token sits in ring slot s_new; it is read from k_new / v_new (this
+      // launch writes the slot), and the split holding that slot also does the append.
+      int s_new = -1;
+      bool evicted = false;
+      const uint8_t *knew = nullptr, *vnew = nullptr;
+      if (args.fuse) {
+        s_new = Lb % R;
+        knew = args.k_new + ((size_t)b * Hkv + kvh) * KVQ_D * 2;
+        vnew = args.v_new + ((size_t)b * Hkv + kvh) * KVQ_D * 2;
+        if (split == s_new / (KVQ_WIN_PAGES * KVQ_PAGE)) evicted = fused_append(args, smem, b, kvh, Lb, s_new);
+      }
       if (wv1 > wv0) {
         stage_q(args, lds, b, hq0, false);
         build_q(cx, lds, false);
@@ -954,8 +1068,19 @@ struct Kern {
           if (args.kv_f32)
             window_chunk<true>(cx, st, ow, args.cache.k_win + win_off, args.cache.v_win + win_off, w, wend);
           else
-            window_chunk<false>(cx, st, ow, args.cache.k_win + win_off, args.cache.v_win + win_off, w, wend);
+            window_chunk<false>(cx, st, ow, args.cache.k_win + win_off, args.cache.v_win + win_off, w, wend, s_new,
+                                knew, vnew);
         }
+      }
+      if (evicted) {
+        if (lay.kg == 32)
+          evicted_pair<0>(args, cx, st, smem, b, hq0);
+        else if (lay.kg == 64)
+          evicted_pair<1>(args, cx, st, smem, b, hq0);
+        else
+          evicted_pair<2>(args, cx, st, smem, b, hq0);
+        write_partial<PART_CODES>(args, cx, st, nullptr, lds, b, kvh, split);
+        return;
       }
       if (args.kv_f32)
         write_partial<PART_WIN_VALU>(args, cx, st, ow, lds, b, kvh, split);
@@ -967,14 +1092,18 @@ struct Kern {
     // Quantized splits take full-page pairs round-robin: pair sq, sq + SQ, sq + 2 SQ, ... so that at
     // any moment the waves of one unit read neighbouring pairs.
     const int SQ = S - args.wsplits, sq = split - args.wsplits;
-    const int full_pages = nq / KVQ_PAGE;  // pages with all 16 tokens quantized
+    // Fused step: the token leaving the window is stored and attended by the window split; the
+    // quantized splits cover the tokens stored before the step.
+    const int nqs = args.fuse ? (Lb > R ? Lb - R : 0) : nq;
+    const int qpages_s = (nqs + KVQ_PAGE - 1) / KVQ_PAGE;
+    const int full_pages = nqs / KVQ_PAGE;  // pages with all 16 tokens quantized
     const int tp = full_pages / 2;         // full pairs of this sequence
     // Pairs of full pages, next pairs prefetched while the current one is processed.  The 1-2
     // pages after the last full pair (an odd full page and/or the partial page) form one masked
     // pair; it goes to the split next in the rotation, whose cursor reaches it right after its
     // full pairs, so it streams through the same ring.
     const int npairs = tp > sq ? (tp - sq + SQ - 1) / SQ : 0;
-    const bool tail = sq == tp % SQ && 2 * tp < qpages;
+    const bool tail = sq == tp % SQ && 2 * tp < qpages_s;
     // Folded window (bf16 rings): 16-token block i of the ring goes to split SQ - 1 - i, the
     // splits that end the pair rotation and so have at most as many pairs as the others.
     WinBlock wb;
@@ -993,8 +1122,9 @@ struct Kern {
       int tail_va = 0, tail_vb = 0;
       if (tail) {
         const int p = 2 * tp;
-        tail_va = (nq - p * KVQ_PAGE) < KVQ_PAGE ? (nq - p * KVQ_PAGE) : KVQ_PAGE;
-        tail_vb = p + 1 < qpages ? ((nq - (p + 1) * KVQ_PAGE) < KVQ_PAGE ? (nq - (p + 1) * KVQ_PAGE) : KVQ_PAGE) : 0;
+        tail_va = (nqs - p * KVQ_PAGE) < KVQ_PAGE ? (nqs - p * KVQ_PAGE) : KVQ_PAGE;
+        tail_vb = p + 1 < qpages_s ? ((nqs - (p + 1) * KVQ_PAGE) < KVQ_PAGE ? (nqs - (p + 1) * KVQ_PAGE) : KVQ_PAGE)
+                                   : 0;
       }
       // The query operand is built while the first pages stream in: without rotation the
       // query loads are issued before the prologue DMAs (vmcnt retires them first); with

@@ -87,6 +87,11 @@ struct KvqAttnArgs {
   int32_t wfold;                     // 1: no window splits; 16-token window blocks go to the quantized splits
   int32_t max_len;  // host-validated upper bound of seq_lens (device lengths are clamped to it)
   float sigma_u;  // softmax_scale * log2(e) * 2^33
+  // Fused decode step (fuse = 1; bf16 rings, window > 0): seq_lens are the lengths before the
+  // step, k_new / v_new [B][1][Hkv][128] bf16 the appended token, attended at length + 1.
+  const uint8_t *k_new, *v_new;
+  int32_t fuse;
+  int32_t len_plus1;  // attend at seq_lens[b] + 1 (a decode step; set whenever fuse is)
 };
 
 

@@ -144,6 +144,39 @@ class GpuRun:
         q = self._q_dev(step)
         return self.attend(seq_lens, int(L.max()), q, out_dtype)
 
+    def decode_step(self, step: int, out_dtype: str = "f32", phases: bool = False) -> np.ndarray:
+        """One decode step through kvq_decode_step (append fused into the attention launch where it
+        applies), or through kvq_decode_step_partials + kvq_decode_combine when phases."""
+        wl = self.wl
+        pos = self.current_lengths()
+        k = self._rows_at(W.TENSOR_K, pos)
+        v = self._rows_at(W.TENSOR_V, pos)
+        before = torch.from_numpy(pos.astype(np.int32)).cuda()
+        max_len = int(pos.max()) + 1
+        ws_bytes = K.kvq_decode_workspace_bytes(self.params, wl.batch, max_len)
+        if getattr(self, "ws", None) is None or self.ws.numel() < ws_bytes:
+            self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim),
+                          dtype=torch.float32 if out_dtype == "f32" else torch.int16, device="cuda")
+        qd = K.KVQ_F32 if wl.q_dtype == "f32" else K.KVQ_BF16
+        od = K.KVQ_F32 if out_dtype == "f32" else K.KVQ_BF16
+        q = self._q_dev(step)
+        if phases:
+            K.kvq_decode_step_partials(self.params, self.cache.struct, before, k, v, max_len, q, qd, 0.0, self.ws,
+                                       ws_bytes)
+            K.kvq_decode_combine(self.params, wl.batch, max_len, qd, self.ws, out, od)
+        else:
+            K.kvq_decode_step(self.params, self.cache.struct, before, k, v, max_len, q, qd, out, od, 0.0, self.ws,
+                              ws_bytes)
+        torch.cuda.synchronize()
+        self.steps_done += 1
+        flags = self.cache.device_errors()
+        assert flags == 0, f"kernels reported device-side input errors: flags {flags:#x}"
+        o = out.cpu().numpy()
+        if out_dtype == "bf16":
+            return W.bf16_bits_to_f32(o.view(np.uint16))
+        return o
+
     def attend(self, seq_lens, max_len, q, out_dtype="f32") -> np.ndarray:
         wl = self.wl
         ws_bytes = K.kvq_decode_workspace_bytes(self.params, wl.batch, max_len)
