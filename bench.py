@@ -64,7 +64,7 @@ def source_digest():
     """Digest of the sources the split kernel is built from (invalidates stored counter data)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_kv_kvq_amd", "csrc")
-    for name in ("kvq_attn_impl.h", "kvq_layout.h", "kvq_internal.h", os.path.join("inst", "kvq_attn_k4v2.hip")):
+    for name in ("kvq_attn_impl.h", "kvq_layout.h", "kvq_internal.h", "kvq_quant.h", "kvq_attn_inst.hip"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -292,18 +292,20 @@ def cpu_baseline(wl, target_seconds=12.0, max_units=None, workers=None):
     }
 
 
-def error_budget_sweep(dev):
-    """kvq_error_budget over the bit pairs of the paged batch-8 workload (lengths 1k-16k, 3 key
-    outlier channels x10 per kv head): each pair's cache is filled by one append of every
-    sequence's rows, then diagnosed against those rows for decode step 0's query."""
+def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
+    """The paged batch-8 workload (lengths 1k-16k, 16-token pages through a random block table) for
+    each bit pair: its cache filled by one append of every sequence's rows; the decode attention's
+    split kernel (kvq_decode_partials, read-only) timed cold (cycling over copies of the page pool
+    far above the Infinity Cache) and warm, against the same launch with every split sized from the
+    longest sequence (KVQ_PAGES_PER_SPLIT=32, the plan before splits were sized per sequence); the
+    merge; and the error-budget diagnostics against the original rows for decode step 0's query."""
     import numpy as np
-    import torch
 
     import mixed_precision_kv_kvq_amd as K
     import workloads as W
     from workloads.device import DeviceGenerator
 
-    rows = []
+    rows, eb_rows = [], []
     for kb, vb in W.SWEEP_BITS:
         wl = W.WORKLOADS[4].with_bits(kb, vb)
         Lb = wl.context_lengths()
@@ -319,13 +321,53 @@ def error_budget_sweep(dev):
         before = torch.zeros(wl.batch, dtype=torch.int32, device=dev)
         n_new = torch.from_numpy(Lb.astype(np.int32)).to(dev)
         K.kvq_quantize_append(prm, cb.struct, before, n_new, k_ref, v_ref, Lmax)
+        q = gen.q(0)
+        per_th = wl.head_dim * kb // 8 + (wl.head_dim // wl.k_group) * 4 + wl.head_dim * vb // 8 \
+            + (wl.head_dim // wl.v_group) * 4
+        qpages = -(-Lb // 16)
+        nbytes = int(wl.num_kv_heads * (Lb.sum() * per_th + qpages.sum() * 4)
+                     + wl.batch * wl.num_q_heads * wl.head_dim * 2)
+        n_cp = copies_for(nbytes)
+        copies = [cb] + [clone_cache(K, torch, cb, prm, wl.batch, pool, table) for _ in range(n_cp - 1)]
+        wsb = K.kvq_decode_workspace_bytes(prm, wl.batch, Lmax)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+        calls = [K.bound_call("kvq_decode_partials", prm, c.struct, n_new, Lmax, q, K.KVQ_BF16, 0.0, ws, wsb,
+                              stream=stream) for c in copies]
+        warm = time_calls(torch, calls[:1], reps, stream)
+        cold = time_rotating(torch, calls, reps, stream)
+        plan(f"paged K{kb}V{vb}: warm", 1 + reps, 1)
+        plan(f"paged K{kb}V{vb}: cold", n_cp + reps, n_cp)
+        comb = time_calls(torch, [K.bound_call("kvq_decode_combine", prm, wl.batch, Lmax, K.KVQ_BF16, ws, out,
+                                               K.KVQ_F32, stream=stream)], reps, stream)
+        splits = K.kvq_decode_splits(prm, wl.batch, Lmax, K.KVQ_BF16)
+        old_env = os.environ.get("KVQ_PAGES_PER_SPLIT")
+        os.environ["KVQ_PAGES_PER_SPLIT"] = "32"
+        try:
+            wsb2 = K.kvq_decode_workspace_bytes(prm, wl.batch, Lmax)
+            ws2 = torch.empty(wsb2, dtype=torch.uint8, device=dev)
+            calls2 = [K.bound_call("kvq_decode_partials", prm, c.struct, n_new, Lmax, q, K.KVQ_BF16, 0.0, ws2, wsb2,
+                                   stream=stream) for c in copies]
+            cold_uniform = time_rotating(torch, calls2, reps, stream)
+            plan(f"paged K{kb}V{vb}: cold, uniform plan", n_cp + reps, n_cp)
+        finally:
+            if old_env is None:
+                os.environ.pop("KVQ_PAGES_PER_SPLIT", None)
+            else:
+                os.environ["KVQ_PAGES_PER_SPLIT"] = old_env
+        rf = kernel_roofline(cold, warm, nbytes, ceiling_GBs)
+        rows.append(dict(k_bits=kb, v_bits=vb, row_stride_splits=splits, combine_us=round(comb, 2),
+                         uniform_plan_us_cold=round(cold_uniform, 2),
+                         uniform_plan_frac_cold=round(nbytes / cold_uniform / 1e3 / PEAK_HBM_GBS, 4), **rf))
+        del copies, calls, calls2, ws2
+        # error-budget diagnostics on the same cache
         hs = torch.empty((wl.batch, wl.num_q_heads, K.KVQ_EB_HEAD), dtype=torch.float32, device=dev)
         us = torch.empty((wl.batch, wl.num_kv_heads, K.KVQ_EB_UNIT), dtype=torch.float32, device=dev)
-        K.kvq_error_budget(prm, cb.struct, n_new, Lmax, k_ref, v_ref, gen.q(0), K.KVQ_BF16, 0.0, hs, us)
+        K.kvq_error_budget(prm, cb.struct, n_new, Lmax, k_ref, v_ref, q, K.KVQ_BF16, 0.0, hs, us)
         torch.cuda.synchronize()
         h_ = hs.cpu().numpy().astype(np.float64)
         u_ = us.cpu().numpy().astype(np.float64)
-        rows.append({
+        eb_rows.append({
             "k_bits": kb, "v_bits": vb, "payload_bits_per_key_value_pair": kb + vb,
             "rel_reconstruction_error_keys": round(float(np.sqrt(u_[..., 0].sum() / u_[..., 4].sum())), 4),
             "rel_reconstruction_error_values": round(float(np.sqrt(u_[..., 1].sum() / u_[..., 5].sum())), 4),
@@ -335,9 +377,78 @@ def error_budget_sweep(dev):
             "median_rel_output_error_keys_only": round(float(np.median(h_[..., 4] / h_[..., 6])), 4),
             "median_rel_output_error_both": round(float(np.median(h_[..., 5] / h_[..., 6])), 4),
         })
-        del cb, k_ref, v_ref, table
+        del cb, k_ref, v_ref, table, ws
         torch.cuda.synchronize()
-    return {"workload": W.WORKLOADS[4].name, "query": "decode step 0", "rows": rows}
+    wl = W.WORKLOADS[4]
+    sweep = {"workload": wl.name, "lengths": [int(x) for x in wl.context_lengths()],
+             "what": "kvq_decode_partials (split kernel, read-only) per bit pair; algorithmic bytes = codes and "
+                     "metadata of every stored token-head + block-table entries + queries; cold: cycling over copies "
+                     "of the page pool; uniform plan: every split sized from the longest sequence",
+             "rows": rows}
+    ebs = {"workload": wl.name, "query": "decode step 0", "rows": eb_rows}
+    return sweep, ebs
+
+
+def rotated_131k(torch, dev, reps, stream, ceiling_GBs, plan):
+    """The batch-64 x 131072-token workload with rotated keys (64 query / 8 kv heads): bulk prefill of
+    the whole context (appends of 4096 tokens per sequence, inputs generated into HBM first, one
+    chunk at a time), then the decode attention's split kernel timed back to back on two copies of
+    the 7.8 GB cache (cold: every launch reads data far beyond the Infinity Cache) and the merge."""
+    import mixed_precision_kv_kvq_amd as K
+    import workloads as W
+    from workloads.device import DeviceGenerator
+
+    wl = W.WORKLOADS[5]
+    B, Hq, Hkv, d, L = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.context
+    prm = K.make_params(d, Hq, Hkv, wl.k_bits, wl.k_group, wl.v_bits, wl.v_group, 0, 1, K.KVQ_BF16, 0)
+    cb = K.CacheBuffers(prm, B, L)
+    gen = DeviceGenerator(wl)
+    chunk = 4096
+    kbuf = torch.empty((B, chunk, Hkv, d), dtype=torch.int16, device=dev)
+    vbuf = torch.empty_like(kbuf)
+    app_us = 0.0
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for t0 in range(0, L, chunk):
+        gen.kv(W.TENSOR_K, t0, chunk, out=kbuf)
+        gen.kv(W.TENSOR_V, t0, chunk, out=vbuf)
+        before = torch.full((B,), t0, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        K.kvq_quantize_append(prm, cb.struct, before, None, kbuf, vbuf, chunk)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        app_us += e[0].elapsed_time(e[1]) * 1e3
+    del kbuf, vbuf
+    per_th = d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4
+    prefill_bytes = B * Hkv * L * (2 * d * 2 + per_th)  # every row read once, its codes written once
+    q = gen.q(0)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    nbytes = B * Hkv * L * per_th + B * Hq * d * 2
+    copies = [cb, clone_cache(K, torch, cb, prm, B, L)]
+    wsb = K.kvq_decode_workspace_bytes(prm, B, L)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.int16, device=dev)
+    calls = [K.bound_call("kvq_decode_partials", prm, c.struct, lens, L, q, K.KVQ_BF16, 0.0, ws, wsb, stream=stream)
+             for c in copies]
+    cold = time_rotating(torch, calls, reps, stream)
+    plan("rotated 131k: cold", 2 + reps, 2)
+    warm = time_calls(torch, calls[:1], reps, stream)
+    plan("rotated 131k: warm", 1 + reps, 1)
+    comb = time_calls(torch, [K.bound_call("kvq_decode_combine", prm, B, L, K.KVQ_BF16, ws, out, K.KVQ_BF16,
+                                           stream=stream)], reps, stream)
+    del copies, calls, cb, ws
+    torch.cuda.synchronize()
+    rf = kernel_roofline(cold, warm, nbytes, ceiling_GBs)
+    return {"workload": wl.name, "what": "kvq_decode_partials (split kernel, read-only, rotated query) + "
+                                         "kvq_decode_combine (bf16 output); algorithmic bytes = codes and metadata "
+                                         "of every token-head + queries",
+            "split_kernel": rf, "combine_us": round(comb, 2), "attention_us_cold": round(cold + comb, 2),
+            "effective_tokens_per_s": round(B * L / ((cold + comb) * 1e-6), 1),
+            "prefill_quantize": {"what": f"{L // chunk} appends of {chunk} tokens per sequence (key rotation, fp64 "
+                                         f"quantizer), each between two events, inputs generated into HBM before "
+                                         f"each", "us": round(app_us, 1), "algorithmic_bytes": int(prefill_bytes),
+                                 "achieved_GBs": round(prefill_bytes / app_us / 1e3, 1),
+                                 "frac_of_peak": round(prefill_bytes / app_us / 1e3 / PEAK_HBM_GBS, 4)}}
 
 
 # --------------------------------------------------------------------------------------------
@@ -798,7 +909,11 @@ def main():
         res["unfused_baseline"] = unfused
     if errb is not None:
         res["error_budget"] = errb
-        res["error_budget_bit_pairs"] = error_budget_sweep(dev)
+    if not args.no_extra:
+        sweep, ebs = paged_sweep(torch, dev, reps, stream, ceil_GBs, plan)
+        res["paged_sweep"] = sweep
+        res["error_budget_bit_pairs"] = ebs
+        res["rotated_131k"] = rotated_131k(torch, dev, reps, stream, ceil_GBs, plan)
     if cpu_res is not None:
         res["cpu_baseline"] = cpu_res
     res["split_kernel_dispatch_plan"] = dispatch_plan

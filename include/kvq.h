@@ -195,20 +195,26 @@ kvq_status kvq_decode_attention(const kvq_params *params, const kvq_cache *cache
 /* The two launches of kvq_decode_attention, for callers that merge the partial results
  * themselves or schedule the two phases apart.  kvq_decode_partials takes the arguments of
  * kvq_decode_attention except out/out_dtype and leaves in the workspace, for every
- * (sequence, query head) row and split s of S, KVQ_PART_FLOATS fp32 values
- * {m_s, l_s, 0, 0, acc_s[128]}: m_s a running maximum of the scores of the split in log2
- * units (score * softmax_scale * log2(e)), l_s the sum of 2^(score_log2 - m_s) and acc_s the
- * matching unnormalised sum of values, l_s and acc_s scaled by one common power of two;
- * empty splits have m_s = -inf.  With M = max_s m_s the attention output is
+ * (sequence, query head) row, entries s = 0 .. S-1 of KVQ_PART_FLOATS fp32 values
+ * {m_s, l_s, n, 0, acc_s[128]}.  The first n entries of a row hold its splits (n is the same in
+ * all of them, 1 <= n <= S; entries from n on are not written and hold garbage).  For a split, m_s is
+ * a running maximum of its scores in log2 units (score * softmax_scale * log2(e)), l_s the sum of
+ * 2^(score_log2 - m_s) and acc_s the matching unnormalised sum of values, l_s and acc_s scaled by
+ * one common power of two; an empty split has m_s = -inf (its l_s and acc_s are 0).  With
+ * M = max_s m_s over the split entries the attention output is
  * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s ([P1] "Error pada key masuk sebelum softmax").
- * Rows are [batch][num_q_heads][S]; S depends on (params, batch, max_seq_len, q_dtype) and on
- * the environment variables KVQ_PAGES_PER_SPLIT / KVQ_TARGET_WAVES / KVQ_WINDOW_FOLD (1: the
- * bf16 recent window is processed by the quantized splits instead of splits of its own), which
- * must not change between the two calls.  kvq_decode_combine computes that merge into `out`
+ * With value_rotation the acc_s are sums over rotated values: the merged row must then be
+ * multiplied by the normalized 128-point Walsh-Hadamard matrix (kvq_decode_combine does this).
+ * Rows are [batch][num_q_heads][S].  S (kvq_decode_splits) depends on (params, batch, max_seq_len,
+ * q_dtype) and on the environment variables KVQ_PAGES_PER_SPLIT / KVQ_TARGET_WAVES, which must not
+ * change between the two calls.  The split kernel sizes each sequence's splits from the lengths on
+ * the device: the launch's waves are shared out over the sequences in proportion to their stored
+ * pages (at most twice an equal share per (sequence, kv head)), so n differs between sequences of
+ * different lengths.  kvq_decode_combine computes that merge into `out`
  * ([batch][num_q_heads][128] of out_dtype) from a workspace filled by kvq_decode_partials
  * with the same params, batch, max_seq_len and q_dtype.  Errors as for kvq_decode_attention. */
 #define KVQ_PART_FLOATS 132
-/* Number of splits S of the partial results for these arguments (0 for invalid ones). */
+/* Row stride S (entries per row) of the partial results for these arguments (0 for invalid ones). */
 int32_t kvq_decode_splits(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype);
 kvq_status kvq_decode_partials(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
                                int64_t max_seq_len, const void *q, int32_t q_dtype, float softmax_scale,
@@ -228,8 +234,8 @@ kvq_status kvq_decode_combine(const kvq_params *params, int32_t batch, int64_t m
  * With a bf16 window (window > 0) the append runs inside the split-K launch: the split holding
  * the new token's ring slot quantizes the token leaving the window, stores it, attends it and
  * writes the new token into the ring, while the other splits read the stored tokens before the
- * step; then the merge launch.  Otherwise (no window, fp32 rings, or KVQ_WINDOW_FOLD=1) the
- * append kernel runs first, then the split-K and merge launches.
+ * step; then the merge launch.  Otherwise (no window, or fp32 rings) the append kernel runs
+ * first, then the split-K and merge launches.
  * kvq_decode_step_partials stops before the merge: kvq_decode_combine(params, batch, max_seq_len,
  * q_dtype, ...) completes it.  Errors as for kvq_decode_attention, plus KVQ_EINVAL for null or
  * misaligned k_new / v_new; nothing is launched on an error. */

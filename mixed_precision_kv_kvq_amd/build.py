@@ -37,17 +37,25 @@ GEN_LIB = os.path.join(ROOT, "workloads", "libkvqgen.so")
 BUILD_DIR = os.environ.get("KVQ_BUILD_DIR") or os.path.join(PKG, "_build")
 
 
-def _sources():
+# Bit widths of the split-kernel instantiations: kvq_attn_inst.hip is compiled once per pair.
+ATTN_BITS = [(kb, vb) for kb in (1, 2, 4, 8) for vb in (1, 2, 4, 8)]
+
+
+def _units():
+    """Compile units: (source, object, extra flags)."""
     csrc = os.path.join(PKG, "csrc")
-    srcs = sorted(glob.glob(os.path.join(csrc, "*.hip"))) + sorted(glob.glob(os.path.join(csrc, "inst", "*.hip")))
-    srcs.append(os.path.join(csrc, "kvq_api.cpp"))
+    units = []
+    for src in sorted(glob.glob(os.path.join(csrc, "*.hip"))):
+        if os.path.basename(src) == "kvq_attn_inst.hip":
+            for kb, vb in ATTN_BITS:
+                units.append((src, os.path.join(BUILD_DIR, f"kvq_attn_k{kb}v{vb}.o"),
+                              [f"-DKVQ_KB={kb}", f"-DKVQ_VB={vb}", "-Rpass-analysis=kernel-resource-usage"]))
+        else:
+            units.append((src, os.path.join(BUILD_DIR, os.path.basename(src) + ".o"), []))
+    api = os.path.join(csrc, "kvq_api.cpp")
+    units.append((api, os.path.join(BUILD_DIR, "kvq_api.cpp.o"), []))
     headers = sorted(glob.glob(os.path.join(csrc, "*.h"))) + [os.path.join(ROOT, "include", "kvq.h")]
-    return srcs, headers
-
-
-def _obj_path(src):
-    rel = os.path.relpath(src, os.path.join(PKG, "csrc")).replace(os.sep, "_")
-    return os.path.join(BUILD_DIR, rel + ".o")
+    return units, headers
 
 
 def _run(cmd):
@@ -75,33 +83,32 @@ def _spills(out: str) -> list:
 def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> None:
     """Compile every HIP source for gfx950 and link the shared libraries."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs, headers = _sources()
+    units, headers = _units()
     newest_header = max(os.path.getmtime(h) for h in headers)
     todo = []
-    for s in srcs:
-        o = _obj_path(s)
-        if force or not os.path.exists(o) or os.path.getmtime(o) < max(os.path.getmtime(s), newest_header):
-            todo.append((s, o))
+    for src, obj, flags in units:
+        if force or not os.path.exists(obj) or os.path.getmtime(obj) < max(os.path.getmtime(src), newest_header):
+            todo.append((src, obj, flags))
     jobs = jobs or min(16, os.cpu_count() or 4)
     errors = []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         # The attention instantiations report their register use; a spill there is a build error.
-        futs = {ex.submit(_run, [HIPCC, *COMMON, *(["-Rpass-analysis=kernel-resource-usage"] if "inst" in s else []),
-                                 "-c", s, "-o", o]): s for s, o in todo}
+        futs = {ex.submit(_run, [HIPCC, *COMMON, *flags, "-c", src, "-o", obj]): (src, obj) for src, obj, flags in todo}
         for f in cf.as_completed(futs):
             rc, out, dt = f.result()
+            src, obj = futs[f]
             spills = _spills(out)
             if verbose or rc:
                 shown = "\n".join(l for l in out.splitlines() if "remark:" not in l)
-                print(f"[build] {os.path.basename(futs[f])} rc={rc} {dt:.1f}s\n{shown}", file=sys.stderr)
+                print(f"[build] {os.path.basename(obj)} rc={rc} {dt:.1f}s\n{shown}", file=sys.stderr)
             if spills:
-                print(f"[build] {os.path.basename(futs[f])}: scratch in {spills}", file=sys.stderr)
-                os.remove(_obj_path(futs[f]))
+                print(f"[build] {os.path.basename(obj)}: scratch in {spills}", file=sys.stderr)
+                os.remove(obj)
             if rc or spills:
-                errors.append(futs[f])
+                errors.append(os.path.basename(obj))
     if errors:
         raise RuntimeError(f"hipcc failed for: {errors}")
-    objs = [_obj_path(s) for s in srcs]
+    objs = [obj for _, obj, _ in units]
     if force or todo or not os.path.exists(LIB):
         rc, out, _ = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs])
         if rc:

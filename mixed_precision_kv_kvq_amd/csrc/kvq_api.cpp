@@ -60,78 +60,62 @@ KvqCacheDev dev_cache(const kvq_params *p, const kvq_cache *c) {
 
 KvqLayout layout_of(const kvq_params *p) { return kvq_make_layout(p->k_bits, p->k_group, p->v_bits, p->v_group); }
 
-// Split plan.  Quantized splits cover the quantized pages, pps pages each, sized so that all
-// waves of the launch are resident at once.  A bf16 recent window (no key rotation) is folded
-// into them: 16-token block i of the ring goes to the i-th split from the end, processed while
-// that split's first pages stream in, so no wave is left with only the window's short,
-// latency-bound work.  Otherwise (fp32 window, rotated keys, or more window blocks than splits)
-// splits [0, wsplits) cover the window, KVQ_WIN_PAGES pages each, and come first in dispatch
-// order so that their work overlaps the streaming of the quantized pages.
+// Split plan.  Every (sequence, kv head) unit gets `ws` window splits (KVQ_WIN_PAGES pages of the
+// recent window each) and a number of quantized splits that the split kernel works out per sequence
+// from the device lengths: the launch's quantized waves (target_q, sized so that every wave of the
+// launch is resident at once) are shared out over the sequences in proportion to their quantized
+// pages, at most cap_max per unit.  The host only knows max_seq_len, so it sizes the launch (grid)
+// and the partial rows (S_max) for the worst case; waves past the plan's total exit at once.
 struct SplitPlan {
-  int splits, wsplits, pps, wfold;
-  int bound;  // most splits any length <= max_seq_len can get (workspace size)
+  int ws, S_max, target_q, cap_max, fixed_per;
+  int eager;  // entries the merge reads eagerly: the splits of a unit with an equal share
+  int64_t grid;
 };
 
-SplitPlan split_plan_mode(const kvq_params *p, int32_t batch, int64_t max_seq_len, int q_parts, bool fold) {
+SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, int q_parts) {
   const int R = p->window;
   const int64_t nq = max_seq_len > R ? max_seq_len - R : 0;
   const int64_t nw = max_seq_len < R ? max_seq_len : R;
-  const int64_t qpages = (nq + KVQ_PAGE - 1) / KVQ_PAGE;
-  const int64_t wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;  // also the folded window blocks
-  SplitPlan sp;
-  sp.wfold = fold ? 1 : 0;
-  sp.wsplits = fold ? 0 : (int)((wpages + KVQ_WIN_PAGES - 1) / KVQ_WIN_PAGES);
+  const int64_t qpmax = (nq + KVQ_PAGE - 1) / KVQ_PAGE;
+  const int64_t wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;
   const int64_t units = (int64_t)batch * p->num_kv_heads;
-  int64_t per = 0, cap = 0;
+  SplitPlan sp = {};
+  sp.ws = (int)((wpages + KVQ_WIN_PAGES - 1) / KVQ_WIN_PAGES);
+  int64_t per = 0;
   if (const char *env = getenv("KVQ_PAGES_PER_SPLIT")) per = atoll(env);
-  const bool fixed = per > 0;
-  if (!fixed) {
+  int64_t qs_max;
+  if (per > 0) {  // fixed pages per quantized split
+    per = per < 2 ? 2 : (per + 1) & ~int64_t(1);
+    sp.fixed_per = (int)per;
+    qs_max = (qpmax + per - 1) / per;
+    if (qs_max < 1) qs_max = 1;
+    sp.grid = units * (sp.ws + qs_max);
+  } else {
     const int g = p->num_q_heads / p->num_kv_heads;
     int64_t target = (int64_t)kNumCUs * kvq_attn_waves_per_cu(p->k_bits, p->v_bits, KVQ_D / p->v_group, g, q_parts);
     if (const char *env = getenv("KVQ_TARGET_WAVES")) target = atoll(env) > 0 ? atoll(env) : target;
-    // quantized splits per unit: at most ceil(target / units) - wsplits, at least 1
-    cap = (target + units - 1) / units - sp.wsplits;
-    if (cap < 1) cap = 1;
-    per = (qpages + cap - 1) / cap;
+    int64_t tq = target - units * sp.ws;
+    if (tq < units) tq = units;
+    // a unit may take up to twice the equal share of the launch
+    int64_t cap = 2 * ((target + units - 1) / units);
+    sp.target_q = (int)tq;
+    sp.cap_max = (int)cap;
+    qs_max = (qpmax + 1) / 2 < cap ? (qpmax + 1) / 2 : cap;
+    if (qs_max < 1) qs_max = 1;
+    // sum over units of the quantized splits <= tq + units (each unit's share rounds down, then up to >= 1)
+    sp.grid = units * sp.ws + tq + units;
   }
-  if (per < 2) per = 2;
-  per = (per + 1) & ~int64_t(1);
-  int64_t qsplits = (qpages + per - 1) / per;
-  if (fold && qsplits < wpages) qsplits = wpages;  // every window block needs a split
-  sp.pps = (int)per;
-  sp.splits = (int)(sp.wsplits + qsplits);
-  if (sp.splits < 1) sp.splits = 1;
-  // Bound over all lengths up to max_seq_len.  wsplits(L) + ceil(qpages(L) / per) is
-  // non-decreasing in L for a fixed per; otherwise qsplits <= min(ceil(qpages / 2), cap) and
-  // both wsplits + ceil(qpages / 2) and wsplits + cap = max(ceil(target / units), wsplits + 1)
-  // are non-decreasing in L, so their minimum at max_seq_len bounds every shorter length.  A
-  // folded plan has at least wpages(L) splits, also non-decreasing in L.
-  int64_t bound = sp.wsplits + qsplits;
-  if (!fixed) {
-    const int64_t a = sp.wsplits + (qpages + 1) / 2, b = sp.wsplits + cap;
-    bound = a < b ? a : b;
-    if (fold && bound < wpages) bound = wpages;
+  sp.S_max = (int)(sp.ws + qs_max);
+  // the merge reads the headers and rows of a unit's equal share at once (exactly the split count
+  // of every unit when the lengths are equal)
+  if (sp.fixed_per) {
+    sp.eager = sp.S_max;
+  } else {
+    const int64_t share = sp.target_q / units;
+    sp.eager = (int)(sp.ws + (share > 1 ? share : 1));
   }
-  if (bound < sp.splits) bound = sp.splits;
-  sp.bound = (int)bound;
+  if (sp.eager > sp.S_max) sp.eager = sp.S_max;
   return sp;
-}
-
-bool fold_allowed(const kvq_params *p) {
-  if (p->window <= 0 || p->kv_dtype != KVQ_BF16 || p->key_rotation != KVQ_ROT_NONE) return false;
-  const char *env = getenv("KVQ_WINDOW_FOLD");  // opt-in: measured slower at the 32k config
-  return env && env[0] == '1';
-}
-
-SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, int q_parts) {
-  if (fold_allowed(p)) {
-    // Fold when every window block finds a split of its own.
-    const SplitPlan f = split_plan_mode(p, batch, max_seq_len, q_parts, true);
-    const SplitPlan u = split_plan_mode(p, batch, max_seq_len, q_parts, false);
-    if (f.splits <= u.splits) return f;
-    return u;
-  }
-  return split_plan_mode(p, batch, max_seq_len, q_parts, false);
 }
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
@@ -179,15 +163,12 @@ kvq_status kvq_quantize_append(const kvq_params *params, const kvq_cache *cache,
 
 size_t kvq_decode_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len) {
   if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0) return 0;
-  // The query dtype is not known here: cover both query-part counts.
-  // Cover both query-part counts and both window plans (the choice between them can change
-  // with the length).
+  // The query dtype is not known here: cover both query-part counts.  S_max never decreases as
+  // max_seq_len grows (ws, the quantized pages and the caps are all non-decreasing in it).
   int bound = 0;
   for (int parts = 1; parts <= 2; ++parts) {
-    for (int fold = 0; fold <= 1; ++fold) {
-      const SplitPlan sp = split_plan_mode(params, batch, max_seq_len, parts, fold != 0);
-      bound = sp.bound > bound ? sp.bound : bound;
-    }
+    const SplitPlan sp = split_plan(params, batch, max_seq_len, parts);
+    bound = sp.S_max > bound ? sp.S_max : bound;
   }
   return (size_t)batch * params->num_q_heads * (size_t)bound * KVQ_PART_STRIDE * sizeof(float);
 }
@@ -198,7 +179,7 @@ namespace {
 
 // Decode steps fuse their append into the attention launch for bf16 rings (window > 0) with the
 // window in splits of its own; otherwise the append kernel runs first.
-bool step_fusable(const kvq_params *p) { return p->window > 0 && p->kv_dtype == KVQ_BF16 && !fold_allowed(p); }
+bool step_fusable(const kvq_params *p) { return p->window > 0 && p->kv_dtype == KVQ_BF16; }
 
 // The split-kernel launch of kvq_decode_partials (step = 0) or of a decode step (step = 1: lengths
 // before the step, attended at length + 1; k_new / v_new appended in the same launch when fuse).
@@ -234,9 +215,12 @@ kvq_status partials_impl(const kvq_params *params, const kvq_cache *cache, const
   a.rotation = params->key_rotation;
   const int q_parts = (q_dtype == KVQ_BF16 && !params->key_rotation) ? 1 : 2;
   const SplitPlan sp = split_plan(params, cache->batch, max_seq_len, q_parts);
-  a.splits = sp.splits;
-  a.wsplits = sp.wsplits;
-  a.wfold = sp.wfold;
+  a.splits = sp.S_max;
+  a.ws = sp.ws;
+  a.target_q = sp.target_q;
+  a.cap_max = sp.cap_max;
+  a.fixed_per = sp.fixed_per;
+  a.grid = sp.grid;
   a.max_len = (int32_t)(max_seq_len < INT32_MAX ? max_seq_len : INT32_MAX);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
   a.sigma_u = (float)((double)scale * 1.4426950408889634 * 8589934592.0);  // * log2(e) * 2^33
@@ -307,7 +291,7 @@ int32_t kvq_decode_splits(const kvq_params *params, int32_t batch, int64_t max_s
   if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0) return 0;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return 0;
   const int q_parts = (q_dtype == KVQ_BF16 && !params->key_rotation) ? 1 : 2;
-  return split_plan(params, batch, max_seq_len, q_parts).splits;
+  return split_plan(params, batch, max_seq_len, q_parts).S_max;
 }
 
 kvq_status kvq_decode_combine(const kvq_params *params, int32_t batch, int64_t max_seq_len, int32_t q_dtype,
@@ -324,7 +308,9 @@ kvq_status kvq_decode_combine(const kvq_params *params, int32_t batch, int64_t m
   c.out_f32 = out_dtype == KVQ_F32;
   c.B = batch;
   c.Hq = params->num_q_heads;
-  c.splits = split_plan(params, batch, max_seq_len, q_parts).splits;
+  const SplitPlan sp = split_plan(params, batch, max_seq_len, q_parts);
+  c.splits = sp.S_max;
+  c.eager = sp.eager;
   c.value_rotation = params->value_rotation;
   return hip_status(kvq_launch_combine(c, stream));
 }
@@ -436,6 +422,7 @@ kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, c
   c.B = batch;
   c.Hq = a.Hq;
   c.splits = a.splits;
+  c.eager = a.splits;  // every dense split is written
   c.value_rotation = 0;  // the dense cache is in the original domain
   return hip_status(kvq_launch_combine(c, stream));
 }

@@ -789,79 +789,6 @@ struct Kern {
     }
   }
 
-  // A folded block of up to 16 bf16 window tokens (ring slots [w0, w0 + n)), processed by a
-  // quantized split before its pairs: one 16-token column set of the score contraction (raw
-  // keys, unscaled query), weights through the exchange buffer (page-A slots; page-B slots get
-  // zero weights), exact bf16 values as the B operand of the value contraction.  The value
-  // accumulators hold only this block's output afterwards; they are brought to the scale of the
-  // quantized code contractions (tile m: 2^(s_m - 133), see write_partial) with exact
-  // power-of-two multiplies, so the pages that follow accumulate on top.
-  struct WinBlock {
-    int w0, n;
-    const uint8_t *kwin, *vwin;
-  };
-  struct WinRegs {
-    u32x4 kr[4];        // B operand of the score contraction, per 32-channel chunk
-    uint32_t vb[8][2];  // value tile m, k slots 0..3 (tokens 4 quad + 0..3) packed in pairs
-  };
-  static __device__ __forceinline__ void load_win_block(WinRegs &wr, const Ctx &cx, const WinBlock &wb) {
-    const int slot = wb.w0 + (cx.col < wb.n ? cx.col : 0);  // columns past the block re-read its first row
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-      wr.kr[kc] = gload<u32x4>(wb.kwin + ((size_t)slot * KVQ_D + 32 * kc + 8 * cx.quad) * 2);
-    const uint16_t *vrow[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 4 * cx.quad + j;
-      vrow[j] = reinterpret_cast<const uint16_t *>(wb.vwin) + (size_t)(wb.w0 + (t < wb.n ? t : 0)) * KVQ_D + cx.col;
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t lo = gload<uint16_t>(vrow[2 * i] + 16 * m);
-        const uint32_t hi = gload<uint16_t>(vrow[2 * i + 1] + 16 * m);
-        wr.vb[m][i] = lo | (hi << 16);
-      }
-    }
-  }
-  // Needs the unscaled query operand in cx.qA; leaves the code-scale accumulators in st.
-  static __device__ __forceinline__ void win_block(const Ctx &cx, St &st, const WinRegs &wr, const WinBlock &wb) {
-    f32x4 D[NACC];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) D[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int part = 0; part < P; ++part) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-          D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], __builtin_bit_cast(bf16x8, wr.kr[kc]),
-                                                          D[hb], 0, 0, 0);
-      }
-    }
-    float sA[HB], sB[HB];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const float acc = (D[hb][0] + D[hb][1]) + (D[hb][2] + D[hb][3]);
-      sA[hb] = cx.col < wb.n ? acc * EXP2_M66 * EXP2_M67 : -__builtin_inff();
-      sB[hb] = -__builtin_inff();
-    }
-    softmax_update<true, false>(cx, st, sA, sB, nullptr);
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) xchg_put(cx, 0, hb, sA[hb], 0.f);
-    u32x4 xa = xchg_get(cx, 0);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xa)::"memory");
-    const bf16x8 Aop = __builtin_bit_cast(bf16x8, xa);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, pack8(wr.vb[m][0], wr.vb[m][1], 0u, 0u), st.acc[m], 0, 0, 0);
-      const float f = __builtin_amdgcn_ldexpf(1.0f, vtile_scale(m) - 66);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.acc[m][r] = st.acc[m][r] * f * EXP2_M67;
-    }
-  }
-
   // ---- fused decode step ---------------------------------------------------------------
   // LDS of a window split beyond the staged query ([G][128] fp32): a page record holding only the
   // token that leaves the window (at token slot 0), then that token's codes and metadata words.
@@ -927,8 +854,8 @@ struct Kern {
 
   // Attention over the token that left the window (the one-token record at VREC_OFF), on top of
   // the window tokens already in st: the value accumulators are brought from the window's scale
-  // to the scale of the code contractions (exact power-of-two multiplies, as for a folded window
-  // block), the code-scaled query operand (rotated when keys are) is built, and the record goes
+  // to the scale of the code contractions (tile m: 2^(s_m - 133), exact power-of-two multiplies),
+  // the code-scaled query operand (rotated when keys are) is built, and the record goes
   // through the masked pair path with one valid token.
   template <int KS>
   static __device__ __forceinline__ void evicted_pair(const KvqAttnArgs &args, Ctx &cx, St &st, uint8_t *smem,
@@ -983,27 +910,102 @@ struct Kern {
     }
   }
 
+  // ---- per-sequence split plan ------------------------------------------------------------
+  // Quantized splits of each kv head of a sequence with qp quantized pages, out of Q pages over
+  // the batch: a share of the launch's quantized waves proportional to its pages (at most cap_max,
+  // at least 1), pages per split even (whole pairs) and at least 2.  With equal lengths this is
+  // the same count for every sequence.  The share is floor(target_q * qp / (Hkv * Q)) taken in fp64:
+  // both products are integers below 2^50, so a non-integer quotient lies at least 1 / (Hkv * Q)
+  // from an integer, far above the rounding of the division, and the floor is exact.
+  static __device__ __forceinline__ int plan_qsplits(const KvqAttnArgs &a, int qp, double Q) {
+    int per;
+    if (a.fixed_per > 0) {
+      per = a.fixed_per;
+    } else {
+      int cap = Q > 0.0 ? (int)__builtin_floor((double)a.target_q * (double)qp / ((double)a.Hkv * Q)) : 1;
+      cap = cap < 1 ? 1 : (cap > a.cap_max ? a.cap_max : cap);
+      per = (qp + cap - 1) / cap;
+    }
+    per = per < 2 ? 2 : per;
+    per = (per + 1) & ~1;
+    const int s = (qp + per - 1) / per;
+    return s < 1 ? 1 : s;
+  }
+  // Sequence b's kv heads take waves [Hkv * O_b, Hkv * (O_b + S_b)) of the launch, S_b = window
+  // splits + plan_qsplits, O_b = sum of S over the sequences before b, one kv head after the other.
+  // Computed by the whole wave from the device lengths (lane i handles sequences i, i + 64, ...;
+  // for batches up to 64 the lengths are loaded once).  Returns false for a wave past the last
+  // sequence's.  Results are wave-uniform (read with readlane), so everything derived from them
+  // stays scalar; len_out is the sequence's length as stored in seq_lens (not clamped).
+  static __device__ __forceinline__ bool plan_wave(const KvqAttnArgs &a, int wave, int &b_out, int &kvh_out,
+                                                   int &split_out, int &S_out, int &len_out) {
+    const int lane = threadIdx.x, B = a.cache.batch, R = a.R;
+    const int lmax = a.max_len - a.len_plus1;
+    int raw0 = 0;  // lane's length in the first chunk of 64 sequences
+    auto qpages_of = [&](int raw) {
+      int L = raw < 0 ? 0 : (raw > lmax ? lmax : raw);
+      L += a.len_plus1;
+      return ((L > R ? L - R : 0) + KVQ_PAGE - 1) / KVQ_PAGE;
+    };
+    double Q = 0.0;  // exact: a sum of integers below 2^53
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int raw = b0 + lane < B ? a.seq_lens[b0 + lane] : 0;
+      if (b0 == 0) raw0 = raw;
+      double v = b0 + lane < B ? (double)qpages_of(raw) : 0.0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      Q += v;
+    }
+    int base = 0;  // waves of the sequences before this chunk of 64
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int b = b0 + lane;
+      const int raw = b0 == 0 ? raw0 : (b < B ? a.seq_lens[b] : 0);
+      const int Sb = b < B ? a.ws + plan_qsplits(a, qpages_of(raw), Q) : 0;
+      const int nw_b = a.Hkv * Sb;
+      int incl = nw_b;  // inclusive prefix over the lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      const int lo = base + incl - nw_b;
+      const uint64_t m = __ballot(b < B && wave >= lo && wave < lo + nw_b);
+      if (m) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        const int bb = __builtin_amdgcn_readlane(b, src), S = __builtin_amdgcn_readlane(Sb, src);
+        const int idx = wave - __builtin_amdgcn_readlane(lo, src);
+        const int kvh = idx / S;
+        const int unit = bb * a.Hkv + kvh;
+        // Consecutive waves are the splits of one unit, on the 8 XCDs in turn (block mod 8): with S
+        // a multiple of 8 the split at position k of every unit would land on the same XCD, so the
+        // split index is rotated by the unit pair, which spreads each split (the window splits in
+        // particular, which carry less work) evenly over the XCDs.  Units 2i and 2i+1 keep the same
+        // rotation: their page records are adjacent and share a cache line (a 1856-byte K4V2 record
+        // is 14.5 lines), which is then fetched into one XCD's L2 only.
+        b_out = bb;
+        kvh_out = kvh;
+        split_out = (idx % S + unit / 2) % S;
+        S_out = S;
+        len_out = __builtin_amdgcn_readlane(raw, src);
+        return true;
+      }
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return false;
+  }
+
   static __device__ void run(const KvqAttnArgs &args, uint8_t *smem) {
     float *lds = reinterpret_cast<float *>(smem);
     const int lane = threadIdx.x;
-    const int64_t wave = blockIdx.x;
-    const int S = args.splits;
-    const int64_t unit = wave / S;
-    // Consecutive blocks go to the 8 XCDs in turn (block mod 8), so with S a multiple of 8 the
-    // split at position k of every unit would land on the same XCD: rotating the split index by
-    // the unit pair spreads each split (the window splits in particular, which carry less work)
-    // evenly over the XCDs.  Units 2i and 2i+1 keep the same rotation: their page records are
-    // adjacent and share a cache line (a 1856-byte K4V2 record is 14.5 lines), which is then
-    // fetched into one XCD's L2 only.
-    const int split = (int)((wave % S + unit / 2) % S);
     const int Hkv = args.Hkv;
-    const int kvh = (int)(unit % Hkv), b = (int)(unit / Hkv);
-    if (b >= args.cache.batch) return;
+    int b, kvh, split, S, Lraw;
+    if (!plan_wave(args, (int)blockIdx.x, b, kvh, split, S, Lraw)) return;
     const KvqLayout &lay = args.lay;
     const int R = args.R;
-    int L = args.seq_lens[b];
-    // a length outside [0, max_len] is clamped (reported once per unit, by its split 0); in a fused
+    // a length outside [0, max_len] is clamped (reported once per unit, by its split 0); in a decode
     // step the lengths are those before the appended token: [0, max_len - 1]
+    // (the same clamp as the plan's)
+    int L = Lraw;
     const int lmax = args.max_len - args.len_plus1;
     kvq_raise(args.cache, split == 0 && (L < 0 || L > lmax), KVQ_DEV_LENGTH);
     L = L < 0 ? 0 : (L > lmax ? lmax : L);
@@ -1012,9 +1014,8 @@ struct Kern {
     const int nq = L > R ? L - R : 0;
     const int nw = L < R ? L : R;
     const int wpages = (nw + KVQ_PAGE - 1) / KVQ_PAGE;
-    // Window splits first, then quantized splits (see the host split plan).  With the window
-    // folded into the quantized splits there are no window splits.
-    const bool win_split = split < args.wsplits;
+    // Window splits first, then quantized splits.
+    const bool win_split = split < args.ws;
     int wv0 = 0, wv1 = 0;
     if (win_split) {
       wv0 = split * KVQ_WIN_PAGES;
@@ -1079,19 +1080,19 @@ struct Kern {
           evicted_pair<1>(args, cx, st, smem, b, hq0);
         else
           evicted_pair<2>(args, cx, st, smem, b, hq0);
-        write_partial<PART_CODES>(args, cx, st, nullptr, lds, b, kvh, split);
+        write_partial<PART_CODES>(args, cx, st, nullptr, lds, b, kvh, split, S);
         return;
       }
       if (args.kv_f32)
-        write_partial<PART_WIN_VALU>(args, cx, st, ow, lds, b, kvh, split);
+        write_partial<PART_WIN_VALU>(args, cx, st, ow, lds, b, kvh, split, S);
       else
-        write_partial<PART_WIN_ACC>(args, cx, st, ow, lds, b, kvh, split);
+        write_partial<PART_WIN_ACC>(args, cx, st, ow, lds, b, kvh, split, S);
       return;
     }
 
     // Quantized splits take full-page pairs round-robin: pair sq, sq + SQ, sq + 2 SQ, ... so that at
     // any moment the waves of one unit read neighbouring pairs.
-    const int SQ = S - args.wsplits, sq = split - args.wsplits;
+    const int SQ = S - args.ws, sq = split - args.ws;
     // Fused step: the token leaving the window is stored and attended by the window split; the
     // quantized splits cover the tokens stored before the step.
     const int nqs = args.fuse ? (Lb > R ? Lb - R : 0) : nq;
@@ -1104,21 +1105,7 @@ struct Kern {
     // full pairs, so it streams through the same ring.
     const int npairs = tp > sq ? (tp - sq + SQ - 1) / SQ : 0;
     const bool tail = sq == tp % SQ && 2 * tp < qpages_s;
-    // Folded window (bf16 rings): 16-token block i of the ring goes to split SQ - 1 - i, the
-    // splits that end the pair rotation and so have at most as many pairs as the others.
-    WinBlock wb;
-    wb.w0 = -1;
-    if (args.wfold) {
-      const int i = SQ - 1 - sq;
-      if (i * KVQ_PAGE < nw) {
-        wb.w0 = i * KVQ_PAGE;
-        wb.n = (nw - wb.w0) < KVQ_PAGE ? (nw - wb.w0) : KVQ_PAGE;
-        const size_t win_off = ((size_t)b * Hkv + kvh) * R * KVQ_D * 2;
-        wb.kwin = args.cache.k_win + win_off;
-        wb.vwin = args.cache.v_win + win_off;
-      }
-    }
-    if (npairs > 0 || tail || wb.w0 >= 0) {
+    if (npairs > 0 || tail) {
       int tail_va = 0, tail_vb = 0;
       if (tail) {
         const int p = 2 * tp;
@@ -1138,13 +1125,13 @@ struct Kern {
         load_q_regs(qr, args, cx, b, hq0);
       }
       if (lay.kg == 32)
-        stream_pairs<0>(args, cx, st, smem, qr, wb, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+        stream_pairs<0>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
       else if (lay.kg == 64)
-        stream_pairs<1>(args, cx, st, smem, qr, wb, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+        stream_pairs<1>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
       else
-        stream_pairs<2>(args, cx, st, smem, qr, wb, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
+        stream_pairs<2>(args, cx, st, smem, qr, b, kvh, sq, SQ, npairs, tail, tail_va, tail_vb);
     }
-    write_partial<PART_CODES>(args, cx, st, nullptr, lds, b, kvh, split);
+    write_partial<PART_CODES>(args, cx, st, nullptr, lds, b, kvh, split, S);
   }
 
   // Pairs sq, sq + SQ, ... (npairs of them) of one unit through the wave's LDS ring of NPS page
@@ -1157,7 +1144,7 @@ struct Kern {
   // KS = log2(key group / 32).
   template <int KS>
   static __device__ __forceinline__ void stream_pairs(const KvqAttnArgs &args, Ctx &cx, St &st, uint8_t *smem,
-                                                      const QRegs &qr, const WinBlock &wb, int b, int kvh, int sq,
+                                                      const QRegs &qr, int b, int kvh, int sq,
                                                       int SQ, int npairs, bool tail, int tail_va, int tail_vb) {
     const KvqLayout &lay = args.lay;
     const int lane = cx.lane, Hkv = args.Hkv;
@@ -1208,19 +1195,10 @@ struct Kern {
       dma_page_buf(wslot, src, rec, loff, lane);
       wslot = next_slot(wslot);
     };
-    // A folded window block's loads are issued before the prologue DMAs, so that they retire
-    // first (vmcnt counts in issue order) and the block is processed while the ring fills.
-    WinRegs wr;
-    const bool has_win = wb.w0 >= 0;
-    if (has_win) load_win_block(wr, cx, wb);
     // The prologue always issues AHEAD pages (fillers past the split's own pages), so the number
-    // of DMAs behind the window loads is fixed.
+    // of DMAs in flight is fixed.
 #pragma unroll
     for (int k = 0; k < AHEAD; ++k) issue((k & 1) != 0, k);
-    if (has_win) {
-      build_q_regs(cx, qr, args.q_f32, false);
-      win_block(cx, st, wr, wb);
-    }
     if (!args.rotation) build_q_regs(cx, qr, args.q_f32);
     // Zero-point query sums per key group.
     float Qg[HB][4];
@@ -1276,14 +1254,16 @@ struct Kern {
   }
 
   // Reduce the state across lanes and write this split's partial result:
-  // [m (log2 units), l, 0, 0, o[128]] per query head, o unnormalised.
+  // [m (log2 units), l, nsplits, 0, o[128]] per query head, o unnormalised, nsplits the number of
+  // entries of the row that hold splits.
   // MODE: PART_CODES (quantized pages: value-code scales and zero-point sums apply),
   // PART_WIN_ACC (bf16 window: MFMA accumulators hold the output as is), PART_WIN_VALU (fp32
   // window: the output is in ow).
   static constexpr int PART_CODES = 0, PART_WIN_ACC = 1, PART_WIN_VALU = 2;
   template <int MODE>
   static __device__ __forceinline__ void write_partial(const KvqAttnArgs &args, const Ctx &cx, const St &st,
-                                                       float (*ow)[2], float *lds, int b, int kvh, int split) {
+                                                       float (*ow)[2], float *lds, int b, int kvh, int split,
+                                                       int nsplits) {
     constexpr bool WIN = MODE != PART_CODES;
     const int lane = threadIdx.x;
     const int hq0 = kvh * G;
@@ -1341,7 +1321,7 @@ struct Kern {
       if (lane == 0) {
         dst[0] = hdr[h * 4 + 0];
         dst[1] = hdr[h * 4 + 1];
-        dst[2] = 0.f;
+        dst[2] = (float)nsplits;  // entries [nsplits, splits) of the row are not written
         dst[3] = 0.f;
       }
     }

@@ -8,67 +8,93 @@
 #include "kvq_internal.h"
 
 namespace kvq_attn {
-hipError_t launch_k1v1(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k1v2(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k1v4(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k1v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k2v1(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k2v2(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k2v4(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k2v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k4v1(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k4v2(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k4v4(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k4v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k8v1(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k8v2(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k8v4(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-hipError_t launch_k8v8(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+#define KVQ_DECLARE_LAUNCH(kb, vb) \
+  hipError_t launch_k##kb##v##vb(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
+KVQ_DECLARE_LAUNCH(1, 1) KVQ_DECLARE_LAUNCH(1, 2) KVQ_DECLARE_LAUNCH(1, 4) KVQ_DECLARE_LAUNCH(1, 8)
+KVQ_DECLARE_LAUNCH(2, 1) KVQ_DECLARE_LAUNCH(2, 2) KVQ_DECLARE_LAUNCH(2, 4) KVQ_DECLARE_LAUNCH(2, 8)
+KVQ_DECLARE_LAUNCH(4, 1) KVQ_DECLARE_LAUNCH(4, 2) KVQ_DECLARE_LAUNCH(4, 4) KVQ_DECLARE_LAUNCH(4, 8)
+KVQ_DECLARE_LAUNCH(8, 1) KVQ_DECLARE_LAUNCH(8, 2) KVQ_DECLARE_LAUNCH(8, 4) KVQ_DECLARE_LAUNCH(8, 8)
+#undef KVQ_DECLARE_LAUNCH
 }  // namespace kvq_attn
 
 namespace {
 
-// One wave per (sequence, query head).  Splits are taken 32 at a time: the
-// headers (lane s holds split s) and all 32 accumulator rows are requested
-// before any is used, so a chunk costs one memory round trip; chunks are
-// merged online (running max M, sum l and output o rescaled as M grows).
-constexpr int kChunk = 32;
+// One wave per (sequence, query head).  Entries are taken 64 at a time (lane s holds entry s's
+// header), accumulator rows in halves of 32.  Every written header holds the number n of entries
+// of its row that hold splits; entries from n on are never written.  The first group reads the
+// headers and rows of its first `eager` entries together (the equal share of the launch: with equal
+// lengths every row has exactly that many entries, all just written and cache-resident), so such a
+// row costs one memory round trip and touches no unwritten line; headers of entries [eager, n) and
+// rows of later live entries are read once n and the headers are known.  An empty split has
+// m = -inf and is not accumulated (rows read for unwritten or empty entries are skipped, not
+// multiplied by 0).  Groups are merged online (running max M, sum l and output o rescaled as M
+// grows).
+constexpr int kHalf = 32;
 
 __global__ __launch_bounds__(64) void kvq_combine_kernel(KvqCombineArgs a) {
   const int lane = threadIdx.x;
   const size_t bh = blockIdx.x;
   const float *base = a.partials + bh * (size_t)a.splits * KVQ_PART_STRIDE;
   const float ninf = -__builtin_inff();
+  auto header = [&](int e) { return *reinterpret_cast<const float4 *>(base + (size_t)e * KVQ_PART_STRIDE); };
   float M = ninf, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s0 = 0; s0 < a.splits; s0 += kChunk) {
-    const int n = (a.splits - s0) < kChunk ? (a.splits - s0) : kChunk;
-    const float *cb = base + (size_t)s0 * KVQ_PART_STRIDE;
-    const bool mine = lane < n;
-    const float ms = mine ? cb[(size_t)lane * KVQ_PART_STRIDE] : ninf;
-    const float ls = mine ? cb[(size_t)lane * KVQ_PART_STRIDE + 1] : 0.f;
-    float2 acc[kChunk];
+  // first group: headers and rows of the eager entries
+  int eager = a.eager < a.splits ? a.eager : a.splits;
+  eager = eager < 1 ? 1 : (eager > 2 * kHalf ? 2 * kHalf : eager);
+  float4 hd = lane < eager ? header(lane) : make_float4(ninf, 0.f, 0.f, 0.f);
+  float2 acc[kHalf];
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u)
-      acc[u] = u < n ? reinterpret_cast<const float2 *>(cb + (size_t)u * KVQ_PART_STRIDE + 4)[lane]
-                     : make_float2(0.f, 0.f);
-    float Mc = ms;
-    for (int off = 32; off >= 1; off >>= 1) Mc = __builtin_fmaxf(Mc, __shfl_xor(Mc, off));
-    if (Mc == ninf) continue;  // every split of this chunk is empty
-    const float Mn = __builtin_fmaxf(M, Mc);
-    const float r = (M == ninf) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);  // rescale what came before
-    const float w = (ms == ninf) ? 0.f : __builtin_amdgcn_exp2f(ms - Mn);
-    float lc = ls * w;
-    for (int off = 32; off >= 1; off >>= 1) lc += __shfl_xor(lc, off);
-    l = __builtin_fmaf(l, r, lc);
-    o0 *= r;
-    o1 *= r;
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
-      o0 = __builtin_fmaf(acc[u].x, wj, o0);
-      o1 = __builtin_fmaf(acc[u].y, wj, o1);
+  for (int u = 0; u < kHalf; ++u)
+    acc[u] = u < eager ? reinterpret_cast<const float2 *>(base + (size_t)u * KVQ_PART_STRIDE + 4)[lane]
+                       : make_float2(0.f, 0.f);
+  int nrow;
+  {
+    const int c = (int)__builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, hd.z)));
+    nrow = c < 1 ? 1 : (c < a.splits ? c : a.splits);
+  }
+  for (int s0 = 0; s0 < nrow; s0 += 2 * kHalf) {
+    const int n = (nrow - s0) < 2 * kHalf ? (nrow - s0) : 2 * kHalf;
+    const int pre = s0 == 0 ? (eager < n ? eager : n) : 0;  // entries whose header (and row, below 32) is read
+    if (pre < n) {
+      const float4 h2 = (lane >= pre && lane < n) ? header(s0 + lane) : make_float4(ninf, 0.f, 0.f, 0.f);
+      if (lane >= pre) hd = h2;
     }
-    M = Mn;
+    const float ms = lane < n ? hd.x : ninf;
+    const float ls = lane < n ? hd.y : 0.f;
+    const uint64_t live = __ballot(ms != ninf);
+    if (live) {
+      float Mc = ms;
+      for (int off = 32; off >= 1; off >>= 1) Mc = __builtin_fmaxf(Mc, __shfl_xor(Mc, off));
+      const float Mn = __builtin_fmaxf(M, Mc);
+      const float r = (M == ninf) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);  // rescale what came before
+      const float w = (ms == ninf) ? 0.f : __builtin_amdgcn_exp2f(ms - Mn);
+      float lc = ls * w;
+      for (int off = 32; off >= 1; off >>= 1) lc += __shfl_xor(lc, off);
+      l = __builtin_fmaf(l, r, lc);
+      o0 *= r;
+      o1 *= r;
+      const float *cb = base + (size_t)s0 * KVQ_PART_STRIDE;
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint32_t hmask = (uint32_t)(live >> (kHalf * hf));
+        if (!hmask) continue;
+        const int got = hf == 0 ? (pre < kHalf ? pre : kHalf) : 0;  // rows already read
+        const uint32_t late = got >= kHalf ? 0u : hmask & ~((1u << got) - 1u);
+        const float *hb = cb + (size_t)(kHalf * hf) * KVQ_PART_STRIDE;
+#pragma unroll
+        for (int u = 0; u < kHalf; ++u)
+          if ((late >> u) & 1) acc[u] = reinterpret_cast<const float2 *>(hb + (size_t)u * KVQ_PART_STRIDE + 4)[lane];
+#pragma unroll
+        for (int u = 0; u < kHalf; ++u) {
+          if (!((hmask >> u) & 1)) continue;  // wave-uniform
+          const float wj =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), kHalf * hf + u));
+          o0 = __builtin_fmaf(acc[u].x, wj, o0);
+          o1 = __builtin_fmaf(acc[u].y, wj, o1);
+        }
+      }
+      M = Mn;
+    }
+    hd = make_float4(ninf, 0.f, 0.f, 0.f);
   }
   if (M != ninf) {
     o0 = o0 / l;

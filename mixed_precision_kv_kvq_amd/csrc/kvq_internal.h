@@ -82,9 +82,13 @@ struct KvqAttnArgs {
   const void *q;
   float *partials;  // [B][Hq][S][KVQ_PART_STRIDE]
   int32_t q_f32, kv_f32, Hq, Hkv, R, rotation;
-  int32_t splits;                    // all splits
-  int32_t wsplits;                   // leading splits that cover the recent window, KVQ_WIN_PAGES pages each
-  int32_t wfold;                     // 1: no window splits; 16-token window blocks go to the quantized splits
+  // Split plan (computed per sequence on the device from the lengths, see the split kernel):
+  int32_t splits;     // row stride S_max of the partial rows: no sequence gets more splits
+  int32_t ws;         // leading splits of every unit that cover the recent window, KVQ_WIN_PAGES pages each
+  int32_t target_q;   // quantized waves to share out over the batch, in proportion to its pages
+  int32_t cap_max;    // most quantized splits of one unit
+  int32_t fixed_per;  // > 0: pages per quantized split fixed instead (KVQ_PAGES_PER_SPLIT)
+  int64_t grid;       // waves launched (an upper bound of the plan's total; the rest exit)
   int32_t max_len;  // host-validated upper bound of seq_lens (device lengths are clamped to it)
   float sigma_u;  // softmax_scale * log2(e) * 2^33
   // Fused decode step (fuse = 1; bf16 rings, window > 0): seq_lens are the lengths before the
@@ -99,6 +103,7 @@ struct KvqCombineArgs {
   const float *partials;
   void *out;
   int32_t out_f32, B, Hq, splits;
+  int32_t eager;  // entries whose rows are read together with the headers (the rest once seen live)
   int32_t value_rotation;  // the partials are over rotated values: rotate the merged row back
 };
 struct KvqDebugArgs {

@@ -223,7 +223,7 @@ __global__ __launch_bounds__(64) void kvq_dense_partials_kernel(KvqDenseArgs a) 
     for (int hh = 0; hh < G; ++hh) {
       float *pr = a.partials + (((size_t)b * a.Hq + h * G + hh) * a.splits + s) * KVQ_PART_STRIDE;
       reinterpret_cast<float2 *>(pr + 4)[lane] = make_float2(0.f, 0.f);
-      if (lane == 0) *reinterpret_cast<float4 *>(pr) = make_float4(ninf, 0.f, 0.f, 0.f);
+      if (lane == 0) *reinterpret_cast<float4 *>(pr) = make_float4(ninf, 0.f, (float)a.splits, 0.f);
     }
     return;
   }
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(64) void kvq_dense_partials_kernel(KvqDenseArgs a) 
       dst[0] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
       dst[1] = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
     }
-    if (lane == 0) *reinterpret_cast<float4 *>(pr) = make_float4(m[hh], l[hh], 0.f, 0.f);
+    if (lane == 0) *reinterpret_cast<float4 *>(pr) = make_float4(m[hh], l[hh], (float)a.splits, 0.f);  // every entry written
   }
 }
 

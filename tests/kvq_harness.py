@@ -42,10 +42,11 @@ class GpuRun:
     """
 
     def __init__(self, wl: W.Workload, device_gen: bool = False, chunk: int = 4096, kv_override=None,
-                 q_override=None):
+                 q_override=None, lengths=None):
         self.wl = wl
         self.params = params_of(wl)
-        self.L0 = wl.context_lengths()
+        self.L0 = wl.context_lengths() if lengths is None else np.asarray(lengths, dtype=np.int64)
+        assert len(self.L0) == wl.batch
         self.device_gen = device_gen
         self.kv_override = kv_override
         self.q_override = q_override

@@ -156,26 +156,27 @@ def test_edge_case(name):
     full_check(run, 0)
 
 
-# The recent window folded into the quantized splits (opt-in split plan, KVQ_WINDOW_FOLD=1): the
-# same comparisons on configurations with a bf16 window.
-FOLD = {
-    "config3-structure": dict(batch=2, context=1000, window=128, steps=3),
-    "window-ragged": dict(context=300, window=40),
-    "window-longer-than-seq": dict(context=50, window=128),
-    "window-plus-one": dict(context=129, window=128),
-    "paged-window": dict(context=0, var_len=(1, 300), block_size=16, window=16, batch=4),
-    "g8-window": dict(context=150, num_q_heads=16, num_kv_heads=2, window=32),
-    "f32-q-window": dict(context=160, window=48, q_dtype="f32"),
-    "kgroup64-vgroup64-window": dict(context=150, k_group=64, v_group=64, window=40),
+# The split plan is made per sequence on the device: a sequence's share of the launch follows its
+# length.  Batches with very different lengths, empty sequences, more than 64 sequences (the plan's
+# prefix sum runs over chunks of 64), windows, paged storage and decode steps.
+RAGGED = {
+    "long-and-short": dict(batch=4, context=0, var_len=(16, 6000)),
+    "one-long-many-empty": dict(batch=6, context=0, var_len=(0, 1), lengths=[0, 1, 5000, 0, 17, 2]),
+    "batch-70": dict(batch=70, num_q_heads=8, num_kv_heads=2, context=0, var_len=(0, 600)),
+    "window-ragged-steps": dict(batch=3, context=0, var_len=(50, 3000), window=64, steps=3),
+    "paged-ragged": dict(batch=5, context=0, var_len=(1, 4000), block_size=16),
+    "g8-rotated-ragged": dict(batch=3, num_q_heads=16, num_kv_heads=2, context=0, var_len=(100, 3000),
+                              rotation=True),
 }
 
 
-@pytest.mark.parametrize("name", list(FOLD))
-def test_folded_window(name, monkeypatch):
-    monkeypatch.setenv("KVQ_WINDOW_FOLD", "1")
-    wl = small(BASE, config=400 + list(FOLD).index(name), **FOLD[name])
-    say(f"folded window {name}: {FOLD[name]}")
-    run = GpuRun(wl, chunk=64)
+@pytest.mark.parametrize("name", list(RAGGED))
+def test_ragged_split_plan(name):
+    kw = dict(RAGGED[name])
+    lengths = kw.pop("lengths", None)
+    wl = small(BASE, config=400 + list(RAGGED).index(name), **kw)
+    say(f"ragged plan {name}: {RAGGED[name]}")
+    run = GpuRun(wl, chunk=1024, lengths=lengths)
     for s in range(max(wl.steps, 1)):  # steps == 0: one attention over the context
         full_check(run, s, out_check_bf16=(s == 0))
 
@@ -302,10 +303,18 @@ def test_phase_entry_points_match_attention():
     assert S >= 1 and wl.batch * wl.num_q_heads * S * K.KVQ_PART_FLOATS * 4 <= wsb
     blk = ws.view(torch.float32)[: wl.batch * wl.num_q_heads * S * K.KVQ_PART_FLOATS].cpu().numpy()
     blk = blk.astype(np.float64).reshape(wl.batch, wl.num_q_heads, S, K.KVQ_PART_FLOATS)
-    m, l, acc = blk[..., 0], blk[..., 1], blk[..., 4:]
-    assert np.all(blk[..., 2:4] == 0.0)
+    # entries [n, S) of a row are not written (n in every written header); empty splits have m = -inf
+    n = blk[:, :, :1, 2].astype(np.int64)
+    assert np.all(n >= 1) and np.all(n <= S)
+    written = np.arange(S)[None, None, :] < n
+    assert np.all(blk[..., 2][written] == np.broadcast_to(n, written.shape)[written])
+    assert np.all(blk[..., 3][written] == 0.0)
+    m, l, acc = np.where(written, blk[..., 0], -np.inf), blk[..., 1], blk[..., 4:]
+    empty = np.isneginf(m)
+    l = np.where(empty, 0.0, l)
+    acc = np.where(empty[..., None], 0.0, acc)
     M = m.max(axis=2, keepdims=True)
-    w = np.where(np.isneginf(m), 0.0, np.exp2(np.where(np.isneginf(m), 0.0, m - M)))
+    w = np.where(empty, 0.0, np.exp2(np.where(empty, 0.0, m - M)))
     o = (w[..., None] * acc).sum(axis=2) / (w * l).sum(axis=2)[..., None]
     assert np.allclose(o, got, rtol=1e-5, atol=1e-6)
 
