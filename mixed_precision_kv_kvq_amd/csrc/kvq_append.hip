@@ -9,16 +9,17 @@
 // from the nalar.dev article's section "Pertumbuhan cache mengubah trade pada
 // serving".
 //
-// One 64-lane wave per work item; lane l owns channels 2l and 2l+1.  Work
-// items of sequence b (L = current length, n = tokens appended, R = window):
-//   item i < min(n, R): ring slot (L + i) mod R.  The token leaving that slot
-//       (position L + i - R, when >= 0) is quantized from the ring, then the
-//       last new token that lands in the slot is written to it.
-//   item i >= R (only when n > R): new token L + i - R, which is already older
-//       than the window when the append finishes, is quantized directly.
-// Each ring slot is owned by exactly one wave, so the read of the old token and
-// the write of the new one never race.  All quantizer arithmetic is IEEE fp64
-// with no contraction, in the same operation order as its definition.
+// An append of n tokens to a sequence of length L with a window of R quantizes the positions
+// [max(L - R, 0), max(L + n - R, 0)): the old ring tokens that leave the window and, when n > R,
+// new tokens that are already older than the window on arrival.  Position t is read from ring
+// slot t mod R when t < L, else from input row t - L.  Whole 16-token pages of that range go to the
+// page kernel (one wave per page), the partial pages at either end (at most 15 tokens each) to the
+// per-token kernel (one wave per token, lane l owning channels 2l and 2l + 1).  Whoever reads an
+// old token from its ring slot also writes the slot's new content (the last appended token that
+// maps to it) after the read, in the same lanes: no slot is read and written by different waves.
+// Slots that held no token yet (L < R) are written by write-only items of the per-token kernel.
+// All quantizer arithmetic is IEEE fp64 with no contraction, in the same operation order as its
+// definition.
 #include <type_traits>
 
 #include "kvq_quant.h"
@@ -34,27 +35,34 @@ __device__ inline double load_elem(const uint8_t *row, int c, int kv_f32) {
   return (double)kvq_bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(row)[c]);
 }
 
-// Tokens quantized on arrival (an append of n > R tokens to a length-L sequence: input tokens
-// j < m = n - R go to positions L + j) are split between the two kernels: whole 16-token pages
-// inside [L, L + m) go to the page kernel, the partial pages at either end to the per-token
-// kernel (at most 15 tokens each).
-struct DirectSplit {
-  int64_t p_start, p_end;  // whole pages [p_start, p_end)
-  int head, tail;          // tokens before p_start and after p_end handled one by one
+// Positions quantized by an append of n tokens to a length-L sequence with window R, and their
+// split between the two kernels: whole pages [p_start, p_end) to the page kernel, `head` positions
+// before p_start and `tail` positions from p_end * 16 to the per-token kernel.
+struct QuantRange {
+  int64_t q0, q1;          // quantized positions [q0, q1)
+  int64_t p_start, p_end;  // whole pages
+  int head, tail;
 };
-__device__ inline DirectSplit direct_split(int64_t L, int m) {
-  DirectSplit d;
-  d.p_start = (L + KVQ_PAGE - 1) / KVQ_PAGE;
-  d.p_end = (L + m) / KVQ_PAGE;
+__device__ inline QuantRange quant_range(int64_t L, int n, int R) {
+  QuantRange d;
+  d.q0 = L - R > 0 ? L - R : 0;
+  d.q1 = L + n - R > 0 ? L + n - R : 0;
+  d.p_start = (d.q0 + KVQ_PAGE - 1) / KVQ_PAGE;
+  d.p_end = d.q1 / KVQ_PAGE;
   if (d.p_end > d.p_start) {
-    d.head = (int)(d.p_start * KVQ_PAGE - L);
-    d.tail = (int)(L + m - d.p_end * KVQ_PAGE);
+    d.head = (int)(d.p_start * KVQ_PAGE - d.q0);
+    d.tail = (int)(d.q1 - d.p_end * KVQ_PAGE);
   } else {
-    d.p_end = d.p_start;
-    d.head = m;
+    d.p_start = d.p_end = 0;
+    d.head = (int)(d.q1 - d.q0);
     d.tail = 0;
   }
   return d;
+}
+// The last appended position (< L + n) that maps to ring slot t mod R, for an old position t < L
+// that leaves the window in this append (so that position is t + R or later, an appended token).
+__device__ inline int64_t ring_final(int64_t t, int64_t L, int n, int R) {
+  return t + (int64_t)R * ((L + n - 1 - t) / R);
 }
 
 // Tokens appended to sequence b: n_new_per_seq[b] clamped into [0, n_new] (the rows of k_new and
@@ -74,16 +82,14 @@ __device__ inline int append_base(const KvqAppendArgs &a, int b) {
   return L < 0 ? 0 : L;
 }
 
-__global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
-  __shared__ uint8_t ck[KVQ_D];
-  __shared__ uint8_t cv[KVQ_D];
-  __shared__ uint32_t mk[KVQ_D / 32];
-  __shared__ uint32_t mv[KVQ_D / 64];
-
-  const int item = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+// One position of the quantized range outside whole pages (one wave, lane l owning channels 2l
+// and 2l + 1), item < head + tail; lds: at least 280 bytes.
+__device__ void token_item(const KvqAppendArgs &a, int item, int h, int b, uint8_t *lds) {
+  uint8_t *ck = lds, *cv = lds + KVQ_D;
+  uint32_t *mk = reinterpret_cast<uint32_t *>(lds + 2 * KVQ_D), *mv = mk + KVQ_D / 32;
+  const int lane = threadIdx.x;
   const int L = append_base(a, b);
   const int nb = append_count(a, b);
-  if (item >= nb) return;
   const int R = a.R, Hkv = a.Hkv;
   const int esz = a.kv_f32 ? 4 : 2;
   const size_t row_bytes = (size_t)KVQ_D * esz;
@@ -93,38 +99,24 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
   const uint8_t *srcK = nullptr, *srcV = nullptr;
   uint8_t *dstK = nullptr, *dstV = nullptr;
   const uint8_t *newK = nullptr, *newV = nullptr;
-  const int nring = nb < R ? nb : R;
-  if (item < nring) {
-    const int64_t slot = ((int64_t)L + item) % R;
-    const size_t win_off = (((size_t)b * Hkv + h) * R + slot) * row_bytes;
-    dstK = a.cache.k_win + win_off;
-    dstV = a.cache.v_win + win_off;
-    const int64_t t_old = (int64_t)L + item - R;
-    if (t_old >= 0) {
-      t_q = t_old;
+  const QuantRange d = quant_range(L, nb, R);
+  auto input_row = [&](int64_t pos) { return (((size_t)b * a.n_new + (size_t)(pos - L)) * Hkv + h) * row_bytes; };
+  auto ring_row = [&](int64_t pos) { return (((size_t)b * Hkv + h) * R + (size_t)(pos % R)) * row_bytes; };
+  if (item >= d.head + d.tail) return;
+  {
+    t_q = item < d.head ? d.q0 + item : d.p_end * KVQ_PAGE + (item - d.head);
+    if (t_q < L) {  // an old token leaving the ring: read it, then write the slot's new content
+      dstK = a.cache.k_win + ring_row(t_q);
+      dstV = a.cache.v_win + ring_row(t_q);
       srcK = dstK;
       srcV = dstV;
+      const int64_t f = ring_final(t_q, L, nb, R);
+      newK = a.k_new + input_row(f);
+      newV = a.v_new + input_row(f);
+    } else {
+      srcK = a.k_new + input_row(t_q);
+      srcV = a.v_new + input_row(t_q);
     }
-    const int64_t first = (int64_t)L + item, last = (int64_t)L + nb - 1;
-    const int64_t t_final = first + (int64_t)R * ((last - first) / R);
-    const size_t in_off = (((size_t)b * a.n_new + (size_t)(t_final - L)) * Hkv + h) * row_bytes;
-    newK = a.k_new + in_off;
-    newV = a.v_new + in_off;
-  } else {
-    // item nring + k: the k-th token quantized on arrival that is not in a whole page
-    const DirectSplit d = direct_split(L, nb - R);
-    const int k = item - nring;
-    int j;
-    if (k < d.head)
-      j = k;
-    else if (k - d.head < d.tail)
-      j = (int)(d.p_end * KVQ_PAGE - L) + (k - d.head);
-    else
-      return;
-    t_q = (int64_t)L + j;
-    const size_t in_off = (((size_t)b * a.n_new + j) * Hkv + h) * row_bytes;
-    srcK = a.k_new + in_off;
-    srcV = a.v_new + in_off;
   }
 
   double k0 = 0, k1 = 0, v0 = 0, v1 = 0;
@@ -179,17 +171,16 @@ __global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a) {
 // ROT: keys and/or values (a.rotation, a.value_rotation) are rotated first; the lane's values
 // are then fp64 (the transform's results).  Without rotation they are the inputs themselves,
 // exact in fp32, which halves the registers.
+constexpr int kMaxRecordWords = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 4;
+
 template <bool ROT>
-__global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
-  constexpr int kMaxRecordWords = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 4;
-  __shared__ __attribute__((aligned(16))) uint32_t rw[kMaxRecordWords];
-  const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+__device__ void page_item(const KvqAppendArgs &a, int pidx, int h, int b, uint32_t *rw) {
+  const int lane = threadIdx.x;
   const int L = append_base(a, b);
   const int nb = append_count(a, b);
-  const int m = nb - a.R;
-  if (m <= 0) return;
-  const DirectSplit d = direct_split(L, m);
-  const int64_t page = d.p_start + blockIdx.x;
+  const int R = a.R;
+  const QuantRange d = quant_range(L, nb, R);
+  const int64_t page = d.p_start + pidx;
   if (page >= d.p_end) return;
   if (page >= (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq)) {  // beyond the cache: dropped
     kvq_raise(a.cache, true, KVQ_DEV_CAPACITY);
@@ -200,15 +191,20 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   const int t = lane & 15, q = lane >> 4;
   const int esz = a.kv_f32 ? 4 : 2;
   const size_t row_bytes = (size_t)KVQ_D * esz;
-  const int j = (int)(page * KVQ_PAGE + t - L);  // input token of this lane's page token
-  const size_t in_off = (((size_t)b * a.n_new + j) * Hkv + h) * row_bytes;
+  // this lane's page token: an old token in ring slot pos mod R, or input row pos - L
+  const int64_t pos = page * KVQ_PAGE + t;
+  const bool from_ring = pos < L;
+  const size_t src_off = from_ring ? (((size_t)b * Hkv + h) * R + (size_t)(pos % (R > 0 ? R : 1))) * row_bytes
+                                   : (((size_t)b * a.n_new + (size_t)(pos - L)) * Hkv + h) * row_bytes;
+  const uint8_t *srcK = (from_ring ? a.cache.k_win : a.k_new) + src_off;
+  const uint8_t *srcV = (from_ring ? a.cache.v_win : a.v_new) + src_off;
   for (int w = lane; w < lay.record / 4; w += 64) rw[w] = 0u;
   __syncthreads();
 
   typedef typename std::conditional<ROT, double, float>::type Val;
   Val x[32];
   // This lane's 32 channels of a key or value row: 16-byte loads of bf16 or fp32 values.
-  auto load32 = [&](const uint8_t *row) {
+  auto load32 = [&](const uint8_t *row) __attribute__((always_inline)) {
     if (a.kv_f32) {
       const uint4 *p = reinterpret_cast<const uint4 *>(row + 128 * q);
 #pragma unroll
@@ -236,7 +232,7 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   // Normalized 128-point Walsh-Hadamard transform of the row: butterflies in stage order
   // 1, 2, ..., 64, stages up to 16 inside the lane, 32 and 64 across lanes q ^ 1 and q ^ 2
   // (same operands and order as the definition).
-  auto rotate = [&]() {
+  auto rotate = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int hs = 1; hs < 32; hs <<= 1) {
 #pragma unroll
@@ -262,7 +258,7 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     for (int e = 0; e < 32; ++e) x[e] = x[e] * KVQ_WHT_C;
   };
   // ---- keys ----
-  load32(a.k_new + in_off);
+  load32(srcK);
   if constexpr (ROT) {
     if (a.rotation) rotate();
   }
@@ -306,7 +302,7 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
     if ((32 * q) % lay.kg == 0) rw[lay.k_meta_off / 4 + kvq_meta_dword(lay.nkg, t, grp)] = g.sb | (g.zb << 16);
   }
   // ---- values ----
-  load32(a.v_new + in_off);
+  load32(srcV);
   if constexpr (ROT) {
     if (a.value_rotation) rotate();
   }
@@ -344,6 +340,60 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
   uint4 *rec = reinterpret_cast<uint4 *>(a.cache.pages + (size_t)rec_idx * lay.record);
   const uint4 *src = reinterpret_cast<const uint4 *>(rw);
   for (int c = lane; c < lay.record / 16; c += 64) rec[c] = src[c];
+  // A token read from the ring: its slot receives the last appended token that maps to it (this
+  // lane read those very bytes above, so the read precedes the write).
+  if (from_ring) {
+    const size_t in_off = (((size_t)b * a.n_new + (size_t)(ring_final(pos, L, nb, R) - L)) * Hkv + h) * row_bytes;
+    const int cb = 32 * esz;  // this lane's 32 channels
+    const uint4 *nk = reinterpret_cast<const uint4 *>(a.k_new + in_off + cb * q);
+    const uint4 *nv = reinterpret_cast<const uint4 *>(a.v_new + in_off + cb * q);
+    uint4 *dk = reinterpret_cast<uint4 *>(a.cache.k_win + src_off + cb * q);
+    uint4 *dv = reinterpret_cast<uint4 *>(a.cache.v_win + src_off + cb * q);
+    for (int k = 0; k < cb / 16; ++k) {
+      dk[k] = nk[k];
+      dv[k] = nv[k];
+    }
+  }
+}
+
+// Appended positions that stay in the ring and whose slot held no token before the append (the
+// ring was not yet full): plain row copies, all of one (sequence, kv head) by one wave, 16 bytes
+// per lane per instruction.
+__device__ void write_only_rows(const KvqAppendArgs &a, int h, int b) {
+  const int lane = threadIdx.x, R = a.R, Hkv = a.Hkv;
+  if (R == 0) return;
+  const int L = append_base(a, b);
+  const int nb = append_count(a, b);
+  const size_t row_bytes = (size_t)KVQ_D * (a.kv_f32 ? 4 : 2);
+  const int chunks = (int)(row_bytes / 16);  // 16-byte chunks per row
+  // the kept positions [first_kept, L + nb) (at most R) whose slot had no occupant before the
+  // append: the occupant, L - R + ((pos - L) mod R), is negative
+  const int64_t first_kept = L + nb - R > L ? L + nb - R : L;
+  const int64_t npos = L + nb - first_kept;
+  for (int64_t e = lane; e < npos * chunks; e += 64) {
+    const int64_t pos = first_kept + e / chunks;
+    const int c = (int)(e % chunks);
+    if (L - R + (pos - L) % R >= 0) continue;
+    const size_t in_off = (((size_t)b * a.n_new + (size_t)(pos - L)) * Hkv + h) * row_bytes + 16 * c;
+    const size_t win_off = (((size_t)b * Hkv + h) * R + (size_t)(pos % R)) * row_bytes + 16 * c;
+    *reinterpret_cast<uint4 *>(a.cache.k_win + win_off) = *reinterpret_cast<const uint4 *>(a.k_new + in_off);
+    *reinterpret_cast<uint4 *>(a.cache.v_win + win_off) = *reinterpret_cast<const uint4 *>(a.v_new + in_off);
+  }
+}
+
+// One launch per append: blocks [0, pages) take whole pages of the quantized range, the next
+// `tokens` blocks one position each of its partial pages, the last block the write-only ring rows.
+// The three kinds touch disjoint ring slots and records, so they run concurrently.
+template <bool ROT>
+__global__ __launch_bounds__(64) void kvq_append_kernel(KvqAppendArgs a, int pages, int tokens) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kMaxRecordWords];
+  const int bx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (bx < pages)
+    page_item<ROT>(a, bx, h, b, lds);
+  else if (bx < pages + tokens)
+    token_item(a, bx - pages, h, b, reinterpret_cast<uint8_t *>(lds));
+  else
+    write_only_rows(a, h, b);
 }
 
 }  // namespace
@@ -351,20 +401,15 @@ __global__ __launch_bounds__(64) void kvq_append_pages_kernel(KvqAppendArgs a) {
 hipError_t kvq_launch_append(const KvqAppendArgs &a, hipStream_t s) {
   if (a.n_new <= 0 || a.cache.batch <= 0) return hipSuccess;
   (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
-  // per-token kernel: the ring items, then at most 2 * 15 tokens quantized on arrival outside
-  // whole pages; page kernel: the whole pages (at most (n - R) / 16 per sequence)
-  const int ring = a.n_new < a.R ? a.n_new : a.R;
-  const int direct = a.n_new - ring;
-  const int items = ring + (direct < 2 * (KVQ_PAGE - 1) ? direct : 2 * (KVQ_PAGE - 1));
-  hipLaunchKernelGGL(kvq_append_kernel, dim3((unsigned)items, (unsigned)a.Hkv, (unsigned)a.cache.batch), dim3(64), 0,
-                     s, a);
-  if (direct >= KVQ_PAGE) {
-    const unsigned pages = (unsigned)(direct / KVQ_PAGE);
-    const dim3 grid(pages, (unsigned)a.Hkv, (unsigned)a.cache.batch);
-    if (a.rotation || a.value_rotation)
-      hipLaunchKernelGGL(kvq_append_pages_kernel<true>, grid, dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL(kvq_append_pages_kernel<false>, grid, dim3(64), 0, s, a);
-  }
+  // The quantized range of a sequence is at most n positions long: at most ceil(n / 16) whole pages
+  // (none when n < 16) and at most 15 positions before and 15 after them.
+  const int n = a.n_new;
+  const int pages = n >= KVQ_PAGE ? (n + KVQ_PAGE - 1) / KVQ_PAGE : 0;
+  const int part = n < KVQ_PAGE - 1 ? n : KVQ_PAGE - 1;
+  const dim3 grid((unsigned)(pages + 2 * part + (a.R > 0 ? 1 : 0)), (unsigned)a.Hkv, (unsigned)a.cache.batch);
+  if (a.rotation || a.value_rotation)
+    hipLaunchKernelGGL(kvq_append_kernel<true>, grid, dim3(64), 0, s, a, pages, 2 * part);
+  else
+    hipLaunchKernelGGL(kvq_append_kernel<false>, grid, dim3(64), 0, s, a, pages, 2 * part);
   return hipGetLastError();
 }
