@@ -70,52 +70,116 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-SPLIT_KERNEL = "kvq_attn_split_kernel<4, 2, 4, 1, 1>"
-COPY_KERNEL_HINT = "copy"  # torch's device-to-device copy kernel name contains this
+SPLIT_KERNEL = "kvq_attn_split_kernel<4, 2, 4, 1, 1>"  # the instantiation of the timed decode step
+SPLIT_PREFIX = "kvq_attn_split_kernel<"  # every instantiation (the dispatch plan counts them all)
+CALIBRATION_KERNEL = "stream_copy_kernel"  # kvq_gen_stream_copy: a copy of known size
+# phases whose per-launch counters are kept in the traffic file (decode step; paged and rotated
+# workloads), each keyed by its phase name in the dispatch plan
+TRAFFIC_PHASES = ("fused split kernel, cold", "attention-only split kernel, cold", "paged K4V2: cold",
+                  "rotated 131k: cold")
 
 
-def summarize_pmc(fetch_dir, write_dir, copy_bytes):
-    """Per-launch HBM bytes of the split kernel from two rocprofv3 --pmc runs (FETCH_SIZE, then
-    WRITE_SIZE, in KiB per dispatch) of `bench.py --copy-calibration-mib N`, each scaled by the
-    ratio of the copy kernel's known bytes to what the same counter reports for it."""
+def progress(msg):
+    """A progress line on stderr (long runs report each phase as it starts)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _split_name(name):
+    """The template instantiation of a split-kernel dispatch name, e.g. '<4, 2, 4, 1, 1>'."""
+    name = name.replace("  ", " ")
+    i = name.find(SPLIT_PREFIX)
+    return name[i + len(SPLIT_PREFIX) - 1:name.index(">", i) + 1]
+
+
+def _plan_slices(split_rows, plan):
+    """Yield (phase, all rows of the phase, timed rows) by walking the dispatch plan over the
+    split-kernel dispatches in launch order."""
+    i = 0
+    for ph in plan:
+        seg = split_rows[i:i + ph["launches"]]
+        i += ph["launches"]
+        yield ph, seg, seg[ph["untimed_first"]:]
+
+
+def _last_json(path):
+    with open(path) as fh:
+        return json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+
+
+def summarize_pmc(fetch_dir, write_dir, bench_json, copy_bytes, out_path=TRAFFIC_FILE):
+    """Per-launch HBM bytes of the split kernel in the phases of TRAFFIC_PHASES from two rocprofv3
+    --pmc runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch) of `bench.py
+    --copy-calibration-mib N` with the same arguments, each counter scaled by the ratio of the
+    calibration copy's known bytes to what the same counter reports for it.  Dispatches are
+    assigned to phases by the dispatch plan the run printed (bench_json)."""
     import csv
     import glob
+
+    plan = _last_json(bench_json)["split_kernel_dispatch_plan"]
 
     def read(d, counter):
         rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
-        split = [float(r["Counter_Value"]) for r in rows if SPLIT_KERNEL in r["Kernel_Name"].replace("  ", " ")]
-        copy = [float(r["Counter_Value"]) for r in rows
-                if COPY_KERNEL_HINT in r["Kernel_Name"].lower() and "kvq" not in r["Kernel_Name"]]
-        if not split or not copy:
-            raise SystemExit(f"{counter}: no split-kernel or copy-kernel rows under {d}")
-        return sum(split) / len(split), max(copy), len(split)
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id") or r["Correlation_Id"]))
+        split = [r for r in rows if SPLIT_PREFIX in r["Kernel_Name"].replace("  ", " ")]
+        cal = [float(r["Counter_Value"]) for r in rows if CALIBRATION_KERNEL in r["Kernel_Name"]]
+        if not split or not cal:
+            raise SystemExit(f"{counter}: no split-kernel or calibration rows under {d}")
+        if len(split) != sum(p["launches"] for p in plan):
+            raise SystemExit(f"{counter}: {len(split)} split-kernel dispatches, the plan expects "
+                             f"{sum(p['launches'] for p in plan)}")
+        per = {}
+        for ph, _, timed in _plan_slices(split, plan):
+            if ph["phase"] in TRAFFIC_PHASES and timed:
+                per[ph["phase"]] = (sum(float(r["Counter_Value"]) for r in timed) / len(timed), len(timed),
+                                    _split_name(timed[0]["Kernel_Name"]))
+        return per, sum(cal) / len(cal)
 
-    fs, fc, n1 = read(fetch_dir, "FETCH_SIZE")
-    ws, wc, n2 = read(write_dir, "WRITE_SIZE")
+    fetch, fc = read(fetch_dir, "FETCH_SIZE")
+    write, wc = read(write_dir, "WRITE_SIZE")
     f_factor = copy_bytes / (fc * 1024.0)
     w_factor = copy_bytes / (wc * 1024.0)
+    phases = {}
+    for name in TRAFFIC_PHASES:
+        if name in fetch and name in write:
+            rd = int(fetch[name][0] * 1024.0 * f_factor)
+            wr = int(write[name][0] * 1024.0 * w_factor)
+            phases[name] = {"instantiation": fetch[name][2], "launches": [fetch[name][1], write[name][1]],
+                            "fetch_kib_raw": fetch[name][0], "write_kib_raw": write[name][0],
+                            "read_bytes_per_launch": rd, "write_bytes_per_launch": wr, "bytes_per_launch": rd + wr}
+    head = phases.get(TRAFFIC_PHASES[0])
     out = {
         "kernel": SPLIT_KERNEL,
         "source_digest": source_digest(),
-        "fetch_kib_per_launch_raw": fs, "write_kib_per_launch_raw": ws,
         "copy_bytes": copy_bytes, "copy_fetch_kib_raw": fc, "copy_write_kib_raw": wc,
         "fetch_scale": f_factor, "write_scale": w_factor,
-        "launches": [n1, n2],
-        "bytes_per_launch": int(fs * 1024.0 * f_factor + ws * 1024.0 * w_factor),
-        "read_bytes_per_launch": int(fs * 1024.0 * f_factor),
-        "write_bytes_per_launch": int(ws * 1024.0 * w_factor),
+        "bytes_per_launch": head["bytes_per_launch"] if head else None,
+        "phases": phases,
     }
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
+def stored_traffic(phase):
+    """Counter-measured HBM bytes per launch of a phase, or None when absent or taken from other
+    kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tr.get("source_digest") != source_digest():
+        return None
+    return (tr.get("phases") or {}).get(phase, {}).get("bytes_per_launch")
+
+
 def summarize_trace(trace_dir, bench_json, out_md, command):
-    """Per-phase average durations of the split kernel (and the other kernels' averages) from a
-    `rocprofv3 --kernel-trace` run of this script, sliced by the dispatch plan the run printed."""
+    """Per-phase average durations of the split kernel (every instantiation) and the other
+    kernels' averages from a `rocprofv3 --kernel-trace` run of this script, sliced by the
+    dispatch plan the run printed."""
     import csv
     import glob
 
@@ -132,42 +196,46 @@ def summarize_trace(trace_dir, bench_json, out_md, command):
         con.close()
     if not rows:
         raise SystemExit(f"no kernel trace under {trace_dir}")
-    with open(bench_json) as fh:
-        res = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+    res = _last_json(bench_json)
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
 
     def dur(r):
         return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # ns -> µs
 
-    split = [r for r in rows if SPLIT_KERNEL in r["Kernel_Name"].replace("  ", " ")]
-    lines = [f"# Kernel trace of `{res['config']['workload']}`", "", "Command (repository root on the GPU box):", "",
-             "```", command, "```", "",
-             f"Split kernel `{SPLIT_KERNEL}`: {len(split)} dispatches; the plan printed by the run expects "
-             f"{sum(p['launches'] for p in res['split_kernel_dispatch_plan'])}.", "",
-             "| phase | launches | timed | trace avg µs | trace min µs | trace max µs |", "|---|---:|---:|---:|---:|---:|"]
-    i = 0
-    for ph in res["split_kernel_dispatch_plan"]:
-        seg = split[i:i + ph["launches"]][ph["untimed_first"]:]
-        i += ph["launches"]
-        if seg:
-            d = [dur(r) for r in seg]
-            lines.append(f"| {ph['phase']} | {ph['launches']} | {len(seg)} | {sum(d) / len(d):.2f} | {min(d):.2f} | "
-                         f"{max(d):.2f} |")
+    split = [r for r in rows if SPLIT_PREFIX in r["Kernel_Name"].replace("  ", " ")]
+    plan = res["split_kernel_dispatch_plan"]
+    expect = sum(p["launches"] for p in plan)
+    lines = [f"# Kernel trace of `{res['config']['workload']}` and the bench's other workloads", "",
+             "Command (repository root on the GPU box):", "", "```", command, "```", "",
+             f"Split kernel (`kvq_attn::kvq_attn_split_kernel<KB, VB, G, P, NVG>`, every instantiation): "
+             f"{len(split)} dispatches; the dispatch plan printed by the run expects {expect}"
+             + ("." if len(split) == expect else " (MISMATCH: phases below are unreliable)."), "",
+             "| phase | instantiation | launches | timed | trace avg µs | trace min µs | trace max µs |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    for ph, seg, timed in _plan_slices(split, plan):
+        inst = _split_name(seg[0]["Kernel_Name"]) if seg else ""
+        if timed:
+            d = [dur(r) for r in timed]
+            lines.append(f"| {ph['phase']} | `{inst}` | {ph['launches']} | {len(timed)} | {sum(d) / len(d):.2f} | "
+                         f"{min(d):.2f} | {max(d):.2f} |")
         else:
-            lines.append(f"| {ph['phase']} | {ph['launches']} | 0 | | | |")
+            lines.append(f"| {ph['phase']} | `{inst}` | {ph['launches']} | 0 | | | |")
+    rf = res["roofline"]
     lines += ["", "Bench figures of the same run (HIP events):", "",
-              f"- value (µs per fused step, wall clock): {res['value']}; events: {res['gpu_us_per_step']}",
-              f"- split kernel cold / warm (µs): {res['split_kernel_us_cold']} / {res['split_kernel_us_warm']}",
+              f"- value (µs per fused decode step, wall clock): {res['value']}; events: {res['gpu_us_per_step']}",
+              f"- fused split kernel cold / warm (µs): {res['split_kernel_us_cold']} / {res['split_kernel_us_warm']}"
+              f" (roofline frac cold {rf['frac']}, warm {rf['frac_warm']}; streaming ceiling "
+              f"{rf['stream_ceiling_GBs']} GB/s)",
               f"- attention-only split kernel cold / warm (µs): {res['attention_split_kernel']['us_cold']} / "
               f"{res['attention_split_kernel']['us_warm']}",
               f"- merge (µs): {res['combine_us']}", "", "Other kernels (all dispatches):", "",
               "| kernel | dispatches | avg µs |", "|---|---:|---:|"]
     by = {}
     for r in rows:
-        if SPLIT_KERNEL in r["Kernel_Name"].replace("  ", " "):
+        if SPLIT_PREFIX in r["Kernel_Name"].replace("  ", " "):
             continue
         by.setdefault(r["Kernel_Name"][:90], []).append(dur(r))
-    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1]))[:12]:
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1]))[:14]:
         lines.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -357,6 +425,7 @@ def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
                 os.environ["KVQ_PAGES_PER_SPLIT"] = old_env
         rf = kernel_roofline(cold, warm, nbytes, ceiling_GBs)
         rows.append(dict(k_bits=kb, v_bits=vb, row_stride_splits=splits, combine_us=round(comb, 2),
+                         traffic=stored_traffic(f"paged K{kb}V{vb}: cold"),
                          uniform_plan_us_cold=round(cold_uniform, 2),
                          uniform_plan_frac_cold=round(nbytes / cold_uniform / 1e3 / PEAK_HBM_GBS, 4), **rf))
         del copies, calls, calls2, ws2
@@ -418,6 +487,8 @@ def rotated_131k(torch, dev, reps, stream, ceiling_GBs, plan):
         e[1].record(stream)
         torch.cuda.synchronize()
         app_us += e[0].elapsed_time(e[1]) * 1e3
+        if (t0 // chunk) % 8 == 7:
+            progress(f"rotated 131k prefill: {t0 + chunk} tokens")
     del kbuf, vbuf
     per_th = d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4
     prefill_bytes = B * Hkv * L * (2 * d * 2 + per_th)  # every row read once, its codes written once
@@ -439,6 +510,7 @@ def rotated_131k(torch, dev, reps, stream, ceiling_GBs, plan):
     del copies, calls, cb, ws
     torch.cuda.synchronize()
     rf = kernel_roofline(cold, warm, nbytes, ceiling_GBs)
+    rf["traffic"] = stored_traffic("rotated 131k: cold")
     return {"workload": wl.name, "what": "kvq_decode_partials (split kernel, read-only, rotated query) + "
                                          "kvq_decode_combine (bf16 output); algorithmic bytes = codes and metadata "
                                          "of every token-head + queries",
@@ -552,7 +624,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON", "COPY_MIB"),
                     help="write the split kernel's per-launch HBM traffic from two --pmc runs and exit")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD", "COMMAND"),
                     help="per-phase split-kernel durations of a --kernel-trace run of this script, and exit")
@@ -561,7 +633,8 @@ def main():
         summarize_trace(*args.summarize_trace)
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], int(args.summarize_pmc[2]) << 20)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2],
+                      int(args.summarize_pmc[3]) << 20)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path shards over (sequence, kv head) "
@@ -575,6 +648,8 @@ def main():
     # The oracle baseline runs first, in forked single-threaded workers, before this process
     # touches the GPU.
     cpu_res = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seconds)
+    if cpu_res is not None:
+        progress(f"oracle baseline: {cpu_res['value']} {cpu_res['unit']}")
 
     import numpy as np
     import torch
@@ -605,15 +680,19 @@ def main():
         pre.append((t0, n, gen.kv(W.TENSOR_K, t0, n), gen.kv(W.TENSOR_V, t0, n),
                     torch.full((B,), t0, dtype=torch.int32, device=dev)))
     prefill_bytes = sum(append_bytes(wl, t0, n) for t0, n, _, _, _ in pre)
+    # arguments marshalled before timing, so the launches reach the GPU back to back
+    pre_calls = [K.bound_call("kvq_quantize_append", params, cache.struct, before, None, k, v, n, stream=stream)
+                 for t0, n, k, v, before in pre]
     ev_p = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev_p[0].record(stream)
-    for t0, n, k, v, before in pre:
-        K.kvq_quantize_append(params, cache.struct, before, None, k, v, n)
+    for f in pre_calls:
+        f()
     ev_p[1].record(stream)
     torch.cuda.synchronize()
     prefill_us = ev_p[0].elapsed_time(ev_p[1]) * 1e3
-    del pre
+    progress(f"prefill of {L0} tokens: {prefill_us:.0f} us")
+    del pre, pre_calls
     # per-step inputs, resident in HBM before timing
     k_steps = [gen.kv(W.TENSOR_K, L0 + s, 1) for s in range(total_steps)]
     v_steps = [gen.kv(W.TENSOR_V, L0 + s, 1) for s in range(total_steps)]
@@ -626,10 +705,13 @@ def main():
     setup_s = time.time() - t_setup
 
     if args.copy_calibration_mib:
-        # uint8 -> int8: an elementwise copy kernel reading and writing exactly N bytes each
+        # the generator library's plain copy kernel, reading and writing exactly N bytes each
+        from workloads.device import stream_copy
+
         src = torch.zeros(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty(src.shape, dtype=torch.int8, device=dev)
-        dst.copy_(src)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            stream_copy(dst, src, src.numel(), stream)
         torch.cuda.synchronize()
         del src, dst
 
@@ -676,6 +758,7 @@ def main():
 
     def plan(phase, launches, untimed_first=0):
         dispatch_plan.append({"phase": phase, "launches": int(launches), "untimed_first": int(untimed_first)})
+        progress(f"done: {phase}")
 
     for s in range(args.warmup):
         for f in step_fused(s):
@@ -841,14 +924,7 @@ def main():
         del k_ref, v_ref
         torch.cuda.synchronize()
 
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("source_digest") == source_digest():
-            traffic = tr.get("bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    traffic = stored_traffic("fused split kernel, cold")
 
     step_cold_us = split_cold_us + combine_us  # the two launches of a cold decode step
     res = {
@@ -878,7 +954,8 @@ def main():
         "split_kernel_us_cold": round(split_cold_us, 2),
         "split_kernel_us_warm": round(split_warm_us, 2),
         "attention_split_kernel": dict(attn_rf, what="kvq_decode_partials at the same length (attention only, "
-                                                     "read-only)"),
+                                                     "read-only)",
+                                       traffic=stored_traffic("attention-only split kernel, cold")),
         "combine_us": round(combine_us, 2),
         "decode_append_us_separate_kernel": round(append_us, 2),
         "tokens_per_s": round(B / (us_per_step * 1e-6), 1),
@@ -898,8 +975,8 @@ def main():
         "setup_s": round(setup_s, 2),
         "prefill_quantize": {
             "what": f"bulk append + quantize of the {L0}-token context, {(L0 + chunk - 1) // chunk} appends of "
-                    f"{chunk} tokens per sequence (kvq_quantize_append) back to back between two events, "
-                    f"inputs already in HBM",
+                    f"{chunk} tokens per sequence (kvq_quantize_append, arguments marshalled beforehand) back to "
+                    f"back between two events, inputs already in HBM",
             "us": round(prefill_us, 1), "algorithmic_bytes": int(prefill_bytes),
             "achieved_GBs": round(prefill_bytes / (prefill_us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(prefill_bytes / (prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),

@@ -35,6 +35,11 @@ int kvq_gen_q(void *out, int out_f32, uint64_t key, const float *table, int B, i
 int kvq_gen_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int nontemporal,
                         hipStream_t stream);
 
+/* Counter calibration: copy floor(bytes / 16) 16-byte words from `src` to `dst` (device, 16-byte
+ * aligned, not overlapping), a kernel whose HBM traffic is known exactly (that many bytes read
+ * and written).  Returns a hipError_t. */
+int kvq_gen_stream_copy(void *dst, const void *src, size_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
 
 def test_generator_exports():
     names = declared("kvq_gen.h")
-    assert names == ["kvq_gen_kv", "kvq_gen_q", "kvq_gen_stream_read"]
+    assert names == ["kvq_gen_kv", "kvq_gen_q", "kvq_gen_stream_copy", "kvq_gen_stream_read"]
     lib = ctypes.CDLL(os.path.join(ROOT, "workloads", "libkvqgen.so"))
     for n in names:
         assert hasattr(lib, n)

@@ -33,6 +33,8 @@ def _lib():
         lib.kvq_gen_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                             ctypes.c_int, ctypes.c_void_p]
         lib.kvq_gen_stream_read.restype = ctypes.c_int
+        lib.kvq_gen_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.kvq_gen_stream_copy.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -87,3 +89,11 @@ def stream_read_call(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, blocks:
             raise RuntimeError(f"kvq_gen_stream_read failed: hip error {rc}")
 
     return call
+
+
+def stream_copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int, stream):
+    """Launch the plain copy kernel over nbytes (a kernel of known traffic, for counter calibration)."""
+    assert dst.numel() * dst.element_size() >= nbytes and src.numel() * src.element_size() >= nbytes
+    rc = _lib().kvq_gen_stream_copy(dst.data_ptr(), src.data_ptr(), int(nbytes), stream.cuda_stream)
+    if rc:
+        raise RuntimeError(f"kvq_gen_stream_copy failed: hip error {rc}")

@@ -79,6 +79,12 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4v *p, int64
   if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
 }
 
+// Plain copy of n16 16-byte words (a kernel of known traffic: n16 * 16 bytes read and written).
+__global__ __launch_bounds__(256) void stream_copy_kernel(u32x4v *dst, const u32x4v *src, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 unsigned grid_for(int64_t total) {
   int64_t g = (total + 255) / 256;
   if (g > 65536) g = 65536;
@@ -119,5 +125,14 @@ extern "C" int kvq_gen_stream_read(const void *buf, size_t bytes, uint32_t *sink
   else
     hipLaunchKernelGGL(stream_read_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const u32x4v *)buf, n16, sink);
+  return (int)hipGetLastError();
+}
+
+extern "C" int kvq_gen_stream_copy(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 <= 0) return 0;
+  (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(grid_for(n16 / 4)), dim3(256), 0, stream, (u32x4v *)dst,
+                     (const u32x4v *)src, n16);
   return (int)hipGetLastError();
 }
