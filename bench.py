@@ -374,7 +374,7 @@ def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
     from workloads.device import DeviceGenerator
 
     rows, eb_rows = [], []
-    for kb, vb in W.SWEEP_BITS:
+    for kb, vb in W.SWEEP_BITS + W.PLANE_BITS:
         wl = W.WORKLOADS[4].with_bits(kb, vb)
         Lb = wl.context_lengths()
         Lmax = int(Lb.max())

@@ -35,7 +35,10 @@
  *     [V codes 256*v_bits B][V meta 64*(128/v_group) B]
  * whose internal order matches the register layout of the attention kernel;
  * kvq_dequantize_debug reads it back in logical order.  Metadata entries are
- * {fp16 scale, fp16 zero} pairs.
+ * {fp16 scale, fp16 zero} pairs.  Codes of 3, 5 and 6 bits are stored as bit
+ * planes of 4, 2 and 1 bits (the binary digits of the width), each plane an area
+ * of its own in the layout of a code of that width, so the code areas still take
+ * 256 bits-per-code bytes: a record holds exactly the payload and the metadata.
  *   block_size == 0 (contiguous, page-major): page p of kv head h of sequence b is
  *       record p * (batch * num_kv_heads) + b * num_kv_heads + h, for
  *       p < ceil(capacity / 16); the records of one (sequence, kv head) are spread
@@ -54,7 +57,7 @@
  *   - Sequence lengths are read on the device; the library never writes them.
  *     The caller advances them between append and attention.
  *   - Inputs must be finite with |x| < 2^15; non-finite inputs give unspecified (but
- *     memory-safe) results.  The fp16 metadata is then finite for 2..8-bit codes.  With
+ *     memory-safe) results.  The fp16 metadata is then finite for 2- to 8-bit codes.  With
  *     1-bit codes a group whose range (max - zero) exceeds 65504 has no finite fp16 scale:
  *     it gets scale +inf and all codes 0, as the quantizer's definition gives, and its
  *     dequantized values (and any attention over them) are NaN; |x| < 2^14 (or bf16 inputs,
@@ -87,7 +90,10 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 typedef enum { KVQ_ROT_NONE = 0, KVQ_ROT_WHT = 1 } kvq_rotation;
 
 /* Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
- * k_bits, v_bits in {1, 2, 4, 8}; k_group in {32, 64, 128}; v_group in {64, 128};
+ * k_bits, v_bits in {1, 2, 3, 4, 5, 6, 8} (gist.science summary of "Quantize What
+ * Counts", section "Resultaten": bit widths from 1 to 8 for keys and values
+ * separately; 7 is not offered);
+ * k_group in {32, 64, 128}; v_group in {64, 128};
  * window >= 0; block_size in {0, 16}; value_rotation only with window == 0. */
 typedef struct {
   int32_t head_dim;

@@ -37,8 +37,10 @@ GEN_LIB = os.path.join(ROOT, "workloads", "libkvqgen.so")
 BUILD_DIR = os.environ.get("KVQ_BUILD_DIR") or os.path.join(PKG, "_build")
 
 
-# Bit widths of the split-kernel instantiations: kvq_attn_inst.hip is compiled once per pair.
-ATTN_BITS = [(kb, vb) for kb in (1, 2, 4, 8) for vb in (1, 2, 4, 8)]
+# Bit widths of the split-kernel instantiations: kvq_attn_inst.hip is compiled once per pair
+# (about a minute of compiler time each).  7-bit codes (three bit planes) are left out.
+WIDTHS = (1, 2, 3, 4, 5, 6, 8)
+ATTN_BITS = [(kb, vb) for kb in WIDTHS for vb in WIDTHS]
 
 
 def _units():

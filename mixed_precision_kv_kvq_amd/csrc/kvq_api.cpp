@@ -10,7 +10,8 @@ constexpr int kNumCUs = KVQ_NUM_CUS;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool is_pow2_bits(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+// 1..6 and 8 bits (the split kernel is instantiated for these widths)
+bool bits_ok(int b) { return b >= 1 && b <= 8 && b != 7; }
 
 kvq_status check_params(const kvq_params *p) {
   if (!p) return KVQ_EINVAL;
@@ -21,7 +22,7 @@ kvq_status check_params(const kvq_params *p) {
   if (p->head_dim != KVQ_D) return KVQ_EUNSUPPORTED;
   const int g = p->num_q_heads / p->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_EUNSUPPORTED;
-  if (!is_pow2_bits(p->k_bits) || !is_pow2_bits(p->v_bits)) return KVQ_EUNSUPPORTED;
+  if (!bits_ok(p->k_bits) || !bits_ok(p->v_bits)) return KVQ_EUNSUPPORTED;
   if (p->k_group != 32 && p->k_group != 64 && p->k_group != 128) return KVQ_EUNSUPPORTED;
   if (p->v_group != 64 && p->v_group != 128) return KVQ_EUNSUPPORTED;
   if (p->block_size != 0 && p->block_size != KVQ_PAGE) return KVQ_EUNSUPPORTED;

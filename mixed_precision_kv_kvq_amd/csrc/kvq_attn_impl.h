@@ -57,19 +57,24 @@ constexpr float EXP2_EQ = 0x1p100f;  // query operand scale
 constexpr float P_BIAS_LOG2 = 64.0f;
 constexpr float EXP2_OUT = 0x1p69f;
 
-// Position of a b-bit field within a 16-bit half when extracted without a full
-// shift: fields whose bits end inside the low byte are read in place (a bf16
-// bit pattern x in the low byte is the value x * 2^-133, so a field at bit s
-// reads as code * 2^s); higher fields are first shifted down by 8.
-template <int B>
-__device__ __forceinline__ constexpr int field_scale_log2(int bit) {
-  return (bit + B <= 8) ? bit : bit - 8;
+// Scale (log2) at which a b-bit code is read when its lowest plane's field sits at bit `bit` of a
+// 16-bit half: in place when the whole code then ends inside the low byte (a bf16 bit pattern x
+// in the low byte is the value x * 2^-133, so a code moved to bit s reads as code * 2^s); after
+// a shift by 8 when that is enough; else moved down to bit 0.  The other planes' values are moved
+// next to it (plane at code offset o to bit s + o).
+__host__ __device__ constexpr int code_read_scale(int b, int bit) {
+  return bit + b <= 8 ? bit : ((bit >= 8 && bit - 8 + b <= 8) ? bit - 8 : 0);
 }
-// Extract the field of both 16-bit halves at `bit` as a bf16 pair, scaled by 2^field_scale_log2.
-template <int B>
-__device__ __forceinline__ uint32_t field_pair(uint32_t word, uint32_t word_sh8, int bit) {
-  constexpr uint32_t m = ((1u << B) - 1u) * 0x00010001u;
-  return (bit + B <= 8) ? (word & (m << bit)) : (word_sh8 & (m << (bit - 8)));
+// The field of width w at `bit` of both 16-bit halves of `word`, moved to bit `to` of each half
+// (word_sh8 = word >> 8, shared by the fields a shift by 8 brings into place).  Masking after the
+// shift keeps exactly the field's own bits: the target bits [to, to + w) of each half receive
+// source bits [bit, bit + w) of the same half.
+__device__ __forceinline__ uint32_t field_move(uint32_t word, uint32_t word_sh8, int w, int bit, int to) {
+  const uint32_t m = (((1u << w) - 1u) * 0x00010001u) << to;
+  const int d = bit - to;
+  if (d == 0) return word & m;
+  if (d == 8) return word_sh8 & m;
+  return d > 0 ? ((word >> d) & m) : ((word << -d) & m);
 }
 
 template <int N>
@@ -210,7 +215,8 @@ struct Kern {
   static constexpr int HB = (G + 3) / 4;   // head blocks: row q of the score layout holds heads q + 4 hb
   static constexpr int HSN = G < 4 ? G : 4;  // rows of the score layout in use
   static constexpr int NACC = HB;           // score accumulators (both query parts add into one)
-  static constexpr int PERK = 16 / KB;
+  static constexpr int NPK = kvq_nplanes(KB), NPV = kvq_nplanes(VB);  // bit planes of a code
+  static constexpr int KW0 = kvq_plane_width(KB, 0), VW0 = kvq_plane_width(VB, 0);
   typedef State<HB, NVG> St;
 
   struct Ctx {
@@ -223,9 +229,9 @@ struct Kern {
     float tau;  // lazy-max margin in score units (16 in log2 units)
   };
 
-  // Scale (log2) at which the key codes of chunk kc, pair slot i are read (see field_pair).
+  // Scale (log2) at which the key codes of chunk kc, pair slot i are read (see code_read_scale).
   static __device__ __forceinline__ constexpr int kslot_scale(int kc, int i) {
-    return field_scale_log2<KB>(KB * ((4 * kc + i) % PERK));
+    return code_read_scale(KB, KW0 * ((4 * kc + i) % (16 / KW0)));
   }
 
   // The query operand (A of the score contraction).  Row rho = 4 hs + j of head block hb
@@ -351,15 +357,23 @@ struct Kern {
     uint32_t vm[NVG];  // this lane's token: {scale, zero} per value group
   };
 
-  // Key codes of chunk kc of one page as the B operand (slot scales per kslot_scale).
+  // Key codes of chunk kc of one page as the B operand (slot scales per kslot_scale): per pair
+  // slot, the value of each bit plane moved into place and OR-ed (one plane: masked in place or
+  // after the shared shift by 8).
   template <int KS>
   static __device__ __forceinline__ bf16x8 key_operand(const PageData<KS> &pd, int kc) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int u = 4 * kc + i;
-      const uint32_t word = pd.kc.w[u / PERK];
-      w[i] = field_pair<KB>(word, word >> 8, KB * (u % PERK));
+      const int u = 4 * kc + i, sc = kslot_scale(kc, i);
+      uint32_t v = 0;
+#pragma unroll
+      for (int p = 0; p < NPK; ++p) {
+        const int pw = kvq_plane_width(KB, p), po = kvq_plane_off(KB, p), per = 16 / pw;
+        const uint32_t word = pd.kc.w[po + u / per];
+        v |= field_move(word, word >> 8, pw, pw * (u % per), sc + po);
+      }
+      w[i] = v;
     }
     return pack8(w[0], w[1], w[2], w[3]);
   }
@@ -468,7 +482,7 @@ struct Kern {
   }
 
   // Scale (log2) at which the value codes of tile m are read (independent of the pair slot).
-  static __device__ __forceinline__ constexpr int vtile_scale(int m) { return field_scale_log2<VB>((m * VB) & 15); }
+  static __device__ __forceinline__ constexpr int vtile_scale(int m) { return code_read_scale(VB, (m * VW0) & 15); }
 
   // Value contraction of a page pair: weights p (carried as p * 2^64) times the value scale of
   // each token go through the exchange buffer into the A operand, the masked codes are B.
@@ -503,9 +517,15 @@ struct Kern {
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int pos = (i & 1) * 8 * VB + m * VB;
-        const uint32_t word = (i < 2) ? A.vc.w[pos >> 4] : B.vc.w[pos >> 4];
-        w[i] = field_pair<VB>(word, word >> 8, pos & 15);
+        uint32_t v = 0;
+#pragma unroll
+        for (int p = 0; p < NPV; ++p) {
+          const int pw = kvq_plane_width(VB, p), po = kvq_plane_off(VB, p);
+          const int pos = (i & 1) * 8 * pw + m * pw;
+          const uint32_t word = (i < 2) ? A.vc.w[po + (pos >> 4)] : B.vc.w[po + (pos >> 4)];
+          v |= field_move(word, word >> 8, pw, pos & 15, vtile_scale(m) + po);
+        }
+        w[i] = v;
       }
       const u32x4 x = xa[m / (8 / NVG)];
       st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), pack8(w[0], w[1], w[2], w[3]),
@@ -570,41 +590,78 @@ struct Kern {
   }
 
   // Offsets of this lane's operands inside a record.
+  // Offsets of this lane's operands inside a record (codes: one per bit plane).
   struct RecOff {
-    uint32_t kc, km, vc, vm;
+    uint32_t kc[NPK], km, vc[NPV], vm;
   };
   template <int KS>
   static __device__ __forceinline__ RecOff rec_offsets(const Ctx &cx, const KvqLayout &lay) {
     RecOff o;
-    o.kc = lay.k_codes_off + cx.lane * 4 * KB;
+#pragma unroll
+    for (int p = 0; p < NPK; ++p)
+      o.kc[p] = lay.k_codes_off + 256 * kvq_plane_off(KB, p) + cx.lane * 4 * kvq_plane_width(KB, p);
     o.km = lay.k_meta_off + cx.col * 4 * (4 >> KS);
-    o.vc = lay.v_codes_off + cx.lane * 4 * VB;
+#pragma unroll
+    for (int p = 0; p < NPV; ++p)
+      o.vc[p] = lay.v_codes_off + 256 * kvq_plane_off(VB, p) + cx.lane * 4 * kvq_plane_width(VB, p);
     o.vm = lay.v_meta_off + cx.col * 4 * NVG;
     return o;
   }
 
+  // Plane widths as template arguments (1 for planes a code does not have).
+  static constexpr int kpw(int p) { return p < NPK ? kvq_plane_width(KB, p) : 1; }
+  static constexpr int vpw(int p) { return p < NPV ? kvq_plane_width(VB, p) : 1; }
+
   template <int KS>
   static __device__ __forceinline__ void read_page_at(PageData<KS> &pd, uint32_t base, const RecOff &o) {
     constexpr int NKM = 4 >> KS;
-    RawWords<KB> rk;
+    RawWords<kpw(0)> rk0;
+    RawWords<kpw(1)> rk1;
+    RawWords<kpw(2)> rk2;
     RawWords<NKM> rkm;
-    RawWords<VB> rv;
+    RawWords<vpw(0)> rv0;
+    RawWords<vpw(1)> rv1;
+    RawWords<vpw(2)> rv2;
     RawWords<NVG> rvm;
-    ds_read_words(rk, base + o.kc);
+    ds_read_words(rk0, base + o.kc[0]);
+    if constexpr (NPK > 1) ds_read_words(rk1, base + o.kc[NPK > 1 ? 1 : 0]);
+    if constexpr (NPK > 2) ds_read_words(rk2, base + o.kc[NPK > 2 ? 2 : 0]);
     ds_read_words(rkm, base + o.km);
-    ds_read_words(rv, base + o.vc);
+    ds_read_words(rv0, base + o.vc[0]);
+    if constexpr (NPV > 1) ds_read_words(rv1, base + o.vc[NPV > 1 ? 1 : 0]);
+    if constexpr (NPV > 2) ds_read_words(rv2, base + o.vc[NPV > 2 ? 2 : 0]);
     ds_read_words(rvm, base + o.vm);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    tie(rk);
+    tie(rk0);
+    if constexpr (NPK > 1) tie(rk1);
+    if constexpr (NPK > 2) tie(rk2);
     tie(rkm);
-    tie(rv);
+    tie(rv0);
+    if constexpr (NPV > 1) tie(rv1);
+    if constexpr (NPV > 2) tie(rv2);
     tie(rvm);
 #pragma unroll
-    for (int i = 0; i < KB; ++i) pd.kc.w[i] = rk.w(i);
+    for (int i = 0; i < kpw(0); ++i) pd.kc.w[i] = rk0.w(i);
+    if constexpr (NPK > 1) {
+#pragma unroll
+      for (int i = 0; i < kpw(1); ++i) pd.kc.w[kvq_plane_off(KB, 1) + i] = rk1.w(i);
+    }
+    if constexpr (NPK > 2) {
+#pragma unroll
+      for (int i = 0; i < kpw(2); ++i) pd.kc.w[kvq_plane_off(KB, 2) + i] = rk2.w(i);
+    }
 #pragma unroll
     for (int i = 0; i < NKM; ++i) pd.km[i] = rkm.w(i);
 #pragma unroll
-    for (int i = 0; i < VB; ++i) pd.vc.w[i] = rv.w(i);
+    for (int i = 0; i < vpw(0); ++i) pd.vc.w[i] = rv0.w(i);
+    if constexpr (NPV > 1) {
+#pragma unroll
+      for (int i = 0; i < vpw(1); ++i) pd.vc.w[kvq_plane_off(VB, 1) + i] = rv1.w(i);
+    }
+    if constexpr (NPV > 2) {
+#pragma unroll
+      for (int i = 0; i < vpw(2); ++i) pd.vc.w[kvq_plane_off(VB, 2) + i] = rv2.w(i);
+    }
 #pragma unroll
     for (int v = 0; v < NVG; ++v) pd.vm[v] = rvm.w(v);
   }

@@ -8,12 +8,14 @@
 #include "kvq_internal.h"
 
 namespace kvq_attn {
+// Every (key bits, value bits) pair of widths 1..6 and 8 (kvq_attn_inst.hip compiled once per pair).
+#define KVQ_FOR_VBITS(X, kb) X(kb, 1) X(kb, 2) X(kb, 3) X(kb, 4) X(kb, 5) X(kb, 6) X(kb, 8)
+#define KVQ_FOR_ALL_BITS(X)                                                                             \
+  KVQ_FOR_VBITS(X, 1) KVQ_FOR_VBITS(X, 2) KVQ_FOR_VBITS(X, 3) KVQ_FOR_VBITS(X, 4) KVQ_FOR_VBITS(X, 5) \
+  KVQ_FOR_VBITS(X, 6) KVQ_FOR_VBITS(X, 8)
 #define KVQ_DECLARE_LAUNCH(kb, vb) \
   hipError_t launch_k##kb##v##vb(const KvqAttnArgs &a, int g, int p, int nvg, hipStream_t s);
-KVQ_DECLARE_LAUNCH(1, 1) KVQ_DECLARE_LAUNCH(1, 2) KVQ_DECLARE_LAUNCH(1, 4) KVQ_DECLARE_LAUNCH(1, 8)
-KVQ_DECLARE_LAUNCH(2, 1) KVQ_DECLARE_LAUNCH(2, 2) KVQ_DECLARE_LAUNCH(2, 4) KVQ_DECLARE_LAUNCH(2, 8)
-KVQ_DECLARE_LAUNCH(4, 1) KVQ_DECLARE_LAUNCH(4, 2) KVQ_DECLARE_LAUNCH(4, 4) KVQ_DECLARE_LAUNCH(4, 8)
-KVQ_DECLARE_LAUNCH(8, 1) KVQ_DECLARE_LAUNCH(8, 2) KVQ_DECLARE_LAUNCH(8, 4) KVQ_DECLARE_LAUNCH(8, 8)
+KVQ_FOR_ALL_BITS(KVQ_DECLARE_LAUNCH)
 #undef KVQ_DECLARE_LAUNCH
 }  // namespace kvq_attn
 
@@ -136,22 +138,11 @@ hipError_t kvq_launch_attention(const KvqAttnArgs &a, int g, int q_parts, hipStr
   if (a.cache.batch <= 0) return hipSuccess;
   const int nvg = a.lay.nvg;
   switch (a.lay.kb * 16 + a.lay.vb) {
-    case 17: return kvq_attn::launch_k1v1(a, g, q_parts, nvg, s);
-    case 18: return kvq_attn::launch_k1v2(a, g, q_parts, nvg, s);
-    case 20: return kvq_attn::launch_k1v4(a, g, q_parts, nvg, s);
-    case 24: return kvq_attn::launch_k1v8(a, g, q_parts, nvg, s);
-    case 33: return kvq_attn::launch_k2v1(a, g, q_parts, nvg, s);
-    case 34: return kvq_attn::launch_k2v2(a, g, q_parts, nvg, s);
-    case 36: return kvq_attn::launch_k2v4(a, g, q_parts, nvg, s);
-    case 40: return kvq_attn::launch_k2v8(a, g, q_parts, nvg, s);
-    case 65: return kvq_attn::launch_k4v1(a, g, q_parts, nvg, s);
-    case 66: return kvq_attn::launch_k4v2(a, g, q_parts, nvg, s);
-    case 68: return kvq_attn::launch_k4v4(a, g, q_parts, nvg, s);
-    case 72: return kvq_attn::launch_k4v8(a, g, q_parts, nvg, s);
-    case 129: return kvq_attn::launch_k8v1(a, g, q_parts, nvg, s);
-    case 130: return kvq_attn::launch_k8v2(a, g, q_parts, nvg, s);
-    case 132: return kvq_attn::launch_k8v4(a, g, q_parts, nvg, s);
-    case 136: return kvq_attn::launch_k8v8(a, g, q_parts, nvg, s);
+#define KVQ_LAUNCH_CASE(kb, vb) \
+  case kb * 16 + vb:            \
+    return kvq_attn::launch_k##kb##v##vb(a, g, q_parts, nvg, s);
+    KVQ_FOR_ALL_BITS(KVQ_LAUNCH_CASE)
+#undef KVQ_LAUNCH_CASE
   }
   return hipErrorInvalidValue;
 }

@@ -29,11 +29,8 @@ __global__ __launch_bounds__(64) void kvq_debug_kernel(KvqDebugArgs a) {
       const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, a.seq, h, t / KVQ_PAGE);
       const uint8_t *rec = a.cache.pages + (size_t)rec_idx * lay.record;
       const int n = (int)(t % KVQ_PAGE);
-      int off, bit;
-      kvq_k_code_pos(lay.kb, n, c, &off, &bit);
-      kc = (*reinterpret_cast<const uint32_t *>(rec + lay.k_codes_off + off) >> bit) & ((1u << lay.kb) - 1u);
-      kvq_v_code_pos(lay.vb, n, c, &off, &bit);
-      vc = (*reinterpret_cast<const uint32_t *>(rec + lay.v_codes_off + off) >> bit) & ((1u << lay.vb) - 1u);
+      kc = kvq_k_code(rec + lay.k_codes_off, lay.kb, n, c);
+      vc = kvq_v_code(rec + lay.v_codes_off, lay.vb, n, c);
       const uint32_t km = reinterpret_cast<const uint32_t *>(rec + lay.k_meta_off)[kvq_meta_dword(lay.nkg, n, c / lay.kg)];
       const uint32_t vm = reinterpret_cast<const uint32_t *>(rec + lay.v_meta_off)[kvq_meta_dword(lay.nvg, n, c / lay.vg)];
       kh = (float)(kvq_f16_bits_to_f64(km >> 16) + (double)kc * kvq_f16_bits_to_f64(km & 0xFFFF));

@@ -110,13 +110,9 @@ __device__ __attribute__((always_inline)) inline void load8(const KvqErrArgs &a,
   const float zero = f16f(m >> 16), scale = f16f(m & 0xFFFF);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    int off, bit;
-    if (KEYS)
-      kvq_k_code_pos(bits, p.n, 8 * c + e, &off, &bit);
-    else
-      kvq_v_code_pos(bits, p.n, 8 * c + e, &off, &bit);
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(p.rec + (KEYS ? lay.k_codes_off : lay.v_codes_off) + off);
-    xh[e] = zero + (float)((w >> bit) & ((1u << bits) - 1u)) * scale;
+    const uint32_t code = KEYS ? kvq_k_code(p.rec + lay.k_codes_off, bits, p.n, 8 * c + e)
+                               : kvq_v_code(p.rec + lay.v_codes_off, bits, p.n, 8 * c + e);
+    xh[e] = zero + (float)code * scale;
   }
 }
 

@@ -9,24 +9,31 @@
 //   B operand:                              lane l holds col l%16, k = 8*(l/16) + e
 //   D (4 x fp32):                          lane l holds col l%16, rows 4*(l/16) + r (r = 0..3)
 //
+// Codes of b bits are stored as bit planes: b = 8, 4, 2, 1 is one plane; any other b in 1..7
+// is split into the binary digits of b from the highest (3 = 2 + 1, 5 = 4 + 1, 6 = 4 + 2,
+// 7 = 4 + 2 + 1).  Plane p of width w holds bits [off, off + w) of every code (off = the
+// widths of the planes before it) and is an area of its own, 256 * w bytes, in the layout of a
+// w-bit code; the areas follow each other in plane order (plane p at byte 256 * off of the code
+// area).  So a b-bit code area is 256 * b bytes for every b, and within each plane:
 // K codes: lane-slot l = 16*j + n (token n of the page, channel octet j).  The
-//   slot has kb 32-bit words holding, for the four 32-channel chunks kc, the
+//   slot has w 32-bit words holding, for the four 32-channel chunks kc, the
 //   channels 32*kc + 8*j + e.  Channel e = 2*i + h of chunk kc has index
-//   u = 4*kc + i; it sits in word u / (16/kb) at bit 16*h + kb*(u % (16/kb)).
-//   So (word >> kb*s) & mask(kb, both halves) is one bf16 pair of codes.
+//   u = 4*kc + i; it sits in word u / (16/w) at bit 16*h + w*(u % (16/w)).
+//   So (word >> w*s) & mask(w, both halves) is one bf16 pair of plane values.
 // K meta: entry (token n, group g) at dword n*nkg + g (a token's groups are
 //   contiguous, so one lane reads all of them with one load):
 //   low half = fp16 scale, high half = fp16 zero.
 // V codes: lane-slot l = 16*jj + c16 (channels c16 + 16*m, m = 0..7; tokens
-//   4*jj + r, r = 0..3).  The slot has vb words.  Token r = 2*i + h, tile m:
-//   position p = i*8*vb + m*vb in the half-word stream h, i.e. word p / 16,
+//   4*jj + r, r = 0..3).  The slot has w words.  Token r = 2*i + h, tile m:
+//   position p = i*8*w + m*w in the half-word stream h, i.e. word p / 16,
 //   bit 16*h + p % 16.  A token's bits in one slot never share a byte with
 //   another token's, so tokens of a page can be written concurrently.
 // V meta: entry (token n, group g) at dword n*nvg + g.
 //
 // A code c read as a bf16 bit pattern is the value c * 2^-133 for every c in
 // 0..255 (subnormal below 128, continuing into the first normal binade), so
-// masking the packed word gives exact, offset-free MFMA operands.
+// masking the packed word (and, for several planes, OR-ing the planes' values
+// into place) gives exact, offset-free MFMA operands.
 #pragma once
 #include <stdint.h>
 
@@ -59,23 +66,71 @@ __host__ __device__ inline KvqLayout kvq_make_layout(int kb, int kg, int vb, int
   return L;
 }
 
-// Byte offset (within the record) and bit of the K code of (token n, channel ch).
-__host__ __device__ inline void kvq_k_code_pos(int kb, int n, int ch, int *byte_off, int *bit) {
-  const int kc = ch >> 5, w = ch & 31, j = w >> 3, e = w & 7;
-  const int i = e >> 1, h = e & 1;
-  const int u = 4 * kc + i, per = 16 / kb;
-  const int word = u / per, s = u % per;
-  *byte_off = (16 * j + n) * 4 * kb + 4 * word;
-  *bit = 16 * h + kb * s;
+// Bit planes of a b-bit code (see above): their number, the width of plane p and its offset
+// (bit offset inside the code = word offset of its lane-slot words = its area's offset / 256).
+__host__ __device__ constexpr int kvq_nplanes(int b) {
+  return b == 8 ? 1 : ((b >> 2) & 1) + ((b >> 1) & 1) + (b & 1);
+}
+__host__ __device__ constexpr int kvq_plane_width(int b, int p) {
+  if (b == 8) return 8;
+  for (int w = 4; w >= 1; w >>= 1) {
+    if (b & w) {
+      if (p == 0) return w;
+      --p;
+    }
+  }
+  return 0;
+}
+__host__ __device__ constexpr int kvq_plane_off(int b, int p) {
+  int o = 0;
+  for (int q = 0; q < p; ++q) o += kvq_plane_width(b, q);
+  return o;
 }
 
-// Byte offset (within the V-code area) and bit of the V code of (token tt, channel ch).
-__host__ __device__ inline void kvq_v_code_pos(int vb, int tt, int ch, int *byte_off, int *bit) {
+// Byte offset (within a w-bit plane area) and bit of the K plane value of (token n, channel ch).
+__host__ __device__ inline void kvq_k_code_pos(int w, int n, int ch, int *byte_off, int *bit) {
+  const int kc = ch >> 5, x = ch & 31, j = x >> 3, e = x & 7;
+  const int i = e >> 1, h = e & 1;
+  const int u = 4 * kc + i, per = 16 / w;
+  const int word = u / per, s = u % per;
+  *byte_off = (16 * j + n) * 4 * w + 4 * word;
+  *bit = 16 * h + w * s;
+}
+
+// Byte offset (within a w-bit plane area of the V codes) and bit of the V plane value of
+// (token tt, channel ch).
+__host__ __device__ inline void kvq_v_code_pos(int w, int tt, int ch, int *byte_off, int *bit) {
   const int jj = tt >> 2, r = tt & 3, i = r >> 1, h = r & 1;
   const int m = ch >> 4, c16 = ch & 15;
-  const int p = i * 8 * vb + m * vb;
-  *byte_off = (16 * jj + c16) * 4 * vb + 4 * (p >> 4);
+  const int p = i * 8 * w + m * w;
+  *byte_off = (16 * jj + c16) * 4 * w + 4 * (p >> 4);
   *bit = 16 * h + (p & 15);
+}
+
+// The b-bit K code of (token n, channel ch) from a record's K code area (all planes).
+__host__ __device__ inline uint32_t kvq_k_code(const uint8_t *kcodes, int b, int n, int ch) {
+  uint32_t c = 0;
+  for (int p = 0; p < kvq_nplanes(b); ++p) {
+    const int w = kvq_plane_width(b, p);
+    int off, bit;
+    kvq_k_code_pos(w, n, ch, &off, &bit);
+    const uint32_t word = *reinterpret_cast<const uint32_t *>(kcodes + 256 * kvq_plane_off(b, p) + off);
+    c |= ((word >> bit) & ((1u << w) - 1u)) << kvq_plane_off(b, p);
+  }
+  return c;
+}
+
+// The b-bit V code of (token tt, channel ch) from a record's V code area (all planes).
+__host__ __device__ inline uint32_t kvq_v_code(const uint8_t *vcodes, int b, int tt, int ch) {
+  uint32_t c = 0;
+  for (int p = 0; p < kvq_nplanes(b); ++p) {
+    const int w = kvq_plane_width(b, p);
+    int off, bit;
+    kvq_v_code_pos(w, tt, ch, &off, &bit);
+    const uint32_t word = *reinterpret_cast<const uint32_t *>(vcodes + 256 * kvq_plane_off(b, p) + off);
+    c |= ((word >> bit) & ((1u << w) - 1u)) << kvq_plane_off(b, p);
+  }
+  return c;
 }
 
 __host__ __device__ inline int kvq_meta_dword(int ngroups, int tt, int grp) { return tt * ngroups + grp; }

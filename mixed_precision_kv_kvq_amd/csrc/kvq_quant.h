@@ -89,45 +89,52 @@ __device__ inline void quantize_pair(double x0, double x1, int bits, int G, uint
 
 // Codes and metadata of one token (codes ck[128], cv[128] and metadata words mk[128 / k_group],
 // mv[128 / v_group], all in LDS) into token slot n of page record `rec` (global memory or LDS),
-// by the 64 lanes of one wave.  K codes: the token owns kb whole words in each of its four
-// octet slots; V codes: it owns half-words (one byte at 1 bit) of its value slots; metadata: one
-// dword per group.  Bytes of other tokens of the page are not touched.
+// by the 64 lanes of one wave, one bit plane after the other.  K codes: in each plane of width w
+// the token owns w whole words in each of its four octet slots; V codes: it owns half-words (one
+// byte at width 1) of its value slots; metadata: one dword per group.  Bytes of other tokens of
+// the page are not touched.
 __device__ inline void kvq_write_token(uint8_t *rec, const KvqLayout &lay, int n, const uint8_t *ck,
                                        const uint8_t *cv, const uint32_t *mk, const uint32_t *mv, int lane) {
-  // K codes: 4 slots (octets j) x kb words.
-  const int kb = lay.kb, per_k = 16 / kb;
-  if (lane < 4 * kb) {
-    const int j = lane / kb, wi = lane % kb;
-    uint32_t word = 0;
-    for (int s = 0; s < per_k; ++s) {
-      const int u = wi * per_k + s, kc = u >> 2, i = u & 3;
-      const int ch = 32 * kc + 8 * j + 2 * i;
-      word |= (uint32_t)ck[ch] << (kb * s);
-      word |= (uint32_t)ck[ch + 1] << (16 + kb * s);
-    }
-    *reinterpret_cast<uint32_t *>(rec + lay.k_codes_off + (16 * j + n) * 4 * kb + 4 * wi) = word;
-  }
-  // V codes: 16 slots; each token owns half-words (or one byte when vb == 1) of its slot.
-  const int vb = lay.vb;
-  const int jj = n >> 2, r = n & 3, ii = r >> 1, hh = r & 1;
-  uint8_t *vbase = rec + lay.v_codes_off;
-  if (vb == 1) {
-    if (lane < 16) {
-      uint32_t byte = 0;
-      for (int m = 0; m < 8; ++m) byte |= (uint32_t)cv[16 * m + lane] << m;
-      vbase[(16 * jj + lane) * 4 + 2 * hh + ii] = (uint8_t)byte;
-    }
-  } else {
-    const int nhw = vb / 2, per_v = 16 / vb;
-    if (lane < 16 * nhw) {
-      const int c16 = lane & 15, hw = lane >> 4;
-      uint32_t half = 0;
-      for (int q = 0; q < per_v; ++q) {
-        const int m = hw * per_v + q;
-        half |= (uint32_t)cv[16 * m + c16] << ((m * vb) & 15);
+  // K codes: per plane, 4 slots (octets j) x w words.
+  for (int pl = 0; pl < kvq_nplanes(lay.kb); ++pl) {
+    const int w = kvq_plane_width(lay.kb, pl), sh = kvq_plane_off(lay.kb, pl), per = 16 / w;
+    const uint32_t mask = (1u << w) - 1u;
+    if (lane < 4 * w) {
+      const int j = lane / w, wi = lane % w;
+      uint32_t word = 0;
+      for (int s = 0; s < per; ++s) {
+        const int u = wi * per + s, kc = u >> 2, i = u & 3;
+        const int ch = 32 * kc + 8 * j + 2 * i;
+        word |= (((uint32_t)ck[ch] >> sh) & mask) << (w * s);
+        word |= (((uint32_t)ck[ch + 1] >> sh) & mask) << (16 + w * s);
       }
-      const int wi = ii * (vb / 2) + hw;
-      *reinterpret_cast<uint16_t *>(vbase + (16 * jj + c16) * 4 * vb + 4 * wi + 2 * hh) = (uint16_t)half;
+      *reinterpret_cast<uint32_t *>(rec + lay.k_codes_off + 256 * sh + (16 * j + n) * 4 * w + 4 * wi) = word;
+    }
+  }
+  // V codes: per plane, 16 slots; each token owns half-words (or one byte at width 1) of its slot.
+  const int jj = n >> 2, r = n & 3, ii = r >> 1, hh = r & 1;
+  for (int pl = 0; pl < kvq_nplanes(lay.vb); ++pl) {
+    const int w = kvq_plane_width(lay.vb, pl), sh = kvq_plane_off(lay.vb, pl);
+    const uint32_t mask = (1u << w) - 1u;
+    uint8_t *vbase = rec + lay.v_codes_off + 256 * sh;
+    if (w == 1) {
+      if (lane < 16) {
+        uint32_t byte = 0;
+        for (int m = 0; m < 8; ++m) byte |= (((uint32_t)cv[16 * m + lane] >> sh) & 1u) << m;
+        vbase[(16 * jj + lane) * 4 + 2 * hh + ii] = (uint8_t)byte;
+      }
+    } else {
+      const int nhw = w / 2, per = 16 / w;
+      if (lane < 16 * nhw) {
+        const int c16 = lane & 15, hw = lane >> 4;
+        uint32_t half = 0;
+        for (int q = 0; q < per; ++q) {
+          const int m = hw * per + q;
+          half |= (((uint32_t)cv[16 * m + c16] >> sh) & mask) << ((m * w) & 15);
+        }
+        const int wi = ii * (w / 2) + hw;
+        *reinterpret_cast<uint16_t *>(vbase + (16 * jj + c16) * 4 * w + 4 * wi + 2 * hh) = (uint16_t)half;
+      }
     }
   }
   // Metadata.

@@ -76,7 +76,6 @@ __global__ __launch_bounds__(64) void kvq_dequantize_dense_kernel(KvqDenseArgs a
   const uint8_t *rs = reinterpret_cast<const uint8_t *>(rec_s);
   const size_t row0 = ((size_t)b * Hkv + h) * (size_t)a.max_len;
   const int esz = a.kv_f32 ? 4 : 2;
-  const uint32_t kmask = (1u << lay.kb) - 1u, vmask = (1u << lay.vb) - 1u;
   if (!a.rotation && !a.value_rotation) {
     // Lane 16 r + c8 writes channels [8 c8, 8 c8 + 8) of position 4 it + r: one 16-byte store
     // per tensor, four whole 256-byte rows per store instruction.
@@ -98,11 +97,8 @@ __global__ __launch_bounds__(64) void kvq_dequantize_dense_kernel(KvqDenseArgs a
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int ch = 8 * c8 + 2 * i + e;
-            int off, bit;
-            kvq_k_code_pos(lay.kb, n, ch, &off, &bit);
-            kc[e] = (*reinterpret_cast<const uint32_t *>(rs + lay.k_codes_off + off) >> bit) & kmask;
-            kvq_v_code_pos(lay.vb, n, ch, &off, &bit);
-            vc[e] = (*reinterpret_cast<const uint32_t *>(rs + lay.v_codes_off + off) >> bit) & vmask;
+            kc[e] = kvq_k_code(rs + lay.k_codes_off, lay.kb, n, ch);
+            vc[e] = kvq_v_code(rs + lay.v_codes_off, lay.vb, n, ch);
           }
           ko[i] = affine_bf16(kz, ks, kc[0]) | (affine_bf16(kz, ks, kc[1]) << 16);
           vo[i] = affine_bf16(vz, vs, vc[0]) | (affine_bf16(vz, vs, vc[1]) << 16);
@@ -144,15 +140,11 @@ __global__ __launch_bounds__(64) void kvq_dequantize_dense_kernel(KvqDenseArgs a
     if (t >= L) break;
     uint32_t kout, vout;
     if (t < nq) {
-      // channels 2 lane and 2 lane + 1 share a key word (bit 16 apart) and both groups
-      int off, bit;
-      kvq_k_code_pos(lay.kb, n, 2 * lane, &off, &bit);
-      const uint32_t kw = *reinterpret_cast<const uint32_t *>(rs + lay.k_codes_off + off);
-      const uint32_t kc0 = (kw >> bit) & kmask, kc1 = (kw >> (bit + 16)) & kmask;
-      kvq_v_code_pos(lay.vb, n, 2 * lane, &off, &bit);
-      const uint32_t vc0 = (*reinterpret_cast<const uint32_t *>(rs + lay.v_codes_off + off) >> bit) & vmask;
-      kvq_v_code_pos(lay.vb, n, 2 * lane + 1, &off, &bit);
-      const uint32_t vc1 = (*reinterpret_cast<const uint32_t *>(rs + lay.v_codes_off + off) >> bit) & vmask;
+      // channels 2 lane and 2 lane + 1 (both in one group)
+      const uint32_t kc0 = kvq_k_code(rs + lay.k_codes_off, lay.kb, n, 2 * lane);
+      const uint32_t kc1 = kvq_k_code(rs + lay.k_codes_off, lay.kb, n, 2 * lane + 1);
+      const uint32_t vc0 = kvq_v_code(rs + lay.v_codes_off, lay.vb, n, 2 * lane);
+      const uint32_t vc1 = kvq_v_code(rs + lay.v_codes_off, lay.vb, n, 2 * lane + 1);
       const uint32_t km = reinterpret_cast<const uint32_t *>(rs + lay.k_meta_off)[kvq_meta_dword(lay.nkg, n, (2 * lane) / lay.kg)];
       const uint32_t vm = reinterpret_cast<const uint32_t *>(rs + lay.v_meta_off)[kvq_meta_dword(lay.nvg, n, (2 * lane) / lay.vg)];
       if (a.rotation) {

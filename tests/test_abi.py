@@ -43,7 +43,8 @@ def p(**kw):
     return K.make_params(**base)
 
 
-@pytest.mark.parametrize("kb,vb,expect", [(4, 2, 116), (4, 4, 148), (2, 4, 116), (2, 2, 84), (1, 2, 68)])
+@pytest.mark.parametrize("kb,vb,expect", [(4, 2, 116), (4, 4, 148), (2, 4, 116), (2, 2, 84), (1, 2, 68), (3, 2, 100),
+                                          (5, 3, 148), (6, 2, 148), (8, 8, 276)])
 def test_record_size_matches_memory_model(kb, vb, expect):
     s = K.kvq_cache_sizes(p(k_bits=kb, v_bits=vb), 2, 100)
     assert s.record_bytes == 16 * expect == 16 * O.bytes_per_token_head(128, kb, 32, vb, 128)
@@ -60,8 +61,10 @@ def test_window_and_paged_sizes():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), K.KVQ_EUNSUPPORTED),
-    (dict(k_bits=3), K.KVQ_EUNSUPPORTED),
+    (dict(k_bits=9), K.KVQ_EUNSUPPORTED),
+    (dict(v_bits=7), K.KVQ_EUNSUPPORTED),
     (dict(v_bits=0), K.KVQ_EUNSUPPORTED),
+    (dict(k_bits=0), K.KVQ_EUNSUPPORTED),
     (dict(k_group=16), K.KVQ_EUNSUPPORTED),
     (dict(v_group=32), K.KVQ_EUNSUPPORTED),
     (dict(num_q_heads=48, num_kv_heads=8), K.KVQ_EUNSUPPORTED),
@@ -99,7 +102,7 @@ def test_append_validation():
                                  None) == K.KVQ_EINVAL
     assert L.kvq_quantize_append(ctypes.byref(p(block_size=16)), ctypes.byref(cache()), FAKE, None, FAKE, FAKE, 1,
                                  None) == K.KVQ_EINVAL
-    assert L.kvq_quantize_append(ctypes.byref(p(k_bits=5)), ctypes.byref(cache()), FAKE, None, FAKE, FAKE, 1,
+    assert L.kvq_quantize_append(ctypes.byref(p(k_bits=9)), ctypes.byref(cache()), FAKE, None, FAKE, FAKE, 1,
                                  None) == K.KVQ_EUNSUPPORTED
     # zero tokens: nothing to do, no launch
     assert L.kvq_quantize_append(ctypes.byref(prm), ctypes.byref(cache()), FAKE, None, None, None, 0, None) == K.KVQ_OK
@@ -128,7 +131,8 @@ def test_attention_validation():
     # paged: more pages than the table row holds
     assert call(c=cache(block_table=FAKE, max_blocks_per_seq=3), prm_=p(block_size=16), mx=49,
                 wsb=K.kvq_decode_workspace_bytes(p(block_size=16), 2, 49)) == K.KVQ_ENOSPACE
-    assert K.kvq_decode_workspace_bytes(p(k_bits=3), 2, 64) == 0
+    assert K.kvq_decode_workspace_bytes(p(k_bits=9), 2, 64) == 0
+    assert K.kvq_decode_workspace_bytes(p(k_bits=3), 2, 64) > 0
     # value rotation: a flag, and not with a recent window (the window's values are not rotated)
     assert call(prm_=p(value_rotation=2)) == K.KVQ_EINVAL
     assert K.kvq_decode_workspace_bytes(p(value_rotation=1), 2, 64) > 0
@@ -150,7 +154,7 @@ def test_phase_entry_points_validation():
     assert part(q=None) == K.KVQ_EINVAL
     assert part(ws=FAKE + 4) == K.KVQ_EINVAL
     assert part(qd=7) == K.KVQ_EINVAL
-    assert part(prm_=p(v_bits=3)) == K.KVQ_EUNSUPPORTED
+    assert part(prm_=p(v_bits=9)) == K.KVQ_EUNSUPPORTED
 
     def comb(batch=2, ws=FAKE, out=FAKE, qd=K.KVQ_BF16, od=K.KVQ_F32, prm_=prm):
         return L.kvq_decode_combine(ctypes.byref(prm_), batch, 64, qd, ws, out, od, None)
@@ -186,12 +190,12 @@ def test_unfused_baseline_validation():
     assert deq(mx=-1) == K.KVQ_EINVAL
     assert deq(mx=1 << 31) == K.KVQ_EINVAL
     assert deq(c=cache(pages=FAKE + 8)) == K.KVQ_EINVAL
-    assert deq(prm_=p(k_bits=3)) == K.KVQ_EUNSUPPORTED
+    assert deq(prm_=p(k_bits=12)) == K.KVQ_EUNSUPPORTED
 
     need = K.kvq_dense_workspace_bytes(prm, 2, 600)
     assert need == 2 * 32 * 3 * K.KVQ_PART_FLOATS * 4  # three splits of 256 positions
     assert K.kvq_dense_workspace_bytes(prm, 2, 0) == 2 * 32 * 1 * K.KVQ_PART_FLOATS * 4
-    assert K.kvq_dense_workspace_bytes(p(k_bits=3), 2, 600) == 0
+    assert K.kvq_dense_workspace_bytes(p(k_bits=9), 2, 600) == 0
 
     def att(b=2, k=FAKE, v=FAKE, seq=FAKE, mx=600, q=FAKE, qd=K.KVQ_BF16, out=FAKE, od=K.KVQ_F32, sc=0.0, ws=FAKE,
             wsb=need):
@@ -291,7 +295,7 @@ def test_noalloc_validation():
     st = L.kvq_decode_attention_noalloc(ctypes.byref(prm), ctypes.byref(cs), FAKE, 131072, FAKE, K.KVQ_BF16, FAKE,
                                         K.KVQ_F32, 0.0, None)
     assert st == K.KVQ_ENOSPACE
-    assert L.kvq_decode_attention_noalloc(ctypes.byref(p(k_bits=3)), ctypes.byref(cs), FAKE, 16, FAKE, K.KVQ_BF16,
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(p(k_bits=9)), ctypes.byref(cs), FAKE, 16, FAKE, K.KVQ_BF16,
                                           FAKE, K.KVQ_F32, 0.0, None) == K.KVQ_EUNSUPPORTED
     assert L.kvq_decode_attention_noalloc(ctypes.byref(prm), None, FAKE, 16, FAKE, K.KVQ_BF16, FAKE, K.KVQ_F32, 0.0,
                                           None) == K.KVQ_EINVAL

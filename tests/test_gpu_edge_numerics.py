@@ -117,6 +117,8 @@ CASES = {
     "k4v2-value-rotation": (base(value_rotation=True, window=0, steps=2), True),
     "f32-k4v2-window": (base(kv_dtype="f32", q_dtype="f32"), False),
     "paged-k4v4": (base(k_bits=4, v_bits=4, block_size=16, window=4), False),
+    "k3v5-window": (base(k_bits=3, v_bits=5), False),
+    "f32-k6v5-no-window": (base(kv_dtype="f32", q_dtype="f32", k_bits=6, v_bits=5, window=0), False),
 }
 
 

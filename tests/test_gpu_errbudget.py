@@ -38,6 +38,9 @@ CASES = {
     "g2-window": dict(context=220, num_q_heads=16, num_kv_heads=8, window=24),
     "paged-window": dict(context=0, var_len=(1, 300), block_size=16, window=16, batch=4),
     "ragged-lengths-with-empty": dict(context=0, var_len=(0, 600), batch=4),
+    "k3v2": dict(context=300, k_bits=3, v_bits=2),
+    "k5v3-window": dict(context=280, window=24, k_bits=5, v_bits=3),
+    "k6v5-rotated-both": dict(context=200, k_bits=6, v_bits=5, rotation=True, value_rotation=True),
 }
 
 

@@ -89,7 +89,7 @@ def test_full_config3_all_steps():
     check_units(run, [(0, 0), (3, 2), (6, 6), (9, 5), (12, 1), (15, 7)], wl.steps - 1, o32, obf)
 
 
-@pytest.mark.parametrize("kb,vb", W.SWEEP_BITS)
+@pytest.mark.parametrize("kb,vb", W.SWEEP_BITS + W.PLANE_BITS)
 def test_full_config4_paged_sweep(kb, vb):
     """Batch 8, lengths uniform in [1024, 16384], paged 16-token blocks through a seeded block table."""
     wl = W.WORKLOADS[4].with_bits(kb, vb)

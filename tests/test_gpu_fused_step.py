@@ -67,6 +67,13 @@ CASES = {
     "k1v1-window16": small(B3, batch=2, context=300, steps=4, k_bits=1, v_bits=1, window=16),
     "window-200": small(B3, batch=2, context=900, steps=3, window=200),  # two window splits
     "paged-window": small(B3, batch=3, context=0, var_len=(200, 700), steps=3, block_size=16, window=32),
+    # codes of 3, 5 and 6 bits (bit planes) quantized inside the split kernel
+    "k3v2-window32": small(B3, batch=2, context=400, steps=4, k_bits=3, v_bits=2, window=32),
+    "k5v3-rotation": small(B3, batch=2, context=500, steps=3, k_bits=5, v_bits=3, rotation=True),
+    "k6v2-g8-vgroup64": small(B3, batch=2, num_q_heads=16, num_kv_heads=2, context=300, steps=3, k_bits=6, v_bits=2,
+                              v_group=64),
+    "k5v6-paged-window": small(B3, batch=3, context=0, var_len=(100, 500), steps=3, block_size=16, window=16,
+                               k_bits=5, v_bits=6),
     # append kernel first, then attention (no fusion): no window, and fp32 rings
     "no-window": small(B3, batch=2, context=500, steps=3, window=0),
     "f32-window": small(B3, batch=2, context=500, steps=3, kv_dtype="f32", q_dtype="f32"),

@@ -181,6 +181,49 @@ def test_ragged_split_plan(name):
         full_check(run, s, out_check_bf16=(s == 0))
 
 
+# Codes of 3, 5 and 6 bits, stored as bit planes (4, 2 and 1 bits) and recombined into one MFMA
+# operand per pair slot: both append kernels (whole pages and single tokens), every attention
+# feature, and decode steps through the append kernel.
+NPOW2 = {
+    "k3v2": dict(context=300, k_bits=3, v_bits=2),
+    "k5v3-window": dict(context=260, k_bits=5, v_bits=3, window=32),
+    "k6v2-steps": dict(batch=2, context=600, k_bits=6, v_bits=2, window=0, steps=3),
+    "k6v5-g8-vgroup64": dict(context=200, num_q_heads=16, num_kv_heads=2, k_bits=6, v_bits=5, v_group=64),
+    "k3v5-kgroup64": dict(context=180, k_bits=3, v_bits=5, k_group=64),
+    "k5v6-f32-window": dict(context=160, k_bits=5, v_bits=6, kv_dtype="f32", q_dtype="f32", window=20),
+    "k6v3-rotation-window": dict(context=200, k_bits=6, v_bits=3, rotation=True, window=16),
+    "k3v3-keys-and-values-rotated": dict(context=250, k_bits=3, v_bits=3, rotation=True, value_rotation=True),
+    "k5v1-paged": dict(context=0, var_len=(1, 400), block_size=16, batch=4, k_bits=5, v_bits=1),
+    "k1v6-g1": dict(context=150, num_q_heads=8, num_kv_heads=8, k_bits=1, v_bits=6),
+    "k6v6-g2-kgroup128": dict(context=140, num_q_heads=16, num_kv_heads=8, k_bits=6, v_bits=6, k_group=128),
+    "k5v5-ragged": dict(batch=4, context=0, var_len=(16, 3000), k_bits=5, v_bits=5),
+}
+
+
+@pytest.mark.parametrize("name", list(NPOW2))
+def test_non_power_of_two_bits(name):
+    wl = small(BASE, config=600 + list(NPOW2).index(name), **NPOW2[name])
+    say(f"bit planes {name}: {NPOW2[name]}")
+    run = GpuRun(wl, chunk=64)
+    for s in range(max(wl.steps, 1)):
+        full_check(run, s, out_check_bf16=(s == 0))
+
+
+WIDTHS = (1, 2, 3, 4, 5, 6, 8)
+
+
+@pytest.mark.parametrize("kb", WIDTHS)
+def test_every_bit_pair(kb):
+    """Every (key bits, value bits) instantiation of the split kernel, small: 2 sequences of 70
+    tokens (whole pages and a partial one), 4 query heads per kv head."""
+    for vb in WIDTHS:
+        wl = small(BASE, config=700 + 8 * kb + vb, batch=2, num_q_heads=8, num_kv_heads=2, context=70, k_bits=kb,
+                   v_bits=vb)
+        say(f"bit pair K{kb}V{vb}")
+        run = GpuRun(wl, chunk=64)
+        full_check(run, 0, out_check_bf16=False)
+
+
 # Values rotated before quantization and the output rotated back in the merge: whole pages go
 # through the page kernel, the rest through the per-token kernel.
 VROT = {

@@ -38,6 +38,9 @@ CASES = {
     "f32-kv-window": dict(context=160, window=20, kv_dtype="f32", q_dtype="f32"),
     "paged-window": dict(context=0, var_len=(1, 300), block_size=16, window=16, batch=4),
     "ragged-lengths-with-empty": dict(context=0, var_len=(0, 1100), batch=5),
+    "k3v5-window": dict(context=300, window=24, k_bits=3, v_bits=5),
+    "k6v3-rotated-both": dict(context=200, k_bits=6, v_bits=3, rotation=True, value_rotation=True),
+    "k5v6-g8-vgroup64": dict(context=170, num_q_heads=16, num_kv_heads=2, v_group=64, k_bits=5, v_bits=6),
 }
 
 

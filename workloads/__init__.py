@@ -239,3 +239,6 @@ WORKLOADS = {
 
 # Bit-width sweep of the paged workload (key bits, value bits).
 SWEEP_BITS = [(4, 4), (4, 2), (2, 4), (2, 2), (1, 2)]
+# Widths between the powers of two on the same paged workload: K3V3 at the payload of K4V2 and
+# K2V4 (6 bits per key-value pair), and K3V2, K5V3, K6V2.
+PLANE_BITS = [(3, 3), (3, 2), (5, 3), (6, 2)]
