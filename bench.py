@@ -460,8 +460,8 @@ def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
 
 def rotated_131k(torch, dev, reps, stream, ceiling_GBs, plan):
     """The batch-64 x 131072-token workload with rotated keys (64 query / 8 kv heads): bulk prefill of
-    the whole context (appends of 4096 tokens per sequence, inputs generated into HBM first, one
-    chunk at a time), then the decode attention's split kernel timed back to back on two copies of
+    the whole context (appends of 4096 tokens per sequence back to back, all inputs generated into
+    HBM first), then the decode attention's split kernel timed back to back on two copies of
     the 7.8 GB cache (cold: every launch reads data far beyond the Infinity Cache) and the merge."""
     import mixed_precision_kv_kvq_amd as K
     import workloads as W
@@ -473,23 +473,24 @@ def rotated_131k(torch, dev, reps, stream, ceiling_GBs, plan):
     cb = K.CacheBuffers(prm, B, L)
     gen = DeviceGenerator(wl)
     chunk = 4096
-    kbuf = torch.empty((B, chunk, Hkv, d), dtype=torch.int16, device=dev)
-    vbuf = torch.empty_like(kbuf)
-    app_us = 0.0
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    # every chunk's rows generated into HBM first (34.4 GB of bf16 keys and values), then the
+    # appends back to back between two events, arguments marshalled beforehand
+    pre = []
     for t0 in range(0, L, chunk):
-        gen.kv(W.TENSOR_K, t0, chunk, out=kbuf)
-        gen.kv(W.TENSOR_V, t0, chunk, out=vbuf)
-        before = torch.full((B,), t0, dtype=torch.int32, device=dev)
-        torch.cuda.synchronize()
-        e[0].record(stream)
-        K.kvq_quantize_append(prm, cb.struct, before, None, kbuf, vbuf, chunk)
-        e[1].record(stream)
-        torch.cuda.synchronize()
-        app_us += e[0].elapsed_time(e[1]) * 1e3
-        if (t0 // chunk) % 8 == 7:
-            progress(f"rotated 131k prefill: {t0 + chunk} tokens")
-    del kbuf, vbuf
+        pre.append((gen.kv(W.TENSOR_K, t0, chunk), gen.kv(W.TENSOR_V, t0, chunk),
+                    torch.full((B,), t0, dtype=torch.int32, device=dev)))
+    calls = [K.bound_call("kvq_quantize_append", prm, cb.struct, before, None, k, v, chunk, stream=stream)
+             for k, v, before in pre]
+    progress(f"rotated 131k: {len(pre)} chunks of inputs generated")
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    e[0].record(stream)
+    for f in calls:
+        f()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    app_us = e[0].elapsed_time(e[1]) * 1e3
+    del pre, calls
     per_th = d * wl.k_bits // 8 + (d // wl.k_group) * 4 + d * wl.v_bits // 8 + (d // wl.v_group) * 4
     prefill_bytes = B * Hkv * L * (2 * d * 2 + per_th)  # every row read once, its codes written once
     q = gen.q(0)
@@ -517,8 +518,9 @@ def rotated_131k(torch, dev, reps, stream, ceiling_GBs, plan):
             "split_kernel": rf, "combine_us": round(comb, 2), "attention_us_cold": round(cold + comb, 2),
             "effective_tokens_per_s": round(B * L / ((cold + comb) * 1e-6), 1),
             "prefill_quantize": {"what": f"{L // chunk} appends of {chunk} tokens per sequence (key rotation, fp64 "
-                                         f"quantizer), each between two events, inputs generated into HBM before "
-                                         f"each", "us": round(app_us, 1), "algorithmic_bytes": int(prefill_bytes),
+                                         f"quantizer) back to back between two events, every chunk's inputs "
+                                         f"generated into HBM before", "us": round(app_us, 1),
+                                 "algorithmic_bytes": int(prefill_bytes),
                                  "achieved_GBs": round(prefill_bytes / app_us / 1e3, 1),
                                  "frac_of_peak": round(prefill_bytes / app_us / 1e3 / PEAK_HBM_GBS, 4)}}
 
@@ -680,7 +682,13 @@ def main():
         pre.append((t0, n, gen.kv(W.TENSOR_K, t0, n), gen.kv(W.TENSOR_V, t0, n),
                     torch.full((B,), t0, dtype=torch.int32, device=dev)))
     prefill_bytes = sum(append_bytes(wl, t0, n) for t0, n, _, _, _ in pre)
-    # arguments marshalled before timing, so the launches reach the GPU back to back
+    # arguments marshalled before timing, so the launches reach the GPU back to back; the library's
+    # first kernel launch in a process loads its code object (about a millisecond), so one untimed
+    # append to a scratch cache comes first
+    warm_cache = K.CacheBuffers(params, B, 64)
+    K.kvq_quantize_append(params, warm_cache.struct, pre[0][4], None, pre[0][2], pre[0][3], 16)
+    torch.cuda.synchronize()
+    del warm_cache
     pre_calls = [K.bound_call("kvq_quantize_append", params, cache.struct, before, None, k, v, n, stream=stream)
                  for t0, n, k, v, before in pre]
     ev_p = [torch.cuda.Event(enable_timing=True) for _ in range(2)]

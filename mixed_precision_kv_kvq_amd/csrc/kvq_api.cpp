@@ -106,6 +106,9 @@ SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, in
     // sum over units of the quantized splits <= tq + units (each unit's share rounds down, then up to >= 1)
     sp.grid = units * sp.ws + tq + units;
   }
+  // with an even Hkv the waves of the two kv heads of a pair sit 8 apart in groups of 16: up to 14
+  // waves at the end of the last group hold no item
+  if (p->num_kv_heads % 2 == 0) sp.grid += 16;
   sp.S_max = (int)(sp.ws + qs_max);
   // the merge reads the headers and rows of a unit's equal share at once (exactly the split count
   // of every unit when the lengths are equal)

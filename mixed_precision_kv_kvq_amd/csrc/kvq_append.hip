@@ -284,8 +284,11 @@ __device__ void page_item(const KvqAppendArgs &a, int pidx, int h, int b, uint32
       // per bit plane (width w, bits [sh, sh + w) of the codes): the octet's channel pairs
       // u = 4q + i fill word u / (16 / w) of slot 16 jo + t in the plane's area: one word for
       // widths up to 4, two at 8; the plane values are gathered per word before one OR
-      for (int pl = 0; pl < kvq_nplanes(lay.kb); ++pl) {
-        const int w = kvq_plane_width(lay.kb, pl), sh = kvq_plane_off(lay.kb, pl), per = 16 / w;
+      int sh = 0;
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1) {
+        if (!(lay.kb == 8 ? w == 8 : (w < 8 && (lay.kb & w) != 0))) continue;  // not a plane of kb
+        const int per = 16 / w;
         const uint32_t mask = (1u << w) - 1u;
         uint32_t *kw = rw + (lay.k_codes_off + 256 * sh) / 4;
         uint32_t acc = 0;
@@ -302,6 +305,7 @@ __device__ void page_item(const KvqAppendArgs &a, int pidx, int h, int b, uint32
                  (((c[2 * i + 1] >> sh) & mask) << (16 + w * (u % per)));
         }
         atomicOr(kw + (16 * jo + t) * w + wcur, acc);
+        sh += w;
       }
     }
     const int grp = (32 * q) / lay.kg;
@@ -332,13 +336,16 @@ __device__ void page_item(const KvqAppendArgs &a, int pidx, int h, int b, uint32
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t c0 = group_code_fast(x[e], g, r32, qmax32), c1 = group_code_fast(x[e + 16], g, r32, qmax32);
-      for (int pl = 0; pl < kvq_nplanes(lay.vb); ++pl) {
-        const int w = kvq_plane_width(lay.vb, pl), sh = kvq_plane_off(lay.vb, pl);
+      int sh = 0;
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1) {
+        if (!(lay.vb == 8 ? w == 8 : (w < 8 && (lay.vb & w) != 0))) continue;  // not a plane of vb
         const uint32_t mask = (1u << w) - 1u;
         const int m0 = 2 * q, pos0 = iv * 8 * w + m0 * w, pos1 = pos0 + w;
         const uint32_t bits = (((c0 >> sh) & mask) << (16 * hv + (pos0 & 15))) |
                               (((c1 >> sh) & mask) << (16 * hv + (pos1 & 15)));
         atomicOr(rw + (lay.v_codes_off + 256 * sh) / 4 + (16 * jj + e) * w + (pos0 >> 4), bits);
+        sh += w;
       }
     }
     const int grp = (32 * q) / lay.vg;

@@ -216,7 +216,15 @@ struct Kern {
   static constexpr int HSN = G < 4 ? G : 4;  // rows of the score layout in use
   static constexpr int NACC = HB;           // score accumulators (both query parts add into one)
   static constexpr int NPK = kvq_nplanes(KB), NPV = kvq_nplanes(VB);  // bit planes of a code
+  // plane widths and offsets as constants (a width of 1 for planes a code does not have)
   static constexpr int KW0 = kvq_plane_width(KB, 0), VW0 = kvq_plane_width(VB, 0);
+  static constexpr int KW1 = NPK > 1 ? kvq_plane_width(KB, 1) : 1, KW2 = NPK > 2 ? kvq_plane_width(KB, 2) : 1;
+  static constexpr int VW1 = NPV > 1 ? kvq_plane_width(VB, 1) : 1, VW2 = NPV > 2 ? kvq_plane_width(VB, 2) : 1;
+  static constexpr int KO1 = KW0, KO2 = KW0 + KW1, VO1 = VW0, VO2 = VW0 + VW1;
+  static __device__ __forceinline__ constexpr int kpw(int p) { return p == 0 ? KW0 : (p == 1 ? KW1 : KW2); }
+  static __device__ __forceinline__ constexpr int vpw(int p) { return p == 0 ? VW0 : (p == 1 ? VW1 : VW2); }
+  static __device__ __forceinline__ constexpr int kpo(int p) { return p == 0 ? 0 : (p == 1 ? KO1 : KO2); }
+  static __device__ __forceinline__ constexpr int vpo(int p) { return p == 0 ? 0 : (p == 1 ? VO1 : VO2); }
   typedef State<HB, NVG> St;
 
   struct Ctx {
@@ -369,7 +377,7 @@ struct Kern {
       uint32_t v = 0;
 #pragma unroll
       for (int p = 0; p < NPK; ++p) {
-        const int pw = kvq_plane_width(KB, p), po = kvq_plane_off(KB, p), per = 16 / pw;
+        const int pw = kpw(p), po = kpo(p), per = 16 / pw;
         const uint32_t word = pd.kc.w[po + u / per];
         v |= field_move(word, word >> 8, pw, pw * (u % per), sc + po);
       }
@@ -520,7 +528,7 @@ struct Kern {
         uint32_t v = 0;
 #pragma unroll
         for (int p = 0; p < NPV; ++p) {
-          const int pw = kvq_plane_width(VB, p), po = kvq_plane_off(VB, p);
+          const int pw = vpw(p), po = vpo(p);
           const int pos = (i & 1) * 8 * pw + m * pw;
           const uint32_t word = (i < 2) ? A.vc.w[po + (pos >> 4)] : B.vc.w[po + (pos >> 4)];
           v |= field_move(word, word >> 8, pw, pos & 15, vtile_scale(m) + po);
@@ -599,29 +607,25 @@ struct Kern {
     RecOff o;
 #pragma unroll
     for (int p = 0; p < NPK; ++p)
-      o.kc[p] = lay.k_codes_off + 256 * kvq_plane_off(KB, p) + cx.lane * 4 * kvq_plane_width(KB, p);
+      o.kc[p] = lay.k_codes_off + 256 * kpo(p) + cx.lane * 4 * kpw(p);
     o.km = lay.k_meta_off + cx.col * 4 * (4 >> KS);
 #pragma unroll
     for (int p = 0; p < NPV; ++p)
-      o.vc[p] = lay.v_codes_off + 256 * kvq_plane_off(VB, p) + cx.lane * 4 * kvq_plane_width(VB, p);
+      o.vc[p] = lay.v_codes_off + 256 * vpo(p) + cx.lane * 4 * vpw(p);
     o.vm = lay.v_meta_off + cx.col * 4 * NVG;
     return o;
   }
 
-  // Plane widths as template arguments (1 for planes a code does not have).
-  static constexpr int kpw(int p) { return p < NPK ? kvq_plane_width(KB, p) : 1; }
-  static constexpr int vpw(int p) { return p < NPV ? kvq_plane_width(VB, p) : 1; }
-
   template <int KS>
   static __device__ __forceinline__ void read_page_at(PageData<KS> &pd, uint32_t base, const RecOff &o) {
     constexpr int NKM = 4 >> KS;
-    RawWords<kpw(0)> rk0;
-    RawWords<kpw(1)> rk1;
-    RawWords<kpw(2)> rk2;
+    RawWords<KW0> rk0;
+    RawWords<KW1> rk1;
+    RawWords<KW2> rk2;
     RawWords<NKM> rkm;
-    RawWords<vpw(0)> rv0;
-    RawWords<vpw(1)> rv1;
-    RawWords<vpw(2)> rv2;
+    RawWords<VW0> rv0;
+    RawWords<VW1> rv1;
+    RawWords<VW2> rv2;
     RawWords<NVG> rvm;
     ds_read_words(rk0, base + o.kc[0]);
     if constexpr (NPK > 1) ds_read_words(rk1, base + o.kc[NPK > 1 ? 1 : 0]);
@@ -641,26 +645,26 @@ struct Kern {
     if constexpr (NPV > 2) tie(rv2);
     tie(rvm);
 #pragma unroll
-    for (int i = 0; i < kpw(0); ++i) pd.kc.w[i] = rk0.w(i);
+    for (int i = 0; i < KW0; ++i) pd.kc.w[i] = rk0.w(i);
     if constexpr (NPK > 1) {
 #pragma unroll
-      for (int i = 0; i < kpw(1); ++i) pd.kc.w[kvq_plane_off(KB, 1) + i] = rk1.w(i);
+      for (int i = 0; i < KW1; ++i) pd.kc.w[KO1 + i] = rk1.w(i);
     }
     if constexpr (NPK > 2) {
 #pragma unroll
-      for (int i = 0; i < kpw(2); ++i) pd.kc.w[kvq_plane_off(KB, 2) + i] = rk2.w(i);
+      for (int i = 0; i < KW2; ++i) pd.kc.w[KO2 + i] = rk2.w(i);
     }
 #pragma unroll
     for (int i = 0; i < NKM; ++i) pd.km[i] = rkm.w(i);
 #pragma unroll
-    for (int i = 0; i < vpw(0); ++i) pd.vc.w[i] = rv0.w(i);
+    for (int i = 0; i < VW0; ++i) pd.vc.w[i] = rv0.w(i);
     if constexpr (NPV > 1) {
 #pragma unroll
-      for (int i = 0; i < vpw(1); ++i) pd.vc.w[kvq_plane_off(VB, 1) + i] = rv1.w(i);
+      for (int i = 0; i < VW1; ++i) pd.vc.w[VO1 + i] = rv1.w(i);
     }
     if constexpr (NPV > 2) {
 #pragma unroll
-      for (int i = 0; i < vpw(2); ++i) pd.vc.w[kvq_plane_off(VB, 2) + i] = rv2.w(i);
+      for (int i = 0; i < VW2; ++i) pd.vc.w[VO2 + i] = rv2.w(i);
     }
 #pragma unroll
     for (int v = 0; v < NVG; ++v) pd.vm[v] = rvm.w(v);
@@ -861,7 +865,8 @@ struct Kern {
   // (Lb - R) mod 16; other splits of this launch read that page only with the token masked out)
   // and into a one-token record at VREC_OFF for evicted_pair.  The new token is written to slot
   // s_new.  Returns whether a token left the window.
-  static __device__ bool fused_append(const KvqAttnArgs &args, uint8_t *smem, int b, int kvh, int Lb, int s_new) {
+  static __device__ __forceinline__ bool fused_append(const KvqAttnArgs &args, uint8_t *smem, int b, int kvh, int Lb,
+                                                      int s_new) {
     const int lane = threadIdx.x, R = args.R, Hkv = args.Hkv;
     const KvqLayout &lay = args.lay;
     const size_t row = (size_t)KVQ_D * 2, unit = (size_t)b * Hkv + kvh;
@@ -988,12 +993,20 @@ struct Kern {
     const int s = (qp + per - 1) / per;
     return s < 1 ? 1 : s;
   }
-  // Sequence b's kv heads take waves [Hkv * O_b, Hkv * (O_b + S_b)) of the launch, S_b = window
-  // splits + plan_qsplits, O_b = sum of S over the sequences before b, one kv head after the other.
-  // Computed by the whole wave from the device lengths (lane i handles sequences i, i + 64, ...;
-  // for batches up to 64 the lengths are loaded once).  Returns false for a wave past the last
-  // sequence's.  Results are wave-uniform (read with readlane), so everything derived from them
-  // stays scalar; len_out is the sequence's length as stored in seq_lens (not clamped).
+  // Work items of the launch, sequence after sequence: S_b = window splits + plan_qsplits for each
+  // kv head of sequence b.  Blocks go to the 8 XCDs round-robin (block mod 8), and the page
+  // records of kv heads 2i and 2i + 1 are adjacent (a 1856-byte K4V2 record is 14.5 cache lines
+  // of 128 bytes, so the two share a line): with an even Hkv the items are pair items (kv-head
+  // pair, split), and pair item k runs on waves 16 (k / 8) + k mod 8 (kv head 2i) and that + 8
+  // (kv head 2i + 1), so both halves of every shared line are fetched into one XCD's L2 whatever
+  // the split counts (up to 14 waves at the end of the grid stay idle).  With an odd Hkv an item
+  // is one (kv head, split) per wave.  Within a unit the split index is rotated by the unit pair,
+  // which spreads each split index (the window splits in particular, which carry less work)
+  // evenly over the XCDs.  Computed by the whole wave from the device lengths (lane i handles
+  // sequences i, i + 64, ...; for batches up to 64 the lengths are loaded once).  Returns false
+  // for a wave past the last item.  Results are wave-uniform (read with readlane), so everything
+  // derived from them stays scalar; len_out is the sequence's length as stored in seq_lens (not
+  // clamped).
   static __device__ __forceinline__ bool plan_wave(const KvqAttnArgs &a, int wave, int &b_out, int &kvh_out,
                                                    int &split_out, int &S_out, int &len_out) {
     const int lane = threadIdx.x, B = a.cache.batch, R = a.R;
@@ -1013,12 +1026,16 @@ struct Kern {
       for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
       Q += v;
     }
-    int base = 0;  // waves of the sequences before this chunk of 64
+    const bool paired = (a.Hkv & 1) == 0;
+    const int item = paired ? 8 * (wave >> 4) + (wave & 7) : wave;
+    const int member = paired ? (wave >> 3) & 1 : 0;
+    const int per_seq = paired ? a.Hkv / 2 : a.Hkv;  // items per split index of a sequence
+    int base = 0;  // items of the sequences before this chunk of 64
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int b = b0 + lane;
       const int raw = b0 == 0 ? raw0 : (b < B ? a.seq_lens[b] : 0);
       const int Sb = b < B ? a.ws + plan_qsplits(a, qpages_of(raw), Q) : 0;
-      const int nw_b = a.Hkv * Sb;
+      const int nw_b = per_seq * Sb;
       int incl = nw_b;  // inclusive prefix over the lanes
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -1026,19 +1043,13 @@ struct Kern {
         if (lane >= off) incl += t;
       }
       const int lo = base + incl - nw_b;
-      const uint64_t m = __ballot(b < B && wave >= lo && wave < lo + nw_b);
+      const uint64_t m = __ballot(b < B && item >= lo && item < lo + nw_b);
       if (m) {
         const int src = __ffsll((unsigned long long)m) - 1;
         const int bb = __builtin_amdgcn_readlane(b, src), S = __builtin_amdgcn_readlane(Sb, src);
-        const int idx = wave - __builtin_amdgcn_readlane(lo, src);
-        const int kvh = idx / S;
+        const int idx = item - __builtin_amdgcn_readlane(lo, src);
+        const int kvh = paired ? 2 * (idx / S) + member : idx / S;
         const int unit = bb * a.Hkv + kvh;
-        // Consecutive waves are the splits of one unit, on the 8 XCDs in turn (block mod 8): with S
-        // a multiple of 8 the split at position k of every unit would land on the same XCD, so the
-        // split index is rotated by the unit pair, which spreads each split (the window splits in
-        // particular, which carry less work) evenly over the XCDs.  Units 2i and 2i+1 keep the same
-        // rotation: their page records are adjacent and share a cache line (a 1856-byte K4V2 record
-        // is 14.5 lines), which is then fetched into one XCD's L2 only.
         b_out = bb;
         kvh_out = kvh;
         split_out = (idx % S + unit / 2) % S;
@@ -1051,7 +1062,7 @@ struct Kern {
     return false;
   }
 
-  static __device__ void run(const KvqAttnArgs &args, uint8_t *smem) {
+  static __device__ __forceinline__ void run(const KvqAttnArgs &args, uint8_t *smem) {
     float *lds = reinterpret_cast<float *>(smem);
     const int lane = threadIdx.x;
     const int Hkv = args.Hkv;

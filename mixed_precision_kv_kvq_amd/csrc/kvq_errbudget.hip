@@ -23,27 +23,41 @@ __device__ __attribute__((always_inline)) inline void bf16x8(const uint4 w, floa
 
 __device__ inline float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
+// Sum over the 16 lanes of a lane row, in every lane of the row: row rotations by 8, 4, 2, 1 (DPP,
+// no LDS round trip).
+__device__ __forceinline__ float row_ror(float v, int sh) {
+  int r;
+  switch (sh) {
+    case 8: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
 __device__ inline float row16_sum(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+#pragma unroll
+  for (int sh = 8; sh >= 1; sh >>= 1) v += row_ror(v, sh);
   return v;
 }
 
 // Normalized 128-point Walsh-Hadamard transform of a row held as 8 channels [8c, 8c + 8) in
 // each of the 16 lanes of a lane row (c = lane mod 16), fp32: butterflies in stage order 1, 2,
 // 4 inside the lane, then 8, 16, 32, 64 across lanes c ^ 1, c ^ 2, c ^ 4, c ^ 8.  Every lane of
-// the wave must take part (cross-lane reads).
-__device__ __attribute__((always_inline)) inline void row_wht(float *x, int c) {
+// the wave must take part (cross-lane reads); rows whose `apply` is false (the same in the 16
+// lanes of the row) keep their values.
+__device__ __attribute__((always_inline)) inline void row_wht(float *x, int c, bool apply) {
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = x[e];
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if ((e & h) == 0) {
-        const float u = x[e], v = x[e + h];
-        x[e] = u + v;
-        x[e + h] = u - v;
+        const float u = y[e], v = y[e + h];
+        y[e] = u + v;
+        y[e + h] = u - v;
       }
     }
   }
@@ -52,12 +66,12 @@ __device__ __attribute__((always_inline)) inline void row_wht(float *x, int c) {
     const bool upper = (c & lx) != 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = __shfl_xor(x[e], lx);
-      x[e] = upper ? p - x[e] : x[e] + p;
+      const float p = __shfl_xor(y[e], lx);
+      y[e] = upper ? p - y[e] : y[e] + p;
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= (float)KVQ_WHT_C;
+  for (int e = 0; e < 8; ++e) x[e] = apply ? y[e] * (float)KVQ_WHT_C : x[e];
 }
 
 // The same transform for a row held as channels 2l, 2l + 1 in lane l of the wave: stage 1 inside
@@ -80,61 +94,43 @@ __device__ __attribute__((always_inline)) inline void pair_wht(float &x0, float 
   x1 *= (float)KVQ_WHT_C;
 }
 
-struct Pos {
-  bool valid, quant;
-  const uint8_t *rec;  // page record of a quantized position
-  int n;               // position within the page
-};
-
-// Keys (or values) of 8 channels [8c, 8c + 8) of one position: original and reconstructed.
-// Window positions are stored exactly, so their reconstruction is the original row.
+// The reconstruction of 8 channels [8c, 8c + 8) of token n of a page record staged in LDS (keys
+// or values), as zero + code * scale in fp32.
 template <bool KEYS>
-__device__ __attribute__((always_inline)) inline void load8(const KvqErrArgs &a, const Pos &p, const uint16_t *ref_row, int c, float *x,
-                             float *xh) {
-  if (!p.valid) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = xh[e] = 0.f;
-    return;
-  }
-  bf16x8(reinterpret_cast<const uint4 *>(ref_row)[c], x);
-  if (!p.quant) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xh[e] = x[e];
-    return;
-  }
-  const KvqLayout &lay = a.lay;
-  const int bits = KEYS ? lay.kb : lay.vb;
-  const int grp = (8 * c) / (KEYS ? lay.kg : lay.vg);
-  const uint32_t m = *reinterpret_cast<const uint32_t *>(
-      p.rec + (KEYS ? lay.k_meta_off : lay.v_meta_off) + 4 * kvq_meta_dword(KEYS ? lay.nkg : lay.nvg, p.n, grp));
+__device__ __attribute__((always_inline)) inline void decode8(const KvqLayout &lay, const uint8_t *rs, int n, int c,
+                                                              float *xh) {
+  const uint32_t m = reinterpret_cast<const uint32_t *>(rs + (KEYS ? lay.k_meta_off : lay.v_meta_off))
+      [kvq_meta_dword(KEYS ? lay.nkg : lay.nvg, n, (8 * c) / (KEYS ? lay.kg : lay.vg))];
   const float zero = f16f(m >> 16), scale = f16f(m & 0xFFFF);
+  uint32_t code[8];
+  if (KEYS)
+    kvq_k_codes8(rs + lay.k_codes_off, lay.kb, n, c, code);
+  else
+    kvq_v_codes8(rs + lay.v_codes_off, lay.vb, n, c, code);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t code = KEYS ? kvq_k_code(p.rec + lay.k_codes_off, bits, p.n, 8 * c + e)
-                               : kvq_v_code(p.rec + lay.v_codes_off, bits, p.n, 8 * c + e);
-    xh[e] = zero + (float)code * scale;
-  }
+  for (int e = 0; e < 8; ++e) xh[e] = zero + (float)code[e] * scale;
 }
 
-// One workgroup of EB_WAVES waves per (group of HG query heads of one kv head, sequence); wave w
-// takes positions 4 (w + k EB_WAVES) + r, lane 16 r + c holding channels [8c, 8c + 8), so each
-// position's keys and values are decoded once for the HG heads.  Pass 1: exact and quantized
-// scores with online maxima and sums (log2 units) and the score-error statistics; the first head
-// group of each kv head also accumulates the key reconstruction error.  The waves' maxima and
-// sums are merged through LDS (every wave merges them in the same order).  Pass 2: the weights a
-// (exact keys) and a' (quantized keys), their total variation, and the four weighted sums a V,
-// a V_hat, a' V, a' V_hat, merged over the waves through LDS at the end.
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 constexpr int EB_WAVES = 8;
+constexpr int EB_REC16 = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 16;  // largest record, 16-byte units
 template <int HG>
 __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs a) {
   __shared__ float red[EB_WAVES][6 * HG];
   __shared__ float ured[EB_WAVES][6];
   __shared__ float accs[4][HG][KVQ_D];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, b = blockIdx.y;
-  const int hq0 = blockIdx.x * HG;  // first query head of the group
+  __shared__ uint4 recs[EB_WAVES][2][EB_REC16];  // page records (two: the next one lands meanwhile)
+  __shared__ uint4 rows[EB_WAVES][2][KVQ_PAGE * 16];  // the page's original K and V rows
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane >> 4, c = lane & 15;
-  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, h = hq0 / g;
-  const bool unit_lead = (hq0 % g) == 0;
+  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, ngrp = g / HG;
+  // workgroup -> (unit, head group): the groups of unit u at blocks 8 ngrp (u / 8) + 8 grp + u mod 8
+  const int blk = blockIdx.x / (8 * ngrp), rem = blockIdx.x % (8 * ngrp);
+  const int grp = rem / 8, unit = 8 * blk + rem % 8;
+  if (unit >= a.B * Hkv) return;  // padding of the last group of 8 units
+  const int b = unit / Hkv, h = unit % Hkv;
+  const int hq0 = h * g + grp * HG;  // first query head of the group
+  const bool unit_lead = grp == 0;
   int64_t L = a.seq_lens[b];
   kvq_raise(a.cache, hq0 == 0 && (L < 0 || L > a.max_len), KVQ_DEV_LENGTH);
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
@@ -142,6 +138,8 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   const int64_t cap_tokens = (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq) * KVQ_PAGE;
   if (nq > cap_tokens) nq = cap_tokens;
   const float ninf = -__builtin_inff();
+  const KvqLayout &lay = a.lay;
+  const int rec16 = lay.record / 16;
 
   float q[HG][8];
 #pragma unroll
@@ -156,30 +154,50 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       bf16x8(*reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qrow), q[j]);
     }
   }
-  // Rotated keys are scored with the rotated query: (H q).(H k) = q.k.  Window keys stay raw.
-  float qr[HG][8];
-#pragma unroll
-  for (int j = 0; j < HG; ++j) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qr[j][e] = q[j][e];
-    if (a.rotation) row_wht(qr[j], c);
-  }
-  auto pos_of = [&](int64_t t) {
-    Pos p;
-    p.valid = t < L;
-    p.quant = t < nq;
-    p.n = (int)(t % KVQ_PAGE);
-    p.rec = nullptr;
-    if (p.valid && p.quant) {
-      const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, b, h, t / KVQ_PAGE);
-      p.rec = a.cache.pages + (size_t)rec_idx * a.lay.record;
-    }
-    return p;
+  // This lane's 16 bytes (8 channels) of original row t (t < L; callers pass a valid t).
+  auto ref8 = [&](const uint16_t *base, int64_t t) {
+    return *reinterpret_cast<const uint4 *>(base + (((size_t)b * a.max_len + (size_t)t) * Hkv + h) * KVQ_D + 8 * c);
   };
-  auto ref_row = [&](const uint16_t *base, int64_t t) {
-    return base + (((size_t)b * a.max_len + (size_t)t) * Hkv + h) * KVQ_D;
+  // One page's original rows in flight: the lane's 16 bytes of the K (and V) rows of positions
+  // 4 i + r, loaded for the next page before the current one is computed, then stored to the
+  // wave's LDS region (positions past L re-read row L - 1).  The page record goes straight to LDS
+  // (buffer loads to LDS, one lane per 16-byte chunk) into the other of the wave's two record
+  // buffers; an explicit wait for all of the wave's loads precedes each page.
+  struct PageRegs {
+    uint4 k[4], v[4];
+  };
+  auto load_rows = [&](int64_t pg, PageRegs &pr, bool with_v) __attribute__((always_inline)) {
+    const int64_t t0 = pg * KVQ_PAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + 4 * i + r < L ? t0 + 4 * i + r : L - 1;
+      pr.k[i] = ref8(a.k_ref, t);
+      if (with_v) pr.v[i] = ref8(a.v_ref, t);
+    }
+  };
+  auto store_rows = [&](const PageRegs &pr, bool with_v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rows[w][0][(4 * i + r) * 16 + c] = pr.k[i];
+      if (with_v) rows[w][1][(4 * i + r) * 16 + c] = pr.v[i];
+    }
+  };
+  auto load_rec = [&](int64_t pg, int buf) __attribute__((always_inline)) {
+    if (pg * KVQ_PAGE >= nq) return;  // no quantized position on this page
+    const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, b, h, pg);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(a.cache.pages + (size_t)rec_idx * lay.record), 0, lay.record,
+                                          0x00020000);
+    const uint32_t dst = (uint32_t)(uintptr_t)&recs[w][buf][0];
+#pragma unroll
+    for (int i = 0; i < (EB_REC16 + 63) / 64; ++i) {
+      if (64 * i < rec16 && lane + 64 * i < rec16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(size_t)(dst + 1024u * i), 16, 16 * (lane + 64 * i),
+                                                 0, 0, 0);
+    }
   };
   const float sl2 = a.scale * 1.4426950408889634f;  // softmax scale in log2 units
+  const int64_t npages = (L + KVQ_PAGE - 1) / KVQ_PAGE;
 
   // ---- pass 1 ----
   float m0[HG], z0[HG], m1[HG], z1[HG], ds_max[HG], ds_sq[HG];
@@ -189,42 +207,72 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     z0[j] = z1[j] = ds_max[j] = ds_sq[j] = 0.f;
   }
   float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;  // key reconstruction error (lead group)
-  for (int64_t i0 = 4 * w; i0 < L; i0 += 4 * EB_WAVES) {
-    const int64_t t = i0 + r;
-    const Pos p = pos_of(t);
-    float k[8], kh[8];
-    load8<true>(a, p, ref_row(a.k_ref, t < L ? t : 0), c, k, kh);
-    const bool krot = a.rotation && p.quant;  // uniform over the lane row of one position
-#pragma unroll
-    for (int j = 0; j < HG; ++j) {
-      float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        d0 = __builtin_fmaf(q[j][e], k[e], d0);
-        d1 = __builtin_fmaf(krot ? qr[j][e] : q[j][e], kh[e], d1);
-      }
-      d0 = row16_sum(d0);
-      d1 = row16_sum(d1);
-      if (p.valid) {
-        const float s0 = d0 * sl2, s1 = d1 * sl2;
-        const float n0 = __builtin_fmaxf(m0[j], s0), n1 = __builtin_fmaxf(m1[j], s1);
-        z0[j] = z0[j] * __builtin_amdgcn_exp2f(m0[j] - n0) + __builtin_amdgcn_exp2f(s0 - n0);
-        z1[j] = z1[j] * __builtin_amdgcn_exp2f(m1[j] - n1) + __builtin_amdgcn_exp2f(s1 - n1);
-        m0[j] = n0;
-        m1[j] = n1;
-        const float ds = (d1 - d0) * a.scale;
-        ds_max[j] = __builtin_fmaxf(ds_max[j], __builtin_fabsf(ds));
-        ds_sq[j] = __builtin_fmaf(ds, ds, ds_sq[j]);
-      }
+  PageRegs pr;
+  int buf = 0;
+  if (w < npages) {
+    load_rows(w, pr, false);
+    load_rec(w, 0);
+  }
+  for (int64_t pg = w; pg < npages; pg += EB_WAVES, buf ^= 1) {
+    const int64_t t0 = pg * KVQ_PAGE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page's rows and record have landed
+    store_rows(pr, false);
+    if (pg + EB_WAVES < npages) {
+      load_rows(pg + EB_WAVES, pr, false);
+      load_rec(pg + EB_WAVES, buf ^ 1);
     }
-    if (unit_lead && a.rotation) row_wht(kh, c);  // reconstruction in the original domain
-    if (unit_lead && p.valid && p.quant) {
+    const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
+#pragma unroll 1
+    for (int it = 0; it < 4; ++it) {
+      const int n = 4 * it + r;
+      const int64_t t = t0 + n;
+      const bool valid = t < L, quant = t < nq;
+      float k[8], kh[8];
+      if (valid) {
+        bf16x8(rows[w][0][n * 16 + c], k);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float err = kh[e] - k[e];
-        ek_sq = __builtin_fmaf(err, err, ek_sq);
-        ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
-        k_sq = __builtin_fmaf(k[e], k[e], k_sq);
+        for (int e = 0; e < 8; ++e) k[e] = 0.f;
+      }
+      if (quant) {
+        decode8<true>(lay, rs, n, c, kh);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kh[e] = k[e];
+      }
+      // Rotated keys are rotated back first (the normalized transform is its own inverse), so
+      // both scores use the raw query: q.(H kh) = (H q).kh.  Window keys are stored raw.
+      if (a.rotation) row_wht(kh, c, quant);
+#pragma unroll
+      for (int j = 0; j < HG; ++j) {
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          d0 = __builtin_fmaf(q[j][e], k[e], d0);
+          d1 = __builtin_fmaf(q[j][e], kh[e], d1);
+        }
+        d0 = row16_sum(d0);
+        d1 = row16_sum(d1);
+        if (valid) {
+          const float s0 = d0 * sl2, s1 = d1 * sl2;
+          const float n0 = __builtin_fmaxf(m0[j], s0), n1 = __builtin_fmaxf(m1[j], s1);
+          z0[j] = z0[j] * __builtin_amdgcn_exp2f(m0[j] - n0) + __builtin_amdgcn_exp2f(s0 - n0);
+          z1[j] = z1[j] * __builtin_amdgcn_exp2f(m1[j] - n1) + __builtin_amdgcn_exp2f(s1 - n1);
+          m0[j] = n0;
+          m1[j] = n1;
+          const float ds = (d1 - d0) * a.scale;
+          ds_max[j] = __builtin_fmaxf(ds_max[j], __builtin_fabsf(ds));
+          ds_sq[j] = __builtin_fmaf(ds, ds, ds_sq[j]);
+        }
+      }
+      if (unit_lead && valid && quant) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float err = kh[e] - k[e];
+          ek_sq = __builtin_fmaf(err, err, ek_sq);
+          ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
+          k_sq = __builtin_fmaf(k[e], k[e], k_sq);
+        }
       }
     }
   }
@@ -285,44 +333,76 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     for (int e = 0; e < 8; ++e) o[j][e] = ov[j][e] = ok[j][e] = oj[j][e] = 0.f;
   }
   float ev_sq = 0.f, ev_max = 0.f, v_sq = 0.f;
-  for (int64_t i0 = 4 * w; i0 < L; i0 += 4 * EB_WAVES) {
-    const int64_t t = i0 + r;
-    const Pos p = pos_of(t);
-    float k[8], kh[8], v[8], vh[8];
-    load8<true>(a, p, ref_row(a.k_ref, t < L ? t : 0), c, k, kh);
-    load8<false>(a, p, ref_row(a.v_ref, t < L ? t : 0), c, v, vh);
-    const bool krot = a.rotation && p.quant;
-#pragma unroll
-    for (int j = 0; j < HG; ++j) {
-      float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        d0 = __builtin_fmaf(q[j][e], k[e], d0);
-        d1 = __builtin_fmaf(krot ? qr[j][e] : q[j][e], kh[e], d1);
-      }
-      d0 = row16_sum(d0);
-      d1 = row16_sum(d1);
-      const float w0 = p.valid ? __builtin_amdgcn_exp2f(d0 * sl2 - m0[j]) * z0[j] : 0.f;
-      const float w1 = p.valid ? __builtin_amdgcn_exp2f(d1 * sl2 - m1[j]) * z1[j] : 0.f;
-      if (c == 0) tv[j] += __builtin_fabsf(w1 - w0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        o[j][e] = __builtin_fmaf(w0, v[e], o[j][e]);
-        ov[j][e] = __builtin_fmaf(w0, vh[e], ov[j][e]);
-        ok[j][e] = __builtin_fmaf(w1, v[e], ok[j][e]);
-        oj[j][e] = __builtin_fmaf(w1, vh[e], oj[j][e]);
-      }
+  buf = 0;
+  if (w < npages) {
+    load_rows(w, pr, true);
+    load_rec(w, 0);
+  }
+  for (int64_t pg = w; pg < npages; pg += EB_WAVES, buf ^= 1) {
+    const int64_t t0 = pg * KVQ_PAGE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page's rows and record have landed
+    store_rows(pr, true);
+    if (pg + EB_WAVES < npages) {
+      load_rows(pg + EB_WAVES, pr, true);
+      load_rec(pg + EB_WAVES, buf ^ 1);
     }
-    // With rotated values the sums over vh are in the rotated domain (rotated back per head at
-    // the end; no recent window then); the reconstruction statistics rotate each position back.
-    if (unit_lead && a.value_rotation) row_wht(vh, c);
-    if (unit_lead && p.valid && p.quant) {
+    const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
+#pragma unroll 1
+    for (int it = 0; it < 4; ++it) {
+      const int n = 4 * it + r;
+      const int64_t t = t0 + n;
+      const bool valid = t < L, quant = t < nq;
+      float k[8], kh[8], v[8], vh[8];
+      if (valid) {
+        bf16x8(rows[w][0][n * 16 + c], k);
+        bf16x8(rows[w][1][n * 16 + c], v);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float err = vh[e] - v[e];
-        ev_sq = __builtin_fmaf(err, err, ev_sq);
-        ev_max = __builtin_fmaxf(ev_max, __builtin_fabsf(err));
-        v_sq = __builtin_fmaf(v[e], v[e], v_sq);
+        for (int e = 0; e < 8; ++e) k[e] = v[e] = 0.f;
+      }
+      if (quant) {
+        decode8<true>(lay, rs, n, c, kh);
+        decode8<false>(lay, rs, n, c, vh);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kh[e] = k[e];
+          vh[e] = v[e];
+        }
+      }
+      if (a.rotation) row_wht(kh, c, quant);
+#pragma unroll
+      for (int j = 0; j < HG; ++j) {
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          d0 = __builtin_fmaf(q[j][e], k[e], d0);
+          d1 = __builtin_fmaf(q[j][e], kh[e], d1);
+        }
+        d0 = row16_sum(d0);
+        d1 = row16_sum(d1);
+        const float w0 = valid ? __builtin_amdgcn_exp2f(d0 * sl2 - m0[j]) * z0[j] : 0.f;
+        const float w1 = valid ? __builtin_amdgcn_exp2f(d1 * sl2 - m1[j]) * z1[j] : 0.f;
+        if (c == 0) tv[j] += __builtin_fabsf(w1 - w0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[j][e] = __builtin_fmaf(w0, v[e], o[j][e]);
+          ov[j][e] = __builtin_fmaf(w0, vh[e], ov[j][e]);
+          ok[j][e] = __builtin_fmaf(w1, v[e], ok[j][e]);
+          oj[j][e] = __builtin_fmaf(w1, vh[e], oj[j][e]);
+        }
+      }
+      // With rotated values the sums over vh are in the rotated domain (rotated back per head at
+      // the end; no recent window then); the reconstruction statistics rotate each position back.
+      if (unit_lead && a.value_rotation) row_wht(vh, c, true);
+      if (unit_lead && valid && quant) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float err = vh[e] - v[e];
+          ev_sq = __builtin_fmaf(err, err, ev_sq);
+          ev_max = __builtin_fmaxf(ev_max, __builtin_fabsf(err));
+          v_sq = __builtin_fmaf(v[e], v[e], v_sq);
+        }
       }
     }
   }
@@ -463,7 +543,9 @@ hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s) {
   (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
   // two heads per group: four would need more than the 256 registers of two waves per SIMD
   const int g = a.Hq / a.Hkv, hg = g < 2 ? g : 2;
-  const dim3 grid((unsigned)(a.Hq / hg), (unsigned)a.B), block(64 * EB_WAVES);
+  const int units = a.B * a.Hkv;
+  // groups of 8 units, each group's head groups 8 workgroups apart (padding after the last unit)
+  const dim3 grid((unsigned)(((units + 7) / 8) * 8 * (g / hg))), block(64 * EB_WAVES);
   if (hg == 1)
     hipLaunchKernelGGL(kvq_errbudget_kernel<1>, grid, block, 0, s, a);
   else

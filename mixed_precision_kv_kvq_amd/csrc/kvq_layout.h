@@ -107,15 +107,20 @@ __host__ __device__ inline void kvq_v_code_pos(int w, int tt, int ch, int *byte_
   *bit = 16 * h + (p & 15);
 }
 
-// The b-bit K code of (token n, channel ch) from a record's K code area (all planes).
+// The b-bit K code of (token n, channel ch) from a record's K code area (all planes: the candidate
+// widths 8, 4, 2, 1 in plane order, a width present when it is a plane of b).
 __host__ __device__ inline uint32_t kvq_k_code(const uint8_t *kcodes, int b, int n, int ch) {
   uint32_t c = 0;
-  for (int p = 0; p < kvq_nplanes(b); ++p) {
-    const int w = kvq_plane_width(b, p);
-    int off, bit;
-    kvq_k_code_pos(w, n, ch, &off, &bit);
-    const uint32_t word = *reinterpret_cast<const uint32_t *>(kcodes + 256 * kvq_plane_off(b, p) + off);
-    c |= ((word >> bit) & ((1u << w) - 1u)) << kvq_plane_off(b, p);
+  int sh = 0;
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) {
+    if (b == 8 ? w == 8 : (w < 8 && (b & w) != 0)) {
+      int off, bit;
+      kvq_k_code_pos(w, n, ch, &off, &bit);
+      const uint32_t word = *reinterpret_cast<const uint32_t *>(kcodes + 256 * sh + off);
+      c |= ((word >> bit) & ((1u << w) - 1u)) << sh;
+      sh += w;
+    }
   }
   return c;
 }
@@ -123,14 +128,63 @@ __host__ __device__ inline uint32_t kvq_k_code(const uint8_t *kcodes, int b, int
 // The b-bit V code of (token tt, channel ch) from a record's V code area (all planes).
 __host__ __device__ inline uint32_t kvq_v_code(const uint8_t *vcodes, int b, int tt, int ch) {
   uint32_t c = 0;
-  for (int p = 0; p < kvq_nplanes(b); ++p) {
-    const int w = kvq_plane_width(b, p);
-    int off, bit;
-    kvq_v_code_pos(w, tt, ch, &off, &bit);
-    const uint32_t word = *reinterpret_cast<const uint32_t *>(vcodes + 256 * kvq_plane_off(b, p) + off);
-    c |= ((word >> bit) & ((1u << w) - 1u)) << kvq_plane_off(b, p);
+  int sh = 0;
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) {
+    if (b == 8 ? w == 8 : (w < 8 && (b & w) != 0)) {
+      int off, bit;
+      kvq_v_code_pos(w, tt, ch, &off, &bit);
+      const uint32_t word = *reinterpret_cast<const uint32_t *>(vcodes + 256 * sh + off);
+      c |= ((word >> bit) & ((1u << w) - 1u)) << sh;
+      sh += w;
+    }
   }
   return c;
+}
+
+// The b-bit K codes of channels [8c, 8c + 8) of token n (c < 16) from a record's K code area, one
+// bit plane at a time: in each plane of width up to 4 they sit in one word of slot 16 (c mod 4) + n
+// (two words at width 8).
+__host__ __device__ inline void kvq_k_codes8(const uint8_t *kcodes, int b, int n, int c, uint32_t code[8]) {
+  for (int e = 0; e < 8; ++e) code[e] = 0;
+  const int kc = c >> 2, j = c & 3;
+  int sh = 0;
+#pragma unroll 1
+  for (int lw = 3; lw >= 0; --lw) {
+    const int w = 1 << lw;
+    if (!(b == 8 ? w == 8 : (w < 8 && (b & w) != 0))) continue;  // not a plane of b
+    const int lper = 4 - lw;  // log2 of the channel pairs per word
+    const uint32_t mask = (1u << w) - 1u;
+    const uint32_t *slot = reinterpret_cast<const uint32_t *>(kcodes + 256 * sh + (16 * j + n) * 4 * w);
+    const uint32_t wa = slot[(4 * kc) >> lper], wb = slot[(4 * kc + 2) >> lper];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int u = 4 * kc + (e >> 1);
+      const uint32_t word = (e >> 2) ? wb : wa;
+      code[e] |= ((word >> (16 * (e & 1) + w * (u & ((1 << lper) - 1)))) & mask) << sh;
+    }
+    sh += w;
+  }
+}
+
+// The b-bit V codes of channels [8c, 8c + 8) of token tt (c < 16) from a record's V code area, one
+// bit plane at a time: in each plane they sit in the same word of value slots 16 (tt / 4) + 8 (c
+// mod 2) + e, e = 0..7.
+__host__ __device__ inline void kvq_v_codes8(const uint8_t *vcodes, int b, int tt, int c, uint32_t code[8]) {
+  for (int e = 0; e < 8; ++e) code[e] = 0;
+  const int jj = tt >> 2, i = (tt & 3) >> 1, h = tt & 1, m = c >> 1;
+  int sh = 0;
+#pragma unroll 1
+  for (int lw = 3; lw >= 0; --lw) {
+    const int w = 1 << lw;
+    if (!(b == 8 ? w == 8 : (w < 8 && (b & w) != 0))) continue;  // not a plane of b
+    const uint32_t mask = (1u << w) - 1u;
+    const int p = i * 8 * w + m * w, bit = 16 * h + (p & 15);
+    const uint8_t *base = vcodes + 256 * sh + (16 * jj + 8 * (c & 1)) * 4 * w + 4 * (p >> 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) code[e] |= ((*reinterpret_cast<const uint32_t *>(base + e * 4 * w) >> bit) & mask) << sh;
+    sh += w;
+  }
 }
 
 __host__ __device__ inline int kvq_meta_dword(int ngroups, int tt, int grp) { return tt * ngroups + grp; }

@@ -96,8 +96,11 @@ __device__ inline void quantize_pair(double x0, double x1, int bits, int G, uint
 __device__ inline void kvq_write_token(uint8_t *rec, const KvqLayout &lay, int n, const uint8_t *ck,
                                        const uint8_t *cv, const uint32_t *mk, const uint32_t *mv, int lane) {
   // K codes: per plane, 4 slots (octets j) x w words.
-  for (int pl = 0; pl < kvq_nplanes(lay.kb); ++pl) {
-    const int w = kvq_plane_width(lay.kb, pl), sh = kvq_plane_off(lay.kb, pl), per = 16 / w;
+  int sh = 0;  // bit offset of the plane in the code (its area's offset / 256)
+#pragma unroll 1
+  for (int w = 8; w >= 1; w >>= 1) {
+    if (!(lay.kb == 8 ? w == 8 : (w < 8 && (lay.kb & w) != 0))) continue;  // not a plane of kb
+    const int per = 16 / w;
     const uint32_t mask = (1u << w) - 1u;
     if (lane < 4 * w) {
       const int j = lane / w, wi = lane % w;
@@ -110,11 +113,14 @@ __device__ inline void kvq_write_token(uint8_t *rec, const KvqLayout &lay, int n
       }
       *reinterpret_cast<uint32_t *>(rec + lay.k_codes_off + 256 * sh + (16 * j + n) * 4 * w + 4 * wi) = word;
     }
+    sh += w;
   }
   // V codes: per plane, 16 slots; each token owns half-words (or one byte at width 1) of its slot.
   const int jj = n >> 2, r = n & 3, ii = r >> 1, hh = r & 1;
-  for (int pl = 0; pl < kvq_nplanes(lay.vb); ++pl) {
-    const int w = kvq_plane_width(lay.vb, pl), sh = kvq_plane_off(lay.vb, pl);
+  sh = 0;
+#pragma unroll 1
+  for (int w = 8; w >= 1; w >>= 1) {
+    if (!(lay.vb == 8 ? w == 8 : (w < 8 && (lay.vb & w) != 0))) continue;  // not a plane of vb
     const uint32_t mask = (1u << w) - 1u;
     uint8_t *vbase = rec + lay.v_codes_off + 256 * sh;
     if (w == 1) {
@@ -136,6 +142,7 @@ __device__ inline void kvq_write_token(uint8_t *rec, const KvqLayout &lay, int n
         *reinterpret_cast<uint16_t *>(vbase + (16 * jj + c16) * 4 * w + 4 * wi + 2 * hh) = (uint16_t)half;
       }
     }
+    sh += w;
   }
   // Metadata.
   if (lane < lay.nkg)

@@ -91,17 +91,13 @@ __global__ __launch_bounds__(64) void kvq_dequantize_dense_kernel(KvqDenseArgs a
         const uint32_t vm = reinterpret_cast<const uint32_t *>(rs + lay.v_meta_off)[kvq_meta_dword(lay.nvg, n, (8 * c8) / lay.vg)];
         const float kz = f16_bits_to_f32(km >> 16), ks = f16_bits_to_f32(km & 0xFFFF);
         const float vz = f16_bits_to_f32(vm >> 16), vs = f16_bits_to_f32(vm & 0xFFFF);
+        uint32_t kc[8], vc[8];
+        kvq_k_codes8(rs + lay.k_codes_off, lay.kb, n, c8, kc);
+        kvq_v_codes8(rs + lay.v_codes_off, lay.vb, n, c8, vc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t kc[2], vc[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int ch = 8 * c8 + 2 * i + e;
-            kc[e] = kvq_k_code(rs + lay.k_codes_off, lay.kb, n, ch);
-            vc[e] = kvq_v_code(rs + lay.v_codes_off, lay.vb, n, ch);
-          }
-          ko[i] = affine_bf16(kz, ks, kc[0]) | (affine_bf16(kz, ks, kc[1]) << 16);
-          vo[i] = affine_bf16(vz, vs, vc[0]) | (affine_bf16(vz, vs, vc[1]) << 16);
+          ko[i] = affine_bf16(kz, ks, kc[2 * i]) | (affine_bf16(kz, ks, kc[2 * i + 1]) << 16);
+          vo[i] = affine_bf16(vz, vs, vc[2 * i]) | (affine_bf16(vz, vs, vc[2 * i + 1]) << 16);
         }
       } else if (t < wstart) {  // beyond the cache: not stored
 #pragma unroll
