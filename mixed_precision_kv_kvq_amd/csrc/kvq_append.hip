@@ -276,36 +276,60 @@ __device__ void page_item(const KvqAppendArgs &a, int pidx, int h, int b, uint32
     }
     const GroupMeta g = group_meta(mn, mx, lay.kb);
     const float r32 = 1.0f / (float)g.sf, qmax32 = (float)g.qmax;  // fp16 scale: exact in fp32
+    if ((lay.kb & (lay.kb - 1)) == 0) {
+      // a single-plane width: the octet's channel pairs u = 4q + i fill word u / per of slot
+      // 16 jo + t: one word for widths up to 4, two at 8; the codes are gathered per word
+      // before one OR
+      const int kb = lay.kb, per = 16 / kb;
+      uint32_t *kw = rw + lay.k_codes_off / 4;
 #pragma unroll
-    for (int jo = 0; jo < 4; ++jo) {      // channel octet within the chunk
-      uint32_t c[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = group_code_fast(x[8 * jo + e], g, r32, qmax32);
-      // per bit plane (width w, bits [sh, sh + w) of the codes): the octet's channel pairs
-      // u = 4q + i fill word u / (16 / w) of slot 16 jo + t in the plane's area: one word for
-      // widths up to 4, two at 8; the plane values are gathered per word before one OR
-      int sh = 0;
-#pragma unroll
-      for (int w = 8; w >= 1; w >>= 1) {
-        if (!(lay.kb == 8 ? w == 8 : (w < 8 && (lay.kb & w) != 0))) continue;  // not a plane of kb
-        const int per = 16 / w;
-        const uint32_t mask = (1u << w) - 1u;
-        uint32_t *kw = rw + (lay.k_codes_off + 256 * sh) / 4;
+      for (int jo = 0; jo < 4; ++jo) {      // channel octet within the chunk
         uint32_t acc = 0;
         int wcur = (4 * q) / per;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {       // channel pair within the octet
+          const uint32_t c0 = group_code_fast(x[8 * jo + 2 * i], g, r32, qmax32);
+          const uint32_t c1 = group_code_fast(x[8 * jo + 2 * i + 1], g, r32, qmax32);
           const int u = 4 * q + i;
           if (u / per != wcur) {
-            atomicOr(kw + (16 * jo + t) * w + wcur, acc);
+            atomicOr(kw + (16 * jo + t) * kb + wcur, acc);
             acc = 0;
             wcur = u / per;
           }
-          acc |= (((c[2 * i] >> sh) & mask) << (w * (u % per))) |
-                 (((c[2 * i + 1] >> sh) & mask) << (16 + w * (u % per)));
+          acc |= (c0 << (kb * (u % per))) | (c1 << (16 + kb * (u % per)));
         }
-        atomicOr(kw + (16 * jo + t) * w + wcur, acc);
-        sh += w;
+        atomicOr(kw + (16 * jo + t) * kb + wcur, acc);
+      }
+    } else {
+      // bit planes: the same per plane (width w, bits [sh, sh + w) of the codes) in its area
+#pragma unroll
+      for (int jo = 0; jo < 4; ++jo) {
+        uint32_t c[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = group_code_fast(x[8 * jo + e], g, r32, qmax32);
+        int sh = 0;
+#pragma unroll
+        for (int w = 4; w >= 1; w >>= 1) {
+          if ((lay.kb & w) == 0) continue;  // not a plane of kb
+          const int per = 16 / w;
+          const uint32_t mask = (1u << w) - 1u;
+          uint32_t *kw = rw + (lay.k_codes_off + 256 * sh) / 4;
+          uint32_t acc = 0;
+          int wcur = (4 * q) / per;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int u = 4 * q + i;
+            if (u / per != wcur) {
+              atomicOr(kw + (16 * jo + t) * w + wcur, acc);
+              acc = 0;
+              wcur = u / per;
+            }
+            acc |= (((c[2 * i] >> sh) & mask) << (w * (u % per))) |
+                   (((c[2 * i + 1] >> sh) & mask) << (16 + w * (u % per)));
+          }
+          atomicOr(kw + (16 * jo + t) * w + wcur, acc);
+          sh += w;
+        }
       }
     }
     const int grp = (32 * q) / lay.kg;
@@ -333,19 +357,31 @@ __device__ void page_item(const KvqAppendArgs &a, int pidx, int h, int b, uint32
     const int jj = t >> 2, r = t & 3, iv = r >> 1, hv = r & 1;
     // channels 32 q + e and 32 q + 16 + e (tiles 2q and 2q + 1, same column) share a word of
     // every plane area for every width: one OR per plane for both codes
+    if ((lay.vb & (lay.vb - 1)) == 0) {  // a single-plane width
+      const int vb = lay.vb;
+      uint32_t *vw = rw + lay.v_codes_off / 4;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t c0 = group_code_fast(x[e], g, r32, qmax32), c1 = group_code_fast(x[e + 16], g, r32, qmax32);
-      int sh = 0;
+      for (int e = 0; e < 16; ++e) {
+        const int m0 = 2 * q, pos0 = iv * 8 * vb + m0 * vb, pos1 = pos0 + vb;
+        const uint32_t bits = (group_code_fast(x[e], g, r32, qmax32) << (16 * hv + (pos0 & 15))) |
+                              (group_code_fast(x[e + 16], g, r32, qmax32) << (16 * hv + (pos1 & 15)));
+        atomicOr(vw + (16 * jj + e) * vb + (pos0 >> 4), bits);
+      }
+    } else {
 #pragma unroll
-      for (int w = 8; w >= 1; w >>= 1) {
-        if (!(lay.vb == 8 ? w == 8 : (w < 8 && (lay.vb & w) != 0))) continue;  // not a plane of vb
-        const uint32_t mask = (1u << w) - 1u;
-        const int m0 = 2 * q, pos0 = iv * 8 * w + m0 * w, pos1 = pos0 + w;
-        const uint32_t bits = (((c0 >> sh) & mask) << (16 * hv + (pos0 & 15))) |
-                              (((c1 >> sh) & mask) << (16 * hv + (pos1 & 15)));
-        atomicOr(rw + (lay.v_codes_off + 256 * sh) / 4 + (16 * jj + e) * w + (pos0 >> 4), bits);
-        sh += w;
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t c0 = group_code_fast(x[e], g, r32, qmax32), c1 = group_code_fast(x[e + 16], g, r32, qmax32);
+        int sh = 0;
+#pragma unroll
+        for (int w = 4; w >= 1; w >>= 1) {
+          if ((lay.vb & w) == 0) continue;  // not a plane of vb
+          const uint32_t mask = (1u << w) - 1u;
+          const int m0 = 2 * q, pos0 = iv * 8 * w + m0 * w, pos1 = pos0 + w;
+          const uint32_t bits = (((c0 >> sh) & mask) << (16 * hv + (pos0 & 15))) |
+                                (((c1 >> sh) & mask) << (16 * hv + (pos1 & 15)));
+          atomicOr(rw + (lay.v_codes_off + 256 * sh) / 4 + (16 * jj + e) * w + (pos0 >> 4), bits);
+          sh += w;
+        }
       }
     }
     const int grp = (32 * q) / lay.vg;

@@ -146,8 +146,8 @@ __host__ __device__ inline uint32_t kvq_v_code(const uint8_t *vcodes, int b, int
 // bit plane at a time: in each plane of width up to 4 they sit in one word of slot 16 (c mod 4) + n
 // (two words at width 8).
 __host__ __device__ inline void kvq_k_codes8(const uint8_t *kcodes, int b, int n, int c, uint32_t code[8]) {
-  for (int e = 0; e < 8; ++e) code[e] = 0;
   const int kc = c >> 2, j = c & 3;
+  for (int e = 0; e < 8; ++e) code[e] = 0;
   int sh = 0;
 #pragma unroll 1
   for (int lw = 3; lw >= 0; --lw) {
@@ -171,8 +171,8 @@ __host__ __device__ inline void kvq_k_codes8(const uint8_t *kcodes, int b, int n
 // bit plane at a time: in each plane they sit in the same word of value slots 16 (tt / 4) + 8 (c
 // mod 2) + e, e = 0..7.
 __host__ __device__ inline void kvq_v_codes8(const uint8_t *vcodes, int b, int tt, int c, uint32_t code[8]) {
-  for (int e = 0; e < 8; ++e) code[e] = 0;
   const int jj = tt >> 2, i = (tt & 3) >> 1, h = tt & 1, m = c >> 1;
+  for (int e = 0; e < 8; ++e) code[e] = 0;
   int sh = 0;
 #pragma unroll 1
   for (int lw = 3; lw >= 0; --lw) {
@@ -185,6 +185,25 @@ __host__ __device__ inline void kvq_v_codes8(const uint8_t *vcodes, int b, int t
     for (int e = 0; e < 8; ++e) code[e] |= ((*reinterpret_cast<const uint32_t *>(base + e * 4 * w) >> bit) & mask) << sh;
     sh += w;
   }
+}
+
+// The same for a single-plane width b (1, 2, 4 or 8): no plane offsets to apply.
+__host__ __device__ inline void kvq_k_codes8_one(const uint8_t *kcodes, int b, int n, int c, uint32_t code[8]) {
+  const int kc = c >> 2, j = c & 3, per = 16 / b;
+  const uint32_t mask = (1u << b) - 1u;
+  const uint32_t *slot = reinterpret_cast<const uint32_t *>(kcodes + (16 * j + n) * 4 * b);
+  const uint32_t wa = slot[(4 * kc) / per], wb = slot[(4 * kc + 2) / per];
+  for (int e = 0; e < 8; ++e) {
+    const int u = 4 * kc + (e >> 1);
+    code[e] = (((e >> 2) ? wb : wa) >> (16 * (e & 1) + b * (u % per))) & mask;
+  }
+}
+__host__ __device__ inline void kvq_v_codes8_one(const uint8_t *vcodes, int b, int tt, int c, uint32_t code[8]) {
+  const int jj = tt >> 2, i = (tt & 3) >> 1, h = tt & 1, m = c >> 1;
+  const uint32_t mask = (1u << b) - 1u;
+  const int p = i * 8 * b + m * b, bit = 16 * h + (p & 15);
+  const uint8_t *base = vcodes + (16 * jj + 8 * (c & 1)) * 4 * b + 4 * (p >> 4);
+  for (int e = 0; e < 8; ++e) code[e] = (*reinterpret_cast<const uint32_t *>(base + e * 4 * b) >> bit) & mask;
 }
 
 __host__ __device__ inline int kvq_meta_dword(int ngroups, int tt, int grp) { return tt * ngroups + grp; }

@@ -92,8 +92,14 @@ __global__ __launch_bounds__(64) void kvq_dequantize_dense_kernel(KvqDenseArgs a
         const float kz = f16_bits_to_f32(km >> 16), ks = f16_bits_to_f32(km & 0xFFFF);
         const float vz = f16_bits_to_f32(vm >> 16), vs = f16_bits_to_f32(vm & 0xFFFF);
         uint32_t kc[8], vc[8];
-        kvq_k_codes8(rs + lay.k_codes_off, lay.kb, n, c8, kc);
-        kvq_v_codes8(rs + lay.v_codes_off, lay.vb, n, c8, vc);
+        if ((lay.kb & (lay.kb - 1)) == 0)
+          kvq_k_codes8_one(rs + lay.k_codes_off, lay.kb, n, c8, kc);
+        else
+          kvq_k_codes8(rs + lay.k_codes_off, lay.kb, n, c8, kc);
+        if ((lay.vb & (lay.vb - 1)) == 0)
+          kvq_v_codes8_one(rs + lay.v_codes_off, lay.vb, n, c8, vc);
+        else
+          kvq_v_codes8(rs + lay.v_codes_off, lay.vb, n, c8, vc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ko[i] = affine_bf16(kz, ks, kc[2 * i]) | (affine_bf16(kz, ks, kc[2 * i + 1]) << 16);
