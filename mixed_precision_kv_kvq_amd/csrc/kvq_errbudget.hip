@@ -94,85 +94,248 @@ __device__ __attribute__((always_inline)) inline void pair_wht(float &x0, float 
   x1 *= (float)KVQ_WHT_C;
 }
 
+// The bit planes of a code width b (1..6 or 8), widest first: at most two (w1 = 0: one plane).
+// Plane 0 sits at offset 0 of a code area with its fields at bit 0 of the code; plane 1 at byte
+// 256 w0 with its fields at bit w0.
+struct EbPlanes {
+  int w0, w1;
+};
+__device__ __forceinline__ EbPlanes eb_planes(int b) {
+  const int w0 = b == 8 ? 8 : (b >= 4 ? 4 : (b >= 2 ? 2 : 1));
+  return {w0, b - w0};
+}
+// Both 16-bit halves of pair slot u of a slot of one plane (width w, the slot's bytes at s): the
+// w-bit fields at bit u w mod 16 of word u w / 16 of each half, moved to bit 0.
+__device__ __forceinline__ uint32_t plane_pair(const uint8_t *s, int u, int w) {
+  const int bit = u * w;
+  const uint32_t word = *reinterpret_cast<const uint32_t *>(s + 4 * (bit >> 4));
+  return (word >> (bit & 15)) & (((1u << w) - 1u) * 0x00010001u);
+}
+// Pair slot u of slot `slot` of a code area, both planes combined: two codes, one per 16-bit half.
+// K: slot 16 j + n holds token n's channel octet j of each 32-channel chunk kc, pair slot
+// u = 4 kc + i its channels 32 kc + 8 j + 2 i (low half) and + 1 (high half).  V: slot 16 jj + c16
+// holds channel 16 m + c16 of tokens 4 jj .. 4 jj + 3, pair slot u = 8 i + m its tokens 4 jj + 2 i
+// (low half) and + 1 (high half).
+__device__ __forceinline__ uint32_t eb_pair(const uint8_t *area, int slot, int u, EbPlanes P) {
+  uint32_t v = plane_pair(area + slot * 4 * P.w0, u, P.w0);
+  if (P.w1) v |= plane_pair(area + 256 * P.w0 + slot * 4 * P.w1, u, P.w1) << P.w0;
+  return v;
+}
+
 // The reconstruction of 8 channels [8c, 8c + 8) of token n of a page record staged in LDS (keys
 // or values), as zero + code * scale in fp32.
 template <bool KEYS>
-__device__ __attribute__((always_inline)) inline void decode8(const KvqLayout &lay, const uint8_t *rs, int n, int c,
-                                                              float *xh) {
+__device__ __attribute__((always_inline)) inline void decode8(const KvqLayout &lay, EbPlanes P, const uint8_t *rs,
+                                                              int n, int c, float *xh) {
   const uint32_t m = reinterpret_cast<const uint32_t *>(rs + (KEYS ? lay.k_meta_off : lay.v_meta_off))
       [kvq_meta_dword(KEYS ? lay.nkg : lay.nvg, n, (8 * c) / (KEYS ? lay.kg : lay.vg))];
   const float zero = f16f(m >> 16), scale = f16f(m & 0xFFFF);
   uint32_t code[8];
-  if (KEYS)
-    kvq_k_codes8(rs + lay.k_codes_off, lay.kb, n, c, code);
-  else
-    kvq_v_codes8(rs + lay.v_codes_off, lay.vb, n, c, code);
+  if (KEYS) {  // channels 8 c + 2 i, + 1: pair slot 4 (c / 4) + i of slot 16 (c mod 4) + n
+    const uint8_t *area = rs + lay.k_codes_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = eb_pair(area, 16 * (c & 3) + n, 4 * (c >> 2) + i, P);
+      code[2 * i] = v & 0xFFFFu;
+      code[2 * i + 1] = v >> 16;
+    }
+  } else {  // channel 8 c + e: slot 16 (n / 4) + 8 (c mod 2) + e, pair slot 8 ((n mod 4) / 2) + c / 2
+    const uint8_t *area = rs + lay.v_codes_off;
+    const int hs = 16 * (n & 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      code[e] = (eb_pair(area, 16 * (n >> 2) + 8 * (c & 1) + e, 8 * ((n & 3) >> 1) + (c >> 1), P) >> hs) & 0xFFFFu;
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) xh[e] = zero + (float)code[e] * scale;
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef short eb_s8 __attribute__((__vector_size__(8 * sizeof(short))));  // 8 bf16: 16x16x32 operand
+typedef short eb_s4 __attribute__((ext_vector_type(4)));                   // 4 bf16: 16x16x16 operand
+typedef float eb_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t eb_u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t eb_u2 __attribute__((ext_vector_type(2)));
+typedef __bf16 eb_bf2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  eb_bf2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ eb_s8 pack8s(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+  eb_u4 u;
+  u[0] = a0;
+  u[1] = a1;
+  u[2] = a2;
+  u[3] = a3;
+  return __builtin_bit_cast(eb_s8, u);
+}
+__device__ __forceinline__ eb_s4 pack4s(uint32_t a0, uint32_t a1) {
+  eb_u2 u;
+  u[0] = a0;
+  u[1] = a1;
+  return __builtin_bit_cast(eb_s4, u);
+}
+__device__ __forceinline__ float bf_lo(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }
+// hi and lo bf16 parts of two fp32 values (x = hi + lo to about 2^-16 relative)
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = pk_bf16(x0, x1);
+  lo = pk_bf16(x0 - bf_lo(hi), x1 - bf_hi(hi));
+}
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+  for (int sh = 8; sh >= 1; sh >>= 1) v = __builtin_fmaxf(v, row_ror(v, sh));
+  return v;
+}
+
+// A code of b bits read as a bf16 bit pattern is code * 2^-133 (c < 256).
+
 constexpr int EB_WAVES = 8;
 constexpr int EB_REC16 = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 16;  // largest record, 16-byte units
-template <int HG>
+constexpr float EB_Q = 0x1p100f;  // query operand scale
+
+// One workgroup of EB_WAVES waves per (group of HS <= 2 query heads of one kv head, sequence); the
+// head groups of a kv head run on workgroups 8 apart (one XCD), so the second to read a page finds
+// it in that XCD's L2.  Wave w takes pages w, w + EB_WAVES, ...: a page's original rows and record
+// are loaded while the wave computes the page before, then stored to the wave's LDS region.
+//
+// Scores on MFMA (16x16x32 bf16): the query, scaled by 2^100 and split into bf16 hi and lo parts,
+// is the A operand (row 4 hs + j: head hs restricted to 32-channel chunk j); the B operand is the
+// page's original keys (exact bf16) for the exact scores and its key codes (code * 2^-133) for the
+// quantized ones, so D row 4 q + r of lane 16 q + t holds head q's dot with chunk r of token t.
+// The quantized score applies the token's group scales and zero points:
+// s' = sum_r scale_r (q . c)_r + sum_g zero_g sum(q over g).  With rotated keys the code scores
+// use the rotated query (the normalized transform is orthogonal); window tokens are stored exact
+// (s' = s).  Lane 16 q + t then holds both scores of token t for head q.
+//
+// Pass 1: online maxima and sums of both score sets (log2 units) and the score-error statistics,
+// merged over the 16 lanes of a head and the waves.  Pass 2: the weights a (exact keys) and a'
+// (quantized keys), their total variation, and the four weighted sums on MFMA (16x16x16 bf16,
+// k = the page's 16 tokens): A rows 8 set + 4 part + q hold the weights of set a / a' (hi and lo
+// parts) of head q, through a per-wave LDS exchange buffer; B is the original values (exact bf16:
+// a V, a' V) or the value codes (a V_hat, a' V_hat; A = weight * scale * 2^64, window tokens take
+// their exact values as B with A = weight * 2^-69, so every product carries 2^-69), plus the
+// weighted zero points.  The first head group of each kv head also accumulates the reconstruction
+// errors (per element, 8 channels per lane).
+template <int HS>
 __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs a) {
-  __shared__ float red[EB_WAVES][6 * HG];
+  __shared__ float red[EB_WAVES][6 * HS];
   __shared__ float ured[EB_WAVES][6];
-  __shared__ float accs[4][HG][KVQ_D];
-  __shared__ uint4 recs[EB_WAVES][2][EB_REC16];  // page records (two: the next one lands meanwhile)
+  __shared__ float accs[4][HS][KVQ_D];
+  __shared__ float qs[2][HS][KVQ_D];      // the group's queries: raw, and the one the codes are scored with
+  __shared__ float qg[HS][4];             // sums of the code query over each key group
+  __shared__ float zred[EB_WAVES][2][HS][2];  // weighted zero points (set, head, value group)
+  __shared__ float tvred[EB_WAVES][HS];
+  __shared__ uint4 recs[EB_WAVES][2][EB_REC16];       // page records (two: the next one lands meanwhile)
   __shared__ uint4 rows[EB_WAVES][2][KVQ_PAGE * 16];  // the page's original K and V rows
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = lane >> 4, c = lane & 15;
-  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, ngrp = g / HG;
+  __shared__ uint32_t xbuf[EB_WAVES][3][16][8];        // value A operands: [raw, code v0, code v1][row][16 bf16]
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: page loop and record addresses in SGPRs
+  const int r = lane >> 4, c = lane & 15;       // element layout: row r, 8 channels [8c, 8c + 8)
+  const int q = lane >> 4, t = lane & 15;       // score layout: head q, token t
+  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, ngrp = g / HS;
   // workgroup -> (unit, head group): the groups of unit u at blocks 8 ngrp (u / 8) + 8 grp + u mod 8
   const int blk = blockIdx.x / (8 * ngrp), rem = blockIdx.x % (8 * ngrp);
   const int grp = rem / 8, unit = 8 * blk + rem % 8;
   if (unit >= a.B * Hkv) return;  // padding of the last group of 8 units
   const int b = unit / Hkv, h = unit % Hkv;
-  const int hq0 = h * g + grp * HG;  // first query head of the group
+  const int hq0 = h * g + grp * HS;  // first query head of the group
   const bool unit_lead = grp == 0;
-  int64_t L = a.seq_lens[b];
-  kvq_raise(a.cache, hq0 == 0 && (L < 0 || L > a.max_len), KVQ_DEV_LENGTH);
-  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
-  int64_t nq = L > a.R ? L - a.R : 0;
+  int L = (int)a.seq_lens[b];
+  kvq_raise(a.cache, hq0 == 0 && (L < 0 || (int64_t)L > a.max_len), KVQ_DEV_LENGTH);
+  L = L < 0 ? 0 : ((int64_t)L > a.max_len ? (int)a.max_len : L);
+  int nq = L > a.R ? L - a.R : 0;
   const int64_t cap_tokens = (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq) * KVQ_PAGE;
-  if (nq > cap_tokens) nq = cap_tokens;
+  if ((int64_t)nq > cap_tokens) nq = (int)cap_tokens;
   const float ninf = -__builtin_inff();
   const KvqLayout &lay = a.lay;
   const int rec16 = lay.record / 16;
+  const EbPlanes KP = eb_planes(lay.kb), VP = eb_planes(lay.vb);
+  const bool qlive = q < HS;  // score-layout lanes of a head of the group
 
-  float q[HG][8];
-#pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    const size_t qrow = ((size_t)b * a.Hq + hq0 + j) * KVQ_D + 8 * c;
-    if (a.q_f32) {
-      const float4 *qp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow);
-      const float4 x = qp[0], y = qp[1];
-      q[j][0] = x.x; q[j][1] = x.y; q[j][2] = x.z; q[j][3] = x.w;
-      q[j][4] = y.x; q[j][5] = y.y; q[j][6] = y.z; q[j][7] = y.w;
+  // ---- queries: raw and code-scoring (rotated when keys are) rows, and the group sums ----
+  for (int i = threadIdx.x; i < 3 * 16 * 8 * EB_WAVES; i += 64 * EB_WAVES)
+    (&xbuf[0][0][0][0])[i] = 0u;  // rows of heads beyond HS stay zero
+  for (int i = threadIdx.x; i < 4 * HS * KVQ_D; i += 64 * EB_WAVES) (&accs[0][0][0])[i] = 0.f;
+  if (w == 0) {
+    float x[8];
+    if (r < HS) {
+      const size_t qrow = ((size_t)b * a.Hq + hq0 + r) * KVQ_D + 8 * c;
+      if (a.q_f32) {
+        const float4 *qp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow);
+        const float4 u0 = qp[0], u1 = qp[1];
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+      } else {
+        bf16x8(*reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qrow), x);
+      }
     } else {
-      bf16x8(*reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + qrow), q[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    float xr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xr[e] = x[e];
+    row_wht(xr, c, a.rotation != 0);  // every lane takes part
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part += xr[e];
+    // sum over the lanes of one key group (kg / 8 lanes: 4, 8 or 16)
+    for (int sh = 1; sh < lay.kg / 8; sh <<= 1) part += __shfl_xor(part, sh);
+    if (r < HS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qs[0][r][8 * c + e] = x[e];
+        qs[1][r][8 * c + e] = xr[e];
+      }
+      if ((8 * c) % lay.kg == 0) qg[r][(8 * c) / lay.kg] = part;
     }
   }
+  __syncthreads();
+  // A operands of the score contractions: row 4 hs + j = head hs restricted to chunk j, so the
+  // operand of chunk kc is the lane's data where kc = j and zero elsewhere (applied per page).
+  // qd[set][part]: set 0 the raw query, 1 the code-scoring one; parts hi and lo (lo = 0 for a bf16
+  // query scored against unrotated codes).
+  eb_u4 qd[2][2];
+  float qgl[4];
+  const int jrow = lane & 3;  // the chunk of the lane's A row
+  const bool lo0 = a.q_f32 != 0, lo1 = a.q_f32 != 0 || a.rotation != 0;
+  {
+    const int rho = lane & 15, hs = rho >> 2, oct = lane >> 4;
+#pragma unroll
+    for (int set = 0; set < 2; ++set) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v0 = hs < HS ? qs[set][hs < HS ? hs : 0][32 * jrow + 8 * oct + 2 * i] * EB_Q : 0.f;
+        const float v1 = hs < HS ? qs[set][hs < HS ? hs : 0][32 * jrow + 8 * oct + 2 * i + 1] * EB_Q : 0.f;
+        uint32_t hi, lo;
+        split2(v0, v1, hi, lo);
+        qd[set][0][i] = hi;
+        qd[set][1][i] = lo;
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) qgl[gi] = (qlive && gi < lay.nkg) ? qg[qlive ? q : 0][gi] : 0.f;
+  }
+
   // This lane's 16 bytes (8 channels) of original row t (t < L; callers pass a valid t).
-  auto ref8 = [&](const uint16_t *base, int64_t t) {
-    return *reinterpret_cast<const uint4 *>(base + (((size_t)b * a.max_len + (size_t)t) * Hkv + h) * KVQ_D + 8 * c);
+  auto ref8 = [&](const uint16_t *base, int tt) {
+    return *reinterpret_cast<const uint4 *>(base + (((size_t)b * a.max_len + (size_t)tt) * Hkv + h) * KVQ_D + 8 * c);
   };
-  // One page's original rows in flight: the lane's 16 bytes of the K (and V) rows of positions
-  // 4 i + r, loaded for the next page before the current one is computed, then stored to the
-  // wave's LDS region (positions past L re-read row L - 1).  The page record goes straight to LDS
-  // (buffer loads to LDS, one lane per 16-byte chunk) into the other of the wave's two record
-  // buffers; an explicit wait for all of the wave's loads precedes each page.
   struct PageRegs {
     uint4 k[4], v[4];
   };
-  auto load_rows = [&](int64_t pg, PageRegs &pr, bool with_v) __attribute__((always_inline)) {
-    const int64_t t0 = pg * KVQ_PAGE;
+  auto load_rows = [&](int pg, PageRegs &pr, bool with_v) __attribute__((always_inline)) {
+    const int t0 = pg * KVQ_PAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + 4 * i + r < L ? t0 + 4 * i + r : L - 1;
-      pr.k[i] = ref8(a.k_ref, t);
-      if (with_v) pr.v[i] = ref8(a.v_ref, t);
+      const int tt = t0 + 4 * i + r < L ? t0 + 4 * i + r : L - 1;
+      pr.k[i] = ref8(a.k_ref, tt);
+      if (with_v) pr.v[i] = ref8(a.v_ref, tt);
     }
   };
   auto store_rows = [&](const PageRegs &pr, bool with_v) __attribute__((always_inline)) {
@@ -182,7 +345,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       if (with_v) rows[w][1][(4 * i + r) * 16 + c] = pr.v[i];
     }
   };
-  auto load_rec = [&](int64_t pg, int buf) __attribute__((always_inline)) {
+  auto load_rec = [&](int pg, int buf) __attribute__((always_inline)) {
     if (pg * KVQ_PAGE >= nq) return;  // no quantized position on this page
     const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, b, h, pg);
     const __amdgpu_buffer_rsrc_t rsrc =
@@ -197,15 +360,51 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     }
   };
   const float sl2 = a.scale * 1.4426950408889634f;  // softmax scale in log2 units
-  const int64_t npages = (L + KVQ_PAGE - 1) / KVQ_PAGE;
+  const int npages = (L + KVQ_PAGE - 1) / KVQ_PAGE;
+  const uint8_t *krow = reinterpret_cast<const uint8_t *>(rows[w][0]);
+  const uint8_t *vrow = reinterpret_cast<const uint8_t *>(rows[w][1]);
+
+  // Exact and quantized dots (in dot units, no softmax scale) of token t of page t0 for head q.
+  auto page_scores = [&](const uint8_t *rs, int t0, float &s0, float &s1) __attribute__((always_inline)) {
+    eb_f4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+    const int n = lane & 15, oct = lane >> 4;  // B operand: token n, channel octet oct of each chunk
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      uint32_t mk = kc == jrow ? ~0u : 0u;
+      asm volatile("" : "+v"(mk));  // keeps the masked operands in the loop (no 48 registers of zeros)
+      const eb_u4 kv = *reinterpret_cast<const eb_u4 *>(krow + n * 256 + (32 * kc + 8 * oct) * 2);
+      const eb_s8 bk = __builtin_bit_cast(eb_s8, kv);
+      D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][0] & mk), bk, D0, 0, 0, 0);
+      if (lo0) D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][1] & mk), bk, D0, 0, 0, 0);
+    }
+    s0 = (D0[0] + D0[1] + D0[2] + D0[3]) * 0x1p-100f;
+    s1 = s0;
+    if (t0 < nq) {  // the page holds quantized tokens
+      const uint8_t *kcodes = rs + lay.k_codes_off;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        uint32_t mk = kc == jrow ? ~0u : 0u;
+        asm volatile("" : "+v"(mk));
+        const eb_s8 bc = pack8s(eb_pair(kcodes, 16 * oct + n, 4 * kc + 0, KP), eb_pair(kcodes, 16 * oct + n, 4 * kc + 1, KP),
+                                eb_pair(kcodes, 16 * oct + n, 4 * kc + 2, KP), eb_pair(kcodes, 16 * oct + n, 4 * kc + 3, KP));
+        D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[1][0] & mk), bc, D1, 0, 0, 0);
+        if (lo1) D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[1][1] & mk), bc, D1, 0, 0, 0);
+      }
+      if (t0 + t < nq) {
+        const uint32_t *km = reinterpret_cast<const uint32_t *>(rs + lay.k_meta_off) + t * lay.nkg;
+        float acc = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc = __builtin_fmaf(D1[rr] * 0x1p33f, f16f(km[(32 * rr) / lay.kg] & 0xFFFF), acc);
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+          if (gi < lay.nkg) acc = __builtin_fmaf(f16f(km[gi] >> 16), qgl[gi], acc);
+        s1 = acc;
+      }
+    }
+  };
 
   // ---- pass 1 ----
-  float m0[HG], z0[HG], m1[HG], z1[HG], ds_max[HG], ds_sq[HG];
-#pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    m0[j] = m1[j] = ninf;
-    z0[j] = z1[j] = ds_max[j] = ds_sq[j] = 0.f;
-  }
+  float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f, ds_max = 0.f, ds_sq = 0.f;
   float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;  // key reconstruction error (lead group)
   PageRegs pr;
   int buf = 0;
@@ -213,8 +412,8 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     load_rows(w, pr, false);
     load_rec(w, 0);
   }
-  for (int64_t pg = w; pg < npages; pg += EB_WAVES, buf ^= 1) {
-    const int64_t t0 = pg * KVQ_PAGE;
+  for (int pg = w; pg < npages; pg += EB_WAVES, buf ^= 1) {
+    const int t0 = pg * KVQ_PAGE;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page's rows and record have landed
     store_rows(pr, false);
     if (pg + EB_WAVES < npages) {
@@ -222,205 +421,204 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       load_rec(pg + EB_WAVES, buf ^ 1);
     }
     const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
+    float s0, s1;
+    page_scores(rs, t0, s0, s1);
+    if (qlive && t0 + t < L) {
+      const float x0 = s0 * sl2, x1 = s1 * sl2;
+      const float n0 = __builtin_fmaxf(m0, x0), n1 = __builtin_fmaxf(m1, x1);
+      z0 = z0 * __builtin_amdgcn_exp2f(m0 - n0) + __builtin_amdgcn_exp2f(x0 - n0);
+      z1 = z1 * __builtin_amdgcn_exp2f(m1 - n1) + __builtin_amdgcn_exp2f(x1 - n1);
+      m0 = n0;
+      m1 = n1;
+      const float ds = (s1 - s0) * a.scale;
+      ds_max = __builtin_fmaxf(ds_max, __builtin_fabsf(ds));
+      ds_sq = __builtin_fmaf(ds, ds, ds_sq);
+    }
+    if (unit_lead) {  // key reconstruction errors, 8 channels of positions 4 i + r per lane
 #pragma unroll 1
-    for (int it = 0; it < 4; ++it) {
-      const int n = 4 * it + r;
-      const int64_t t = t0 + n;
-      const bool valid = t < L, quant = t < nq;
-      float k[8], kh[8];
-      if (valid) {
+      for (int it = 0; it < 4; ++it) {
+        const int n = 4 * it + r;
+        const bool quant = t0 + n < nq;  // (positions past L are not quantized either)
+        float k[8], kh[8];
         bf16x8(rows[w][0][n * 16 + c], k);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k[e] = 0.f;
-      }
-      if (quant) {
-        decode8<true>(lay, rs, n, c, kh);
-      } else {
+        for (int e = 0; e < 8; ++e) kh[e] = 0.f;
+        if (quant) decode8<true>(lay, KP, rs, n, c, kh);
+        if (a.rotation) row_wht(kh, c, quant);  // back to the original domain
+        if (quant) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kh[e] = k[e];
-      }
-      // Rotated keys are rotated back first (the normalized transform is its own inverse), so
-      // both scores use the raw query: q.(H kh) = (H q).kh.  Window keys are stored raw.
-      if (a.rotation) row_wht(kh, c, quant);
-#pragma unroll
-      for (int j = 0; j < HG; ++j) {
-        float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          d0 = __builtin_fmaf(q[j][e], k[e], d0);
-          d1 = __builtin_fmaf(q[j][e], kh[e], d1);
-        }
-        d0 = row16_sum(d0);
-        d1 = row16_sum(d1);
-        if (valid) {
-          const float s0 = d0 * sl2, s1 = d1 * sl2;
-          const float n0 = __builtin_fmaxf(m0[j], s0), n1 = __builtin_fmaxf(m1[j], s1);
-          z0[j] = z0[j] * __builtin_amdgcn_exp2f(m0[j] - n0) + __builtin_amdgcn_exp2f(s0 - n0);
-          z1[j] = z1[j] * __builtin_amdgcn_exp2f(m1[j] - n1) + __builtin_amdgcn_exp2f(s1 - n1);
-          m0[j] = n0;
-          m1[j] = n1;
-          const float ds = (d1 - d0) * a.scale;
-          ds_max[j] = __builtin_fmaxf(ds_max[j], __builtin_fabsf(ds));
-          ds_sq[j] = __builtin_fmaf(ds, ds, ds_sq[j]);
-        }
-      }
-      if (unit_lead && valid && quant) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float err = kh[e] - k[e];
-          ek_sq = __builtin_fmaf(err, err, ek_sq);
-          ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
-          k_sq = __builtin_fmaf(k[e], k[e], k_sq);
+          for (int e = 0; e < 8; ++e) {
+            const float err = kh[e] - k[e];
+            ek_sq = __builtin_fmaf(err, err, ek_sq);
+            ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
+            k_sq = __builtin_fmaf(k[e], k[e], k_sq);
+          }
         }
       }
     }
   }
-  // combine the four position classes (lanes of one row hold equal values), then the waves
-#pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float om0 = __shfl_xor(m0[j], off), oz0 = __shfl_xor(z0[j], off);
-      const float om1 = __shfl_xor(m1[j], off), oz1 = __shfl_xor(z1[j], off);
-      const float n0 = __builtin_fmaxf(m0[j], om0), n1 = __builtin_fmaxf(m1[j], om1);
-      z0[j] = (n0 == ninf) ? 0.f : z0[j] * __builtin_amdgcn_exp2f(m0[j] - n0) + oz0 * __builtin_amdgcn_exp2f(om0 - n0);
-      z1[j] = (n1 == ninf) ? 0.f : z1[j] * __builtin_amdgcn_exp2f(m1[j] - n1) + oz1 * __builtin_amdgcn_exp2f(om1 - n1);
-      m0[j] = n0;
-      m1[j] = n1;
-      ds_max[j] = __builtin_fmaxf(ds_max[j], __shfl_xor(ds_max[j], off));
-      ds_sq[j] += __shfl_xor(ds_sq[j], off);
-    }
-    if (lane == 0) {
-      red[w][6 * j + 0] = m0[j];
-      red[w][6 * j + 1] = z0[j];
-      red[w][6 * j + 2] = m1[j];
-      red[w][6 * j + 3] = z1[j];
-      red[w][6 * j + 4] = ds_max[j];
-      red[w][6 * j + 5] = ds_sq[j];
+  // merge the 16 tokens of a head (one lane row), then the waves
+  {
+    const float M0 = row16_max(m0), M1 = row16_max(m1);
+    const float Z0 = row16_sum(M0 == ninf ? 0.f : z0 * __builtin_amdgcn_exp2f(m0 - M0));
+    const float Z1 = row16_sum(M1 == ninf ? 0.f : z1 * __builtin_amdgcn_exp2f(m1 - M1));
+    const float dmx = row16_max(ds_max), dsq = row16_sum(ds_sq);
+    if (qlive && t == 0) {
+      red[w][6 * q + 0] = M0;
+      red[w][6 * q + 1] = Z0;
+      red[w][6 * q + 2] = M1;
+      red[w][6 * q + 3] = Z1;
+      red[w][6 * q + 4] = dmx;
+      red[w][6 * q + 5] = dsq;
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    float M0 = ninf, M1 = ninf;
+  // every lane of a head takes the head's merged statistics (the same order in every wave)
+  float M0 = ninf, M1 = ninf, iZ0 = 0.f, iZ1 = 0.f, dmx_h = 0.f, dsq_h = 0.f;
+  {
+    const int qq = qlive ? q : 0;
     for (int i = 0; i < EB_WAVES; ++i) {
-      M0 = __builtin_fmaxf(M0, red[i][6 * j + 0]);
-      M1 = __builtin_fmaxf(M1, red[i][6 * j + 2]);
+      M0 = __builtin_fmaxf(M0, red[i][6 * qq + 0]);
+      M1 = __builtin_fmaxf(M1, red[i][6 * qq + 2]);
     }
-    float Z0 = 0.f, Z1 = 0.f, dmx = 0.f, dsq = 0.f;
+    float Z0 = 0.f, Z1 = 0.f;
     for (int i = 0; i < EB_WAVES; ++i) {
-      if (red[i][6 * j + 0] != ninf) Z0 += red[i][6 * j + 1] * __builtin_amdgcn_exp2f(red[i][6 * j + 0] - M0);
-      if (red[i][6 * j + 2] != ninf) Z1 += red[i][6 * j + 3] * __builtin_amdgcn_exp2f(red[i][6 * j + 2] - M1);
-      dmx = __builtin_fmaxf(dmx, red[i][6 * j + 4]);
-      dsq += red[i][6 * j + 5];
+      if (red[i][6 * qq + 0] != ninf) Z0 += red[i][6 * qq + 1] * __builtin_amdgcn_exp2f(red[i][6 * qq + 0] - M0);
+      if (red[i][6 * qq + 2] != ninf) Z1 += red[i][6 * qq + 3] * __builtin_amdgcn_exp2f(red[i][6 * qq + 2] - M1);
+      dmx_h = __builtin_fmaxf(dmx_h, red[i][6 * qq + 4]);
+      dsq_h += red[i][6 * qq + 5];
     }
-    m0[j] = M0;
-    m1[j] = M1;
-    z0[j] = Z0 > 0.f ? 1.f / Z0 : 0.f;  // from here on: reciprocal sums
-    z1[j] = Z1 > 0.f ? 1.f / Z1 : 0.f;
-    ds_max[j] = dmx;
-    ds_sq[j] = dsq;
+    iZ0 = Z0 > 0.f ? 1.f / Z0 : 0.f;
+    iZ1 = Z1 > 0.f ? 1.f / Z1 : 0.f;
   }
   __syncthreads();
 
   // ---- pass 2 ----
-  float tv[HG];
-  float o[HG][8], ov[HG][8], ok[HG][8], oj[HG][8];
+  float tv = 0.f;
+  float zs[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // weighted zero points: set x value group (this lane's head)
+  eb_f4 Dr[8], Dc[8];                        // value sums per 16-channel tile: original values, codes
 #pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    tv[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[j][e] = ov[j][e] = ok[j][e] = oj[j][e] = 0.f;
-  }
+  for (int m = 0; m < 8; ++m) Dr[m] = Dc[m] = eb_f4{0.f, 0.f, 0.f, 0.f};
   float ev_sq = 0.f, ev_max = 0.f, v_sq = 0.f;
+  const int nvg = lay.nvg;
   buf = 0;
   if (w < npages) {
     load_rows(w, pr, true);
     load_rec(w, 0);
   }
-  for (int64_t pg = w; pg < npages; pg += EB_WAVES, buf ^= 1) {
-    const int64_t t0 = pg * KVQ_PAGE;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page's rows and record have landed
+  for (int pg = w; pg < npages; pg += EB_WAVES, buf ^= 1) {
+    const int t0 = pg * KVQ_PAGE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     store_rows(pr, true);
     if (pg + EB_WAVES < npages) {
       load_rows(pg + EB_WAVES, pr, true);
       load_rec(pg + EB_WAVES, buf ^ 1);
     }
     const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
+    float s0, s1;
+    page_scores(rs, t0, s0, s1);
+    const bool valid = qlive && t0 + t < L, quant = t0 + t < nq;
+    const float w0 = valid ? __builtin_amdgcn_exp2f(s0 * sl2 - M0) * iZ0 : 0.f;
+    const float w1 = valid ? __builtin_amdgcn_exp2f(s1 * sl2 - M1) * iZ1 : 0.f;
+    tv += __builtin_fabsf(w1 - w0);
+    // A operands: raw rows take the weights; code rows the weights times the token's value scale
+    // (times 2^64) for quantized tokens, the weights times 2^-69 for window tokens
+    if (qlive) {
+      const uint32_t *vm = reinterpret_cast<const uint32_t *>(rs + lay.v_meta_off) + t * nvg;
+      uint16_t *xr = reinterpret_cast<uint16_t *>(&xbuf[w][0][0][0]);
+      uint32_t hi, lo;
+      split2(w0, w1, hi, lo);
+      xr[(0 + q) * 16 + t] = (uint16_t)hi;          // set 0, hi
+      xr[(4 + q) * 16 + t] = (uint16_t)lo;          // set 0, lo
+      xr[(8 + q) * 16 + t] = (uint16_t)(hi >> 16);  // set 1, hi
+      xr[(12 + q) * 16 + t] = (uint16_t)(lo >> 16); // set 1, lo
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        if (v >= nvg) break;
+        float f0, f1;
+        if (quant) {
+          const float sc = f16f(vm[v] & 0xFFFF) * 0x1p64f, zr = f16f(vm[v] >> 16);
+          f0 = w0 * sc;
+          f1 = w1 * sc;
+          zs[0][v] = __builtin_fmaf(w0, zr, zs[0][v]);
+          zs[1][v] = __builtin_fmaf(w1, zr, zs[1][v]);
+        } else {
+          f0 = w0 * 0x1p-69f;
+          f1 = w1 * 0x1p-69f;
+        }
+        split2(f0, f1, hi, lo);
+        uint16_t *xc = reinterpret_cast<uint16_t *>(&xbuf[w][1 + v][0][0]);
+        xc[(0 + q) * 16 + t] = (uint16_t)hi;
+        xc[(4 + q) * 16 + t] = (uint16_t)lo;
+        xc[(8 + q) * 16 + t] = (uint16_t)(hi >> 16);
+        xc[(12 + q) * 16 + t] = (uint16_t)(lo >> 16);
+      }
+    }
+    // A operand of lane l: row l mod 16, tokens 4 (l / 16) .. + 3 (LDS operations of a wave complete in order)
+    const eb_s4 ar = __builtin_bit_cast(eb_s4, *reinterpret_cast<const eb_u2 *>(&xbuf[w][0][lane & 15][2 * (lane >> 4)]));
+    const eb_s4 ac0 = __builtin_bit_cast(eb_s4, *reinterpret_cast<const eb_u2 *>(&xbuf[w][1][lane & 15][2 * (lane >> 4)]));
+    const eb_s4 ac1 = __builtin_bit_cast(eb_s4, *reinterpret_cast<const eb_u2 *>(&xbuf[w][2][lane & 15][2 * (lane >> 4)]));
+    // B operands: column = channel 16 m + (lane mod 16), k = tokens 4 kk .. 4 kk + 3 (kk = lane / 16)
+    const int kk = lane >> 4, col = lane & 15;
+    const int tq = nq - t0;  // tokens of the page below it are quantized
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const uint16_t *vr = reinterpret_cast<const uint16_t *>(vrow) + 16 * m + col;
+      const uint32_t r0 = (uint32_t)vr[(4 * kk + 0) * 128] | ((uint32_t)vr[(4 * kk + 1) * 128] << 16);
+      const uint32_t r1 = (uint32_t)vr[(4 * kk + 2) * 128] | ((uint32_t)vr[(4 * kk + 3) * 128] << 16);
+      Dr[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ar, pack4s(r0, r1), Dr[m], 0, 0, 0);
+      uint32_t c0 = r0, c1 = r1;  // window tokens: exact values
+      if (tq > 0) {
+        const uint8_t *vcodes = rs + lay.v_codes_off;
+        const uint32_t q0 = eb_pair(vcodes, lane, m, VP), q1 = eb_pair(vcodes, lane, 8 + m, VP);
+        const int tb = 4 * kk;  // first token of the lane's four
+        c0 = (tb + 0 < tq ? (q0 & 0xFFFFu) : (r0 & 0xFFFFu)) | (tb + 1 < tq ? (q0 & 0xFFFF0000u) : (r0 & 0xFFFF0000u));
+        c1 = (tb + 2 < tq ? (q1 & 0xFFFFu) : (r1 & 0xFFFFu)) | (tb + 3 < tq ? (q1 & 0xFFFF0000u) : (r1 & 0xFFFF0000u));
+      }
+      Dc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k((m < 4 || nvg == 1) ? ac0 : ac1, pack4s(c0, c1), Dc[m], 0, 0, 0);
+    }
+    if (unit_lead) {  // value reconstruction errors
 #pragma unroll 1
-    for (int it = 0; it < 4; ++it) {
-      const int n = 4 * it + r;
-      const int64_t t = t0 + n;
-      const bool valid = t < L, quant = t < nq;
-      float k[8], kh[8], v[8], vh[8];
-      if (valid) {
-        bf16x8(rows[w][0][n * 16 + c], k);
+      for (int it = 0; it < 4; ++it) {
+        const int n = 4 * it + r;
+        const bool qn = t0 + n < nq;
+        float v[8], vh[8];
         bf16x8(rows[w][1][n * 16 + c], v);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k[e] = v[e] = 0.f;
-      }
-      if (quant) {
-        decode8<true>(lay, rs, n, c, kh);
-        decode8<false>(lay, rs, n, c, vh);
-      } else {
+        for (int e = 0; e < 8; ++e) vh[e] = 0.f;
+        if (qn) decode8<false>(lay, VP, rs, n, c, vh);
+        // with rotated values the reconstruction is rotated back (no recent window then)
+        if (a.value_rotation) row_wht(vh, c, qn);
+        if (qn) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kh[e] = k[e];
-          vh[e] = v[e];
-        }
-      }
-      if (a.rotation) row_wht(kh, c, quant);
-#pragma unroll
-      for (int j = 0; j < HG; ++j) {
-        float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          d0 = __builtin_fmaf(q[j][e], k[e], d0);
-          d1 = __builtin_fmaf(q[j][e], kh[e], d1);
-        }
-        d0 = row16_sum(d0);
-        d1 = row16_sum(d1);
-        const float w0 = valid ? __builtin_amdgcn_exp2f(d0 * sl2 - m0[j]) * z0[j] : 0.f;
-        const float w1 = valid ? __builtin_amdgcn_exp2f(d1 * sl2 - m1[j]) * z1[j] : 0.f;
-        if (c == 0) tv[j] += __builtin_fabsf(w1 - w0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          o[j][e] = __builtin_fmaf(w0, v[e], o[j][e]);
-          ov[j][e] = __builtin_fmaf(w0, vh[e], ov[j][e]);
-          ok[j][e] = __builtin_fmaf(w1, v[e], ok[j][e]);
-          oj[j][e] = __builtin_fmaf(w1, vh[e], oj[j][e]);
-        }
-      }
-      // With rotated values the sums over vh are in the rotated domain (rotated back per head at
-      // the end; no recent window then); the reconstruction statistics rotate each position back.
-      if (unit_lead && a.value_rotation) row_wht(vh, c, true);
-      if (unit_lead && valid && quant) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float err = vh[e] - v[e];
-          ev_sq = __builtin_fmaf(err, err, ev_sq);
-          ev_max = __builtin_fmaxf(ev_max, __builtin_fabsf(err));
-          v_sq = __builtin_fmaf(v[e], v[e], v_sq);
+          for (int e = 0; e < 8; ++e) {
+            const float err = vh[e] - v[e];
+            ev_sq = __builtin_fmaf(err, err, ev_sq);
+            ev_max = __builtin_fmaxf(ev_max, __builtin_fabsf(err));
+            v_sq = __builtin_fmaf(v[e], v[e], v_sq);
+          }
         }
       }
     }
   }
-  // sums over the position classes, then over the waves (one wave at a time into LDS)
+
+  // ---- merge: TV and weighted zero points per head, value sums per head and channel ----
+  {
+    const float tvt = row16_sum(tv);
+    float zt[2][2];
 #pragma unroll
-  for (int j = 0; j < HG; ++j) {
+    for (int set = 0; set < 2; ++set) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[j][e] += __shfl_xor(o[j][e], 16);
-      o[j][e] += __shfl_xor(o[j][e], 32);
-      ov[j][e] += __shfl_xor(ov[j][e], 16);
-      ov[j][e] += __shfl_xor(ov[j][e], 32);
-      ok[j][e] += __shfl_xor(ok[j][e], 16);
-      ok[j][e] += __shfl_xor(ok[j][e], 32);
-      oj[j][e] += __shfl_xor(oj[j][e], 16);
-      oj[j][e] += __shfl_xor(oj[j][e], 32);
+      for (int v = 0; v < 2; ++v) zt[set][v] = row16_sum(zs[set][v]);
     }
-    for (int off = 1; off <= 32; off <<= 1) tv[j] += __shfl_xor(tv[j], off);
+    if (qlive && t == 0) {
+      tvred[w][q] = tvt;
+#pragma unroll
+      for (int set = 0; set < 2; ++set) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) zred[w][set][q][v] = zt[set][v];
+      }
+    }
   }
   if (unit_lead) {
     for (int off = 1; off <= 32; off <<= 1) {
@@ -431,39 +629,49 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       ek_max = __builtin_fmaxf(ek_max, __shfl_xor(ek_max, off));
       ev_max = __builtin_fmaxf(ev_max, __shfl_xor(ev_max, off));
     }
+    if (lane == 0) {
+      ured[w][0] = ek_sq;
+      ured[w][1] = ev_sq;
+      ured[w][2] = ek_max;
+      ured[w][3] = ev_max;
+      ured[w][4] = k_sq;
+      ured[w][5] = v_sq;
+    }
   }
-  if (lane == 0) {
+  __syncthreads();
+  // value sums: D row 4 (l / 16) + r of lane l = (set, part, head r) = (l / 32, (l / 16) mod 2, r);
+  // the hi and lo parts are added across lanes l and l ^ 16; one wave at a time into LDS
+  {
+    const int G4 = lane >> 4, col = lane & 15, set = G4 >> 1;
+    for (int i = 0; i < EB_WAVES; ++i) {
+      if (w == i) {
 #pragma unroll
-    for (int j = 0; j < HG; ++j) red[w][j] = tv[j];
-    ured[w][0] = ek_sq;
-    ured[w][1] = ev_sq;
-    ured[w][2] = ek_max;
-    ured[w][3] = ev_max;
-    ured[w][4] = k_sq;
-    ured[w][5] = v_sq;
-  }
-  for (int i = 0; i < EB_WAVES; ++i) {
-    if (w == i && r == 0) {
+        for (int m = 0; m < 8; ++m) {
+          const int vg = (nvg == 2 && m >= 4) ? 1 : 0;
 #pragma unroll
-      for (int j = 0; j < HG; ++j) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = 8 * c + e;
-          accs[0][j][ch] = (i == 0 ? 0.f : accs[0][j][ch]) + o[j][e];
-          accs[1][j][ch] = (i == 0 ? 0.f : accs[1][j][ch]) + ov[j][e];
-          accs[2][j][ch] = (i == 0 ? 0.f : accs[2][j][ch]) + ok[j][e];
-          accs[3][j][ch] = (i == 0 ? 0.f : accs[3][j][ch]) + oj[j][e];
+          for (int rr = 0; rr < 4; ++rr) {
+            const float dr = Dr[m][rr] + __shfl_xor(Dr[m][rr], 16);
+            const float dc = Dc[m][rr] + __shfl_xor(Dc[m][rr], 16);
+            if ((G4 & 1) == 0 && rr < HS) {
+              const int ch = 16 * m + col;
+              accs[set == 0 ? 0 : 2][rr][ch] += dr;
+              accs[set == 0 ? 1 : 3][rr][ch] += __builtin_fmaf(dc, 0x1p69f, zred[i][set][rr][vg]);
+            }
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
-  // wave j < HG finishes head j: norms over the channels (lane l takes channels l and l + 64)
-  if (w < HG) {
+  // wave j < HS finishes head j: norms over the channels (lane l takes channels 2l, 2l + 1)
+  if (w < HS) {
     const int j = w;
-    float tvj = 0.f;
-    for (int i = 0; i < EB_WAVES; ++i) tvj += red[i][j];
-    // lane l takes channels 2l, 2l + 1; sums over rotated values are rotated back first
+    float tvj = 0.f, dmx = 0.f, dsq = 0.f;
+    for (int i = 0; i < EB_WAVES; ++i) {
+      tvj += tvred[i][j];
+      dmx = __builtin_fmaxf(dmx, red[i][6 * j + 4]);
+      dsq += red[i][6 * j + 5];
+    }
     float o2[2], v2[2], k2[2], j2[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -472,6 +680,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       k2[e] = accs[2][j][2 * lane + e];
       j2[e] = accs[3][j][2 * lane + e];
     }
+    // sums over rotated values are in the rotated domain: rotated back
     if (a.value_rotation) {
       pair_wht(v2[0], v2[1], lane);
       pair_wht(j2[0], j2[1], lane);
@@ -491,15 +700,6 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       nk += __shfl_xor(nk, off);
       nj += __shfl_xor(nj, off);
       no += __shfl_xor(no, off);
-    }
-    // the head's pass-1 statistics: every wave merged them identically
-    float dmx = 0.f, dsq = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < HG; ++jj) {
-      if (jj == j) {
-        dmx = ds_max[jj];
-        dsq = ds_sq[jj];
-      }
     }
     float *hs = a.head_stats + ((size_t)b * a.Hq + hq0 + j) * KVQ_EB_HEAD;
     if (lane == 0) {
@@ -541,12 +741,12 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
 hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
-  // two heads per group: four would need more than the 256 registers of two waves per SIMD
-  const int g = a.Hq / a.Hkv, hg = g < 2 ? g : 2;
+  // up to two heads per group (one workgroup per group keeps the grid near two per CU's worth)
+  const int g = a.Hq / a.Hkv, hs = g < 2 ? g : 2;
   const int units = a.B * a.Hkv;
   // groups of 8 units, each group's head groups 8 workgroups apart (padding after the last unit)
-  const dim3 grid((unsigned)(((units + 7) / 8) * 8 * (g / hg))), block(64 * EB_WAVES);
-  if (hg == 1)
+  const dim3 grid((unsigned)(((units + 7) / 8) * 8 * (g / hs))), block(64 * EB_WAVES);
+  if (hs == 1)
     hipLaunchKernelGGL(kvq_errbudget_kernel<1>, grid, block, 0, s, a);
   else
     hipLaunchKernelGGL(kvq_errbudget_kernel<2>, grid, block, 0, s, a);
