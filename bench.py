@@ -432,7 +432,9 @@ def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
         # error-budget diagnostics on the same cache
         hs = torch.empty((wl.batch, wl.num_q_heads, K.KVQ_EB_HEAD), dtype=torch.float32, device=dev)
         us = torch.empty((wl.batch, wl.num_kv_heads, K.KVQ_EB_UNIT), dtype=torch.float32, device=dev)
-        K.kvq_error_budget(prm, cb.struct, n_new, Lmax, k_ref, v_ref, q, K.KVQ_BF16, 0.0, hs, us)
+        ewsb = K.kvq_error_budget_workspace_bytes(prm, wl.batch, Lmax)
+        ews = torch.empty(ewsb, dtype=torch.uint8, device=dev)
+        K.kvq_error_budget(prm, cb.struct, n_new, Lmax, k_ref, v_ref, q, K.KVQ_BF16, 0.0, hs, us, ews, ewsb)
         torch.cuda.synchronize()
         h_ = hs.cpu().numpy().astype(np.float64)
         u_ = us.cpu().numpy().astype(np.float64)
@@ -906,8 +908,10 @@ def main():
         v_ref = gen.kv(W.TENSOR_V, 0, L_last)
         hs = torch.empty((B, Hq, K.KVQ_EB_HEAD), dtype=torch.float32, device=dev)
         us = torch.empty((B, Hkv, K.KVQ_EB_UNIT), dtype=torch.float32, device=dev)
+        ewsb = K.kvq_error_budget_workspace_bytes(params, B, L_last)
+        ews = torch.empty(ewsb, dtype=torch.uint8, device=dev)
         eb = K.bound_call("kvq_error_budget", params, cache.struct, lens_last, L_last, k_ref, v_ref, q_last,
-                          K.KVQ_BF16, 0.0, hs, us, stream=stream)
+                          K.KVQ_BF16, 0.0, hs, us, ews, ewsb, stream=stream)
         eb_us = time_calls(torch, [eb], 3, stream)
         h_ = hs.cpu().numpy().astype(np.float64)
         u_ = us.cpu().numpy().astype(np.float64)

@@ -332,13 +332,19 @@ kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, c
  *    sum k^2, sum v^2, number of quantized positions, 0}.
  * fp32 arithmetic, reconstructions zero + code * scale rounded to fp32.  Reconstructions of
  * rotated keys or values are rotated back first: every error is taken in the original domain.
- * Errors as for kvq_decode_attention. */
+ * The query is taken as bf16 hi + lo parts (exact for a bf16 query; about 16 significant bits of
+ * an fp32 one) and must stay below 2^27 in magnitude.  workspace (device, 16-byte aligned) of at
+ * least kvq_error_budget_workspace_bytes(params, cache->batch, max_seq_len) bytes holds the
+ * per-range partial results of the three launches (statistics, weighted sums, merge); its
+ * contents are not needed between calls.  Errors as for kvq_decode_attention, and KVQ_ENOSPACE
+ * for a short workspace. */
 #define KVQ_EB_HEAD 8
 #define KVQ_EB_UNIT 8
+size_t kvq_error_budget_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len);
 kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
                             int64_t max_seq_len, const uint16_t *k_ref, const uint16_t *v_ref, const void *q,
                             int32_t q_dtype, float softmax_scale, float *head_stats, float *unit_stats,
-                            hipStream_t stream);
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *kvq_status_str(kvq_status status);

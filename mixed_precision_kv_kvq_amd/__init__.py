@@ -41,6 +41,7 @@ EXPORTED = [
     "kvq_dequantize_dense",
     "kvq_dense_workspace_bytes",
     "kvq_dense_decode_attention",
+    "kvq_error_budget_workspace_bytes",
     "kvq_error_budget",
     "kvq_device_status",
     "kvq_status_str",
@@ -134,8 +135,10 @@ def _load():
                                                c_void_p, c_int32, c_void_p, c_int32, c_float, c_void_p, c_size_t,
                                                c_void_p]
     lib.kvq_dense_decode_attention.restype = c_int32
+    lib.kvq_error_budget_workspace_bytes.argtypes = [P(kvq_params), c_int32, c_int64]
+    lib.kvq_error_budget_workspace_bytes.restype = c_size_t
     lib.kvq_error_budget.argtypes = [P(kvq_params), P(kvq_cache), c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
-                                     c_int32, c_float, c_void_p, c_void_p, c_void_p]
+                                     c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.kvq_error_budget.restype = c_int32
     lib.kvq_device_status.argtypes = [P(kvq_cache), P(ctypes.c_uint32), c_void_p]
     lib.kvq_device_status.restype = c_int32
@@ -325,11 +328,16 @@ KVQ_EB_HEAD = 8  # per (sequence, query head) error statistics
 KVQ_EB_UNIT = 8  # per (sequence, kv head) reconstruction statistics
 
 
+def kvq_error_budget_workspace_bytes(params, batch: int, max_seq_len: int) -> int:
+    return int(_lib.kvq_error_budget_workspace_bytes(ctypes.byref(params), batch, max_seq_len))
+
+
 def kvq_error_budget(params, cache, seq_lens, max_seq_len, k_ref, v_ref, q, q_dtype, softmax_scale, head_stats,
-                     unit_stats, stream=None, check=True):
+                     unit_stats, workspace, workspace_bytes, stream=None, check=True):
     st = _lib.kvq_error_budget(ctypes.byref(params), ctypes.byref(cache), _ptr(seq_lens), int(max_seq_len),
                                _ptr(k_ref), _ptr(v_ref), _ptr(q), int(q_dtype), float(softmax_scale),
-                               _ptr(head_stats), _ptr(unit_stats), _stream(stream))
+                               _ptr(head_stats), _ptr(unit_stats), _ptr(workspace), int(workspace_bytes),
+                               _stream(stream))
     if check:
         _check(st, "kvq_error_budget")
     return st

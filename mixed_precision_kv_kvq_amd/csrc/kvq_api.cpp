@@ -431,18 +431,47 @@ kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, c
   return hip_status(kvq_launch_combine(c, stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Ranges of pages per sequence for the error-budget passes: about one workgroup per CU over all
+// (unit, head group, range) items, at least one page per wave of a range.
+int errbudget_splits(const kvq_params *p, int32_t batch, int64_t max_seq_len) {
+  const int g = p->num_q_heads / p->num_kv_heads, ngrp = g / kvq_errbudget_heads_per_group(g);
+  const int64_t items = (int64_t)batch * p->num_kv_heads * ngrp;
+  const int64_t pages = (max_seq_len + KVQ_PAGE - 1) / KVQ_PAGE;
+  int64_t s = (kNumCUs + items - 1) / items;
+  const int64_t smax = (pages + 7) / 8;
+  if (s > smax) s = smax;
+  return s < 1 ? 1 : (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_error_budget_workspace_bytes(const kvq_params *params, int32_t batch, int64_t max_seq_len) {
+  if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0 || max_seq_len > INT32_MAX) return 0;
+  const int g = params->num_q_heads / params->num_kv_heads, ngrp = g / kvq_errbudget_heads_per_group(g);
+  const size_t items = (size_t)batch * params->num_kv_heads * ngrp * errbudget_splits(params, batch, max_seq_len);
+  return items * kvq_errbudget_item_floats() * sizeof(float);
+}
+
 kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,
                             int64_t max_seq_len, const uint16_t *k_ref, const uint16_t *v_ref, const void *q,
                             int32_t q_dtype, float softmax_scale, float *head_stats, float *unit_stats,
-                            hipStream_t stream) {
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (kvq_status st = check_params(params)) return st;
   if (kvq_status st = check_cache(params, cache)) return st;
   if (!seq_lens || max_seq_len < 0 || max_seq_len > INT32_MAX) return KVQ_EINVAL;
-  if (!k_ref || !v_ref || !q || !head_stats || !unit_stats) return KVQ_EINVAL;
-  if (!aligned16(k_ref) || !aligned16(v_ref) || !aligned16(q) || !aligned16(head_stats) || !aligned16(unit_stats))
+  if (!k_ref || !v_ref || !q || !head_stats || !unit_stats || !workspace) return KVQ_EINVAL;
+  if (!aligned16(k_ref) || !aligned16(v_ref) || !aligned16(q) || !aligned16(head_stats) || !aligned16(unit_stats) ||
+      !aligned16(workspace))
     return KVQ_EINVAL;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_EINVAL;
   if (!(softmax_scale >= 0.f) || isinf(softmax_scale)) return KVQ_EINVAL;
+  if (workspace_bytes < kvq_error_budget_workspace_bytes(params, cache->batch, max_seq_len)) return KVQ_ENOSPACE;
   KvqErrArgs a = {};
   a.lay = layout_of(params);
   a.cache = dev_cache(params, cache);
@@ -461,6 +490,8 @@ kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, co
   a.rotation = params->key_rotation;
   a.value_rotation = params->value_rotation;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)KVQ_D);
+  a.ws = (float *)workspace;
+  a.splits = errbudget_splits(params, cache->batch, max_seq_len);
   return hip_status(kvq_launch_errbudget(a, stream));
 }
 

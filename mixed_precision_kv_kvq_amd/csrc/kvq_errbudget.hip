@@ -198,9 +198,10 @@ constexpr int EB_WAVES = 8;
 constexpr int EB_REC16 = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 16;  // largest record, 16-byte units
 constexpr float EB_Q = 0x1p100f;  // query operand scale
 
-// One workgroup of EB_WAVES waves per (group of HS <= 2 query heads of one kv head, sequence); the
-// head groups of a kv head run on workgroups 8 apart (one XCD), so the second to read a page finds
-// it in that XCD's L2.  Wave w takes pages w, w + EB_WAVES, ...: a page's original rows and record
+// One workgroup of EB_WAVES waves per work item: a group of HS <= 4 query heads of one kv head and
+// sequence, and one of S consecutive ranges of the sequence's pages.  The head groups of a range
+// run on workgroups 8 apart (one XCD), so the second to read a page finds it in that XCD's L2.
+// Wave w of an item takes pages p0 + w, p0 + w + EB_WAVES, ...: a page's original rows and record
 // are loaded while the wave computes the page before, then stored to the wave's LDS region.
 //
 // Scores on MFMA (16x16x32 bf16): the query, scaled by 2^100 and split into bf16 hi and lo parts,
@@ -212,41 +213,58 @@ constexpr float EB_Q = 0x1p100f;  // query operand scale
 // use the rotated query (the normalized transform is orthogonal); window tokens are stored exact
 // (s' = s).  Lane 16 q + t then holds both scores of token t for head q.
 //
-// Pass 1: online maxima and sums of both score sets (log2 units) and the score-error statistics,
-// merged over the 16 lanes of a head and the waves.  Pass 2: the weights a (exact keys) and a'
-// (quantized keys), their total variation, and the four weighted sums on MFMA (16x16x16 bf16,
-// k = the page's 16 tokens): A rows 8 set + 4 part + q hold the weights of set a / a' (hi and lo
-// parts) of head q, through a per-wave LDS exchange buffer; B is the original values (exact bf16:
-// a V, a' V) or the value codes (a V_hat, a' V_hat; A = weight * scale * 2^64, window tokens take
-// their exact values as B with A = weight * 2^-69, so every product carries 2^-69), plus the
-// weighted zero points.  The first head group of each kv head also accumulates the reconstruction
-// errors (per element, 8 channels per lane).
-template <int HS>
+// PASS 1: online maxima and sums of both score sets (log2 units) and the score-error statistics
+// over the item's pages, merged over the 16 lanes of a head and the waves, to the workspace.
+// PASS 2: the maxima and sums of all ranges merged; the weights a (exact keys) and a' (quantized
+// keys), their total variation, and the four weighted sums on MFMA (16x16x16 bf16, k = the page's
+// 16 tokens): A rows 8 set + 4 part + q hold the weights of set a / a' (hi and lo parts) of head q,
+// through a per-wave LDS exchange buffer; B is the original values (exact bf16: a V, a' V) or the
+// value codes (a V_hat, a' V_hat; A = weight * scale * 2^64, window tokens take their exact values
+// as B with A = weight * 2^-69, so every product carries 2^-69), plus the weighted zero points;
+// the range's sums to the workspace (the weights are final, so the ranges' sums add).  Key
+// reconstruction errors are taken in pass 1 by head group 0, value ones in pass 2 by the last
+// head group (per element, 8 channels per lane).
+//
+// Workspace item (floats, one per (kv head unit, head group, range)): pass-1 statistics of each
+// head {M0, Z0, M1, Z1, max |ds|, sum ds^2}, key reconstruction {sum e^2, max |e|, sum k^2}, then
+// the four sums [sum][head][channel], the total variation of each head, value reconstruction.
+constexpr int EB_W_STATS = 0;
+constexpr int EB_W_KREC = 24;
+constexpr int EB_W_SUMS = 32;
+constexpr int EB_W_TV = EB_W_SUMS + 4 * 4 * KVQ_D;
+constexpr int EB_W_VREC = EB_W_TV + 4;
+constexpr int EB_W_ITEM = EB_W_VREC + 4;
+
+template <int HS, int PASS>
 __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs a) {
   __shared__ float red[EB_WAVES][6 * HS];
-  __shared__ float ured[EB_WAVES][6];
-  __shared__ float accs[4][HS][KVQ_D];
-  __shared__ float qs[2][HS][KVQ_D];      // the group's queries: raw, and the one the codes are scored with
-  __shared__ float qg[HS][4];             // sums of the code query over each key group
+  __shared__ float ured[EB_WAVES][3];
+  __shared__ float qg[HS][4];                 // sums of the code query over each key group
   __shared__ float zred[EB_WAVES][2][HS][2];  // weighted zero points (set, head, value group)
-  __shared__ float tvred[EB_WAVES][HS];
   __shared__ uint4 recs[EB_WAVES][2][EB_REC16];       // page records (two: the next one lands meanwhile)
   __shared__ uint4 rows[EB_WAVES][2][KVQ_PAGE * 16];  // the page's original K and V rows
   __shared__ uint32_t xbuf[EB_WAVES][3][16][8];        // value A operands: [raw, code v0, code v1][row][16 bf16]
+  // before the page loop: the group's queries (raw, and the one the codes are scored with); after
+  // it: the four weighted sums of the workgroup
+  float(*qs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&rows[0][0][0]);
+  float(*accs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&rows[0][0][0]);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: page loop and record addresses in SGPRs
   const int r = lane >> 4, c = lane & 15;       // element layout: row r, 8 channels [8c, 8c + 8)
   const int q = lane >> 4, t = lane & 15;       // score layout: head q, token t
-  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, ngrp = g / HS;
-  // workgroup -> (unit, head group): the groups of unit u at blocks 8 ngrp (u / 8) + 8 grp + u mod 8
+  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, ngrp = g / HS, S = a.splits;
+  // workgroup -> (unit, range, head group): work unit wu = unit S + range; the groups of wu at
+  // blocks 8 ngrp (wu / 8) + 8 grp + wu mod 8
   const int blk = blockIdx.x / (8 * ngrp), rem = blockIdx.x % (8 * ngrp);
-  const int grp = rem / 8, unit = 8 * blk + rem % 8;
-  if (unit >= a.B * Hkv) return;  // padding of the last group of 8 units
+  const int grp = rem / 8, wu = 8 * blk + rem % 8;
+  if (wu >= a.B * Hkv * S) return;  // padding of the last group of 8 work units
+  const int unit = wu / S, split = wu % S;
   const int b = unit / Hkv, h = unit % Hkv;
   const int hq0 = h * g + grp * HS;  // first query head of the group
-  const bool unit_lead = grp == 0;
+  float *ws = a.ws + (size_t)((unit * ngrp + grp) * S + split) * EB_W_ITEM;
+  const bool krec = PASS == 1 && grp == 0, vrec = PASS == 2 && grp == ngrp - 1;
   int L = (int)a.seq_lens[b];
-  kvq_raise(a.cache, hq0 == 0 && (L < 0 || (int64_t)L > a.max_len), KVQ_DEV_LENGTH);
+  if (PASS == 1) kvq_raise(a.cache, hq0 == 0 && split == 0 && (L < 0 || (int64_t)L > a.max_len), KVQ_DEV_LENGTH);
   L = L < 0 ? 0 : ((int64_t)L > a.max_len ? (int)a.max_len : L);
   int nq = L > a.R ? L - a.R : 0;
   const int64_t cap_tokens = (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq) * KVQ_PAGE;
@@ -256,11 +274,17 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   const int rec16 = lay.record / 16;
   const EbPlanes KP = eb_planes(lay.kb), VP = eb_planes(lay.vb);
   const bool qlive = q < HS;  // score-layout lanes of a head of the group
+  // the item's pages: range `split` of S near-equal ranges
+  const int npages = (L + KVQ_PAGE - 1) / KVQ_PAGE;
+  const int per = (npages + S - 1) / S;
+  const int pbeg = split * per < npages ? split * per : npages;
+  const int pend = pbeg + per < npages ? pbeg + per : npages;
 
   // ---- queries: raw and code-scoring (rotated when keys are) rows, and the group sums ----
-  for (int i = threadIdx.x; i < 3 * 16 * 8 * EB_WAVES; i += 64 * EB_WAVES)
-    (&xbuf[0][0][0][0])[i] = 0u;  // rows of heads beyond HS stay zero
-  for (int i = threadIdx.x; i < 4 * HS * KVQ_D; i += 64 * EB_WAVES) (&accs[0][0][0])[i] = 0.f;
+  if (HS < 4) {
+    for (int i = threadIdx.x; i < 3 * 16 * 8 * EB_WAVES; i += 64 * EB_WAVES)
+      (&xbuf[0][0][0][0])[i] = 0u;  // rows of heads beyond HS stay zero
+  }
   if (w == 0) {
     float x[8];
     if (r < HS) {
@@ -321,28 +345,41 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) qgl[gi] = (qlive && gi < lay.nkg) ? qg[qlive ? q : 0][gi] : 0.f;
   }
+  __syncthreads();  // the queries' LDS becomes page rows
 
-  // This lane's 16 bytes (8 channels) of original row t (t < L; callers pass a valid t).
-  auto ref8 = [&](const uint16_t *base, int tt) {
-    return *reinterpret_cast<const uint4 *>(base + (((size_t)b * a.max_len + (size_t)tt) * Hkv + h) * KVQ_D + 8 * c);
-  };
-  struct PageRegs {
-    uint4 k[4], v[4];
-  };
-  auto load_rows = [&](int pg, PageRegs &pr, bool with_v) __attribute__((always_inline)) {
+  // This lane's 16 bytes (8 channels) of original rows t0 + 4 i + r, i < 4 (clamped to L - 1 on the
+  // last page): a uniform page base and a 32-bit per-lane offset.
+  const uint32_t row_elems = (uint32_t)Hkv * KVQ_D;  // elements between consecutive positions
+  // the next page's rows in flight: pk[i], pv[i] = positions 4 i + r (written out, no indexed array)
+  uint4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
+  auto load_rows = [&](int pg, bool with_v) __attribute__((always_inline)) {
     const int t0 = pg * KVQ_PAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = t0 + 4 * i + r < L ? t0 + 4 * i + r : L - 1;
-      pr.k[i] = ref8(a.k_ref, tt);
-      if (with_v) pr.v[i] = ref8(a.v_ref, tt);
+    const size_t base = ((size_t)b * a.max_len + (size_t)t0) * row_elems + (size_t)h * KVQ_D;
+    const uint16_t *kp = a.k_ref + base, *vp = a.v_ref + base;
+    const int last = L - 1 - t0;
+    auto off = [&](int i) { return (uint32_t)(4 * i + r < last ? 4 * i + r : last) * row_elems + 8 * c; };
+    const uint32_t o0 = off(0), o1 = off(1), o2 = off(2), o3 = off(3);
+    pk0 = *reinterpret_cast<const uint4 *>(kp + o0);
+    pk1 = *reinterpret_cast<const uint4 *>(kp + o1);
+    pk2 = *reinterpret_cast<const uint4 *>(kp + o2);
+    pk3 = *reinterpret_cast<const uint4 *>(kp + o3);
+    if (with_v) {
+      pv0 = *reinterpret_cast<const uint4 *>(vp + o0);
+      pv1 = *reinterpret_cast<const uint4 *>(vp + o1);
+      pv2 = *reinterpret_cast<const uint4 *>(vp + o2);
+      pv3 = *reinterpret_cast<const uint4 *>(vp + o3);
     }
   };
-  auto store_rows = [&](const PageRegs &pr, bool with_v) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rows[w][0][(4 * i + r) * 16 + c] = pr.k[i];
-      if (with_v) rows[w][1][(4 * i + r) * 16 + c] = pr.v[i];
+  auto store_rows = [&](bool with_v) __attribute__((always_inline)) {
+    rows[w][0][(0 + r) * 16 + c] = pk0;
+    rows[w][0][(4 + r) * 16 + c] = pk1;
+    rows[w][0][(8 + r) * 16 + c] = pk2;
+    rows[w][0][(12 + r) * 16 + c] = pk3;
+    if (with_v) {
+      rows[w][1][(0 + r) * 16 + c] = pv0;
+      rows[w][1][(4 + r) * 16 + c] = pv1;
+      rows[w][1][(8 + r) * 16 + c] = pv2;
+      rows[w][1][(12 + r) * 16 + c] = pv3;
     }
   };
   auto load_rec = [&](int pg, int buf) __attribute__((always_inline)) {
@@ -360,7 +397,6 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     }
   };
   const float sl2 = a.scale * 1.4426950408889634f;  // softmax scale in log2 units
-  const int npages = (L + KVQ_PAGE - 1) / KVQ_PAGE;
   const uint8_t *krow = reinterpret_cast<const uint8_t *>(rows[w][0]);
   const uint8_t *vrow = reinterpret_cast<const uint8_t *>(rows[w][1]);
 
@@ -403,97 +439,140 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     }
   };
 
-  // ---- pass 1 ----
-  float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f, ds_max = 0.f, ds_sq = 0.f;
-  float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;  // key reconstruction error (lead group)
-  PageRegs pr;
   int buf = 0;
-  if (w < npages) {
-    load_rows(w, pr, false);
-    load_rec(w, 0);
-  }
-  for (int pg = w; pg < npages; pg += EB_WAVES, buf ^= 1) {
-    const int t0 = pg * KVQ_PAGE;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page's rows and record have landed
-    store_rows(pr, false);
-    if (pg + EB_WAVES < npages) {
-      load_rows(pg + EB_WAVES, pr, false);
-      load_rec(pg + EB_WAVES, buf ^ 1);
+  if constexpr (PASS == 1) {
+    float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f, ds_max = 0.f, ds_sq = 0.f;
+    float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;  // key reconstruction error (head group 0)
+    if (pbeg + w < pend) {
+      load_rows(pbeg + w, false);
+      load_rec(pbeg + w, 0);
     }
-    const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
-    float s0, s1;
-    page_scores(rs, t0, s0, s1);
-    if (qlive && t0 + t < L) {
-      const float x0 = s0 * sl2, x1 = s1 * sl2;
-      const float n0 = __builtin_fmaxf(m0, x0), n1 = __builtin_fmaxf(m1, x1);
-      z0 = z0 * __builtin_amdgcn_exp2f(m0 - n0) + __builtin_amdgcn_exp2f(x0 - n0);
-      z1 = z1 * __builtin_amdgcn_exp2f(m1 - n1) + __builtin_amdgcn_exp2f(x1 - n1);
-      m0 = n0;
-      m1 = n1;
-      const float ds = (s1 - s0) * a.scale;
-      ds_max = __builtin_fmaxf(ds_max, __builtin_fabsf(ds));
-      ds_sq = __builtin_fmaf(ds, ds, ds_sq);
-    }
-    if (unit_lead) {  // key reconstruction errors, 8 channels of positions 4 i + r per lane
+    for (int pg = pbeg + w; pg < pend; pg += EB_WAVES, buf ^= 1) {
+      const int t0 = pg * KVQ_PAGE;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page's rows and record have landed
+      store_rows(false);
+      if (pg + EB_WAVES < pend) {
+        load_rows(pg + EB_WAVES, false);
+        load_rec(pg + EB_WAVES, buf ^ 1);
+      }
+      const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
+      float s0, s1;
+      page_scores(rs, t0, s0, s1);
+      if (qlive && t0 + t < L) {
+        const float x0 = s0 * sl2, x1 = s1 * sl2;
+        const float n0 = __builtin_fmaxf(m0, x0), n1 = __builtin_fmaxf(m1, x1);
+        z0 = z0 * __builtin_amdgcn_exp2f(m0 - n0) + __builtin_amdgcn_exp2f(x0 - n0);
+        z1 = z1 * __builtin_amdgcn_exp2f(m1 - n1) + __builtin_amdgcn_exp2f(x1 - n1);
+        m0 = n0;
+        m1 = n1;
+        const float ds = (s1 - s0) * a.scale;
+        ds_max = __builtin_fmaxf(ds_max, __builtin_fabsf(ds));
+        ds_sq = __builtin_fmaf(ds, ds, ds_sq);
+      }
+      if (krec) {  // key reconstruction errors, 8 channels of positions 4 i + r per lane
 #pragma unroll 1
-      for (int it = 0; it < 4; ++it) {
-        const int n = 4 * it + r;
-        const bool quant = t0 + n < nq;  // (positions past L are not quantized either)
-        float k[8], kh[8];
-        bf16x8(rows[w][0][n * 16 + c], k);
+        for (int it = 0; it < 4; ++it) {
+          const int n = 4 * it + r;
+          const bool quant = t0 + n < nq;  // (positions past L are not quantized either)
+          float k[8], kh[8];
+          bf16x8(rows[w][0][n * 16 + c], k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kh[e] = 0.f;
-        if (quant) decode8<true>(lay, KP, rs, n, c, kh);
-        if (a.rotation) row_wht(kh, c, quant);  // back to the original domain
-        if (quant) {
+          for (int e = 0; e < 8; ++e) kh[e] = 0.f;
+          if (quant) decode8<true>(lay, KP, rs, n, c, kh);
+          if (a.rotation) row_wht(kh, c, quant);  // back to the original domain
+          if (quant) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float err = kh[e] - k[e];
-            ek_sq = __builtin_fmaf(err, err, ek_sq);
-            ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
-            k_sq = __builtin_fmaf(k[e], k[e], k_sq);
+            for (int e = 0; e < 8; ++e) {
+              const float err = kh[e] - k[e];
+              ek_sq = __builtin_fmaf(err, err, ek_sq);
+              ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
+              k_sq = __builtin_fmaf(k[e], k[e], k_sq);
+            }
           }
         }
       }
     }
-  }
-  // merge the 16 tokens of a head (one lane row), then the waves
-  {
-    const float M0 = row16_max(m0), M1 = row16_max(m1);
-    const float Z0 = row16_sum(M0 == ninf ? 0.f : z0 * __builtin_amdgcn_exp2f(m0 - M0));
-    const float Z1 = row16_sum(M1 == ninf ? 0.f : z1 * __builtin_amdgcn_exp2f(m1 - M1));
-    const float dmx = row16_max(ds_max), dsq = row16_sum(ds_sq);
-    if (qlive && t == 0) {
-      red[w][6 * q + 0] = M0;
-      red[w][6 * q + 1] = Z0;
-      red[w][6 * q + 2] = M1;
-      red[w][6 * q + 3] = Z1;
-      red[w][6 * q + 4] = dmx;
-      red[w][6 * q + 5] = dsq;
+    // merge the 16 tokens of a head (one lane row), then the waves
+    {
+      const float M0 = row16_max(m0), M1 = row16_max(m1);
+      const float Z0 = row16_sum(M0 == ninf ? 0.f : z0 * __builtin_amdgcn_exp2f(m0 - M0));
+      const float Z1 = row16_sum(M1 == ninf ? 0.f : z1 * __builtin_amdgcn_exp2f(m1 - M1));
+      const float dmx = row16_max(ds_max), dsq = row16_sum(ds_sq);
+      if (qlive && t == 0) {
+        red[w][6 * q + 0] = M0;
+        red[w][6 * q + 1] = Z0;
+        red[w][6 * q + 2] = M1;
+        red[w][6 * q + 3] = Z1;
+        red[w][6 * q + 4] = dmx;
+        red[w][6 * q + 5] = dsq;
+      }
     }
+    if (krec) {
+      for (int off = 1; off <= 32; off <<= 1) {
+        ek_sq += __shfl_xor(ek_sq, off);
+        k_sq += __shfl_xor(k_sq, off);
+        ek_max = __builtin_fmaxf(ek_max, __shfl_xor(ek_max, off));
+      }
+      if (lane == 0) {
+        ured[w][0] = ek_sq;
+        ured[w][1] = ek_max;
+        ured[w][2] = k_sq;
+      }
+    }
+    __syncthreads();
+    if (w == 0 && lane < HS) {  // lane j: head j's statistics over the item's pages
+      const int j = lane;
+      float M0 = ninf, M1 = ninf;
+      for (int i = 0; i < EB_WAVES; ++i) {
+        M0 = __builtin_fmaxf(M0, red[i][6 * j + 0]);
+        M1 = __builtin_fmaxf(M1, red[i][6 * j + 2]);
+      }
+      float Z0 = 0.f, Z1 = 0.f, dmx = 0.f, dsq = 0.f;
+      for (int i = 0; i < EB_WAVES; ++i) {
+        if (red[i][6 * j + 0] != ninf) Z0 += red[i][6 * j + 1] * __builtin_amdgcn_exp2f(red[i][6 * j + 0] - M0);
+        if (red[i][6 * j + 2] != ninf) Z1 += red[i][6 * j + 3] * __builtin_amdgcn_exp2f(red[i][6 * j + 2] - M1);
+        dmx = __builtin_fmaxf(dmx, red[i][6 * j + 4]);
+        dsq += red[i][6 * j + 5];
+      }
+      float *st = ws + EB_W_STATS + 6 * j;
+      st[0] = M0;
+      st[1] = Z0;
+      st[2] = M1;
+      st[3] = Z1;
+      st[4] = dmx;
+      st[5] = dsq;
+    }
+    if (krec && w == 0 && lane == 0) {
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+      for (int i = 0; i < EB_WAVES; ++i) {
+        s0 += ured[i][0];
+        s1 = __builtin_fmaxf(s1, ured[i][1]);
+        s2 += ured[i][2];
+      }
+      ws[EB_W_KREC + 0] = s0;
+      ws[EB_W_KREC + 1] = s1;
+      ws[EB_W_KREC + 2] = s2;
+    }
+    return;
   }
-  __syncthreads();
-  // every lane of a head takes the head's merged statistics (the same order in every wave)
-  float M0 = ninf, M1 = ninf, iZ0 = 0.f, iZ1 = 0.f, dmx_h = 0.f, dsq_h = 0.f;
+
+  // ---- pass 2: the head's maxima and sums over all ranges of the sequence ----
+  float M0 = ninf, M1 = ninf, iZ0 = 0.f, iZ1 = 0.f;
   {
-    const int qq = qlive ? q : 0;
-    for (int i = 0; i < EB_WAVES; ++i) {
-      M0 = __builtin_fmaxf(M0, red[i][6 * qq + 0]);
-      M1 = __builtin_fmaxf(M1, red[i][6 * qq + 2]);
+    const float *st0 = a.ws + (size_t)(unit * ngrp + grp) * S * EB_W_ITEM + EB_W_STATS + 6 * (qlive ? q : 0);
+    for (int s = 0; s < S; ++s) {
+      M0 = __builtin_fmaxf(M0, st0[(size_t)s * EB_W_ITEM + 0]);
+      M1 = __builtin_fmaxf(M1, st0[(size_t)s * EB_W_ITEM + 2]);
     }
     float Z0 = 0.f, Z1 = 0.f;
-    for (int i = 0; i < EB_WAVES; ++i) {
-      if (red[i][6 * qq + 0] != ninf) Z0 += red[i][6 * qq + 1] * __builtin_amdgcn_exp2f(red[i][6 * qq + 0] - M0);
-      if (red[i][6 * qq + 2] != ninf) Z1 += red[i][6 * qq + 3] * __builtin_amdgcn_exp2f(red[i][6 * qq + 2] - M1);
-      dmx_h = __builtin_fmaxf(dmx_h, red[i][6 * qq + 4]);
-      dsq_h += red[i][6 * qq + 5];
+    for (int s = 0; s < S; ++s) {
+      const float *st = st0 + (size_t)s * EB_W_ITEM;
+      if (st[0] != ninf) Z0 += st[1] * __builtin_amdgcn_exp2f(st[0] - M0);
+      if (st[2] != ninf) Z1 += st[3] * __builtin_amdgcn_exp2f(st[2] - M1);
     }
     iZ0 = Z0 > 0.f ? 1.f / Z0 : 0.f;
     iZ1 = Z1 > 0.f ? 1.f / Z1 : 0.f;
   }
-  __syncthreads();
-
-  // ---- pass 2 ----
   float tv = 0.f;
   float zs[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // weighted zero points: set x value group (this lane's head)
   eb_f4 Dr[8], Dc[8];                        // value sums per 16-channel tile: original values, codes
@@ -501,17 +580,16 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   for (int m = 0; m < 8; ++m) Dr[m] = Dc[m] = eb_f4{0.f, 0.f, 0.f, 0.f};
   float ev_sq = 0.f, ev_max = 0.f, v_sq = 0.f;
   const int nvg = lay.nvg;
-  buf = 0;
-  if (w < npages) {
-    load_rows(w, pr, true);
-    load_rec(w, 0);
+  if (pbeg + w < pend) {
+    load_rows(pbeg + w, true);
+    load_rec(pbeg + w, 0);
   }
-  for (int pg = w; pg < npages; pg += EB_WAVES, buf ^= 1) {
+  for (int pg = pbeg + w; pg < pend; pg += EB_WAVES, buf ^= 1) {
     const int t0 = pg * KVQ_PAGE;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    store_rows(pr, true);
-    if (pg + EB_WAVES < npages) {
-      load_rows(pg + EB_WAVES, pr, true);
+    store_rows(true);
+    if (pg + EB_WAVES < pend) {
+      load_rows(pg + EB_WAVES, true);
       load_rec(pg + EB_WAVES, buf ^ 1);
     }
     const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
@@ -577,7 +655,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       }
       Dc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k((m < 4 || nvg == 1) ? ac0 : ac1, pack4s(c0, c1), Dc[m], 0, 0, 0);
     }
-    if (unit_lead) {  // value reconstruction errors
+    if (vrec) {  // value reconstruction errors
 #pragma unroll 1
       for (int it = 0; it < 4; ++it) {
         const int n = 4 * it + r;
@@ -612,7 +690,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       for (int v = 0; v < 2; ++v) zt[set][v] = row16_sum(zs[set][v]);
     }
     if (qlive && t == 0) {
-      tvred[w][q] = tvt;
+      red[w][q] = tvt;
 #pragma unroll
       for (int set = 0; set < 2; ++set) {
 #pragma unroll
@@ -620,24 +698,20 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       }
     }
   }
-  if (unit_lead) {
+  if (vrec) {
     for (int off = 1; off <= 32; off <<= 1) {
-      ek_sq += __shfl_xor(ek_sq, off);
-      k_sq += __shfl_xor(k_sq, off);
       ev_sq += __shfl_xor(ev_sq, off);
       v_sq += __shfl_xor(v_sq, off);
-      ek_max = __builtin_fmaxf(ek_max, __shfl_xor(ek_max, off));
       ev_max = __builtin_fmaxf(ev_max, __shfl_xor(ev_max, off));
     }
     if (lane == 0) {
-      ured[w][0] = ek_sq;
-      ured[w][1] = ev_sq;
-      ured[w][2] = ek_max;
-      ured[w][3] = ev_max;
-      ured[w][4] = k_sq;
-      ured[w][5] = v_sq;
+      ured[w][0] = ev_sq;
+      ured[w][1] = ev_max;
+      ured[w][2] = v_sq;
     }
   }
+  __syncthreads();  // every wave is past its pages: the rows' LDS becomes the sums
+  for (int i = threadIdx.x; i < 4 * HS * KVQ_D; i += 64 * EB_WAVES) (&accs[0][0][0])[i] = 0.f;
   __syncthreads();
   // value sums: D row 4 (l / 16) + r of lane l = (set, part, head r) = (l / 32, (l / 16) mod 2, r);
   // the hi and lo parts are added across lanes l and l ^ 16; one wave at a time into LDS
@@ -663,66 +737,106 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       __syncthreads();
     }
   }
-  // wave j < HS finishes head j: norms over the channels (lane l takes channels 2l, 2l + 1)
-  if (w < HS) {
-    const int j = w;
-    float tvj = 0.f, dmx = 0.f, dsq = 0.f;
-    for (int i = 0; i < EB_WAVES; ++i) {
-      tvj += tvred[i][j];
-      dmx = __builtin_fmaxf(dmx, red[i][6 * j + 4]);
-      dsq += red[i][6 * j + 5];
-    }
-    float o2[2], v2[2], k2[2], j2[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      o2[e] = accs[0][j][2 * lane + e];
-      v2[e] = accs[1][j][2 * lane + e];
-      k2[e] = accs[2][j][2 * lane + e];
-      j2[e] = accs[3][j][2 * lane + e];
-    }
-    // sums over rotated values are in the rotated domain: rotated back
-    if (a.value_rotation) {
-      pair_wht(v2[0], v2[1], lane);
-      pair_wht(j2[0], j2[1], lane);
-    }
-    float nv = 0.f, nk = 0.f, nj = 0.f, no = 0.f;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float oo = o2[e];
-      const float dv = v2[e] - oo, dk = k2[e] - oo, dj = j2[e] - oo;
-      nv = __builtin_fmaf(dv, dv, nv);
-      nk = __builtin_fmaf(dk, dk, nk);
-      nj = __builtin_fmaf(dj, dj, nj);
-      no = __builtin_fmaf(oo, oo, no);
-    }
-    for (int off = 1; off <= 32; off <<= 1) {
-      nv += __shfl_xor(nv, off);
-      nk += __shfl_xor(nk, off);
-      nj += __shfl_xor(nj, off);
-      no += __shfl_xor(no, off);
-    }
-    float *hs = a.head_stats + ((size_t)b * a.Hq + hq0 + j) * KVQ_EB_HEAD;
-    if (lane == 0) {
-      const float n = (float)L;
-      hs[0] = dmx;
-      hs[1] = L > 0 ? sqrtf(dsq / n) : 0.f;
-      hs[2] = 0.5f * tvj;
-      hs[3] = sqrtf(nv);
-      hs[4] = sqrtf(nk);
-      hs[5] = sqrtf(nj);
-      hs[6] = sqrtf(no);
-      hs[7] = 0.f;
-    }
+  // the item's sums, total variation and value reconstruction to the workspace
+  for (int i = threadIdx.x; i < 4 * HS * KVQ_D; i += 64 * EB_WAVES) {
+    const int s = i / (HS * KVQ_D), j = (i / KVQ_D) % HS, ch = i % KVQ_D;
+    ws[EB_W_SUMS + (4 * s + j) * KVQ_D + ch] = accs[s][j][ch];
   }
-  if (unit_lead && w == 0 && lane == 0) {
-    float s[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (w == 0 && lane < HS) {
+    float tvj = 0.f;
+    for (int i = 0; i < EB_WAVES; ++i) tvj += red[i][lane];
+    ws[EB_W_TV + lane] = tvj;
+  }
+  if (vrec && w == 0 && lane == 0) {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f;
     for (int i = 0; i < EB_WAVES; ++i) {
-      s[0] += ured[i][0];
-      s[1] += ured[i][1];
-      s[2] = __builtin_fmaxf(s[2], ured[i][2]);
-      s[3] = __builtin_fmaxf(s[3], ured[i][3]);
-      s[4] += ured[i][4];
-      s[5] += ured[i][5];
+      s0 += ured[i][0];
+      s1 = __builtin_fmaxf(s1, ured[i][1]);
+      s2 += ured[i][2];
+    }
+    ws[EB_W_VREC + 0] = s0;
+    ws[EB_W_VREC + 1] = s1;
+    ws[EB_W_VREC + 2] = s2;
+  }
+}
+
+// One workgroup of HS waves per (kv head unit, head group): wave j adds the S ranges' sums of head
+// j (lane l: channels 2l, 2l + 1) and writes its statistics; the unit's reconstruction errors come
+// from head group 0 (keys) and the last head group (values).
+template <int HS>
+__global__ __launch_bounds__(64 * HS) void kvq_errbudget_final_kernel(KvqErrArgs a) {
+  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int Hkv = a.Hkv, g = a.Hq / a.Hkv, ngrp = g / HS, S = a.splits;
+  const int unit = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
+  const int b = unit / Hkv, h = unit % Hkv;
+  const int hq0 = h * g + grp * HS;
+  int L = (int)a.seq_lens[b];
+  L = L < 0 ? 0 : ((int64_t)L > a.max_len ? (int)a.max_len : L);
+  int nq = L > a.R ? L - a.R : 0;
+  const int64_t cap_tokens = (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq) * KVQ_PAGE;
+  if ((int64_t)nq > cap_tokens) nq = (int)cap_tokens;
+  const float *it0 = a.ws + (size_t)(unit * ngrp + grp) * S * EB_W_ITEM;
+  float o2[2] = {0.f, 0.f}, v2[2] = {0.f, 0.f}, k2[2] = {0.f, 0.f}, j2[2] = {0.f, 0.f};
+  float tvj = 0.f, dmx = 0.f, dsq = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float *it = it0 + (size_t)s * EB_W_ITEM;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int ch = 2 * lane + e;
+      o2[e] += it[EB_W_SUMS + (4 * 0 + j) * KVQ_D + ch];
+      v2[e] += it[EB_W_SUMS + (4 * 1 + j) * KVQ_D + ch];
+      k2[e] += it[EB_W_SUMS + (4 * 2 + j) * KVQ_D + ch];
+      j2[e] += it[EB_W_SUMS + (4 * 3 + j) * KVQ_D + ch];
+    }
+    tvj += it[EB_W_TV + j];
+    dmx = __builtin_fmaxf(dmx, it[EB_W_STATS + 6 * j + 4]);
+    dsq += it[EB_W_STATS + 6 * j + 5];
+  }
+  // sums over rotated values are in the rotated domain: rotated back
+  if (a.value_rotation) {
+    pair_wht(v2[0], v2[1], lane);
+    pair_wht(j2[0], j2[1], lane);
+  }
+  float nv = 0.f, nk = 0.f, nj = 0.f, no = 0.f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float oo = o2[e];
+    const float dv = v2[e] - oo, dk = k2[e] - oo, dj = j2[e] - oo;
+    nv = __builtin_fmaf(dv, dv, nv);
+    nk = __builtin_fmaf(dk, dk, nk);
+    nj = __builtin_fmaf(dj, dj, nj);
+    no = __builtin_fmaf(oo, oo, no);
+  }
+  for (int off = 1; off <= 32; off <<= 1) {
+    nv += __shfl_xor(nv, off);
+    nk += __shfl_xor(nk, off);
+    nj += __shfl_xor(nj, off);
+    no += __shfl_xor(no, off);
+  }
+  float *hs = a.head_stats + ((size_t)b * a.Hq + hq0 + j) * KVQ_EB_HEAD;
+  if (lane == 0) {
+    const float n = (float)L;
+    hs[0] = dmx;
+    hs[1] = L > 0 ? sqrtf(dsq / n) : 0.f;
+    hs[2] = 0.5f * tvj;
+    hs[3] = sqrtf(nv);
+    hs[4] = sqrtf(nk);
+    hs[5] = sqrtf(nj);
+    hs[6] = sqrtf(no);
+    hs[7] = 0.f;
+  }
+  if (grp == 0 && j == 0 && lane == 0) {
+    const float *kit = a.ws + (size_t)(unit * ngrp + 0) * S * EB_W_ITEM;
+    const float *vit = a.ws + (size_t)(unit * ngrp + ngrp - 1) * S * EB_W_ITEM;
+    float s[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < S; ++sp) {
+      const float *kr = kit + (size_t)sp * EB_W_ITEM + EB_W_KREC, *vr = vit + (size_t)sp * EB_W_ITEM + EB_W_VREC;
+      s[0] += kr[0];
+      s[2] = __builtin_fmaxf(s[2], kr[1]);
+      s[4] += kr[2];
+      s[1] += vr[0];
+      s[3] = __builtin_fmaxf(s[3], vr[1]);
+      s[5] += vr[2];
     }
     float *us = a.unit_stats + ((size_t)b * Hkv + h) * KVQ_EB_UNIT;
     us[0] = s[0];
@@ -736,19 +850,29 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   }
 }
 
+template <int HS>
+void launch_eb(const KvqErrArgs &a, int ngrp, hipStream_t s) {
+  const int wus = a.B * a.Hkv * a.splits;
+  // groups of 8 work units, each group's head groups 8 workgroups apart (padding after the last)
+  const dim3 grid((unsigned)(((wus + 7) / 8) * 8 * ngrp)), block(64 * EB_WAVES);
+  hipLaunchKernelGGL((kvq_errbudget_kernel<HS, 1>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((kvq_errbudget_kernel<HS, 2>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((kvq_errbudget_final_kernel<HS>), dim3((unsigned)(a.B * a.Hkv * ngrp)), dim3(64 * HS), 0, s, a);
+}
+
 }  // namespace
+
+int kvq_errbudget_heads_per_group(int g) { return g < 4 ? g : 4; }
+size_t kvq_errbudget_item_floats() { return EB_W_ITEM; }
 
 hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   (void)hipGetLastError();  // drop a stale error left by an earlier, unrelated call
-  // up to two heads per group (one workgroup per group keeps the grid near two per CU's worth)
-  const int g = a.Hq / a.Hkv, hs = g < 2 ? g : 2;
-  const int units = a.B * a.Hkv;
-  // groups of 8 units, each group's head groups 8 workgroups apart (padding after the last unit)
-  const dim3 grid((unsigned)(((units + 7) / 8) * 8 * (g / hs))), block(64 * EB_WAVES);
-  if (hs == 1)
-    hipLaunchKernelGGL(kvq_errbudget_kernel<1>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(kvq_errbudget_kernel<2>, grid, block, 0, s, a);
+  const int g = a.Hq / a.Hkv, hs = kvq_errbudget_heads_per_group(g);
+  switch (hs) {
+    case 1: launch_eb<1>(a, g / hs, s); break;
+    case 2: launch_eb<2>(a, g / hs, s); break;
+    default: launch_eb<4>(a, g / hs, s); break;
+  }
   return hipGetLastError();
 }

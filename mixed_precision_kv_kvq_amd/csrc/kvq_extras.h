@@ -32,5 +32,9 @@ struct KvqErrArgs {
   int32_t B, Hq, Hkv, R, q_f32;
   int32_t rotation, value_rotation;  // stored keys / values are rotated
   float scale;
+  float *ws;       // workspace: kvq_errbudget_item_floats() floats per (unit, head group, range)
+  int32_t splits;  // ranges of pages per sequence
 };
+int kvq_errbudget_heads_per_group(int g);
+size_t kvq_errbudget_item_floats();
 hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s);

@@ -213,20 +213,41 @@ def test_unfused_baseline_validation():
 
 def test_error_budget_validation():
     L = K.lib()
+    need = K.kvq_error_budget_workspace_bytes(p(), 2, 64)
 
-    def call(prm_=None, c=None, seq=FAKE, mx=64, kr=FAKE, vr=FAKE, q=FAKE, qd=K.KVQ_BF16, sc=0.0, hs=FAKE, us=FAKE):
+    def call(prm_=None, c=None, seq=FAKE, mx=64, kr=FAKE, vr=FAKE, q=FAKE, qd=K.KVQ_BF16, sc=0.0, hs=FAKE, us=FAKE,
+             ws=FAKE, wsb=need):
         return L.kvq_error_budget(ctypes.byref(prm_ or p()), ctypes.byref(c or cache()), seq, mx, kr, vr, q, qd, sc,
-                                  hs, us, None)
+                                  hs, us, ws, wsb, None)
 
     assert call(seq=None) == K.KVQ_EINVAL
     assert call(kr=None) == K.KVQ_EINVAL
     assert call(vr=FAKE + 2) == K.KVQ_EINVAL
     assert call(hs=FAKE + 4) == K.KVQ_EINVAL
     assert call(us=None) == K.KVQ_EINVAL
+    assert call(ws=None) == K.KVQ_EINVAL
+    assert call(ws=FAKE + 8) == K.KVQ_EINVAL
+    assert call(wsb=need - 4) == K.KVQ_ENOSPACE
     assert call(qd=4) == K.KVQ_EINVAL
     assert call(sc=-2.0) == K.KVQ_EINVAL
     assert call(mx=-1) == K.KVQ_EINVAL
     assert call(prm_=p(v_group=32)) == K.KVQ_EUNSUPPORTED
+
+
+def test_error_budget_workspace_plan():
+    # one item per (sequence, kv head, group of up to 4 query heads, range of pages); about one
+    # workgroup per CU, at least one page per wave of a range
+    item = 4 * (32 + 4 * 4 * 128 + 4 + 4)
+    units = 2 * 8  # batch 2 x 8 kv heads, 4 query heads per kv head: one head group
+    for length, ranges in [(0, 1), (1, 1), (128, 1), (129, 2), (16 * 8 * 16, 16), (32768, 16)]:
+        assert K.kvq_error_budget_workspace_bytes(p(), 2, length) == units * ranges * item, length
+    # 8 query heads per kv head: two head groups
+    assert K.kvq_error_budget_workspace_bytes(p(num_q_heads=64), 2, 32768) == 2 * units * 8 * item
+    # batch 16 x 8 kv heads: 128 items, two ranges each
+    assert K.kvq_error_budget_workspace_bytes(p(), 16, 32768) == 128 * 2 * item
+    assert K.kvq_error_budget_workspace_bytes(p(k_bits=9), 2, 600) == 0
+    assert K.kvq_error_budget_workspace_bytes(p(), 0, 600) == 0
+    assert K.kvq_error_budget_workspace_bytes(p(), 2, -1) == 0
 
 
 def test_status_strings():

@@ -63,7 +63,10 @@ def test_error_budget_matches_oracle(name):
     hs = torch.full((B, Hq, K.KVQ_EB_HEAD), float("nan"), dtype=torch.float32, device="cuda")
     us = torch.full((B, Hkv, K.KVQ_EB_UNIT), float("nan"), dtype=torch.float32, device="cuda")
     qd = K.KVQ_F32 if wl.q_dtype == "f32" else K.KVQ_BF16
-    K.kvq_error_budget(run.params, run.cache.struct, seq_lens, max_len, k_ref, v_ref, run._q_dev(0), qd, 0.0, hs, us)
+    wsb = K.kvq_error_budget_workspace_bytes(run.params, B, max_len)
+    ws = torch.full((wsb // 4,), float("nan"), dtype=torch.float32, device="cuda")  # no field may be read unwritten
+    K.kvq_error_budget(run.params, run.cache.struct, seq_lens, max_len, k_ref, v_ref, run._q_dev(0), qd, 0.0, hs, us,
+                       ws, wsb)
     torch.cuda.synchronize()
     hs = hs.cpu().numpy().astype(np.float64)
     us = us.cpu().numpy().astype(np.float64)

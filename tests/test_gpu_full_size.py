@@ -137,7 +137,10 @@ def test_full_config3_unfused_and_error_budget():
     v_ref = run.dgen.kv(W.TENSOR_V, 0, Lmax)
     hs = torch.empty((B, Hq, K.KVQ_EB_HEAD), dtype=torch.float32, device="cuda")
     us = torch.empty((B, Hkv, K.KVQ_EB_UNIT), dtype=torch.float32, device="cuda")
-    K.kvq_error_budget(run.params, run.cache.struct, seq_lens, Lmax, k_ref, v_ref, q_dev, K.KVQ_BF16, 0.0, hs, us)
+    ewsb = K.kvq_error_budget_workspace_bytes(run.params, B, Lmax)
+    ews = torch.full((ewsb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    K.kvq_error_budget(run.params, run.cache.struct, seq_lens, Lmax, k_ref, v_ref, q_dev, K.KVQ_BF16, 0.0, hs, us, ews,
+                       ewsb)
     torch.cuda.synchronize()
     o32 = o32.cpu().numpy()
     hs = hs.cpu().numpy().astype(np.float64)

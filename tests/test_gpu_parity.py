@@ -323,11 +323,16 @@ def test_outputs_deterministic_and_split_invariant():
             os.environ["KVQ_PAGES_PER_SPLIT"] = old
 
 
-def test_phase_entry_points_match_attention():
+@pytest.mark.parametrize("variant", ["window", "value-rotation"])
+def test_phase_entry_points_match_attention(variant):
     """kvq_decode_partials + kvq_decode_combine give bit for bit what kvq_decode_attention gives,
-    and the workspace rows follow the documented merge rule."""
-    wl = small(W.WORKLOADS[3], batch=2, context=700, steps=1, config=303)
-    say("partials + combine")
+    and the workspace rows follow the documented merge rule; with rotated values the merged row
+    is in the rotated domain and the normalized Hadamard matrix brings it back."""
+    if variant == "window":
+        wl = small(W.WORKLOADS[3], batch=2, context=700, steps=1, config=303)
+    else:
+        wl = small(W.WORKLOADS[3], batch=2, context=700, steps=0, window=0, value_rotation=True, config=305)
+    say(f"partials + combine ({variant})")
     run = GpuRun(wl, chunk=256)
     L = run.current_lengths()
     lens = torch.from_numpy(L.astype(np.int32)).cuda()
@@ -359,7 +364,11 @@ def test_phase_entry_points_match_attention():
     M = m.max(axis=2, keepdims=True)
     w = np.where(empty, 0.0, np.exp2(np.where(empty, 0.0, m - M)))
     o = (w[..., None] * acc).sum(axis=2) / (w * l).sum(axis=2)[..., None]
-    assert np.allclose(o, got, rtol=1e-5, atol=1e-6)
+    if wl.value_rotation:
+        from scipy.linalg import hadamard
+
+        o = o @ (hadamard(128).astype(np.float64) / np.sqrt(128.0))
+    assert np.allclose(o, got, rtol=1e-5, atol=2e-6)
 
 
 def test_graph_replays_match_eager():
