@@ -334,8 +334,9 @@ kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, c
  * rotated keys or values are rotated back first: every error is taken in the original domain.
  * The query is taken as bf16 hi + lo parts (exact for a bf16 query; about 16 significant bits of
  * an fp32 one) and must stay below 2^27 in magnitude.  workspace (device, 16-byte aligned) of at
- * least kvq_error_budget_workspace_bytes(params, cache->batch, max_seq_len) bytes holds the
- * per-range partial results of the three launches (statistics, weighted sums, merge); its
+ * least kvq_error_budget_workspace_bytes(params, cache->batch, max_seq_len) bytes (about
+ * 8 * batch * num_q_heads * max_seq_len) holds what the three launches pass on: per range of each
+ * sequence, the score statistics and the weighted sums, and both scores of every position; its
  * contents are not needed between calls.  Errors as for kvq_decode_attention, and KVQ_ENOSPACE
  * for a short workspace. */
 #define KVQ_EB_HEAD 8

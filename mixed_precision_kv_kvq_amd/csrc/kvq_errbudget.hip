@@ -195,39 +195,22 @@ __device__ __forceinline__ float row16_max(float v) {
 // A code of b bits read as a bf16 bit pattern is code * 2^-133 (c < 256).
 
 constexpr int EB_WAVES = 8;
-constexpr int EB_REC16 = (256 * 8 + 64 * 4 + 256 * 8 + 64 * 2) / 16;  // largest record, 16-byte units
-constexpr float EB_Q = 0x1p100f;  // query operand scale
+constexpr int EB_K16 = (256 * 8 + 64 * 4) / 16;  // largest key part of a record, 16-byte units
+constexpr int EB_V16 = (256 * 8 + 64 * 2) / 16;  // largest value part
+constexpr float EB_Q = 0x1p100f;                 // query operand scale
 
-// One workgroup of EB_WAVES waves per work item: a group of HS <= 4 query heads of one kv head and
-// sequence, and one of S consecutive ranges of the sequence's pages.  The head groups of a range
-// run on workgroups 8 apart (one XCD), so the second to read a page finds it in that XCD's L2.
-// Wave w of an item takes pages p0 + w, p0 + w + EB_WAVES, ...: a page's original rows and record
-// are loaded while the wave computes the page before, then stored to the wave's LDS region.
+// Work items: one workgroup of EB_WAVES waves per (group of HS <= 4 query heads of one kv head and
+// sequence, range): range `split` of S near-equal ranges of the sequence's pages.  The head groups
+// of a range run on workgroups 8 apart (one XCD), so the second to read a page finds it in that
+// XCD's L2.  Wave w of an item takes pages p0 + w, p0 + w + EB_WAVES, ...: a page's original rows
+// and record part are loaded while the wave computes the page before, then stored to the wave's
+// LDS region.
 //
-// Scores on MFMA (16x16x32 bf16): the query, scaled by 2^100 and split into bf16 hi and lo parts,
-// is the A operand (row 4 hs + j: head hs restricted to 32-channel chunk j); the B operand is the
-// page's original keys (exact bf16) for the exact scores and its key codes (code * 2^-133) for the
-// quantized ones, so D row 4 q + r of lane 16 q + t holds head q's dot with chunk r of token t.
-// The quantized score applies the token's group scales and zero points:
-// s' = sum_r scale_r (q . c)_r + sum_g zero_g sum(q over g).  With rotated keys the code scores
-// use the rotated query (the normalized transform is orthogonal); window tokens are stored exact
-// (s' = s).  Lane 16 q + t then holds both scores of token t for head q.
-//
-// PASS 1: online maxima and sums of both score sets (log2 units) and the score-error statistics
-// over the item's pages, merged over the 16 lanes of a head and the waves, to the workspace.
-// PASS 2: the maxima and sums of all ranges merged; the weights a (exact keys) and a' (quantized
-// keys), their total variation, and the four weighted sums on MFMA (16x16x16 bf16, k = the page's
-// 16 tokens): A rows 8 set + 4 part + q hold the weights of set a / a' (hi and lo parts) of head q,
-// through a per-wave LDS exchange buffer; B is the original values (exact bf16: a V, a' V) or the
-// value codes (a V_hat, a' V_hat; A = weight * scale * 2^64, window tokens take their exact values
-// as B with A = weight * 2^-69, so every product carries 2^-69), plus the weighted zero points;
-// the range's sums to the workspace (the weights are final, so the ranges' sums add).  Key
-// reconstruction errors are taken in pass 1 by head group 0, value ones in pass 2 by the last
-// head group (per element, 8 channels per lane).
-//
-// Workspace item (floats, one per (kv head unit, head group, range)): pass-1 statistics of each
-// head {M0, Z0, M1, Z1, max |ds|, sum ds^2}, key reconstruction {sum e^2, max |e|, sum k^2}, then
-// the four sums [sum][head][channel], the total variation of each head, value reconstruction.
+// Workspace: one item of EB_W_ITEM floats per (kv head unit, head group, range), then the scores
+// [batch][query head][max_len][2] (exact, quantized; dot units) that pass 1 writes for pass 2.  An
+// item holds the pass-1 statistics of each head {M0, Z0, M1, Z1, max |ds|, sum ds^2}, the key
+// reconstruction sums {sum e^2, max |e|, sum k^2}, then the pass-2 sums [sum][head][channel] of
+// a V, a V_hat, a' V, a' V_hat, the total variation of each head and the value reconstruction sums.
 constexpr int EB_W_STATS = 0;
 constexpr int EB_W_KREC = 24;
 constexpr int EB_W_SUMS = 32;
@@ -235,60 +218,96 @@ constexpr int EB_W_TV = EB_W_SUMS + 4 * 4 * KVQ_D;
 constexpr int EB_W_VREC = EB_W_TV + 4;
 constexpr int EB_W_ITEM = EB_W_VREC + 4;
 
-template <int HS, int PASS>
-__global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs a) {
-  __shared__ float red[EB_WAVES][6 * HS];
-  __shared__ float ured[EB_WAVES][3];
-  __shared__ float qg[HS][4];                 // sums of the code query over each key group
-  __shared__ float zred[EB_WAVES][2][HS][2];  // weighted zero points (set, head, value group)
-  __shared__ uint4 recs[EB_WAVES][2][EB_REC16];       // page records (two: the next one lands meanwhile)
-  __shared__ uint4 rows[EB_WAVES][2][KVQ_PAGE * 16];  // the page's original K and V rows
-  __shared__ uint32_t xbuf[EB_WAVES][3][16][8];        // value A operands: [raw, code v0, code v1][row][16 bf16]
-  // before the page loop: the group's queries (raw, and the one the codes are scored with); after
-  // it: the four weighted sums of the workgroup
-  float(*qs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&rows[0][0][0]);
-  float(*accs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&rows[0][0][0]);
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: page loop and record addresses in SGPRs
-  const int r = lane >> 4, c = lane & 15;       // element layout: row r, 8 channels [8c, 8c + 8)
-  const int q = lane >> 4, t = lane & 15;       // score layout: head q, token t
+struct EbItem {
+  int unit, grp, split, b, h, hq0, L, nq, pbeg, pend;
+  float *ws;
+};
+// workgroup -> item: work unit wu = unit S + range; the head groups of wu at blocks
+// 8 ngrp (wu / 8) + 8 grp + wu mod 8.  False for the padding after the last group of 8 work units.
+template <int HS>
+__device__ __forceinline__ bool eb_item(const KvqErrArgs &a, EbItem &it) {
   const int Hkv = a.Hkv, g = a.Hq / a.Hkv, ngrp = g / HS, S = a.splits;
-  // workgroup -> (unit, range, head group): work unit wu = unit S + range; the groups of wu at
-  // blocks 8 ngrp (wu / 8) + 8 grp + wu mod 8
   const int blk = blockIdx.x / (8 * ngrp), rem = blockIdx.x % (8 * ngrp);
-  const int grp = rem / 8, wu = 8 * blk + rem % 8;
-  if (wu >= a.B * Hkv * S) return;  // padding of the last group of 8 work units
-  const int unit = wu / S, split = wu % S;
-  const int b = unit / Hkv, h = unit % Hkv;
-  const int hq0 = h * g + grp * HS;  // first query head of the group
-  float *ws = a.ws + (size_t)((unit * ngrp + grp) * S + split) * EB_W_ITEM;
-  const bool krec = PASS == 1 && grp == 0, vrec = PASS == 2 && grp == ngrp - 1;
-  int L = (int)a.seq_lens[b];
-  if (PASS == 1) kvq_raise(a.cache, hq0 == 0 && split == 0 && (L < 0 || (int64_t)L > a.max_len), KVQ_DEV_LENGTH);
+  it.grp = rem / 8;
+  const int wu = 8 * blk + rem % 8;
+  if (wu >= a.B * Hkv * S) return false;
+  it.unit = wu / S;
+  it.split = wu % S;
+  it.b = it.unit / Hkv;
+  it.h = it.unit % Hkv;
+  it.hq0 = it.h * g + it.grp * HS;
+  it.ws = a.ws + (size_t)((it.unit * ngrp + it.grp) * S + it.split) * EB_W_ITEM;
+  int L = (int)a.seq_lens[it.b];
   L = L < 0 ? 0 : ((int64_t)L > a.max_len ? (int)a.max_len : L);
   int nq = L > a.R ? L - a.R : 0;
   const int64_t cap_tokens = (a.cache.paged ? (int64_t)a.cache.mbps : a.cache.pages_per_seq) * KVQ_PAGE;
   if ((int64_t)nq > cap_tokens) nq = (int)cap_tokens;
-  const float ninf = -__builtin_inff();
-  const KvqLayout &lay = a.lay;
-  const int rec16 = lay.record / 16;
-  const EbPlanes KP = eb_planes(lay.kb), VP = eb_planes(lay.vb);
-  const bool qlive = q < HS;  // score-layout lanes of a head of the group
-  // the item's pages: range `split` of S near-equal ranges
+  it.L = L;
+  it.nq = nq;
   const int npages = (L + KVQ_PAGE - 1) / KVQ_PAGE;
   const int per = (npages + S - 1) / S;
-  const int pbeg = split * per < npages ? split * per : npages;
-  const int pend = pbeg + per < npages ? pbeg + per : npages;
+  it.pbeg = it.split * per < npages ? it.split * per : npages;
+  it.pend = it.pbeg + per < npages ? it.pbeg + per : npages;
+  return true;
+}
+
+// DMA of bytes [from, from + 16 n16) of page pg's record into LDS at dst (per wave; every lane of
+// the wave takes part, nothing for a page without quantized positions).
+__device__ __forceinline__ void eb_load_rec(const KvqErrArgs &a, const EbItem &it, int pg, int from, int n16,
+                                            uint32_t dst, int lane, int max16) {
+  if (pg * KVQ_PAGE >= it.nq) return;
+  const int64_t rec_idx = kvq_record_index_dev(a.cache, a.Hkv, it.b, it.h, pg);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.cache.pages + (size_t)rec_idx * a.lay.record + from), 0, 16 * n16, 0x00020000);
+  for (int i = 0; i < (max16 + 63) / 64; ++i) {
+    if (64 * i < n16 && lane + 64 * i < n16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(size_t)(dst + 1024u * i), 16, 16 * (lane + 64 * i), 0,
+                                               0, 0);
+  }
+}
+
+// PASS 1, scores and their statistics.  Scores on MFMA (16x16x32 bf16): the query, scaled by 2^100
+// and split into bf16 hi and lo parts, is the A operand (row 4 hs + j: head hs restricted to
+// 32-channel chunk j); the B operand is the page's original keys (exact bf16) for the exact scores
+// and its key codes (code * 2^-133) for the quantized ones, so D row 4 q + r of lane 16 q + t holds
+// head q's dot with chunk r of token t.  The quantized score applies the token's group scales and
+// zero points: s' = sum_r scale_r (q . c)_r + sum_g zero_g sum(q over g).  With rotated keys the
+// code scores use the rotated query (the normalized transform is orthogonal); window tokens are
+// stored exact (s' = s).  Lane 16 q + t then holds both scores of token t for head q: written to the
+// workspace, and folded into online maxima and sums (log2 units) and the score-error statistics,
+// merged over the 16 lanes of a head and the waves.  Head group 0 also takes the key
+// reconstruction errors (8 channels of a position per lane).
+template <int HS>
+__global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_scores_kernel(KvqErrArgs a) {
+  __shared__ float red[EB_WAVES][6 * HS];
+  __shared__ float ured[EB_WAVES][3];
+  __shared__ float qg[HS][4];                    // sums of the code query over each key group
+  __shared__ uint4 recs[EB_WAVES][2][EB_K16];    // key parts of page records (the next one lands meanwhile)
+  __shared__ uint4 rows[EB_WAVES][KVQ_PAGE * 16];  // the page's original key rows
+  // before the page loop: the group's queries (raw, and the one the codes are scored with)
+  float(*qs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&rows[0][0]);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: page loop and record addresses in SGPRs
+  const int r = lane >> 4, c = lane & 15;  // element layout: row r, 8 channels [8c, 8c + 8)
+  const int q = lane >> 4, t = lane & 15;  // score layout: head q, token t
+  EbItem it;
+  if (!eb_item<HS>(a, it)) return;
+  const int b = it.b, h = it.h, L = it.L, nq = it.nq, pbeg = it.pbeg, pend = it.pend;
+  {
+    const int raw = (int)a.seq_lens[b];
+    kvq_raise(a.cache, it.hq0 == 0 && it.split == 0 && (raw < 0 || (int64_t)raw > a.max_len), KVQ_DEV_LENGTH);
+  }
+  const bool krec = it.grp == 0;
+  const float ninf = -__builtin_inff();
+  const KvqLayout &lay = a.lay;
+  const EbPlanes KP = eb_planes(lay.kb);
+  const bool qlive = q < HS;  // score-layout lanes of a head of the group
 
   // ---- queries: raw and code-scoring (rotated when keys are) rows, and the group sums ----
-  if (HS < 4) {
-    for (int i = threadIdx.x; i < 3 * 16 * 8 * EB_WAVES; i += 64 * EB_WAVES)
-      (&xbuf[0][0][0][0])[i] = 0u;  // rows of heads beyond HS stay zero
-  }
   if (w == 0) {
     float x[8];
     if (r < HS) {
-      const size_t qrow = ((size_t)b * a.Hq + hq0 + r) * KVQ_D + 8 * c;
+      const size_t qrow = ((size_t)b * a.Hq + it.hq0 + r) * KVQ_D + 8 * c;
       if (a.q_f32) {
         const float4 *qp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + qrow);
         const float4 u0 = qp[0], u1 = qp[1];
@@ -347,219 +366,234 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   }
   __syncthreads();  // the queries' LDS becomes page rows
 
-  // This lane's 16 bytes (8 channels) of original rows t0 + 4 i + r, i < 4 (clamped to L - 1 on the
-  // last page): a uniform page base and a 32-bit per-lane offset.
-  const uint32_t row_elems = (uint32_t)Hkv * KVQ_D;  // elements between consecutive positions
-  // the next page's rows in flight: pk[i], pv[i] = positions 4 i + r (written out, no indexed array)
-  uint4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
-  auto load_rows = [&](int pg, bool with_v) __attribute__((always_inline)) {
+  // the next page's rows in flight: pk_i = this lane's 8 channels of position 4 i + r (clamped to
+  // L - 1 on the last page), from a uniform page base and a 32-bit per-lane offset
+  const uint32_t row_elems = (uint32_t)a.Hkv * KVQ_D;  // elements between consecutive positions
+  uint4 pk0, pk1, pk2, pk3;
+  auto load_rows = [&](int pg) __attribute__((always_inline)) {
     const int t0 = pg * KVQ_PAGE;
-    const size_t base = ((size_t)b * a.max_len + (size_t)t0) * row_elems + (size_t)h * KVQ_D;
-    const uint16_t *kp = a.k_ref + base, *vp = a.v_ref + base;
+    const uint16_t *kp = a.k_ref + ((size_t)b * a.max_len + (size_t)t0) * row_elems + (size_t)h * KVQ_D;
     const int last = L - 1 - t0;
     auto off = [&](int i) { return (uint32_t)(4 * i + r < last ? 4 * i + r : last) * row_elems + 8 * c; };
-    const uint32_t o0 = off(0), o1 = off(1), o2 = off(2), o3 = off(3);
-    pk0 = *reinterpret_cast<const uint4 *>(kp + o0);
-    pk1 = *reinterpret_cast<const uint4 *>(kp + o1);
-    pk2 = *reinterpret_cast<const uint4 *>(kp + o2);
-    pk3 = *reinterpret_cast<const uint4 *>(kp + o3);
-    if (with_v) {
-      pv0 = *reinterpret_cast<const uint4 *>(vp + o0);
-      pv1 = *reinterpret_cast<const uint4 *>(vp + o1);
-      pv2 = *reinterpret_cast<const uint4 *>(vp + o2);
-      pv3 = *reinterpret_cast<const uint4 *>(vp + o3);
-    }
+    pk0 = *reinterpret_cast<const uint4 *>(kp + off(0));
+    pk1 = *reinterpret_cast<const uint4 *>(kp + off(1));
+    pk2 = *reinterpret_cast<const uint4 *>(kp + off(2));
+    pk3 = *reinterpret_cast<const uint4 *>(kp + off(3));
   };
-  auto store_rows = [&](bool with_v) __attribute__((always_inline)) {
-    rows[w][0][(0 + r) * 16 + c] = pk0;
-    rows[w][0][(4 + r) * 16 + c] = pk1;
-    rows[w][0][(8 + r) * 16 + c] = pk2;
-    rows[w][0][(12 + r) * 16 + c] = pk3;
-    if (with_v) {
-      rows[w][1][(0 + r) * 16 + c] = pv0;
-      rows[w][1][(4 + r) * 16 + c] = pv1;
-      rows[w][1][(8 + r) * 16 + c] = pv2;
-      rows[w][1][(12 + r) * 16 + c] = pv3;
-    }
+  auto store_rows = [&]() __attribute__((always_inline)) {
+    rows[w][(0 + r) * 16 + c] = pk0;
+    rows[w][(4 + r) * 16 + c] = pk1;
+    rows[w][(8 + r) * 16 + c] = pk2;
+    rows[w][(12 + r) * 16 + c] = pk3;
   };
+  const int kpart16 = lay.v_codes_off / 16;  // the record's key codes and key metadata
   auto load_rec = [&](int pg, int buf) __attribute__((always_inline)) {
-    if (pg * KVQ_PAGE >= nq) return;  // no quantized position on this page
-    const int64_t rec_idx = kvq_record_index_dev(a.cache, Hkv, b, h, pg);
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(a.cache.pages + (size_t)rec_idx * lay.record), 0, lay.record,
-                                          0x00020000);
-    const uint32_t dst = (uint32_t)(uintptr_t)&recs[w][buf][0];
-#pragma unroll
-    for (int i = 0; i < (EB_REC16 + 63) / 64; ++i) {
-      if (64 * i < rec16 && lane + 64 * i < rec16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(size_t)(dst + 1024u * i), 16, 16 * (lane + 64 * i),
-                                                 0, 0, 0);
-    }
+    eb_load_rec(a, it, pg, 0, kpart16, (uint32_t)(uintptr_t)&recs[w][buf][0], lane, EB_K16);
   };
   const float sl2 = a.scale * 1.4426950408889634f;  // softmax scale in log2 units
-  const uint8_t *krow = reinterpret_cast<const uint8_t *>(rows[w][0]);
-  const uint8_t *vrow = reinterpret_cast<const uint8_t *>(rows[w][1]);
+  const uint8_t *krow = reinterpret_cast<const uint8_t *>(rows[w]);
+  float2 *scores = reinterpret_cast<float2 *>(a.ws + (size_t)a.B * a.Hkv * (a.Hq / a.Hkv / HS) * a.splits * EB_W_ITEM) +
+                   ((size_t)b * a.Hq + it.hq0 + (qlive ? q : 0)) * a.max_len;
 
-  // Exact and quantized dots (in dot units, no softmax scale) of token t of page t0 for head q.
-  auto page_scores = [&](const uint8_t *rs, int t0, float &s0, float &s1) __attribute__((always_inline)) {
-    eb_f4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
-    const int n = lane & 15, oct = lane >> 4;  // B operand: token n, channel octet oct of each chunk
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      uint32_t mk = kc == jrow ? ~0u : 0u;
-      asm volatile("" : "+v"(mk));  // keeps the masked operands in the loop (no 48 registers of zeros)
-      const eb_u4 kv = *reinterpret_cast<const eb_u4 *>(krow + n * 256 + (32 * kc + 8 * oct) * 2);
-      const eb_s8 bk = __builtin_bit_cast(eb_s8, kv);
-      D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][0] & mk), bk, D0, 0, 0, 0);
-      if (lo0) D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][1] & mk), bk, D0, 0, 0, 0);
+  float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f, ds_max = 0.f, ds_sq = 0.f;
+  float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;  // key reconstruction error (head group 0)
+  int buf = 0;
+  if (pbeg + w < pend) {
+    load_rows(pbeg + w);
+    load_rec(pbeg + w, 0);
+  }
+  for (int pg = pbeg + w; pg < pend; pg += EB_WAVES, buf ^= 1) {
+    const int t0 = pg * KVQ_PAGE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page's rows and record have landed
+    store_rows();
+    if (pg + EB_WAVES < pend) {
+      load_rows(pg + EB_WAVES);
+      load_rec(pg + EB_WAVES, buf ^ 1);
     }
-    s0 = (D0[0] + D0[1] + D0[2] + D0[3]) * 0x1p-100f;
-    s1 = s0;
-    if (t0 < nq) {  // the page holds quantized tokens
-      const uint8_t *kcodes = rs + lay.k_codes_off;
+    const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
+    // exact and quantized dots (dot units, no softmax scale) of token t of the page for head q
+    float s0, s1;
+    {
+      eb_f4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+      const int n = lane & 15, oct = lane >> 4;  // B operand: token n, channel octet oct of each chunk
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
         uint32_t mk = kc == jrow ? ~0u : 0u;
-        asm volatile("" : "+v"(mk));
-        const eb_s8 bc = pack8s(eb_pair(kcodes, 16 * oct + n, 4 * kc + 0, KP), eb_pair(kcodes, 16 * oct + n, 4 * kc + 1, KP),
-                                eb_pair(kcodes, 16 * oct + n, 4 * kc + 2, KP), eb_pair(kcodes, 16 * oct + n, 4 * kc + 3, KP));
-        D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[1][0] & mk), bc, D1, 0, 0, 0);
-        if (lo1) D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[1][1] & mk), bc, D1, 0, 0, 0);
+        asm volatile("" : "+v"(mk));  // keeps the masked operands in the loop (no 48 registers of zeros)
+        const eb_u4 kv = *reinterpret_cast<const eb_u4 *>(krow + n * 256 + (32 * kc + 8 * oct) * 2);
+        const eb_s8 bk = __builtin_bit_cast(eb_s8, kv);
+        D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][0] & mk), bk, D0, 0, 0, 0);
+        if (lo0) D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][1] & mk), bk, D0, 0, 0, 0);
       }
-      if (t0 + t < nq) {
-        const uint32_t *km = reinterpret_cast<const uint32_t *>(rs + lay.k_meta_off) + t * lay.nkg;
-        float acc = 0.f;
+      s0 = (D0[0] + D0[1] + D0[2] + D0[3]) * 0x1p-100f;
+      s1 = s0;
+      if (t0 < nq) {  // the page holds quantized tokens
+        const uint8_t *kcodes = rs + lay.k_codes_off;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc = __builtin_fmaf(D1[rr] * 0x1p33f, f16f(km[(32 * rr) / lay.kg] & 0xFFFF), acc);
+        for (int kc = 0; kc < 4; ++kc) {
+          uint32_t mk = kc == jrow ? ~0u : 0u;
+          asm volatile("" : "+v"(mk));
+          const eb_s8 bc = pack8s(eb_pair(kcodes, 16 * oct + n, 4 * kc + 0, KP), eb_pair(kcodes, 16 * oct + n, 4 * kc + 1, KP),
+                                  eb_pair(kcodes, 16 * oct + n, 4 * kc + 2, KP), eb_pair(kcodes, 16 * oct + n, 4 * kc + 3, KP));
+          D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[1][0] & mk), bc, D1, 0, 0, 0);
+          if (lo1) D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[1][1] & mk), bc, D1, 0, 0, 0);
+        }
+        if (t0 + t < nq) {
+          const uint32_t *km = reinterpret_cast<const uint32_t *>(rs + lay.k_meta_off) + t * lay.nkg;
+          float acc = 0.f;
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-          if (gi < lay.nkg) acc = __builtin_fmaf(f16f(km[gi] >> 16), qgl[gi], acc);
-        s1 = acc;
+          for (int rr = 0; rr < 4; ++rr) acc = __builtin_fmaf(D1[rr] * 0x1p33f, f16f(km[(32 * rr) / lay.kg] & 0xFFFF), acc);
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi)
+            if (gi < lay.nkg) acc = __builtin_fmaf(f16f(km[gi] >> 16), qgl[gi], acc);
+          s1 = acc;
+        }
       }
     }
-  };
-
-  int buf = 0;
-  if constexpr (PASS == 1) {
-    float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f, ds_max = 0.f, ds_sq = 0.f;
-    float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;  // key reconstruction error (head group 0)
-    if (pbeg + w < pend) {
-      load_rows(pbeg + w, false);
-      load_rec(pbeg + w, 0);
+    if (qlive && t0 + t < L) {
+      scores[t0 + t] = make_float2(s0, s1);
+      const float x0 = s0 * sl2, x1 = s1 * sl2;
+      const float n0 = __builtin_fmaxf(m0, x0), n1 = __builtin_fmaxf(m1, x1);
+      z0 = z0 * __builtin_amdgcn_exp2f(m0 - n0) + __builtin_amdgcn_exp2f(x0 - n0);
+      z1 = z1 * __builtin_amdgcn_exp2f(m1 - n1) + __builtin_amdgcn_exp2f(x1 - n1);
+      m0 = n0;
+      m1 = n1;
+      const float ds = (s1 - s0) * a.scale;
+      ds_max = __builtin_fmaxf(ds_max, __builtin_fabsf(ds));
+      ds_sq = __builtin_fmaf(ds, ds, ds_sq);
     }
-    for (int pg = pbeg + w; pg < pend; pg += EB_WAVES, buf ^= 1) {
-      const int t0 = pg * KVQ_PAGE;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page's rows and record have landed
-      store_rows(false);
-      if (pg + EB_WAVES < pend) {
-        load_rows(pg + EB_WAVES, false);
-        load_rec(pg + EB_WAVES, buf ^ 1);
-      }
-      const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
-      float s0, s1;
-      page_scores(rs, t0, s0, s1);
-      if (qlive && t0 + t < L) {
-        const float x0 = s0 * sl2, x1 = s1 * sl2;
-        const float n0 = __builtin_fmaxf(m0, x0), n1 = __builtin_fmaxf(m1, x1);
-        z0 = z0 * __builtin_amdgcn_exp2f(m0 - n0) + __builtin_amdgcn_exp2f(x0 - n0);
-        z1 = z1 * __builtin_amdgcn_exp2f(m1 - n1) + __builtin_amdgcn_exp2f(x1 - n1);
-        m0 = n0;
-        m1 = n1;
-        const float ds = (s1 - s0) * a.scale;
-        ds_max = __builtin_fmaxf(ds_max, __builtin_fabsf(ds));
-        ds_sq = __builtin_fmaf(ds, ds, ds_sq);
-      }
-      if (krec) {  // key reconstruction errors, 8 channels of positions 4 i + r per lane
+    if (krec) {  // key reconstruction errors, 8 channels of positions 4 i + r per lane
 #pragma unroll 1
-        for (int it = 0; it < 4; ++it) {
-          const int n = 4 * it + r;
-          const bool quant = t0 + n < nq;  // (positions past L are not quantized either)
-          float k[8], kh[8];
-          bf16x8(rows[w][0][n * 16 + c], k);
+      for (int ii = 0; ii < 4; ++ii) {
+        const int n = 4 * ii + r;
+        const bool quant = t0 + n < nq;  // (positions past L are not quantized either)
+        float k[8], kh[8];
+        bf16x8(rows[w][n * 16 + c], k);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kh[e] = 0.f;
-          if (quant) decode8<true>(lay, KP, rs, n, c, kh);
-          if (a.rotation) row_wht(kh, c, quant);  // back to the original domain
-          if (quant) {
+        for (int e = 0; e < 8; ++e) kh[e] = 0.f;
+        if (quant) decode8<true>(lay, KP, rs, n, c, kh);
+        if (a.rotation) row_wht(kh, c, quant);  // back to the original domain
+        if (quant) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float err = kh[e] - k[e];
-              ek_sq = __builtin_fmaf(err, err, ek_sq);
-              ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
-              k_sq = __builtin_fmaf(k[e], k[e], k_sq);
-            }
+          for (int e = 0; e < 8; ++e) {
+            const float err = kh[e] - k[e];
+            ek_sq = __builtin_fmaf(err, err, ek_sq);
+            ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
+            k_sq = __builtin_fmaf(k[e], k[e], k_sq);
           }
         }
       }
     }
-    // merge the 16 tokens of a head (one lane row), then the waves
-    {
-      const float M0 = row16_max(m0), M1 = row16_max(m1);
-      const float Z0 = row16_sum(M0 == ninf ? 0.f : z0 * __builtin_amdgcn_exp2f(m0 - M0));
-      const float Z1 = row16_sum(M1 == ninf ? 0.f : z1 * __builtin_amdgcn_exp2f(m1 - M1));
-      const float dmx = row16_max(ds_max), dsq = row16_sum(ds_sq);
-      if (qlive && t == 0) {
-        red[w][6 * q + 0] = M0;
-        red[w][6 * q + 1] = Z0;
-        red[w][6 * q + 2] = M1;
-        red[w][6 * q + 3] = Z1;
-        red[w][6 * q + 4] = dmx;
-        red[w][6 * q + 5] = dsq;
-      }
-    }
-    if (krec) {
-      for (int off = 1; off <= 32; off <<= 1) {
-        ek_sq += __shfl_xor(ek_sq, off);
-        k_sq += __shfl_xor(k_sq, off);
-        ek_max = __builtin_fmaxf(ek_max, __shfl_xor(ek_max, off));
-      }
-      if (lane == 0) {
-        ured[w][0] = ek_sq;
-        ured[w][1] = ek_max;
-        ured[w][2] = k_sq;
-      }
-    }
-    __syncthreads();
-    if (w == 0 && lane < HS) {  // lane j: head j's statistics over the item's pages
-      const int j = lane;
-      float M0 = ninf, M1 = ninf;
-      for (int i = 0; i < EB_WAVES; ++i) {
-        M0 = __builtin_fmaxf(M0, red[i][6 * j + 0]);
-        M1 = __builtin_fmaxf(M1, red[i][6 * j + 2]);
-      }
-      float Z0 = 0.f, Z1 = 0.f, dmx = 0.f, dsq = 0.f;
-      for (int i = 0; i < EB_WAVES; ++i) {
-        if (red[i][6 * j + 0] != ninf) Z0 += red[i][6 * j + 1] * __builtin_amdgcn_exp2f(red[i][6 * j + 0] - M0);
-        if (red[i][6 * j + 2] != ninf) Z1 += red[i][6 * j + 3] * __builtin_amdgcn_exp2f(red[i][6 * j + 2] - M1);
-        dmx = __builtin_fmaxf(dmx, red[i][6 * j + 4]);
-        dsq += red[i][6 * j + 5];
-      }
-      float *st = ws + EB_W_STATS + 6 * j;
-      st[0] = M0;
-      st[1] = Z0;
-      st[2] = M1;
-      st[3] = Z1;
-      st[4] = dmx;
-      st[5] = dsq;
-    }
-    if (krec && w == 0 && lane == 0) {
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f;
-      for (int i = 0; i < EB_WAVES; ++i) {
-        s0 += ured[i][0];
-        s1 = __builtin_fmaxf(s1, ured[i][1]);
-        s2 += ured[i][2];
-      }
-      ws[EB_W_KREC + 0] = s0;
-      ws[EB_W_KREC + 1] = s1;
-      ws[EB_W_KREC + 2] = s2;
-    }
-    return;
   }
+  // merge the 16 tokens of a head (one lane row), then the waves
+  {
+    const float M0 = row16_max(m0), M1 = row16_max(m1);
+    const float Z0 = row16_sum(M0 == ninf ? 0.f : z0 * __builtin_amdgcn_exp2f(m0 - M0));
+    const float Z1 = row16_sum(M1 == ninf ? 0.f : z1 * __builtin_amdgcn_exp2f(m1 - M1));
+    const float dmx = row16_max(ds_max), dsq = row16_sum(ds_sq);
+    if (qlive && t == 0) {
+      red[w][6 * q + 0] = M0;
+      red[w][6 * q + 1] = Z0;
+      red[w][6 * q + 2] = M1;
+      red[w][6 * q + 3] = Z1;
+      red[w][6 * q + 4] = dmx;
+      red[w][6 * q + 5] = dsq;
+    }
+  }
+  if (krec) {
+    for (int off = 1; off <= 32; off <<= 1) {
+      ek_sq += __shfl_xor(ek_sq, off);
+      k_sq += __shfl_xor(k_sq, off);
+      ek_max = __builtin_fmaxf(ek_max, __shfl_xor(ek_max, off));
+    }
+    if (lane == 0) {
+      ured[w][0] = ek_sq;
+      ured[w][1] = ek_max;
+      ured[w][2] = k_sq;
+    }
+  }
+  __syncthreads();
+  if (w == 0 && lane < HS) {  // lane j: head j's statistics over the item's pages
+    const int j = lane;
+    float M0 = ninf, M1 = ninf;
+    for (int i = 0; i < EB_WAVES; ++i) {
+      M0 = __builtin_fmaxf(M0, red[i][6 * j + 0]);
+      M1 = __builtin_fmaxf(M1, red[i][6 * j + 2]);
+    }
+    float Z0 = 0.f, Z1 = 0.f, dmx = 0.f, dsq = 0.f;
+    for (int i = 0; i < EB_WAVES; ++i) {
+      if (red[i][6 * j + 0] != ninf) Z0 += red[i][6 * j + 1] * __builtin_amdgcn_exp2f(red[i][6 * j + 0] - M0);
+      if (red[i][6 * j + 2] != ninf) Z1 += red[i][6 * j + 3] * __builtin_amdgcn_exp2f(red[i][6 * j + 2] - M1);
+      dmx = __builtin_fmaxf(dmx, red[i][6 * j + 4]);
+      dsq += red[i][6 * j + 5];
+    }
+    float *st = it.ws + EB_W_STATS + 6 * j;
+    st[0] = M0;
+    st[1] = Z0;
+    st[2] = M1;
+    st[3] = Z1;
+    st[4] = dmx;
+    st[5] = dsq;
+  }
+  if (krec && w == 0 && lane == 0) {
+    float e0 = 0.f, e1 = 0.f, e2 = 0.f;
+    for (int i = 0; i < EB_WAVES; ++i) {
+      e0 += ured[i][0];
+      e1 = __builtin_fmaxf(e1, ured[i][1]);
+      e2 += ured[i][2];
+    }
+    it.ws[EB_W_KREC + 0] = e0;
+    it.ws[EB_W_KREC + 1] = e1;
+    it.ws[EB_W_KREC + 2] = e2;
+  }
+}
 
-  // ---- pass 2: the head's maxima and sums over all ranges of the sequence ----
+// PASS 2, weights and weighted sums.  The maxima and sums of all ranges merged; the weights a
+// (exact keys) and a' (quantized keys) from the stored scores, their total variation, and the four
+// weighted sums on MFMA (16x16x16 bf16, k = the page's 16 tokens): A rows 8 set + 4 part + q hold
+// the weights of set a / a' (hi and lo parts) of head q, through a per-wave LDS exchange buffer;
+// B is the original values (exact bf16: a V, a' V) or the value codes (a V_hat, a' V_hat;
+// A = weight * scale * 2^64, window tokens take their exact values as B with A = weight * 2^-69,
+// so every product carries 2^-69), plus the weighted zero points.  The original values are stored
+// to LDS transposed (channel-major, 16 positions of a channel in 32 bytes), so a B operand (4
+// positions of one channel) is one 8-byte read.  The range's sums go to the workspace: the weights
+// are final, so the ranges' sums add.  The last head group also takes the value reconstruction
+// errors, in the same layout as the B operands (4 positions x 8 channels per lane).
+template <int HS>
+__global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a) {
+  __shared__ float red[EB_WAVES][HS];             // total variation per wave and head
+  __shared__ float ured[EB_WAVES][3];
+  __shared__ float zred[EB_WAVES][2][HS][2];      // weighted zero points (set, head, value group)
+  __shared__ uint4 recs[EB_WAVES][2][EB_V16];     // value parts of page records (the next one lands meanwhile)
+  __shared__ uint4 vt[EB_WAVES][KVQ_D * 2];       // the page's original values, [channel][16 positions]
+  __shared__ uint32_t xbuf[EB_WAVES][3][16][8];   // value A operands: [raw, code v0, code v1][row][16 bf16]
+  // after the page loop: the four weighted sums of the workgroup
+  float(*accs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&vt[0][0]);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane >> 4, c = lane & 15;  // row loads: positions 4 r .. 4 r + 3, channels [8c, 8c + 8)
+  const int q = lane >> 4, t = lane & 15;  // weight layout: head q, token t
+  const int kk = lane >> 4, col = lane & 15;  // B operands: positions 4 kk .. + 3, channel 16 m + col
+  EbItem it;
+  if (!eb_item<HS>(a, it)) return;
+  const int Hkv = a.Hkv, ngrp = a.Hq / a.Hkv / HS, S = a.splits;
+  const int b = it.b, h = it.h, L = it.L, nq = it.nq, pbeg = it.pbeg, pend = it.pend;
+  const bool vrec = it.grp == ngrp - 1;
+  const float ninf = -__builtin_inff();
+  const KvqLayout &lay = a.lay;
+  const EbPlanes VP = eb_planes(lay.vb);
+  const bool qlive = q < HS;
+  const int nvg = lay.nvg;
+  const int vmeta = lay.v_meta_off - lay.v_codes_off;  // value metadata in the staged part
+
+  if (HS < 4) {
+    for (int i = threadIdx.x; i < 3 * 16 * 8 * EB_WAVES; i += 64 * EB_WAVES)
+      (&xbuf[0][0][0][0])[i] = 0u;  // rows of heads beyond HS stay zero
+  }
+  // the head's maxima and sums over all ranges of the sequence
   float M0 = ninf, M1 = ninf, iZ0 = 0.f, iZ1 = 0.f;
   {
-    const float *st0 = a.ws + (size_t)(unit * ngrp + grp) * S * EB_W_ITEM + EB_W_STATS + 6 * (qlive ? q : 0);
+    const float *st0 = a.ws + (size_t)(it.unit * ngrp + it.grp) * S * EB_W_ITEM + EB_W_STATS + 6 * (qlive ? q : 0);
     for (int s = 0; s < S; ++s) {
       M0 = __builtin_fmaxf(M0, st0[(size_t)s * EB_W_ITEM + 0]);
       M1 = __builtin_fmaxf(M1, st0[(size_t)s * EB_W_ITEM + 2]);
@@ -573,36 +607,79 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     iZ0 = Z0 > 0.f ? 1.f / Z0 : 0.f;
     iZ1 = Z1 > 0.f ? 1.f / Z1 : 0.f;
   }
+  __syncthreads();  // xbuf cleared
+
+  const uint32_t row_elems = (uint32_t)Hkv * KVQ_D;
+  const float2 *scores = reinterpret_cast<const float2 *>(a.ws + (size_t)a.B * Hkv * ngrp * S * EB_W_ITEM) +
+                         ((size_t)b * a.Hq + it.hq0 + (qlive ? q : 0)) * a.max_len;
+  // the next page in flight: pv_i = 8 channels of position 4 r + i (clamped to L - 1), its scores
+  uint4 pv0, pv1, pv2, pv3;
+  float2 psc;
+  auto load_page = [&](int pg) __attribute__((always_inline)) {
+    const int t0 = pg * KVQ_PAGE;
+    const uint16_t *vp = a.v_ref + ((size_t)b * a.max_len + (size_t)t0) * row_elems + (size_t)h * KVQ_D;
+    const int last = L - 1 - t0;
+    auto off = [&](int i) { return (uint32_t)(4 * r + i < last ? 4 * r + i : last) * row_elems + 8 * c; };
+    pv0 = *reinterpret_cast<const uint4 *>(vp + off(0));
+    pv1 = *reinterpret_cast<const uint4 *>(vp + off(1));
+    pv2 = *reinterpret_cast<const uint4 *>(vp + off(2));
+    pv3 = *reinterpret_cast<const uint4 *>(vp + off(3));
+    psc = scores[t0 + t < L ? t0 + t : L - 1];
+  };
+  // transposed store: channel 8 c + e, positions 4 r .. 4 r + 3 -> 8 bytes at [8 c + e][4 r]
+  auto store_page = [&]() __attribute__((always_inline)) {
+    const uint32_t wk[4][4] = {{pv0.x, pv0.y, pv0.z, pv0.w}, {pv1.x, pv1.y, pv1.z, pv1.w},
+                               {pv2.x, pv2.y, pv2.z, pv2.w}, {pv3.x, pv3.y, pv3.z, pv3.w}};
+    uint8_t *base = reinterpret_cast<uint8_t *>(vt[w]) + (8 * c) * 32 + 8 * r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int wi = e >> 1;
+      uint2 v;
+      if (e & 1) {
+        v.x = (wk[0][wi] >> 16) | (wk[1][wi] & 0xFFFF0000u);
+        v.y = (wk[2][wi] >> 16) | (wk[3][wi] & 0xFFFF0000u);
+      } else {
+        v.x = (wk[0][wi] & 0xFFFFu) | (wk[1][wi] << 16);
+        v.y = (wk[2][wi] & 0xFFFFu) | (wk[3][wi] << 16);
+      }
+      *reinterpret_cast<uint2 *>(base + e * 32) = v;
+    }
+  };
+  const int vpart16 = (lay.record - lay.v_codes_off) / 16;  // the record's value codes and metadata
+  auto load_rec = [&](int pg, int bf) __attribute__((always_inline)) {
+    eb_load_rec(a, it, pg, lay.v_codes_off, vpart16, (uint32_t)(uintptr_t)&recs[w][bf][0], lane, EB_V16);
+  };
+  const float sl2 = a.scale * 1.4426950408889634f;
+
   float tv = 0.f;
   float zs[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // weighted zero points: set x value group (this lane's head)
   eb_f4 Dr[8], Dc[8];                        // value sums per 16-channel tile: original values, codes
 #pragma unroll
   for (int m = 0; m < 8; ++m) Dr[m] = Dc[m] = eb_f4{0.f, 0.f, 0.f, 0.f};
   float ev_sq = 0.f, ev_max = 0.f, v_sq = 0.f;
-  const int nvg = lay.nvg;
+  int buf = 0;
   if (pbeg + w < pend) {
-    load_rows(pbeg + w, true);
+    load_page(pbeg + w);
     load_rec(pbeg + w, 0);
   }
   for (int pg = pbeg + w; pg < pend; pg += EB_WAVES, buf ^= 1) {
     const int t0 = pg * KVQ_PAGE;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    store_rows(true);
+    store_page();
+    const float2 sc = psc;
     if (pg + EB_WAVES < pend) {
-      load_rows(pg + EB_WAVES, true);
+      load_page(pg + EB_WAVES);
       load_rec(pg + EB_WAVES, buf ^ 1);
     }
-    const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);
-    float s0, s1;
-    page_scores(rs, t0, s0, s1);
+    const uint8_t *rs = reinterpret_cast<const uint8_t *>(recs[w][buf]);  // value codes at 0
     const bool valid = qlive && t0 + t < L, quant = t0 + t < nq;
-    const float w0 = valid ? __builtin_amdgcn_exp2f(s0 * sl2 - M0) * iZ0 : 0.f;
-    const float w1 = valid ? __builtin_amdgcn_exp2f(s1 * sl2 - M1) * iZ1 : 0.f;
+    const float w0 = valid ? __builtin_amdgcn_exp2f(sc.x * sl2 - M0) * iZ0 : 0.f;
+    const float w1 = valid ? __builtin_amdgcn_exp2f(sc.y * sl2 - M1) * iZ1 : 0.f;
     tv += __builtin_fabsf(w1 - w0);
     // A operands: raw rows take the weights; code rows the weights times the token's value scale
     // (times 2^64) for quantized tokens, the weights times 2^-69 for window tokens
     if (qlive) {
-      const uint32_t *vm = reinterpret_cast<const uint32_t *>(rs + lay.v_meta_off) + t * nvg;
+      const uint32_t *vm = reinterpret_cast<const uint32_t *>(rs + vmeta) + t * nvg;
       uint16_t *xr = reinterpret_cast<uint16_t *>(&xbuf[w][0][0][0]);
       uint32_t hi, lo;
       split2(w0, w1, hi, lo);
@@ -615,9 +692,9 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
         if (v >= nvg) break;
         float f0, f1;
         if (quant) {
-          const float sc = f16f(vm[v] & 0xFFFF) * 0x1p64f, zr = f16f(vm[v] >> 16);
-          f0 = w0 * sc;
-          f1 = w1 * sc;
+          const float vs = f16f(vm[v] & 0xFFFF) * 0x1p64f, zr = f16f(vm[v] >> 16);
+          f0 = w0 * vs;
+          f1 = w1 * vs;
           zs[0][v] = __builtin_fmaf(w0, zr, zs[0][v]);
           zs[1][v] = __builtin_fmaf(w1, zr, zs[1][v]);
         } else {
@@ -636,37 +713,70 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
     const eb_s4 ar = __builtin_bit_cast(eb_s4, *reinterpret_cast<const eb_u2 *>(&xbuf[w][0][lane & 15][2 * (lane >> 4)]));
     const eb_s4 ac0 = __builtin_bit_cast(eb_s4, *reinterpret_cast<const eb_u2 *>(&xbuf[w][1][lane & 15][2 * (lane >> 4)]));
     const eb_s4 ac1 = __builtin_bit_cast(eb_s4, *reinterpret_cast<const eb_u2 *>(&xbuf[w][2][lane & 15][2 * (lane >> 4)]));
-    // B operands: column = channel 16 m + (lane mod 16), k = tokens 4 kk .. 4 kk + 3 (kk = lane / 16)
-    const int kk = lane >> 4, col = lane & 15;
     const int tq = nq - t0;  // tokens of the page below it are quantized
+    const uint8_t *vtb = reinterpret_cast<const uint8_t *>(vt[w]) + col * 32 + 8 * kk;
+    // value reconstruction in the B layout: the metadata of positions 4 kk + i, group v
+    float rsc[2][4], rzr[2][4];
+    const bool vr_on = vrec && tq > 0 && !a.value_rotation;
+    if (vr_on) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t mm = v < nvg ? reinterpret_cast<const uint32_t *>(rs + vmeta)[(4 * kk + i) * nvg + v] : 0u;
+          rsc[v][i] = f16f(mm & 0xFFFF);
+          rzr[v][i] = f16f(mm >> 16);
+        }
+      }
+    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const uint16_t *vr = reinterpret_cast<const uint16_t *>(vrow) + 16 * m + col;
-      const uint32_t r0 = (uint32_t)vr[(4 * kk + 0) * 128] | ((uint32_t)vr[(4 * kk + 1) * 128] << 16);
-      const uint32_t r1 = (uint32_t)vr[(4 * kk + 2) * 128] | ((uint32_t)vr[(4 * kk + 3) * 128] << 16);
+      const uint2 rv = *reinterpret_cast<const uint2 *>(vtb + m * 16 * 32);
+      const uint32_t r0 = rv.x, r1 = rv.y;
       Dr[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ar, pack4s(r0, r1), Dr[m], 0, 0, 0);
       uint32_t c0 = r0, c1 = r1;  // window tokens: exact values
       if (tq > 0) {
-        const uint8_t *vcodes = rs + lay.v_codes_off;
-        const uint32_t q0 = eb_pair(vcodes, lane, m, VP), q1 = eb_pair(vcodes, lane, 8 + m, VP);
-        const int tb = 4 * kk;  // first token of the lane's four
-        c0 = (tb + 0 < tq ? (q0 & 0xFFFFu) : (r0 & 0xFFFFu)) | (tb + 1 < tq ? (q0 & 0xFFFF0000u) : (r0 & 0xFFFF0000u));
-        c1 = (tb + 2 < tq ? (q1 & 0xFFFFu) : (r1 & 0xFFFFu)) | (tb + 3 < tq ? (q1 & 0xFFFF0000u) : (r1 & 0xFFFF0000u));
+        const uint32_t q0 = eb_pair(rs, lane, m, VP), q1 = eb_pair(rs, lane, 8 + m, VP);
+        if (tq >= KVQ_PAGE) {
+          c0 = q0;
+          c1 = q1;
+        } else {
+          const int tb = 4 * kk;  // first token of the lane's four
+          c0 = (tb + 0 < tq ? (q0 & 0xFFFFu) : (r0 & 0xFFFFu)) | (tb + 1 < tq ? (q0 & 0xFFFF0000u) : (r0 & 0xFFFF0000u));
+          c1 = (tb + 2 < tq ? (q1 & 0xFFFFu) : (r1 & 0xFFFFu)) | (tb + 3 < tq ? (q1 & 0xFFFF0000u) : (r1 & 0xFFFF0000u));
+        }
+        if (vr_on) {  // errors of the quantized positions among 4 kk + i, channel 16 m + col
+          const int v = (nvg == 2 && m >= 4) ? 1 : 0;
+          const uint32_t cw[4] = {q0 & 0xFFFFu, q0 >> 16, q1 & 0xFFFFu, q1 >> 16};
+          const uint32_t rw[4] = {r0 << 16, r0 & 0xFFFF0000u, r1 << 16, r1 & 0xFFFF0000u};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (4 * kk + i < tq) {
+              const float x = __builtin_bit_cast(float, rw[i]);
+              const float err = (rzr[v][i] + (float)cw[i] * rsc[v][i]) - x;
+              ev_sq = __builtin_fmaf(err, err, ev_sq);
+              ev_max = __builtin_fmaxf(ev_max, __builtin_fabsf(err));
+              v_sq = __builtin_fmaf(x, x, v_sq);
+            }
+          }
+        }
       }
       Dc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k((m < 4 || nvg == 1) ? ac0 : ac1, pack4s(c0, c1), Dc[m], 0, 0, 0);
     }
-    if (vrec) {  // value reconstruction errors
+    if (vrec && a.value_rotation && tq > 0) {  // rotated values: whole rows rotated back
 #pragma unroll 1
-      for (int it = 0; it < 4; ++it) {
-        const int n = 4 * it + r;
+      for (int ii = 0; ii < 4; ++ii) {
+        const int n = 4 * ii + r;
         const bool qn = t0 + n < nq;
         float v[8], vh[8];
-        bf16x8(rows[w][1][n * 16 + c], v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vh[e] = 0.f;
-        if (qn) decode8<false>(lay, VP, rs, n, c, vh);
-        // with rotated values the reconstruction is rotated back (no recent window then)
-        if (a.value_rotation) row_wht(vh, c, qn);
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t u = reinterpret_cast<const uint16_t *>(vt[w])[(8 * c + e) * 16 + n];
+          v[e] = kvq_bf16_bits_to_f32(u);
+          vh[e] = 0.f;
+        }
+        if (qn) decode8<false>(lay, VP, rs - lay.v_codes_off, n, c, vh);
+        row_wht(vh, c, qn);
         if (qn) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -710,13 +820,13 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
       ured[w][2] = v_sq;
     }
   }
-  __syncthreads();  // every wave is past its pages: the rows' LDS becomes the sums
+  __syncthreads();  // every wave is past its pages: the values' LDS becomes the sums
   for (int i = threadIdx.x; i < 4 * HS * KVQ_D; i += 64 * EB_WAVES) (&accs[0][0][0])[i] = 0.f;
   __syncthreads();
   // value sums: D row 4 (l / 16) + r of lane l = (set, part, head r) = (l / 32, (l / 16) mod 2, r);
   // the hi and lo parts are added across lanes l and l ^ 16; one wave at a time into LDS
   {
-    const int G4 = lane >> 4, col = lane & 15, set = G4 >> 1;
+    const int G4 = lane >> 4, set = G4 >> 1;
     for (int i = 0; i < EB_WAVES; ++i) {
       if (w == i) {
 #pragma unroll
@@ -740,23 +850,23 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_errbudget_kernel(KvqErrArgs
   // the item's sums, total variation and value reconstruction to the workspace
   for (int i = threadIdx.x; i < 4 * HS * KVQ_D; i += 64 * EB_WAVES) {
     const int s = i / (HS * KVQ_D), j = (i / KVQ_D) % HS, ch = i % KVQ_D;
-    ws[EB_W_SUMS + (4 * s + j) * KVQ_D + ch] = accs[s][j][ch];
+    it.ws[EB_W_SUMS + (4 * s + j) * KVQ_D + ch] = accs[s][j][ch];
   }
   if (w == 0 && lane < HS) {
     float tvj = 0.f;
     for (int i = 0; i < EB_WAVES; ++i) tvj += red[i][lane];
-    ws[EB_W_TV + lane] = tvj;
+    it.ws[EB_W_TV + lane] = tvj;
   }
   if (vrec && w == 0 && lane == 0) {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+    float e0 = 0.f, e1 = 0.f, e2 = 0.f;
     for (int i = 0; i < EB_WAVES; ++i) {
-      s0 += ured[i][0];
-      s1 = __builtin_fmaxf(s1, ured[i][1]);
-      s2 += ured[i][2];
+      e0 += ured[i][0];
+      e1 = __builtin_fmaxf(e1, ured[i][1]);
+      e2 += ured[i][2];
     }
-    ws[EB_W_VREC + 0] = s0;
-    ws[EB_W_VREC + 1] = s1;
-    ws[EB_W_VREC + 2] = s2;
+    it.ws[EB_W_VREC + 0] = e0;
+    it.ws[EB_W_VREC + 1] = e1;
+    it.ws[EB_W_VREC + 2] = e2;
   }
 }
 
@@ -855,8 +965,8 @@ void launch_eb(const KvqErrArgs &a, int ngrp, hipStream_t s) {
   const int wus = a.B * a.Hkv * a.splits;
   // groups of 8 work units, each group's head groups 8 workgroups apart (padding after the last)
   const dim3 grid((unsigned)(((wus + 7) / 8) * 8 * ngrp)), block(64 * EB_WAVES);
-  hipLaunchKernelGGL((kvq_errbudget_kernel<HS, 1>), grid, block, 0, s, a);
-  hipLaunchKernelGGL((kvq_errbudget_kernel<HS, 2>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((kvq_eb_scores_kernel<HS>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((kvq_eb_sums_kernel<HS>), grid, block, 0, s, a);
   hipLaunchKernelGGL((kvq_errbudget_final_kernel<HS>), dim3((unsigned)(a.B * a.Hkv * ngrp)), dim3(64 * HS), 0, s, a);
 }
 
