@@ -435,13 +435,14 @@ kvq_status kvq_dense_decode_attention(const kvq_params *params, int32_t batch, c
 
 namespace {
 
-// Ranges of pages per sequence for the error-budget passes: about one workgroup per CU over all
-// (unit, head group, range) items, at least one page per wave of a range.
+// Ranges of pages per sequence for the error-budget passes: about two workgroups per CU over all
+// (unit, head group, range) items (the scores pass holds two per CU), at least one page per wave
+// of a range.
 int errbudget_splits(const kvq_params *p, int32_t batch, int64_t max_seq_len) {
   const int g = p->num_q_heads / p->num_kv_heads, ngrp = g / kvq_errbudget_heads_per_group(g);
   const int64_t items = (int64_t)batch * p->num_kv_heads * ngrp;
   const int64_t pages = (max_seq_len + KVQ_PAGE - 1) / KVQ_PAGE;
-  int64_t s = (kNumCUs + items - 1) / items;
+  int64_t s = (2 * kNumCUs + items - 1) / items;
   const int64_t smax = (pages + 7) / 8;
   if (s > smax) s = smax;
   return s < 1 ? 1 : (int)s;

@@ -157,6 +157,7 @@ typedef float eb_f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t eb_u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t eb_u2 __attribute__((ext_vector_type(2)));
 typedef __bf16 eb_bf2 __attribute__((ext_vector_type(2)));
+typedef uint16_t eb_h2 __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> packed bf16 pair, round to nearest even.
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
@@ -278,12 +279,14 @@ __device__ __forceinline__ void eb_load_rec(const KvqErrArgs &a, const EbItem &i
 // merged over the 16 lanes of a head and the waves.  Head group 0 also takes the key
 // reconstruction errors (8 channels of a position per lane).
 template <int HS>
-__global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_scores_kernel(KvqErrArgs a) {
+__global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrArgs a) {  // two workgroups per CU
   __shared__ float red[EB_WAVES][6 * HS];
   __shared__ float ured[EB_WAVES][3];
   __shared__ float qg[HS][4];                    // sums of the code query over each key group
   __shared__ uint4 recs[EB_WAVES][2][EB_K16];    // key parts of page records (the next one lands meanwhile)
-  __shared__ uint4 rows[EB_WAVES][KVQ_PAGE * 16];  // the page's original key rows
+  // the page's original key rows: channel octet o of position n at n * 16 + (o ^ n), so the 16
+  // positions of a B operand (same octet) and the 16 octets of a row fall in distinct banks
+  __shared__ uint4 rows[EB_WAVES][KVQ_PAGE * 16];
   // before the page loop: the group's queries (raw, and the one the codes are scored with)
   float(*qs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&rows[0][0]);
   const int lane = threadIdx.x & 63;
@@ -381,10 +384,10 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_scores_kernel(KvqErrArgs
     pk3 = *reinterpret_cast<const uint4 *>(kp + off(3));
   };
   auto store_rows = [&]() __attribute__((always_inline)) {
-    rows[w][(0 + r) * 16 + c] = pk0;
-    rows[w][(4 + r) * 16 + c] = pk1;
-    rows[w][(8 + r) * 16 + c] = pk2;
-    rows[w][(12 + r) * 16 + c] = pk3;
+    rows[w][(0 + r) * 16 + (c ^ (0 + r))] = pk0;
+    rows[w][(4 + r) * 16 + (c ^ (4 + r))] = pk1;
+    rows[w][(8 + r) * 16 + (c ^ (8 + r))] = pk2;
+    rows[w][(12 + r) * 16 + (c ^ (12 + r))] = pk3;
   };
   const int kpart16 = lay.v_codes_off / 16;  // the record's key codes and key metadata
   auto load_rec = [&](int pg, int buf) __attribute__((always_inline)) {
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_scores_kernel(KvqErrArgs
       for (int kc = 0; kc < 4; ++kc) {
         uint32_t mk = kc == jrow ? ~0u : 0u;
         asm volatile("" : "+v"(mk));  // keeps the masked operands in the loop (no 48 registers of zeros)
-        const eb_u4 kv = *reinterpret_cast<const eb_u4 *>(krow + n * 256 + (32 * kc + 8 * oct) * 2);
+        const eb_u4 kv = *reinterpret_cast<const eb_u4 *>(krow + 16 * (n * 16 + ((4 * kc + oct) ^ n)));
         const eb_s8 bk = __builtin_bit_cast(eb_s8, kv);
         D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][0] & mk), bk, D0, 0, 0, 0);
         if (lo0) D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][1] & mk), bk, D0, 0, 0, 0);
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_scores_kernel(KvqErrArgs
         const int n = 4 * ii + r;
         const bool quant = t0 + n < nq;  // (positions past L are not quantized either)
         float k[8], kh[8];
-        bf16x8(rows[w][n * 16 + c], k);
+        bf16x8(rows[w][n * 16 + (c ^ n)], k);
 #pragma unroll
         for (int e = 0; e < 8; ++e) kh[e] = 0.f;
         if (quant) decode8<true>(lay, KP, rs, n, c, kh);
@@ -554,9 +557,9 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_scores_kernel(KvqErrArgs
 // the weights of set a / a' (hi and lo parts) of head q, through a per-wave LDS exchange buffer;
 // B is the original values (exact bf16: a V, a' V) or the value codes (a V_hat, a' V_hat;
 // A = weight * scale * 2^64, window tokens take their exact values as B with A = weight * 2^-69,
-// so every product carries 2^-69), plus the weighted zero points.  The original values are stored
-// to LDS transposed (channel-major, 16 positions of a channel in 32 bytes), so a B operand (4
-// positions of one channel) is one 8-byte read.  The range's sums go to the workspace: the weights
+// so every product carries 2^-69), plus the weighted zero points.  The B operands of the original
+// values are read as 16-bit elements from rows staged with the same swizzle as the key rows.  The
+// range's sums go to the workspace: the weights
 // are final, so the ranges' sums add.  The last head group also takes the value reconstruction
 // errors, in the same layout as the B operands (4 positions x 8 channels per lane).
 template <int HS>
@@ -565,7 +568,9 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
   __shared__ float ured[EB_WAVES][3];
   __shared__ float zred[EB_WAVES][2][HS][2];      // weighted zero points (set, head, value group)
   __shared__ uint4 recs[EB_WAVES][2][EB_V16];     // value parts of page records (the next one lands meanwhile)
-  __shared__ uint4 vt[EB_WAVES][KVQ_D * 2];       // the page's original values, [channel][16 positions]
+  // the page's original value rows, channel octet o of position n at n * 16 + (o ^ n): the 4
+  // positions x 16 channels of a B-operand read fall in distinct banks
+  __shared__ uint4 vt[EB_WAVES][KVQ_PAGE * 16];
   __shared__ uint32_t xbuf[EB_WAVES][3][16][8];   // value A operands: [raw, code v0, code v1][row][16 bf16]
   // after the page loop: the four weighted sums of the workgroup
   float(*accs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&vt[0][0]);
@@ -612,38 +617,25 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
   const uint32_t row_elems = (uint32_t)Hkv * KVQ_D;
   const float2 *scores = reinterpret_cast<const float2 *>(a.ws + (size_t)a.B * Hkv * ngrp * S * EB_W_ITEM) +
                          ((size_t)b * a.Hq + it.hq0 + (qlive ? q : 0)) * a.max_len;
-  // the next page in flight: pv_i = 8 channels of position 4 r + i (clamped to L - 1), its scores
+  // the next page in flight: pv_i = 8 channels of position 4 i + r (clamped to L - 1), its scores
   uint4 pv0, pv1, pv2, pv3;
   float2 psc;
   auto load_page = [&](int pg) __attribute__((always_inline)) {
     const int t0 = pg * KVQ_PAGE;
     const uint16_t *vp = a.v_ref + ((size_t)b * a.max_len + (size_t)t0) * row_elems + (size_t)h * KVQ_D;
     const int last = L - 1 - t0;
-    auto off = [&](int i) { return (uint32_t)(4 * r + i < last ? 4 * r + i : last) * row_elems + 8 * c; };
+    auto off = [&](int i) { return (uint32_t)(4 * i + r < last ? 4 * i + r : last) * row_elems + 8 * c; };
     pv0 = *reinterpret_cast<const uint4 *>(vp + off(0));
     pv1 = *reinterpret_cast<const uint4 *>(vp + off(1));
     pv2 = *reinterpret_cast<const uint4 *>(vp + off(2));
     pv3 = *reinterpret_cast<const uint4 *>(vp + off(3));
     psc = scores[t0 + t < L ? t0 + t : L - 1];
   };
-  // transposed store: channel 8 c + e, positions 4 r .. 4 r + 3 -> 8 bytes at [8 c + e][4 r]
   auto store_page = [&]() __attribute__((always_inline)) {
-    const uint32_t wk[4][4] = {{pv0.x, pv0.y, pv0.z, pv0.w}, {pv1.x, pv1.y, pv1.z, pv1.w},
-                               {pv2.x, pv2.y, pv2.z, pv2.w}, {pv3.x, pv3.y, pv3.z, pv3.w}};
-    uint8_t *base = reinterpret_cast<uint8_t *>(vt[w]) + (8 * c) * 32 + 8 * r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int wi = e >> 1;
-      uint2 v;
-      if (e & 1) {
-        v.x = (wk[0][wi] >> 16) | (wk[1][wi] & 0xFFFF0000u);
-        v.y = (wk[2][wi] >> 16) | (wk[3][wi] & 0xFFFF0000u);
-      } else {
-        v.x = (wk[0][wi] & 0xFFFFu) | (wk[1][wi] << 16);
-        v.y = (wk[2][wi] & 0xFFFFu) | (wk[3][wi] << 16);
-      }
-      *reinterpret_cast<uint2 *>(base + e * 32) = v;
-    }
+    vt[w][(0 + r) * 16 + (c ^ (0 + r))] = pv0;
+    vt[w][(4 + r) * 16 + (c ^ (4 + r))] = pv1;
+    vt[w][(8 + r) * 16 + (c ^ (8 + r))] = pv2;
+    vt[w][(12 + r) * 16 + (c ^ (12 + r))] = pv3;
   };
   const int vpart16 = (lay.record - lay.v_codes_off) / 16;  // the record's value codes and metadata
   auto load_rec = [&](int pg, int bf) __attribute__((always_inline)) {
@@ -714,7 +706,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
     const eb_s4 ac0 = __builtin_bit_cast(eb_s4, *reinterpret_cast<const eb_u2 *>(&xbuf[w][1][lane & 15][2 * (lane >> 4)]));
     const eb_s4 ac1 = __builtin_bit_cast(eb_s4, *reinterpret_cast<const eb_u2 *>(&xbuf[w][2][lane & 15][2 * (lane >> 4)]));
     const int tq = nq - t0;  // tokens of the page below it are quantized
-    const uint8_t *vtb = reinterpret_cast<const uint8_t *>(vt[w]) + col * 32 + 8 * kk;
+    const uint16_t *vtb = reinterpret_cast<const uint16_t *>(vt[w]) + (col & 7);
     // value reconstruction in the B layout: the metadata of positions 4 kk + i, group v
     float rsc[2][4], rzr[2][4];
     const bool vr_on = vrec && tq > 0 && !a.value_rotation;
@@ -731,8 +723,18 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
     }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const uint2 rv = *reinterpret_cast<const uint2 *>(vtb + m * 16 * 32);
-      const uint32_t r0 = rv.x, r1 = rv.y;
+      // positions 4 kk + i, channel 16 m + col: octet 2 m + col / 8
+      eb_h2 h01, h23;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 4 * kk + i;
+        const uint16_t x = vtb[8 * (n * 16 + ((2 * m + (col >> 3)) ^ n))];
+        if (i == 0) h01[0] = x;
+        if (i == 1) h01[1] = x;
+        if (i == 2) h23[0] = x;
+        if (i == 3) h23[1] = x;
+      }
+      const uint32_t r0 = __builtin_bit_cast(uint32_t, h01), r1 = __builtin_bit_cast(uint32_t, h23);
       Dr[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ar, pack4s(r0, r1), Dr[m], 0, 0, 0);
       uint32_t c0 = r0, c1 = r1;  // window tokens: exact values
       if (tq > 0) {
@@ -771,10 +773,9 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
         float v[8], vh[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint16_t u = reinterpret_cast<const uint16_t *>(vt[w])[(8 * c + e) * 16 + n];
-          v[e] = kvq_bf16_bits_to_f32(u);
           vh[e] = 0.f;
         }
+        bf16x8(vt[w][n * 16 + (c ^ n)], v);
         if (qn) decode8<false>(lay, VP, rs - lay.v_codes_off, n, c, vh);
         row_wht(vh, c, qn);
         if (qn) {

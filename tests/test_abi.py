@@ -235,17 +235,17 @@ def test_error_budget_validation():
 
 
 def test_error_budget_workspace_plan():
-    # one item per (sequence, kv head, group of up to 4 query heads, range of pages); about one
-    # workgroup per CU, at least one page per wave of a range
+    # one item per (sequence, kv head, group of up to 4 query heads, range of pages); about two
+    # workgroups per CU, at least one page per wave of a range
     # and both fp32 scores of every (sequence, query head, position)
     item = 4 * (32 + 4 * 4 * 128 + 4 + 4)
     units = 2 * 8  # batch 2 x 8 kv heads, 4 query heads per kv head: one head group
-    for length, ranges in [(0, 1), (1, 1), (128, 1), (129, 2), (16 * 8 * 16, 16), (32768, 16)]:
+    for length, ranges in [(0, 1), (1, 1), (128, 1), (129, 2), (16 * 8 * 16, 16), (32768, 32)]:
         assert K.kvq_error_budget_workspace_bytes(p(), 2, length) == units * ranges * item + 2 * 32 * length * 8, length
     # 8 query heads per kv head: two head groups
-    assert K.kvq_error_budget_workspace_bytes(p(num_q_heads=64), 2, 32768) == 2 * units * 8 * item + 2 * 64 * 32768 * 8
-    # batch 16 x 8 kv heads: 128 items, two ranges each
-    assert K.kvq_error_budget_workspace_bytes(p(), 16, 32768) == 128 * 2 * item + 16 * 32 * 32768 * 8
+    assert K.kvq_error_budget_workspace_bytes(p(num_q_heads=64), 2, 32768) == 2 * units * 16 * item + 2 * 64 * 32768 * 8
+    # batch 16 x 8 kv heads: 128 items, four ranges each
+    assert K.kvq_error_budget_workspace_bytes(p(), 16, 32768) == 128 * 4 * item + 16 * 32 * 32768 * 8
     assert K.kvq_error_budget_workspace_bytes(p(k_bits=9), 2, 600) == 0
     assert K.kvq_error_budget_workspace_bytes(p(), 0, 600) == 0
     assert K.kvq_error_budget_workspace_bytes(p(), 2, -1) == 0
