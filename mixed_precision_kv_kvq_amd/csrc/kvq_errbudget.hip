@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t eb_pair(const uint8_t *area, int slot, int u
 }
 
 // The reconstruction of 8 channels [8c, 8c + 8) of token n of a page record staged in LDS (keys
-// or values), as zero + code * scale in fp32.
+// or values), zero + code * scale rounded once to fp32 (fused multiply-add).
 template <bool KEYS>
 __device__ __attribute__((always_inline)) inline void decode8(const KvqLayout &lay, EbPlanes P, const uint8_t *rs,
                                                               int n, int c, float *xh) {
@@ -147,7 +147,7 @@ __device__ __attribute__((always_inline)) inline void decode8(const KvqLayout &l
       code[e] = (eb_pair(area, 16 * (n >> 2) + 8 * (c & 1) + e, 8 * ((n & 3) >> 1) + (c >> 1), P) >> hs) & 0xFFFFu;
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) xh[e] = zero + (float)code[e] * scale;
+  for (int e = 0; e < 8; ++e) xh[e] = __builtin_fmaf((float)code[e], scale, zero);
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -199,6 +199,10 @@ constexpr int EB_WAVES = 8;
 constexpr int EB_K16 = (256 * 8 + 64 * 4) / 16;  // largest key part of a record, 16-byte units
 constexpr int EB_V16 = (256 * 8 + 64 * 2) / 16;  // largest value part
 constexpr float EB_Q = 0x1p100f;                 // query operand scale
+// Rows staged in LDS are 17 x 16 bytes apart: the 16 positions of a B operand (same channels), the
+// 16 octets of a row, and 4 positions x 16 channels all fall in distinct banks, and every offset
+// within a page is a constant added to a per-lane base.
+constexpr int EB_ROW16 = 17;
 
 // Work items: one workgroup of EB_WAVES waves per (group of HS <= 4 query heads of one kv head and
 // sequence, range): range `split` of S near-equal ranges of the sequence's pages.  The head groups
@@ -284,9 +288,7 @@ __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrA
   __shared__ float ured[EB_WAVES][3];
   __shared__ float qg[HS][4];                    // sums of the code query over each key group
   __shared__ uint4 recs[EB_WAVES][2][EB_K16];    // key parts of page records (the next one lands meanwhile)
-  // the page's original key rows: channel octet o of position n at n * 16 + (o ^ n), so the 16
-  // positions of a B operand (same octet) and the 16 octets of a row fall in distinct banks
-  __shared__ uint4 rows[EB_WAVES][KVQ_PAGE * 16];
+  __shared__ uint4 rows[EB_WAVES][KVQ_PAGE * EB_ROW16];  // the page's original key rows
   // before the page loop: the group's queries (raw, and the one the codes are scored with)
   float(*qs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&rows[0][0]);
   const int lane = threadIdx.x & 63;
@@ -384,10 +386,10 @@ __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrA
     pk3 = *reinterpret_cast<const uint4 *>(kp + off(3));
   };
   auto store_rows = [&]() __attribute__((always_inline)) {
-    rows[w][(0 + r) * 16 + (c ^ (0 + r))] = pk0;
-    rows[w][(4 + r) * 16 + (c ^ (4 + r))] = pk1;
-    rows[w][(8 + r) * 16 + (c ^ (8 + r))] = pk2;
-    rows[w][(12 + r) * 16 + (c ^ (12 + r))] = pk3;
+    rows[w][(0 + r) * EB_ROW16 + c] = pk0;
+    rows[w][(4 + r) * EB_ROW16 + c] = pk1;
+    rows[w][(8 + r) * EB_ROW16 + c] = pk2;
+    rows[w][(12 + r) * EB_ROW16 + c] = pk3;
   };
   const int kpart16 = lay.v_codes_off / 16;  // the record's key codes and key metadata
   auto load_rec = [&](int pg, int buf) __attribute__((always_inline)) {
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrA
       for (int kc = 0; kc < 4; ++kc) {
         uint32_t mk = kc == jrow ? ~0u : 0u;
         asm volatile("" : "+v"(mk));  // keeps the masked operands in the loop (no 48 registers of zeros)
-        const eb_u4 kv = *reinterpret_cast<const eb_u4 *>(krow + 16 * (n * 16 + ((4 * kc + oct) ^ n)));
+        const eb_u4 kv = *reinterpret_cast<const eb_u4 *>(krow + 16 * (n * EB_ROW16 + 4 * kc + oct));
         const eb_s8 bk = __builtin_bit_cast(eb_s8, kv);
         D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][0] & mk), bk, D0, 0, 0, 0);
         if (lo0) D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[0][1] & mk), bk, D0, 0, 0, 0);
@@ -471,7 +473,7 @@ __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrA
         const int n = 4 * ii + r;
         const bool quant = t0 + n < nq;  // (positions past L are not quantized either)
         float k[8], kh[8];
-        bf16x8(rows[w][n * 16 + (c ^ n)], k);
+        bf16x8(rows[w][n * EB_ROW16 + c], k);
 #pragma unroll
         for (int e = 0; e < 8; ++e) kh[e] = 0.f;
         if (quant) decode8<true>(lay, KP, rs, n, c, kh);
@@ -558,8 +560,7 @@ __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrA
 // B is the original values (exact bf16: a V, a' V) or the value codes (a V_hat, a' V_hat;
 // A = weight * scale * 2^64, window tokens take their exact values as B with A = weight * 2^-69,
 // so every product carries 2^-69), plus the weighted zero points.  The B operands of the original
-// values are read as 16-bit elements from rows staged with the same swizzle as the key rows.  The
-// range's sums go to the workspace: the weights
+// values are read as 16-bit elements from the staged rows.  The range's sums go to the workspace: the weights
 // are final, so the ranges' sums add.  The last head group also takes the value reconstruction
 // errors, in the same layout as the B operands (4 positions x 8 channels per lane).
 template <int HS>
@@ -568,9 +569,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
   __shared__ float ured[EB_WAVES][3];
   __shared__ float zred[EB_WAVES][2][HS][2];      // weighted zero points (set, head, value group)
   __shared__ uint4 recs[EB_WAVES][2][EB_V16];     // value parts of page records (the next one lands meanwhile)
-  // the page's original value rows, channel octet o of position n at n * 16 + (o ^ n): the 4
-  // positions x 16 channels of a B-operand read fall in distinct banks
-  __shared__ uint4 vt[EB_WAVES][KVQ_PAGE * 16];
+  __shared__ uint4 vt[EB_WAVES][KVQ_PAGE * EB_ROW16];  // the page's original value rows
   __shared__ uint32_t xbuf[EB_WAVES][3][16][8];   // value A operands: [raw, code v0, code v1][row][16 bf16]
   // after the page loop: the four weighted sums of the workgroup
   float(*accs)[HS][KVQ_D] = reinterpret_cast<float(*)[HS][KVQ_D]>(&vt[0][0]);
@@ -632,10 +631,10 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
     psc = scores[t0 + t < L ? t0 + t : L - 1];
   };
   auto store_page = [&]() __attribute__((always_inline)) {
-    vt[w][(0 + r) * 16 + (c ^ (0 + r))] = pv0;
-    vt[w][(4 + r) * 16 + (c ^ (4 + r))] = pv1;
-    vt[w][(8 + r) * 16 + (c ^ (8 + r))] = pv2;
-    vt[w][(12 + r) * 16 + (c ^ (12 + r))] = pv3;
+    vt[w][(0 + r) * EB_ROW16 + c] = pv0;
+    vt[w][(4 + r) * EB_ROW16 + c] = pv1;
+    vt[w][(8 + r) * EB_ROW16 + c] = pv2;
+    vt[w][(12 + r) * EB_ROW16 + c] = pv3;
   };
   const int vpart16 = (lay.record - lay.v_codes_off) / 16;  // the record's value codes and metadata
   auto load_rec = [&](int pg, int bf) __attribute__((always_inline)) {
@@ -728,7 +727,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = 4 * kk + i;
-        const uint16_t x = vtb[8 * (n * 16 + ((2 * m + (col >> 3)) ^ n))];
+        const uint16_t x = vtb[8 * (n * EB_ROW16 + 2 * m + (col >> 3))];
         if (i == 0) h01[0] = x;
         if (i == 1) h01[1] = x;
         if (i == 2) h23[0] = x;
@@ -755,7 +754,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
           for (int i = 0; i < 4; ++i) {
             if (4 * kk + i < tq) {
               const float x = __builtin_bit_cast(float, rw[i]);
-              const float err = (rzr[v][i] + (float)cw[i] * rsc[v][i]) - x;
+              const float err = __builtin_fmaf((float)cw[i], rsc[v][i], rzr[v][i]) - x;
               ev_sq = __builtin_fmaf(err, err, ev_sq);
               ev_max = __builtin_fmaxf(ev_max, __builtin_fabsf(err));
               v_sq = __builtin_fmaf(x, x, v_sq);
@@ -775,7 +774,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
         for (int e = 0; e < 8; ++e) {
           vh[e] = 0.f;
         }
-        bf16x8(vt[w][n * 16 + (c ^ n)], v);
+        bf16x8(vt[w][n * EB_ROW16 + c], v);
         if (qn) decode8<false>(lay, VP, rs - lay.v_codes_off, n, c, vh);
         row_wht(vh, c, qn);
         if (qn) {
