@@ -374,6 +374,7 @@ def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
     from workloads.device import DeviceGenerator
 
     rows, eb_rows = [], []
+    small_ceiling = None
     for kb, vb in W.SWEEP_BITS + W.PLANE_BITS:
         wl = W.WORKLOADS[4].with_bits(kb, vb)
         Lb = wl.context_lengths()
@@ -395,6 +396,9 @@ def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
         qpages = -(-Lb // 16)
         nbytes = int(wl.num_kv_heads * (Lb.sum() * per_th + qpages.sum() * 4)
                      + wl.batch * wl.num_q_heads * wl.head_dim * 2)
+        if small_ceiling is None:
+            # the read-only streaming ceiling at this launch's size (the first bit pair, K4V2)
+            small_ceiling = stream_ceiling(torch, nbytes, stream, reps)
         n_cp = copies_for(nbytes)
         copies = [cb] + [clone_cache(K, torch, cb, prm, wl.batch, pool, table) for _ in range(n_cp - 1)]
         wsb = K.kvq_decode_workspace_bytes(prm, wl.batch, Lmax)
@@ -424,6 +428,7 @@ def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
             else:
                 os.environ["KVQ_PAGES_PER_SPLIT"] = old_env
         rf = kernel_roofline(cold, warm, nbytes, ceiling_GBs)
+        rf["frac_of_size_matched_stream_ceiling_cold"] = round(nbytes / cold / 1e3 / small_ceiling["best"]["cold_GBs"], 4)
         rows.append(dict(k_bits=kb, v_bits=vb, row_stride_splits=splits, combine_us=round(comb, 2),
                          traffic=stored_traffic(f"paged K{kb}V{vb}: cold"),
                          uniform_plan_us_cold=round(cold_uniform, 2),
@@ -454,8 +459,11 @@ def paged_sweep(torch, dev, reps, stream, ceiling_GBs, plan):
     sweep = {"workload": wl.name, "lengths": [int(x) for x in wl.context_lengths()],
              "what": "kvq_decode_partials (split kernel, read-only) per bit pair; algorithmic bytes = codes and "
                      "metadata of every stored token-head + block-table entries + queries; cold: cycling over copies "
-                     "of the page pool; uniform plan: every split sized from the longest sequence",
-             "rows": rows}
+                     "of the page pool; uniform plan: every split sized from the longest sequence; "
+                     "frac_of_stream_ceiling_cold against the 32k decode step's streaming ceiling, "
+                     "frac_of_size_matched_stream_ceiling_cold against stream_ceiling_at_this_size (the "
+                     "read-only streaming kernel over the K4V2 launch's byte count)",
+             "stream_ceiling_at_this_size": small_ceiling, "rows": rows}
     ebs = {"workload": wl.name, "query": "decode step 0", "rows": eb_rows}
     return sweep, ebs
 
