@@ -456,9 +456,9 @@ size_t kvq_error_budget_workspace_bytes(const kvq_params *params, int32_t batch,
   if (check_params(params) != KVQ_OK || batch <= 0 || max_seq_len < 0 || max_seq_len > INT32_MAX) return 0;
   const int g = params->num_q_heads / params->num_kv_heads, ngrp = g / kvq_errbudget_heads_per_group(g);
   const size_t items = (size_t)batch * params->num_kv_heads * ngrp * errbudget_splits(params, batch, max_seq_len);
-  // the items, then both scores of every (sequence, query head, position)
+  // the items, then both scores of every (sequence, query head, position), rows padded to whole pages
   return items * kvq_errbudget_item_floats() * sizeof(float) +
-         (size_t)batch * params->num_q_heads * (size_t)max_seq_len * 2 * sizeof(float);
+         (size_t)batch * params->num_q_heads * kvq_errbudget_score_stride(max_seq_len) * 2 * sizeof(float);
 }
 
 kvq_status kvq_error_budget(const kvq_params *params, const kvq_cache *cache, const int32_t *seq_lens,

@@ -212,16 +212,21 @@ constexpr int EB_ROW16 = 17;
 // LDS region.
 //
 // Workspace: one item of EB_W_ITEM floats per (kv head unit, head group, range), then the scores
-// [batch][query head][max_len][2] (exact, quantized; dot units) that pass 1 writes for pass 2.  An
-// item holds the pass-1 statistics of each head {M0, Z0, M1, Z1, max |ds|, sum ds^2}, the key
-// reconstruction sums {sum e^2, max |e|, sum k^2}, then the pass-2 sums [sum][head][channel] of
-// a V, a V_hat, a' V, a' V_hat, the total variation of each head and the value reconstruction sums.
+// [batch][query head][max_len rounded up to 16][2] (exact, quantized; dot units) that pass 1
+// writes for pass 2.  An item holds the pass-1 statistics of each head {M0, Z0, M1, Z1,
+// max |ds|, sum ds^2}, the key reconstruction sums {sum e^2, max |e|, sum k^2}, then the pass-2
+// sums [sum][head][channel] of a V, a V_hat, a' V, a' V_hat, the total variation of each head and
+// the value reconstruction sums.
 constexpr int EB_W_STATS = 0;
 constexpr int EB_W_KREC = 24;
 constexpr int EB_W_SUMS = 32;
 constexpr int EB_W_TV = EB_W_SUMS + 4 * 4 * KVQ_D;
 constexpr int EB_W_VREC = EB_W_TV + 4;
-constexpr int EB_W_ITEM = EB_W_VREC + 4;
+constexpr int EB_W_ITEM = (EB_W_VREC + 4 + 31) / 32 * 32;  // whole 128-byte lines
+
+// Positions per (sequence, query head) row of the stored scores: a whole number of pages, so each
+// page's 16 scores of a head are one aligned 128-byte segment.
+__host__ __device__ inline size_t eb_score_stride(int64_t max_len) { return (size_t)((max_len + 15) / 16) * 16; }
 
 struct EbItem {
   int unit, grp, split, b, h, hq0, L, nq, pbeg, pend;
@@ -398,7 +403,7 @@ __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrA
   const float sl2 = a.scale * 1.4426950408889634f;  // softmax scale in log2 units
   const uint8_t *krow = reinterpret_cast<const uint8_t *>(rows[w]);
   float2 *scores = reinterpret_cast<float2 *>(a.ws + (size_t)a.B * a.Hkv * (a.Hq / a.Hkv / HS) * a.splits * EB_W_ITEM) +
-                   ((size_t)b * a.Hq + it.hq0 + (qlive ? q : 0)) * a.max_len;
+                   ((size_t)b * a.Hq + it.hq0 + (qlive ? q : 0)) * eb_score_stride(a.max_len);
 
   float m0 = ninf, z0 = 0.f, m1 = ninf, z1 = 0.f, ds_max = 0.f, ds_sq = 0.f;
   float ek_sq = 0.f, ek_max = 0.f, k_sq = 0.f;  // key reconstruction error (head group 0)
@@ -615,7 +620,7 @@ __global__ __launch_bounds__(64 * EB_WAVES) void kvq_eb_sums_kernel(KvqErrArgs a
 
   const uint32_t row_elems = (uint32_t)Hkv * KVQ_D;
   const float2 *scores = reinterpret_cast<const float2 *>(a.ws + (size_t)a.B * Hkv * ngrp * S * EB_W_ITEM) +
-                         ((size_t)b * a.Hq + it.hq0 + (qlive ? q : 0)) * a.max_len;
+                         ((size_t)b * a.Hq + it.hq0 + (qlive ? q : 0)) * eb_score_stride(a.max_len);
   // the next page in flight: pv_i = 8 channels of position 4 i + r (clamped to L - 1), its scores
   uint4 pv0, pv1, pv2, pv3;
   float2 psc;
@@ -974,6 +979,7 @@ void launch_eb(const KvqErrArgs &a, int ngrp, hipStream_t s) {
 
 int kvq_errbudget_heads_per_group(int g) { return g < 4 ? g : 4; }
 size_t kvq_errbudget_item_floats() { return EB_W_ITEM; }
+size_t kvq_errbudget_score_stride(int64_t max_len) { return eb_score_stride(max_len); }
 
 hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;

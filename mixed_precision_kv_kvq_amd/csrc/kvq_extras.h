@@ -37,4 +37,5 @@ struct KvqErrArgs {
 };
 int kvq_errbudget_heads_per_group(int g);
 size_t kvq_errbudget_item_floats();
+size_t kvq_errbudget_score_stride(int64_t max_len);  // positions per row of the stored scores
 hipError_t kvq_launch_errbudget(const KvqErrArgs &a, hipStream_t s);

@@ -238,10 +238,11 @@ def test_error_budget_workspace_plan():
     # one item per (sequence, kv head, group of up to 4 query heads, range of pages); about two
     # workgroups per CU, at least one page per wave of a range
     # and both fp32 scores of every (sequence, query head, position)
-    item = 4 * (32 + 4 * 4 * 128 + 4 + 4)
+    item = 4 * 2112  # 32 + 4 x 4 x 128 + 4 + 4 floats, padded to whole 128-byte lines
     units = 2 * 8  # batch 2 x 8 kv heads, 4 query heads per kv head: one head group
     for length, ranges in [(0, 1), (1, 1), (128, 1), (129, 2), (16 * 8 * 16, 16), (32768, 32)]:
-        assert K.kvq_error_budget_workspace_bytes(p(), 2, length) == units * ranges * item + 2 * 32 * length * 8, length
+        rows = -(-length // 16) * 16  # score rows padded to whole 16-position pages
+        assert K.kvq_error_budget_workspace_bytes(p(), 2, length) == units * ranges * item + 2 * 32 * rows * 8, length
     # 8 query heads per kv head: two head groups
     assert K.kvq_error_budget_workspace_bytes(p(num_q_heads=64), 2, 32768) == 2 * units * 16 * item + 2 * 64 * 32768 * 8
     # batch 16 x 8 kv heads: 128 items, four ranges each
