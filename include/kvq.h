@@ -76,7 +76,13 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* A status crosses the ABI as a 32-bit int; in C++ the enum has that underlying type, so any
+ * value a caller passes (kvq_status_str) is a valid object of it. */
+typedef enum
+#ifdef __cplusplus
+    : int32_t
+#endif
+{
   KVQ_OK = 0,
   KVQ_EINVAL = 1,       /* null or misaligned pointer, inconsistent shapes       */
   KVQ_EUNSUPPORTED = 2, /* a parameter outside the supported set (see below)      */
@@ -94,7 +100,10 @@ typedef enum { KVQ_ROT_NONE = 0, KVQ_ROT_WHT = 1 } kvq_rotation;
  * Counts", section "Resultaten": bit widths from 1 to 8 for keys and values
  * separately; 7 is not offered);
  * k_group in {32, 64, 128}; v_group in {64, 128};
- * window >= 0; block_size in {0, 16}; value_rotation only with window == 0. */
+ * 0 <= window <= KVQ_MAX_WINDOW; num_q_heads <= KVQ_MAX_HEADS; block_size in {0, 16};
+ * value_rotation only with window == 0. */
+#define KVQ_MAX_HEADS 4096
+#define KVQ_MAX_WINDOW (1 << 20)
 typedef struct {
   int32_t head_dim;
   int32_t num_q_heads;

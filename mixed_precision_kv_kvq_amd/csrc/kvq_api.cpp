@@ -17,6 +17,8 @@ kvq_status check_params(const kvq_params *p) {
   if (!p) return KVQ_EINVAL;
   if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads) return KVQ_EINVAL;
   if (p->window < 0 || p->key_rotation < 0 || p->key_rotation > 1) return KVQ_EINVAL;
+  // bounds that keep every size and plan product far inside 64 bits
+  if (p->num_q_heads > KVQ_MAX_HEADS || p->window > KVQ_MAX_WINDOW) return KVQ_EUNSUPPORTED;
   if (p->value_rotation < 0 || p->value_rotation > 1) return KVQ_EINVAL;
   if (p->kv_dtype != KVQ_F32 && p->kv_dtype != KVQ_BF16) return KVQ_EINVAL;
   if (p->head_dim != KVQ_D) return KVQ_EUNSUPPORTED;
@@ -74,6 +76,7 @@ struct SplitPlan {
 };
 
 SplitPlan split_plan(const kvq_params *p, int32_t batch, int64_t max_seq_len, int q_parts) {
+  if (max_seq_len > INT32_MAX) max_seq_len = INT32_MAX;  // device lengths are int32 (the launch clamps too)
   const int R = p->window;
   const int64_t nq = max_seq_len > R ? max_seq_len - R : 0;
   const int64_t nw = max_seq_len < R ? max_seq_len : R;
@@ -132,12 +135,19 @@ kvq_status kvq_cache_sizes(const kvq_params *params, int32_t batch, int64_t capa
   if (kvq_status st = check_params(params)) return st;
   if (!out || batch <= 0 || capacity <= 0) return KVQ_EINVAL;
   const KvqLayout lay = layout_of(params);
+  // byte counts that do not fit size_t are reported as invalid arguments
+  size_t pages, pb, wb;
+  if (params->block_size)
+    pages = (size_t)capacity;
+  else if (__builtin_mul_overflow((size_t)batch, (size_t)kvq_pages_per_seq(capacity), &pages))
+    return KVQ_EINVAL;
+  if (__builtin_mul_overflow(pages, (size_t)params->num_kv_heads * (size_t)lay.record, &pb)) return KVQ_EINVAL;
+  if (__builtin_mul_overflow((size_t)batch * params->num_kv_heads,
+                             (size_t)params->window * KVQ_D * (params->kv_dtype == KVQ_F32 ? 4 : 2), &wb))
+    return KVQ_EINVAL;
   out->record_bytes = (size_t)lay.record;
-  const size_t pages = params->block_size ? (size_t)capacity
-                                          : (size_t)batch * kvq_pages_per_seq(capacity);
-  out->pages_bytes = pages * params->num_kv_heads * (size_t)lay.record;
-  out->window_bytes = (size_t)batch * params->num_kv_heads * (size_t)params->window * KVQ_D *
-                      (params->kv_dtype == KVQ_F32 ? 4 : 2);
+  out->pages_bytes = pb;
+  out->window_bytes = wb;
   return KVQ_OK;
 }
 

@@ -42,7 +42,9 @@
 #define KVQ_PAGE 16
 #define KVQ_D 128
 // Pages per sequence of a contiguous store of `capacity` tokens.
-__host__ __device__ inline int64_t kvq_pages_per_seq(int64_t capacity) { return (capacity + KVQ_PAGE - 1) / KVQ_PAGE; }
+__host__ __device__ inline int64_t kvq_pages_per_seq(int64_t capacity) {
+  return capacity / KVQ_PAGE + (capacity % KVQ_PAGE != 0);  // (no overflow near INT64_MAX)
+}
 
 struct KvqLayout {
   int kb, kg, vb, vg;

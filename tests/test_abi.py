@@ -52,6 +52,15 @@ def test_record_size_matches_memory_model(kb, vb, expect):
     assert s.window_bytes == 0
 
 
+def test_sizes_that_do_not_fit_are_rejected():
+    out = K.kvq_sizes()
+    L = K.lib()
+    assert L.kvq_cache_sizes(ctypes.byref(p()), 2 ** 31 - 1, 2 ** 63 - 1, ctypes.byref(out)) == K.KVQ_EINVAL
+    assert L.kvq_cache_sizes(ctypes.byref(p(block_size=16)), 1, 2 ** 62, ctypes.byref(out)) == K.KVQ_EINVAL
+    assert L.kvq_cache_sizes(ctypes.byref(p()), 1, 2 ** 40, ctypes.byref(out)) == K.KVQ_OK  # 2^36 pages x 8 x 1856 B
+    assert out.pages_bytes == (2 ** 36) * 8 * out.record_bytes
+
+
 def test_window_and_paged_sizes():
     s = K.kvq_cache_sizes(p(window=128), 16, 32832)
     assert s.window_bytes == 16 * 8 * 128 * 128 * 2
@@ -75,6 +84,8 @@ def test_window_and_paged_sizes():
     (dict(key_rotation=2), K.KVQ_EINVAL),
     (dict(value_rotation=-1), K.KVQ_EINVAL),
     (dict(value_rotation=1, window=4), K.KVQ_EUNSUPPORTED),
+    (dict(num_q_heads=8192, num_kv_heads=1024), K.KVQ_EUNSUPPORTED),  # beyond KVQ_MAX_HEADS
+    (dict(window=(1 << 20) + 1), K.KVQ_EUNSUPPORTED),  # beyond KVQ_MAX_WINDOW
 ])
 def test_bad_params_rejected(kw, status):
     out = K.kvq_sizes()
