@@ -286,7 +286,9 @@ __device__ __forceinline__ void eb_load_rec(const KvqErrArgs &a, const EbItem &i
 // stored exact (s' = s).  Lane 16 q + t then holds both scores of token t for head q: written to the
 // workspace, and folded into online maxima and sums (log2 units) and the score-error statistics,
 // merged over the 16 lanes of a head and the waves.  Head group 0 also takes the key
-// reconstruction errors (8 channels of a position per lane).
+// reconstruction errors: from the code and key operands of the score contraction (32 channels of
+// one position per lane), or, with rotated keys, from whole rows rotated back (8 channels of a
+// position per lane).
 template <int HS>
 __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrArgs a) {  // two workgroups per CU
   __shared__ float red[EB_WAVES][6 * HS];
@@ -439,14 +441,33 @@ __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrA
       s1 = s0;
       if (t0 < nq) {  // the page holds quantized tokens
         const uint8_t *kcodes = rs + lay.k_codes_off;
+        const uint32_t *kmn = reinterpret_cast<const uint32_t *>(rs + lay.k_meta_off) + n * lay.nkg;
+        const bool kerr = krec && !a.rotation && t0 + n < nq;  // errors in the operand layout (lane: token n)
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
           uint32_t mk = kc == jrow ? ~0u : 0u;
           asm volatile("" : "+v"(mk));
-          const eb_s8 bc = pack8s(eb_pair(kcodes, 16 * oct + n, 4 * kc + 0, KP), eb_pair(kcodes, 16 * oct + n, 4 * kc + 1, KP),
-                                  eb_pair(kcodes, 16 * oct + n, 4 * kc + 2, KP), eb_pair(kcodes, 16 * oct + n, 4 * kc + 3, KP));
+          const uint32_t p0 = eb_pair(kcodes, 16 * oct + n, 4 * kc + 0, KP), p1 = eb_pair(kcodes, 16 * oct + n, 4 * kc + 1, KP);
+          const uint32_t p2 = eb_pair(kcodes, 16 * oct + n, 4 * kc + 2, KP), p3 = eb_pair(kcodes, 16 * oct + n, 4 * kc + 3, KP);
+          const eb_s8 bc = pack8s(p0, p1, p2, p3);
           D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[1][0] & mk), bc, D1, 0, 0, 0);
           if (lo1) D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(eb_s8, qd[1][1] & mk), bc, D1, 0, 0, 0);
+          if (kerr) {  // channels 32 kc + 8 oct + e of token n: one key group (groups of 32 or more)
+            const uint32_t mm = kmn[(32 * kc) / lay.kg];
+            const float ksc = f16f(mm & 0xFFFF), kz = f16f(mm >> 16);
+            const eb_u4 kv = *reinterpret_cast<const eb_u4 *>(krow + 16 * (n * EB_ROW16 + 4 * kc + oct));
+            const uint32_t pc[4] = {p0, p1, p2, p3};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t cw = (e & 1) ? (pc[e >> 1] >> 16) : (pc[e >> 1] & 0xFFFFu);
+              const uint32_t kw = (e & 1) ? (kv[e >> 1] & 0xFFFF0000u) : (kv[e >> 1] << 16);
+              const float x = __builtin_bit_cast(float, kw);
+              const float err = __builtin_fmaf((float)cw, ksc, kz) - x;
+              ek_sq = __builtin_fmaf(err, err, ek_sq);
+              ek_max = __builtin_fmaxf(ek_max, __builtin_fabsf(err));
+              k_sq = __builtin_fmaf(x, x, k_sq);
+            }
+          }
         }
         if (t0 + t < nq) {
           const uint32_t *km = reinterpret_cast<const uint32_t *>(rs + lay.k_meta_off) + t * lay.nkg;
@@ -472,7 +493,7 @@ __global__ __launch_bounds__(64 * EB_WAVES, 4) void kvq_eb_scores_kernel(KvqErrA
       ds_max = __builtin_fmaxf(ds_max, __builtin_fabsf(ds));
       ds_sq = __builtin_fmaf(ds, ds, ds_sq);
     }
-    if (krec) {  // key reconstruction errors, 8 channels of positions 4 i + r per lane
+    if (krec && a.rotation && t0 < nq) {  // rotated keys: whole rows rotated back, 8 channels of positions 4 i + r
 #pragma unroll 1
       for (int ii = 0; ii < 4; ++ii) {
         const int n = 4 * ii + r;
