@@ -30,7 +30,12 @@
 //      Lane 16 q + t then holds, in accumulator row r, head q's partial dot with
 //      chunk r of token t, so the group scales and zero points are applied and the
 //      chunks summed inside the lane: one score per (token, head) per lane, no
-//      cross-lane reduction and no replicated softmax work.
+//      cross-lane reduction and no replicated softmax work.  With 8 or 16 (head,
+//      query part) rows (8 heads, or hi + lo query parts) the A rows are those
+//      pairs over a whole chunk instead: one MFMA per chunk into its own
+//      accumulator, lane 16 q + t holding head q + 4 hb's rows of token t, the
+//      chunk's scale applied per token in the lane (4 MFMAs per page instead of
+//      up to 16).
 //   V: 8 MFMAs (one per 16-channel tile), A = softmax weights (rows = hi/lo
 //      part x head, k = 32 tokens), B = value codes (k = tokens, col = channel).
 //      The weights reach the A-operand layout through a small per-wave LDS
@@ -215,6 +220,17 @@ struct Kern {
   static constexpr int HB = (G + 3) / 4;   // head blocks: row q of the score layout holds heads q + 4 hb
   static constexpr int HSN = G < 4 ? G : 4;  // rows of the score layout in use
   static constexpr int NACC = HB;           // score accumulators (both query parts add into one)
+  // Query layout of the score contraction.  With at most 4 (head, part) rows (G * P <= 4) the A
+  // rows are (head slot, chunk) and one accumulator per head block collects every chunk's partial
+  // dot in its own row (build_q_with).  With 8 or 16 such rows (ROWQ) that layout would repeat the
+  // contraction once per part and head block with three quarters of the A rows zero; instead the A
+  // rows are (head, part) over a whole chunk, one MFMA per chunk covers every head and part, and
+  // each chunk has its own accumulator (build_q_rows).
+  static constexpr bool ROWQ = G * P >= 8;
+  static constexpr int QAP = ROWQ ? 1 : P, QAH = ROWQ ? 1 : HB;
+  // Row of a ROWQ score accumulator (lane 16 q + t: rows 4 q .. 4 q + 3) holding head q + 4 hb,
+  // query part `part`.
+  static __device__ __forceinline__ constexpr int qrow(int hb, int part) { return P == 2 ? 2 * hb + part : hb; }
   static constexpr int NPK = kvq_nplanes(KB), NPV = kvq_nplanes(VB);  // bit planes of a code
   // plane widths and offsets as constants (a width of 1 for planes a code does not have)
   static constexpr int KW0 = kvq_plane_width(KB, 0), VW0 = kvq_plane_width(VB, 0);
@@ -228,7 +244,7 @@ struct Kern {
   typedef State<HB, NVG> St;
 
   struct Ctx {
-    bf16x8 qA[P][HB][4];  // query operand per part, head block and 32-channel chunk
+    bf16x8 qA[QAP][QAH][4];  // query operand per 32-channel chunk (per part and head block unless ROWQ)
     float Qc[HB][4];     // sum of the query operand over chunk r of head quad + 4 hb, x 2^-133
     uint32_t xw;         // exchange-buffer address of this lane's (head row, page-A slot)
     uint32_t xr;         // exchange-buffer address of this lane's A-operand row segment
@@ -304,19 +320,91 @@ struct Kern {
     }
   }
 
+  // ROWQ query operand.  Row rho = 4 hs + r holds head hs + 4 hb, part `part` (r = qrow(hb, part)),
+  // over all 32 channels of each chunk: qA[0][0][kc] is the A operand of chunk kc (lane 16 c + rho:
+  // channels 32 kc + 8 c + e), so D row 4 q + qrow(hb, part) of chunk kc's accumulator (lane
+  // 16 q + t) is head q + 4 hb's partial dot with chunk kc of token t for that part.  getq(kc, e)
+  // returns the fp32 query of the lane's row head at channel 32 kc + 8 (lane / 16) + e.  Code
+  // operands divide each pair slot by its read scale as in build_q_with.
+  template <class GetQ>
+  static __device__ __forceinline__ void build_q_rows(Ctx &cx, GetQ getq, bool code_scaled) {
+    const int rho = cx.lane & 15, hs = rho >> 2, r = rho & 3;
+    const int hb = P == 2 ? (r >> 1) : r, part = P == 2 ? (r & 1) : 0;
+    const bool live = hs < HSN && hb < HB;
+    float qsum[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = live ? getq(kc, e) * EXP2_EQ : 0.f;
+      uint32_t w[4];
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hi = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+        const uint32_t lo = pack_bf16x2(v[2 * i] - bf16lo_f32(hi), v[2 * i + 1] - bf16hi_f32(hi));
+        const uint32_t pr = part ? lo : hi;
+        const float e0 = bf16lo_f32(pr), e1 = bf16hi_f32(pr);
+        sum += e0 + e1;
+        const float f = code_scaled ? __builtin_amdgcn_ldexpf(1.0f, -kslot_scale(kc, i)) : 1.0f;
+        w[i] = pack_bf16x2(e0 * f, e1 * f);  // exact: power-of-two scaling
+      }
+      qsum[kc] = sum;
+      cx.qA[0][0][kc] = pack8(w[0], w[1], w[2], w[3]);
+    }
+    // Chunk sums of each row (its four lanes hold the chunk's 32 channels), then for lane 16 q + t
+    // the sums of its heads q + 4 hb over both parts.
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) qsum[kc] = rows_sum(qsum[kc]) * EXP2_M66 * EXP2_M67;
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        float q = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp) q += __shfl(qsum[kc], 4 * cx.quad + qrow(h, pp));
+        cx.Qc[h][kc] = q;
+      }
+    }
+  }
+
   // Query from LDS (fp32 [G][128]).
   static __device__ __forceinline__ void build_q(Ctx &cx, const float *qs, bool code_scaled = true) {
-    const int rho = cx.lane & 15, hs = (rho >> 2) < HSN ? (rho >> 2) : 0, ch0 = 32 * (rho & 3) + 8 * cx.quad;
-    build_q_with(cx, [&](int hb, int e) { return qs[(hs + 4 * hb) * KVQ_D + ch0 + e]; }, code_scaled);
+    if constexpr (ROWQ) {
+      const int rho = cx.lane & 15, r = rho & 3, hb = P == 2 ? (r >> 1) : r;
+      const int h = ((rho >> 2) < HSN && hb < HB) ? (rho >> 2) + 4 * hb : 0;
+      build_q_rows(cx, [&](int kc, int e) { return qs[h * KVQ_D + 32 * kc + 8 * cx.quad + e]; }, code_scaled);
+    } else {
+      const int rho = cx.lane & 15, hs = (rho >> 2) < HSN ? (rho >> 2) : 0, ch0 = 32 * (rho & 3) + 8 * cx.quad;
+      build_q_with(cx, [&](int hb, int e) { return qs[(hs + 4 * hb) * KVQ_D + ch0 + e]; }, code_scaled);
+    }
   }
 
   // This lane's query channels (one octet of one chunk per head block), straight from global
   // memory: 16-byte loads, fp32 or bf16 as stored.
+  // (ROWQ: one octet of every chunk of the lane's row head.)
+  static constexpr int QRN = ROWQ ? 4 : HB;
   struct QRegs {
-    u32x4 v[HB][2];
+    u32x4 v[QRN][2];
   };
   static __device__ __forceinline__ void load_q_regs(QRegs &qr, const KvqAttnArgs &args, const Ctx &cx, int b,
                                                      int hq0) {
+    if constexpr (ROWQ) {
+      const int rho = cx.lane & 15, r = rho & 3, hb = P == 2 ? (r >> 1) : r;
+      const int h = ((rho >> 2) < HSN && hb < HB) ? (rho >> 2) + 4 * hb : 0;
+      const uint8_t *row = (const uint8_t *)args.q + ((size_t)b * args.Hq + hq0 + h) * KVQ_D * (args.q_f32 ? 4 : 2);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const int ch0 = 32 * kc + 8 * cx.quad;
+        if (args.q_f32) {
+          qr.v[kc][0] = gload<u32x4>(row + 4 * ch0);
+          qr.v[kc][1] = gload<u32x4>(row + 4 * ch0 + 16);
+        } else {
+          qr.v[kc][0] = gload<u32x4>(row + 2 * ch0);
+        }
+      }
+      return;
+    }
     const int rho = cx.lane & 15, hs = (rho >> 2) < HSN ? (rho >> 2) : 0, ch0 = 32 * (rho & 3) + 8 * cx.quad;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -331,17 +419,18 @@ struct Kern {
     }
   }
   static __device__ __forceinline__ void build_q_regs(Ctx &cx, const QRegs &qr, bool q_f32, bool code_scaled = true) {
-    build_q_with(
-        cx,
-        [&](int hb, int e) {
-          // (copy the vector element out first: a bit cast of the element lvalue itself
-          // reads the vector's first element)
-          const uint32_t u = qr.v[hb][e >> 2][e & 3];
-          if (q_f32) return __builtin_bit_cast(float, u);
-          const uint32_t w = qr.v[hb][0][e >> 1];
-          return kvq_bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFF));
-        },
-        code_scaled);
+    // (copy the vector element out first: a bit cast of the element lvalue itself reads the
+    // vector's first element)
+    auto get = [&](int i, int e) {
+      const uint32_t u = qr.v[i][e >> 2][e & 3];
+      if (q_f32) return __builtin_bit_cast(float, u);
+      const uint32_t w = qr.v[i][0][e >> 1];
+      return kvq_bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFF));
+    };
+    if constexpr (ROWQ)
+      build_q_rows(cx, get, code_scaled);
+    else
+      build_q_with(cx, get, code_scaled);
   }
 
   static __device__ __forceinline__ void init_ctx(Ctx &cx, float sig, uint32_t xbase) {
@@ -674,6 +763,27 @@ struct Kern {
   template <int KS>
   static __device__ __forceinline__ void page_scores(const Ctx &cx, const float (*Qg)[4], const PageData<KS> &pd,
                                                      float s[HB]) {
+    if constexpr (ROWQ) {
+      // one MFMA per chunk into its own accumulator; the chunk's group scale applies per token
+      f32x4 Dk[4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        Dk[kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[0][0][kc], key_operand(pd, kc),
+                                                         f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float acc = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const float d = P == 2 ? Dk[kc][qrow(hb, 0)] + Dk[kc][qrow(hb, 1)] : Dk[kc][qrow(hb, 0)];
+          acc = __builtin_fmaf(d, h2f(pd.km[kc >> KS] & 0xFFFF), acc);
+        }
+#pragma unroll
+        for (int g = 0; g < (4 >> KS); ++g) acc = __builtin_fmaf(h2f(pd.km[g] >> 16), Qg[hb][g], acc);
+        s[hb] = acc;
+      }
+      return;
+    }
     f32x4 D[NACC];
 #pragma unroll
     for (int a = 0; a < NACC; ++a) D[a] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -783,9 +893,9 @@ struct Kern {
           }
           const bf16x8 kh = pack8(hi[0], hi[1], hi[2], hi[3]), kl = pack8(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
-          for (int part = 0; part < P; ++part) {
+          for (int part = 0; part < QAP; ++part) {
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
+            for (int hb = 0; hb < QAH; ++hb) {
               D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], kh, D[hb], 0, 0, 0);
               D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], kl, D[hb], 0, 0, 0);
             }
@@ -799,9 +909,9 @@ struct Kern {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
-          for (int part = 0; part < P; ++part) {
+          for (int part = 0; part < QAP; ++part) {
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
+            for (int hb = 0; hb < QAH; ++hb)
               D[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.qA[part][hb][kc], __builtin_bit_cast(bf16x8, kr[kc]),
                                                               D[hb], 0, 0, 0);
           }
@@ -809,7 +919,9 @@ struct Kern {
       }
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const float acc = (D[hb][0] + D[hb][1]) + (D[hb][2] + D[hb][3]);
+        // ROWQ: one accumulator, rows (head, part); else one per head block, rows (head, chunk)
+        const float acc = ROWQ ? (P == 2 ? D[0][qrow(hb, 0)] + D[0][qrow(hb, 1)] : D[0][qrow(hb, 0)])
+                               : (D[hb][0] + D[hb][1]) + (D[hb][2] + D[hb][3]);
         s[sub][hb] = ok ? acc * EXP2_M66 * EXP2_M67 : -__builtin_inff();
       }
     }
