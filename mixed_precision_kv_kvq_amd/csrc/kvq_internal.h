@@ -121,17 +121,14 @@ struct KvqDebugArgs {
 #define KVQ_WIN_PAGES 8  // window pages (128 tokens) per window split
 
 // Waves per SIMD each split-kernel instantiation is compiled for (register budget
-// 512 / waves): 2 for all but the widest ones.  With 8 waves per CU each wave gets an LDS ring
-// of up to 8 pages (6 in flight while a pair is processed, the same bytes in flight per CU as
-// 16 waves with 3 each), and the 32k batch-16 K4V2 launch measured 91 µs against 94 µs at 4
-// waves per SIMD (3 waves per SIMD measured 114 µs, 1 wave 143 µs).  Sixteen query rows
-// (8 heads per kv head, query split into hi and lo parts) fit 256 registers only for 4-bit
-// keys, 2-bit values and one value group (the rotated-key configuration); the other
-// sixteen-row instantiations run at 1 wave per SIMD.  No instantiation spills at its budget
-// (the build checks this).
-__host__ __device__ constexpr int kvq_attn_wpe(int kb, int vb, int g, int p, int nvg) {
-  return (g * p == 16 && !(kb == 4 && vb == 2 && nvg == 1)) ? 1 : 2;
-}
+// 512 / waves): 2 for every one.  With 8 waves per CU each wave gets an LDS ring of up to 8
+// pages (6 in flight while a pair is processed, the same bytes in flight per CU as 16 waves
+// with 3 each), and the 32k batch-16 K4V2 launch measured 91 µs against 94 µs at 4 waves per
+// SIMD (3 waves per SIMD measured 114 µs, 1 wave 143 µs).  With the score operand laid out as
+// (head, query part) rows when there are 8 or 16 of them, the widest instantiations (8 heads
+// per kv head, query in hi and lo parts) need 188-195 registers.  No instantiation spills at
+// its budget (the build checks this).
+__host__ __device__ constexpr int kvq_attn_wpe(int, int, int, int, int) { return 2; }
 
 #define KVQ_LDS_PER_CU (160 * 1024)
 
