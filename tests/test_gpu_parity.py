@@ -181,6 +181,37 @@ def test_ragged_split_plan(name):
         full_check(run, s, out_check_bf16=(s == 0))
 
 
+# Score operands with 8 or 16 (head, query part) rows (8 heads per kv head and/or a query in hi and
+# lo parts) are laid out as those rows over whole 32-channel chunks, one accumulator per chunk: key
+# groups of 32, 64 and 128 (the group scale of chunk r is group r / (group / 32)), ragged tails,
+# bf16 and fp32 windows, decode steps through the fused step (the evicted token scored in the
+# window split) and through the append kernel, rotated keys.
+ROW_OPERAND = {
+    "g8-kgroup64-vgroup64-window": dict(context=301, num_q_heads=16, num_kv_heads=2, k_group=64, v_group=64,
+                                        window=40),
+    "g8-f32q-kgroup128": dict(context=233, num_q_heads=16, num_kv_heads=2, q_dtype="f32", k_group=128),
+    "g4-f32q-kgroup64-window": dict(context=187, q_dtype="f32", k_group=64, window=24),
+    "g8-f32kv-window": dict(context=170, num_q_heads=16, num_kv_heads=2, kv_dtype="f32", q_dtype="f32",
+                            window=20),
+    "g8-fused-steps": dict(batch=2, context=400, num_q_heads=16, num_kv_heads=2, window=32, steps=3),
+    "g8-f32q-fused-steps-kgroup64": dict(batch=2, context=350, num_q_heads=16, num_kv_heads=2, q_dtype="f32",
+                                         k_group=64, window=32, steps=3),
+    "g8-rotated-kgroup128-steps": dict(batch=2, context=500, num_q_heads=16, num_kv_heads=2, rotation=True,
+                                       k_group=128, window=0, steps=3),
+    "g8-rotated-ragged-kgroup64": dict(batch=3, context=0, var_len=(20, 900), num_q_heads=16, num_kv_heads=2,
+                                       rotation=True, k_group=64, window=16),
+}
+
+
+@pytest.mark.parametrize("name", list(ROW_OPERAND))
+def test_row_score_operand(name):
+    wl = small(BASE, config=900 + list(ROW_OPERAND).index(name), **ROW_OPERAND[name])
+    say(f"row operand {name}: {ROW_OPERAND[name]}")
+    run = GpuRun(wl, chunk=64)
+    for s in range(max(wl.steps, 1)):
+        full_check(run, s)
+
+
 # Codes of 3, 5 and 6 bits, stored as bit planes (4, 2 and 1 bits) and recombined into one MFMA
 # operand per pair slot: both append kernels (whole pages and single tokens), every attention
 # feature, and decode steps through the append kernel.
